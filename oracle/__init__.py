@@ -1,0 +1,20 @@
+"""Plain, slow fp64 CPU oracle of TurboQuant-style online vector quantization.
+
+TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.  Only the test suite
+(tests/), the smoke check in __graft_entry__.py and the CPU-baseline leg of
+bench.py may import it.  The HIP library never calls it, and it shares no code,
+table or constant generator with the library: both implement the same written
+definitions independently.
+
+Modules:
+  philox      Philox4x32-10 counter RNG, Box-Muller, bf16 rounding, plan randomness
+  codebook    Lloyd-Max codebook for the rotated-coordinate Beta law
+  rotation    randomized Hadamard rotation as dense fp64 matrices
+  turboquant  encode / query preparation / estimate / top-k
+  layout      packed byte layout of the codes
+
+Parity status of each function is listed in the module docstrings; the only
+function without an external pin is the exact Philox bit stream (no published
+known-answer vectors are available here): it is pinned by statistics and by
+agreement with the library's independent implementation only.
+"""

@@ -1,0 +1,179 @@
+"""The TurboQuant-style quantizer and estimator, step by step in fp64.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+Steps (TurboQuant technical overview, intelliparadigm.com; TurboQuant deep
+dive, blog.hotdry.top):
+  1. norm split: x is zero-padded to D, n = ||x||, u = x / n (u = 0 if n = 0);
+     the norm is stored on its own (overview §4.2.1).
+  2. rotation z = Pi u (overview §2.1; oracle/rotation.py).
+  3. (b-1)-bit Lloyd-Max scalar quantizer on every coordinate (overview
+     §1.2.2, §1.2.3 first stage): idx_i = #{j : t_j <= z_i}, zhat_i = c[idx_i].
+  4. residual r = z - zhat (overview §2.3.1), gamma = ||r||.
+  5. 1-bit QJL: p = S r with S a k x D Gaussian matrix, beta_j = [p_j >= 0]
+     (overview §2.3.2; deep dive §3: one sign bit per dimension, so k = D).
+  6. asymmetric estimate against a full-precision query y (deep dive §3:
+     high-precision query, low-precision data; overview §4.2.2: the query takes
+     the same rotation):
+        y' = Pi pad(y),  w = S y',
+        est = n * ( <y', zhat> + gamma * sqrt(pi/2) / k * sum_j w_j (2 beta_j - 1) ).
+     The constant sqrt(pi/2)/k is not printed on the pages; it is the one that
+     makes the estimate unbiased (overview §1.2.3): for a Gaussian row s,
+     E[sign(<s, r>) <s, y'>] = sqrt(2/pi) <r, y'> / ||r||.
+  7. top-k by estimate, ties broken by the smaller key index (overview §4.2.2,
+     first retrieval stage).
+
+With an outlier mask (overview §4.1.1: a share of outlier channels kept at a
+higher bit-width) the channels split into two independent sub-plans, each
+padded to its own power of two with its own rotation, codebook and QJL
+matrix; the estimate is the sum of the two sub-estimates.
+"""
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from . import codebook, philox, rotation
+
+MIN_D = 32
+MAX_D = 2048
+
+
+def padded_length(d):
+    """D = smallest power of two >= d, and at least 32 (one 32-bit code word)."""
+    D = MIN_D
+    while D < d:
+        D *= 2
+    return D
+
+
+@dataclass
+class Plan:
+    d: int                 # channels this (sub-)plan quantizes
+    bits: int              # b: total bits per coordinate (b-1 MSE + 1 QJL)
+    seed: int
+    subset: int            # 0 regular channels, 1 outlier channels
+    D: int
+    R: int
+    k: int
+    levels: np.ndarray     # 2^R ascending, fp64
+    thresholds: np.ndarray  # 2^R - 1 ascending, fp64
+    signs: np.ndarray      # (3, D) +-1
+    S: np.ndarray          # (k, D), bf16-valued fp64
+
+
+def make_plan(d, bits, seed, subset=0):
+    D = padded_length(d)
+    R = bits - 1
+    levels, thresholds = codebook.solve_codebook(D, R)
+    signs = philox.rotation_signs(seed, subset, D)
+    S = philox.qjl_matrix(seed, subset, D, D)
+    return Plan(d=d, bits=bits, seed=seed, subset=subset, D=D, R=R, k=D,
+                levels=levels, thresholds=thresholds, signs=signs, S=S)
+
+
+@dataclass
+class SplitPlan:
+    """Sub-plans over channel subsets (one subset when there is no mask)."""
+    d: int
+    channels: list          # per sub-plan: int array of channel indices
+    plans: list
+
+
+def make_split_plan(d, bits, seed, mask=None, outlier_bits=0):
+    if mask is None:
+        return SplitPlan(d=d, channels=[np.arange(d)], plans=[make_plan(d, bits, seed, 0)])
+    mask = np.asarray(mask).astype(bool)
+    reg = np.nonzero(~mask)[0]
+    out = np.nonzero(mask)[0]
+    return SplitPlan(d=d, channels=[reg, out],
+                     plans=[make_plan(len(reg), bits, seed, 0),
+                            make_plan(len(out), outlier_bits, seed, 1)])
+
+
+def pad(X, D):
+    X = np.asarray(X, dtype=np.float64)
+    out = np.zeros(X.shape[:-1] + (D,))
+    out[..., :X.shape[-1]] = X
+    return out
+
+
+def bucketize(z, thresholds):
+    """idx = number of thresholds t_j with t_j <= z."""
+    return np.sum(z[..., None] >= thresholds, axis=-1)
+
+
+def qjl_signs(S, r):
+    """beta_j = 1 if (S r)_j >= 0 else 0, for each row r."""
+    p = r @ S.T
+    return (p >= 0).astype(np.uint8), p
+
+
+def encode(plan, X):
+    """Codes of the rows of X (n x d): dict with idx (n, D), beta (n, k),
+    norm (n,), gamma (n,), and the intermediates z, r, p."""
+    Xp = pad(X, plan.D)
+    norm = np.sqrt(np.sum(Xp * Xp, axis=-1))
+    safe = np.where(norm > 0, norm, 1.0)
+    U = np.where(norm[:, None] > 0, Xp / safe[:, None], 0.0)
+    z = rotation.rotate(U, plan.signs)
+    idx = bucketize(z, plan.thresholds)
+    zhat = plan.levels[idx]
+    r = z - zhat
+    gamma = np.sqrt(np.sum(r * r, axis=-1))
+    beta, p = qjl_signs(plan.S, r)
+    return dict(idx=idx, beta=beta, norm=norm, gamma=gamma, z=z, r=r, p=p)
+
+
+def prepare_query(plan, Y):
+    """y' = Pi pad(y) and w = S y' for each row y of Y."""
+    yr = rotation.rotate(pad(Y, plan.D), plan.signs)
+    return yr, yr @ plan.S.T
+
+
+def qjl_constant(k):
+    return math.sqrt(math.pi / 2.0) / k
+
+
+def score(plan, codes, Y):
+    """est[q, n] for every query row of Y against every encoded key (per-key
+    centroid lookup summed with the query coordinates, plus the QJL term)."""
+    yr, w = prepare_query(plan, Y)
+    zhat = plan.levels[codes["idx"]]                      # (n, D)
+    mse_term = yr @ zhat.T                                # (nq, n)
+    s = 2.0 * codes["beta"].astype(np.float64) - 1.0      # (n, k)
+    qjl_term = (w @ s.T) * (codes["gamma"][None, :] * qjl_constant(plan.k))
+    return codes["norm"][None, :] * (mse_term + qjl_term)
+
+
+def score_by_reconstruction(plan, codes, Y):
+    """The same estimate computed another way: reconstruct the key's rotated
+    direction zhat + gamma sqrt(pi/2)/k S^T (2 beta - 1), scale by n, and take
+    the plain inner product with the rotated query."""
+    yr = rotation.rotate(pad(Y, plan.D), plan.signs)
+    s = 2.0 * codes["beta"].astype(np.float64) - 1.0
+    recon = plan.levels[codes["idx"]] + \
+        (codes["gamma"] * qjl_constant(plan.k))[:, None] * (s @ plan.S)
+    return yr @ (recon * codes["norm"][:, None]).T
+
+
+def encode_split(sp, X):
+    return [encode(p, np.asarray(X)[..., ch]) for p, ch in zip(sp.plans, sp.channels)]
+
+
+def score_split(sp, codes_list, Y):
+    Y = np.asarray(Y)
+    return sum(score(p, c, Y[..., ch]) for p, c, ch in zip(sp.plans, codes_list, sp.channels))
+
+
+def topk(est, k):
+    """Per row: the k largest estimates, ordered by (-estimate, key index)."""
+    est = np.asarray(est)
+    n = est.shape[-1]
+    ids = np.empty(est.shape[:-1] + (k,), dtype=np.int64)
+    vals = np.empty(est.shape[:-1] + (k,), dtype=est.dtype)
+    for q in np.ndindex(est.shape[:-1]):
+        order = np.lexsort((np.arange(n), -est[q]))[:k]
+        ids[q] = order
+        vals[q] = est[q][order]
+    return ids, vals

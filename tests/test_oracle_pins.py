@@ -1,0 +1,400 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: exact
+identities, closed forms, a published table, an independent library routine,
+brute force on tiny inputs, or statistics of the estimator over seeds.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy import integrate, special, stats
+
+from oracle import codebook, layout, philox, rotation
+from oracle import turboquant as tq
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- Hadamard / rotation
+
+@pytest.mark.parametrize("D", [32, 128, 2048])
+def test_hadamard_is_sylvester_and_orthogonal(D):
+    """H_D from the popcount formula equals the Kronecker power of [[1,1],[1,-1]]
+    and satisfies H H = D I exactly (TurboQuant technical overview, §2.1.1)."""
+    H = rotation.sylvester_hadamard(D)
+    K = np.array([[1.0]])
+    while K.shape[0] < D:
+        K = np.kron(np.array([[1.0, 1.0], [1.0, -1.0]]), K)
+    assert np.array_equal(H, K)
+    assert np.array_equal(H @ H, D * np.eye(D))
+
+
+@pytest.mark.parametrize("D", [32, 128, 2048])
+def test_rotation_orthogonal_and_norm_preserving(D):
+    signs = philox.rotation_signs(7, 0, D)
+    rng = np.random.default_rng(1)
+    X = rng.standard_normal((16, D)) * rng.uniform(0.1, 10, (16, 1))
+    Z = rotation.rotate(X, signs)
+    assert np.max(np.abs(np.linalg.norm(Z, axis=1) / np.linalg.norm(X, axis=1) - 1)) < 1e-12
+    if D <= 128:
+        P = rotation.rotation_matrix(signs)
+        assert np.max(np.abs(P.T @ P - np.eye(D))) < 1e-12
+        assert np.max(np.abs(Z - X @ P.T)) < 1e-12 * np.max(np.abs(Z))
+
+
+def test_rotation_round_order():
+    """Pi = Ht S3 Ht S2 Ht S1: with all diagonals +1 it is Ht^3 = Ht; with only
+    S1 non-trivial it is Ht S1 (the diagonal acts before the transform)."""
+    D = 64
+    Ht = rotation.sylvester_hadamard(D) / np.sqrt(D)
+    x = np.random.default_rng(2).standard_normal(D)
+    ones = np.ones((3, D))
+    assert np.allclose(rotation.rotate(x[None], ones)[0], Ht @ x, atol=1e-13)
+    s = ones.copy()
+    s[0] = philox.rotation_signs(3, 0, D)[0]
+    assert np.allclose(rotation.rotate(x[None], s)[0], Ht @ (s[0] * x), atol=1e-13)
+    s = ones.copy()
+    s[2] = philox.rotation_signs(3, 0, D)[2]
+    assert np.allclose(rotation.rotate(x[None], s)[0], Ht @ (s[2] * (Ht @ (Ht @ x))), atol=1e-13)
+
+
+def _beta_law_cdf(D):
+    a = (D - 1) / 2.0
+    return lambda t: stats.beta.cdf((1.0 + t) / 2.0, a, a)
+
+
+@pytest.mark.parametrize("D,n", [(32, 10000), (128, 3000)])
+def test_beta_law_under_haar_rotation(D, n):
+    """A Haar-rotated unit vector has coordinates 2 Beta((D-1)/2, (D-1)/2) - 1
+    (technical overview §1.2.1, §2.2.1): KS test of one coordinate."""
+    rng = np.random.default_rng(11)
+    u = np.zeros(D)
+    u[0] = 1.0
+    z = np.array([(rotation.haar_rotation(D, rng) @ u)[3] for _ in range(n)])
+    assert stats.kstest(z, _beta_law_cdf(D)).pvalue > 0.01
+
+
+def _config_like_vectors(D, rng):
+    g = rng.standard_normal(D)
+    out = g.copy()
+    out[rng.choice(D, max(1, D // 32), replace=False)] *= 10.0
+    t = stats.t.rvs(3, size=D, random_state=rng)
+    aniso = rng.standard_normal(D) / np.sqrt(np.arange(1, D + 1))
+    return {"gaussian": g, "outliers_x10": out, "student_t3": t, "anisotropic": aniso}
+
+
+@pytest.mark.parametrize("D", [128, 2048])
+def test_beta_law_under_structured_rotation(D):
+    """The three-round randomized Hadamard rotation gives the same coordinate law
+    over seeds on the config-like input laws; also E z = 0, E z^2 = 1/D."""
+    n_seeds = 10000 if D == 128 else 2000
+    rng = np.random.default_rng(5)
+    vecs = _config_like_vectors(D, rng)
+    Ht = rotation.sylvester_hadamard(D) / np.sqrt(D)
+    # signs for all seeds in one batch of Philox calls
+    words = []
+    for r in range(3):
+        n_words = D // 32
+        b = np.arange((n_words + 3) // 4, dtype=np.uint64)
+        seeds = np.arange(n_seeds, dtype=np.uint64)
+        w = philox.philox4x32_10(b[None, :], 0, philox.domain_word(1, 0, r), 0,
+                                 seeds[:, None], 0)
+        words.append(np.stack(w, axis=2).reshape(n_seeds, -1)[:, :n_words])
+    i = np.arange(D)
+    signs = np.stack([np.where((w[:, i // 32] >> (i % 32).astype(np.uint64)) & np.uint64(1), -1.0, 1.0)
+                      for w in words], axis=1)                         # (seeds, 3, D)
+    assert np.array_equal(signs[7], philox.rotation_signs(7, 0, D))
+    for name, v in vecs.items():
+        u = v / np.linalg.norm(v)
+        z = np.tile(u, (n_seeds, 1))
+        for r in range(3):
+            z = (z * signs[:, r, :]) @ Ht.T
+        coord = z[:, 5]
+        p = stats.kstest(coord, _beta_law_cdf(D)).pvalue
+        assert p > 0.01, (name, p)
+        assert abs(coord.mean()) < 4 * math.sqrt(1.0 / D / n_seeds), name
+        assert abs(np.mean(coord ** 2) * D - 1) < 4 * math.sqrt(2.0 / n_seeds), name
+
+
+# ---------------------------------------------------------------- codebook
+
+CODEBOOK_CASES = [(128, 3), (128, 2), (128, 1), (32, 4), (32, 3), (2048, 3), (64, 2)]
+
+
+@pytest.mark.parametrize("D,R", CODEBOOK_CASES)
+def test_codebook_lloyd_max_conditions(D, R):
+    """Midpoint condition, centroid condition (checked by adaptive quadrature of
+    the density, independent of the incomplete-Beta path), symmetry."""
+    levels, t = codebook.solve_codebook(D, R)
+    assert len(levels) == 2 ** R and len(t) == 2 ** R - 1
+    assert np.all(np.diff(levels) > 0)
+    # fixed point reached to the iteration's stopping tolerance (1e-13 / sqrt(D))
+    assert np.allclose(t, 0.5 * (levels[:-1] + levels[1:]), rtol=0, atol=2e-13 / math.sqrt(D))
+    a = (D - 3) / 2.0
+    f = lambda s: (1 - s * s) ** a
+    edges = np.concatenate([[-1.0], t, [1.0]])
+    for j in range(len(levels)):
+        lo, hi = edges[j], edges[j + 1]
+        m0 = integrate.quad(f, lo, hi, epsabs=0, epsrel=1e-13, limit=200)[0]
+        m1 = integrate.quad(lambda s: s * f(s), lo, hi, epsabs=0, epsrel=1e-13, limit=200)[0]
+        assert abs(m1 / m0 - levels[j]) < 1e-11 * max(abs(levels[j]), 1 / math.sqrt(D))
+    assert np.max(np.abs(levels + levels[::-1])) < 1e-14
+
+
+@pytest.mark.parametrize("D", [32, 128, 2048])
+def test_codebook_one_bit_closed_form(D):
+    """R = 1: levels are +-E|T| = +-Gamma(D/2) / (sqrt(pi) Gamma((D+1)/2))."""
+    levels, t = codebook.solve_codebook(D, 1)
+    expect = math.exp(special.gammaln(D / 2) - special.gammaln((D + 1) / 2)) / math.sqrt(math.pi)
+    assert np.allclose(levels, [-expect, expect], rtol=1e-12, atol=0)
+    assert abs(t[0]) < 1e-15
+
+
+@pytest.mark.parametrize("R", [1, 2, 3, 4])
+def test_codebook_D3_is_uniform_quantizer(R):
+    """D = 3: the coordinate law is uniform on [-1, 1], so Lloyd-Max is the uniform
+    quantizer with levels -1 + (2j+1)/2^R and MSE 1 / (3 4^R)."""
+    L = 2 ** R
+    levels, t = codebook.solve_codebook(3, R)
+    assert np.allclose(levels, -1 + (2 * np.arange(L) + 1) / L, atol=1e-12)
+    assert abs(codebook.codebook_mse(3, levels, t) - 1 / (3 * 4 ** R)) < 1e-12
+
+
+@pytest.mark.parametrize("R", [2, 3])
+def test_codebook_large_D_tends_to_max_gaussian_table(R):
+    gold = json.load(open(os.path.join(GOLDEN, "max1960_gaussian_lloyd_max.json")))
+    g_levels, _ = codebook.solve_gaussian_codebook(R)
+    table = np.array(gold["levels"][str(R)])
+    L = 2 ** R
+    assert np.allclose(g_levels[L // 2:], table, atol=gold["abs_tol"], rtol=0)
+    levels, _ = codebook.solve_codebook(2048, R)
+    assert np.allclose(math.sqrt(2048) * levels[L // 2:], table, atol=gold["abs_tol"], rtol=0)
+
+
+@pytest.mark.parametrize("D,R", CODEBOOK_CASES)
+def test_mse_within_2_7_of_shannon_bound(D, R):
+    """Per-vector MSE of the MSE stage <= 2.7 * 4^-R (technical overview §3.1,
+    D*(R) = 4^-R for a unit vector at R bits per coordinate)."""
+    levels, t = codebook.solve_codebook(D, R)
+    mse_vec = D * codebook.codebook_mse(D, levels, t)
+    assert mse_vec <= 2.7 * 4.0 ** (-R)
+    assert mse_vec >= 4.0 ** (-R)   # cannot beat the bound
+
+
+@pytest.mark.parametrize("D,R", [(128, 2), (128, 3), (32, 4)])
+def test_empirical_mse_matches_analytic(D, R):
+    plan = tq.make_plan(D, R + 1, seed=0)
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((10000, D))
+    c = tq.encode(plan, X)
+    err = np.sum((c["z"] - plan.levels[c["idx"]]) ** 2, axis=1)
+    analytic = D * codebook.codebook_mse(D, plan.levels, plan.thresholds)
+    assert abs(err.mean() - analytic) < 3 * err.std() / math.sqrt(len(err))
+
+
+@pytest.mark.parametrize("D,n", [(4, 300), (8, 100)])
+def test_bucketize_is_nearest_codeword(D, n):
+    """Threshold bucketize == exhaustive nearest point of the product codebook."""
+    levels, t = codebook.solve_codebook(32, 2)
+    L = len(levels)
+    rng = np.random.default_rng(4)
+    z = rng.uniform(-0.6, 0.6, (n, D))
+    grid = np.array(np.meshgrid(*([np.arange(L)] * D), indexing="ij")).reshape(D, -1).T
+    cw = levels[grid]                                                   # (L^D, D)
+    best = np.argmin(((z[:, None, :] - cw[None]) ** 2).sum(-1), axis=1)
+    assert np.array_equal(grid[best], tq.bucketize(z, t))
+
+
+# ---------------------------------------------------------------- estimator
+
+def _plan_for_seed(D, bits, seed, levels, t):
+    return tq.Plan(d=D, bits=bits, seed=seed, subset=0, D=D, R=bits - 1, k=D, levels=levels,
+                   thresholds=t, signs=philox.rotation_signs(seed, 0, D),
+                   S=philox.qjl_matrix(seed, 0, D, D))
+
+
+@pytest.mark.parametrize("case", ["gaussian", "outliers"])
+def test_estimator_unbiased_over_seeds(case):
+    """E[est(x, y)] = <x, y> over 10^4 plan seeds (technical overview §1.2.3):
+    |mean - <x,y>| < 3 standard errors."""
+    D, bits = 128, 3
+    levels, t = codebook.solve_codebook(D, bits - 1)
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal(D)
+    y = rng.standard_normal(D)
+    if case == "outliers":
+        x[[3, 70]] *= 10
+        y[[3, 9]] *= 10
+    ests = np.array([tq.score(p, tq.encode(p, x[None]), y[None])[0, 0]
+                     for p in (_plan_for_seed(D, bits, s, levels, t) for s in range(10000))])
+    se = ests.std(ddof=1) / math.sqrt(len(ests))
+    assert abs(ests.mean() - x @ y) < 3 * se
+
+
+def test_qjl_term_variance_closed_form():
+    """At a fixed rotation, over S draws: Var(QJL term) =
+    n^2 gamma^2 / k * (pi/2 ||y'||^2 - <y', r/gamma>^2) within 5%."""
+    D, bits, draws = 32, 3, 20000
+    levels, t = codebook.solve_codebook(D, bits - 1)
+    base = _plan_for_seed(D, bits, 0, levels, t)
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal(D)
+    y = rng.standard_normal(D)
+    c0 = tq.encode(base, x[None])
+    yr = rotation.rotate(y[None], base.signs)[0]
+    n, g, r = c0["norm"][0], c0["gamma"][0], c0["r"][0]
+    mse_part = n * yr @ base.levels[c0["idx"][0]]
+    vals = []
+    for s in range(1, draws + 1):
+        S = philox.qjl_matrix(s, 0, D, D)
+        p = tq.Plan(**{**base.__dict__, "S": S})
+        vals.append(tq.score(p, tq.encode(p, x[None]), y[None])[0, 0] - mse_part)
+    vals = np.array(vals)
+    expect = n * n * g * g / D * (math.pi / 2 * yr @ yr - (yr @ r / g) ** 2)
+    assert abs(vals.var() / expect - 1) < 0.05
+    assert abs(vals.mean() - n * yr @ r) < 3 * vals.std() / math.sqrt(draws)
+
+
+@pytest.mark.parametrize("D,bits", [(128, 4), (2048, 4), (32, 5)])
+def test_score_two_ways_agree(D, bits):
+    plan = tq.make_plan(D, bits, seed=1)
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((50, D))
+    Y = rng.standard_normal((7, D))
+    c = tq.encode(plan, X)
+    a = tq.score(plan, c, Y)
+    b = tq.score_by_reconstruction(plan, c, Y)
+    assert np.max(np.abs(a - b)) < 1e-12 * np.max(np.abs(a))
+
+
+def test_more_bits_converge_to_exact_inner_product():
+    D = 128
+    rng = np.random.default_rng(10)
+    X = rng.standard_normal((200, D))
+    Y = rng.standard_normal((8, D))
+    exact = Y @ X.T
+    errs, gammas = [], []
+    for bits in [2, 3, 4, 5, 6]:
+        p = tq.make_plan(D, bits, seed=0)
+        c = tq.encode(p, X)
+        errs.append(np.sqrt(np.mean((tq.score(p, c, Y) - exact) ** 2)))
+        gammas.append(c["gamma"].mean())
+    assert all(a > b for a, b in zip(errs, errs[1:]))
+    assert all(a > b for a, b in zip(gammas, gammas[1:]))
+    assert gammas[-1] < 0.05
+
+
+def test_zero_vector_and_zero_query():
+    p = tq.make_plan(100, 3, seed=0)
+    X = np.zeros((2, 100))
+    X[1, 5] = 2.0
+    c = tq.encode(p, X)
+    assert c["norm"][0] == 0 and np.all(np.isfinite(c["z"]))
+    est = tq.score(p, c, np.ones((1, 100)))
+    assert est[0, 0] == 0.0
+    assert tq.score(p, c, np.zeros((1, 100)))[0, 1] == 0.0
+
+
+def test_split_plan_scores_sum_of_subsets():
+    d = 128
+    rng = np.random.default_rng(12)
+    mask = np.zeros(d, dtype=np.uint8)
+    mask[rng.choice(d, 32, replace=False)] = 1
+    sp = tq.make_split_plan(d, 3, 0, mask, 5)
+    assert [p.D for p in sp.plans] == [128, 32] and [p.R for p in sp.plans] == [2, 4]
+    X = rng.standard_normal((40, d))
+    Y = rng.standard_normal((4, d))
+    cl = tq.encode_split(sp, X)
+    est = tq.score_split(sp, cl, Y)
+    ch0, ch1 = sp.channels
+    assert np.allclose(est, tq.score(sp.plans[0], cl[0], Y[:, ch0]) +
+                       tq.score(sp.plans[1], cl[1], Y[:, ch1]))
+    # distinct subsets draw distinct randomness
+    assert not np.array_equal(sp.plans[0].signs[:, :32], sp.plans[1].signs)
+
+
+def test_topk_matches_brute_force_with_ties():
+    rng = np.random.default_rng(13)
+    est = np.round(rng.standard_normal((5, 300)), 1)     # many exact ties
+    ids, vals = tq.topk(est, 10)
+    for q in range(5):
+        ref = sorted(range(300), key=lambda i: (-est[q, i], i))[:10]
+        assert list(ids[q]) == ref
+        assert np.array_equal(vals[q], est[q, ref])
+
+
+# ---------------------------------------------------------------- randomness
+
+def test_philox_uniform_and_gaussian_statistics():
+    w = philox.stream_words(0, philox.PURPOSE_GAUSS, 0, 0, 1 << 18)
+    u = philox.uniforms_from_words(w)
+    assert u.min() > 0 and u.max() < 1
+    assert stats.kstest(u, "uniform").pvalue > 0.01
+    bits = np.unpackbits(w.astype("<u4").view(np.uint8))
+    assert abs(bits.mean() - 0.5) < 4 * 0.5 / math.sqrt(bits.size)
+    g = philox.gaussian_stream(0, 0, 1 << 20)
+    assert stats.kstest(g, "norm").pvalue > 0.01
+    assert abs(g.mean()) < 4 / math.sqrt(g.size) and abs(g.var() - 1) < 4 * math.sqrt(2 / g.size)
+    # consecutive elements uncorrelated (pairs share a Box-Muller radius)
+    assert abs(np.corrcoef(g[:-1], g[1:])[0, 1]) < 4 / math.sqrt(g.size)
+
+
+def test_philox_streams_distinct_and_counter_bijective():
+    n = 1 << 16
+    a = philox.stream_words(0, 1, 0, 0, n)
+    assert len(np.unique(a.reshape(-1, 4), axis=0)) == n
+    others = [philox.stream_words(1, 1, 0, 0, 64), philox.stream_words(0, 1, 0, 1, 64),
+              philox.stream_words(0, 1, 1, 0, 64), philox.stream_words(0, 2, 0, 0, 64),
+              philox.stream_words(1 << 32, 1, 0, 0, 64)]
+    for o in others:
+        assert np.mean(o == a[:256]) < 0.05
+
+
+def test_bf16_rounding_ties_to_even_and_matches_fp32_conversion():
+    import torch
+    e = 2.0 ** -8
+    cases = {1 + e: 1.0, 1 + 3 * e: 1 + 4 * e, 1 + e + 2 ** -30: 1 + 2 * e,
+             -(1 + e): -1.0, 0.0: 0.0, 3.0: 3.0, 1 - 2 ** -10: 1.0}
+    for x, want in cases.items():
+        assert philox.round_to_bf16(np.float64(x)) == want, x
+    f = np.random.default_rng(14).standard_normal(100000).astype(np.float32)
+    f[:1000] = (1 + (2 * np.arange(1000) + 1) * 2.0 ** -9).astype(np.float32)   # exact ties
+    ref = torch.from_numpy(f).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(philox.round_to_bf16(f.astype(np.float64)), ref)
+
+
+def test_qjl_matrix_is_bf16_gaussian():
+    S = philox.qjl_matrix(0, 0, 128, 128)
+    assert np.array_equal(S, philox.round_to_bf16(S))
+    assert stats.kstest(S.ravel(), "norm").pvalue > 0.01
+    assert not np.array_equal(S, philox.qjl_matrix(0, 1, 128, 128))
+
+
+# ---------------------------------------------------------------- layout
+
+def test_layout_bit_positions_by_hand():
+    D, R = 64, 2
+    idx = np.zeros((1, D), dtype=np.int64)
+    beta = np.zeros((1, D), dtype=np.uint8)
+    idx[0, 0] = 3          # chunk 0: word 0 bit 0 and word 1 bit 0
+    idx[0, 33] = 2         # chunk 1: word 1 (plane 1) bit 1
+    beta[0, 31] = 1        # chunk 0: word 2 bit 31
+    beta[0, 63] = 1        # chunk 1: word 2 bit 31
+    rec = layout.pack(dict(idx=idx, beta=beta, norm=np.array([2.0]), gamma=np.array([0.5])), D, R)
+    assert rec.shape == (1, layout.record_bytes(D, R)) == (1, 32)
+    words = rec[0, :24].view("<u4")
+    assert list(words) == [1, 1, 1 << 31, 0, 2, 1 << 31]
+    assert list(rec[0, 24:].view("<f4")) == [2.0, 0.5]
+
+
+@pytest.mark.parametrize("D,R", [(32, 4), (128, 2), (2048, 3)])
+def test_layout_roundtrip(D, R):
+    rng = np.random.default_rng(15)
+    c = dict(idx=rng.integers(0, 2 ** R, (5, D)), beta=rng.integers(0, 2, (5, D)).astype(np.uint8),
+             norm=rng.uniform(0, 5, 5).astype(np.float32), gamma=rng.uniform(0, 1, 5).astype(np.float32))
+    u = layout.unpack(layout.pack(c, D, R), D, R)
+    assert np.array_equal(u["idx"], c["idx"]) and np.array_equal(u["beta"], c["beta"])
+    assert np.array_equal(u["norm"], c["norm"]) and np.array_equal(u["gamma"], c["gamma"])
