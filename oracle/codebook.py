@@ -83,7 +83,12 @@ def lloyd_max(mass, first_moment, support, init_thresholds, tol, max_iter):
 
 def solve_codebook(D, R, tol_rel=1e-13, max_iter=400000):
     """Lloyd-Max levels (2^R, ascending) and thresholds (2^R - 1) for the law of
-    one rotated coordinate in D dimensions."""
+    one rotated coordinate in D dimensions.
+
+    The law is symmetric about 0 (a Beta law with equal parameters), so the
+    optimal quantizer is odd-symmetric: the levels returned are mirrored
+    exactly (c_l = -c_{L-1-l}) and the thresholds are their midpoints, which
+    puts the middle threshold exactly at 0 (a zero coordinate counts as >= it)."""
     L = 2 ** R
     s = 1.0 / np.sqrt(D)
     span = min(4.0 * s, 0.999)
@@ -91,7 +96,8 @@ def solve_codebook(D, R, tol_rel=1e-13, max_iter=400000):
     levels, t, _ = lloyd_max(lambda lo, hi: beta_cell_mass(D, lo, hi),
                              lambda lo, hi: beta_cell_first_moment(D, lo, hi),
                              (-1.0, 1.0), init, tol_rel * s, max_iter)
-    return levels, t
+    levels = 0.5 * (levels - levels[::-1])
+    return levels, 0.5 * (levels[:-1] + levels[1:])
 
 
 def solve_gaussian_codebook(R, tol=1e-13, max_iter=400000):

@@ -131,8 +131,8 @@ def test_codebook_lloyd_max_conditions(D, R):
     levels, t = codebook.solve_codebook(D, R)
     assert len(levels) == 2 ** R and len(t) == 2 ** R - 1
     assert np.all(np.diff(levels) > 0)
-    # fixed point reached to the iteration's stopping tolerance (1e-13 / sqrt(D))
-    assert np.allclose(t, 0.5 * (levels[:-1] + levels[1:]), rtol=0, atol=2e-13 / math.sqrt(D))
+    assert np.array_equal(t, 0.5 * (levels[:-1] + levels[1:]))
+    assert t[len(t) // 2] == 0.0
     a = (D - 3) / 2.0
     f = lambda s: (1 - s * s) ** a
     edges = np.concatenate([[-1.0], t, [1.0]])
@@ -141,7 +141,7 @@ def test_codebook_lloyd_max_conditions(D, R):
         m0 = integrate.quad(f, lo, hi, epsabs=0, epsrel=1e-13, limit=200)[0]
         m1 = integrate.quad(lambda s: s * f(s), lo, hi, epsabs=0, epsrel=1e-13, limit=200)[0]
         assert abs(m1 / m0 - levels[j]) < 1e-11 * max(abs(levels[j]), 1 / math.sqrt(D))
-    assert np.max(np.abs(levels + levels[::-1])) < 1e-14
+    assert np.array_equal(levels, -levels[::-1])
 
 
 @pytest.mark.parametrize("D", [32, 128, 2048])
@@ -150,7 +150,7 @@ def test_codebook_one_bit_closed_form(D):
     levels, t = codebook.solve_codebook(D, 1)
     expect = math.exp(special.gammaln(D / 2) - special.gammaln((D + 1) / 2)) / math.sqrt(math.pi)
     assert np.allclose(levels, [-expect, expect], rtol=1e-12, atol=0)
-    assert abs(t[0]) < 1e-15
+    assert t[0] == 0.0
 
 
 @pytest.mark.parametrize("R", [1, 2, 3, 4])
