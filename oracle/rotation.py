@@ -36,13 +36,16 @@ def sylvester_hadamard(D):
 
 def rotate(U, signs):
     """Rows of U (n x D) mapped through Pi: for each round r, multiply by the
-    diagonal S_r, then by the normalized Hadamard matrix."""
+    diagonal S_r, then by the Hadamard matrix; the three 1/sqrt(D) factors of
+    Ht = H_D / sqrt(D) are applied together as one final D^(-3/2).  With the
+    integer matrix H_D the transform is exact for inputs with few significant
+    bits, so coordinates that are exactly zero stay exactly zero."""
     D = U.shape[-1]
-    Ht = sylvester_hadamard(D) / np.sqrt(D)
+    H = sylvester_hadamard(D)
     Z = np.asarray(U, dtype=np.float64)
     for r in range(3):
-        Z = (Z * signs[r][None, :]) @ Ht.T
-    return Z
+        Z = (Z * signs[r][None, :]) @ H.T
+    return Z * float(D) ** -1.5
 
 
 def rotation_matrix(signs):
