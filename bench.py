@@ -1,0 +1,147 @@
+"""Benchmark of the quantizer's hot path on one MI355X.
+
+One step = encode every key of the long-context decode workload (norm split,
+randomized Hadamard rotation, Lloyd-Max indices, QJL signs: one fused launch)
+and score every query head against its KV head's codes (query preparation +
+the streaming estimator).  Inputs are resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is scores per second over whole steps; the
+per-kernel rates, the roofline of the dominant kernel (algorithmic bytes per
+launch / mean HIP-event duration on the launch stream) and the fp64 CPU oracle
+timed on a bounded sample of the same workload ride along.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-keys", type=int, default=1 << 18)
+    return ap.parse_args()
+
+
+def cpu_baseline(keys_sample, queries_sample, bits, seed):
+    """The fp64 oracle, as it stands, on one KV head's first keys and its 4 query heads."""
+    import numpy as np
+    from oracle import turboquant as otq
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    x = keys_sample.astype(np.float64)
+    y = queries_sample.astype(np.float64)
+    plan = otq.make_plan(x.shape[1], bits, seed)
+    t0 = time.perf_counter()
+    codes = otq.encode(plan, x)
+    est = otq.score(plan, codes, y)
+    dt = time.perf_counter() - t0
+    return {"value": est.size / dt, "unit": "scores/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d keys of one (sequence, KV head) x its %d query heads: fp64 encode + "
+                      "score (plan solve excluded), %.1f s" % (x.shape[0], y.shape[0], dt)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only; --gpus %d is not supported (the multi-GPU layout "
+              "is described in DESIGN.md, not run)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import rotation_online_vector_amd as tq
+    import workloads
+
+    W = workloads.LONGCTX
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    keys, queries, _ = workloads.longctx_inputs(dev)
+    n_seq, n_kv, n_tok, d, G = W["n_seq"], W["n_kv"], W["n_tok"], W["d"], W["group"]
+    n_keys = n_seq * n_kv * n_tok
+    n_groups = n_seq * n_kv
+    plan = tq.tq_plan_create(d, W["bits"], W["seed"])
+    rb = plan.record_bytes
+    codes = torch.empty((n_keys, rb), dtype=torch.uint8, device=dev)
+    scores = torch.empty((n_seq * n_kv * G, n_tok), dtype=torch.float32, device=dev)
+    xk = keys.view(n_keys, d)
+    qv = queries.view(n_groups * G, d)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        tq.tq_encode(plan, xk, codes)
+        if ev is not None:
+            ev[1].record(stream)
+        tq.tq_score(plan, qv, codes, n=n_tok, nq_per_group=G, n_groups=n_groups, scores=scores)
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    sc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_step = wall * 1e3 / args.steps
+    n_scores = n_groups * G * n_tok
+
+    # algorithmic bytes per launch
+    enc_bytes = n_keys * d * 2 + n_keys * rb                     # bf16 keys in, records out
+    sc_bytes = n_keys * rb + n_scores * 4 + n_groups * G * d * 2  # records + logits + queries
+    kern = {
+        "tq_encode": {"ms": enc_ms, "bytes": enc_bytes, "gbs": enc_bytes / enc_ms / 1e6,
+                      "vectors_per_s": n_keys / enc_ms * 1e3},
+        "tq_score": {"ms": sc_ms, "bytes": sc_bytes, "gbs": sc_bytes / sc_ms / 1e6,
+                     "scores_per_s": n_scores / sc_ms * 1e3},
+    }
+    dom = max(kern, key=lambda k: kern[k]["ms"])
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(kern[dom]["gbs"], 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
+            "traffic": None, "bytes_per_launch": kern[dom]["bytes"]}
+    out = {
+        "metric": "quantized-key scores/sec + HBM GB/s (d=128, 3-bit); encode vectors/sec",
+        "value": n_scores / (ms_step / 1e3),
+        "unit": "scores/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": W["name"], "n_seq": n_seq, "kv_heads": n_kv, "tokens": n_tok,
+                   "d": d, "bits": W["bits"], "query_heads_per_seq": n_kv * G, "gqa_group": G,
+                   "keys_per_step": n_keys, "scores_per_step": n_scores, "record_bytes": rb},
+        "encode_vectors_per_s": kern["tq_encode"]["vectors_per_s"],
+        "score_scores_per_s": kern["tq_score"]["scores_per_s"],
+        "kernels": {k: {"ms": round(v["ms"], 4), "alg_bytes": v["bytes"], "alg_gbs": round(v["gbs"], 1),
+                        "hbm_frac": round(v["gbs"] / HBM_PEAK_GBS, 4)} for k, v in kern.items()},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        ks = keys[0, 0, :args.cpu_sample_keys].float().cpu().numpy()
+        qs = queries[0, :G].float().cpu().numpy()
+        out["cpu_baseline"] = cpu_baseline(ks, qs, W["bits"], W["seed"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

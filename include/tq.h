@@ -1,0 +1,188 @@
+/*
+ * tq.h -- C ABI of the TurboQuant-style online vector quantizer for AMD MI355X (gfx950).
+ *
+ * The method (TurboQuant technical overview, intelliparadigm.com; TurboQuant
+ * deep dive, blog.hotdry.top): every vector is split into its L2 norm and a
+ * unit direction; the direction is rotated by a seeded randomized Hadamard
+ * transform (three rounds of a +-1 diagonal followed by a normalized
+ * Walsh-Hadamard transform); every rotated coordinate is quantized with a
+ * (b-1)-bit Lloyd-Max codebook solved for the Beta((D-1)/2, (D-1)/2) law of a
+ * rotated coordinate; the residual gets a 1-bit QJL sign sketch under a
+ * seeded Gaussian matrix.  A full-precision query is rotated the same way and
+ * scored against the packed codes with an unbiased inner-product estimate.
+ *
+ * Conventions for every call:
+ *   - Status is returned, never thrown; nothing aborts or prints.
+ *   - "device" pointers are HIP device memory of the current device; "host"
+ *     pointers are ordinary CPU memory.  The caller owns every buffer it passes.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  tq_encode,
+ *     tq_score, tq_qjl and tq_topk only enqueue work on it and return; their
+ *     outputs are valid once the stream reaches that point.  A launch failure
+ *     is reported as TQ_EDEVICE.
+ *   - A plan is immutable after creation and may be used from several streams
+ *     and threads at once.  Destroying a plan while work that uses it is still
+ *     queued is undefined.
+ *
+ * Code layout (the "record" of one vector; little-endian 32-bit words):
+ *   For a sub-plan with rotated length D (a power of two, 32..2048) and R
+ *   index bits, the record is, for each chunk g = 0 .. D/32-1:
+ *       R words: bit t of word m = bit m of the index of coordinate 32g+t
+ *       1 word:  bit t = QJL sign bit of projection row 32g+t (1 = non-negative)
+ *   followed by float32 norm ||x|| and float32 residual norm gamma.
+ *   Size: 4*(R+1)*D/32 + 8 bytes.  With an outlier mask the record of a vector
+ *   is the regular sub-plan's record followed by the outlier sub-plan's
+ *   record.  Records of consecutive vectors are contiguous.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tq_status {
+  TQ_OK = 0,
+  TQ_EINVAL = -1,       /* invalid argument (null, size, alignment, range) */
+  TQ_ENOMEM = -2,       /* host or device allocation failed */
+  TQ_EDEVICE = -3,      /* no usable HIP device, or a HIP call/launch failed */
+  TQ_EUNSUPPORTED = -4  /* valid request this build does not implement */
+} tq_status;
+
+typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
+
+typedef struct tq_plan tq_plan;
+
+typedef struct tq_subplan_desc {
+  int32_t d;              /* input channels of this sub-plan */
+  int32_t D;              /* rotated length: max(32, next power of two >= d) */
+  int32_t R;              /* index bits per coordinate (b - 1) */
+  int32_t k;              /* QJL rows (= D: one sign bit per rotated coordinate) */
+  int32_t record_offset;  /* byte offset of this sub-plan's record in a vector's record */
+  int32_t record_bytes;   /* 4*(R+1)*D/32 + 8 */
+} tq_subplan_desc;
+
+typedef struct tq_plan_desc {
+  int32_t d;              /* channels of an input vector */
+  int32_t n_subplans;     /* 1, or 2 with an outlier mask (0 = regular, 1 = outlier) */
+  int32_t record_bytes;   /* bytes per encoded vector */
+  int32_t reserved;
+  tq_subplan_desc sub[2];
+} tq_plan_desc;
+
+/* Human-readable name of a status code (static string). */
+const char* tq_status_string(tq_status status);
+
+/*
+ * Create a plan: solve the Lloyd-Max codebook(s) on the host, draw the
+ * rotation signs and the QJL matrix from `seed`, and upload them to the
+ * current device.
+ *   d            input dimension, 1 <= d <= 2048
+ *   bits         b, total bits per coordinate for the regular channels, 2..5
+ *                (b-1 Lloyd-Max bits + 1 QJL bit; TurboQuant overview §1.2.3)
+ *   seed         64-bit seed of all plan randomness (overview §2.1.2)
+ *   outlier_mask host array of d bytes (nonzero = outlier channel) or NULL;
+ *                copied.  Outlier channels form a second, independent
+ *                sub-plan with its own rotation and QJL matrix (overview
+ *                §4.1.1 outlier channels); the mask must select 1..d-1 channels.
+ *   outlier_bits b of the outlier sub-plan, 2..5 (ignored when the mask is NULL)
+ *   out          receives the plan
+ * Errors: TQ_EINVAL (range, null `out`), TQ_ENOMEM, TQ_EDEVICE (no device,
+ * upload failure).  On error *out is set to NULL.
+ */
+tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_mask,
+                         int outlier_bits, tq_plan** out);
+
+/* Release a plan's host and device tables.  NULL is accepted. */
+void tq_plan_destroy(tq_plan* plan);
+
+/* Describe a plan (sizes and record layout) into *desc (host memory). */
+tq_status tq_plan_info(const tq_plan* plan, tq_plan_desc* desc);
+
+/*
+ * Encode n vectors (norm split, rotation, Lloyd-Max indices, residual norm,
+ * QJL signs: overview §1.2, §2.1, §2.3; one fused launch).
+ *   x      device, n rows of d elements of type dt, row i at x + i*ldx elements;
+ *          4-byte aligned (bf16) / 4-byte aligned (f32)
+ *   ldx    row stride in elements, ldx >= d
+ *   codes  device, n * record_bytes bytes, 16-byte aligned; written entirely
+ * Errors: TQ_EINVAL (null with n > 0, n < 0, ldx < d, misalignment),
+ * TQ_EDEVICE.  n = 0 is a no-op.
+ */
+tq_status tq_encode(const tq_plan* plan, const void* x, tq_dtype dt, int64_t n, int64_t ldx,
+                    void* codes, void* stream);
+
+/*
+ * Score queries against encoded vectors with the unbiased estimate
+ *   est = n_x * ( <y', c[idx]> + gamma * sqrt(pi/2)/k * sum_j (S y')_j (2 beta_j - 1) ),
+ *   y' = the plan's rotation applied to the zero-padded query
+ * (overview §1.2.3 and §4.2.2; deep dive §3: full-precision query against
+ * low-precision data); summed over sub-plans when there is an outlier mask.
+ * Queries and codes are grouped (grouped-query attention: query head h reads
+ * key head h / nq_per_group):
+ *   q       device, n_groups*nq_per_group rows of d elements (dtype dt), row
+ *           stride ldq elements; rows g*nq_per_group .. +nq_per_group-1 are group g
+ *   codes   device, n_groups * n records; group g's records start at record g*n
+ *   scores  device float32 [n_groups*nq_per_group][n], row-major, written entirely
+ * Raw inner-product estimates: no 1/sqrt(d), no softmax.
+ * Uses a stream-ordered temporary of n_groups*nq_per_group*(6*D) floats per
+ * sub-plan (hipMallocAsync / hipFreeAsync on `stream`).
+ * Errors: TQ_EINVAL (null, negative sizes, ldq < d, misalignment), TQ_ENOMEM,
+ * TQ_EDEVICE.  Empty sizes are a no-op.
+ */
+tq_status tq_score(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_per_group,
+                   int64_t n_groups, int64_t ldq, const void* codes, int64_t n, float* scores,
+                   void* stream);
+
+/*
+ * Top-k per row of a score matrix (the first, quantized stage of two-stage
+ * retrieval: overview §4.2.2): for each of nq rows of `scores` (device
+ * float32 [nq][n]) the k largest values, ordered by (-value, index).
+ *   ids   device int64 [nq][k], vals device float32 [nq][k]
+ * Errors: TQ_EINVAL (null, k < 1, k > 64, k > n, n >= 2^31), TQ_EDEVICE.
+ * NaN scores are not supported.
+ */
+tq_status tq_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids, float* vals,
+                  void* stream);
+
+/*
+ * The QJL stage alone (overview §2.3.2): beta_j = [ (S r)_j >= 0 ] for n
+ * residual vectors r already in the rotated domain of sub-plan `subplan`.
+ *   r     device float32 [n][D]
+ *   beta  device uint32 [n][D/32]; bit t of word g = beta of row 32g+t
+ * The same kernel code as the sign stage fused inside tq_encode.
+ * Errors: TQ_EINVAL, TQ_EDEVICE.
+ */
+tq_status tq_qjl(const tq_plan* plan, int subplan, const float* r, int64_t n, uint32_t* beta,
+                 void* stream);
+
+/* ---- Host building blocks of a plan (no device needed) ---------------------------------- */
+
+/*
+ * Lloyd-Max codebook for one rotated coordinate in D dimensions with R bits
+ * (overview §1.2.2, §2.2): 2^R ascending levels and 2^R - 1 thresholds (host
+ * double arrays).  Density proportional to (1 - t^2)^((D-3)/2) on [-1, 1].
+ * 3 <= D <= 65536, 1 <= R <= 8.  Errors: TQ_EINVAL.
+ */
+tq_status tq_codebook(int D, int R, double* levels, double* thresholds);
+
+/*
+ * The three +-1 rotation diagonals of sub-plan `subset` (0 regular, 1 outlier)
+ * for `seed`: signs[r*D + i] in {+1, -1} (host int8 [3][D]).  32 <= D <= 65536,
+ * D a power of two.  Errors: TQ_EINVAL.
+ */
+tq_status tq_rotation_signs(uint64_t seed, int subset, int D, int8_t* signs);
+
+/*
+ * The QJL matrix S (k x D) of sub-plan `subset`: bfloat16 bit patterns,
+ * S[j*D + i] = bf16 round-to-nearest-even of a fp64 Box-Muller normal
+ * (host uint16 [k][D]).  1 <= k, D <= 65536.  Errors: TQ_EINVAL.
+ */
+tq_status tq_qjl_matrix(uint64_t seed, int subset, int k, int D, uint16_t* S_bf16);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

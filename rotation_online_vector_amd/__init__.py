@@ -1,0 +1,258 @@
+"""TurboQuant-style online vector quantization on AMD MI355X (gfx950).
+
+A thin ctypes binding over the C ABI of libtq (include/tq.h): the functions
+below carry the ABI's names and only marshal arguments (tensor pointers, sizes,
+the current HIP stream) and allocate output tensors with torch.  Every step of
+encode, scoring and top-k runs in the library's HIP kernels; there is no
+fallback: if the library is missing or no GPU is present, the calls raise.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "_lib", "libtq.so")
+
+TQ_OK, TQ_EINVAL, TQ_ENOMEM, TQ_EDEVICE, TQ_EUNSUPPORTED = 0, -1, -2, -3, -4
+TQ_F32, TQ_BF16 = 0, 1
+
+
+class TqError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (fn, _status_string(status), status))
+
+
+class tq_subplan_desc(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("D", ctypes.c_int32), ("R", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("record_offset", ctypes.c_int32),
+                ("record_bytes", ctypes.c_int32)]
+
+
+class tq_plan_desc(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("n_subplans", ctypes.c_int32),
+                ("record_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("sub", tq_subplan_desc * 2)]
+
+
+EXPORTED = ["tq_status_string", "tq_plan_create", "tq_plan_destroy", "tq_plan_info",
+            "tq_encode", "tq_score", "tq_topk", "tq_qjl", "tq_codebook",
+            "tq_rotation_signs", "tq_qjl_matrix"]
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libtq.so (after torch, so that both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    try:
+        import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+    except ImportError:
+        pass
+    if not os.path.exists(path):
+        raise RuntimeError("libtq.so not built at %s: run `python -m rotation_online_vector_amd.build`"
+                           % path)
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64
+    lib.tq_status_string.argtypes = [i32]
+    lib.tq_status_string.restype = ctypes.c_char_p
+    lib.tq_plan_create.argtypes = [i32, i32, u64, vp, i32, ctypes.POINTER(vp)]
+    lib.tq_plan_create.restype = i32
+    lib.tq_plan_destroy.argtypes = [vp]
+    lib.tq_plan_destroy.restype = None
+    lib.tq_plan_info.argtypes = [vp, ctypes.POINTER(tq_plan_desc)]
+    lib.tq_plan_info.restype = i32
+    lib.tq_encode.argtypes = [vp, vp, i32, i64, i64, vp, vp]
+    lib.tq_encode.restype = i32
+    lib.tq_score.argtypes = [vp, vp, i32, i64, i64, i64, vp, i64, vp, vp]
+    lib.tq_score.restype = i32
+    lib.tq_topk.argtypes = [vp, i64, i64, i32, vp, vp, vp]
+    lib.tq_topk.restype = i32
+    lib.tq_qjl.argtypes = [vp, i32, vp, i64, vp, vp]
+    lib.tq_qjl.restype = i32
+    lib.tq_codebook.argtypes = [i32, i32, vp, vp]
+    lib.tq_codebook.restype = i32
+    lib.tq_rotation_signs.argtypes = [u64, i32, i32, vp]
+    lib.tq_rotation_signs.restype = i32
+    lib.tq_qjl_matrix.argtypes = [u64, i32, i32, i32, vp]
+    lib.tq_qjl_matrix.restype = i32
+    _lib = lib
+    return lib
+
+
+def _status_string(status):
+    try:
+        return load_library().tq_status_string(status).decode()
+    except Exception:
+        return "status"
+
+
+def _check(fn, status):
+    if status != TQ_OK:
+        raise TqError(fn, status)
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return TQ_BF16
+    if t.dtype == torch.float32:
+        return TQ_F32
+    raise TypeError("expected a bfloat16 or float32 tensor, got %s" % t.dtype)
+
+
+def _rows(t, d):
+    """(n, ld) of a tensor viewed as rows of d elements with unit inner stride."""
+    if t.shape[-1] != d or t.stride(-1) != 1:
+        raise ValueError("last dimension must be %d with unit stride" % d)
+    if t.dim() == 1:
+        return 1, d
+    if t.dim() == 2:
+        return t.shape[0], t.stride(0)
+    if not t.is_contiguous():
+        raise ValueError("tensors of rank > 2 must be contiguous")
+    return t.numel() // d, d
+
+
+class Plan:
+    """A plan handle (owns the library plan; destroyed with the object)."""
+
+    def __init__(self, handle, desc):
+        self._h = handle
+        self.desc = desc
+        self.d = desc["d"]
+        self.record_bytes = desc["record_bytes"]
+
+    @property
+    def handle(self):
+        if self._h is None:
+            raise ValueError("plan destroyed")
+        return self._h
+
+    def __del__(self):
+        try:
+            tq_plan_destroy(self)
+        except Exception:
+            pass
+
+
+def tq_plan_create(d, bits, seed, outlier_mask=None, outlier_bits=0):
+    lib = load_library()
+    h = ctypes.c_void_p()
+    mask_buf = None
+    if outlier_mask is not None:
+        mask_buf = np.ascontiguousarray(np.asarray(outlier_mask).astype(np.uint8))
+        if mask_buf.shape != (d,):
+            raise ValueError("outlier_mask must have d entries")
+    _check("tq_plan_create", lib.tq_plan_create(
+        int(d), int(bits), ctypes.c_uint64(int(seed)),
+        None if mask_buf is None else mask_buf.ctypes.data_as(ctypes.c_void_p),
+        int(outlier_bits), ctypes.byref(h)))
+    desc = tq_plan_desc()
+    _check("tq_plan_info", lib.tq_plan_info(h, ctypes.byref(desc)))
+    info = {"d": desc.d, "n_subplans": desc.n_subplans, "record_bytes": desc.record_bytes,
+            "sub": [{f: getattr(desc.sub[i], f) for f, _ in tq_subplan_desc._fields_}
+                    for i in range(desc.n_subplans)]}
+    return Plan(h, info)
+
+
+def tq_plan_destroy(plan):
+    if plan is not None and plan._h is not None:
+        load_library().tq_plan_destroy(plan._h)
+        plan._h = None
+
+
+def tq_plan_info(plan):
+    return plan.desc
+
+
+def tq_encode(plan, x, codes=None, stream=None):
+    """Encode the rows of x (cuda bf16/f32, last dim d) into codes (uint8 [n, record_bytes])."""
+    import torch
+    n, ld = _rows(x, plan.d)
+    if codes is None:
+        codes = torch.empty((n, plan.record_bytes), dtype=torch.uint8, device=x.device)
+    _check("tq_encode", load_library().tq_encode(
+        plan.handle, ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ld,
+        ctypes.c_void_p(codes.data_ptr()), _stream(stream)))
+    return codes
+
+
+def tq_score(plan, q, codes, n, nq_per_group=None, n_groups=1, scores=None, stream=None):
+    """Scores [n_groups*nq_per_group, n] of query rows q against grouped codes."""
+    import torch
+    nq, ld = _rows(q, plan.d)
+    if nq_per_group is None:
+        nq_per_group = nq // n_groups
+    if nq_per_group * n_groups != nq:
+        raise ValueError("query rows != nq_per_group * n_groups")
+    if codes.numel() < n_groups * n * plan.record_bytes:
+        raise ValueError("codes buffer too small")
+    if scores is None:
+        scores = torch.empty((nq, n), dtype=torch.float32, device=q.device)
+    _check("tq_score", load_library().tq_score(
+        plan.handle, ctypes.c_void_p(q.data_ptr()), _dtype_code(q), nq_per_group, n_groups, ld,
+        ctypes.c_void_p(codes.data_ptr()), n, ctypes.c_void_p(scores.data_ptr()), _stream(stream)))
+    return scores
+
+
+def tq_topk(scores, k, ids=None, vals=None, stream=None):
+    import torch
+    if scores.dtype != torch.float32 or not scores.is_contiguous():
+        raise ValueError("scores must be contiguous float32")
+    n = scores.shape[-1]
+    nq = scores.numel() // n if n else 0
+    if ids is None:
+        ids = torch.empty((nq, k), dtype=torch.int64, device=scores.device)
+    if vals is None:
+        vals = torch.empty((nq, k), dtype=torch.float32, device=scores.device)
+    _check("tq_topk", load_library().tq_topk(
+        ctypes.c_void_p(scores.data_ptr()), nq, n, int(k), ctypes.c_void_p(ids.data_ptr()),
+        ctypes.c_void_p(vals.data_ptr()), _stream(stream)))
+    return ids, vals
+
+
+def tq_qjl(plan, subplan, r, beta=None, stream=None):
+    import torch
+    D = plan.desc["sub"][subplan]["D"]
+    if r.dtype != torch.float32 or not r.is_contiguous() or r.shape[-1] != D:
+        raise ValueError("r must be contiguous float32 [n, D]")
+    n = r.numel() // D
+    if beta is None:
+        beta = torch.empty((n, D // 32), dtype=torch.int32, device=r.device)
+    _check("tq_qjl", load_library().tq_qjl(
+        plan.handle, int(subplan), ctypes.c_void_p(r.data_ptr()), n,
+        ctypes.c_void_p(beta.data_ptr()), _stream(stream)))
+    return beta
+
+
+def tq_codebook(D, R):
+    lv = np.zeros(2 ** R)
+    th = np.zeros(2 ** R - 1)
+    _check("tq_codebook", load_library().tq_codebook(
+        int(D), int(R), lv.ctypes.data_as(ctypes.c_void_p), th.ctypes.data_as(ctypes.c_void_p)))
+    return lv, th
+
+
+def tq_rotation_signs(seed, subset, D):
+    out = np.zeros((3, D), dtype=np.int8)
+    _check("tq_rotation_signs", load_library().tq_rotation_signs(
+        ctypes.c_uint64(int(seed)), int(subset), int(D), out.ctypes.data_as(ctypes.c_void_p)))
+    return out
+
+
+def tq_qjl_matrix(seed, subset, k, D):
+    out = np.zeros((k, D), dtype=np.uint16)
+    _check("tq_qjl_matrix", load_library().tq_qjl_matrix(
+        ctypes.c_uint64(int(seed)), int(subset), int(k), int(D), out.ctypes.data_as(ctypes.c_void_p)))
+    return out

@@ -1,0 +1,973 @@
+// HIP kernels for gfx950 (CDNA4, wave64): encode (norm split, randomized Hadamard rotation,
+// Lloyd-Max bucketize, bit-plane packing, QJL signs on bf16 MFMA), query preparation,
+// scoring (bit-sliced fp8 x fp4 MFMA for D <= 128, a vector-unit scorer otherwise) and
+// top-k.  The method is the one of the TurboQuant technical overview (intelliparadigm.com)
+// and the TurboQuant deep dive (blog.hotdry.top); section references are given per kernel.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;   // 4 waves per workgroup
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float flip_sign(float v, uint32_t bit) {
+  return __uint_as_float(__float_as_uint(v) ^ (bit << 31));
+}
+
+// ============================================================================ encode
+// Norm split, rotation z = Pi x / ||x|| with Pi = Ht S3 Ht S2 Ht S1 (TurboQuant technical
+// overview §2.1.1-2.1.2; diagonal then transform, three rounds), Lloyd-Max bucketize
+// idx = #{t_j <= z} (§1.2.2), residual r = z - c[idx] and its norm (§2.3.1), QJL signs
+// beta = [S r >= 0] (§2.3.2) computed on bf16 MFMA with r split into two bf16 limbs.
+//
+// Layout inside a workgroup: a vector of length D is held by TPV = D/EPT lanes, each lane
+// owning EPT consecutive coordinates, so the Walsh-Hadamard butterflies over the low
+// log2(EPT) index bits stay in registers and the rest are lane exchanges.
+
+template <int D> struct EncCfg {
+  static constexpr int EPT = (D >= 2048) ? 32 : 16;      // coordinates per lane
+  static constexpr int TPV = D / EPT;                      // lanes per vector
+  static constexpr int VPP = kWave / TPV;                  // vectors per wave pass
+  static constexpr int V = (D <= 32) ? 128 : (D <= 512) ? 64 : (D == 1024 ? 32 : 16);  // per tile
+  static constexpr int RSTRIDE = D + 8;                    // bf16 row stride of residual limbs
+};
+
+// In-register + cross-lane fast Walsh-Hadamard transform (unnormalized) of one vector.
+template <int EPT, int TPV>
+__device__ __forceinline__ void fwht_lanes(float (&v)[EPT], int t) {
+#pragma unroll
+  for (int h = 1; h < EPT; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < EPT; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < TPV; m <<= 1) {
+    const float sgn = (t & m) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const float p = __shfl_xor(v[e], m);
+      v[e] = fmaf(sgn, v[e], p);   // lower lane: v + p ; upper lane: p - v
+    }
+  }
+}
+
+template <int TPV>
+__device__ __forceinline__ float lane_group_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < TPV; m <<= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+// QJL sign stage for V vectors whose residual limbs are in LDS.  Writes each 32-row word of
+// signs to words[v * vstride + g * gstride + goff] (LDS).
+template <int D, int V>
+__device__ __forceinline__ void qjl_signs_mfma(const SubDev& s, const uint16_t* rhi,
+                                               const uint16_t* rlo, uint32_t* words, int vstride,
+                                               int gstride, int goff) {
+  constexpr int RS = D + 8;
+  constexpr int NG = D / 32;
+  constexpr int NT = (V / 16) * NG;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  for (int task = wave; task < NT; task += kBlock / kWave) {
+    const int vt = task / NG, g = task % NG;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* ah = rhi + (vt * 16 + col) * RS + 8 * grp;
+    const uint16_t* al = rlo + (vt * 16 + col) * RS + 8 * grp;
+    const uint16_t* b0p = s.S + (size_t)(32 * g + col) * D + 8 * grp;
+    const uint16_t* b1p = b0p + (size_t)16 * D;
+#pragma unroll 2
+    for (int i0 = 0; i0 < D; i0 += 32) {
+      const bf16x8 a_hi = *reinterpret_cast<const bf16x8*>(ah + i0);
+      const bf16x8 a_lo = *reinterpret_cast<const bf16x8*>(al + i0);
+      const bf16x8 b0 = *reinterpret_cast<const bf16x8*>(b0p + i0);
+      const bf16x8 b1 = *reinterpret_cast<const bf16x8*>(b1p + i0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_hi, b1, acc1, 0, 0, 0);
+      acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_lo, b1, acc1, 0, 0, 0);
+    }
+    // acc_T[e] at lane l: P[vector 4*(l/16)+e][row 32g + 16T + l%16]
+    const uint64_t b00 = __ballot(acc0[0] >= 0.f), b01 = __ballot(acc0[1] >= 0.f);
+    const uint64_t b02 = __ballot(acc0[2] >= 0.f), b03 = __ballot(acc0[3] >= 0.f);
+    const uint64_t b10 = __ballot(acc1[0] >= 0.f), b11 = __ballot(acc1[1] >= 0.f);
+    const uint64_t b12 = __ballot(acc1[2] >= 0.f), b13 = __ballot(acc1[3] >= 0.f);
+    if (lane < 16) {
+      const int v = lane, q = v >> 2, e = v & 3;
+      const uint64_t b0 = e == 0 ? b00 : e == 1 ? b01 : e == 2 ? b02 : b03;
+      const uint64_t b1 = e == 0 ? b10 : e == 1 ? b11 : e == 2 ? b12 : b13;
+      const uint32_t lo = (uint32_t)(b0 >> (16 * q)) & 0xFFFFu;
+      const uint32_t hi = (uint32_t)(b1 >> (16 * q)) & 0xFFFFu;
+      words[(vt * 16 + v) * vstride + g * gstride + goff] = lo | (hi << 16);
+    }
+  }
+}
+
+struct EncodeArgs {
+  SubDev s;
+  const void* x;
+  int64_t n;
+  int64_t ldx;
+  uint8_t* codes;
+  int rec_bytes;
+  int is_bf16;
+  int vec_load;   // rows 16-byte aligned and no channel gather: vector loads
+};
+
+template <int D>
+__global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
+  using C = EncCfg<D>;
+  constexpr int EPT = C::EPT, TPV = C::TPV, VPP = C::VPP, V = C::V, RS = C::RSTRIDE;
+  const SubDev& s = a.s;
+  const int R = s.R;
+  const int recw = s.rec_sub / 4;   // words per sub-record
+  __shared__ __attribute__((aligned(16))) uint16_t rhi[V * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t rlo[V * RS];
+  __shared__ __attribute__((aligned(16))) uint32_t rec[V * ((4 * (kMaxR + 1) * D / 32 + 8) / 4)];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = lane % TPV;                 // lane within its vector
+  const int c0 = t * EPT;                   // first coordinate owned by this lane
+  const int64_t tile0 = (int64_t)blockIdx.x * V;
+
+  // sign bits of this lane's coordinates for the three rounds
+  uint32_t sw[3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r) sw[r] = s.signs[r * (D / 32) + c0 / 32] >> (c0 % 32);
+
+  constexpr int PASSES = V / (4 * VPP);
+#pragma unroll 1
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int vl = wave * (V / 4) + pass * VPP + lane / TPV;   // vector within the tile
+    const int64_t row = tile0 + vl;
+    const bool live = row < a.n;
+    float v[EPT];
+    // ---- load (zero padding beyond d) ----
+    if (live && a.vec_load && c0 + EPT <= s.d) {
+      if (a.is_bf16) {
+        const uint4* p = reinterpret_cast<const uint4*>(
+            reinterpret_cast<const uint16_t*>(a.x) + row * a.ldx + c0);
+#pragma unroll
+        for (int q = 0; q < EPT / 8; ++q) {
+          const uint4 u = p[q];
+          const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            v[8 * q + 2 * h] = __uint_as_float(w[h] << 16);
+            v[8 * q + 2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
+          }
+        }
+      } else {
+        const float4* p = reinterpret_cast<const float4*>(
+            reinterpret_cast<const float*>(a.x) + row * a.ldx + c0);
+#pragma unroll
+        for (int q = 0; q < EPT / 4; ++q) {
+          const float4 u = p[q];
+          v[4 * q] = u.x; v[4 * q + 1] = u.y; v[4 * q + 2] = u.z; v[4 * q + 3] = u.w;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int i = c0 + e;
+        float val = 0.f;
+        if (live && i < s.d) {
+          const int64_t ch = s.chan ? s.chan[i] : i;
+          if (a.is_bf16)
+            val = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.x)[row * a.ldx + ch]);
+          else
+            val = reinterpret_cast<const float*>(a.x)[row * a.ldx + ch];
+        }
+        v[e] = val;
+      }
+    }
+    // ---- norm ----
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) ss = fmaf(v[e], v[e], ss);
+    ss = lane_group_sum<TPV>(ss);
+    const float nrm = sqrtf(ss);
+    // ---- rotation: three rounds of (+-1 diagonal, Walsh-Hadamard) ----
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) v[e] = flip_sign(v[e], (sw[r] >> e) & 1u);
+      fwht_lanes<EPT, TPV>(v, t);
+    }
+    const float scale = nrm > 0.f ? s.inv_scale / nrm : 0.f;
+    // ---- bucketize, residual ----
+    uint32_t planes[kMaxR];
+#pragma unroll
+    for (int m = 0; m < kMaxR; ++m) planes[m] = 0;
+    float gg = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      const float z = v[e] * scale;
+      int idx = 0;
+      float lv = s.lev[0];
+      for (int j = 0; j < (1 << R) - 1; ++j) {
+        const bool ge = z >= s.thr[j];
+        idx += ge ? 1 : 0;
+        lv = ge ? s.lev[j + 1] : lv;
+      }
+      const float rr = z - lv;
+      gg = fmaf(rr, rr, gg);
+      v[e] = rr;
+#pragma unroll
+      for (int m = 0; m < kMaxR; ++m) planes[m] |= (uint32_t)((idx >> m) & 1) << e;
+    }
+    gg = lane_group_sum<TPV>(gg);
+    // ---- residual limbs to LDS ----
+    {
+      uint32_t hi[EPT / 2], lo[EPT / 2];
+#pragma unroll
+      for (int e = 0; e < EPT; e += 2) {
+        const uint32_t h0 = f32_to_bf16_rne(v[e]), h1 = f32_to_bf16_rne(v[e + 1]);
+        const uint32_t l0 = f32_to_bf16_rne(v[e] - bf16_bits_to_f32(h0));
+        const uint32_t l1 = f32_to_bf16_rne(v[e + 1] - bf16_bits_to_f32(h1));
+        hi[e / 2] = h0 | (h1 << 16);
+        lo[e / 2] = l0 | (l1 << 16);
+      }
+      uint4* ph = reinterpret_cast<uint4*>(rhi + vl * RS + c0);
+      uint4* pl = reinterpret_cast<uint4*>(rlo + vl * RS + c0);
+#pragma unroll
+      for (int q = 0; q < EPT / 8; ++q) {
+        ph[q] = make_uint4(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
+        pl[q] = make_uint4(lo[4 * q], lo[4 * q + 1], lo[4 * q + 2], lo[4 * q + 3]);
+      }
+    }
+    // ---- index bit-planes, norm and gamma into the staged record ----
+    uint32_t* myrec = rec + vl * recw;
+    if (EPT == 32) {
+      for (int m = 0; m < R; ++m) myrec[(c0 / 32) * (R + 1) + m] = planes[m];
+    } else {
+#pragma unroll
+      for (int m = 0; m < kMaxR; ++m) {
+        const uint32_t other = __shfl_xor(planes[m], 1);
+        if (m < R && (t & 1) == 0) myrec[(c0 / 32) * (R + 1) + m] = planes[m] | (other << 16);
+      }
+    }
+    if (t == 0) {
+      myrec[(D / 32) * (R + 1)] = __float_as_uint(nrm);
+      myrec[(D / 32) * (R + 1) + 1] = __float_as_uint(sqrtf(gg));
+    }
+  }
+  __syncthreads();
+  qjl_signs_mfma<D, V>(s, rhi, rlo, rec, recw, R + 1, R);
+  __syncthreads();
+  // ---- write records ----
+  const int64_t nv = (a.n - tile0 < V) ? (a.n - tile0) : V;
+  if (s.rec_sub == a.rec_bytes) {
+    const int nw = (int)nv * recw;
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.codes + tile0 * a.rec_bytes);
+    if ((nw & 3) == 0) {
+      for (int i = threadIdx.x; i < nw / 4; i += kBlock)
+        reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(rec)[i];
+    } else {
+      for (int i = threadIdx.x; i < nw; i += kBlock) dst[i] = rec[i];
+    }
+  } else {
+    for (int i = threadIdx.x; i < (int)nv * recw; i += kBlock) {
+      const int vv = i / recw, w = i % recw;
+      reinterpret_cast<uint32_t*>(a.codes + (tile0 + vv) * a.rec_bytes + s.rec_off)[w] = rec[i];
+    }
+  }
+}
+
+// Standalone QJL stage: residuals already rotated, fp32 [n][D] -> sign words [n][D/32].
+template <int D>
+__global__ void __launch_bounds__(kBlock) qjl_kernel(SubDev s, const float* r, int64_t n,
+                                                     uint32_t* beta) {
+  using C = EncCfg<D>;
+  constexpr int V = C::V, RS = C::RSTRIDE;
+  __shared__ __attribute__((aligned(16))) uint16_t rhi[V * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t rlo[V * RS];
+  __shared__ uint32_t words[V * (D / 32)];
+  const int64_t tile0 = (int64_t)blockIdx.x * V;
+  for (int i = threadIdx.x; i < V * D; i += kBlock) {
+    const int vv = i / D, c = i % D;
+    const float x = (tile0 + vv < n) ? r[(tile0 + vv) * D + c] : 0.f;
+    const uint32_t h = f32_to_bf16_rne(x);
+    rhi[vv * RS + c] = (uint16_t)h;
+    rlo[vv * RS + c] = (uint16_t)f32_to_bf16_rne(x - bf16_bits_to_f32(h));
+  }
+  __syncthreads();
+  qjl_signs_mfma<D, V>(s, rhi, rlo, words, D / 32, 1, 0);
+  __syncthreads();
+  for (int i = threadIdx.x; i < V * (D / 32); i += kBlock) {
+    const int vv = i / (D / 32);
+    if (tile0 + vv < n) beta[tile0 * (D / 32) + i] = words[i];
+  }
+}
+
+// ============================================================================ queries
+// y' = Pi pad(y) (same rotation as the keys: technical overview §4.2.2; the query is kept in
+// full precision: deep dive §3), w = S y', and the sums used by the estimate.
+
+struct QPrepArgs {
+  SubDev s;
+  const void* q;
+  int64_t ldq;
+  int is_bf16;
+  float* yrot;    // [nq][D]
+  float* w;       // [nq][D]
+  float* sums;    // [nq][2]: sum y', sum w
+};
+
+__global__ void __launch_bounds__(kBlock) qprep_kernel(QPrepArgs a) {
+  const SubDev& s = a.s;
+  const int D = s.D;
+  const int64_t qi = blockIdx.x;
+  __shared__ float y[kMaxD];
+  __shared__ float red[2][kBlock / kWave];
+  for (int i = threadIdx.x; i < D; i += kBlock) {
+    float val = 0.f;
+    if (i < s.d) {
+      const int64_t ch = s.chan ? s.chan[i] : i;
+      val = a.is_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi * a.ldq + ch])
+                      : reinterpret_cast<const float*>(a.q)[qi * a.ldq + ch];
+    }
+    y[i] = val;
+  }
+  __syncthreads();
+  for (int r = 0; r < 3; ++r) {
+    for (int i = threadIdx.x; i < D; i += kBlock)
+      y[i] = flip_sign(y[i], (s.signs[r * (D / 32) + i / 32] >> (i % 32)) & 1u);
+    __syncthreads();
+    for (int h = 1; h < D; h <<= 1) {
+      for (int p = threadIdx.x; p < D / 2; p += kBlock) {
+        const int i = (p / h) * 2 * h + (p % h);
+        const float u = y[i], v = y[i + h];
+        y[i] = u + v;
+        y[i + h] = u - v;
+      }
+      __syncthreads();
+    }
+  }
+  float sy = 0.f;
+  for (int i = threadIdx.x; i < D; i += kBlock) {
+    const float v = y[i] * s.inv_scale;
+    y[i] = v;
+    a.yrot[qi * D + i] = v;
+    sy += v;
+  }
+  __syncthreads();
+  // w_j = sum_i S[j][i] y'_i : one wave per row j, lanes across i
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float sw = 0.f;
+  for (int j = wave; j < s.k; j += kBlock / kWave) {
+    const uint16_t* Sj = s.S + (size_t)j * D;
+    float acc = 0.f;
+    for (int i = lane; i < D; i += kWave) acc = fmaf(bf16_bits_to_f32(Sj[i]), y[i], acc);
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (lane == 0) { a.w[qi * D + j] = acc; sw += acc; }
+  }
+  for (int m = 32; m >= 1; m >>= 1) sy += __shfl_xor(sy, m);
+  if (lane == 0) { red[0][wave] = sy; red[1][wave] = sw; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t0 = 0.f, t1 = 0.f;
+    for (int i = 0; i < kBlock / kWave; ++i) { t0 += red[0][i]; t1 += red[1][i]; }
+    a.sums[qi * 2] = t0;
+    a.sums[qi * 2 + 1] = t1;
+  }
+}
+
+// fp8 e4m3 (bias 7, max 448, no infinities) encode with round-to-nearest-even, and decode.
+__device__ __forceinline__ uint32_t e4m3_encode(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
+  float a = fabsf(v);
+  if (a == 0.f) return sign;
+  if (a >= 448.f) return sign | 0x7Eu;
+  int ex;
+  frexpf(a, &ex);                  // a = m 2^ex, m in [0.5, 1)
+  int e = ex - 1;                  // a = 1.f * 2^e
+  if (e < -6) {                    // subnormal: multiples of 2^-9
+    const int q = (int)rintf(ldexpf(a, 9));
+    return sign | (uint32_t)q;     // q == 8 is the smallest normal, encoded the same way
+  }
+  int m = (int)rintf((ldexpf(a, -e) - 1.f) * 8.f);
+  if (m == 8) { m = 0; e += 1; }
+  if (e > 8) return sign | 0x7Eu;
+  return sign | (uint32_t)((e + 7) << 3) | (uint32_t)m;
+}
+
+__device__ __forceinline__ float e4m3_decode(uint32_t b) {
+  const float sgn = (b & 0x80u) ? -1.f : 1.f;
+  const int e = (b >> 3) & 15, m = b & 7;
+  const float mag = e == 0 ? ldexpf((float)m, -9) : ldexpf(1.f + m / 8.f, e - 7);
+  return sgn * mag;
+}
+
+// ----------------------------------------------------------------- bit-sliced scorer images
+// For a symmetric codebook the level of an R-bit index expands over the parity planes of odd
+// subsets of its bits: c[idx] = sum_S a_S (2 p_S - 1).  The MSE term of a key becomes
+// 2 sum_S a_S <y', p_S> - A0 sum y', and the QJL term 2 <w, beta> - sum w: binary dot
+// products.  Keys are fed to the MFMA as fp4 values 0 / 0.5 straight from their bits; the
+// query side is an fp8 image holding three limbs of a_S y' (or w) per query, so that the
+// four queries of a group and their three limbs fill the 16 rows of one MFMA tile.
+//
+// A-operand (fp8, 16 x 128) lane layout of v_mfma_scale_f32_16x16x128_f8f6f4 on gfx950:
+// row = lane % 16; element e of lane group G = lane / 16 is K = 16 G + e (e < 16) or
+// K = 64 + 16 G + (e - 16).  B-operand (fp4, 128 x 16): column = lane % 16, element e of
+// lane group G is K = 32 G + e.  A key plane word W of chunk G gives the B dwords
+// (W >> j) & 0x11111111, j = 0..3: nibble m of dword j is coordinate 32 G + 4 m + j at
+// K = 32 G + 8 j + m.
+
+__device__ __forceinline__ int bitslice_coord(int K) {
+  const int G = K >> 5, j = (K & 31) >> 3, m = K & 7;
+  return 32 * G + 4 * m + j;
+}
+
+struct QImageArgs {
+  SubDev s;
+  const float* yrot;   // [nq_total][D]
+  const float* w;
+  const float* sums;   // [nq_total][2]
+  int64_t nq_per_group;
+  int n_qtiles;        // ceil(nq_per_group / 4)
+  uint32_t* img;       // [groups*qtiles][n_planes+1][64 lanes][8 words]
+  float* ec;           // [groups*qtiles][4 queries][4]: c0, c1, c2, c3
+};
+
+// one wave per (group, query tile)
+__global__ void __launch_bounds__(kWave) qimage_kernel(QImageArgs a) {
+  const SubDev& s = a.s;
+  const int D = s.D;
+  const int gt = blockIdx.x;                    // group * n_qtiles + qtile
+  const int64_t grp = gt / a.n_qtiles, qt = gt % a.n_qtiles;
+  const int lane = threadIdx.x;
+  const int np = s.n_planes;
+  float cmax = 0.f;
+  for (int p = 0; p < np; ++p) cmax = fmaxf(cmax, fabsf(s.coef[p]));
+  // per-query scales: powers of two putting the largest image magnitude in (128, 256]
+  __shared__ float sc_mse[4], sc_qjl[4];
+  for (int q = 0; q < 4; ++q) {
+    const int64_t qq = qt * 4 + q;
+    float my = 0.f, mw = 0.f;
+    if (qq < a.nq_per_group) {
+      const int64_t qi = grp * a.nq_per_group + qq;
+      for (int i = lane; i < D; i += kWave) {
+        my = fmaxf(my, fabsf(a.yrot[qi * D + i]));
+        mw = fmaxf(mw, fabsf(a.w[qi * D + i]));
+      }
+    }
+    for (int m = 32; m >= 1; m >>= 1) {
+      my = fmaxf(my, __shfl_xor(my, m));
+      mw = fmaxf(mw, __shfl_xor(mw, m));
+    }
+    if (lane == 0) {
+      const float M1 = my * cmax, M2 = mw;
+      sc_mse[q] = M1 > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(M1))) : 1.f;
+      sc_qjl[q] = M2 > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(M2))) : 1.f;
+    }
+  }
+  __syncthreads();
+  const int row = lane & 15, Ga = lane >> 4;
+  const int q = row >> 2, limb = row & 3;
+  const int64_t qq = qt * 4 + q;
+  const bool valid = (qq < a.nq_per_group) && limb < 3;
+  const int64_t qi = grp * a.nq_per_group + qq;
+  for (int p = 0; p <= np; ++p) {
+    uint32_t words[8];
+    for (int wd = 0; wd < 8; ++wd) {
+      uint32_t word = 0;
+      for (int b = 0; b < 4; ++b) {
+        const int e = 4 * wd + b;
+        const int K = e < 16 ? 16 * Ga + e : 64 + 16 * Ga + (e - 16);
+        const int c = bitslice_coord(K);
+        uint32_t byte = 0;
+        if (valid && c < D) {
+          const float v = (p < np) ? s.coef[p] * a.yrot[qi * D + c] * sc_mse[q]
+                                   : a.w[qi * D + c] * sc_qjl[q];
+          float rem = v;
+          uint32_t code = 0;
+          for (int l = 0; l <= limb; ++l) {
+            code = e4m3_encode(rem);
+            rem -= e4m3_decode(code);
+          }
+          byte = code;
+        }
+        word |= byte << (8 * b);
+      }
+      words[wd] = word;
+    }
+    uint4* dst = reinterpret_cast<uint4*>(a.img + ((size_t)gt * (np + 1) + p) * 64 * 8 + lane * 8);
+    dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
+    dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+  }
+  if (lane < 4) {
+    const int64_t q2 = qt * 4 + lane;
+    float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
+    if (q2 < a.nq_per_group) {
+      const int64_t qi2 = grp * a.nq_per_group + q2;
+      const float K = sqrtf(0.5f * (float)M_PI) / (float)s.k;
+      c0 = -s.coef_sum * a.sums[qi2 * 2];
+      c1 = 4.f / sc_mse[lane];
+      c2 = -K * a.sums[qi2 * 2 + 1];
+      c3 = 4.f * K / sc_qjl[lane];
+    }
+    float* e = a.ec + ((size_t)gt * 4 + lane) * 4;
+    e[0] = c0; e[1] = c1; e[2] = c2; e[3] = c3;
+  }
+}
+
+// ============================================================================ scorers
+// est = n (<y', c[idx]> + gamma sqrt(pi/2)/k <w, 2 beta - 1>), summed over sub-plans
+// (technical overview §1.2.3 unbiased two-stage estimate, §4.2.2 per-coordinate centroid
+// lookup with the query under the same rotation).
+
+struct ScoreArgs {
+  PlanDev p;
+  const uint8_t* codes;
+  int64_t n;
+  int64_t nq_per_group;
+  int n_qtiles;
+  float* scores;
+  const uint32_t* img[2];
+  const float* ec[2];
+  const float* yrot[2];
+  const float* w[2];
+};
+
+template <int NP> struct PlaneImg { i32x8 a[NP + 1]; };
+
+__device__ __forceinline__ i32x8 fp4_operand(uint32_t W) {
+  i32x8 b;
+  b[0] = (int)(W & 0x11111111u);
+  b[1] = (int)((W >> 1) & 0x11111111u);
+  b[2] = (int)((W >> 2) & 0x11111111u);
+  b[3] = (int)((W >> 3) & 0x11111111u);
+  b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
+  return b;
+}
+
+// Contribution of one sub-plan (R index bits, D <= 128) to 16 keys; lane l handles key
+// column l % 16.  The MFMA reads the B registers of every lane, so all lanes must reach it
+// with defined operands: loads are branch-free from an always-valid record (`key_safe`)
+// and masked by selects.
+template <int R>
+__device__ __forceinline__ float bitslice_sub(const SubDev& s, const uint8_t* codes,
+                                              int rec_bytes, int64_t key_safe, bool key_ok,
+                                              const i32x8* A, const float* e4) {
+  constexpr int NP = 1 << (R - 1);
+  const int lane = threadIdx.x & 63, G = lane >> 4;
+  const bool chunk_ok = 32 * G < s.D;
+  const uint8_t* rec = codes + key_safe * rec_bytes + s.rec_off;
+  const uint32_t* pw = reinterpret_cast<const uint32_t*>(rec) + (chunk_ok ? G : 0) * (R + 1);
+  uint32_t wd[R + 1];
+#pragma unroll
+  for (int m = 0; m <= R; ++m) {
+    const uint32_t v = pw[m];
+    wd[m] = (key_ok && chunk_ok) ? v : 0u;
+  }
+  const uint32_t* tail = reinterpret_cast<const uint32_t*>(rec + (s.D / 32) * (R + 1) * 4);
+  const float nrm = key_ok ? __uint_as_float(tail[0]) : 0.f;
+  const float gam = key_ok ? __uint_as_float(tail[1]) : 0.f;
+  f32x4 am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    uint32_t P = 0;
+#pragma unroll
+    for (int m = 0; m < R; ++m)
+      if ((s.plane_mask[p] >> m) & 1) P ^= wd[m];
+    am = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[p], fp4_operand(P), am, 0, 4, 0, 127, 0, 127);
+  }
+  aq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[NP], fp4_operand(wd[R]), aq, 0, 4, 0, 127, 0, 127);
+  const float msum = am[0] + am[1] + am[2];
+  const float qsum = aq[0] + aq[1] + aq[2];
+  return nrm * (fmaf(e4[1], msum, e4[0]) + gam * fmaf(e4[3], qsum, e4[2]));
+}
+
+template <int R0, int R1>
+__global__ void __launch_bounds__(kBlock) score_bitslice_kernel(ScoreArgs a, int keys_per_block) {
+  constexpr int NP0 = 1 << (R0 - 1);
+  constexpr int NP1 = R1 > 0 ? (1 << (R1 - 1)) : 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gt = blockIdx.y;                           // group * n_qtiles + qtile
+  const int64_t grp = gt / a.n_qtiles, qt = gt % a.n_qtiles;
+  const int G = lane >> 4, col = lane & 15;
+  i32x8 A0[NP0 + 1];
+  i32x8 A1[NP1 + 1];
+  {
+    const uint32_t* base = a.img[0] + (size_t)gt * (NP0 + 1) * 64 * 8 + lane * 8;
+#pragma unroll
+    for (int p = 0; p <= NP0; ++p) {
+      const uint4 u0 = reinterpret_cast<const uint4*>(base + p * 64 * 8)[0];
+      const uint4 u1 = reinterpret_cast<const uint4*>(base + p * 64 * 8)[1];
+      A0[p][0] = u0.x; A0[p][1] = u0.y; A0[p][2] = u0.z; A0[p][3] = u0.w;
+      A0[p][4] = u1.x; A0[p][5] = u1.y; A0[p][6] = u1.z; A0[p][7] = u1.w;
+    }
+  }
+  if constexpr (R1 > 0) {
+    const uint32_t* base = a.img[1] + (size_t)gt * (NP1 + 1) * 64 * 8 + lane * 8;
+#pragma unroll
+    for (int p = 0; p <= NP1; ++p) {
+      const uint4 u0 = reinterpret_cast<const uint4*>(base + p * 64 * 8)[0];
+      const uint4 u1 = reinterpret_cast<const uint4*>(base + p * 64 * 8)[1];
+      A1[p][0] = u0.x; A1[p][1] = u0.y; A1[p][2] = u0.z; A1[p][3] = u0.w;
+      A1[p][4] = u1.x; A1[p][5] = u1.y; A1[p][6] = u1.z; A1[p][7] = u1.w;
+    }
+  }
+  float e0[4], e1[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) e0[i] = a.ec[0][((size_t)gt * 4 + G) * 4 + i];
+  if constexpr (R1 > 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) e1[i] = a.ec[1][((size_t)gt * 4 + G) * 4 + i];
+  }
+  const int64_t qq = qt * 4 + G;
+  const bool q_ok = qq < a.nq_per_group;
+  float* out = a.scores + (grp * a.nq_per_group + qq) * a.n;
+  const uint8_t* codes = a.codes + grp * a.n * (int64_t)a.p.rec_bytes;
+  const int64_t kb0 = (int64_t)blockIdx.x * keys_per_block;
+  const int64_t kend = (kb0 + keys_per_block < a.n) ? kb0 + keys_per_block : a.n;
+  for (int64_t k0 = kb0 + wave * 16; k0 < kend; k0 += 16 * (kBlock / kWave)) {
+    const int64_t key = k0 + col;
+    const bool key_ok = key < kend;
+    const int64_t key_safe = key_ok ? key : kend - 1;
+    float est = bitslice_sub<R0>(a.p.sub[0], codes, a.p.rec_bytes, key_safe, key_ok, A0, e0);
+    if constexpr (R1 > 0)
+      est += bitslice_sub<R1>(a.p.sub[1], codes, a.p.rec_bytes, key_safe, key_ok, A1, e1);
+    // Pin the value here, in the full-wave region: otherwise the MFMAs feeding it may be
+    // sunk into the masked store below and run with inactive lanes.
+    asm volatile("" : "+v"(est));
+    if (q_ok && key_ok) out[key] = est;
+  }
+}
+
+// Vector-unit scorer for any D: one key per thread, up to kQT queries of a group per block,
+// rotated query and its projection staged in LDS (2 kQT sum(D) floats <= 64 KiB).
+template <int kQT>
+__global__ void __launch_bounds__(kBlock) score_generic_kernel(ScoreArgs a) {
+  extern __shared__ float smem[];   // per sub-plan: y'[QT][D], w[QT][D]
+  const int gt = blockIdx.y;
+  const int64_t grp = gt / a.n_qtiles, qt = gt % a.n_qtiles;
+  const int64_t q0 = qt * kQT;
+  const int nq = (int)((a.nq_per_group - q0 < kQT) ? (a.nq_per_group - q0) : kQT);
+  int off = 0;
+  for (int sb = 0; sb < a.p.nsub; ++sb) {
+    const int D = a.p.sub[sb].D;
+    for (int i = threadIdx.x; i < kQT * D; i += kBlock) {
+      const int qq = i / D, c = i % D;
+      const int64_t qi = grp * a.nq_per_group + q0 + qq;
+      smem[off + i] = qq < nq ? a.yrot[sb][qi * D + c] : 0.f;
+      smem[off + kQT * D + i] = qq < nq ? a.w[sb][qi * D + c] : 0.f;
+    }
+    off += 2 * kQT * D;
+  }
+  __syncthreads();
+  const int64_t key = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (key >= a.n) return;
+  const uint8_t* rec0 = a.codes + (grp * a.n + key) * (int64_t)a.p.rec_bytes;
+  float est[kQT];
+#pragma unroll
+  for (int q = 0; q < kQT; ++q) est[q] = 0.f;
+  off = 0;
+  for (int sb = 0; sb < a.p.nsub; ++sb) {
+    const SubDev& s = a.p.sub[sb];
+    const int D = s.D, R = s.R;
+    const uint32_t* rec = reinterpret_cast<const uint32_t*>(rec0 + s.rec_off);
+    const float* ys = smem + off;
+    const float* ws = smem + off + kQT * D;
+    float am[kQT], aq[kQT];
+#pragma unroll
+    for (int q = 0; q < kQT; ++q) { am[q] = 0.f; aq[q] = 0.f; }
+    for (int g = 0; g < D / 32; ++g) {
+      uint32_t wd[kMaxR + 1];
+      for (int m = 0; m <= R; ++m) wd[m] = rec[g * (R + 1) + m];
+      for (int t = 0; t < 32; ++t) {
+        int idx = 0;
+        for (int m = 0; m < R; ++m) idx |= ((wd[m] >> t) & 1) << m;
+        const float lv = s.lev[idx];
+        const float sg = ((wd[R] >> t) & 1) ? 1.f : -1.f;
+        const int i = 32 * g + t;
+#pragma unroll
+        for (int q = 0; q < kQT; ++q) {
+          am[q] = fmaf(ys[q * D + i], lv, am[q]);
+          aq[q] = fmaf(ws[q * D + i], sg, aq[q]);
+        }
+      }
+    }
+    const float nrm = __uint_as_float(rec[(D / 32) * (R + 1)]);
+    const float gam = __uint_as_float(rec[(D / 32) * (R + 1) + 1]);
+    const float K = sqrtf(0.5f * (float)M_PI) / (float)s.k;
+#pragma unroll
+    for (int q = 0; q < kQT; ++q) est[q] += nrm * (am[q] + gam * K * aq[q]);
+    off += 2 * kQT * D;
+  }
+  for (int q = 0; q < nq; ++q) a.scores[(grp * a.nq_per_group + q0 + q) * a.n + key] = est[q];
+}
+
+// ============================================================================ top-k
+// Per row, the k largest scores ordered by (-score, index): the quantized first stage of
+// two-stage retrieval (technical overview §4.2.2).  Each lane keeps a sorted list of its
+// KMAX best; lists are merged by k rounds of wave- and block-wide arg-max.
+
+__device__ __forceinline__ bool better(float v, int i, float w, int j) {
+  return v > w || (v == w && i < j);
+}
+
+template <int KMAX>
+__global__ void __launch_bounds__(kBlock) topk_kernel(const float* scores, int64_t n, int k,
+                                                      int64_t* ids, float* vals) {
+  const int64_t row = blockIdx.x;
+  const float* x = scores + row * n;
+  float lv[KMAX];
+  int li[KMAX];
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) { lv[s] = -INFINITY; li[s] = 0x7FFFFFFF; }
+  float thr = -INFINITY;
+  int thr_i = 0x7FFFFFFF;
+  for (int64_t j = threadIdx.x; j < n; j += kBlock) {
+    float cv = x[j];
+    int ci = (int)j;
+    if (better(cv, ci, thr, thr_i)) {
+#pragma unroll
+      for (int s = 0; s < KMAX; ++s) {
+        const bool sw = better(cv, ci, lv[s], li[s]);
+        const float tv = lv[s];
+        const int ti = li[s];
+        lv[s] = sw ? cv : tv;
+        li[s] = sw ? ci : ti;
+        cv = sw ? tv : cv;
+        ci = sw ? ti : ci;
+      }
+#pragma unroll
+      for (int s = 0; s < KMAX; ++s)
+        if (s == k - 1) { thr = lv[s]; thr_i = li[s]; }
+    }
+  }
+  __shared__ float wv[kBlock / kWave];
+  __shared__ int wi[kBlock / kWave];
+  __shared__ int winner;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = 0; r < k; ++r) {
+    float bv = lv[0];
+    int bi = li[0];
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(bv, m);
+      const int oi = __shfl_xor(bi, m);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == 0) { wv[wave] = bv; wi[wave] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float v = wv[0];
+      int i = wi[0];
+      for (int w = 1; w < kBlock / kWave; ++w)
+        if (better(wv[w], wi[w], v, i)) { v = wv[w]; i = wi[w]; }
+      winner = i;
+      ids[row * k + r] = i;
+      vals[row * k + r] = v;
+    }
+    __syncthreads();
+    if (li[0] == winner) {
+#pragma unroll
+      for (int s = 0; s + 1 < KMAX; ++s) { lv[s] = lv[s + 1]; li[s] = li[s + 1]; }
+      lv[KMAX - 1] = -INFINITY;
+      li[KMAX - 1] = 0x7FFFFFFF;
+    }
+  }
+}
+
+// ============================================================================ launchers
+
+static inline int hip_rc(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
+
+template <int D>
+static int launch_encode_d(const EncodeArgs& ea, hipStream_t st) {
+  const int64_t tiles = (ea.n + EncCfg<D>::V - 1) / EncCfg<D>::V;
+  hipLaunchKernelGGL(encode_kernel<D>, dim3((unsigned)tiles), dim3(kBlock), 0, st, ea);
+  return hip_rc(hipGetLastError());
+}
+
+int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, int64_t ldx,
+                  uint8_t* codes, void* stream) {
+  if (n == 0) return 0;
+  EncodeArgs ea;
+  ea.s = p.sub[sub];
+  ea.x = x;
+  ea.n = n;
+  ea.ldx = ldx;
+  ea.codes = codes;
+  ea.rec_bytes = p.rec_bytes;
+  ea.is_bf16 = dt == TQ_BF16;
+  const int es = ea.is_bf16 ? 2 : 4;
+  ea.vec_load = (ea.s.chan == nullptr) && ((uintptr_t)x % 16 == 0) && ((ldx * es) % 16 == 0);
+  hipStream_t st = (hipStream_t)stream;
+  switch (ea.s.D) {
+    case 32: return launch_encode_d<32>(ea, st);
+    case 64: return launch_encode_d<64>(ea, st);
+    case 128: return launch_encode_d<128>(ea, st);
+    case 256: return launch_encode_d<256>(ea, st);
+    case 512: return launch_encode_d<512>(ea, st);
+    case 1024: return launch_encode_d<1024>(ea, st);
+    case 2048: return launch_encode_d<2048>(ea, st);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+template <int D>
+static int launch_qjl_d(const SubDev& s, const float* r, int64_t n, uint32_t* beta, hipStream_t st) {
+  const int64_t tiles = (n + EncCfg<D>::V - 1) / EncCfg<D>::V;
+  hipLaunchKernelGGL(qjl_kernel<D>, dim3((unsigned)tiles), dim3(kBlock), 0, st, s, r, n, beta);
+  return hip_rc(hipGetLastError());
+}
+
+int launch_qjl(const SubDev& s, const float* r, int64_t n, uint32_t* beta, void* stream) {
+  if (n == 0) return 0;
+  hipStream_t st = (hipStream_t)stream;
+  switch (s.D) {
+    case 32: return launch_qjl_d<32>(s, r, n, beta, st);
+    case 64: return launch_qjl_d<64>(s, r, n, beta, st);
+    case 128: return launch_qjl_d<128>(s, r, n, beta, st);
+    case 256: return launch_qjl_d<256>(s, r, n, beta, st);
+    case 512: return launch_qjl_d<512>(s, r, n, beta, st);
+    case 1024: return launch_qjl_d<1024>(s, r, n, beta, st);
+    case 2048: return launch_qjl_d<2048>(s, r, n, beta, st);
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+template <int R0, int R1>
+static void launch_bitslice(const ScoreArgs& sa, int64_t n_gt, hipStream_t st) {
+  const int kpb = 1024;
+  const int64_t kblocks = (sa.n + kpb - 1) / kpb;
+  hipLaunchKernelGGL((score_bitslice_kernel<R0, R1>), dim3((unsigned)kblocks, (unsigned)n_gt),
+                     dim3(kBlock), 0, st, sa, kpb);
+}
+
+static bool dispatch_bitslice(const ScoreArgs& sa, int64_t n_gt, hipStream_t st) {
+  const int r0 = sa.p.sub[0].R, r1 = sa.p.nsub > 1 ? sa.p.sub[1].R : 0;
+#define TQ_BS(A, B) if (r0 == A && r1 == B) { launch_bitslice<A, B>(sa, n_gt, st); return true; }
+  TQ_BS(1, 0) TQ_BS(2, 0) TQ_BS(3, 0) TQ_BS(4, 0)
+  TQ_BS(1, 1) TQ_BS(1, 2) TQ_BS(1, 3) TQ_BS(1, 4)
+  TQ_BS(2, 1) TQ_BS(2, 2) TQ_BS(2, 3) TQ_BS(2, 4)
+  TQ_BS(3, 1) TQ_BS(3, 2) TQ_BS(3, 3) TQ_BS(3, 4)
+  TQ_BS(4, 1) TQ_BS(4, 2) TQ_BS(4, 3) TQ_BS(4, 4)
+#undef TQ_BS
+  return false;
+}
+
+int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, int64_t n_groups,
+                 int64_t ldq, const uint8_t* codes, int64_t n, float* scores, void* stream) {
+  if (n == 0 || nq_per_group == 0 || n_groups == 0) return 0;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t nq = nq_per_group * n_groups;
+  bool small = true;
+  for (int sb = 0; sb < p.nsub; ++sb) small = small && p.sub[sb].D <= 128;
+  const int qt_bs = (int)((nq_per_group + 3) / 4);
+  // workspace: per sub-plan y', w, sums, images, epilogue constants
+  size_t bytes = 0;
+  size_t off_y[2], off_w[2], off_s[2], off_img[2], off_ec[2];
+  auto take = [&](size_t b) { size_t o = bytes; bytes += (b + 255) / 256 * 256; return o; };
+  for (int sb = 0; sb < p.nsub; ++sb) {
+    const size_t D = p.sub[sb].D;
+    off_y[sb] = take(nq * D * 4);
+    off_w[sb] = take(nq * D * 4);
+    off_s[sb] = take(nq * 2 * 4);
+    if (small) {
+      off_img[sb] = take((size_t)n_groups * qt_bs * (p.sub[sb].n_planes + 1) * 64 * 32);
+      off_ec[sb] = take((size_t)n_groups * qt_bs * 16 * 4);
+    }
+  }
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, bytes, st);
+  if (e != hipSuccess) return (int)e;
+  uint8_t* wb = static_cast<uint8_t*>(ws);
+  ScoreArgs sa;
+  sa.p = p;
+  sa.codes = codes;
+  sa.n = n;
+  sa.nq_per_group = nq_per_group;
+  sa.scores = scores;
+  for (int sb = 0; sb < 2; ++sb) { sa.img[sb] = nullptr; sa.ec[sb] = nullptr; sa.yrot[sb] = nullptr; sa.w[sb] = nullptr; }
+  for (int sb = 0; sb < p.nsub; ++sb) {
+    QPrepArgs qa;
+    qa.s = p.sub[sb];
+    qa.q = q;
+    qa.ldq = ldq;
+    qa.is_bf16 = dt == TQ_BF16;
+    qa.yrot = reinterpret_cast<float*>(wb + off_y[sb]);
+    qa.w = reinterpret_cast<float*>(wb + off_w[sb]);
+    qa.sums = reinterpret_cast<float*>(wb + off_s[sb]);
+    hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)nq), dim3(kBlock), 0, st, qa);
+    sa.yrot[sb] = qa.yrot;
+    sa.w[sb] = qa.w;
+    if (small) {
+      QImageArgs ia;
+      ia.s = p.sub[sb];
+      ia.yrot = qa.yrot;
+      ia.w = qa.w;
+      ia.sums = qa.sums;
+      ia.nq_per_group = nq_per_group;
+      ia.n_qtiles = qt_bs;
+      ia.img = reinterpret_cast<uint32_t*>(wb + off_img[sb]);
+      ia.ec = reinterpret_cast<float*>(wb + off_ec[sb]);
+      hipLaunchKernelGGL(qimage_kernel, dim3((unsigned)(n_groups * qt_bs)), dim3(kWave), 0, st, ia);
+      sa.img[sb] = ia.img;
+      sa.ec[sb] = ia.ec;
+    }
+  }
+  int rc = 0;
+  if (small) {
+    sa.n_qtiles = qt_bs;
+    if (!dispatch_bitslice(sa, n_groups * qt_bs, st)) rc = (int)hipErrorInvalidValue;
+  } else {
+    int sumD = 0;
+    for (int sb = 0; sb < p.nsub; ++sb) sumD += p.sub[sb].D;
+    const int qt = (2 * 8 * sumD * 4 <= 65536) ? 8 : (2 * 4 * sumD * 4 <= 65536 ? 4 : 2);
+    sa.n_qtiles = (int)((nq_per_group + qt - 1) / qt);
+    const size_t lds = 2 * (size_t)qt * sumD * 4;
+    const int64_t kblocks = (n + kBlock - 1) / kBlock;
+    const dim3 grid((unsigned)kblocks, (unsigned)(n_groups * sa.n_qtiles));
+    if (qt == 8)
+      hipLaunchKernelGGL(score_generic_kernel<8>, grid, dim3(kBlock), lds, st, sa);
+    else if (qt == 4)
+      hipLaunchKernelGGL(score_generic_kernel<4>, grid, dim3(kBlock), lds, st, sa);
+    else
+      hipLaunchKernelGGL(score_generic_kernel<2>, grid, dim3(kBlock), lds, st, sa);
+  }
+  if (!rc) rc = hip_rc(hipGetLastError());
+  e = hipFreeAsync(ws, st);
+  if (!rc && e != hipSuccess) rc = (int)e;
+  return rc;
+}
+
+int launch_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids, float* vals,
+                void* stream) {
+  if (nq == 0) return 0;
+  hipStream_t st = (hipStream_t)stream;
+  if (k <= 16)
+    hipLaunchKernelGGL(topk_kernel<16>, dim3((unsigned)nq), dim3(kBlock), 0, st, scores, n, k, ids, vals);
+  else
+    hipLaunchKernelGGL(topk_kernel<64>, dim3((unsigned)nq), dim3(kBlock), 0, st, scores, n, k, ids, vals);
+  return hip_rc(hipGetLastError());
+}
+
+}  // namespace tq

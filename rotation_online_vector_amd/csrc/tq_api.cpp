@@ -1,0 +1,306 @@
+// C ABI of libtq: argument validation, plan construction (host tables + one device
+// allocation), and dispatch to the kernel launchers.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "tq_internal.h"
+
+using namespace tq;
+
+namespace {
+
+int padded_length(int d) {
+  int D = kMinD;
+  while (D < d) D *= 2;
+  return D;
+}
+
+int record_bytes_of(int D, int R) { return 4 * (R + 1) * (D / 32) + 8; }
+
+bool current_device(int* dev) {
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess || count < 1) return false;
+  return hipGetDevice(dev) == hipSuccess;
+}
+
+bool plan_device_ok(const tq_plan* p) {
+  int dev = -1;
+  return hipGetDevice(&dev) == hipSuccess && dev == p->device;
+}
+
+tq_status from_hip(int rc) {
+  if (rc == 0) return TQ_OK;
+  if (rc == (int)hipErrorOutOfMemory || rc == (int)hipErrorMemoryAllocation) return TQ_ENOMEM;
+  return TQ_EDEVICE;
+}
+
+// Host description of one sub-plan before upload.
+struct SubHost {
+  int d, D, R;
+  std::vector<int32_t> chan;     // empty = identity
+  std::vector<double> lev, thr;
+  std::vector<uint32_t> signs;   // [3][D/32]
+  std::vector<uint16_t> S;       // [D][D]
+};
+
+// Coefficients a_S of the parity planes of odd subsets S of the R index bits:
+// c[idx] = sum_S a_S * chi_S(idx), chi_S = prod_{m in S} (2 b_m - 1), exact for a
+// codebook symmetric about zero (even subsets have zero weight).
+bool plane_coefficients(const std::vector<double>& lev, int R, float* coef, uint8_t* mask,
+                        int* n_planes, float* coef_sum) {
+  const int L = 1 << R;
+  int np = 0;
+  double sum = 0.0;
+  std::vector<double> a(L, 0.0);
+  for (int S = 1; S < L; ++S) {
+    double acc = 0.0;
+    for (int idx = 0; idx < L; ++idx) {
+      int chi = 1;
+      for (int m = 0; m < R; ++m)
+        if ((S >> m) & 1) chi *= ((idx >> m) & 1) ? 1 : -1;
+      acc += lev[idx] * chi;
+    }
+    a[S] = acc / L;
+  }
+  for (int S = 1; S < L; ++S) {
+    if (__builtin_popcount(S) % 2 == 0) continue;
+    coef[np] = (float)a[S];
+    mask[np] = (uint8_t)S;
+    sum += a[S];
+    ++np;
+  }
+  // reconstruct every level from the odd planes
+  for (int idx = 0; idx < L; ++idx) {
+    double v = 0.0;
+    for (int S = 1; S < L; ++S) {
+      if (__builtin_popcount(S) % 2 == 0) continue;
+      int chi = 1;
+      for (int m = 0; m < R; ++m)
+        if ((S >> m) & 1) chi *= ((idx >> m) & 1) ? 1 : -1;
+      v += a[S] * chi;
+    }
+    if (std::fabs(v - lev[idx]) > 1e-12) return false;
+  }
+  *n_planes = np;
+  *coef_sum = (float)sum;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tq_status_string(tq_status status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_EINVAL: return "invalid argument";
+    case TQ_ENOMEM: return "out of memory";
+    case TQ_EDEVICE: return "HIP device error";
+    case TQ_EUNSUPPORTED: return "unsupported";
+  }
+  return "unknown status";
+}
+
+tq_status tq_codebook(int D, int R, double* levels, double* thresholds) {
+  if (D < 3 || D > 65536 || R < 1 || R > 8 || !levels || !thresholds) return TQ_EINVAL;
+  solve_codebook(D, R, levels, thresholds);
+  return TQ_OK;
+}
+
+tq_status tq_rotation_signs(uint64_t seed, int subset, int D, int8_t* signs) {
+  if (D < 32 || D > 65536 || (D & (D - 1)) || subset < 0 || subset > 1 || !signs) return TQ_EINVAL;
+  std::vector<uint32_t> w(3 * (D / 32));
+  sign_words(seed, subset, D, w.data());
+  for (int r = 0; r < 3; ++r)
+    for (int i = 0; i < D; ++i)
+      signs[r * D + i] = ((w[r * (D / 32) + i / 32] >> (i % 32)) & 1u) ? -1 : 1;
+  return TQ_OK;
+}
+
+tq_status tq_qjl_matrix(uint64_t seed, int subset, int k, int D, uint16_t* S_bf16) {
+  if (k < 1 || k > 65536 || D < 1 || D > 65536 || subset < 0 || subset > 1 || !S_bf16)
+    return TQ_EINVAL;
+  qjl_matrix_bf16(seed, subset, k, D, S_bf16);
+  return TQ_OK;
+}
+
+tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_mask,
+                         int outlier_bits, tq_plan** out) {
+  if (!out) return TQ_EINVAL;
+  *out = nullptr;
+  if (d < 1 || d > kMaxD || bits < 2 || bits > kMaxR + 1) return TQ_EINVAL;
+  std::vector<SubHost> subs;
+  if (outlier_mask) {
+    if (outlier_bits < 2 || outlier_bits > kMaxR + 1) return TQ_EINVAL;
+    SubHost reg, out_s;
+    for (int c = 0; c < d; ++c) (outlier_mask[c] ? out_s.chan : reg.chan).push_back(c);
+    if (reg.chan.empty() || out_s.chan.empty()) return TQ_EINVAL;
+    reg.d = (int)reg.chan.size(); reg.R = bits - 1;
+    out_s.d = (int)out_s.chan.size(); out_s.R = outlier_bits - 1;
+    subs.push_back(std::move(reg));
+    subs.push_back(std::move(out_s));
+  } else {
+    SubHost s;
+    s.d = d; s.R = bits - 1;
+    subs.push_back(std::move(s));
+  }
+  int dev = -1;
+  if (!current_device(&dev)) return TQ_EDEVICE;
+
+  tq_plan* plan = new (std::nothrow) tq_plan();
+  if (!plan) return TQ_ENOMEM;
+  plan->device = dev;
+  plan->seed = seed;
+  plan->bits[0] = bits;
+  plan->bits[1] = outlier_mask ? outlier_bits : 0;
+  PlanDev& pd = plan->dev;
+  pd.d = d;
+  pd.nsub = (int)subs.size();
+  pd.rec_bytes = 0;
+
+  // host tables and device layout
+  size_t bytes = 0;
+  size_t off_sign[2] = {0, 0}, off_S[2] = {0, 0}, off_chan[2] = {0, 0};
+  auto take = [&](size_t b) { size_t o = bytes; bytes += (b + 255) / 256 * 256; return o; };
+  for (int i = 0; i < pd.nsub; ++i) {
+    SubHost& h = subs[i];
+    h.D = padded_length(h.d);
+    const int L = 1 << h.R;
+    h.lev.resize(L);
+    h.thr.resize(L - 1);
+    solve_codebook(h.D, h.R, h.lev.data(), h.thr.data());
+    h.signs.resize(3 * (h.D / 32));
+    sign_words(seed, i, h.D, h.signs.data());
+    h.S.resize((size_t)h.D * h.D);
+    qjl_matrix_bf16(seed, i, h.D, h.D, h.S.data());
+    SubDev& s = pd.sub[i];
+    memset(&s, 0, sizeof(s));
+    s.d = h.d;
+    s.D = h.D;
+    s.logD = __builtin_ctz(h.D);
+    s.R = h.R;
+    s.k = h.D;
+    s.rec_off = pd.rec_bytes;
+    s.rec_sub = record_bytes_of(h.D, h.R);
+    pd.rec_bytes += s.rec_sub;
+    s.inv_scale = (float)std::pow((double)h.D, -1.5);
+    for (int l = 0; l < L; ++l) s.lev[l] = (float)h.lev[l];
+    for (int j = 0; j < L - 1; ++j) s.thr[j] = (float)h.thr[j];
+    if (!plane_coefficients(h.lev, h.R, s.coef, s.plane_mask, &s.n_planes, &s.coef_sum)) {
+      delete plan;
+      return TQ_EDEVICE;
+    }
+    off_sign[i] = take(h.signs.size() * 4);
+    off_S[i] = take(h.S.size() * 2);
+    if (!h.chan.empty()) off_chan[i] = take(h.chan.size() * 4);
+  }
+  void* mem = nullptr;
+  hipError_t e = hipMalloc(&mem, bytes);
+  if (e != hipSuccess) {
+    delete plan;
+    return e == hipErrorOutOfMemory ? TQ_ENOMEM : TQ_EDEVICE;
+  }
+  plan->dev_alloc = mem;
+  uint8_t* base = static_cast<uint8_t*>(mem);
+  for (int i = 0; i < pd.nsub; ++i) {
+    SubHost& h = subs[i];
+    SubDev& s = pd.sub[i];
+    e = hipMemcpy(base + off_sign[i], h.signs.data(), h.signs.size() * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess)
+      e = hipMemcpy(base + off_S[i], h.S.data(), h.S.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && !h.chan.empty())
+      e = hipMemcpy(base + off_chan[i], h.chan.data(), h.chan.size() * 4, hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      (void)hipFree(mem);
+      delete plan;
+      return TQ_EDEVICE;
+    }
+    s.signs = reinterpret_cast<const uint32_t*>(base + off_sign[i]);
+    s.S = reinterpret_cast<const uint16_t*>(base + off_S[i]);
+    s.chan = h.chan.empty() ? nullptr : reinterpret_cast<const int32_t*>(base + off_chan[i]);
+  }
+  *out = plan;
+  return TQ_OK;
+}
+
+void tq_plan_destroy(tq_plan* plan) {
+  if (!plan) return;
+  if (plan->dev_alloc) (void)hipFree(plan->dev_alloc);
+  delete plan;
+}
+
+tq_status tq_plan_info(const tq_plan* plan, tq_plan_desc* desc) {
+  if (!plan || !desc) return TQ_EINVAL;
+  memset(desc, 0, sizeof(*desc));
+  desc->d = plan->dev.d;
+  desc->n_subplans = plan->dev.nsub;
+  desc->record_bytes = plan->dev.rec_bytes;
+  for (int i = 0; i < plan->dev.nsub; ++i) {
+    const SubDev& s = plan->dev.sub[i];
+    desc->sub[i].d = s.d;
+    desc->sub[i].D = s.D;
+    desc->sub[i].R = s.R;
+    desc->sub[i].k = s.k;
+    desc->sub[i].record_offset = s.rec_off;
+    desc->sub[i].record_bytes = s.rec_sub;
+  }
+  return TQ_OK;
+}
+
+tq_status tq_encode(const tq_plan* plan, const void* x, tq_dtype dt, int64_t n, int64_t ldx,
+                    void* codes, void* stream) {
+  if (!plan || n < 0 || (dt != TQ_F32 && dt != TQ_BF16)) return TQ_EINVAL;
+  if (n == 0) return TQ_OK;
+  const int es = dt == TQ_BF16 ? 2 : 4;
+  if (!x || !codes || ldx < plan->dev.d || (uintptr_t)x % es || (uintptr_t)codes % 16)
+    return TQ_EINVAL;
+  if (!plan_device_ok(plan)) return TQ_EINVAL;
+  for (int i = 0; i < plan->dev.nsub; ++i) {
+    const int rc = launch_encode(plan->dev, i, x, (int)dt, n, ldx, static_cast<uint8_t*>(codes), stream);
+    if (rc) return from_hip(rc);
+  }
+  return TQ_OK;
+}
+
+tq_status tq_score(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_per_group,
+                   int64_t n_groups, int64_t ldq, const void* codes, int64_t n, float* scores,
+                   void* stream) {
+  if (!plan || nq_per_group < 0 || n_groups < 0 || n < 0 || (dt != TQ_F32 && dt != TQ_BF16))
+    return TQ_EINVAL;
+  if (nq_per_group == 0 || n_groups == 0 || n == 0) return TQ_OK;
+  const int es = dt == TQ_BF16 ? 2 : 4;
+  if (!q || !codes || !scores || ldq < plan->dev.d || (uintptr_t)q % es || (uintptr_t)codes % 16 ||
+      (uintptr_t)scores % 4)
+    return TQ_EINVAL;
+  if (nq_per_group * n_groups > (int64_t)1 << 31 || n_groups > 65535 * 64) return TQ_EINVAL;
+  if (!plan_device_ok(plan)) return TQ_EINVAL;
+  return from_hip(launch_score(plan->dev, q, (int)dt, nq_per_group, n_groups, ldq,
+                               static_cast<const uint8_t*>(codes), n, scores, stream));
+}
+
+tq_status tq_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids, float* vals,
+                  void* stream) {
+  if (nq < 0 || n < 0 || k < 1 || k > 64 || k > n || n >= ((int64_t)1 << 31)) return TQ_EINVAL;
+  if (nq == 0) return TQ_OK;
+  if (!scores || !ids || !vals || (uintptr_t)scores % 4 || (uintptr_t)ids % 8 || (uintptr_t)vals % 4)
+    return TQ_EINVAL;
+  int dev;
+  if (hipGetDevice(&dev) != hipSuccess) return TQ_EDEVICE;
+  return from_hip(launch_topk(scores, nq, n, k, ids, vals, stream));
+}
+
+tq_status tq_qjl(const tq_plan* plan, int subplan, const float* r, int64_t n, uint32_t* beta,
+                 void* stream) {
+  if (!plan || subplan < 0 || subplan >= plan->dev.nsub || n < 0) return TQ_EINVAL;
+  if (n == 0) return TQ_OK;
+  if (!r || !beta || (uintptr_t)r % 4 || (uintptr_t)beta % 4) return TQ_EINVAL;
+  if (!plan_device_ok(plan)) return TQ_EINVAL;
+  return from_hip(launch_qjl(plan->dev.sub[subplan], r, n, beta, stream));
+}
+
+}  // extern "C"

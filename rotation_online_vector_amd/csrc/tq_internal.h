@@ -1,0 +1,67 @@
+// Internal declarations shared by the host code and the HIP kernels of libtq.
+#pragma once
+#include <cstdint>
+
+#include "../../include/tq.h"
+
+namespace tq {
+
+constexpr int kMaxR = 4;         // index bits per coordinate: b - 1 with b <= 5
+constexpr int kMinD = 32;
+constexpr int kMaxD = 2048;
+
+// Host tables (host_tables.cpp)
+void philox4x32_10(uint64_t block, uint32_t domain, uint64_t seed, uint32_t out[4]);
+void sign_words(uint64_t seed, int subset, int D, uint32_t* words);
+uint16_t bf16_rne_from_double(double x);
+void qjl_matrix_bf16(uint64_t seed, int subset, int k, int D, uint16_t* S);
+int solve_codebook(int D, int R, double* levels, double* thresholds);
+
+// Per-sub-plan parameters handed to kernels by value.
+struct SubDev {
+  int d;            // channels of this sub-plan
+  int D;            // rotated length (power of two)
+  int logD;
+  int R;            // index bits
+  int k;            // QJL rows (= D)
+  int rec_off;      // byte offset of the sub-record inside a vector record
+  int rec_sub;      // bytes of the sub-record
+  int n_planes;     // 2^(R-1) odd-subset planes used by the bit-sliced scorer
+  float inv_scale;  // D^(-3/2): the three normalized transforms folded into one multiply
+  float thr[15];    // 2^R - 1 thresholds (ascending)
+  float lev[16];    // 2^R levels (ascending)
+  float coef[8];    // coefficient of each odd-subset parity plane (scorer)
+  uint8_t plane_mask[8];  // bit m set = index bit m enters the parity plane
+  float coef_sum;   // sum of coef
+  const uint32_t* signs;  // device [3][D/32]; bit set = -1
+  const uint16_t* S;      // device [k][D] bf16 bit patterns
+  const int32_t* chan;    // device [d] input channel of each coordinate, or null (identity)
+};
+
+struct PlanDev {
+  int d;
+  int nsub;
+  int rec_bytes;
+  SubDev sub[2];
+};
+
+}  // namespace tq
+
+struct tq_plan {
+  tq::PlanDev dev;      // device pointers inside
+  int device;           // HIP device the tables live on
+  void* dev_alloc;      // single device allocation holding every table
+  uint64_t seed;
+  int bits[2];
+};
+
+// Kernel launchers (kernels.hip).  Return 0 or a HIP error code.
+namespace tq {
+int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, int64_t ldx,
+                  uint8_t* codes, void* stream);
+int launch_qjl(const SubDev& s, const float* r, int64_t n, uint32_t* beta, void* stream);
+int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, int64_t n_groups,
+                 int64_t ldq, const uint8_t* codes, int64_t n, float* scores, void* stream);
+int launch_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids, float* vals,
+                void* stream);
+}  // namespace tq

@@ -1,0 +1,206 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import layout
+from oracle import turboquant as otq
+from tests import parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import rotation_online_vector_amd as tq  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _encode_and_compare(sp, plan, x_t, what):
+    codes = tq.tq_encode(plan, x_t)
+    torch.cuda.synchronize()
+    got = parity.unpack_gpu(sp, codes.cpu().numpy())
+    xs = _np(x_t).reshape(-1, sp.d)
+    ref = otq.encode_split(sp, xs)
+    stats = [parity.compare_codes(p, r, g, "%s/sub%d" % (what, i))
+             for i, (p, r, g) in enumerate(zip(sp.plans, ref, got))]
+    return codes, ref, got, stats
+
+
+# ----------------------------------------------------------------------------- small config
+
+@pytest.fixture(scope="module")
+def small():
+    keys, queries = workloads.small_inputs()
+    sp = otq.make_split_plan(128, 4, 0)
+    plan = tq.tq_plan_create(128, 4, 0)
+    return keys, queries, sp, plan
+
+
+def test_plan_layout(small):
+    _, _, sp, plan = small
+    assert plan.record_bytes == layout.record_bytes(128, 3) == 72
+    assert plan.desc["sub"][0]["D"] == 128 and plan.desc["sub"][0]["R"] == 3
+
+
+def test_encode_small_matches_oracle(small):
+    keys, _, sp, plan = small
+    x = torch.from_numpy(keys).to(DEV)
+    _, _, _, stats = _encode_and_compare(sp, plan, x, "small")
+    print(stats)
+
+
+def test_encode_is_deterministic(small):
+    keys, _, _, plan = small
+    x = torch.from_numpy(keys).to(DEV)
+    a = tq.tq_encode(plan, x)
+    b = tq.tq_encode(plan, x)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_qjl_stage_matches_oracle(small):
+    _, _, sp, plan = small
+    p = sp.plans[0]
+    rng = np.random.default_rng(3)
+    r = (rng.standard_normal((1000, 128)) * 0.03).astype(np.float32)
+    beta = tq.tq_qjl(plan, 0, torch.from_numpy(r).to(DEV)).cpu().numpy().view(np.uint32)
+    got = ((beta[:, :, None] >> np.arange(32, dtype=np.uint32)) & 1).reshape(1000, 128)
+    ref, proj = otq.qjl_signs(p.S, r.astype(np.float64))
+    mis = got != ref
+    band = parity.sign_band(p, r.astype(np.float64), proj)
+    assert not (mis & ~band).any()
+    assert mis.sum() <= 1
+
+
+def test_score_small_matches_oracle_on_oracle_codes(small):
+    keys, queries, sp, plan = small
+    ref = parity.stored(otq.encode(sp.plans[0], keys.astype(np.float64)))
+    rec = layout.pack(ref, 128, 3)
+    codes = torch.from_numpy(rec).to(DEV)
+    q = torch.from_numpy(queries).to(DEV)
+    est = tq.tq_score(plan, q, codes, n=4096).cpu().numpy()
+    est_ref = otq.score(sp.plans[0], ref, queries.astype(np.float64))
+    r = parity.check_scores(est, est_ref, np.linalg.norm(queries, axis=1),
+                            np.linalg.norm(keys, axis=1), "small")
+    print("max err / tol:", r)
+
+
+def test_end_to_end_small_and_topk(small):
+    keys, queries, sp, plan = small
+    x = torch.from_numpy(keys).to(DEV)
+    codes = tq.tq_encode(plan, x)
+    q = torch.from_numpy(queries).to(DEV)
+    est = tq.tq_score(plan, q, codes, n=4096)
+    ids, vals = tq.tq_topk(est, 10)
+    torch.cuda.synchronize()
+    est = est.cpu().numpy()
+    got = parity.unpack_gpu(sp, codes.cpu().numpy())[0]
+    ref = otq.encode(sp.plans[0], keys.astype(np.float64))
+    same = np.all(got["idx"] == ref["idx"], axis=1) & np.all(got["beta"] == ref["beta"], axis=1)
+    assert same.mean() > 0.99
+    est_ref = otq.score(sp.plans[0], parity.stored(ref), queries.astype(np.float64))
+    qn, xn = np.linalg.norm(queries, axis=1), np.linalg.norm(keys, axis=1)
+    parity.check_scores(est[:, same], est_ref[:, same], qn, xn[same], "small e2e")
+    parity.check_topk(ids.cpu().numpy(), vals.cpu().numpy(), est_ref, 10, qn, xn, "small top-10")
+    # values returned are the GPU scores of the returned ids
+    assert np.array_equal(vals.cpu().numpy(), np.take_along_axis(est, ids.cpu().numpy(), 1))
+
+
+# ----------------------------------------------------------------------------- top-k
+
+@pytest.mark.parametrize("nq,n,k", [(5, 1000, 10), (3, 4096, 1), (2, 300000, 64), (4, 37, 37),
+                                    (1, 1, 1), (7, 70000, 16)])
+def test_topk_matches_oracle_exactly_with_ties(nq, n, k):
+    rng = np.random.default_rng(nq * 1000 + k)
+    s = np.round(rng.standard_normal((nq, n)), 2).astype(np.float32)   # many ties
+    ids, vals = tq.tq_topk(torch.from_numpy(s).to(DEV), k)
+    ids_ref, vals_ref = otq.topk(s.astype(np.float64), k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.array_equal(vals.cpu().numpy().astype(np.float64), vals_ref)
+
+
+# ----------------------------------------------------------------------------- shapes and edges
+
+@pytest.mark.parametrize("d,bits,n,dtype", [
+    (128, 3, 1, "float32"), (128, 3, 1001, "bfloat16"), (100, 3, 517, "float32"),
+    (33, 5, 300, "bfloat16"), (1, 2, 65, "float32"), (64, 2, 200, "float32"),
+    (256, 4, 130, "bfloat16"), (512, 3, 70, "float32"), (1024, 2, 40, "float32"),
+    (1536, 4, 40, "float32"), (2048, 5, 20, "bfloat16"), (32, 4, 129, "float32")])
+def test_encode_and_score_shapes(d, bits, n, dtype):
+    rng = np.random.default_rng(d + n)
+    xs = rng.standard_normal((n, d)).astype(np.float32)
+    if d == 1:
+        # one channel: every vector is a multiple of e_1, so the rotated coordinates that
+        # are exactly zero recur in every row; small integers keep both sides exact there
+        xs = np.rint(4 * xs).astype(np.float32)
+    xs[0] *= 0.0                                             # zero vector
+    ys = rng.standard_normal((6, d)).astype(np.float32)
+    x = torch.from_numpy(xs).to(DEV).to(getattr(torch, dtype))
+    y = torch.from_numpy(ys).to(DEV).to(getattr(torch, dtype))
+    sp = otq.make_split_plan(d, bits, 11)
+    plan = tq.tq_plan_create(d, bits, 11)
+    codes, ref, got, _ = _encode_and_compare(sp, plan, x, "d=%d" % d)
+    xs64, ys64 = _np(x), _np(y)
+    # score kernel on oracle codes, 2 groups of 3 queries (second group reuses the codes)
+    rec = layout.pack_split(sp, [parity.stored(c) for c in ref])
+    rec2 = torch.from_numpy(np.concatenate([rec, rec])).to(DEV)
+    est = tq.tq_score(plan, y, rec2, n=n, nq_per_group=3, n_groups=2).cpu().numpy()
+    est_ref = otq.score_split(sp, [parity.stored(c) for c in ref], ys64)
+    parity.check_scores(est, est_ref, np.linalg.norm(ys64, axis=1), np.linalg.norm(xs64, axis=1),
+                        "d=%d" % d)
+    assert np.all(est[:, 0] == 0.0)
+
+
+def test_strided_rows_and_query_groups():
+    d, n = 128, 300
+    rng = np.random.default_rng(5)
+    big = torch.from_numpy(rng.standard_normal((n, 160)).astype(np.float32)).to(DEV)
+    x = big[:, 16:144]                                       # row stride 160, offset 16
+    sp = otq.make_split_plan(d, 3, 2)
+    plan = tq.tq_plan_create(d, 3, 2)
+    _encode_and_compare(sp, plan, x, "strided")
+    for g in (1, 2, 3, 5, 8):
+        y = torch.from_numpy(rng.standard_normal((2 * g, d)).astype(np.float32)).to(DEV)
+        codes = tq.tq_encode(plan, torch.cat([x, x]).contiguous())
+        est = tq.tq_score(plan, y, codes, n=n, nq_per_group=g, n_groups=2).cpu().numpy()
+        ref = parity.stored(otq.encode(sp.plans[0], _np(x)))
+        got = parity.unpack_gpu(sp, codes[:n].cpu().numpy())[0]
+        same = np.all(got["idx"] == ref["idx"], 1) & np.all(got["beta"] == ref["beta"], 1)
+        est_ref = otq.score(sp.plans[0], ref, _np(y))
+        parity.check_scores(est[:, same], est_ref[:, same], np.linalg.norm(_np(y), axis=1),
+                            np.linalg.norm(_np(x), axis=1)[same], "group %d" % g)
+
+
+def test_outlier_split_plan_small():
+    d = 128
+    rng = np.random.default_rng(9)
+    mask = np.zeros(d, dtype=np.uint8)
+    mask[np.sort(rng.choice(d, 32, replace=False))] = 1
+    xs = rng.standard_normal((700, d)).astype(np.float32)
+    xs[:, mask == 1] *= 10
+    ys = rng.standard_normal((4, d)).astype(np.float32)
+    for bits, obits in ((3, 5), (2, 4)):
+        sp = otq.make_split_plan(d, bits, 0, mask, obits)
+        plan = tq.tq_plan_create(d, bits, 0, mask, obits)
+        assert plan.record_bytes == sum(layout.record_bytes(p.D, p.R) for p in sp.plans)
+        x = torch.from_numpy(xs).to(DEV).to(torch.bfloat16)
+        codes, ref, got, _ = _encode_and_compare(sp, plan, x, "split %d/%d" % (bits, obits))
+        rec = torch.from_numpy(layout.pack_split(sp, [parity.stored(c) for c in ref])).to(DEV)
+        y = torch.from_numpy(ys).to(DEV).to(torch.bfloat16)
+        est = tq.tq_score(plan, y, rec, n=700).cpu().numpy()
+        est_ref = otq.score_split(sp, [parity.stored(c) for c in ref], _np(y))
+        parity.check_scores(est, est_ref, np.linalg.norm(_np(y), axis=1),
+                            np.linalg.norm(_np(x), axis=1), "split score")
+
+
+def test_invalid_calls_raise():
+    plan = tq.tq_plan_create(128, 3, 0)
+    x = torch.zeros((4, 64), device=DEV)
+    with pytest.raises(ValueError):
+        tq.tq_encode(plan, x)
+    with pytest.raises(tq.TqError):
+        tq.tq_topk(torch.zeros((2, 5), device=DEV), 6)
