@@ -30,12 +30,14 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-keys", type=int, default=1 << 18)
+    ap.add_argument("--cpu-sample-groups", type=int, default=16)
     return ap.parse_args()
 
 
-def cpu_baseline(keys_sample, queries_sample, bits, seed):
-    """The fp64 oracle, as it stands, on one KV head's first keys and its 4 query heads."""
+def cpu_baseline(keys, queries, group, bits, seed, n_groups):
+    """The fp64 oracle, as it stands, on the first `n_groups` (sequence, KV head) groups:
+    encode all their keys and score them against their query heads (same work per key as
+    one step of the GPU path)."""
     import numpy as np
     from oracle import turboquant as otq
     try:
@@ -43,16 +45,21 @@ def cpu_baseline(keys_sample, queries_sample, bits, seed):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    x = keys_sample.astype(np.float64)
-    y = queries_sample.astype(np.float64)
-    plan = otq.make_plan(x.shape[1], bits, seed)
-    t0 = time.perf_counter()
-    codes = otq.encode(plan, x)
-    est = otq.score(plan, codes, y)
-    dt = time.perf_counter() - t0
-    return {"value": est.size / dt, "unit": "scores/s", "cores": int(threads), "kind": "oracle",
-            "sample": "%d keys of one (sequence, KV head) x its %d query heads: fp64 encode + "
-                      "score (plan solve excluded), %.1f s" % (x.shape[0], y.shape[0], dt)}
+    n_seq, n_kv, n_tok, d = keys.shape
+    plan = otq.make_plan(d, bits, seed)
+    n_scores, dt = 0, 0.0
+    for g in range(n_groups):
+        s, h = divmod(g, n_kv)
+        x = keys[s, h].float().cpu().numpy().astype(np.float64)
+        y = queries[s, h * group:(h + 1) * group].float().cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        est = otq.score(plan, otq.encode(plan, x), y)
+        dt += time.perf_counter() - t0
+        n_scores += est.size
+    return {"value": n_scores / dt, "unit": "scores/s", "cores": int(threads), "kind": "oracle",
+            "sample": "%d of %d (sequence, KV head) groups: %d keys encoded and scored against "
+                      "their %d query heads in fp64 (plan solve excluded), %.1f s of CPU time"
+                      % (n_groups, n_seq * n_kv, n_groups * n_tok, group, dt)}
 
 
 def main():
@@ -137,9 +144,8 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        ks = keys[0, 0, :args.cpu_sample_keys].float().cpu().numpy()
-        qs = queries[0, :G].float().cpu().numpy()
-        out["cpu_baseline"] = cpu_baseline(ks, qs, W["bits"], W["seed"])
+        out["cpu_baseline"] = cpu_baseline(keys, queries, G, W["bits"], W["seed"],
+                                           args.cpu_sample_groups)
     print(json.dumps(out), flush=True)
 
 

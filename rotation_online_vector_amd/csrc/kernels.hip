@@ -138,16 +138,16 @@ struct EncodeArgs {
   int vec_load;   // rows 16-byte aligned and no channel gather: vector loads
 };
 
-template <int D>
+template <int D, int R>
 __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
   using C = EncCfg<D>;
   constexpr int EPT = C::EPT, TPV = C::TPV, VPP = C::VPP, V = C::V, RS = C::RSTRIDE;
+  constexpr int L = 1 << R;
   const SubDev& s = a.s;
-  const int R = s.R;
   const int recw = s.rec_sub / 4;   // words per sub-record
   __shared__ __attribute__((aligned(16))) uint16_t rhi[V * RS];
   __shared__ __attribute__((aligned(16))) uint16_t rlo[V * RS];
-  __shared__ __attribute__((aligned(16))) uint32_t rec[V * ((4 * (kMaxR + 1) * D / 32 + 8) / 4)];
+  __shared__ __attribute__((aligned(16))) uint32_t rec[V * ((4 * (R + 1) * D / 32 + 8) / 4)];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = lane % TPV;                 // lane within its vector
@@ -219,26 +219,32 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
       fwht_lanes<EPT, TPV>(v, t);
     }
     const float scale = nrm > 0.f ? s.inv_scale / nrm : 0.f;
-    // ---- bucketize, residual ----
-    uint32_t planes[kMaxR];
+    // ---- bucketize (idx = #{t_j <= z}), residual ----
+    float thr[L - 1], lev[L];
 #pragma unroll
-    for (int m = 0; m < kMaxR; ++m) planes[m] = 0;
+    for (int j = 0; j < L - 1; ++j) thr[j] = s.thr[j];
+#pragma unroll
+    for (int j = 0; j < L; ++j) lev[j] = s.lev[j];
+    uint32_t planes[R];
+#pragma unroll
+    for (int m = 0; m < R; ++m) planes[m] = 0;
     float gg = 0.f;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const float z = v[e] * scale;
       int idx = 0;
-      float lv = s.lev[0];
-      for (int j = 0; j < (1 << R) - 1; ++j) {
-        const bool ge = z >= s.thr[j];
+      float lv = lev[0];
+#pragma unroll
+      for (int j = 0; j < L - 1; ++j) {
+        const bool ge = z >= thr[j];
         idx += ge ? 1 : 0;
-        lv = ge ? s.lev[j + 1] : lv;
+        lv = ge ? lev[j + 1] : lv;
       }
       const float rr = z - lv;
       gg = fmaf(rr, rr, gg);
       v[e] = rr;
 #pragma unroll
-      for (int m = 0; m < kMaxR; ++m) planes[m] |= (uint32_t)((idx >> m) & 1) << e;
+      for (int m = 0; m < R; ++m) planes[m] |= (uint32_t)((idx >> m) & 1) << e;
     }
     gg = lane_group_sum<TPV>(gg);
     // ---- residual limbs to LDS ----
@@ -263,12 +269,13 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
     // ---- index bit-planes, norm and gamma into the staged record ----
     uint32_t* myrec = rec + vl * recw;
     if (EPT == 32) {
+#pragma unroll
       for (int m = 0; m < R; ++m) myrec[(c0 / 32) * (R + 1) + m] = planes[m];
     } else {
 #pragma unroll
-      for (int m = 0; m < kMaxR; ++m) {
+      for (int m = 0; m < R; ++m) {
         const uint32_t other = __shfl_xor(planes[m], 1);
-        if (m < R && (t & 1) == 0) myrec[(c0 / 32) * (R + 1) + m] = planes[m] | (other << 16);
+        if ((t & 1) == 0) myrec[(c0 / 32) * (R + 1) + m] = planes[m] | (other << 16);
       }
     }
     if (t == 0) {
@@ -454,24 +461,26 @@ struct QImageArgs {
   float* ec;           // [groups*qtiles][4 queries][4]: c0, c1, c2, c3
 };
 
-// one wave per (group, query tile)
-__global__ void __launch_bounds__(kWave) qimage_kernel(QImageArgs a) {
+// grid (group * query tile, plane); the last plane index is the QJL image
+__global__ void __launch_bounds__(kBlock) qimage_kernel(QImageArgs a) {
   const SubDev& s = a.s;
   const int D = s.D;
   const int gt = blockIdx.x;                    // group * n_qtiles + qtile
+  const int p = blockIdx.y;
   const int64_t grp = gt / a.n_qtiles, qt = gt % a.n_qtiles;
-  const int lane = threadIdx.x;
   const int np = s.n_planes;
+  const int tid = threadIdx.x;
   float cmax = 0.f;
-  for (int p = 0; p < np; ++p) cmax = fmaxf(cmax, fabsf(s.coef[p]));
+  for (int i = 0; i < np; ++i) cmax = fmaxf(cmax, fabsf(s.coef[i]));
   // per-query scales: powers of two putting the largest image magnitude in (128, 256]
+  __shared__ float red[2][4][kBlock / kWave];
   __shared__ float sc_mse[4], sc_qjl[4];
   for (int q = 0; q < 4; ++q) {
     const int64_t qq = qt * 4 + q;
     float my = 0.f, mw = 0.f;
     if (qq < a.nq_per_group) {
       const int64_t qi = grp * a.nq_per_group + qq;
-      for (int i = lane; i < D; i += kWave) {
+      for (int i = tid; i < D; i += kBlock) {
         my = fmaxf(my, fabsf(a.yrot[qi * D + i]));
         mw = fmaxf(mw, fabsf(a.w[qi * D + i]));
       }
@@ -480,58 +489,58 @@ __global__ void __launch_bounds__(kWave) qimage_kernel(QImageArgs a) {
       my = fmaxf(my, __shfl_xor(my, m));
       mw = fmaxf(mw, __shfl_xor(mw, m));
     }
-    if (lane == 0) {
-      const float M1 = my * cmax, M2 = mw;
-      sc_mse[q] = M1 > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(M1))) : 1.f;
-      sc_qjl[q] = M2 > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(M2))) : 1.f;
-    }
+    if ((tid & 63) == 0) { red[0][q][tid >> 6] = my; red[1][q][tid >> 6] = mw; }
   }
   __syncthreads();
-  const int row = lane & 15, Ga = lane >> 4;
-  const int q = row >> 2, limb = row & 3;
-  const int64_t qq = qt * 4 + q;
-  const bool valid = (qq < a.nq_per_group) && limb < 3;
-  const int64_t qi = grp * a.nq_per_group + qq;
-  for (int p = 0; p <= np; ++p) {
-    uint32_t words[8];
-    for (int wd = 0; wd < 8; ++wd) {
-      uint32_t word = 0;
-      for (int b = 0; b < 4; ++b) {
-        const int e = 4 * wd + b;
-        const int K = e < 16 ? 16 * Ga + e : 64 + 16 * Ga + (e - 16);
-        const int c = bitslice_coord(K);
-        uint32_t byte = 0;
-        if (valid && c < D) {
-          const float v = (p < np) ? s.coef[p] * a.yrot[qi * D + c] * sc_mse[q]
-                                   : a.w[qi * D + c] * sc_qjl[q];
-          float rem = v;
-          uint32_t code = 0;
-          for (int l = 0; l <= limb; ++l) {
-            code = e4m3_encode(rem);
-            rem -= e4m3_decode(code);
-          }
-          byte = code;
-        }
-        word |= byte << (8 * b);
-      }
-      words[wd] = word;
-    }
-    uint4* dst = reinterpret_cast<uint4*>(a.img + ((size_t)gt * (np + 1) + p) * 64 * 8 + lane * 8);
-    dst[0] = make_uint4(words[0], words[1], words[2], words[3]);
-    dst[1] = make_uint4(words[4], words[5], words[6], words[7]);
+  if (tid < 4) {
+    float my = 0.f, mw = 0.f;
+    for (int w = 0; w < kBlock / kWave; ++w) { my = fmaxf(my, red[0][tid][w]); mw = fmaxf(mw, red[1][tid][w]); }
+    const float M1 = my * cmax, M2 = mw;
+    sc_mse[tid] = M1 > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(M1))) : 1.f;
+    sc_qjl[tid] = M2 > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(M2))) : 1.f;
   }
-  if (lane < 4) {
-    const int64_t q2 = qt * 4 + lane;
+  __syncthreads();
+  uint32_t* img = a.img + ((size_t)gt * (np + 1) + p) * 64 * 8;
+  for (int widx = tid; widx < 64 * 8; widx += kBlock) {
+    const int lane = widx >> 3, wd = widx & 7;
+    const int row = lane & 15, Ga = lane >> 4;
+    const int q = row >> 2, limb = row & 3;
+    const int64_t qq = qt * 4 + q;
+    const bool valid = (qq < a.nq_per_group) && limb < 3;
+    const int64_t qi = grp * a.nq_per_group + qq;
+    uint32_t word = 0;
+    for (int b = 0; b < 4; ++b) {
+      const int e = 4 * wd + b;
+      const int K = e < 16 ? 16 * Ga + e : 64 + 16 * Ga + (e - 16);
+      const int c = bitslice_coord(K);
+      uint32_t byte = 0;
+      if (valid && c < D) {
+        const float v = (p < np) ? s.coef[p] * a.yrot[qi * D + c] * sc_mse[q]
+                                 : a.w[qi * D + c] * sc_qjl[q];
+        float rem = v;
+        uint32_t code = 0;
+        for (int l = 0; l <= limb; ++l) {
+          code = e4m3_encode(rem);
+          rem -= e4m3_decode(code);
+        }
+        byte = code;
+      }
+      word |= byte << (8 * b);
+    }
+    img[widx] = word;
+  }
+  if (p == 0 && tid < 4) {
+    const int64_t q2 = qt * 4 + tid;
     float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
     if (q2 < a.nq_per_group) {
       const int64_t qi2 = grp * a.nq_per_group + q2;
       const float K = sqrtf(0.5f * (float)M_PI) / (float)s.k;
       c0 = -s.coef_sum * a.sums[qi2 * 2];
-      c1 = 4.f / sc_mse[lane];
+      c1 = 4.f / sc_mse[tid];
       c2 = -K * a.sums[qi2 * 2 + 1];
-      c3 = 4.f * K / sc_qjl[lane];
+      c3 = 4.f * K / sc_qjl[tid];
     }
-    float* e = a.ec + ((size_t)gt * 4 + lane) * 4;
+    float* e = a.ec + ((size_t)gt * 4 + tid) * 4;
     e[0] = c0; e[1] = c1; e[2] = c2; e[3] = c3;
   }
 }
@@ -802,7 +811,14 @@ static inline int hip_rc(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
 template <int D>
 static int launch_encode_d(const EncodeArgs& ea, hipStream_t st) {
   const int64_t tiles = (ea.n + EncCfg<D>::V - 1) / EncCfg<D>::V;
-  hipLaunchKernelGGL(encode_kernel<D>, dim3((unsigned)tiles), dim3(kBlock), 0, st, ea);
+  const dim3 grid((unsigned)tiles), block(kBlock);
+  switch (ea.s.R) {
+    case 1: hipLaunchKernelGGL((encode_kernel<D, 1>), grid, block, 0, st, ea); break;
+    case 2: hipLaunchKernelGGL((encode_kernel<D, 2>), grid, block, 0, st, ea); break;
+    case 3: hipLaunchKernelGGL((encode_kernel<D, 3>), grid, block, 0, st, ea); break;
+    case 4: hipLaunchKernelGGL((encode_kernel<D, 4>), grid, block, 0, st, ea); break;
+    default: return (int)hipErrorInvalidValue;
+  }
   return hip_rc(hipGetLastError());
 }
 
@@ -929,7 +945,8 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
       ia.n_qtiles = qt_bs;
       ia.img = reinterpret_cast<uint32_t*>(wb + off_img[sb]);
       ia.ec = reinterpret_cast<float*>(wb + off_ec[sb]);
-      hipLaunchKernelGGL(qimage_kernel, dim3((unsigned)(n_groups * qt_bs)), dim3(kWave), 0, st, ia);
+      hipLaunchKernelGGL(qimage_kernel, dim3((unsigned)(n_groups * qt_bs), (unsigned)(p.sub[sb].n_planes + 1)),
+                         dim3(kBlock), 0, st, ia);
       sa.img[sb] = ia.img;
       sa.ec[sb] = ia.ec;
     }
