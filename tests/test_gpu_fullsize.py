@@ -1,0 +1,145 @@
+"""Parity at the full benchmark sizes, in the launch configuration bench.py times,
+on sampled outputs the oracle computes one by one."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import turboquant as otq
+from tests import parity
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import rotation_online_vector_amd as tq  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def _np64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _check_sampled(sp, codes_u8, x_rows, keys_idx, q_rows, scores_rows, tag):
+    """codes of sampled keys vs the oracle; scores of the sampled (query, key) pairs."""
+    got = parity.unpack_gpu(sp, codes_u8)
+    ref = otq.encode_split(sp, x_rows)
+    for i, (p, r, g) in enumerate(zip(sp.plans, ref, got)):
+        parity.compare_codes(p, r, g, "%s/sub%d" % (tag, i))
+    same = np.ones(len(keys_idx), dtype=bool)
+    for r, g in zip(ref, got):
+        same &= np.all(r["idx"] == g["idx"], 1) & np.all(r["beta"] == g["beta"], 1)
+    est_ref = otq.score_split(sp, [parity.stored(c) for c in ref], q_rows)
+    parity.check_scores(scores_rows[:, same], est_ref[:, same], np.linalg.norm(q_rows, axis=1),
+                        np.linalg.norm(x_rows, axis=1)[same], tag)
+    return same.mean()
+
+
+def test_kv_cache_shape_full():
+    W = workloads.KV
+    keys, queries, _ = workloads.kv_inputs(DEV, n_kv=W["n_kv"], n_tok=W["n_tok"], d=W["d"],
+                                           group=W["group"], n_outlier=W["n_outlier"],
+                                           outlier_scale=W["outlier_scale"], seed=W["seed"])
+    n_kv, n_tok, d, G = W["n_kv"], W["n_tok"], W["d"], W["group"]
+    plan = tq.tq_plan_create(d, W["bits"], W["seed"])
+    sp = otq.make_split_plan(d, W["bits"], W["seed"])
+    codes = tq.tq_encode(plan, keys.view(-1, d))
+    scores = tq.tq_score(plan, queries, codes, n=n_tok, nq_per_group=G, n_groups=n_kv)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1)
+    for h in (0, 5, 7):
+        kidx = np.sort(rng.choice(n_tok, 1024, replace=False))
+        rows = h * n_tok + kidx
+        frac = _check_sampled(sp, codes[torch.as_tensor(rows, device=DEV)].cpu().numpy(),
+                              _np64(keys[h][torch.as_tensor(kidx, device=DEV)]), kidx,
+                              _np64(queries[h * G:(h + 1) * G]),
+                              scores[h * G:(h + 1) * G][:, torch.as_tensor(kidx, device=DEV)].cpu().numpy(),
+                              "kv head %d" % h)
+        assert frac > 0.99
+
+
+@pytest.mark.parametrize("variant", ["3.5bit", "2.5bit"])
+def test_split_shape_full(variant):
+    W = workloads.SPLIT if variant == "3.5bit" else workloads.SPLIT_25
+    keys, queries, ch = workloads.kv_inputs(DEV, n_kv=W["n_kv"], n_tok=W["n_tok"], d=W["d"],
+                                            group=W["group"], n_outlier=W["n_outlier"],
+                                            outlier_scale=W["outlier_scale"], seed=W["seed"])
+    n_kv, n_tok, d, G = W["n_kv"], W["n_tok"], W["d"], W["group"]
+    rng = np.random.default_rng(2)
+    for h in range(n_kv):
+        mask = np.zeros(d, dtype=np.uint8)
+        mask[ch[h]] = 1
+        plan = tq.tq_plan_create(d, W["bits"], W["seed"], mask, W["outlier_bits"])
+        codes = tq.tq_encode(plan, keys[h])
+        scores = tq.tq_score(plan, queries[h * G:(h + 1) * G], codes, n=n_tok)
+        torch.cuda.synchronize()
+        if h in (0, 3):
+            sp = otq.make_split_plan(d, W["bits"], W["seed"], mask, W["outlier_bits"])
+            kidx = np.sort(rng.choice(n_tok, 1024, replace=False))
+            ki = torch.as_tensor(kidx, device=DEV)
+            frac = _check_sampled(sp, codes[ki].cpu().numpy(), _np64(keys[h][ki]), kidx,
+                                  _np64(queries[h * G:(h + 1) * G]), scores[:, ki].cpu().numpy(),
+                                  "split %s head %d" % (variant, h))
+            assert frac > 0.99
+
+
+def test_long_context_shape_full_as_benchmarked():
+    W = workloads.LONGCTX
+    keys, queries, _ = workloads.longctx_inputs(DEV)
+    n_seq, n_kv, n_tok, d, G = W["n_seq"], W["n_kv"], W["n_tok"], W["d"], W["group"]
+    plan = tq.tq_plan_create(d, W["bits"], W["seed"])
+    sp = otq.make_split_plan(d, W["bits"], W["seed"])
+    codes = tq.tq_encode(plan, keys.view(-1, d))
+    scores = tq.tq_score(plan, queries.view(-1, d), codes, n=n_tok, nq_per_group=G,
+                         n_groups=n_seq * n_kv)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    for (s, h) in ((0, 0), (7, 3), (15, 7)):
+        kidx = np.sort(rng.choice(n_tok, 768, replace=False))
+        ki = torch.as_tensor(kidx, device=DEV)
+        g = s * n_kv + h
+        rows = torch.as_tensor(g * n_tok + kidx, device=DEV)
+        frac = _check_sampled(sp, codes[rows].cpu().numpy(), _np64(keys[s, h][ki]), kidx,
+                              _np64(queries[s, h * G:(h + 1) * G]),
+                              scores[g * G:(g + 1) * G][:, ki].cpu().numpy(),
+                              "long-context seq %d head %d" % (s, h))
+        assert frac > 0.99
+
+
+def test_retrieval_shape_full_with_topk():
+    W = workloads.RETRIEVAL
+    keys, queries = workloads.retrieval_inputs(DEV, n_keys=W["n_keys"], n_queries=W["n_queries"],
+                                               d=W["d"], seed=W["seed"])
+    n, d, k = W["n_keys"], W["d"], W["topk"]
+    plan = tq.tq_plan_create(d, W["bits"], W["seed"])
+    sp = otq.make_split_plan(d, W["bits"], W["seed"])
+    codes = tq.tq_encode(plan, keys)
+    scores = tq.tq_score(plan, queries, codes, n=n)
+    ids, vals = tq.tq_topk(scores, k)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4)
+    kidx = np.sort(rng.choice(n, 512, replace=False))
+    qidx = np.sort(rng.choice(W["n_queries"], 8, replace=False))
+    ki, qi = torch.as_tensor(kidx, device=DEV), torch.as_tensor(qidx, device=DEV)
+    frac = _check_sampled(sp, codes[ki].cpu().numpy(), _np64(keys[ki]), kidx, _np64(queries[qi]),
+                          scores[qi][:, ki].cpu().numpy(), "retrieval")
+    assert frac > 0.99
+    # top-k: values are the scores of the returned ids; the oracle's estimate of every
+    # returned id is at least the oracle's estimate of any sampled key minus the tolerance
+    ids_np, vals_np = ids.cpu().numpy(), vals.cpu().numpy()
+    sc_rows = scores[qi].cpu().numpy()
+    assert np.array_equal(vals_np[qidx], np.take_along_axis(sc_rows, ids_np[qidx], 1))
+    assert np.all(np.diff(vals_np, axis=1) <= 0)
+    for j, q in enumerate(qidx):
+        cand = np.concatenate([ids_np[q], kidx])
+        x = _np64(keys[torch.as_tensor(cand, device=DEV)])
+        est = otq.score_split(sp, [parity.stored(c) for c in otq.encode_split(sp, x)],
+                              _np64(queries[q:q + 1]))[0]
+        qn = float(np.linalg.norm(_np64(queries[q])))
+        kth = est[:k].min()
+        assert np.all(est[k:] <= kth + 2e-3 * qn), "query %d: a sampled key beats the top-%d" % (q, k)
+    # recall@10 of the estimate against exact fp32 inner products (reported)
+    exact = queries[qi] @ keys.T
+    top_exact = torch.topk(exact, k, dim=1).indices.cpu().numpy()
+    recall = np.mean([len(set(top_exact[j]) & set(ids_np[q])) / k for j, q in enumerate(qidx)])
+    print("recall@10 vs exact fp32 on %d queries: %.3f" % (len(qidx), recall))
+    assert recall > 0.5
