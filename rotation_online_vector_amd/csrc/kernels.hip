@@ -305,6 +305,317 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------- MFMA encode
+// For D <= 128 the rotation is applied as one dense, exact product on bf16 MFMA instead of
+// three Walsh-Hadamard rounds on the vector ALU (which, at 3 D log2 D additions per vector,
+// would bound the kernel well above the memory time):
+//     z_raw = K x,   K = H S3 H S2 H S1 = D^(3/2) Pi   (integers, |K| <= D^2 <= 2^14)
+// K is stored as two bf16 limbs that add up to it exactly; a bf16 input is its own exact
+// bf16 limb (an fp32 input is split exactly into three), and every product is exact in the
+// fp32 accumulator.  z = z_raw / ||z_raw|| (||z_raw|| = D^(3/2) ||x||).  The comparisons
+// run on z_raw against thresholds scaled by ||z_raw||, and the residual stays in the
+// accumulator registers, which are already laid out as the k values the QJL product needs
+// (its matrix columns are permuted to match on the host).
+//
+// Lane layout (16x16x32 bf16: A[row][k] and B[k][col] at lane row/col + 16 (k / 8)):
+// rotation tile = K rows (output coordinates) x x^T (16 vectors as columns); lane l then
+// holds vector l % 16 and coordinates 16 jt + 4 G + e (G = l / 16, e < 4) in tile jt.
+// A 32-coordinate code word g is spread over the 4 lane groups (tiles 2g, 2g+1) and is
+// assembled with two lane-group swaps.
+
+constexpr int kEncWaves = 8;
+
+__device__ __forceinline__ uint32_t or_over_lane_groups(uint32_t v) {
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  const uint32_t x = a[0] | a[1];
+  auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return b[0] | b[1];
+}
+
+__device__ __forceinline__ float sum_over_lane_groups(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  const float x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ bf16x8 bf16x8_from_words(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  const u32x4 u = {w0, w1, w2, w3};
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
+  const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)a);
+  const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)b);
+  return lo | (hi << 16);
+}
+
+// 8 consecutive input elements of one row (zero beyond d / past the last row), as XL exact
+// bf16 limbs packed two per word: limbs[l][w] holds elements 2w, 2w+1 of limb l.
+template <int XL>
+__device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0,
+                                        uint32_t (&limbs)[XL][4]) {
+  const SubDev& s = a.s;
+  float v[8];
+  if (row < a.n && a.vec_load && c0 + 8 <= s.d) {
+    if (a.is_bf16) {
+      const uint4 u = *reinterpret_cast<const uint4*>(
+          reinterpret_cast<const uint16_t*>(a.x) + row * a.ldx + c0);
+      if constexpr (XL == 1) {
+        limbs[0][0] = u.x; limbs[0][1] = u.y; limbs[0][2] = u.z; limbs[0][3] = u.w;
+        return;
+      }
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        v[2 * h] = __uint_as_float(w[h] << 16);
+        v[2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(
+          reinterpret_cast<const float*>(a.x) + row * a.ldx + c0);
+      const float4 u0 = p[0], u1 = p[1];
+      v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+      v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = c0 + e;
+      float val = 0.f;
+      if (row < a.n && i < s.d) {
+        const int64_t ch = s.chan ? s.chan[i] : i;
+        val = a.is_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.x)[row * a.ldx + ch])
+                        : reinterpret_cast<const float*>(a.x)[row * a.ldx + ch];
+      }
+      v[e] = val;
+    }
+  }
+  // exact split: truncate to 8 significant bits twice, the remainder fits the third limb
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    float r0 = v[2 * w], r1 = v[2 * w + 1];
+#pragma unroll
+    for (int l = 0; l < XL; ++l) {
+      uint32_t h0, h1;
+      if (l + 1 < XL) {
+        h0 = __float_as_uint(r0) >> 16;
+        h1 = __float_as_uint(r1) >> 16;
+        r0 -= __uint_as_float(h0 << 16);
+        r1 -= __uint_as_float(h1 << 16);
+      } else {
+        const uint32_t pk = pack_bf16_rne(r0, r1);
+        h0 = pk & 0xFFFFu;
+        h1 = pk >> 16;
+      }
+      limbs[l][w] = h0 | (h1 << 16);
+    }
+  }
+}
+
+template <int D, int R, int XL>
+__global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeArgs a) {
+  constexpr int NJT = D / 16;        // 16-row tiles of coordinates
+  constexpr int NKS = D / 32;        // 32-wide k steps
+  constexpr int NG = D / 32;         // code words per plane
+  constexpr int L = 1 << R;
+  constexpr int NP = 1 << (R - 1);
+  constexpr int NT = 2;              // 16-vector tiles per wave iteration
+  __shared__ uint4 kop[2 * NJT * NKS * 64];
+  __shared__ uint4 sop[NJT * NKS * 64];
+  const SubDev& s = a.s;
+  for (int i = threadIdx.x; i < 2 * NJT * NKS * 64; i += kEncWaves * kWave)
+    kop[i] = reinterpret_cast<const uint4*>(s.rotk)[i];
+  for (int i = threadIdx.x; i < NJT * NKS * 64; i += kEncWaves * kWave)
+    sop[i] = reinterpret_cast<const uint4*>(s.sperm)[i];
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, G = lane >> 4;
+  float thr[L - 1], coef[NP];
+  uint32_t pmask[NP];
+#pragma unroll
+  for (int j = 0; j < L - 1; ++j) thr[j] = s.thr[j];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) { coef[p] = s.coef[p]; pmask[p] = s.plane_mask[p]; }
+  const int recw = s.rec_sub / 4;
+
+  for (int64_t v0 = ((int64_t)blockIdx.x * kEncWaves + wave) * 16 * NT; v0 < a.n;
+       v0 += (int64_t)gridDim.x * kEncWaves * 16 * NT) {
+    // ---- x^T operands ----
+    uint32_t xw[NT][NKS][XL][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        uint32_t lb[XL][4];
+        load_x8<XL>(a, v0 + 16 * t + col, 32 * ks + 8 * G, lb);
+#pragma unroll
+        for (int l = 0; l < XL; ++l)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) xw[t][ks][l][w] = lb[l][w];
+      }
+    // ---- z_raw = K x ----
+    f32x4 acc[NT][NJT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) acc[t][jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) {
+        const uint4 uh = kop[(jt * NKS + ks) * 64 + lane];
+        const uint4 ul = kop[((NJT + jt) * NKS + ks) * 64 + lane];
+        const bf16x8 khi = bf16x8_from_words(uh.x, uh.y, uh.z, uh.w);
+        const bf16x8 klo = bf16x8_from_words(ul.x, ul.y, ul.z, ul.w);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int l = 0; l < XL; ++l) {
+            const bf16x8 xb = bf16x8_from_words(xw[t][ks][l][0], xw[t][ks][l][1],
+                                                xw[t][ks][l][2], xw[t][ks][l][3]);
+            acc[t][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, xb, acc[t][jt], 0, 0, 0);
+            if (l < 2)   // the low limbs' product is below fp32 resolution
+              acc[t][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(klo, xb, acc[t][jt], 0, 0, 0);
+          }
+        }
+        if (jt % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // bound the operands in flight
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- per vector: norm, bucketize, residual, index words, residual limbs ----
+    uint32_t words[NT][NG][R + 1];
+    float nrm[NT], gam[NT];
+    bf16x8 rhi[NT][NKS], rlo[NT][NKS];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float ss = 0.f;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ss = fmaf(acc[t][jt][e], acc[t][jt][e], ss);
+      const float zn = sqrtf(sum_over_lane_groups(ss));
+      const float sc = zn > 0.f ? zn : 1.f;
+      float T[L - 1], A[NP];
+#pragma unroll
+      for (int j = 0; j < L - 1; ++j) T[j] = thr[j] * sc;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) A[p] = coef[p] * sc;
+      uint32_t part[NG][R];
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int m = 0; m < R; ++m) part[g][m] = 0;
+      float g2 = 0.f;
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float z = acc[t][jt][e];
+          // binary search over the scaled thresholds: idx = #{T_j <= z}
+          int idx = 0;
+#pragma unroll
+          for (int m = R - 1; m >= 0; --m) {
+            float tsel = T[(1 << m) - 1];
+#pragma unroll
+            for (int k = 1; k < (L >> (m + 1)); ++k)
+              tsel = (idx == (k << (m + 1))) ? T[(k << (m + 1)) + (1 << m) - 1] : tsel;
+            idx |= (z >= tsel ? 1 : 0) << m;
+          }
+          // level = sum over odd parity planes of +-A_p
+          float lv = 0.f;
+#pragma unroll
+          for (int p = 0; p < NP; ++p) {
+            const uint32_t par = __builtin_popcount((uint32_t)idx & pmask[p]) & 1u;
+            lv += par ? A[p] : -A[p];
+          }
+          const float r = z - lv;
+          g2 = fmaf(r, r, g2);
+          acc[t][jt][e] = r;
+#pragma unroll
+          for (int m = 0; m < R; ++m)
+            part[jt >> 1][m] |= (uint32_t)((idx >> m) & 1) << (16 * (jt & 1) + e);
+        }
+      }
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int m = 0; m < R; ++m) words[t][g][m] = or_over_lane_groups(part[g][m] << (4 * G));
+      const float rn = sqrtf(sum_over_lane_groups(g2));
+      nrm[t] = zn * s.inv_scale;
+      gam[t] = rn / sc;
+      // residual limbs, k element e' of step ks = tile 2 ks + e'/4, element e' % 4
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int e0 = 2 * w, e1 = 2 * w + 1;
+          const float r0 = acc[t][2 * ks + (e0 >> 2)][e0 & 3];
+          const float r1 = acc[t][2 * ks + (e1 >> 2)][e1 & 3];
+          const uint32_t hp = pack_bf16_rne(r0, r1);
+          hw[w] = hp;
+          lw[w] = pack_bf16_rne(r0 - __uint_as_float(hp << 16), r1 - __uint_as_float(hp & 0xFFFF0000u));
+        }
+        rhi[t][ks] = bf16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
+        rlo[t][ks] = bf16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // ---- QJL: P^T = S_perm R^T, signs; one code word (two row tiles) at a time ----
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      f32x4 qa[NT][2];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) { qa[t][0] = (f32x4){0.f, 0.f, 0.f, 0.f}; qa[t][1] = qa[t][0]; }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const uint4 us = sop[((2 * g + h) * NKS + ks) * 64 + lane];
+          const bf16x8 sa = bf16x8_from_words(us.x, us.y, us.z, us.w);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            qa[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa, rhi[t][ks], qa[t][h], 0, 0, 0);
+            qa[t][h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(sa, rlo[t][ks], qa[t][h], 0, 0, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        uint32_t part = 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) part |= (uint32_t)(qa[t][h][e] >= 0.f ? 1 : 0) << (16 * h + e);
+        words[t][g][R] = or_over_lane_groups(part << (4 * G));
+      }
+    }
+    // ---- store: lane group G writes code word G of its vector, group 0 the norms ----
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t row = v0 + 16 * t + col;
+      if (row < a.n) {
+        uint32_t* rec = reinterpret_cast<uint32_t*>(a.codes + row * a.rec_bytes + s.rec_off);
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+          if (g == G) {
+#pragma unroll
+            for (int m = 0; m <= R; ++m) rec[g * (R + 1) + m] = words[t][g][m];
+          }
+        if (G == 0) {
+          rec[NG * (R + 1)] = __float_as_uint(nrm[t]);
+          rec[NG * (R + 1) + 1] = __float_as_uint(gam[t]);
+        }
+      }
+    }
+    (void)recw;
+  }
+}
+
 // Standalone QJL stage: residuals already rotated, fp32 [n][D] -> sign words [n][D/32].
 template <int D>
 __global__ void __launch_bounds__(kBlock) qjl_kernel(SubDev s, const float* r, int64_t n,
@@ -822,6 +1133,36 @@ static int launch_encode_d(const EncodeArgs& ea, hipStream_t st) {
   return hip_rc(hipGetLastError());
 }
 
+template <int D, int XL>
+static void launch_encode_mfma_dx(const EncodeArgs& ea, hipStream_t st, dim3 grid) {
+  const dim3 block(kEncWaves * kWave);
+  switch (ea.s.R) {
+    case 1: hipLaunchKernelGGL((encode_mfma_kernel<D, 1, XL>), grid, block, 0, st, ea); break;
+    case 2: hipLaunchKernelGGL((encode_mfma_kernel<D, 2, XL>), grid, block, 0, st, ea); break;
+    case 3: hipLaunchKernelGGL((encode_mfma_kernel<D, 3, XL>), grid, block, 0, st, ea); break;
+    case 4: hipLaunchKernelGGL((encode_mfma_kernel<D, 4, XL>), grid, block, 0, st, ea); break;
+  }
+}
+
+static int launch_encode_mfma(const EncodeArgs& ea, hipStream_t st) {
+  // one wave iteration encodes 32 vectors; enough blocks to fill the chip a few times over,
+  // each looping over its share
+  const int64_t iters = (ea.n + 31) / 32;
+  int64_t blocks = (iters + kEncWaves - 1) / kEncWaves;
+  if (blocks > 2048) blocks = 2048;
+  const dim3 grid((unsigned)blocks);
+  switch (ea.s.D * 2 + ea.is_bf16) {
+    case 32 * 2 + 1: launch_encode_mfma_dx<32, 1>(ea, st, grid); break;
+    case 32 * 2: launch_encode_mfma_dx<32, 3>(ea, st, grid); break;
+    case 64 * 2 + 1: launch_encode_mfma_dx<64, 1>(ea, st, grid); break;
+    case 64 * 2: launch_encode_mfma_dx<64, 3>(ea, st, grid); break;
+    case 128 * 2 + 1: launch_encode_mfma_dx<128, 1>(ea, st, grid); break;
+    case 128 * 2: launch_encode_mfma_dx<128, 3>(ea, st, grid); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return hip_rc(hipGetLastError());
+}
+
 int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, int64_t ldx,
                   uint8_t* codes, void* stream) {
   if (n == 0) return 0;
@@ -836,6 +1177,7 @@ int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, i
   const int es = ea.is_bf16 ? 2 : 4;
   ea.vec_load = (ea.s.chan == nullptr) && ((uintptr_t)x % 16 == 0) && ((ldx * es) % 16 == 0);
   hipStream_t st = (hipStream_t)stream;
+  if (ea.s.D <= 128 && ea.s.rotk) return launch_encode_mfma(ea, st);
   switch (ea.s.D) {
     case 32: return launch_encode_d<32>(ea, st);
     case 64: return launch_encode_d<64>(ea, st);

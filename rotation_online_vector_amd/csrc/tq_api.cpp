@@ -46,7 +46,65 @@ struct SubHost {
   std::vector<double> lev, thr;
   std::vector<uint32_t> signs;   // [3][D/32]
   std::vector<uint16_t> S;       // [D][D]
+  std::vector<uint16_t> rotk;    // MFMA operand tables (D <= 128)
+  std::vector<uint16_t> sperm;
 };
+
+constexpr int kMfmaMaxD = 128;
+
+// The rotation as an integer matrix: K = H S3 H S2 H S1 = D^(3/2) Pi (H the Sylvester
+// Hadamard matrix, S_r the +-1 diagonals), column i = the transform of e_i.  |K| <= D^2.
+std::vector<int64_t> rotation_integer_matrix(const std::vector<uint32_t>& signs, int D) {
+  std::vector<int64_t> K((size_t)D * D);
+  std::vector<int64_t> v(D);
+  for (int i = 0; i < D; ++i) {
+    for (int j = 0; j < D; ++j) v[j] = (j == i);
+    for (int r = 0; r < 3; ++r) {
+      for (int j = 0; j < D; ++j)
+        if ((signs[r * (D / 32) + j / 32] >> (j % 32)) & 1u) v[j] = -v[j];
+      for (int h = 1; h < D; h <<= 1)
+        for (int a = 0; a < D; a += 2 * h)
+          for (int b = a; b < a + h; ++b) {
+            const int64_t x = v[b], y = v[b + h];
+            v[b] = x + y;
+            v[b + h] = x - y;
+          }
+    }
+    for (int j = 0; j < D; ++j) K[(size_t)j * D + i] = v[j];
+  }
+  return K;
+}
+
+// Operand tables of the MFMA encode (16x16x32 bf16: lane l holds row l%16 and the 8
+// consecutive k values 8*(l/16)..+7 of a 32-wide k step).
+//  rotk: K split into two bf16 limbs (exact: |K| <= 2^14 for D <= 128), row tiles of 16
+//        output coordinates, k steps of 32 input coordinates.
+//  sperm: S with its columns permuted so that k element e of lane group G in step ks is
+//        input coordinate 32 ks + 4 G + e (e < 4) or 32 ks + 16 + 4 G + (e - 4): the
+//        coordinates a lane holds after the rotation tile products.
+void mfma_operand_tables(SubHost& h) {
+  const int D = h.D, NJT = D / 16, NKS = D / 32;
+  const std::vector<int64_t> K = rotation_integer_matrix(h.signs, D);
+  h.rotk.assign((size_t)2 * NJT * NKS * 64 * 8, 0);
+  h.sperm.assign((size_t)NJT * NKS * 64 * 8, 0);
+  for (int jt = 0; jt < NJT; ++jt)
+    for (int ks = 0; ks < NKS; ++ks)
+      for (int l = 0; l < 64; ++l)
+        for (int e = 0; e < 8; ++e) {
+          const int row = 16 * jt + l % 16, G = l / 16;
+          const double kv = (double)K[(size_t)row * D + 32 * ks + 8 * G + e];
+          const uint16_t hi = bf16_rne_from_double(kv);
+          uint32_t hb = (uint32_t)hi << 16;
+          float hf;
+          memcpy(&hf, &hb, 4);
+          const uint16_t lo = bf16_rne_from_double(kv - (double)hf);
+          const size_t at = (((size_t)jt * NKS + ks) * 64 + l) * 8 + e;
+          h.rotk[at] = hi;
+          h.rotk[(size_t)NJT * NKS * 64 * 8 + at] = lo;
+          const int col = 32 * ks + 4 * G + (e < 4 ? e : 12 + e);
+          h.sperm[at] = h.S[(size_t)row * D + col];
+        }
+}
 
 // Coefficients a_S of the parity planes of odd subsets S of the R index bits:
 // c[idx] = sum_S a_S * chi_S(idx), chi_S = prod_{m in S} (2 b_m - 1), exact for a
@@ -166,6 +224,7 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
   // host tables and device layout
   size_t bytes = 0;
   size_t off_sign[2] = {0, 0}, off_S[2] = {0, 0}, off_chan[2] = {0, 0};
+  size_t off_rotk[2] = {0, 0}, off_sperm[2] = {0, 0};
   auto take = [&](size_t b) { size_t o = bytes; bytes += (b + 255) / 256 * 256; return o; };
   for (int i = 0; i < pd.nsub; ++i) {
     SubHost& h = subs[i];
@@ -198,6 +257,11 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
     off_sign[i] = take(h.signs.size() * 4);
     off_S[i] = take(h.S.size() * 2);
     if (!h.chan.empty()) off_chan[i] = take(h.chan.size() * 4);
+    if (h.D <= kMfmaMaxD) {
+      mfma_operand_tables(h);
+      off_rotk[i] = take(h.rotk.size() * 2);
+      off_sperm[i] = take(h.sperm.size() * 2);
+    }
   }
   void* mem = nullptr;
   hipError_t e = hipMalloc(&mem, bytes);
@@ -215,6 +279,10 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
       e = hipMemcpy(base + off_S[i], h.S.data(), h.S.size() * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess && !h.chan.empty())
       e = hipMemcpy(base + off_chan[i], h.chan.data(), h.chan.size() * 4, hipMemcpyHostToDevice);
+    if (e == hipSuccess && !h.rotk.empty())
+      e = hipMemcpy(base + off_rotk[i], h.rotk.data(), h.rotk.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && !h.sperm.empty())
+      e = hipMemcpy(base + off_sperm[i], h.sperm.data(), h.sperm.size() * 2, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(mem);
       delete plan;
@@ -223,6 +291,8 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
     s.signs = reinterpret_cast<const uint32_t*>(base + off_sign[i]);
     s.S = reinterpret_cast<const uint16_t*>(base + off_S[i]);
     s.chan = h.chan.empty() ? nullptr : reinterpret_cast<const int32_t*>(base + off_chan[i]);
+    s.rotk = h.rotk.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_rotk[i]);
+    s.sperm = h.sperm.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_sperm[i]);
   }
   *out = plan;
   return TQ_OK;
