@@ -318,10 +318,11 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
 // (its matrix columns are permuted to match on the host).
 //
 // Lane layout (16x16x32 bf16: A[row][k] and B[k][col] at lane row/col + 16 (k / 8)):
-// rotation tile = K rows (output coordinates) x x^T (16 vectors as columns); lane l then
-// holds vector l % 16 and coordinates 16 jt + 4 G + e (G = l / 16, e < 4) in tile jt.
-// A 32-coordinate code word g is spread over the 4 lane groups (tiles 2g, 2g+1) and is
-// assembled with two lane-group swaps.
+// rotation tile = K rows (output coordinates) x x^T (16 vectors as columns).  The host
+// permutes K's rows so that lane l then holds vector l % 16 and coordinates
+// G D/4 + 4 jt + e (G = l / 16, tile jt, e < 4): a lane group holds D/4 consecutive
+// coordinates, i.e. one whole code word at D = 128 (two or four lane groups share a word at
+// D = 64 or 32 and are combined with lane-group swaps).  The QJL rows are permuted alike.
 
 constexpr int kEncWaves = 8;
 
@@ -346,32 +347,35 @@ __device__ __forceinline__ bf16x8 bf16x8_from_words(uint32_t w0, uint32_t w1, ui
 }
 
 __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
-  const uint32_t lo = __builtin_bit_cast(uint16_t, (__bf16)a);
-  const uint32_t hi = __builtin_bit_cast(uint16_t, (__bf16)b);
-  return lo | (hi << 16);
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+#define pack2_bf16 pack_bf16_rne
 
 // 8 consecutive input elements of one row (zero beyond d / past the last row), as XL exact
 // bf16 limbs packed two per word: limbs[l][w] holds elements 2w, 2w+1 of limb l.
-template <int XL>
+// VEC: rows are 16-byte aligned, d = D and no channel gather, so every lane's 8 elements
+// are one vector load (rows past the end read as zero); otherwise element-wise.
+template <int XL, bool VEC>
 __device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0,
                                         uint32_t (&limbs)[XL][4]) {
   const SubDev& s = a.s;
   float v[8];
-  if (row < a.n && a.vec_load && c0 + 8 <= s.d) {
-    if (a.is_bf16) {
+  if (VEC) {
+    if (row >= a.n) {
+#pragma unroll
+      for (int l = 0; l < XL; ++l)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) limbs[l][w] = 0;
+      return;
+    }
+    if constexpr (XL == 1) {       // bf16 input: its own exact limb
       const uint4 u = *reinterpret_cast<const uint4*>(
           reinterpret_cast<const uint16_t*>(a.x) + row * a.ldx + c0);
-      if constexpr (XL == 1) {
-        limbs[0][0] = u.x; limbs[0][1] = u.y; limbs[0][2] = u.z; limbs[0][3] = u.w;
-        return;
-      }
-      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        v[2 * h] = __uint_as_float(w[h] << 16);
-        v[2 * h + 1] = __uint_as_float(w[h] & 0xFFFF0000u);
-      }
+      limbs[0][0] = u.x; limbs[0][1] = u.y; limbs[0][2] = u.z; limbs[0][3] = u.w;
+      return;
     } else {
       const float4* p = reinterpret_cast<const float4*>(
           reinterpret_cast<const float*>(a.x) + row * a.ldx + c0);
@@ -414,13 +418,65 @@ __device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0
   }
 }
 
-template <int D, int R, int XL>
+// The p-th odd-popcount subset of R index bits, in increasing order (the order in which
+// the host lists the parity planes and their coefficients).
+template <int R>
+__host__ __device__ constexpr uint32_t pmask_c(int p) {
+  int n = 0;
+  for (uint32_t S = 1; S < (1u << R); ++S) {
+    if (__builtin_popcount(S) % 2 == 0) continue;
+    if (n == p) return S;
+    ++n;
+  }
+  return 0;
+}
+
+// Two-bit Lloyd-Max step for one coordinate z (thresholds t0 < t1 < t2, levels l0..l3, all
+// pre-scaled): idx = #{t_j <= z} by a two-level binary search, each index bit shifted into
+// n1 / n0 (n = 2 n + bit, carry-in from the comparison mask), residual r = z - l[idx].
+// Written as one fixed VALU sequence: the compiler otherwise rebuilds the selects into an
+// integer index and compare chains.
+__device__ __forceinline__ float bucket2(float z, float t0, float t1, float t2, float l0, float l1,
+                                         float l2, float l3, uint32_t& n1, uint32_t& n0) {
+  float tsel, la, lb, lv, r;
+  uint64_t m;
+  asm("v_cmp_ge_f32_e64 %[m], %[z], %[t1]\n\t"
+      "v_cndmask_b32_e64 %[tsel], %[t0], %[t2], %[m]\n\t"
+      "v_cndmask_b32_e64 %[la], %[l0], %[l2], %[m]\n\t"
+      "v_cndmask_b32_e64 %[lb], %[l1], %[l3], %[m]\n\t"
+      "v_addc_co_u32_e64 %[n1], %[m], %[n1], %[n1], %[m]\n\t"
+      "v_cmp_ge_f32_e64 %[m], %[z], %[tsel]\n\t"
+      "v_cndmask_b32_e64 %[lv], %[la], %[lb], %[m]\n\t"
+      "v_addc_co_u32_e64 %[n0], %[m], %[n0], %[n0], %[m]\n\t"
+      "v_sub_f32_e32 %[r], %[z], %[lv]"
+      : [m] "=&s"(m), [tsel] "=&v"(tsel), [la] "=&v"(la), [lb] "=&v"(lb), [lv] "=&v"(lv),
+        [r] "=&v"(r), [n1] "+v"(n1), [n0] "+v"(n0)
+      : [z] "v"(z), [t0] "v"(t0), [t1] "v"(t1), [t2] "v"(t2), [l0] "v"(l0), [l1] "v"(l1),
+        [l2] "v"(l2), [l3] "v"(l3));
+  return r;
+}
+
+// A lane's partial code word holds its D/4 bits at the top of the order fed (bit 0 = its
+// first coordinate); place it at its offset in the 32-bit word and merge the lane groups
+// that share the word (D = 64: pairs, D = 32: all four).
+template <int D>
+__device__ __forceinline__ uint32_t combine_word(uint32_t part, int G) {
+  if constexpr (D >= 128) {
+    return part;
+  } else if constexpr (D == 64) {
+    const uint32_t v = part << (16 * (G & 1));
+    auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return a[0] | a[1];
+  } else {
+    return or_over_lane_groups(part << (8 * G));
+  }
+}
+
+template <int D, int R, int XL, bool VEC>
 __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeArgs a) {
   constexpr int NJT = D / 16;        // 16-row tiles of coordinates
   constexpr int NKS = D / 32;        // 32-wide k steps
-  constexpr int NG = D / 32;         // code words per plane
   constexpr int L = 1 << R;
-  constexpr int NP = 1 << (R - 1);
   constexpr int NT = 2;              // 16-vector tiles per wave iteration
   __shared__ uint4 kop[2 * NJT * NKS * 64];
   __shared__ uint4 sop[NJT * NKS * 64];
@@ -433,12 +489,11 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, G = lane >> 4;
-  float thr[L - 1], coef[NP];
-  uint32_t pmask[NP];
+  float thr[L - 1], lev[L];
 #pragma unroll
   for (int j = 0; j < L - 1; ++j) thr[j] = s.thr[j];
 #pragma unroll
-  for (int p = 0; p < NP; ++p) { coef[p] = s.coef[p]; pmask[p] = s.plane_mask[p]; }
+  for (int j = 0; j < L; ++j) lev[j] = s.lev[j];
   const int recw = s.rec_sub / 4;
 
   for (int64_t v0 = ((int64_t)blockIdx.x * kEncWaves + wave) * 16 * NT; v0 < a.n;
@@ -450,7 +505,7 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         uint32_t lb[XL][4];
-        load_x8<XL>(a, v0 + 16 * t + col, 32 * ks + 8 * G, lb);
+        load_x8<XL, VEC>(a, v0 + 16 * t + col, 32 * ks + 8 * G, lb);
 #pragma unroll
         for (int l = 0; l < XL; ++l)
 #pragma unroll
@@ -486,7 +541,7 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
     }
     __builtin_amdgcn_sched_barrier(0);
     // ---- per vector: norm, bucketize, residual, index words, residual limbs ----
-    uint32_t words[NT][NG][R + 1];
+    uint32_t words[NT][R + 1];          // this lane group's code word of each plane
     float nrm[NT], gam[NT];
     bf16x8 rhi[NT][NKS], rlo[NT][NKS];
 #pragma unroll
@@ -498,51 +553,61 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
         for (int e = 0; e < 4; ++e) ss = fmaf(acc[t][jt][e], acc[t][jt][e], ss);
       const float zn = sqrtf(sum_over_lane_groups(ss));
       const float sc = zn > 0.f ? zn : 1.f;
-      float T[L - 1], A[NP];
+      // thresholds as a complete binary search tree (root = middle) and the levels, both
+      // scaled by ||z_raw||; each comparison halves both arrays with one select per entry
+      float Ts[L - 1], Ls[L];
 #pragma unroll
-      for (int j = 0; j < L - 1; ++j) T[j] = thr[j] * sc;
+      for (int j = 0; j < L - 1; ++j) Ts[j] = thr[j] * sc;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) A[p] = coef[p] * sc;
-      uint32_t part[NG][R];
-#pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int m = 0; m < R; ++m) part[g][m] = 0;
+      for (int j = 0; j < L; ++j) Ls[j] = lev[j] * sc;
       float g2 = 0.f;
+      // this lane's D/4 coordinates sit at bits 4 jt + e of its part of a code word
+      uint32_t part[R];
+#pragma unroll
+      for (int m = 0; m < R; ++m) part[m] = 0;
 #pragma unroll
       for (int jt = 0; jt < NJT; ++jt) {
+        uint32_t nib[R];
+#pragma unroll
+        for (int m = 0; m < R; ++m) nib[m] = 0;
+        if constexpr (R == 2) {
+#pragma unroll
+          for (int e = 3; e >= 0; --e) {     // highest bit first: nib = 2 nib + bit
+            const float r = bucket2(acc[t][jt][e], Ts[0], Ts[1], Ts[2], Ls[0], Ls[1], Ls[2], Ls[3],
+                                    nib[1], nib[0]);
+            g2 = fmaf(r, r, g2);
+            acc[t][jt][e] = r;
+          }
+        } else
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float z = acc[t][jt][e];
-          // binary search over the scaled thresholds: idx = #{T_j <= z}
-          int idx = 0;
+          float tc[L - 1], lc[L];
+#pragma unroll
+          for (int j = 0; j < L - 1; ++j) tc[j] = Ts[j];
+#pragma unroll
+          for (int j = 0; j < L; ++j) lc[j] = Ls[j];
 #pragma unroll
           for (int m = R - 1; m >= 0; --m) {
-            float tsel = T[(1 << m) - 1];
+            const int half = 1 << m;                    // thresholds left: 2 half - 1
+            const bool b = z >= tc[half - 1];
 #pragma unroll
-            for (int k = 1; k < (L >> (m + 1)); ++k)
-              tsel = (idx == (k << (m + 1))) ? T[(k << (m + 1)) + (1 << m) - 1] : tsel;
-            idx |= (z >= tsel ? 1 : 0) << m;
-          }
-          // level = sum over odd parity planes of +-A_p
-          float lv = 0.f;
+            for (int j = 0; j < half - 1; ++j) tc[j] = b ? tc[half + j] : tc[j];
 #pragma unroll
-          for (int p = 0; p < NP; ++p) {
-            const uint32_t par = __builtin_popcount((uint32_t)idx & pmask[p]) & 1u;
-            lv += par ? A[p] : -A[p];
+            for (int j = 0; j < half; ++j) lc[j] = b ? lc[half + j] : lc[j];
+            nib[m] |= (b ? 1u : 0u) << e;
           }
-          const float r = z - lv;
+          const float r = z - lc[0];
           g2 = fmaf(r, r, g2);
           acc[t][jt][e] = r;
-#pragma unroll
-          for (int m = 0; m < R; ++m)
-            part[jt >> 1][m] |= (uint32_t)((idx >> m) & 1) << (16 * (jt & 1) + e);
         }
+#pragma unroll
+        for (int m = 0; m < R; ++m) part[m] |= nib[m] << (4 * jt);
+        // keep the comparison masks of one tile at a time live (scalar registers)
+        __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
-#pragma unroll
-        for (int m = 0; m < R; ++m) words[t][g][m] = or_over_lane_groups(part[g][m] << (4 * G));
+      for (int m = 0; m < R; ++m) words[t][m] = combine_word<D>(part[m], G);
       const float rn = sqrtf(sum_over_lane_groups(g2));
       nrm[t] = zn * s.inv_scale;
       gam[t] = rn / sc;
@@ -555,26 +620,31 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
           const int e0 = 2 * w, e1 = 2 * w + 1;
           const float r0 = acc[t][2 * ks + (e0 >> 2)][e0 & 3];
           const float r1 = acc[t][2 * ks + (e1 >> 2)][e1 & 3];
-          const uint32_t hp = pack_bf16_rne(r0, r1);
+          const uint32_t hp = pack2_bf16(r0, r1);
           hw[w] = hp;
-          lw[w] = pack_bf16_rne(r0 - __uint_as_float(hp << 16), r1 - __uint_as_float(hp & 0xFFFF0000u));
+          lw[w] = pack2_bf16(r0 - __uint_as_float(hp << 16), r1 - __uint_as_float(hp & 0xFFFF0000u));
         }
         rhi[t][ks] = bf16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
         rlo[t][ks] = bf16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- QJL: P^T = S_perm R^T, signs; one code word (two row tiles) at a time ----
+    // ---- QJL: P^T = S_perm R^T and its signs, four row tiles at a time ----
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-      f32x4 qa[NT][2];
+    for (int t = 0; t < NT; ++t) words[t][R] = 0;
 #pragma unroll
-      for (int t = 0; t < NT; ++t) { qa[t][0] = (f32x4){0.f, 0.f, 0.f, 0.f}; qa[t][1] = qa[t][0]; }
+    for (int jq = NJT - 4 < 0 ? 0 : NJT - 4; jq >= 0; jq -= 4) {
+      constexpr int NQ = NJT < 4 ? NJT : 4;
+      f32x4 qa[NT][NQ];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int h = 0; h < NQ; ++h) qa[t][h] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const uint4 us = sop[((2 * g + h) * NKS + ks) * 64 + lane];
+        for (int h = 0; h < NQ; ++h) {
+          const uint4 us = sop[((jq + h) * NKS + ks) * 64 + lane];
           const bf16x8 sa = bf16x8_from_words(us.x, us.y, us.z, us.w);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
@@ -585,30 +655,31 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
         __builtin_amdgcn_sched_barrier(0);
       }
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        uint32_t part = 0;
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < NQ; ++h) {
+          uint32_t nib = 0;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) part |= (uint32_t)(qa[t][h][e] >= 0.f ? 1 : 0) << (16 * h + e);
-        words[t][g][R] = or_over_lane_groups(part << (4 * G));
-      }
+          for (int e = 0; e < 4; ++e) nib |= (qa[t][h][e] >= 0.f ? 1u : 0u) << e;
+          words[t][R] |= nib << (4 * (jq + h));
+        }
     }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) words[t][R] = combine_word<D>(words[t][R], G);
     // ---- store: lane group G writes code word G of its vector, group 0 the norms ----
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int64_t row = v0 + 16 * t + col;
       if (row < a.n) {
         uint32_t* rec = reinterpret_cast<uint32_t*>(a.codes + row * a.rec_bytes + s.rec_off);
+        if ((G * (D / 4)) % 32 == 0) {          // first lane group of its code word
+          const int g = G * D / 128;
 #pragma unroll
-        for (int g = 0; g < NG; ++g)
-          if (g == G) {
-#pragma unroll
-            for (int m = 0; m <= R; ++m) rec[g * (R + 1) + m] = words[t][g][m];
-          }
+          for (int m = 0; m <= R; ++m) rec[g * (R + 1) + m] = words[t][m];
+        }
         if (G == 0) {
-          rec[NG * (R + 1)] = __float_as_uint(nrm[t]);
-          rec[NG * (R + 1) + 1] = __float_as_uint(gam[t]);
+          rec[(D / 32) * (R + 1)] = __float_as_uint(nrm[t]);
+          rec[(D / 32) * (R + 1) + 1] = __float_as_uint(gam[t]);
         }
       }
     }
@@ -1133,15 +1204,23 @@ static int launch_encode_d(const EncodeArgs& ea, hipStream_t st) {
   return hip_rc(hipGetLastError());
 }
 
-template <int D, int XL>
-static void launch_encode_mfma_dx(const EncodeArgs& ea, hipStream_t st, dim3 grid) {
+template <int D, int XL, bool VEC>
+static void launch_encode_mfma_dxv(const EncodeArgs& ea, hipStream_t st, dim3 grid) {
   const dim3 block(kEncWaves * kWave);
   switch (ea.s.R) {
-    case 1: hipLaunchKernelGGL((encode_mfma_kernel<D, 1, XL>), grid, block, 0, st, ea); break;
-    case 2: hipLaunchKernelGGL((encode_mfma_kernel<D, 2, XL>), grid, block, 0, st, ea); break;
-    case 3: hipLaunchKernelGGL((encode_mfma_kernel<D, 3, XL>), grid, block, 0, st, ea); break;
-    case 4: hipLaunchKernelGGL((encode_mfma_kernel<D, 4, XL>), grid, block, 0, st, ea); break;
+    case 1: hipLaunchKernelGGL((encode_mfma_kernel<D, 1, XL, VEC>), grid, block, 0, st, ea); break;
+    case 2: hipLaunchKernelGGL((encode_mfma_kernel<D, 2, XL, VEC>), grid, block, 0, st, ea); break;
+    case 3: hipLaunchKernelGGL((encode_mfma_kernel<D, 3, XL, VEC>), grid, block, 0, st, ea); break;
+    case 4: hipLaunchKernelGGL((encode_mfma_kernel<D, 4, XL, VEC>), grid, block, 0, st, ea); break;
   }
+}
+
+template <int D, int XL>
+static void launch_encode_mfma_dx(const EncodeArgs& ea, hipStream_t st, dim3 grid) {
+  if (ea.vec_load && ea.s.d == D)
+    launch_encode_mfma_dxv<D, XL, true>(ea, st, grid);
+  else
+    launch_encode_mfma_dxv<D, XL, false>(ea, st, grid);
 }
 
 static int launch_encode_mfma(const EncodeArgs& ea, hipStream_t st) {

@@ -76,12 +76,18 @@ std::vector<int64_t> rotation_integer_matrix(const std::vector<uint32_t>& signs,
 }
 
 // Operand tables of the MFMA encode (16x16x32 bf16: lane l holds row l%16 and the 8
-// consecutive k values 8*(l/16)..+7 of a 32-wide k step).
-//  rotk: K split into two bf16 limbs (exact: |K| <= 2^14 for D <= 128), row tiles of 16
-//        output coordinates, k steps of 32 input coordinates.
-//  sperm: S with its columns permuted so that k element e of lane group G in step ks is
-//        input coordinate 32 ks + 4 G + e (e < 4) or 32 ks + 16 + 4 G + (e - 4): the
-//        coordinates a lane holds after the rotation tile products.
+// consecutive k values 8*(l/16)..+7 of a 32-wide k step; the 16x16 result puts row
+// 4*(l/16) + e of a tile in lane l).  Output rows are permuted so that lane group G of
+// tile jt, element e, receives coordinate G*D/4 + 4*jt + e: each lane group then holds D/4
+// consecutive coordinates, a whole 32-bit code word when D = 128.
+//  rotk: K (rows permuted as above) split into two bf16 limbs (exact: |K| <= 2^14 for
+//        D <= 128); k steps of 32 input coordinates.
+//  sperm: S with rows permuted the same way and columns ordered as the residual registers:
+//        k element e of lane group G in step ks is coordinate G*D/4 + 8*ks + e.
+int permuted_row(int D, int tile, int row_in_tile) {
+  return (row_in_tile / 4) * (D / 4) + 4 * tile + row_in_tile % 4;
+}
+
 void mfma_operand_tables(SubHost& h) {
   const int D = h.D, NJT = D / 16, NKS = D / 32;
   const std::vector<int64_t> K = rotation_integer_matrix(h.signs, D);
@@ -91,7 +97,7 @@ void mfma_operand_tables(SubHost& h) {
     for (int ks = 0; ks < NKS; ++ks)
       for (int l = 0; l < 64; ++l)
         for (int e = 0; e < 8; ++e) {
-          const int row = 16 * jt + l % 16, G = l / 16;
+          const int row = permuted_row(D, jt, l % 16), G = l / 16;
           const double kv = (double)K[(size_t)row * D + 32 * ks + 8 * G + e];
           const uint16_t hi = bf16_rne_from_double(kv);
           uint32_t hb = (uint32_t)hi << 16;
@@ -101,7 +107,7 @@ void mfma_operand_tables(SubHost& h) {
           const size_t at = (((size_t)jt * NKS + ks) * 64 + l) * 8 + e;
           h.rotk[at] = hi;
           h.rotk[(size_t)NJT * NKS * 64 * 8 + at] = lo;
-          const int col = 32 * ks + 4 * G + (e < 4 ? e : 12 + e);
+          const int col = G * (D / 4) + 8 * ks + e;
           h.sperm[at] = h.S[(size_t)row * D + col];
         }
 }
