@@ -31,6 +31,19 @@ __device__ __forceinline__ float flip_sign(float v, uint32_t bit) {
   return __uint_as_float(__float_as_uint(v) ^ (bit << 31));
 }
 
+// The p-th odd-popcount subset of R index bits, in increasing order (the order in which
+// the host lists the parity planes and their coefficients).
+template <int R>
+__host__ __device__ constexpr uint32_t pmask_c(int p) {
+  int n = 0;
+  for (uint32_t S = 1; S < (1u << R); ++S) {
+    if (__builtin_popcount(S) % 2 == 0) continue;
+    if (n == p) return S;
+    ++n;
+  }
+  return 0;
+}
+
 // ============================================================================ encode
 // Norm split, rotation z = Pi x / ||x|| with Pi = Ht S3 Ht S2 Ht S1 (TurboQuant technical
 // overview §2.1.1-2.1.2; diagonal then transform, three rounds), Lloyd-Max bucketize
@@ -418,19 +431,6 @@ __device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0
   }
 }
 
-// The p-th odd-popcount subset of R index bits, in increasing order (the order in which
-// the host lists the parity planes and their coefficients).
-template <int R>
-__host__ __device__ constexpr uint32_t pmask_c(int p) {
-  int n = 0;
-  for (uint32_t S = 1; S < (1u << R); ++S) {
-    if (__builtin_popcount(S) % 2 == 0) continue;
-    if (n == p) return S;
-    ++n;
-  }
-  return 0;
-}
-
 // Two-bit Lloyd-Max step for one coordinate z (thresholds t0 < t1 < t2, levels l0..l3, all
 // pre-scaled): idx = #{t_j <= z} by a two-level binary search, each index bit shifted into
 // n1 / n0 (n = 2 n + bit, carry-in from the comparison mask), residual r = z - l[idx].
@@ -786,32 +786,6 @@ __global__ void __launch_bounds__(kBlock) qprep_kernel(QPrepArgs a) {
   }
 }
 
-// fp8 e4m3 (bias 7, max 448, no infinities) encode with round-to-nearest-even, and decode.
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  float a = fabsf(v);
-  if (a == 0.f) return sign;
-  if (a >= 448.f) return sign | 0x7Eu;
-  int ex;
-  frexpf(a, &ex);                  // a = m 2^ex, m in [0.5, 1)
-  int e = ex - 1;                  // a = 1.f * 2^e
-  if (e < -6) {                    // subnormal: multiples of 2^-9
-    const int q = (int)rintf(ldexpf(a, 9));
-    return sign | (uint32_t)q;     // q == 8 is the smallest normal, encoded the same way
-  }
-  int m = (int)rintf((ldexpf(a, -e) - 1.f) * 8.f);
-  if (m == 8) { m = 0; e += 1; }
-  if (e > 8) return sign | 0x7Eu;
-  return sign | (uint32_t)((e + 7) << 3) | (uint32_t)m;
-}
-
-__device__ __forceinline__ float e4m3_decode(uint32_t b) {
-  const float sgn = (b & 0x80u) ? -1.f : 1.f;
-  const int e = (b >> 3) & 15, m = b & 7;
-  const float mag = e == 0 ? ldexpf((float)m, -9) : ldexpf(1.f + m / 8.f, e - 7);
-  return sgn * mag;
-}
-
 // ----------------------------------------------------------------- bit-sliced scorer images
 // For a symmetric codebook the level of an R-bit index expands over the parity planes of odd
 // subsets of its bits: c[idx] = sum_S a_S (2 p_S - 1).  The MSE term of a key becomes
@@ -832,98 +806,173 @@ __device__ __forceinline__ int bitslice_coord(int K) {
   return 32 * G + 4 * m + j;
 }
 
-struct QImageArgs {
+
+// Query preparation for the bit-sliced scorer (every sub-plan D <= 128): one wave per
+// query computes y' (rotation in registers: lane l holds coordinates l and l + 64), w = S y',
+// the sums, its image scales, writes its three image rows per plane and its epilogue
+// constants; the first query of a tile also clears the rows of tile slots past the last
+// query.
+struct QFusedArgs {
   SubDev s;
-  const float* yrot;   // [nq_total][D]
-  const float* w;
-  const float* sums;   // [nq_total][2]
+  const void* q;
+  int64_t ldq;
+  int is_bf16;
+  int64_t nq;            // total query rows
   int64_t nq_per_group;
-  int n_qtiles;        // ceil(nq_per_group / 4)
-  uint32_t* img;       // [groups*qtiles][n_planes+1][64 lanes][8 words]
-  float* ec;           // [groups*qtiles][4 queries][4]: c0, c1, c2, c3
+  int n_qtiles;
+  uint32_t* img;         // [groups*qtiles][n_planes+1][64][8]
+  float* ec;             // [groups*qtiles][4][4]
 };
 
-// grid (group * query tile, plane); the last plane index is the QJL image
-__global__ void __launch_bounds__(kBlock) qimage_kernel(QImageArgs a) {
+__global__ void __launch_bounds__(kBlock) qprep_bitslice_kernel(QFusedArgs a) {
   const SubDev& s = a.s;
   const int D = s.D;
-  const int gt = blockIdx.x;                    // group * n_qtiles + qtile
-  const int p = blockIdx.y;
-  const int64_t grp = gt / a.n_qtiles, qt = gt % a.n_qtiles;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ float ys_all[kBlock / kWave][128], ws_all[kBlock / kWave][128];
+  float* ys = ys_all[wave];
+  float* ws = ws_all[wave];
+  const int64_t qi = (int64_t)blockIdx.x * (kBlock / kWave) + wave;
+  if (qi >= a.nq) return;
+  const int64_t grp = qi / a.nq_per_group, qq = qi % a.nq_per_group;
+  const int qt = (int)(qq / 4), q = (int)(qq % 4);
+  const int64_t gt = grp * a.n_qtiles + qt;
   const int np = s.n_planes;
-  const int tid = threadIdx.x;
-  float cmax = 0.f;
-  for (int i = 0; i < np; ++i) cmax = fmaxf(cmax, fabsf(s.coef[i]));
-  // per-query scales: powers of two putting the largest image magnitude in (128, 256]
-  __shared__ float red[2][4][kBlock / kWave];
-  __shared__ float sc_mse[4], sc_qjl[4];
-  for (int q = 0; q < 4; ++q) {
-    const int64_t qq = qt * 4 + q;
-    float my = 0.f, mw = 0.f;
-    if (qq < a.nq_per_group) {
-      const int64_t qi = grp * a.nq_per_group + qq;
-      for (int i = tid; i < D; i += kBlock) {
-        my = fmaxf(my, fabsf(a.yrot[qi * D + i]));
-        mw = fmaxf(mw, fabsf(a.w[qi * D + i]));
+  // ---- y' = Pi pad(y) ----
+  float v[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int i = lane + 64 * e;
+    float val = 0.f;
+    if (i < s.d) {
+      const int64_t ch = s.chan ? s.chan[i] : i;
+      val = a.is_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi * a.ldq + ch])
+                      : reinterpret_cast<const float*>(a.q)[qi * a.ldq + ch];
+    }
+    v[e] = val;
+  }
+  const int lanes_used = D < 64 ? D : 64;
+  for (int r = 0; r < 3; ++r) {
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = lane + 64 * e;
+      if (i < D) v[e] = flip_sign(v[e], (s.signs[r * (D / 32) + i / 32] >> (i % 32)) & 1u);
+    }
+    for (int h = 1; h < lanes_used; h <<= 1) {
+      const float sgn = (lane & h) ? -1.f : 1.f;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float pv = __shfl_xor(v[e], h);
+        v[e] = fmaf(sgn, v[e], pv);
       }
     }
-    for (int m = 32; m >= 1; m >>= 1) {
-      my = fmaxf(my, __shfl_xor(my, m));
-      mw = fmaxf(mw, __shfl_xor(mw, m));
+    if (D == 128) {
+      const float x0 = v[0], x1 = v[1];
+      v[0] = x0 + x1;
+      v[1] = x0 - x1;
     }
-    if ((tid & 63) == 0) { red[0][q][tid >> 6] = my; red[1][q][tid >> 6] = mw; }
   }
-  __syncthreads();
-  if (tid < 4) {
-    float my = 0.f, mw = 0.f;
-    for (int w = 0; w < kBlock / kWave; ++w) { my = fmaxf(my, red[0][tid][w]); mw = fmaxf(mw, red[1][tid][w]); }
-    const float M1 = my * cmax, M2 = mw;
-    sc_mse[tid] = M1 > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(M1))) : 1.f;
-    sc_qjl[tid] = M2 > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(M2))) : 1.f;
+  float sy = 0.f, my = 0.f;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int i = lane + 64 * e;
+    if (i < D) {
+      v[e] *= s.inv_scale;
+      ys[i] = v[e];
+      sy += v[e];
+      my = fmaxf(my, fabsf(v[e]));
+    }
   }
-  __syncthreads();
-  uint32_t* img = a.img + ((size_t)gt * (np + 1) + p) * 64 * 8;
-  for (int widx = tid; widx < 64 * 8; widx += kBlock) {
-    const int lane = widx >> 3, wd = widx & 7;
-    const int row = lane & 15, Ga = lane >> 4;
-    const int q = row >> 2, limb = row & 3;
-    const int64_t qq = qt * 4 + q;
-    const bool valid = (qq < a.nq_per_group) && limb < 3;
-    const int64_t qi = grp * a.nq_per_group + qq;
-    uint32_t word = 0;
-    for (int b = 0; b < 4; ++b) {
-      const int e = 4 * wd + b;
-      const int K = e < 16 ? 16 * Ga + e : 64 + 16 * Ga + (e - 16);
-      const int c = bitslice_coord(K);
-      uint32_t byte = 0;
-      if (valid && c < D) {
-        const float v = (p < np) ? s.coef[p] * a.yrot[qi * D + c] * sc_mse[q]
-                                 : a.w[qi * D + c] * sc_qjl[q];
-        float rem = v;
-        uint32_t code = 0;
-        for (int l = 0; l <= limb; ++l) {
-          code = e4m3_encode(rem);
-          rem -= e4m3_decode(code);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // ---- w = S y' : lane owns rows lane, lane + 64 ----
+  float sw = 0.f, mw = 0.f;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int j = lane + 64 * e;
+    if (j < s.k) {
+      const uint16_t* Sj = s.S + (size_t)j * D;
+      float acc = 0.f;
+      for (int i0 = 0; i0 < D; i0 += 8) {
+        const uint4 u = *reinterpret_cast<const uint4*>(Sj + i0);
+        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          acc = fmaf(__uint_as_float(wv[h] << 16), ys[i0 + 2 * h], acc);
+          acc = fmaf(__uint_as_float(wv[h] & 0xFFFF0000u), ys[i0 + 2 * h + 1], acc);
         }
-        byte = code;
       }
-      word |= byte << (8 * b);
+      ws[j] = acc;
+      sw += acc;
+      mw = fmaxf(mw, fabsf(acc));
     }
-    img[widx] = word;
   }
-  if (p == 0 && tid < 4) {
-    const int64_t q2 = qt * 4 + tid;
-    float c0 = 0.f, c1 = 0.f, c2 = 0.f, c3 = 0.f;
-    if (q2 < a.nq_per_group) {
-      const int64_t qi2 = grp * a.nq_per_group + q2;
-      const float K = sqrtf(0.5f * (float)M_PI) / (float)s.k;
-      c0 = -s.coef_sum * a.sums[qi2 * 2];
-      c1 = 4.f / sc_mse[tid];
-      c2 = -K * a.sums[qi2 * 2 + 1];
-      c3 = 4.f * K / sc_qjl[tid];
+  for (int m = 32; m >= 1; m >>= 1) {
+    sy += __shfl_xor(sy, m);
+    sw += __shfl_xor(sw, m);
+    my = fmaxf(my, __shfl_xor(my, m));
+    mw = fmaxf(mw, __shfl_xor(mw, m));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float cmax = 0.f;
+  for (int p = 0; p < np; ++p) cmax = fmaxf(cmax, fabsf(s.coef[p]));
+  const float M1 = my * cmax;
+  // powers of two putting the largest image magnitude in (128, 256]
+  const float sc_mse = M1 > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(M1))) : 1.f;
+  const float sc_qjl = mw > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(mw))) : 1.f;
+  // ---- image rows 4q .. 4q+3 of every plane ----
+  for (int p = 0; p <= np; ++p) {
+    uint32_t* img = a.img + ((size_t)gt * (np + 1) + p) * 64 * 8;
+    const float cf = p < np ? s.coef[p] * sc_mse : sc_qjl;
+    const float* src = p < np ? ys : ws;
+    for (int it = lane; it < 4 * 4 * 8; it += kWave) {      // (limb row, lane group, word)
+      const int limb = it >> 5, Ga = (it >> 3) & 3, wd = it & 7;
+      uint32_t word = 0;
+      if (limb < 3) {
+        float rem[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int e = 4 * wd + b;
+          const int K = e < 16 ? 16 * Ga + e : 64 + 16 * Ga + (e - 16);
+          const int c = bitslice_coord(K);
+          rem[b] = c < D ? cf * src[c] : 0.f;
+        }
+        // limb l = fp8 e4m3 (round to nearest even) of what limbs 0..l-1 left over
+        for (int l = 0; l <= limb; ++l) {
+          word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rem[0], rem[1], 0, false);
+          word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rem[2], rem[3], (int)word, true);
+          rem[0] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 0);
+          rem[1] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 1);
+          rem[2] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 2);
+          rem[3] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 3);
+        }
+      }
+      img[(16 * Ga + 4 * q + limb) * 8 + wd] = word;
     }
-    float* e = a.ec + ((size_t)gt * 4 + tid) * 4;
-    e[0] = c0; e[1] = c1; e[2] = c2; e[3] = c3;
+  }
+  if (lane == 0) {
+    const float K = sqrtf(0.5f * (float)M_PI) / (float)s.k;
+    float* e = a.ec + ((size_t)gt * 4 + q) * 4;
+    e[0] = -s.coef_sum * sy;
+    e[1] = 4.f / sc_mse;
+    e[2] = -K * sw;
+    e[3] = 4.f * K / sc_qjl;
+  }
+  // ---- clear tile slots past the last query (done by the tile's first query) ----
+  if (q == 0) {
+    const int valid = (int)((a.nq_per_group - 4 * qt) < 4 ? (a.nq_per_group - 4 * qt) : 4);
+    for (int qz = valid; qz < 4; ++qz) {
+      for (int p = 0; p <= np; ++p) {
+        uint32_t* img = a.img + ((size_t)gt * (np + 1) + p) * 64 * 8;
+        for (int it = lane; it < 4 * 4 * 8; it += kWave) {
+          const int limb = it >> 5, Ga = (it >> 3) & 3, wd = it & 7;
+          img[(16 * Ga + 4 * qz + limb) * 8 + wd] = 0u;
+        }
+      }
+      if (lane < 4) a.ec[((size_t)gt * 4 + qz) * 4 + lane] = 0.f;
+    }
   }
 }
 
@@ -957,47 +1006,61 @@ __device__ __forceinline__ i32x8 fp4_operand(uint32_t W) {
   return b;
 }
 
-// Contribution of one sub-plan (R index bits, D <= 128) to 16 keys; lane l handles key
-// column l % 16.  The MFMA reads the B registers of every lane, so all lanes must reach it
-// with defined operands: loads are branch-free from an always-valid record (`key_safe`)
-// and masked by selects.
+// One sub-plan's share of a 16-key step (R index bits, D <= 128); lane l handles key column
+// l % 16 and code word l / 16.  The MFMA reads the B registers of every lane, so all lanes
+// must reach it with defined operands: loads are branch-free from an always-valid record
+// (`key_safe`) and masked by selects.
+template <int R> struct KeyWords {
+  uint32_t wd[R + 1];
+  float nrm, gam;
+};
+
 template <int R>
-__device__ __forceinline__ float bitslice_sub(const SubDev& s, const uint8_t* codes,
-                                              int rec_bytes, int64_t key_safe, bool key_ok,
-                                              const i32x8* A, const float* e4) {
-  constexpr int NP = 1 << (R - 1);
-  const int lane = threadIdx.x & 63, G = lane >> 4;
+__device__ __forceinline__ KeyWords<R> load_key_words(const SubDev& s, const uint8_t* codes,
+                                                      int rec_bytes, int64_t key_safe, bool key_ok) {
+  const int G = (threadIdx.x & 63) >> 4;
   const bool chunk_ok = 32 * G < s.D;
   const uint8_t* rec = codes + key_safe * rec_bytes + s.rec_off;
   const uint32_t* pw = reinterpret_cast<const uint32_t*>(rec) + (chunk_ok ? G : 0) * (R + 1);
-  uint32_t wd[R + 1];
+  KeyWords<R> k;
 #pragma unroll
   for (int m = 0; m <= R; ++m) {
     const uint32_t v = pw[m];
-    wd[m] = (key_ok && chunk_ok) ? v : 0u;
+    k.wd[m] = (key_ok && chunk_ok) ? v : 0u;
   }
   const uint32_t* tail = reinterpret_cast<const uint32_t*>(rec + (s.D / 32) * (R + 1) * 4);
-  const float nrm = key_ok ? __uint_as_float(tail[0]) : 0.f;
-  const float gam = key_ok ? __uint_as_float(tail[1]) : 0.f;
+  const uint32_t t0 = tail[0], t1 = tail[1];
+  k.nrm = key_ok ? __uint_as_float(t0) : 0.f;
+  k.gam = key_ok ? __uint_as_float(t1) : 0.f;
+  return k;
+}
+
+template <int R>
+__device__ __forceinline__ float bitslice_estimate(const KeyWords<R>& k, const i32x8* A,
+                                                   const float* e4) {
+  constexpr int NP = 1 << (R - 1);
   f32x4 am = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
     uint32_t P = 0;
 #pragma unroll
     for (int m = 0; m < R; ++m)
-      if ((s.plane_mask[p] >> m) & 1) P ^= wd[m];
+      if ((pmask_c<R>(p) >> m) & 1) P ^= k.wd[m];
     am = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[p], fp4_operand(P), am, 0, 4, 0, 127, 0, 127);
   }
-  aq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[NP], fp4_operand(wd[R]), aq, 0, 4, 0, 127, 0, 127);
+  aq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[NP], fp4_operand(k.wd[R]), aq, 0, 4, 0, 127, 0, 127);
   const float msum = am[0] + am[1] + am[2];
   const float qsum = aq[0] + aq[1] + aq[2];
-  return nrm * (fmaf(e4[1], msum, e4[0]) + gam * fmaf(e4[3], qsum, e4[2]));
+  return k.nrm * (fmaf(e4[1], msum, e4[0]) + k.gam * fmaf(e4[3], qsum, e4[2]));
 }
+
+constexpr int kScoreSteps = 4;   // 16-key steps whose loads are issued together
 
 template <int R0, int R1>
 __global__ void __launch_bounds__(kBlock) score_bitslice_kernel(ScoreArgs a, int keys_per_block) {
   constexpr int NP0 = 1 << (R0 - 1);
   constexpr int NP1 = R1 > 0 ? (1 << (R1 - 1)) : 0;
+  constexpr int U = kScoreSteps;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int gt = blockIdx.y;                           // group * n_qtiles + qtile
   const int64_t grp = gt / a.n_qtiles, qt = gt % a.n_qtiles;
@@ -1037,17 +1100,28 @@ __global__ void __launch_bounds__(kBlock) score_bitslice_kernel(ScoreArgs a, int
   const uint8_t* codes = a.codes + grp * a.n * (int64_t)a.p.rec_bytes;
   const int64_t kb0 = (int64_t)blockIdx.x * keys_per_block;
   const int64_t kend = (kb0 + keys_per_block < a.n) ? kb0 + keys_per_block : a.n;
-  for (int64_t k0 = kb0 + wave * 16; k0 < kend; k0 += 16 * (kBlock / kWave)) {
-    const int64_t key = k0 + col;
-    const bool key_ok = key < kend;
-    const int64_t key_safe = key_ok ? key : kend - 1;
-    float est = bitslice_sub<R0>(a.p.sub[0], codes, a.p.rec_bytes, key_safe, key_ok, A0, e0);
-    if constexpr (R1 > 0)
-      est += bitslice_sub<R1>(a.p.sub[1], codes, a.p.rec_bytes, key_safe, key_ok, A1, e1);
-    // Pin the value here, in the full-wave region: otherwise the MFMAs feeding it may be
-    // sunk into the masked store below and run with inactive lanes.
-    asm volatile("" : "+v"(est));
-    if (q_ok && key_ok) out[key] = est;
+  for (int64_t k0 = kb0 + wave * 16 * U; k0 < kend; k0 += 16 * U * (kBlock / kWave)) {
+    KeyWords<R0> w0[U];
+    KeyWords<(R1 > 0 ? R1 : 1)> w1[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t key = k0 + 16 * u + col;
+      const bool key_ok = key < kend;
+      const int64_t key_safe = key_ok ? key : kend - 1;
+      w0[u] = load_key_words<R0>(a.p.sub[0], codes, a.p.rec_bytes, key_safe, key_ok);
+      if constexpr (R1 > 0)
+        w1[u] = load_key_words<R1>(a.p.sub[1], codes, a.p.rec_bytes, key_safe, key_ok);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t key = k0 + 16 * u + col;
+      float est = bitslice_estimate<R0>(w0[u], A0, e0);
+      if constexpr (R1 > 0) est += bitslice_estimate<R1>(w1[u], A1, e1);
+      // Pin the value here, in the full-wave region: otherwise the MFMAs feeding it may be
+      // sunk into the masked store below and run with inactive lanes.
+      asm volatile("" : "+v"(est));
+      if (q_ok && key < kend) out[key] = est;
+    }
   }
 }
 
@@ -1293,7 +1367,7 @@ int launch_qjl(const SubDev& s, const float* r, int64_t n, uint32_t* beta, void*
 
 template <int R0, int R1>
 static void launch_bitslice(const ScoreArgs& sa, int64_t n_gt, hipStream_t st) {
-  const int kpb = 1024;
+  const int kpb = 2048;
   const int64_t kblocks = (sa.n + kpb - 1) / kpb;
   hipLaunchKernelGGL((score_bitslice_kernel<R0, R1>), dim3((unsigned)kblocks, (unsigned)n_gt),
                      dim3(kBlock), 0, st, sa, kpb);
@@ -1353,23 +1427,26 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
     qa.yrot = reinterpret_cast<float*>(wb + off_y[sb]);
     qa.w = reinterpret_cast<float*>(wb + off_w[sb]);
     qa.sums = reinterpret_cast<float*>(wb + off_s[sb]);
-    hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)nq), dim3(kBlock), 0, st, qa);
     sa.yrot[sb] = qa.yrot;
     sa.w[sb] = qa.w;
     if (small) {
-      QImageArgs ia;
-      ia.s = p.sub[sb];
-      ia.yrot = qa.yrot;
-      ia.w = qa.w;
-      ia.sums = qa.sums;
-      ia.nq_per_group = nq_per_group;
-      ia.n_qtiles = qt_bs;
-      ia.img = reinterpret_cast<uint32_t*>(wb + off_img[sb]);
-      ia.ec = reinterpret_cast<float*>(wb + off_ec[sb]);
-      hipLaunchKernelGGL(qimage_kernel, dim3((unsigned)(n_groups * qt_bs), (unsigned)(p.sub[sb].n_planes + 1)),
-                         dim3(kBlock), 0, st, ia);
-      sa.img[sb] = ia.img;
-      sa.ec[sb] = ia.ec;
+      QFusedArgs fa;
+      fa.s = p.sub[sb];
+      fa.q = q;
+      fa.ldq = ldq;
+      fa.is_bf16 = dt == TQ_BF16;
+      fa.nq = nq;
+      fa.nq_per_group = nq_per_group;
+      fa.n_qtiles = qt_bs;
+      fa.img = reinterpret_cast<uint32_t*>(wb + off_img[sb]);
+      fa.ec = reinterpret_cast<float*>(wb + off_ec[sb]);
+      const int per_block = kBlock / kWave;
+      hipLaunchKernelGGL(qprep_bitslice_kernel, dim3((unsigned)((nq + per_block - 1) / per_block)),
+                         dim3(kBlock), 0, st, fa);
+      sa.img[sb] = fa.img;
+      sa.ec[sb] = fa.ec;
+    } else {
+      hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)nq), dim3(kBlock), 0, st, qa);
     }
   }
   int rc = 0;
