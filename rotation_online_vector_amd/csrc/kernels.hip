@@ -367,23 +367,19 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
 }
 #define pack2_bf16 pack_bf16_rne
 
-// 8 consecutive input elements of one row (zero beyond d / past the last row), as XL exact
-// bf16 limbs packed two per word: limbs[l][w] holds elements 2w, 2w+1 of limb l.
+// 8 consecutive input elements of one row (zero beyond d), as XL exact bf16 limbs packed
+// two per word: limbs[l][w] holds elements 2w, 2w+1 of limb l.  `row` must be a valid row
+// (callers clamp: a column of the tile past the last row repeats a real vector and is never
+// stored; columns of the products are independent).
 // VEC: rows are 16-byte aligned, d = D and no channel gather, so every lane's 8 elements
-// are one vector load (rows past the end read as zero); otherwise element-wise.
+// are one vector load; otherwise element-wise.
+// For XL > 1 (fp32 input) the squares of the 8 values are added to ss.
 template <int XL, bool VEC>
 __device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0,
-                                        uint32_t (&limbs)[XL][4]) {
+                                        uint32_t (&limbs)[XL][4], float& ss) {
   const SubDev& s = a.s;
   float v[8];
   if (VEC) {
-    if (row >= a.n) {
-#pragma unroll
-      for (int l = 0; l < XL; ++l)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) limbs[l][w] = 0;
-      return;
-    }
     if constexpr (XL == 1) {       // bf16 input: its own exact limb
       const uint4 u = *reinterpret_cast<const uint4*>(
           reinterpret_cast<const uint16_t*>(a.x) + row * a.ldx + c0);
@@ -401,13 +397,17 @@ __device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0
     for (int e = 0; e < 8; ++e) {
       const int i = c0 + e;
       float val = 0.f;
-      if (row < a.n && i < s.d) {
+      if (i < s.d) {
         const int64_t ch = s.chan ? s.chan[i] : i;
         val = a.is_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.x)[row * a.ldx + ch])
                         : reinterpret_cast<const float*>(a.x)[row * a.ldx + ch];
       }
       v[e] = val;
     }
+  }
+  if constexpr (XL > 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(v[e], v[e], ss);
   }
   // exact split: truncate to 8 significant bits twice, the remainder fits the third limb
 #pragma unroll
@@ -431,29 +431,60 @@ __device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0
   }
 }
 
-// Two-bit Lloyd-Max step for one coordinate z (thresholds t0 < t1 < t2, levels l0..l3, all
-// pre-scaled): idx = #{t_j <= z} by a two-level binary search, each index bit shifted into
-// n1 / n0 (n = 2 n + bit, carry-in from the comparison mask), residual r = z - l[idx].
-// Written as one fixed VALU sequence: the compiler otherwise rebuilds the selects into an
-// integer index and compare chains.
-__device__ __forceinline__ float bucket2(float z, float t0, float t1, float t2, float l0, float l1,
-                                         float l2, float l3, uint32_t& n1, uint32_t& n0) {
-  float tsel, la, lb, lv, r;
+// Per-lane building blocks of the bucketize.  Each is one instruction written out, so that
+// chains of them stay a fixed sequence (the compiler otherwise rebuilds the selects into an
+// integer index and compare chains).
+// Lane mask of |z| >= t.
+__device__ __forceinline__ uint64_t abs_ge_mask(float z, float t) {
   uint64_t m;
-  asm("v_cmp_ge_f32_e64 %[m], %[z], %[t1]\n\t"
-      "v_cndmask_b32_e64 %[tsel], %[t0], %[t2], %[m]\n\t"
-      "v_cndmask_b32_e64 %[la], %[l0], %[l2], %[m]\n\t"
-      "v_cndmask_b32_e64 %[lb], %[l1], %[l3], %[m]\n\t"
-      "v_addc_co_u32_e64 %[n1], %[m], %[n1], %[n1], %[m]\n\t"
-      "v_cmp_ge_f32_e64 %[m], %[z], %[tsel]\n\t"
-      "v_cndmask_b32_e64 %[lv], %[la], %[lb], %[m]\n\t"
-      "v_addc_co_u32_e64 %[n0], %[m], %[n0], %[n0], %[m]\n\t"
-      "v_sub_f32_e32 %[r], %[z], %[lv]"
-      : [m] "=&s"(m), [tsel] "=&v"(tsel), [la] "=&v"(la), [lb] "=&v"(lb), [lv] "=&v"(lv),
-        [r] "=&v"(r), [n1] "+v"(n1), [n0] "+v"(n0)
-      : [z] "v"(z), [t0] "v"(t0), [t1] "v"(t1), [t2] "v"(t2), [l0] "v"(l0), [l1] "v"(l1),
-        [l2] "v"(l2), [l3] "v"(l3));
+  asm("v_cmp_ge_f32_e64 %0, |%1|, %2" : "=s"(m) : "v"(z), "v"(t));
+  return m;
+}
+// Per lane: m ? b : a.
+__device__ __forceinline__ float select_mask(uint64_t m, float a, float b) {
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(m));
   return r;
+}
+// w = 2 w + (this lane's bit of m).
+__device__ __forceinline__ uint32_t shift_in_mask(uint32_t w, uint64_t m) {
+  uint64_t carry;
+  asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(w), "=s"(carry) : "s"(m));
+  return w;
+}
+// w = 2 w + sign bit of f.
+__device__ __forceinline__ uint32_t shift_in_sign(uint32_t w, float f) {
+  return __builtin_amdgcn_alignbit(w, __float_as_uint(f), 31);
+}
+
+// One coordinate of the symmetric Lloyd-Max quantizer.  The codebook is mirror-symmetric
+// with its middle threshold at 0, so idx = 2^(R-1) [z >= 0] + (z >= 0 ? j : 2^(R-1) - 1 - j)
+// with j the cell of |z| among the positive thresholds tp[] (levels ap[]).  The sign goes to
+// P (bit set = negative), the bits of j to J[R-2..0]; the index planes are formed per word
+// afterwards: plane R-1 = ~P, plane m = J[m] ^ P.  Returns the residual z - c[idx].
+// (|z| equal to a threshold may land in either neighbouring cell; such a coordinate is
+// within rounding of the boundary in any precision.)
+template <int R>
+__device__ __forceinline__ float bucket_sym(float z, const float* tp, const float* ap,
+                                            uint32_t& P, uint32_t* J) {
+  constexpr int H = 1 << (R - 1);
+  float tc[H > 1 ? H - 1 : 1], lc[H];
+#pragma unroll
+  for (int j = 0; j < H - 1; ++j) tc[j] = tp[j];
+#pragma unroll
+  for (int j = 0; j < H; ++j) lc[j] = ap[j];
+#pragma unroll
+  for (int m = R - 2; m >= 0; --m) {
+    const int half = 1 << m;                 // thresholds left: 2 half - 1, middle half - 1
+    const uint64_t mk = abs_ge_mask(z, tc[half - 1]);
+    J[m] = shift_in_mask(J[m], mk);
+#pragma unroll
+    for (int j = 0; j < half - 1; ++j) tc[j] = select_mask(mk, tc[j], tc[half + j]);
+#pragma unroll
+    for (int j = 0; j < half; ++j) lc[j] = select_mask(mk, lc[j], lc[half + j]);
+  }
+  P = shift_in_sign(P, z);
+  return z - copysignf(lc[0], z);
 }
 
 // A lane's partial code word holds its D/4 bits at the top of the order fed (bit 0 = its
@@ -476,8 +507,9 @@ template <int D, int R, int XL, bool VEC>
 __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeArgs a) {
   constexpr int NJT = D / 16;        // 16-row tiles of coordinates
   constexpr int NKS = D / 32;        // 32-wide k steps
-  constexpr int L = 1 << R;
+  constexpr int H = 1 << (R - 1);    // cells of |z|
   constexpr int NT = 2;              // 16-vector tiles per wave iteration
+  constexpr uint32_t kPartMask = D >= 128 ? 0xFFFFFFFFu : (1u << (D / 4)) - 1u;
   __shared__ uint4 kop[2 * NJT * NKS * 64];
   __shared__ uint4 sop[NJT * NKS * 64];
   const SubDev& s = a.s;
@@ -489,149 +521,149 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, G = lane >> 4;
-  float thr[L - 1], lev[L];
+  // positive half of the symmetric codebook
+  float tpos[H > 1 ? H - 1 : 1], apos[H];
 #pragma unroll
-  for (int j = 0; j < L - 1; ++j) thr[j] = s.thr[j];
+  for (int j = 0; j < H - 1; ++j) tpos[j] = s.thr[H + j];
 #pragma unroll
-  for (int j = 0; j < L; ++j) lev[j] = s.lev[j];
-  const int recw = s.rec_sub / 4;
+  for (int j = 0; j < H; ++j) apos[j] = s.lev[H + j];
+  const float kscale = 1.f / s.inv_scale;   // D^(3/2)
 
   for (int64_t v0 = ((int64_t)blockIdx.x * kEncWaves + wave) * 16 * NT; v0 < a.n;
        v0 += (int64_t)gridDim.x * kEncWaves * 16 * NT) {
-    // ---- x^T operands ----
+    // ---- x^T operands (columns past the last vector repeat the last one) ----
     uint32_t xw[NT][NKS][XL][4];
+    float ss[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int t = 0; t < NT; ++t) {
+      ss[t] = 0.f;
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         uint32_t lb[XL][4];
-        load_x8<XL, VEC>(a, v0 + 16 * t + col, 32 * ks + 8 * G, lb);
+        const int64_t row = v0 + 16 * t + col;
+        load_x8<XL, VEC>(a, row < a.n ? row : a.n - 1, 32 * ks + 8 * G, lb, ss[t]);
 #pragma unroll
         for (int l = 0; l < XL; ++l)
 #pragma unroll
           for (int w = 0; w < 4; ++w) xw[t][ks][l][w] = lb[l][w];
       }
-    // ---- z_raw = K x ----
-    f32x4 acc[NT][NJT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) acc[t][jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
-        const uint4 uh = kop[(jt * NKS + ks) * 64 + lane];
-        const uint4 ul = kop[((NJT + jt) * NKS + ks) * 64 + lane];
-        const bf16x8 khi = bf16x8_from_words(uh.x, uh.y, uh.z, uh.w);
-        const bf16x8 klo = bf16x8_from_words(ul.x, ul.y, ul.z, ul.w);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-#pragma unroll
-          for (int l = 0; l < XL; ++l) {
-            const bf16x8 xb = bf16x8_from_words(xw[t][ks][l][0], xw[t][ks][l][1],
-                                                xw[t][ks][l][2], xw[t][ks][l][3]);
-            acc[t][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, xb, acc[t][jt], 0, 0, 0);
-            if (l < 2)   // the low limbs' product is below fp32 resolution
-              acc[t][jt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(klo, xb, acc[t][jt], 0, 0, 0);
-          }
-        }
-        if (jt % 2 == 1) __builtin_amdgcn_sched_barrier(0);   // bound the operands in flight
-      }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- per vector: norm, bucketize, residual, index words, residual limbs ----
-    uint32_t words[NT][R + 1];          // this lane group's code word of each plane
-    float nrm[NT], gam[NT];
+    // ---- norms first (so the bucketize can follow the rotation row tile by row tile):
+    // bf16 input: diagonal of the Gram matrix x^T x on MFMA; fp32 input: the squares ----
+    float nrm[NT], sc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float xx;
+      if constexpr (XL == 1) {
+        f32x4 gram = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          const bf16x8 xb = bf16x8_from_words(xw[t][ks][0][0], xw[t][ks][0][1], xw[t][ks][0][2],
+                                              xw[t][ks][0][3]);
+          gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, xb, gram, 0, 0, 0);
+        }
+        // entry (c, c) sits in lane 16 (c / 4) + c, element c % 4
+        xx = __shfl(gram[col & 3], 16 * (col >> 2) + col, 64);
+      } else {
+        xx = sum_over_lane_groups(ss[t]);
+      }
+      nrm[t] = sqrtf(xx);
+      const float zn = nrm[t] * kscale;          // ||z_raw|| = D^(3/2) ||x||
+      sc[t] = zn > 0.f ? zn : 1.f;
+    }
+    // the positive half of the codebook scaled by ||z_raw||
+    float Ts[NT][H > 1 ? H - 1 : 1], As[NT][H];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int j = 0; j < H - 1; ++j) Ts[t][j] = tpos[j] * sc[t];
+#pragma unroll
+      for (int j = 0; j < H; ++j) As[t][j] = apos[j] * sc[t];
+    }
+    // ---- z_raw = K x one 16-row tile at a time, highest first; the tile rotated in the
+    // previous step is bucketized meanwhile (independent work for the vector ALUs while the
+    // matrix cores run).  This lane's D/4 coordinates sit at bits 4 jt + e of its part of a
+    // code word; fed from the highest, each word shifts left by one per coordinate. ----
+    f32x4 acc[NT][NJT];
+    uint32_t P[NT], J[NT][R > 1 ? R - 1 : 1];
+    float g2[NT];
     bf16x8 rhi[NT][NKS], rlo[NT][NKS];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      float ss = 0.f;
+      P[t] = 0;
+      g2[t] = 0.f;
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt)
+      for (int m = 0; m < R - 1; ++m) J[t][m] = 0;
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ss = fmaf(acc[t][jt][e], acc[t][jt][e], ss);
-      const float zn = sqrtf(sum_over_lane_groups(ss));
-      const float sc = zn > 0.f ? zn : 1.f;
-      // thresholds as a complete binary search tree (root = middle) and the levels, both
-      // scaled by ||z_raw||; each comparison halves both arrays with one select per entry
-      float Ts[L - 1], Ls[L];
+    for (int step = 0; step <= NJT; ++step) {
+      const int jr = NJT - 1 - step;      // row tile rotated in this step
+      const int jb = jr + 1;              // row tile bucketized in this step
+      if (jr >= 0) {
 #pragma unroll
-      for (int j = 0; j < L - 1; ++j) Ts[j] = thr[j] * sc;
+        for (int t = 0; t < NT; ++t) acc[t][jr] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < L; ++j) Ls[j] = lev[j] * sc;
-      float g2 = 0.f;
-      // this lane's D/4 coordinates sit at bits 4 jt + e of its part of a code word
-      uint32_t part[R];
+        for (int ks = 0; ks < NKS; ++ks) {
+          const uint4 uh = kop[(jr * NKS + ks) * 64 + lane];
+          const uint4 ul = kop[((NJT + jr) * NKS + ks) * 64 + lane];
+          const bf16x8 khi = bf16x8_from_words(uh.x, uh.y, uh.z, uh.w);
+          const bf16x8 klo = bf16x8_from_words(ul.x, ul.y, ul.z, ul.w);
 #pragma unroll
-      for (int m = 0; m < R; ++m) part[m] = 0;
+          for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int jt = 0; jt < NJT; ++jt) {
-        uint32_t nib[R];
-#pragma unroll
-        for (int m = 0; m < R; ++m) nib[m] = 0;
-        if constexpr (R == 2) {
-#pragma unroll
-          for (int e = 3; e >= 0; --e) {     // highest bit first: nib = 2 nib + bit
-            const float r = bucket2(acc[t][jt][e], Ts[0], Ts[1], Ts[2], Ls[0], Ls[1], Ls[2], Ls[3],
-                                    nib[1], nib[0]);
-            g2 = fmaf(r, r, g2);
-            acc[t][jt][e] = r;
+            for (int l = 0; l < XL; ++l) {
+              const bf16x8 xb = bf16x8_from_words(xw[t][ks][l][0], xw[t][ks][l][1],
+                                                  xw[t][ks][l][2], xw[t][ks][l][3]);
+              acc[t][jr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(khi, xb, acc[t][jr], 0, 0, 0);
+              if (l < 2)   // the low limbs' product is below fp32 resolution
+                acc[t][jr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(klo, xb, acc[t][jr], 0, 0, 0);
+            }
           }
-        } else
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float z = acc[t][jt][e];
-          float tc[L - 1], lc[L];
-#pragma unroll
-          for (int j = 0; j < L - 1; ++j) tc[j] = Ts[j];
-#pragma unroll
-          for (int j = 0; j < L; ++j) lc[j] = Ls[j];
-#pragma unroll
-          for (int m = R - 1; m >= 0; --m) {
-            const int half = 1 << m;                    // thresholds left: 2 half - 1
-            const bool b = z >= tc[half - 1];
-#pragma unroll
-            for (int j = 0; j < half - 1; ++j) tc[j] = b ? tc[half + j] : tc[j];
-#pragma unroll
-            for (int j = 0; j < half; ++j) lc[j] = b ? lc[half + j] : lc[j];
-            nib[m] |= (b ? 1u : 0u) << e;
-          }
-          const float r = z - lc[0];
-          g2 = fmaf(r, r, g2);
-          acc[t][jt][e] = r;
         }
-#pragma unroll
-        for (int m = 0; m < R; ++m) part[m] |= nib[m] << (4 * jt);
-        // keep the comparison masks of one tile at a time live (scalar registers)
-        __builtin_amdgcn_sched_barrier(0);
       }
+      if (jb < NJT) {
 #pragma unroll
-      for (int m = 0; m < R; ++m) words[t][m] = combine_word<D>(part[m], G);
-      const float rn = sqrtf(sum_over_lane_groups(g2));
-      nrm[t] = zn * s.inv_scale;
-      gam[t] = rn / sc;
-      // residual limbs, k element e' of step ks = tile 2 ks + e'/4, element e' % 4
+        for (int t = 0; t < NT; ++t) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        uint32_t hw[4], lw[4];
+          for (int e = 3; e >= 0; --e) {
+            const float r = bucket_sym<R>(acc[t][jb][e], Ts[t], As[t], P[t], J[t]);
+            g2[t] = fmaf(r, r, g2[t]);
+            acc[t][jb][e] = r;
+          }
+          if (jb % 2 == 0) {
+            // residual limbs of k step ks: element e' = tile 2 ks + e'/4, element e' % 4
+            const int ks = jb / 2;
+            uint32_t hw[4], lw[4];
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const int e0 = 2 * w, e1 = 2 * w + 1;
-          const float r0 = acc[t][2 * ks + (e0 >> 2)][e0 & 3];
-          const float r1 = acc[t][2 * ks + (e1 >> 2)][e1 & 3];
-          const uint32_t hp = pack2_bf16(r0, r1);
-          hw[w] = hp;
-          lw[w] = pack2_bf16(r0 - __uint_as_float(hp << 16), r1 - __uint_as_float(hp & 0xFFFF0000u));
+            for (int w = 0; w < 4; ++w) {
+              const int e0 = 2 * w, e1 = 2 * w + 1;
+              const float r0 = acc[t][2 * ks + (e0 >> 2)][e0 & 3];
+              const float r1 = acc[t][2 * ks + (e1 >> 2)][e1 & 3];
+              const uint32_t hp = pack2_bf16(r0, r1);
+              hw[w] = hp;
+              lw[w] = pack2_bf16(r0 - __uint_as_float(hp << 16),
+                                 r1 - __uint_as_float(hp & 0xFFFF0000u));
+            }
+            rhi[t][ks] = bf16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
+            rlo[t][ks] = bf16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
+          }
         }
-        rhi[t][ks] = bf16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
-        rlo[t][ks] = bf16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    // ---- QJL: P^T = S_perm R^T and its signs, four row tiles at a time ----
+    uint32_t words[NT][R + 1];          // this lane group's code word of each plane
+    float gam[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) words[t][R] = 0;
+    for (int t = 0; t < NT; ++t) {
+      words[t][R - 1] = combine_word<D>(~P[t] & kPartMask, G);
+#pragma unroll
+      for (int m = 0; m < R - 1; ++m) words[t][m] = combine_word<D>((J[t][m] ^ P[t]) & kPartMask, G);
+      gam[t] = sqrtf(sum_over_lane_groups(g2[t])) * __frcp_rn(sc[t]);
+    }
+    // ---- QJL: P^T = S_perm R^T and its signs, four row tiles at a time, highest first ----
+    uint32_t B[NT];                     // sign bits of the projections (set = negative)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) B[t] = 0;
 #pragma unroll
     for (int jq = NJT - 4 < 0 ? 0 : NJT - 4; jq >= 0; jq -= 4) {
       constexpr int NQ = NJT < 4 ? NJT : 4;
@@ -657,15 +689,12 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int h = 0; h < NQ; ++h) {
-          uint32_t nib = 0;
+        for (int h = NQ - 1; h >= 0; --h)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) nib |= (qa[t][h][e] >= 0.f ? 1u : 0u) << e;
-          words[t][R] |= nib << (4 * (jq + h));
-        }
+          for (int e = 3; e >= 0; --e) B[t] = shift_in_sign(B[t], qa[t][h][e]);
     }
 #pragma unroll
-    for (int t = 0; t < NT; ++t) words[t][R] = combine_word<D>(words[t][R], G);
+    for (int t = 0; t < NT; ++t) words[t][R] = combine_word<D>(~B[t] & kPartMask, G);
     // ---- store: lane group G writes code word G of its vector, group 0 the norms ----
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -683,7 +712,6 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
         }
       }
     }
-    (void)recw;
   }
 }
 

@@ -39,7 +39,12 @@ def test_library_codebook_matches_oracle(D, R):
     # iteration contracts by ~0.96 per step, leaving ~3e-12 s to the fixed point
     assert np.max(np.abs(lv - olv)) < 1e-11 * s
     assert np.max(np.abs(th - oth)) < 1e-11 * s
-    assert np.array_equal(lv, -lv[::-1])          # library enforces exact symmetry
+    # exact mirror symmetry with the middle threshold at 0, also after rounding to fp32 (the
+    # encode kernels quantize |z| against the positive half and take the sign separately)
+    assert np.array_equal(lv, -lv[::-1])
+    assert np.array_equal(th, -th[::-1]) and th[(1 << R) // 2 - 1] == 0.0
+    lf, tf = lv.astype(np.float32), th.astype(np.float32)
+    assert np.array_equal(lf, -lf[::-1]) and np.array_equal(tf, -tf[::-1])
 
 
 @pytest.mark.parametrize("seed,subset,D", [(0, 0, 128), (0, 1, 32), (123456789123, 0, 2048),
