@@ -6,6 +6,7 @@ and score every query head against its KV head's codes (query preparation +
 the streaming estimator).  Inputs are resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--copy-calibration MIB]
 
 Prints one JSON line.  `value` is scores per second over whole steps; the
 per-kernel rates, the roofline of the dominant kernel (algorithmic bytes per
@@ -28,10 +29,33 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-groups", type=int, default=16)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB three times (untimed), so a "
+                         "counter run can scale its byte counters by a copy of known size")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_longctx.json")
+KERNEL_SOURCE = os.path.join(ROOT, "rotation_online_vector_amd", "csrc", "kernels.hip")
+
+
+def measured_traffic(kernel_key):
+    """HBM bytes per launch of `kernel_key` from the stored counter runs (FETCH_SIZE and
+    WRITE_SIZE scaled by a copy of known size), or None when there is no record or the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernels_sha256") != src:
+        return None
+    k = rec.get("kernels", {}).get(kernel_key)
+    return None if k is None else k.get("hbm_bytes")
 
 
 def cpu_baseline(keys, queries, group, bits, seed, n_groups):
@@ -98,6 +122,14 @@ def main():
         if ev is not None:
             ev[2].record(stream)
 
+    if args.copy_calibration > 0:
+        nb = args.copy_calibration << 20
+        src = torch.empty(nb, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -125,7 +157,7 @@ def main():
     dom = max(kern, key=lambda k: kern[k]["ms"])
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(kern[dom]["gbs"], 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": None, "bytes_per_launch": kern[dom]["bytes"]}
+            "traffic": measured_traffic(dom), "bytes_per_launch": kern[dom]["bytes"]}
     out = {
         "metric": "quantized-key scores/sec + HBM GB/s (d=128, 3-bit); encode vectors/sec",
         "value": n_scores / (ms_step / 1e3),
