@@ -14,6 +14,7 @@ namespace tq {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 
 constexpr int kWave = 64;
@@ -359,6 +360,25 @@ __device__ __forceinline__ bf16x8 bf16x8_from_words(uint32_t w0, uint32_t w1, ui
   return __builtin_bit_cast(bf16x8, u);
 }
 
+__device__ __forceinline__ f16x8 f16x8_from_words(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
+  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+  const u32x4 u = {w0, w1, w2, w3};
+  return __builtin_bit_cast(f16x8, u);
+}
+
+// Two bf16 values (one word), times a power of two when SCALE, as two fp16 values (one
+// word).  Exact when the (scaled) values lie in the fp16 normal range; smaller ones round
+// toward zero on the fp16 subnormal grid (absolute error below 2^-24).
+template <bool SCALE>
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float scale) {
+  float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
+  if constexpr (SCALE) {
+    lo *= scale;
+    hi *= scale;
+  }
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
   typedef __attribute__((ext_vector_type(2))) float f32x2;
   typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
@@ -431,14 +451,14 @@ __device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0
   }
 }
 
-// Per-lane building blocks of the bucketize.  Each is one instruction written out, so that
-// chains of them stay a fixed sequence (the compiler otherwise rebuilds the selects into an
-// integer index and compare chains).
-// Lane mask of |z| >= t.
+// Per-lane building blocks of the bucketize.  The select and the shift-in are written out
+// as single instructions, so that chains of them stay a fixed sequence (the compiler
+// otherwise rebuilds the selects into an integer index and compare chains).  The comparison,
+// which reads the matrix-core results, stays a builtin: the compiler inserts the wait states
+// a read of an MFMA result needs, which it does not do for an inline-assembly operand.
+// Lane mask of |z| >= t (one v_cmp with the abs modifier; 3 = ordered greater-or-equal).
 __device__ __forceinline__ uint64_t abs_ge_mask(float z, float t) {
-  uint64_t m;
-  asm("v_cmp_ge_f32_e64 %0, |%1|, %2" : "=s"(m) : "v"(z), "v"(t));
-  return m;
+  return __builtin_amdgcn_fcmpf(__builtin_fabsf(z), t, 3);
 }
 // Per lane: m ? b : a.
 __device__ __forceinline__ float select_mask(uint64_t m, float a, float b) {
@@ -503,18 +523,24 @@ __device__ __forceinline__ uint32_t combine_word(uint32_t part, int G) {
   }
 }
 
-template <int D, int R, int XL, bool VEC>
+// F16 (bf16 input only): the rotation runs as one fp16 product with the exact fp16 K and a
+// copy of x scaled per vector by a power of two (2^14 / 2^ceil(log2 ||x||), so every scaled
+// element is below 2^14 and the bf16 values convert exactly unless they sit 2^28 below the
+// norm), in place of two bf16 products with K split in two limbs.
+template <int D, int R, int XL, bool VEC, bool F16>
 __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeArgs a) {
   constexpr int NJT = D / 16;        // 16-row tiles of coordinates
   constexpr int NKS = D / 32;        // 32-wide k steps
   constexpr int H = 1 << (R - 1);    // cells of |z|
   constexpr int NT = 2;              // 16-vector tiles per wave iteration
   constexpr uint32_t kPartMask = D >= 128 ? 0xFFFFFFFFu : (1u << (D / 4)) - 1u;
-  __shared__ uint4 kop[2 * NJT * NKS * 64];
+  static_assert(!F16 || XL == 1, "fp16 rotation takes bf16 input");
+  constexpr int KLIMBS = F16 ? 1 : 2;
+  __shared__ uint4 kop[KLIMBS * NJT * NKS * 64];
   __shared__ uint4 sop[NJT * NKS * 64];
   const SubDev& s = a.s;
-  for (int i = threadIdx.x; i < 2 * NJT * NKS * 64; i += kEncWaves * kWave)
-    kop[i] = reinterpret_cast<const uint4*>(s.rotk)[i];
+  for (int i = threadIdx.x; i < KLIMBS * NJT * NKS * 64; i += kEncWaves * kWave)
+    kop[i] = reinterpret_cast<const uint4*>(F16 ? s.rotk16 : s.rotk)[i];
   for (int i = threadIdx.x; i < NJT * NKS * 64; i += kEncWaves * kWave)
     sop[i] = reinterpret_cast<const uint4*>(s.sperm)[i];
   __syncthreads();
@@ -550,7 +576,7 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
     }
     // ---- norms first (so the bucketize can follow the rotation row tile by row tile):
     // bf16 input: diagonal of the Gram matrix x^T x on MFMA; fp32 input: the squares ----
-    float nrm[NT], sc[NT];
+    float nrm[NT], sc[NT], xs[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       float xx;
@@ -567,9 +593,39 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
       } else {
         xx = sum_over_lane_groups(ss[t]);
       }
-      nrm[t] = sqrtf(xx);
-      const float zn = nrm[t] * kscale;          // ||z_raw|| = D^(3/2) ||x||
+      nrm[t] = __builtin_amdgcn_sqrtf(xx);       // hardware square root (about 1 ulp)
+      float zn = nrm[t] * kscale;                // ||z_raw|| = D^(3/2) ||x||
+      if constexpr (F16) {
+        // x is rotated as x * 2^(14 - e) with ||x|| < 2^e, so z_raw carries the same factor
+        const int e = __builtin_amdgcn_frexp_expf(nrm[t]);
+        xs[t] = __builtin_amdgcn_ldexpf(1.f, 14 - (e < -100 ? -100 : e));
+      }
       sc[t] = zn > 0.f ? zn : 1.f;
+    }
+    uint32_t xh[F16 ? NT : 1][NKS][4];   // fp16 copy of x (F16 only)
+    if constexpr (F16) {
+      // Unscaled when every norm of the wave lies in [2^-4, 2^14): elements then stay below
+      // the fp16 maximum, and the subnormal rounding (< 2^-24) is below 2^-20 ||x||.
+      bool plain = true;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) plain = plain && nrm[t] >= 0.0625f && nrm[t] < 16384.f;
+      if (__all(plain)) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) xh[t][ks][w] = bf16x2_to_f16x2<false>(xw[t][ks][0][w], 1.f);
+      } else {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) xh[t][ks][w] = bf16x2_to_f16x2<true>(xw[t][ks][0][w], xs[t]);
+          sc[t] *= xs[t];              // z_raw carries the factor (zero vectors: harmless)
+        }
+      }
     }
     // the positive half of the codebook scaled by ||z_raw||
     float Ts[NT][H > 1 ? H - 1 : 1], As[NT][H];
@@ -604,6 +660,16 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
         for (int t = 0; t < NT; ++t) acc[t][jr] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < NKS; ++ks) {
+          if constexpr (F16) {
+            const uint4 uk = kop[(jr * NKS + ks) * 64 + lane];
+            const f16x8 kh = f16x8_from_words(uk.x, uk.y, uk.z, uk.w);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              const f16x8 xb = f16x8_from_words(xh[t][ks][0], xh[t][ks][1], xh[t][ks][2], xh[t][ks][3]);
+              acc[t][jr] = __builtin_amdgcn_mfma_f32_16x16x32_f16(kh, xb, acc[t][jr], 0, 0, 0);
+            }
+            continue;
+          }
           const uint4 uh = kop[(jr * NKS + ks) * 64 + lane];
           const uint4 ul = kop[((NJT + jr) * NKS + ks) * 64 + lane];
           const bf16x8 khi = bf16x8_from_words(uh.x, uh.y, uh.z, uh.w);
@@ -658,7 +724,7 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
       words[t][R - 1] = combine_word<D>(~P[t] & kPartMask, G);
 #pragma unroll
       for (int m = 0; m < R - 1; ++m) words[t][m] = combine_word<D>((J[t][m] ^ P[t]) & kPartMask, G);
-      gam[t] = sqrtf(sum_over_lane_groups(g2[t])) * __frcp_rn(sc[t]);
+      gam[t] = __builtin_amdgcn_sqrtf(sum_over_lane_groups(g2[t])) * __builtin_amdgcn_rcpf(sc[t]);
     }
     // ---- QJL: P^T = S_perm R^T and its signs, four row tiles at a time, highest first ----
     uint32_t B[NT];                     // sign bits of the projections (set = negative)
@@ -1306,15 +1372,26 @@ static int launch_encode_d(const EncodeArgs& ea, hipStream_t st) {
   return hip_rc(hipGetLastError());
 }
 
-template <int D, int XL, bool VEC>
-static void launch_encode_mfma_dxv(const EncodeArgs& ea, hipStream_t st, dim3 grid) {
+template <int D, int XL, bool VEC, bool F16>
+static void launch_encode_mfma_dxvf(const EncodeArgs& ea, hipStream_t st, dim3 grid) {
   const dim3 block(kEncWaves * kWave);
   switch (ea.s.R) {
-    case 1: hipLaunchKernelGGL((encode_mfma_kernel<D, 1, XL, VEC>), grid, block, 0, st, ea); break;
-    case 2: hipLaunchKernelGGL((encode_mfma_kernel<D, 2, XL, VEC>), grid, block, 0, st, ea); break;
-    case 3: hipLaunchKernelGGL((encode_mfma_kernel<D, 3, XL, VEC>), grid, block, 0, st, ea); break;
-    case 4: hipLaunchKernelGGL((encode_mfma_kernel<D, 4, XL, VEC>), grid, block, 0, st, ea); break;
+    case 1: hipLaunchKernelGGL((encode_mfma_kernel<D, 1, XL, VEC, F16>), grid, block, 0, st, ea); break;
+    case 2: hipLaunchKernelGGL((encode_mfma_kernel<D, 2, XL, VEC, F16>), grid, block, 0, st, ea); break;
+    case 3: hipLaunchKernelGGL((encode_mfma_kernel<D, 3, XL, VEC, F16>), grid, block, 0, st, ea); break;
+    case 4: hipLaunchKernelGGL((encode_mfma_kernel<D, 4, XL, VEC, F16>), grid, block, 0, st, ea); break;
   }
+}
+
+template <int D, int XL, bool VEC>
+static void launch_encode_mfma_dxv(const EncodeArgs& ea, hipStream_t st, dim3 grid) {
+  if constexpr (XL == 1) {
+    if (ea.s.rotk16 != nullptr) {
+      launch_encode_mfma_dxvf<D, XL, VEC, true>(ea, st, grid);
+      return;
+    }
+  }
+  launch_encode_mfma_dxvf<D, XL, VEC, false>(ea, st, grid);
 }
 
 template <int D, int XL>

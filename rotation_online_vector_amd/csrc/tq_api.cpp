@@ -2,6 +2,7 @@
 // allocation), and dispatch to the kernel launchers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
@@ -47,6 +48,7 @@ struct SubHost {
   std::vector<uint32_t> signs;   // [3][D/32]
   std::vector<uint16_t> S;       // [D][D]
   std::vector<uint16_t> rotk;    // MFMA operand tables (D <= 128)
+  std::vector<uint16_t> rotk16;  // K in one fp16 limb, when every |K| <= 2048 (else empty)
   std::vector<uint16_t> sperm;
 };
 
@@ -82,10 +84,23 @@ std::vector<int64_t> rotation_integer_matrix(const std::vector<uint32_t>& signs,
 // consecutive coordinates, a whole 32-bit code word when D = 128.
 //  rotk: K (rows permuted as above) split into two bf16 limbs (exact: |K| <= 2^14 for
 //        D <= 128); k steps of 32 input coordinates.
+//  rotk16: the same K as a single fp16 limb (16x16x32 f16 operands), present when every
+//        |K| <= 2048 so that each entry is an exact fp16 integer.  With K ~ D N(0,1) per
+//        entry this holds for any practical seed; the bf16 pair remains the fallback.
 //  sperm: S with rows permuted the same way and columns ordered as the residual registers:
 //        k element e of lane group G in step ks is coordinate G*D/4 + 8*ks + e.
 int permuted_row(int D, int tile, int row_in_tile) {
   return (row_in_tile / 4) * (D / 4) + 4 * tile + row_in_tile % 4;
+}
+
+// fp16 bit pattern of an integer with |v| <= 2048 (exact).
+uint16_t fp16_bits_of_small_int(int64_t v) {
+  if (v == 0) return 0;
+  const uint16_t sign = v < 0 ? 0x8000u : 0u;
+  uint64_t a = (uint64_t)(v < 0 ? -v : v);
+  int e = 63 - __builtin_clzll(a);                 // a = 2^e * (1.f), e <= 11
+  const uint32_t mant = (uint32_t)((a << (10 - e)) & 0x3FFu);
+  return (uint16_t)(sign | (uint32_t)(e + 15) << 10 | mant);
 }
 
 void mfma_operand_tables(SubHost& h) {
@@ -93,6 +108,9 @@ void mfma_operand_tables(SubHost& h) {
   const std::vector<int64_t> K = rotation_integer_matrix(h.signs, D);
   h.rotk.assign((size_t)2 * NJT * NKS * 64 * 8, 0);
   h.sperm.assign((size_t)NJT * NKS * 64 * 8, 0);
+  int64_t kmax = 0;
+  for (int64_t v : K) kmax = std::max<int64_t>(kmax, v < 0 ? -v : v);
+  if (kmax <= 2048) h.rotk16.assign((size_t)NJT * NKS * 64 * 8, 0);
   for (int jt = 0; jt < NJT; ++jt)
     for (int ks = 0; ks < NKS; ++ks)
       for (int l = 0; l < 64; ++l)
@@ -107,6 +125,8 @@ void mfma_operand_tables(SubHost& h) {
           const size_t at = (((size_t)jt * NKS + ks) * 64 + l) * 8 + e;
           h.rotk[at] = hi;
           h.rotk[(size_t)NJT * NKS * 64 * 8 + at] = lo;
+          if (!h.rotk16.empty())
+            h.rotk16[at] = fp16_bits_of_small_int(K[(size_t)row * D + 32 * ks + 8 * G + e]);
           const int col = G * (D / 4) + 8 * ks + e;
           h.sperm[at] = h.S[(size_t)row * D + col];
         }
@@ -230,7 +250,7 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
   // host tables and device layout
   size_t bytes = 0;
   size_t off_sign[2] = {0, 0}, off_S[2] = {0, 0}, off_chan[2] = {0, 0};
-  size_t off_rotk[2] = {0, 0}, off_sperm[2] = {0, 0};
+  size_t off_rotk[2] = {0, 0}, off_rotk16[2] = {0, 0}, off_sperm[2] = {0, 0};
   auto take = [&](size_t b) { size_t o = bytes; bytes += (b + 255) / 256 * 256; return o; };
   for (int i = 0; i < pd.nsub; ++i) {
     SubHost& h = subs[i];
@@ -266,6 +286,7 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
     if (h.D <= kMfmaMaxD) {
       mfma_operand_tables(h);
       off_rotk[i] = take(h.rotk.size() * 2);
+      off_rotk16[i] = take(h.rotk16.size() * 2);
       off_sperm[i] = take(h.sperm.size() * 2);
     }
   }
@@ -287,6 +308,9 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
       e = hipMemcpy(base + off_chan[i], h.chan.data(), h.chan.size() * 4, hipMemcpyHostToDevice);
     if (e == hipSuccess && !h.rotk.empty())
       e = hipMemcpy(base + off_rotk[i], h.rotk.data(), h.rotk.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && !h.rotk16.empty())
+      e = hipMemcpy(base + off_rotk16[i], h.rotk16.data(), h.rotk16.size() * 2,
+                    hipMemcpyHostToDevice);
     if (e == hipSuccess && !h.sperm.empty())
       e = hipMemcpy(base + off_sperm[i], h.sperm.data(), h.sperm.size() * 2, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
@@ -298,6 +322,7 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
     s.S = reinterpret_cast<const uint16_t*>(base + off_S[i]);
     s.chan = h.chan.empty() ? nullptr : reinterpret_cast<const int32_t*>(base + off_chan[i]);
     s.rotk = h.rotk.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_rotk[i]);
+    s.rotk16 = h.rotk16.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_rotk16[i]);
     s.sperm = h.sperm.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_sperm[i]);
   }
   *out = plan;

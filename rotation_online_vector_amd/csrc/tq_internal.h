@@ -39,6 +39,7 @@ struct SubDev {
   // D <= 128 only: the rotation and the QJL matrix pre-arranged as MFMA A operands
   // (16x16x32 bf16 tiles, 64 lanes x 8 values each)
   const uint16_t* rotk;   // [2 limbs][D/16 row tiles][D/32 k steps][64][8]: D^(3/2) Pi
+  const uint16_t* rotk16; // [D/16][D/32][64][8]: the same in one exact fp16 limb, or null
   const uint16_t* sperm;  // [D/16][D/32][64][8]: S with columns in the residual register order
 };
 

@@ -155,6 +155,23 @@ def test_encode_and_score_shapes(d, bits, n, dtype):
     assert np.all(est[:, 0] == 0.0)
 
 
+@pytest.mark.parametrize("d,dtype,lo,hi", [(128, "bfloat16", -12, 12), (128, "bfloat16", -2, 4),
+                                           (64, "bfloat16", -12, 12), (100, "bfloat16", -9, 9),
+                                           (32, "float32", -12, 12), (128, "float32", -12, 12)])
+def test_encode_over_a_wide_range_of_norms(d, dtype, lo, hi):
+    """Codes depend on x / ||x|| only; rows scaled by 10^u, u uniform in [lo, hi], cover the
+    kernels' per-vector scaling (and, for moderate norms, its unscaled shortcut)."""
+    rng = np.random.default_rng(d + hi)
+    n = 333
+    xs = rng.standard_normal((n, d)) * 10.0 ** rng.uniform(lo, hi, (n, 1))
+    xs[5] = 0.0
+    x = torch.from_numpy(xs.astype(np.float32)).to(DEV).to(getattr(torch, dtype))
+    for bits in (3, 4):
+        sp = otq.make_split_plan(d, bits, 3)
+        plan = tq.tq_plan_create(d, bits, 3)
+        _encode_and_compare(sp, plan, x, "norms 1e%d..1e%d d=%d b=%d" % (lo, hi, d, bits))
+
+
 def test_strided_rows_and_query_groups():
     d, n = 128, 300
     rng = np.random.default_rng(5)
