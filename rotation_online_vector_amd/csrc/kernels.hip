@@ -387,6 +387,23 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
 }
 #define pack2_bf16 pack_bf16_rne
 
+// v - (one half of the packed bf16 pair hp), exact when that half is v rounded to bf16: one
+// bf16 dot product hp . sel + v with sel = -1 in the chosen half and 0 in the other, which
+// reads the packed pair directly instead of unpacking it first.
+__device__ __forceinline__ float residual_below_bf16(uint32_t hp, uint32_t sel, float v) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hp),
+                                         __builtin_bit_cast(bf16x2, sel), v, false);
+}
+
+// The selector (-1, 0) as a register value.  Written as a constant it is folded into the
+// inline constant -1.0, which this instruction reads as the pair (0, -1): the wrong half.
+__device__ __forceinline__ uint32_t neg_one_low_half() {
+  uint32_t v;
+  asm("v_mov_b32 %0, 0xbf80" : "=v"(v));
+  return v;
+}
+
 // 8 consecutive input elements of one row (zero beyond d), as XL exact bf16 limbs packed
 // two per word: limbs[l][w] holds elements 2w, 2w+1 of limb l.  `row` must be a valid row
 // (callers clamp: a column of the tile past the last row repeats a real vector and is never
@@ -554,6 +571,7 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
 #pragma unroll
   for (int j = 0; j < H; ++j) apos[j] = s.lev[H + j];
   const float kscale = 1.f / s.inv_scale;   // D^(3/2)
+  const uint32_t sel_lo = neg_one_low_half();
 
   for (int64_t v0 = ((int64_t)blockIdx.x * kEncWaves + wave) * 16 * NT; v0 < a.n;
        v0 += (int64_t)gridDim.x * kEncWaves * 16 * NT) {
@@ -707,8 +725,8 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
               const float r1 = acc[t][2 * ks + (e1 >> 2)][e1 & 3];
               const uint32_t hp = pack2_bf16(r0, r1);
               hw[w] = hp;
-              lw[w] = pack2_bf16(r0 - __uint_as_float(hp << 16),
-                                 r1 - __uint_as_float(hp & 0xFFFF0000u));
+              lw[w] = pack2_bf16(residual_below_bf16(hp, sel_lo, r0),
+                                 residual_below_bf16(hp, 0xBF800000u, r1));
             }
             rhi[t][ks] = bf16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
             rlo[t][ks] = bf16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
