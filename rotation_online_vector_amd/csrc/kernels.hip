@@ -936,9 +936,11 @@ struct QFusedArgs {
   float* ec;             // [groups*qtiles][4][4]
 };
 
+// D is a template parameter so that the projection loop unrolls and every lane issues its
+// loads of S together (one L2 round trip instead of one per 8 columns).
+template <int D>
 __global__ void __launch_bounds__(kBlock) qprep_bitslice_kernel(QFusedArgs a) {
   const SubDev& s = a.s;
-  const int D = s.D;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __shared__ float ys_all[kBlock / kWave][128], ws_all[kBlock / kWave][128];
   float* ys = ys_all[wave];
@@ -1002,9 +1004,10 @@ __global__ void __launch_bounds__(kBlock) qprep_bitslice_kernel(QFusedArgs a) {
 #pragma unroll
   for (int e = 0; e < 2; ++e) {
     const int j = lane + 64 * e;
-    if (j < s.k) {
+    if (j < D) {                      // k = D rows
       const uint16_t* Sj = s.S + (size_t)j * D;
       float acc = 0.f;
+#pragma unroll
       for (int i0 = 0; i0 < D; i0 += 8) {
         const uint4 u = *reinterpret_cast<const uint4*>(Sj + i0);
         const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
@@ -1564,8 +1567,12 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
       fa.img = reinterpret_cast<uint32_t*>(wb + off_img[sb]);
       fa.ec = reinterpret_cast<float*>(wb + off_ec[sb]);
       const int per_block = kBlock / kWave;
-      hipLaunchKernelGGL(qprep_bitslice_kernel, dim3((unsigned)((nq + per_block - 1) / per_block)),
-                         dim3(kBlock), 0, st, fa);
+      const dim3 qgrid((unsigned)((nq + per_block - 1) / per_block));
+      switch (p.sub[sb].D) {
+        case 32: hipLaunchKernelGGL(qprep_bitslice_kernel<32>, qgrid, dim3(kBlock), 0, st, fa); break;
+        case 64: hipLaunchKernelGGL(qprep_bitslice_kernel<64>, qgrid, dim3(kBlock), 0, st, fa); break;
+        default: hipLaunchKernelGGL(qprep_bitslice_kernel<128>, qgrid, dim3(kBlock), 0, st, fa); break;
+      }
       sa.img[sb] = fa.img;
       sa.ec[sb] = fa.ec;
     } else {
