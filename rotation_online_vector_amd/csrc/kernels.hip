@@ -919,11 +919,12 @@ __device__ __forceinline__ int bitslice_coord(int K) {
 }
 
 
-// Query preparation for the bit-sliced scorer (every sub-plan D <= 128): one wave per
-// query computes y' (rotation in registers: lane l holds coordinates l and l + 64), w = S y',
-// the sums, its image scales, writes its three image rows per plane and its epilogue
-// constants; the first query of a tile also clears the rows of tile slots past the last
-// query.
+// Query preparation for the bit-sliced scorer (every sub-plan D <= 128): one workgroup per
+// query.  Wave 0 computes y' (rotation in registers: lane l holds coordinates l and l + 64);
+// then two threads per row compute w = S y' (each half a row, all loads of S in flight at
+// once); the block reduces the sums and maxima, writes the query's three image rows per
+// plane and its epilogue constants; the first query of a tile also clears the rows of tile
+// slots past the last query.
 struct QFusedArgs {
   SubDev s;
   const void* q;
@@ -936,157 +937,171 @@ struct QFusedArgs {
   float* ec;             // [groups*qtiles][4][4]
 };
 
-// D is a template parameter so that the projection loop unrolls and every lane issues its
-// loads of S together (one L2 round trip instead of one per 8 columns).
 template <int D>
 __global__ void __launch_bounds__(kBlock) qprep_bitslice_kernel(QFusedArgs a) {
+  static_assert(D == 32 || D == 64 || D == 128, "bit-sliced scorer lengths");
   const SubDev& s = a.s;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  __shared__ float ys_all[kBlock / kWave][128], ws_all[kBlock / kWave][128];
-  float* ys = ys_all[wave];
-  float* ws = ws_all[wave];
-  const int64_t qi = (int64_t)blockIdx.x * (kBlock / kWave) + wave;
-  if (qi >= a.nq) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ float ys[128], ws[128];
+  __shared__ float red[kBlock / kWave][4];
+  const int64_t qi = blockIdx.x;
   const int64_t grp = qi / a.nq_per_group, qq = qi % a.nq_per_group;
   const int qt = (int)(qq / 4), q = (int)(qq % 4);
   const int64_t gt = grp * a.n_qtiles + qt;
   const int np = s.n_planes;
-  // ---- y' = Pi pad(y) ----
-  float v[2];
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int i = lane + 64 * e;
-    float val = 0.f;
-    if (i < s.d) {
-      const int64_t ch = s.chan ? s.chan[i] : i;
-      val = a.is_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi * a.ldq + ch])
-                      : reinterpret_cast<const float*>(a.q)[qi * a.ldq + ch];
-    }
-    v[e] = val;
-  }
-  const int lanes_used = D < 64 ? D : 64;
-  for (int r = 0; r < 3; ++r) {
+  // ---- y' = Pi pad(y) (wave 0) ----
+  if (wave == 0) {
+    float v[2];
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
       const int i = lane + 64 * e;
-      if (i < D) v[e] = flip_sign(v[e], (s.signs[r * (D / 32) + i / 32] >> (i % 32)) & 1u);
+      float val = 0.f;
+      if (i < s.d) {
+        const int64_t ch = s.chan ? s.chan[i] : i;
+        val = a.is_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi * a.ldq + ch])
+                        : reinterpret_cast<const float*>(a.q)[qi * a.ldq + ch];
+      }
+      v[e] = val;
     }
-    for (int h = 1; h < lanes_used; h <<= 1) {
-      const float sgn = (lane & h) ? -1.f : 1.f;
+    constexpr int lanes_used = D < 64 ? D : 64;
+#pragma unroll
+    for (int r = 0; r < 3; ++r) {
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        const float pv = __shfl_xor(v[e], h);
-        v[e] = fmaf(sgn, v[e], pv);
+        const int i = lane + 64 * e;
+        if (i < D) v[e] = flip_sign(v[e], (s.signs[r * (D / 32) + i / 32] >> (i % 32)) & 1u);
       }
-    }
-    if (D == 128) {
-      const float x0 = v[0], x1 = v[1];
-      v[0] = x0 + x1;
-      v[1] = x0 - x1;
-    }
-  }
-  float sy = 0.f, my = 0.f;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int i = lane + 64 * e;
-    if (i < D) {
-      v[e] *= s.inv_scale;
-      ys[i] = v[e];
-      sy += v[e];
-      my = fmaxf(my, fabsf(v[e]));
-    }
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // ---- w = S y' : lane owns rows lane, lane + 64 ----
-  float sw = 0.f, mw = 0.f;
+      for (int h = 1; h < lanes_used; h <<= 1) {
+        const float sgn = (lane & h) ? -1.f : 1.f;
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int j = lane + 64 * e;
-    if (j < D) {                      // k = D rows
-      const uint16_t* Sj = s.S + (size_t)j * D;
-      float acc = 0.f;
-#pragma unroll
-      for (int i0 = 0; i0 < D; i0 += 8) {
-        const uint4 u = *reinterpret_cast<const uint4*>(Sj + i0);
-        const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-          acc = fmaf(__uint_as_float(wv[h] << 16), ys[i0 + 2 * h], acc);
-          acc = fmaf(__uint_as_float(wv[h] & 0xFFFF0000u), ys[i0 + 2 * h + 1], acc);
+        for (int e = 0; e < 2; ++e) {
+          const float pv = __shfl_xor(v[e], h);
+          v[e] = fmaf(sgn, v[e], pv);
         }
       }
-      ws[j] = acc;
-      sw += acc;
-      mw = fmaxf(mw, fabsf(acc));
+      if (D == 128) {
+        const float x0 = v[0], x1 = v[1];
+        v[0] = x0 + x1;
+        v[1] = x0 - x1;
+      }
+    }
+    float sy = 0.f, my = 0.f;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = lane + 64 * e;
+      if (i < D) {
+        v[e] *= s.inv_scale;
+        ys[i] = v[e];
+        sy += v[e];
+        my = fmaxf(my, fabsf(v[e]));
+      }
+    }
+    for (int m = 32; m >= 1; m >>= 1) {
+      sy += __shfl_xor(sy, m);
+      my = fmaxf(my, __shfl_xor(my, m));
+    }
+    if (lane == 0) {
+      red[0][0] = sy;
+      red[0][1] = my;
     }
   }
+  __syncthreads();
+  // ---- w = S y' : thread pair (2 row, 2 row + 1) shares row tid / 2, k = D rows ----
+  constexpr int HALF = D / 2;
+  const int row = tid >> 1, half = tid & 1;
+  float acc = 0.f;
+  if (row < D) {
+    const uint16_t* Sj = s.S + (size_t)row * D + half * HALF;
+    const float* yh = ys + half * HALF;
+    uint4 u[HALF / 8];
+#pragma unroll
+    for (int c = 0; c < HALF / 8; ++c) u[c] = reinterpret_cast<const uint4*>(Sj)[c];
+#pragma unroll
+    for (int c = 0; c < HALF / 8; ++c) {
+      const uint32_t wv[4] = {u[c].x, u[c].y, u[c].z, u[c].w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        acc = fmaf(__uint_as_float(wv[h] << 16), yh[8 * c + 2 * h], acc);
+        acc = fmaf(__uint_as_float(wv[h] & 0xFFFF0000u), yh[8 * c + 2 * h + 1], acc);
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  float sw = 0.f, mw = 0.f;
+  if (row < D && half == 0) {
+    ws[row] = acc;
+    sw = acc;
+    mw = fabsf(acc);
+  }
   for (int m = 32; m >= 1; m >>= 1) {
-    sy += __shfl_xor(sy, m);
     sw += __shfl_xor(sw, m);
-    my = fmaxf(my, __shfl_xor(my, m));
     mw = fmaxf(mw, __shfl_xor(mw, m));
   }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane == 0) {
+    red[wave][2] = sw;
+    red[wave][3] = mw;
+  }
+  __syncthreads();
+  const float sy = red[0][0], my = red[0][1];
+  float swt = 0.f, mwt = 0.f;
+#pragma unroll
+  for (int w = 0; w < kBlock / kWave; ++w) {
+    swt += red[w][2];
+    mwt = fmaxf(mwt, red[w][3]);
+  }
   float cmax = 0.f;
   for (int p = 0; p < np; ++p) cmax = fmaxf(cmax, fabsf(s.coef[p]));
   const float M1 = my * cmax;
   // powers of two putting the largest image magnitude in (128, 256]
   const float sc_mse = M1 > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(M1))) : 1.f;
-  const float sc_qjl = mw > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(mw))) : 1.f;
-  // ---- image rows 4q .. 4q+3 of every plane ----
-  for (int p = 0; p <= np; ++p) {
+  const float sc_qjl = mwt > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(mwt))) : 1.f;
+  // ---- image rows 4q .. 4q+3 of every plane: (plane, limb row, lane group, word) items ----
+  for (int it = tid; it < (np + 1) * 128; it += kBlock) {
+    const int p = it >> 7, limb = (it >> 5) & 3, Ga = (it >> 3) & 3, wd = it & 7;
     uint32_t* img = a.img + ((size_t)gt * (np + 1) + p) * 64 * 8;
     const float cf = p < np ? s.coef[p] * sc_mse : sc_qjl;
     const float* src = p < np ? ys : ws;
-    for (int it = lane; it < 4 * 4 * 8; it += kWave) {      // (limb row, lane group, word)
-      const int limb = it >> 5, Ga = (it >> 3) & 3, wd = it & 7;
-      uint32_t word = 0;
-      if (limb < 3) {
-        float rem[4];
+    uint32_t word = 0;
+    if (limb < 3) {
+      float rem[4];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int e = 4 * wd + b;
-          const int K = e < 16 ? 16 * Ga + e : 64 + 16 * Ga + (e - 16);
-          const int c = bitslice_coord(K);
-          rem[b] = c < D ? cf * src[c] : 0.f;
-        }
-        // limb l = fp8 e4m3 (round to nearest even) of what limbs 0..l-1 left over
-        for (int l = 0; l <= limb; ++l) {
-          word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rem[0], rem[1], 0, false);
-          word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rem[2], rem[3], (int)word, true);
-          rem[0] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 0);
-          rem[1] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 1);
-          rem[2] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 2);
-          rem[3] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 3);
-        }
+      for (int b = 0; b < 4; ++b) {
+        const int e = 4 * wd + b;
+        const int K = e < 16 ? 16 * Ga + e : 64 + 16 * Ga + (e - 16);
+        const int c = bitslice_coord(K);
+        rem[b] = c < D ? cf * src[c] : 0.f;
       }
-      img[(16 * Ga + 4 * q + limb) * 8 + wd] = word;
+      // limb l = fp8 e4m3 (round to nearest even) of what limbs 0..l-1 left over
+      for (int l = 0; l <= limb; ++l) {
+        word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rem[0], rem[1], 0, false);
+        word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rem[2], rem[3], (int)word, true);
+        rem[0] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 0);
+        rem[1] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 1);
+        rem[2] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 2);
+        rem[3] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 3);
+      }
     }
+    img[(16 * Ga + 4 * q + limb) * 8 + wd] = word;
   }
-  if (lane == 0) {
-    const float K = sqrtf(0.5f * (float)M_PI) / (float)s.k;
+  if (tid == 0) {
+    const float K = sqrtf(0.5f * (float)M_PI) / (float)D;
     float* e = a.ec + ((size_t)gt * 4 + q) * 4;
     e[0] = -s.coef_sum * sy;
     e[1] = 4.f / sc_mse;
-    e[2] = -K * sw;
+    e[2] = -K * swt;
     e[3] = 4.f * K / sc_qjl;
   }
   // ---- clear tile slots past the last query (done by the tile's first query) ----
   if (q == 0) {
     const int valid = (int)((a.nq_per_group - 4 * qt) < 4 ? (a.nq_per_group - 4 * qt) : 4);
     for (int qz = valid; qz < 4; ++qz) {
-      for (int p = 0; p <= np; ++p) {
+      for (int it = tid; it < (np + 1) * 128; it += kBlock) {
+        const int p = it >> 7, limb = (it >> 5) & 3, Ga = (it >> 3) & 3, wd = it & 7;
         uint32_t* img = a.img + ((size_t)gt * (np + 1) + p) * 64 * 8;
-        for (int it = lane; it < 4 * 4 * 8; it += kWave) {
-          const int limb = it >> 5, Ga = (it >> 3) & 3, wd = it & 7;
-          img[(16 * Ga + 4 * qz + limb) * 8 + wd] = 0u;
-        }
+        img[(16 * Ga + 4 * qz + limb) * 8 + wd] = 0u;
       }
-      if (lane < 4) a.ec[((size_t)gt * 4 + qz) * 4 + lane] = 0.f;
+      if (tid < 4) a.ec[((size_t)gt * 4 + qz) * 4 + tid] = 0.f;
     }
   }
 }
@@ -1566,8 +1581,7 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
       fa.n_qtiles = qt_bs;
       fa.img = reinterpret_cast<uint32_t*>(wb + off_img[sb]);
       fa.ec = reinterpret_cast<float*>(wb + off_ec[sb]);
-      const int per_block = kBlock / kWave;
-      const dim3 qgrid((unsigned)((nq + per_block - 1) / per_block));
+      const dim3 qgrid((unsigned)nq);
       switch (p.sub[sb].D) {
         case 32: hipLaunchKernelGGL(qprep_bitslice_kernel<32>, qgrid, dim3(kBlock), 0, st, fa); break;
         case 64: hipLaunchKernelGGL(qprep_bitslice_kernel<64>, qgrid, dim3(kBlock), 0, st, fa); break;
