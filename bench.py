@@ -6,7 +6,11 @@ and score every query head against its KV head's codes (query preparation +
 the streaming estimator).  Inputs are resident in HBM before timing starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--copy-calibration MIB]
+                    [--copy-calibration MIB] [--workload NAME]
+
+`--workload` selects one of the other synthetic shapes (kv, split35, split25,
+retrieval, small); their step is encode + score (+ top-k for the two retrieval
+shapes) and the line carries the same fields, without the CPU leg.
 
 Prints one JSON line.  `value` is scores per second over whole steps; the
 per-kernel rates, the roofline of the dominant kernel (algorithmic bytes per
@@ -32,6 +36,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-groups", type=int, default=16)
+    ap.add_argument("--workload", default="longctx",
+                    choices=["longctx", "kv", "split35", "split25", "retrieval", "small"],
+                    help="long-context decode (default, the headline line); the other shapes "
+                         "report the same fields for their own step (no CPU leg)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB three times (untimed), so a "
                          "counter run can scale its byte counters by a copy of known size")
@@ -86,6 +94,123 @@ def cpu_baseline(keys, queries, group, bits, seed, n_groups):
                       % (n_groups, n_seq * n_kv, n_groups * n_tok, group, dt)}
 
 
+def _rate(n, ms):
+    return n / ms * 1e3 if ms > 0 else None
+
+
+def build_workload(name, dev, W_all):
+    """Inputs resident on the device, plans, output buffers and the launch phases of one step.
+
+    Returns dict(config, phases=[(entry point, fn)], bytes={entry point: algorithmic bytes},
+    n_keys, n_scores, keep) -- each fn enqueues that entry point's launches for one step."""
+    import torch
+    import rotation_online_vector_amd as tq
+    import workloads
+    W = W_all[name]
+    if name == "longctx":
+        keys, queries, _ = workloads.longctx_inputs(dev)
+        n_seq, n_kv, n_tok, d, G = W["n_seq"], W["n_kv"], W["n_tok"], W["d"], W["group"]
+        n_keys, n_groups = n_seq * n_kv * n_tok, n_seq * n_kv
+        plan = tq.tq_plan_create(d, W["bits"], W["seed"])
+        rb = plan.record_bytes
+        codes = torch.empty((n_keys, rb), dtype=torch.uint8, device=dev)
+        scores = torch.empty((n_groups * G, n_tok), dtype=torch.float32, device=dev)
+        xk, qv = keys.view(n_keys, d), queries.view(n_groups * G, d)
+        n_scores = n_groups * G * n_tok
+        return dict(
+            config={"workload": W["name"], "n_seq": n_seq, "kv_heads": n_kv, "tokens": n_tok,
+                    "d": d, "bits": W["bits"], "query_heads_per_seq": n_kv * G, "gqa_group": G,
+                    "keys_per_step": n_keys, "scores_per_step": n_scores, "record_bytes": rb},
+            phases=[("tq_encode", lambda: tq.tq_encode(plan, xk, codes)),
+                    ("tq_score", lambda: tq.tq_score(plan, qv, codes, n=n_tok, nq_per_group=G,
+                                                     n_groups=n_groups, scores=scores))],
+            bytes={"tq_encode": n_keys * d * 2 + n_keys * rb,
+                   "tq_score": n_keys * rb + n_scores * 4 + n_groups * G * d * 2},
+            n_keys=n_keys, n_scores=n_scores,
+            keep=(plan, keys, queries, codes, scores))
+    if name == "kv":
+        keys, queries, _ = workloads.kv_inputs(dev, n_kv=W["n_kv"], n_tok=W["n_tok"], d=W["d"],
+                                               group=W["group"], n_outlier=W["n_outlier"],
+                                               outlier_scale=W["outlier_scale"], seed=W["seed"])
+        n_kv, n_tok, d, G = W["n_kv"], W["n_tok"], W["d"], W["group"]
+        n_keys = n_kv * n_tok
+        plan = tq.tq_plan_create(d, W["bits"], W["seed"])
+        rb = plan.record_bytes
+        codes = torch.empty((n_keys, rb), dtype=torch.uint8, device=dev)
+        scores = torch.empty((n_kv * G, n_tok), dtype=torch.float32, device=dev)
+        xk = keys.view(n_keys, d)
+        n_scores = n_kv * G * n_tok
+        return dict(
+            config={"workload": W["name"], "kv_heads": n_kv, "tokens": n_tok, "d": d,
+                    "bits": W["bits"], "gqa_group": G, "keys_per_step": n_keys,
+                    "scores_per_step": n_scores, "record_bytes": rb},
+            phases=[("tq_encode", lambda: tq.tq_encode(plan, xk, codes)),
+                    ("tq_score", lambda: tq.tq_score(plan, queries, codes, n=n_tok, nq_per_group=G,
+                                                     n_groups=n_kv, scores=scores))],
+            bytes={"tq_encode": n_keys * d * 2 + n_keys * rb,
+                   "tq_score": n_keys * rb + n_scores * 4 + n_kv * G * d * 2},
+            n_keys=n_keys, n_scores=n_scores, keep=(plan, keys, queries, codes, scores))
+    if name in ("split35", "split25"):
+        import numpy as np
+        keys, queries, ch = workloads.kv_inputs(dev, n_kv=W["n_kv"], n_tok=W["n_tok"], d=W["d"],
+                                                group=W["group"], n_outlier=W["n_outlier"],
+                                                outlier_scale=W["outlier_scale"], seed=W["seed"])
+        n_kv, n_tok, d, G = W["n_kv"], W["n_tok"], W["d"], W["group"]
+        plans = []
+        for h in range(n_kv):
+            mask = np.zeros(d, dtype=np.uint8)
+            mask[ch[h]] = 1
+            plans.append(tq.tq_plan_create(d, W["bits"], W["seed"], mask, W["outlier_bits"]))
+        rb = plans[0].record_bytes
+        codes = torch.empty((n_kv, n_tok, rb), dtype=torch.uint8, device=dev)
+        scores = torch.empty((n_kv, G, n_tok), dtype=torch.float32, device=dev)
+        qv = queries.view(n_kv, G, d)
+
+        def enc():
+            for h in range(n_kv):
+                tq.tq_encode(plans[h], keys[h], codes[h])
+
+        def sco():
+            for h in range(n_kv):
+                tq.tq_score(plans[h], qv[h], codes[h], n=n_tok, scores=scores[h])
+        n_keys, n_scores = n_kv * n_tok, n_kv * G * n_tok
+        return dict(
+            config={"workload": W["name"], "kv_heads": n_kv, "tokens": n_tok, "d": d,
+                    "bits": W["bits"], "outlier_bits": W["outlier_bits"],
+                    "outlier_channels": W["n_outlier"], "gqa_group": G, "keys_per_step": n_keys,
+                    "scores_per_step": n_scores, "record_bytes": rb},
+            phases=[("tq_encode", enc), ("tq_score", sco)],
+            bytes={"tq_encode": n_keys * d * 2 + n_keys * rb,
+                   "tq_score": n_keys * rb + n_scores * 4 + n_kv * G * d * 2},
+            n_keys=n_keys, n_scores=n_scores, keep=(plans, keys, queries, codes, scores))
+    if name in ("retrieval", "small"):
+        if name == "retrieval":
+            keys, queries = workloads.retrieval_inputs(dev, n_keys=W["n_keys"],
+                                                       n_queries=W["n_queries"], d=W["d"],
+                                                       seed=W["seed"])
+        else:
+            k_np, q_np = workloads.small_inputs(W["n_keys"], W["n_queries"], W["d"], W["seed"])
+            keys, queries = torch.from_numpy(k_np).to(dev), torch.from_numpy(q_np).to(dev)
+        n, nq, d, k = W["n_keys"], W["n_queries"], W["d"], W.get("topk", 10)
+        plan = tq.tq_plan_create(d, W["bits"], W["seed"])
+        rb = plan.record_bytes
+        codes = torch.empty((n, rb), dtype=torch.uint8, device=dev)
+        scores = torch.empty((nq, n), dtype=torch.float32, device=dev)
+        ids = torch.empty((nq, k), dtype=torch.int64, device=dev)
+        vals = torch.empty((nq, k), dtype=torch.float32, device=dev)
+        return dict(
+            config={"workload": W["name"], "keys": n, "queries": nq, "d": d,
+                    "D": plan.desc["sub"][0]["D"], "bits": W["bits"], "topk": k,
+                    "keys_per_step": n, "scores_per_step": n * nq, "record_bytes": rb},
+            phases=[("tq_encode", lambda: tq.tq_encode(plan, keys, codes)),
+                    ("tq_score", lambda: tq.tq_score(plan, queries, codes, n=n, scores=scores)),
+                    ("tq_topk", lambda: tq.tq_topk(scores, k, ids, vals))],
+            bytes={"tq_encode": n * d * 4 + n * rb, "tq_score": n * rb + n * nq * 4 + nq * d * 4,
+                   "tq_topk": n * nq * 4 + nq * k * 12},
+            n_keys=n, n_scores=n * nq, keep=(plan, keys, queries, codes, scores, ids, vals))
+    raise ValueError(name)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -94,33 +219,24 @@ def main():
         sys.exit(2)
     import numpy as np
     import torch
-    import rotation_online_vector_amd as tq
     import workloads
 
-    W = workloads.LONGCTX
+    W_all = {"longctx": workloads.LONGCTX, "kv": workloads.KV, "split35": workloads.SPLIT,
+             "split25": workloads.SPLIT_25, "retrieval": workloads.RETRIEVAL,
+             "small": workloads.SMALL}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    keys, queries, _ = workloads.longctx_inputs(dev)
-    n_seq, n_kv, n_tok, d, G = W["n_seq"], W["n_kv"], W["n_tok"], W["d"], W["group"]
-    n_keys = n_seq * n_kv * n_tok
-    n_groups = n_seq * n_kv
-    plan = tq.tq_plan_create(d, W["bits"], W["seed"])
-    rb = plan.record_bytes
-    codes = torch.empty((n_keys, rb), dtype=torch.uint8, device=dev)
-    scores = torch.empty((n_seq * n_kv * G, n_tok), dtype=torch.float32, device=dev)
-    xk = keys.view(n_keys, d)
-    qv = queries.view(n_groups * G, d)
+    wl = build_workload(args.workload, dev, W_all)
+    phases = wl["phases"]
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
+        for i, (_, fn) in enumerate(phases):
+            if ev is not None:
+                ev[i].record(stream)
+            fn()
         if ev is not None:
-            ev[0].record(stream)
-        tq.tq_encode(plan, xk, codes)
-        if ev is not None:
-            ev[1].record(stream)
-        tq.tq_score(plan, qv, codes, n=n_tok, nq_per_group=G, n_groups=n_groups, scores=scores)
-        if ev is not None:
-            ev[2].record(stream)
+            ev[len(phases)].record(stream)
 
     if args.copy_calibration > 0:
         nb = args.copy_calibration << 20
@@ -133,50 +249,44 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(phases) + 1)]
+           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(evs[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    enc_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    sc_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
     ms_step = wall * 1e3 / args.steps
-    n_scores = n_groups * G * n_tok
-
-    # algorithmic bytes per launch
-    enc_bytes = n_keys * d * 2 + n_keys * rb                     # bf16 keys in, records out
-    sc_bytes = n_keys * rb + n_scores * 4 + n_groups * G * d * 2  # records + logits + queries
-    kern = {
-        "tq_encode": {"ms": enc_ms, "bytes": enc_bytes, "gbs": enc_bytes / enc_ms / 1e6,
-                      "vectors_per_s": n_keys / enc_ms * 1e3},
-        "tq_score": {"ms": sc_ms, "bytes": sc_bytes, "gbs": sc_bytes / sc_ms / 1e6,
-                     "scores_per_s": n_scores / sc_ms * 1e3},
-    }
+    kern = {}
+    for i, (nm, _) in enumerate(phases):
+        ms = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+        b = wl["bytes"][nm]
+        kern[nm] = {"ms": ms, "bytes": b, "gbs": b / ms / 1e6}
     dom = max(kern, key=lambda k: kern[k]["ms"])
+    traffic = measured_traffic(dom) if args.workload == "longctx" else None
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(kern[dom]["gbs"], 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(dom), "bytes_per_launch": kern[dom]["bytes"]}
+            "traffic": traffic, "bytes_per_launch": kern[dom]["bytes"]}
     out = {
         "metric": "quantized-key scores/sec + HBM GB/s (d=128, 3-bit); encode vectors/sec",
-        "value": n_scores / (ms_step / 1e3),
+        "value": wl["n_scores"] / (ms_step / 1e3),
         "unit": "scores/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
-        "config": {"workload": W["name"], "n_seq": n_seq, "kv_heads": n_kv, "tokens": n_tok,
-                   "d": d, "bits": W["bits"], "query_heads_per_seq": n_kv * G, "gqa_group": G,
-                   "keys_per_step": n_keys, "scores_per_step": n_scores, "record_bytes": rb},
-        "encode_vectors_per_s": kern["tq_encode"]["vectors_per_s"],
-        "score_scores_per_s": kern["tq_score"]["scores_per_s"],
+        "config": wl["config"],
+        "encode_vectors_per_s": _rate(wl["n_keys"], kern["tq_encode"]["ms"]),
+        "score_scores_per_s": _rate(wl["n_scores"], kern["tq_score"]["ms"]),
         "kernels": {k: {"ms": round(v["ms"], 4), "alg_bytes": v["bytes"], "alg_gbs": round(v["gbs"], 1),
                         "hbm_frac": round(v["gbs"] / HBM_PEAK_GBS, 4)} for k, v in kern.items()},
         "roofline": roof,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(keys, queries, G, W["bits"], W["seed"],
+    if args.workload == "longctx" and not args.no_cpu_baseline:
+        W = W_all["longctx"]
+        keys, queries = wl["keep"][1], wl["keep"][2]
+        out["cpu_baseline"] = cpu_baseline(keys, queries, W["group"], W["bits"], W["seed"],
                                            args.cpu_sample_groups)
     print(json.dumps(out), flush=True)
 
