@@ -1255,6 +1255,202 @@ __global__ void __launch_bounds__(kBlock) score_bitslice_kernel(ScoreArgs a, int
   }
 }
 
+// ------------------------------------------------------------ bit-sliced scorer, D > 128
+// The same binary-plane form for long vectors and many queries per group (retrieval): the
+// 128-coordinate chunks of a key are MFMA steps of one accumulation, and a 16-row image
+// tile holds eight queries in two fp8 limbs each (row 2 q + limb), which keeps every
+// coordinate to about 2^-10 of its value (the score tolerance is 1e-3 ||q|| ||x||).
+constexpr int kWideQT = 8;        // queries per image tile
+constexpr int kWideKT = 16;       // 16-key tiles per wave (256 keys per block)
+
+struct WideImgArgs {
+  SubDev s;
+  const float* yrot;     // [nq][D]
+  const float* w;        // [nq][D]
+  const float* sums;     // [nq][2]
+  int64_t nq_per_group;
+  int n_qtiles;          // tiles of kWideQT queries per group
+  uint32_t* img;         // [groups*qtiles][D/128][n_planes+1][64][8]
+  float* ec;             // [groups*qtiles][kWideQT][4]
+};
+
+// One workgroup per image tile: per-query maxima, power-of-two scales, both limbs of every
+// plane image of every chunk, the epilogue constants.
+__global__ void __launch_bounds__(kBlock) qimage_wide_kernel(WideImgArgs a) {
+  const SubDev& s = a.s;
+  const int D = s.D, np = s.n_planes, nch = D / 128;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t gt = blockIdx.x;
+  const int64_t grp = gt / a.n_qtiles, qt = gt % a.n_qtiles;
+  __shared__ float mx[kWideQT][2][kBlock / kWave];
+  __shared__ float scl[kWideQT][2];
+  int valid = (int)(a.nq_per_group - qt * kWideQT);
+  valid = valid > kWideQT ? kWideQT : valid;
+  for (int q = 0; q < kWideQT; ++q) {
+    float my = 0.f, mw = 0.f;
+    if (q < valid) {
+      const int64_t qi = grp * a.nq_per_group + qt * kWideQT + q;
+      for (int i = tid; i < D; i += kBlock) {
+        my = fmaxf(my, fabsf(a.yrot[qi * D + i]));
+        mw = fmaxf(mw, fabsf(a.w[qi * D + i]));
+      }
+    }
+    for (int m = 32; m >= 1; m >>= 1) {
+      my = fmaxf(my, __shfl_xor(my, m));
+      mw = fmaxf(mw, __shfl_xor(mw, m));
+    }
+    if (lane == 0) {
+      mx[q][0][wave] = my;
+      mx[q][1][wave] = mw;
+    }
+  }
+  __syncthreads();
+  if (tid < kWideQT) {
+    float my = 0.f, mw = 0.f;
+    for (int w = 0; w < kBlock / kWave; ++w) {
+      my = fmaxf(my, mx[tid][0][w]);
+      mw = fmaxf(mw, mx[tid][1][w]);
+    }
+    float cmax = 0.f;
+    for (int p = 0; p < np; ++p) cmax = fmaxf(cmax, fabsf(s.coef[p]));
+    const float M1 = my * cmax;
+    // powers of two putting the largest image magnitude in (128, 256]
+    const float sc_mse = M1 > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(M1))) : 1.f;
+    const float sc_qjl = mw > 0.f ? ldexpf(1.f, 8 - (int)ceilf(log2f(mw))) : 1.f;
+    scl[tid][0] = sc_mse;
+    scl[tid][1] = sc_qjl;
+    float* e = a.ec + ((size_t)gt * kWideQT + tid) * 4;
+    if (tid < valid) {
+      const int64_t qi = grp * a.nq_per_group + qt * kWideQT + tid;
+      const float K = sqrtf(0.5f * (float)M_PI) / (float)s.k;
+      e[0] = -s.coef_sum * a.sums[qi * 2];
+      e[1] = 4.f / sc_mse;
+      e[2] = -K * a.sums[qi * 2 + 1];
+      e[3] = 4.f * K / sc_qjl;
+    } else {
+      e[0] = e[1] = e[2] = e[3] = 0.f;
+    }
+  }
+  __syncthreads();
+  // image dword (chunk, plane, lane, word): row = lane % 16 = 2 q + limb, lane group G
+  const int total = nch * (np + 1) * 64 * 8;
+  for (int it = tid; it < total; it += kBlock) {
+    const int wd = it & 7, ln = (it >> 3) & 63, cp = it >> 9;
+    const int p = cp % (np + 1), c = cp / (np + 1);
+    const int row = ln & 15, Ga = ln >> 4, q = row >> 1, limb = row & 1;
+    uint32_t word = 0;
+    if (q < valid) {
+      const int64_t qi = grp * a.nq_per_group + qt * kWideQT + q;
+      const float cf = p < np ? s.coef[p] * scl[q][0] : scl[q][1];
+      const float* src = (p < np ? a.yrot : a.w) + qi * D + 128 * c;
+      float rem[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int e = 4 * wd + b;
+        const int K = e < 16 ? 16 * Ga + e : 64 + 16 * Ga + (e - 16);
+        rem[b] = cf * src[bitslice_coord(K)];
+      }
+      // limb l = fp8 e4m3 (round to nearest even) of what limbs 0..l-1 left over
+      for (int l = 0; l <= limb; ++l) {
+        word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rem[0], rem[1], 0, false);
+        word = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(rem[2], rem[3], (int)word, true);
+        rem[0] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 0);
+        rem[1] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 1);
+        rem[2] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 2);
+        rem[3] -= __builtin_amdgcn_cvt_f32_fp8((int)word, 3);
+      }
+    }
+    a.img[(size_t)gt * total + it] = word;
+  }
+}
+
+// grid.x = (group, block of 4 image tiles), fastest, so that the blocks reading the same keys
+// run together and share them through the caches; grid.y strides over 256-key blocks.  Each
+// wave owns one image tile (8 queries) and 16 key tiles, whose accumulators stay in registers
+// across the chunks; per chunk it loads the plane images once for its 16 key tiles.
+template <int R>
+__global__ void __launch_bounds__(kBlock) score_wide_kernel(ScoreArgs a, int64_t n_qblocks) {
+  constexpr int NP = 1 << (R - 1);
+  const SubDev& s = a.p.sub[0];
+  const int nch = s.D / 128;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = lane >> 4, col = lane & 15;
+  const int64_t grp = blockIdx.x / n_qblocks;
+  const int64_t qt = (blockIdx.x % n_qblocks) * (kBlock / kWave) + wave;
+  if (qt >= a.n_qtiles) return;
+  const int64_t gt = grp * a.n_qtiles + qt;
+  const int64_t nkb = (a.n + kWideKT * 16 - 1) / (kWideKT * 16);
+  const uint8_t* codes = a.codes + grp * a.n * (int64_t)a.p.rec_bytes;
+  // epilogue constants of this lane's two queries (rows 4 G .. 4 G + 3 = queries 2 G, 2 G + 1)
+  float ea[4], eb[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    ea[i] = a.ec[0][((size_t)gt * kWideQT + 2 * G) * 4 + i];
+    eb[i] = a.ec[0][((size_t)gt * kWideQT + 2 * G + 1) * 4 + i];
+  }
+  const int64_t qa = qt * kWideQT + 2 * G;
+  const bool qa_ok = qa < a.nq_per_group, qb_ok = qa + 1 < a.nq_per_group;
+  float* out_a = a.scores + (grp * a.nq_per_group + qa) * a.n;
+  float* out_b = out_a + a.n;
+  const uint32_t* img = a.img[0] + (size_t)gt * nch * (NP + 1) * 64 * 8 + lane * 8;
+  for (int64_t kb = blockIdx.y; kb < nkb; kb += gridDim.y) {
+    const int64_t k0 = kb * kWideKT * 16;
+    f32x4 am[kWideKT], aq[kWideKT];
+#pragma unroll
+    for (int t = 0; t < kWideKT; ++t) {
+      am[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      aq[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    }
+    for (int c = 0; c < nch; ++c) {
+      i32x8 A[NP + 1];
+#pragma unroll
+      for (int p = 0; p <= NP; ++p) {
+        const uint4* src = reinterpret_cast<const uint4*>(img + ((size_t)c * (NP + 1) + p) * 64 * 8);
+        const uint4 u0 = src[0], u1 = src[1];
+        A[p][0] = u0.x; A[p][1] = u0.y; A[p][2] = u0.z; A[p][3] = u0.w;
+        A[p][4] = u1.x; A[p][5] = u1.y; A[p][6] = u1.z; A[p][7] = u1.w;
+      }
+      const int cc = 4 * c + G;                  // 32-coordinate code chunk of this lane group
+#pragma unroll
+      for (int t = 0; t < kWideKT; ++t) {
+        int64_t key = k0 + 16 * t + col;
+        key = key < a.n ? key : a.n - 1;         // past the end: a real key, never stored
+        const uint32_t* pw = reinterpret_cast<const uint32_t*>(codes + key * a.p.rec_bytes) +
+                             cc * (R + 1);
+        uint32_t wd[R + 1];
+#pragma unroll
+        for (int m = 0; m <= R; ++m) wd[m] = pw[m];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+          uint32_t P = 0;
+#pragma unroll
+          for (int m = 0; m < R; ++m)
+            if ((pmask_c<R>(p) >> m) & 1) P ^= wd[m];
+          am[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[p], fp4_operand(P), am[t], 0, 4, 0, 127, 0, 127);
+        }
+        aq[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[NP], fp4_operand(wd[R]), aq[t], 0, 4, 0, 127, 0, 127);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kWideKT; ++t) {
+      const int64_t key = k0 + 16 * t + col;
+      const bool key_ok = key < a.n;
+      const int64_t ks = key_ok ? key : a.n - 1;
+      const uint32_t* tail = reinterpret_cast<const uint32_t*>(codes + ks * a.p.rec_bytes +
+                                                               (s.D / 32) * (R + 1) * 4);
+      const float nrm = __uint_as_float(tail[0]), gam = __uint_as_float(tail[1]);
+      float est_a = nrm * (fmaf(ea[1], am[t][0] + am[t][1], ea[0]) +
+                           gam * fmaf(ea[3], aq[t][0] + aq[t][1], ea[2]));
+      float est_b = nrm * (fmaf(eb[1], am[t][2] + am[t][3], eb[0]) +
+                           gam * fmaf(eb[3], aq[t][2] + aq[t][3], eb[2]));
+      // full-wave region: keep the MFMA results from being sunk into the masked stores
+      asm volatile("" : "+v"(est_a), "+v"(est_b));
+      if (key_ok && qa_ok) out_a[key] = est_a;
+      if (key_ok && qb_ok) out_b[key] = est_b;
+    }
+  }
+}
+
 // Vector-unit scorer for any D: one key per thread, up to kQT queries of a group per block,
 // rotated query and its projection staged in LDS (2 kQT sum(D) floats <= 64 KiB).
 template <int kQT>
@@ -1508,10 +1704,15 @@ int launch_qjl(const SubDev& s, const float* r, int64_t n, uint32_t* beta, void*
 
 template <int R0, int R1>
 static void launch_bitslice(const ScoreArgs& sa, int64_t n_gt, hipStream_t st) {
-  const int kpb = 2048;
+  // 2048 keys per block when that still gives ~2048 blocks; fewer (down to one 256-key batch
+  // per block) for short code sets, so that small problems still spread over the chip
+  const int64_t per_gt = n_gt >= 2048 ? 1 : 2048 / n_gt;
+  int64_t kpb = (sa.n + per_gt - 1) / per_gt;
+  kpb = (kpb + 255) / 256 * 256;
+  kpb = kpb < 256 ? 256 : (kpb > 2048 ? 2048 : kpb);
   const int64_t kblocks = (sa.n + kpb - 1) / kpb;
   hipLaunchKernelGGL((score_bitslice_kernel<R0, R1>), dim3((unsigned)kblocks, (unsigned)n_gt),
-                     dim3(kBlock), 0, st, sa, kpb);
+                     dim3(kBlock), 0, st, sa, (int)kpb);
 }
 
 static bool dispatch_bitslice(const ScoreArgs& sa, int64_t n_gt, hipStream_t st) {
@@ -1534,6 +1735,9 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
   bool small = true;
   for (int sb = 0; sb < p.nsub; ++sb) small = small && p.sub[sb].D <= 128;
   const int qt_bs = (int)((nq_per_group + 3) / 4);
+  // long vectors with many queries per group: the bit-sliced form over 128-coordinate chunks
+  const bool wide = !small && p.nsub == 1 && nq_per_group >= kWideQT && p.sub[0].D % 128 == 0;
+  const int qt_w = (int)((nq_per_group + kWideQT - 1) / kWideQT);
   // workspace: per sub-plan y', w, sums, images, epilogue constants
   size_t bytes = 0;
   size_t off_y[2], off_w[2], off_s[2], off_img[2], off_ec[2];
@@ -1546,6 +1750,9 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
     if (small) {
       off_img[sb] = take((size_t)n_groups * qt_bs * (p.sub[sb].n_planes + 1) * 64 * 32);
       off_ec[sb] = take((size_t)n_groups * qt_bs * 16 * 4);
+    } else if (wide) {
+      off_img[sb] = take((size_t)n_groups * qt_w * (D / 128) * (p.sub[sb].n_planes + 1) * 64 * 32);
+      off_ec[sb] = take((size_t)n_groups * qt_w * kWideQT * 4 * 4);
     }
   }
   void* ws = nullptr;
@@ -1591,12 +1798,39 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
       sa.ec[sb] = fa.ec;
     } else {
       hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)nq), dim3(kBlock), 0, st, qa);
+      if (wide) {
+        WideImgArgs wa;
+        wa.s = p.sub[sb];
+        wa.yrot = qa.yrot;
+        wa.w = qa.w;
+        wa.sums = qa.sums;
+        wa.nq_per_group = nq_per_group;
+        wa.n_qtiles = qt_w;
+        wa.img = reinterpret_cast<uint32_t*>(wb + off_img[sb]);
+        wa.ec = reinterpret_cast<float*>(wb + off_ec[sb]);
+        hipLaunchKernelGGL(qimage_wide_kernel, dim3((unsigned)(n_groups * qt_w)), dim3(kBlock), 0,
+                           st, wa);
+        sa.img[sb] = wa.img;
+        sa.ec[sb] = wa.ec;
+      }
     }
   }
   int rc = 0;
   if (small) {
     sa.n_qtiles = qt_bs;
     if (!dispatch_bitslice(sa, n_groups * qt_bs, st)) rc = (int)hipErrorInvalidValue;
+  } else if (wide) {
+    sa.n_qtiles = qt_w;
+    const int64_t n_qblocks = (qt_w + kBlock / kWave - 1) / (kBlock / kWave);
+    const int64_t nkb = (n + kWideKT * 16 - 1) / (kWideKT * 16);
+    const dim3 grid((unsigned)(n_groups * n_qblocks), (unsigned)(nkb < 65535 ? nkb : 65535));
+    switch (p.sub[0].R) {
+      case 1: hipLaunchKernelGGL(score_wide_kernel<1>, grid, dim3(kBlock), 0, st, sa, n_qblocks); break;
+      case 2: hipLaunchKernelGGL(score_wide_kernel<2>, grid, dim3(kBlock), 0, st, sa, n_qblocks); break;
+      case 3: hipLaunchKernelGGL(score_wide_kernel<3>, grid, dim3(kBlock), 0, st, sa, n_qblocks); break;
+      case 4: hipLaunchKernelGGL(score_wide_kernel<4>, grid, dim3(kBlock), 0, st, sa, n_qblocks); break;
+      default: rc = (int)hipErrorInvalidValue;
+    }
   } else {
     int sumD = 0;
     for (int sb = 0; sb < p.nsub; ++sb) sumD += p.sub[sb].D;

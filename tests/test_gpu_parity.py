@@ -172,6 +172,31 @@ def test_encode_over_a_wide_range_of_norms(d, dtype, lo, hi):
         _encode_and_compare(sp, plan, x, "norms 1e%d..1e%d d=%d b=%d" % (lo, hi, d, bits))
 
 
+@pytest.mark.parametrize("d,bits,n,nqg,groups", [
+    (256, 4, 1000, 8, 1), (2048, 4, 300, 13, 1), (1536, 3, 517, 40, 1), (512, 2, 260, 16, 2),
+    (1024, 5, 129, 9, 2), (200, 3, 777, 64, 1)])
+def test_score_many_queries_long_vectors(d, bits, n, nqg, groups):
+    """The chunked bit-sliced scorer (D > 128, at least 8 queries per group), on oracle codes:
+    ragged key counts (not a multiple of the 256-key block), ragged query tiles of 8."""
+    rng = np.random.default_rng(d + nqg)
+    xs = rng.standard_normal((groups * n, d)).astype(np.float32)
+    xs[3] = 0.0
+    ys = rng.standard_normal((groups * nqg, d)).astype(np.float32)
+    sp = otq.make_split_plan(d, bits, 5)
+    plan = tq.tq_plan_create(d, bits, 5)
+    ref = otq.encode_split(sp, xs.astype(np.float64))
+    rec = torch.from_numpy(layout.pack_split(sp, [parity.stored(c) for c in ref])).to(DEV)
+    y = torch.from_numpy(ys).to(DEV)
+    est = tq.tq_score(plan, y, rec, n=n, nq_per_group=nqg, n_groups=groups).cpu().numpy()
+    st = parity.stored(ref[0])
+    for g in range(groups):
+        sub = {k: v[g * n:(g + 1) * n] for k, v in st.items()}
+        est_ref = otq.score(sp.plans[0], sub, ys[g * nqg:(g + 1) * nqg].astype(np.float64))
+        parity.check_scores(est[g * nqg:(g + 1) * nqg], est_ref,
+                            np.linalg.norm(ys[g * nqg:(g + 1) * nqg], axis=1),
+                            np.linalg.norm(xs[g * n:(g + 1) * n], axis=1), "d=%d group %d" % (d, g))
+
+
 def test_strided_rows_and_query_groups():
     d, n = 128, 300
     rng = np.random.default_rng(5)
