@@ -1261,7 +1261,7 @@ __global__ void __launch_bounds__(kBlock) score_bitslice_kernel(ScoreArgs a, int
 // tile holds eight queries in two fp8 limbs each (row 2 q + limb), which keeps every
 // coordinate to about 2^-10 of its value (the score tolerance is 1e-3 ||q|| ||x||).
 constexpr int kWideQT = 8;        // queries per image tile
-constexpr int kWideKT = 16;       // 16-key tiles per wave (256 keys per block)
+constexpr int kWideKT = 8;        // 16-key tiles per wave (128 keys per block)
 
 struct WideImgArgs {
   SubDev s;
@@ -1365,9 +1365,9 @@ __global__ void __launch_bounds__(kBlock) qimage_wide_kernel(WideImgArgs a) {
 }
 
 // grid.x = (group, block of 4 image tiles), fastest, so that the blocks reading the same keys
-// run together and share them through the caches; grid.y strides over 256-key blocks.  Each
-// wave owns one image tile (8 queries) and 16 key tiles, whose accumulators stay in registers
-// across the chunks; per chunk it loads the plane images once for its 16 key tiles.
+// run together and share them through the caches; grid.y strides over 128-key blocks.  Each
+// wave owns one image tile (8 queries) and 8 key tiles, whose accumulators stay in registers
+// across the chunks; per chunk it loads the plane images once for its 8 key tiles.
 template <int R>
 __global__ void __launch_bounds__(kBlock) score_wide_kernel(ScoreArgs a, int64_t n_qblocks) {
   constexpr int NP = 1 << (R - 1);
@@ -1396,10 +1396,14 @@ __global__ void __launch_bounds__(kBlock) score_wide_kernel(ScoreArgs a, int64_t
   for (int64_t kb = blockIdx.y; kb < nkb; kb += gridDim.y) {
     const int64_t k0 = kb * kWideKT * 16;
     f32x4 am[kWideKT], aq[kWideKT];
-#pragma unroll
+    const uint32_t* rec[kWideKT];                // this lane's key of each tile (clamped: a
+#pragma unroll                                    // real key past the end, never stored)
     for (int t = 0; t < kWideKT; ++t) {
       am[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
       aq[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      int64_t key = k0 + 16 * t + col;
+      key = key < a.n ? key : a.n - 1;
+      rec[t] = reinterpret_cast<const uint32_t*>(codes + key * a.p.rec_bytes) + G * (R + 1);
     }
     for (int c = 0; c < nch; ++c) {
       i32x8 A[NP + 1];
@@ -1410,25 +1414,23 @@ __global__ void __launch_bounds__(kBlock) score_wide_kernel(ScoreArgs a, int64_t
         A[p][0] = u0.x; A[p][1] = u0.y; A[p][2] = u0.z; A[p][3] = u0.w;
         A[p][4] = u1.x; A[p][5] = u1.y; A[p][6] = u1.z; A[p][7] = u1.w;
       }
-      const int cc = 4 * c + G;                  // 32-coordinate code chunk of this lane group
+      // code chunk 4 c + G of every tile's key: all loads issued before the first use
+      uint32_t wd[kWideKT][R + 1];
+#pragma unroll
+      for (int t = 0; t < kWideKT; ++t)
+#pragma unroll
+        for (int m = 0; m <= R; ++m) wd[t][m] = rec[t][4 * c * (R + 1) + m];
 #pragma unroll
       for (int t = 0; t < kWideKT; ++t) {
-        int64_t key = k0 + 16 * t + col;
-        key = key < a.n ? key : a.n - 1;         // past the end: a real key, never stored
-        const uint32_t* pw = reinterpret_cast<const uint32_t*>(codes + key * a.p.rec_bytes) +
-                             cc * (R + 1);
-        uint32_t wd[R + 1];
-#pragma unroll
-        for (int m = 0; m <= R; ++m) wd[m] = pw[m];
 #pragma unroll
         for (int p = 0; p < NP; ++p) {
           uint32_t P = 0;
 #pragma unroll
           for (int m = 0; m < R; ++m)
-            if ((pmask_c<R>(p) >> m) & 1) P ^= wd[m];
+            if ((pmask_c<R>(p) >> m) & 1) P ^= wd[t][m];
           am[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[p], fp4_operand(P), am[t], 0, 4, 0, 127, 0, 127);
         }
-        aq[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[NP], fp4_operand(wd[R]), aq[t], 0, 4, 0, 127, 0, 127);
+        aq[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[NP], fp4_operand(wd[t][R]), aq[t], 0, 4, 0, 127, 0, 127);
       }
     }
 #pragma unroll
