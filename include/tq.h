@@ -102,11 +102,15 @@ tq_status tq_plan_info(const tq_plan* plan, tq_plan_desc* desc);
 
 /*
  * Encode n vectors (norm split, rotation, Lloyd-Max indices, residual norm,
- * QJL signs: overview §1.2, §2.1, §2.3; one fused launch).
+ * QJL signs: overview §1.2, §2.1, §2.3; one fused launch for D <= 512).
  *   x      device, n rows of d elements of type dt, row i at x + i*ldx elements;
  *          4-byte aligned (bf16) / 4-byte aligned (f32)
  *   ldx    row stride in elements, ldx >= d
  *   codes  device, n * record_bytes bytes, 16-byte aligned; written entirely
+ * For sub-plans with D >= 1024 the signs are computed by a second launch over
+ * batches of up to 32768 vectors, whose residuals are kept in a stream-ordered
+ * temporary of 4*D bytes per vector of the batch (hipMallocAsync / hipFreeAsync
+ * on `stream`); an allocation failure is reported as TQ_ENOMEM or TQ_EDEVICE.
  * Errors: TQ_EINVAL (null with n > 0, n < 0, ldx < d, misalignment),
  * TQ_EDEVICE.  n = 0 is a no-op.
  */

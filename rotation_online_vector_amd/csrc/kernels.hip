@@ -150,17 +150,21 @@ struct EncodeArgs {
   int rec_bytes;
   int is_bf16;
   int vec_load;   // rows 16-byte aligned and no channel gather: vector loads
+  uint16_t* rw_hi;  // two-pass encode (long vectors): residual limbs [n][D], high and low
+  uint16_t* rw_lo;
 };
 
-template <int D, int R>
+// SPLIT: the QJL stage is left to qjl_gemm_kernel; the residual limbs go to a.rw_hi/rw_lo
+// instead of LDS and the sign words of the records are written by that kernel.
+template <int D, int R, bool SPLIT = false>
 __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
   using C = EncCfg<D>;
   constexpr int EPT = C::EPT, TPV = C::TPV, VPP = C::VPP, V = C::V, RS = C::RSTRIDE;
   constexpr int L = 1 << R;
   const SubDev& s = a.s;
   const int recw = s.rec_sub / 4;   // words per sub-record
-  __shared__ __attribute__((aligned(16))) uint16_t rhi[V * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t rlo[V * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t rhi[SPLIT ? 8 : V * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t rlo[SPLIT ? 8 : V * RS];
   __shared__ __attribute__((aligned(16))) uint32_t rec[V * ((4 * (R + 1) * D / 32 + 8) / 4)];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -272,12 +276,22 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
         hi[e / 2] = h0 | (h1 << 16);
         lo[e / 2] = l0 | (l1 << 16);
       }
-      uint4* ph = reinterpret_cast<uint4*>(rhi + vl * RS + c0);
-      uint4* pl = reinterpret_cast<uint4*>(rlo + vl * RS + c0);
+      uint4* ph;
+      uint4* pl;
+      if constexpr (SPLIT) {
+        const int64_t rrow = live ? row : a.n - 1;   // dead lanes rewrite a real row's limbs...
+        ph = reinterpret_cast<uint4*>(a.rw_hi + rrow * D + c0);
+        pl = reinterpret_cast<uint4*>(a.rw_lo + rrow * D + c0);
+      } else {
+        ph = reinterpret_cast<uint4*>(rhi + vl * RS + c0);
+        pl = reinterpret_cast<uint4*>(rlo + vl * RS + c0);
+      }
+      if (!SPLIT || live) {                           // ...so they store nothing instead
 #pragma unroll
-      for (int q = 0; q < EPT / 8; ++q) {
-        ph[q] = make_uint4(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
-        pl[q] = make_uint4(lo[4 * q], lo[4 * q + 1], lo[4 * q + 2], lo[4 * q + 3]);
+        for (int q = 0; q < EPT / 8; ++q) {
+          ph[q] = make_uint4(hi[4 * q], hi[4 * q + 1], hi[4 * q + 2], hi[4 * q + 3]);
+          pl[q] = make_uint4(lo[4 * q], lo[4 * q + 1], lo[4 * q + 2], lo[4 * q + 3]);
+        }
       }
     }
     // ---- index bit-planes, norm and gamma into the staged record ----
@@ -298,8 +312,10 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
     }
   }
   __syncthreads();
-  qjl_signs_mfma<D, V>(s, rhi, rlo, rec, recw, R + 1, R);
-  __syncthreads();
+  if constexpr (!SPLIT) {
+    qjl_signs_mfma<D, V>(s, rhi, rlo, rec, recw, R + 1, R);
+    __syncthreads();
+  }
   // ---- write records ----
   const int64_t nv = (a.n - tile0 < V) ? (a.n - tile0) : V;
   if (s.rec_sub == a.rec_bytes) {
@@ -317,6 +333,118 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
       reinterpret_cast<uint32_t*>(a.codes + (tile0 + vv) * a.rec_bytes + s.rec_off)[w] = rec[i];
     }
   }
+}
+
+// ------------------------------------------------------------ QJL signs as a tiled GEMM
+// For long vectors (D >= 1024) the projection P = R S^T of a batch of residuals R (two bf16
+// limbs each, written by encode_kernel<.., SPLIT>) is one large product: streaming all of S
+// (8 MiB at D = 2048) for every 16 vectors, as the fused kernel does, would move far more
+// than the residuals themselves.  Block tile: 128 vectors x 256 rows of S, k steps of 32
+// coordinates through double-buffered LDS; 8 waves, each 64 vectors x 64 rows (4 x 4 MFMA
+// tiles, both limbs into one accumulator).  The signs go straight into the records.
+constexpr int kQgBN = 128, kQgBM = 256, kQgKS = 32, kQgRS = kQgKS + 8;   // LDS row: 80 B
+
+struct QjlGemmArgs {
+  const uint16_t* rh;    // [nv][D]
+  const uint16_t* rl;
+  const uint16_t* S;     // [D][D] bf16
+  uint8_t* codes;        // record of the batch's first vector
+  int64_t nv;
+  int rec_bytes, rec_off, R;
+};
+
+template <int D>
+__global__ void __launch_bounds__(512) qjl_gemm_kernel(QjlGemmArgs a) {
+  static_assert(D % kQgBM == 0, "rows of S in whole blocks");
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][2][kQgBN * kQgRS];   // [buf][limb]
+  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kQgBM * kQgRS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = lane & 15, grp = lane >> 4;
+  const int vh = wave & 1, rq = wave >> 1;
+  const int64_t v0 = (int64_t)blockIdx.y * kQgBN;
+  const int r0 = blockIdx.x * kQgBM;
+  // global -> LDS items: A (limb, vector, 16-byte quarter) and B (row, quarter), 2 each
+  const uint16_t* asrc[2];
+  const uint16_t* bsrc[2];
+  int adst[2], bdst[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int it = tid + 512 * i;
+    const int limb = it >> 9, vv = (it >> 2) & (kQgBN - 1), q = it & 3;
+    int64_t v = v0 + vv;
+    v = v < a.nv ? v : a.nv - 1;            // past the batch: a real row, never stored
+    asrc[i] = (limb ? a.rl : a.rh) + v * D + 8 * q;
+    adst[i] = limb * kQgBN * kQgRS + vv * kQgRS + 8 * q;
+    const int rr = it >> 2;
+    bsrc[i] = a.S + (size_t)(r0 + rr) * D + 8 * q;
+    bdst[i] = rr * kQgRS + 8 * q;
+  }
+  uint4 ra0, ra1, rb0, rb1;
+#define TQ_QG_LOAD(k0)                                                     \
+  ra0 = *reinterpret_cast<const uint4*>(asrc[0] + (k0));                   \
+  ra1 = *reinterpret_cast<const uint4*>(asrc[1] + (k0));                   \
+  rb0 = *reinterpret_cast<const uint4*>(bsrc[0] + (k0));                   \
+  rb1 = *reinterpret_cast<const uint4*>(bsrc[1] + (k0));
+#define TQ_QG_STORE(buf)                                                   \
+  *reinterpret_cast<uint4*>(&As[buf][0][0] + adst[0]) = ra0;               \
+  *reinterpret_cast<uint4*>(&As[buf][0][0] + adst[1]) = ra1;               \
+  *reinterpret_cast<uint4*>(&Bs[buf][0] + bdst[0]) = rb0;                  \
+  *reinterpret_cast<uint4*>(&Bs[buf][0] + bdst[1]) = rb1;
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  TQ_QG_LOAD(0)
+  TQ_QG_STORE(0)
+  __syncthreads();
+  constexpr int NK = D / kQgKS;
+  for (int ks = 0; ks < NK; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < NK) { TQ_QG_LOAD(kQgKS * (ks + 1)) }   // next step's tiles, in flight
+    bf16x8 bo[4];
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+      bo[rt] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(64 * rq + 16 * rt + col) * kQgRS + 8 * grp]);
+#pragma unroll
+    for (int vt = 0; vt < 4; ++vt) {
+      const int arow = (64 * vh + 16 * vt + col) * kQgRS + 8 * grp;
+      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&As[buf][0][arow]);
+      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&As[buf][1][arow]);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        acc[vt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bo[rt], acc[vt][rt], 0, 0, 0);
+        acc[vt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bo[rt], acc[vt][rt], 0, 0, 0);
+      }
+    }
+    if (ks + 1 < NK) { TQ_QG_STORE(buf ^ 1) }        // buf ^ 1 was last read before the
+    __syncthreads();                                   // previous barrier
+  }
+#undef TQ_QG_LOAD
+#undef TQ_QG_STORE
+  // acc[vt][rt][e] at lane l: P[vector 16 vt + 4 (l / 16) + e][row 16 rt + l % 16]
+#pragma unroll
+  for (int vt = 0; vt < 4; ++vt)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      uint64_t b0[4], b1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        b0[e] = __ballot(acc[vt][2 * h][e] >= 0.f);
+        b1[e] = __ballot(acc[vt][2 * h + 1][e] >= 0.f);
+      }
+      if (lane < 16) {
+        const int q = lane >> 2, e = lane & 3;
+        const uint64_t x0 = e == 0 ? b0[0] : e == 1 ? b0[1] : e == 2 ? b0[2] : b0[3];
+        const uint64_t x1 = e == 0 ? b1[0] : e == 1 ? b1[1] : e == 2 ? b1[2] : b1[3];
+        const uint32_t word = ((uint32_t)(x0 >> (16 * q)) & 0xFFFFu) |
+                              (((uint32_t)(x1 >> (16 * q)) & 0xFFFFu) << 16);
+        const int64_t v = v0 + 64 * vh + 16 * vt + lane;
+        const int g = (r0 + 64 * rq + 32 * h) / 32;
+        if (v < a.nv)
+          reinterpret_cast<uint32_t*>(a.codes + v * a.rec_bytes + a.rec_off)[g * (a.R + 1) + a.R] = word;
+      }
+    }
 }
 
 // ---------------------------------------------------------------------------- MFMA encode
@@ -1592,18 +1720,61 @@ __global__ void __launch_bounds__(kBlock) topk_kernel(const float* scores, int64
 
 static inline int hip_rc(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
 
-template <int D>
-static int launch_encode_d(const EncodeArgs& ea, hipStream_t st) {
+template <int D, bool SPLIT>
+static int launch_encode_kernel(const EncodeArgs& ea, hipStream_t st) {
   const int64_t tiles = (ea.n + EncCfg<D>::V - 1) / EncCfg<D>::V;
   const dim3 grid((unsigned)tiles), block(kBlock);
   switch (ea.s.R) {
-    case 1: hipLaunchKernelGGL((encode_kernel<D, 1>), grid, block, 0, st, ea); break;
-    case 2: hipLaunchKernelGGL((encode_kernel<D, 2>), grid, block, 0, st, ea); break;
-    case 3: hipLaunchKernelGGL((encode_kernel<D, 3>), grid, block, 0, st, ea); break;
-    case 4: hipLaunchKernelGGL((encode_kernel<D, 4>), grid, block, 0, st, ea); break;
+    case 1: hipLaunchKernelGGL((encode_kernel<D, 1, SPLIT>), grid, block, 0, st, ea); break;
+    case 2: hipLaunchKernelGGL((encode_kernel<D, 2, SPLIT>), grid, block, 0, st, ea); break;
+    case 3: hipLaunchKernelGGL((encode_kernel<D, 3, SPLIT>), grid, block, 0, st, ea); break;
+    case 4: hipLaunchKernelGGL((encode_kernel<D, 4, SPLIT>), grid, block, 0, st, ea); break;
     default: return (int)hipErrorInvalidValue;
   }
   return hip_rc(hipGetLastError());
+}
+
+// Long vectors: batches of kSplitBatch vectors, each encoded without its signs (residual
+// limbs to a stream-ordered temporary of 4 D bytes per vector) and then signed by the GEMM.
+constexpr int64_t kSplitBatch = 32768;
+
+template <int D>
+static int launch_encode_d(const EncodeArgs& ea, hipStream_t st) {
+  if constexpr (D >= 1024) {
+    const int64_t nb = ea.n < kSplitBatch ? ea.n : kSplitBatch;
+    void* ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, (size_t)nb * D * 4, st);
+    if (e != hipSuccess) return (int)e;
+    const int es = ea.is_bf16 ? 2 : 4;
+    int rc = 0;
+    for (int64_t b0 = 0; b0 < ea.n && !rc; b0 += kSplitBatch) {
+      EncodeArgs eb = ea;
+      eb.n = (ea.n - b0) < kSplitBatch ? (ea.n - b0) : kSplitBatch;
+      eb.x = static_cast<const uint8_t*>(ea.x) + b0 * ea.ldx * es;
+      eb.codes = ea.codes + b0 * ea.rec_bytes;
+      eb.rw_hi = static_cast<uint16_t*>(ws);
+      eb.rw_lo = eb.rw_hi + (size_t)eb.n * D;
+      rc = launch_encode_kernel<D, true>(eb, st);
+      if (rc) break;
+      QjlGemmArgs ga;
+      ga.rh = eb.rw_hi;
+      ga.rl = eb.rw_lo;
+      ga.S = ea.s.S;
+      ga.codes = eb.codes;
+      ga.nv = eb.n;
+      ga.rec_bytes = ea.rec_bytes;
+      ga.rec_off = ea.s.rec_off;
+      ga.R = ea.s.R;
+      const dim3 grid((unsigned)(D / kQgBM), (unsigned)((eb.n + kQgBN - 1) / kQgBN));
+      hipLaunchKernelGGL(qjl_gemm_kernel<D>, grid, dim3(512), 0, st, ga);
+      rc = hip_rc(hipGetLastError());
+    }
+    e = hipFreeAsync(ws, st);
+    if (!rc && e != hipSuccess) rc = (int)e;
+    return rc;
+  } else {
+    return launch_encode_kernel<D, false>(ea, st);
+  }
 }
 
 template <int D, int XL, bool VEC, bool F16>
@@ -1668,6 +1839,7 @@ int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, i
   ea.is_bf16 = dt == TQ_BF16;
   const int es = ea.is_bf16 ? 2 : 4;
   ea.vec_load = (ea.s.chan == nullptr) && ((uintptr_t)x % 16 == 0) && ((ldx * es) % 16 == 0);
+  ea.rw_hi = ea.rw_lo = nullptr;
   hipStream_t st = (hipStream_t)stream;
   if (ea.s.D <= 128 && ea.s.rotk) return launch_encode_mfma(ea, st);
   switch (ea.s.D) {
