@@ -1004,25 +1004,70 @@ __global__ void __launch_bounds__(kBlock) qprep_kernel(QPrepArgs a) {
     a.yrot[qi * D + i] = v;
     sy += v;
   }
-  __syncthreads();
-  // w_j = sum_i S[j][i] y'_i : one wave per row j, lanes across i
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float sw = 0.f;
-  for (int j = wave; j < s.k; j += kBlock / kWave) {
-    const uint16_t* Sj = s.S + (size_t)j * D;
-    float acc = 0.f;
-    for (int i = lane; i < D; i += kWave) acc = fmaf(bf16_bits_to_f32(Sj[i]), y[i], acc);
-    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
-    if (lane == 0) { a.w[qi * D + j] = acc; sw += acc; }
-  }
   for (int m = 32; m >= 1; m >>= 1) sy += __shfl_xor(sy, m);
-  if (lane == 0) { red[0][wave] = sy; red[1][wave] = sw; }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[0][wave] = sy;
   __syncthreads();
   if (threadIdx.x == 0) {
-    float t0 = 0.f, t1 = 0.f;
-    for (int i = 0; i < kBlock / kWave; ++i) { t0 += red[0][i]; t1 += red[1][i]; }
+    float t0 = 0.f;
+    for (int i = 0; i < kBlock / kWave; ++i) t0 += red[0][i];
     a.sums[qi * 2] = t0;
-    a.sums[qi * 2 + 1] = t1;
+  }
+}
+
+// w = S y' for kProjQB queries per workgroup: their y' sit in LDS, each thread owns rows
+// j = tid, tid + 256, ... and reads every row of S once for all kProjQB queries (16-byte
+// loads); also the sums of w.
+constexpr int kProjQB = 4;
+
+__global__ void __launch_bounds__(kBlock) qproj_kernel(QPrepArgs a, int64_t nq) {
+  const SubDev& s = a.s;
+  const int D = s.D;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t q0 = (int64_t)blockIdx.x * kProjQB;
+  const int nqb = (nq - q0) < kProjQB ? (int)(nq - q0) : kProjQB;
+  __shared__ __attribute__((aligned(16))) float ys[kProjQB][kMaxD];
+  __shared__ float red[kProjQB][kBlock / kWave];
+  for (int q = 0; q < kProjQB; ++q)
+    for (int i = tid; i < D; i += kBlock) ys[q][i] = q < nqb ? a.yrot[(q0 + q) * D + i] : 0.f;
+  __syncthreads();
+  float sw[kProjQB];
+#pragma unroll
+  for (int q = 0; q < kProjQB; ++q) sw[q] = 0.f;
+  for (int j = tid; j < s.k; j += kBlock) {
+    const uint4* Sj = reinterpret_cast<const uint4*>(s.S + (size_t)j * D);
+    float acc[kProjQB];
+#pragma unroll
+    for (int q = 0; q < kProjQB; ++q) acc[q] = 0.f;
+    for (int c = 0; c < D / 8; ++c) {
+      const uint4 u = Sj[c];
+      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float s0 = __uint_as_float(wv[h] << 16), s1 = __uint_as_float(wv[h] & 0xFFFF0000u);
+#pragma unroll
+        for (int q = 0; q < kProjQB; ++q) {
+          acc[q] = fmaf(s0, ys[q][8 * c + 2 * h], acc[q]);
+          acc[q] = fmaf(s1, ys[q][8 * c + 2 * h + 1], acc[q]);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kProjQB; ++q) {
+      if (q < nqb) a.w[(q0 + q) * D + j] = acc[q];
+      sw[q] += acc[q];
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < kProjQB; ++q) {
+    for (int m = 32; m >= 1; m >>= 1) sw[q] += __shfl_xor(sw[q], m);
+    if (lane == 0) red[q][wave] = sw[q];
+  }
+  __syncthreads();
+  if (tid < nqb) {
+    float t = 0.f;
+    for (int i = 0; i < kBlock / kWave; ++i) t += red[tid][i];
+    a.sums[(q0 + tid) * 2 + 1] = t;
   }
 }
 
@@ -1972,6 +2017,8 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
       sa.ec[sb] = fa.ec;
     } else {
       hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)nq), dim3(kBlock), 0, st, qa);
+      hipLaunchKernelGGL(qproj_kernel, dim3((unsigned)((nq + kProjQB - 1) / kProjQB)), dim3(kBlock),
+                         0, st, qa, nq);
       if (wide) {
         WideImgArgs wa;
         wa.s = p.sub[sb];
