@@ -1698,6 +1698,26 @@ __device__ __forceinline__ bool better(float v, int i, float w, int j) {
   return v > w || (v == w && i < j);
 }
 
+// Insert (cv, ci) into a thread's sorted list when it beats the current k-th entry.
+template <int KMAX>
+__device__ __forceinline__ void topk_consider(float (&lv)[KMAX], int (&li)[KMAX], float& thr,
+                                              int& thr_i, int k, float cv, int ci) {
+  if (!better(cv, ci, thr, thr_i)) return;
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s) {
+    const bool sw = better(cv, ci, lv[s], li[s]);
+    const float tv = lv[s];
+    const int ti = li[s];
+    lv[s] = sw ? cv : tv;
+    li[s] = sw ? ci : ti;
+    cv = sw ? tv : cv;
+    ci = sw ? ti : ci;
+  }
+#pragma unroll
+  for (int s = 0; s < KMAX; ++s)
+    if (s == k - 1) { thr = lv[s]; thr_i = li[s]; }
+}
+
 template <int KMAX>
 __global__ void __launch_bounds__(kBlock) topk_kernel(const float* scores, int64_t n, int k,
                                                       int64_t* ids, float* vals) {
@@ -1709,24 +1729,30 @@ __global__ void __launch_bounds__(kBlock) topk_kernel(const float* scores, int64
   for (int s = 0; s < KMAX; ++s) { lv[s] = -INFINITY; li[s] = 0x7FFFFFFF; }
   float thr = -INFINITY;
   int thr_i = 0x7FFFFFFF;
-  for (int64_t j = threadIdx.x; j < n; j += kBlock) {
-    float cv = x[j];
-    int ci = (int)j;
-    if (better(cv, ci, thr, thr_i)) {
+  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0 && (n & 3) == 0) {
+    // 16-byte loads, four per thread in flight; a candidate is inserted only when it beats
+    // the thread's current k-th value (the common case is one comparison)
+    const float4* x4 = reinterpret_cast<const float4*>(x);
+    const int64_t n4 = n >> 2;
+    for (int64_t j0 = threadIdx.x; j0 < n4; j0 += 4 * kBlock) {
+      float4 u[4];
 #pragma unroll
-      for (int s = 0; s < KMAX; ++s) {
-        const bool sw = better(cv, ci, lv[s], li[s]);
-        const float tv = lv[s];
-        const int ti = li[s];
-        lv[s] = sw ? cv : tv;
-        li[s] = sw ? ci : ti;
-        cv = sw ? tv : cv;
-        ci = sw ? ti : ci;
+      for (int b = 0; b < 4; ++b) {
+        const int64_t j = j0 + b * kBlock;
+        u[b] = j < n4 ? x4[j] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
       }
 #pragma unroll
-      for (int s = 0; s < KMAX; ++s)
-        if (s == k - 1) { thr = lv[s]; thr_i = li[s]; }
+      for (int b = 0; b < 4; ++b) {
+        const int ci = (int)(4 * (j0 + b * kBlock));
+        topk_consider<KMAX>(lv, li, thr, thr_i, k, u[b].x, ci);
+        topk_consider<KMAX>(lv, li, thr, thr_i, k, u[b].y, ci + 1);
+        topk_consider<KMAX>(lv, li, thr, thr_i, k, u[b].z, ci + 2);
+        topk_consider<KMAX>(lv, li, thr, thr_i, k, u[b].w, ci + 3);
+      }
     }
+  } else {
+    for (int64_t j = threadIdx.x; j < n; j += kBlock)
+      topk_consider<KMAX>(lv, li, thr, thr_i, k, x[j], (int)j);
   }
   __shared__ float wv[kBlock / kWave];
   __shared__ int wi[kBlock / kWave];
