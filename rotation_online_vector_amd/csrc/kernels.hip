@@ -343,6 +343,8 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
 // coordinates through double-buffered LDS; 8 waves, each 64 vectors x 64 rows (4 x 4 MFMA
 // tiles, both limbs into one accumulator).  The signs go straight into the records.
 constexpr int kQgBN = 128, kQgBM = 256, kQgKS = 32, kQgRS = kQgKS + 8;   // LDS row: 80 B
+constexpr int kQgNQ = kQgKS / 8;          // 16-byte pieces per row and k step
+constexpr int kQgNI = kQgBM * kQgNQ / 512; // pieces per thread, A and B alike
 
 struct QjlGemmArgs {
   const uint16_t* rh;    // [nv][D]
@@ -355,7 +357,8 @@ struct QjlGemmArgs {
 
 template <int D>
 __global__ void __launch_bounds__(512) qjl_gemm_kernel(QjlGemmArgs a) {
-  static_assert(D % kQgBM == 0, "rows of S in whole blocks");
+  static_assert(D % kQgBM == 0 && D % kQgKS == 0, "whole blocks and k steps");
+  static_assert(2 * kQgBN == kQgBM, "A (two limbs) and B have the same piece count");
   __shared__ __attribute__((aligned(16))) uint16_t As[2][2][kQgBN * kQgRS];   // [buf][limb]
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kQgBM * kQgRS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -363,33 +366,33 @@ __global__ void __launch_bounds__(512) qjl_gemm_kernel(QjlGemmArgs a) {
   const int vh = wave & 1, rq = wave >> 1;
   const int64_t v0 = (int64_t)blockIdx.y * kQgBN;
   const int r0 = blockIdx.x * kQgBM;
-  // global -> LDS items: A (limb, vector, 16-byte quarter) and B (row, quarter), 2 each
-  const uint16_t* asrc[2];
-  const uint16_t* bsrc[2];
-  int adst[2], bdst[2];
+  // global -> LDS pieces: A (limb, vector, 16-byte piece) and B (row, piece)
+  const uint16_t* asrc[kQgNI];
+  const uint16_t* bsrc[kQgNI];
+  int adst[kQgNI], bdst[kQgNI];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < kQgNI; ++i) {
     const int it = tid + 512 * i;
-    const int limb = it >> 9, vv = (it >> 2) & (kQgBN - 1), q = it & 3;
+    const int limb = it / (kQgBN * kQgNQ), vv = (it / kQgNQ) % kQgBN, q = it % kQgNQ;
     int64_t v = v0 + vv;
     v = v < a.nv ? v : a.nv - 1;            // past the batch: a real row, never stored
     asrc[i] = (limb ? a.rl : a.rh) + v * D + 8 * q;
     adst[i] = limb * kQgBN * kQgRS + vv * kQgRS + 8 * q;
-    const int rr = it >> 2;
+    const int rr = it / kQgNQ;
     bsrc[i] = a.S + (size_t)(r0 + rr) * D + 8 * q;
     bdst[i] = rr * kQgRS + 8 * q;
   }
-  uint4 ra0, ra1, rb0, rb1;
+  uint4 ra[kQgNI], rb[kQgNI];
 #define TQ_QG_LOAD(k0)                                                     \
-  ra0 = *reinterpret_cast<const uint4*>(asrc[0] + (k0));                   \
-  ra1 = *reinterpret_cast<const uint4*>(asrc[1] + (k0));                   \
-  rb0 = *reinterpret_cast<const uint4*>(bsrc[0] + (k0));                   \
-  rb1 = *reinterpret_cast<const uint4*>(bsrc[1] + (k0));
+  _Pragma("unroll") for (int i = 0; i < kQgNI; ++i) {                      \
+    ra[i] = *reinterpret_cast<const uint4*>(asrc[i] + (k0));               \
+    rb[i] = *reinterpret_cast<const uint4*>(bsrc[i] + (k0));               \
+  }
 #define TQ_QG_STORE(buf)                                                   \
-  *reinterpret_cast<uint4*>(&As[buf][0][0] + adst[0]) = ra0;               \
-  *reinterpret_cast<uint4*>(&As[buf][0][0] + adst[1]) = ra1;               \
-  *reinterpret_cast<uint4*>(&Bs[buf][0] + bdst[0]) = rb0;                  \
-  *reinterpret_cast<uint4*>(&Bs[buf][0] + bdst[1]) = rb1;
+  _Pragma("unroll") for (int i = 0; i < kQgNI; ++i) {                      \
+    *reinterpret_cast<uint4*>(&As[buf][0][0] + adst[i]) = ra[i];           \
+    *reinterpret_cast<uint4*>(&Bs[buf][0] + bdst[i]) = rb[i];              \
+  }
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -402,19 +405,23 @@ __global__ void __launch_bounds__(512) qjl_gemm_kernel(QjlGemmArgs a) {
   for (int ks = 0; ks < NK; ++ks) {
     const int buf = ks & 1;
     if (ks + 1 < NK) { TQ_QG_LOAD(kQgKS * (ks + 1)) }   // next step's tiles, in flight
-    bf16x8 bo[4];
 #pragma unroll
-    for (int rt = 0; rt < 4; ++rt)
-      bo[rt] = *reinterpret_cast<const bf16x8*>(&Bs[buf][(64 * rq + 16 * rt + col) * kQgRS + 8 * grp]);
+    for (int sub = 0; sub < kQgKS / 32; ++sub) {
+      bf16x8 bo[4];
 #pragma unroll
-    for (int vt = 0; vt < 4; ++vt) {
-      const int arow = (64 * vh + 16 * vt + col) * kQgRS + 8 * grp;
-      const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&As[buf][0][arow]);
-      const bf16x8 al = *reinterpret_cast<const bf16x8*>(&As[buf][1][arow]);
+      for (int rt = 0; rt < 4; ++rt)
+        bo[rt] = *reinterpret_cast<const bf16x8*>(
+            &Bs[buf][(64 * rq + 16 * rt + col) * kQgRS + 32 * sub + 8 * grp]);
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        acc[vt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bo[rt], acc[vt][rt], 0, 0, 0);
-        acc[vt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bo[rt], acc[vt][rt], 0, 0, 0);
+      for (int vt = 0; vt < 4; ++vt) {
+        const int arow = (64 * vh + 16 * vt + col) * kQgRS + 32 * sub + 8 * grp;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&As[buf][0][arow]);
+        const bf16x8 al = *reinterpret_cast<const bf16x8*>(&As[buf][1][arow]);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          acc[vt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bo[rt], acc[vt][rt], 0, 0, 0);
+          acc[vt][rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bo[rt], acc[vt][rt], 0, 0, 0);
+        }
       }
     }
     if (ks + 1 < NK) { TQ_QG_STORE(buf ^ 1) }        // buf ^ 1 was last read before the
