@@ -546,9 +546,10 @@ __device__ __forceinline__ uint32_t neg_one_low_half() {
 // VEC: rows are 16-byte aligned, d = D and no channel gather, so every lane's 8 elements
 // are one vector load; otherwise element-wise.
 // For XL > 1 (fp32 input) the squares of the 8 values are added to ss.
+// Not VEC: chl (LDS) holds the input channel of each coordinate, -1 past d.
 template <int XL, bool VEC>
 __device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0,
-                                        uint32_t (&limbs)[XL][4], float& ss) {
+                                        uint32_t (&limbs)[XL][4], float& ss, const int* chl) {
   const SubDev& s = a.s;
   float v[8];
   if (VEC) {
@@ -565,14 +566,17 @@ __device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0
       v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
     }
   } else {
+    const int4 c4a = reinterpret_cast<const int4*>(chl + c0)[0];
+    const int4 c4b = reinterpret_cast<const int4*>(chl + c0)[1];
+    const int chs[8] = {c4a.x, c4a.y, c4a.z, c4a.w, c4b.x, c4b.y, c4b.z, c4b.w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const int i = c0 + e;
       float val = 0.f;
-      if (i < s.d) {
-        const int64_t ch = s.chan ? s.chan[i] : i;
-        val = a.is_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.x)[row * a.ldx + ch])
-                        : reinterpret_cast<const float*>(a.x)[row * a.ldx + ch];
+      if (chs[e] >= 0) {
+        if constexpr (XL == 1)
+          val = bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.x)[row * a.ldx + chs[e]]);
+        else
+          val = reinterpret_cast<const float*>(a.x)[row * a.ldx + chs[e]];
       }
       v[e] = val;
     }
@@ -695,6 +699,11 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
     kop[i] = reinterpret_cast<const uint4*>(F16 ? s.rotk16 : s.rotk)[i];
   for (int i = threadIdx.x; i < NJT * NKS * 64; i += kEncWaves * kWave)
     sop[i] = reinterpret_cast<const uint4*>(s.sperm)[i];
+  __shared__ __attribute__((aligned(16))) int chl[VEC ? 8 : D];   // input channel per coordinate
+  if constexpr (!VEC) {
+    for (int i = threadIdx.x; i < D; i += kEncWaves * kWave)
+      chl[i] = i < s.d ? (s.chan ? s.chan[i] : i) : -1;
+  }
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -720,7 +729,7 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
       for (int ks = 0; ks < NKS; ++ks) {
         uint32_t lb[XL][4];
         const int64_t row = v0 + 16 * t + col;
-        load_x8<XL, VEC>(a, row < a.n ? row : a.n - 1, 32 * ks + 8 * G, lb, ss[t]);
+        load_x8<XL, VEC>(a, row < a.n ? row : a.n - 1, 32 * ks + 8 * G, lb, ss[t], chl);
 #pragma unroll
         for (int l = 0; l < XL; ++l)
 #pragma unroll
