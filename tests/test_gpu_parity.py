@@ -197,6 +197,26 @@ def test_score_many_queries_long_vectors(d, bits, n, nqg, groups):
                             np.linalg.norm(xs[g * n:(g + 1) * n], axis=1), "d=%d group %d" % (d, g))
 
 
+@pytest.mark.parametrize("d,bits,dtype", [(1024, 3, "float32"), (2048, 4, "bfloat16")])
+def test_long_vector_encode_across_batches(d, bits, dtype):
+    """D >= 1024 encodes in batches of 32768 vectors (signs from a second launch): rows on
+    both sides of the batch boundary and in the ragged last batch match the oracle."""
+    n = 32768 + 77
+    g = torch.Generator(device=DEV)
+    g.manual_seed(d)
+    x = torch.randn((n, d), generator=g, device=DEV, dtype=torch.float32).to(getattr(torch, dtype))
+    sp = otq.make_split_plan(d, bits, 7)
+    plan = tq.tq_plan_create(d, bits, 7)
+    codes = tq.tq_encode(plan, x)
+    torch.cuda.synchronize()
+    rows = np.concatenate([np.arange(0, 40), np.arange(32768 - 40, 32768 + 40), np.arange(n - 37, n)])
+    ri = torch.as_tensor(rows, device=DEV)
+    got = parity.unpack_gpu(sp, codes[ri].cpu().numpy())
+    ref = otq.encode_split(sp, _np(x[ri]))
+    for i, (p, r, gg) in enumerate(zip(sp.plans, ref, got)):
+        parity.compare_codes(p, r, gg, "d=%d batches/sub%d" % (d, i))
+
+
 def test_strided_rows_and_query_groups():
     d, n = 128, 300
     rng = np.random.default_rng(5)
