@@ -116,3 +116,22 @@ def test_plan_create_without_device_reports_device_error():
         pytest.skip("a GPU is present")
     st, h = _create(128, 3)
     assert st == tq.TQ_EDEVICE and h.value is None
+
+
+def test_c_abi_from_plain_c(tmp_path):
+    """The header compiles as C and the library links and answers from a plain C program
+    (gcc, no HIP headers): host building blocks, status strings, argument validation."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    lib_dir = os.path.dirname(tq.LIB_PATH)
+    exe = str(tmp_path / "c_abi_host")
+    src = os.path.join(ROOT, "tests", "c", "c_abi_host.c")
+    subprocess.run([gcc, "-std=c99", "-O1", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    src, "-o", exe, "-L", lib_dir, "-ltq", "-lm", "-Wl,-rpath," + lib_dir],
+                   check=True, capture_output=True, text=True)
+    out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert out.stdout.strip().endswith("all passed")
