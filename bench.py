@@ -9,8 +9,9 @@ the streaming estimator).  Inputs are resident in HBM before timing starts.
                     [--copy-calibration MIB] [--workload NAME]
 
 `--workload` selects one of the other synthetic shapes (kv, split35, split25,
-retrieval, small); their step is encode + score (+ top-k for the two retrieval
-shapes) and the line carries the same fields, without the CPU leg.
+retrieval, small); their step is encode + score (+ top-k for `small`; one fused
+score + top-k call for `retrieval`, whose roofline is the MFMA one) and the line
+carries the same fields, without the CPU leg.
 
 Prints one JSON line.  `value` is scores per second over whole steps; the
 per-kernel rates, the roofline of the dominant kernel (algorithmic bytes per
@@ -27,6 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix peak of the MI355X
 
 
 def parse():
@@ -194,18 +196,32 @@ def build_workload(name, dev, W_all):
         n, nq, d, k = W["n_keys"], W["n_queries"], W["d"], W.get("topk", 10)
         plan = tq.tq_plan_create(d, W["bits"], W["seed"])
         rb = plan.record_bytes
+        D = plan.desc["sub"][0]["D"]
         codes = torch.empty((n, rb), dtype=torch.uint8, device=dev)
-        scores = torch.empty((nq, n), dtype=torch.float32, device=dev)
         ids = torch.empty((nq, k), dtype=torch.int64, device=dev)
         vals = torch.empty((nq, k), dtype=torch.float32, device=dev)
+        config = {"workload": W["name"], "keys": n, "queries": nq, "d": d, "D": D,
+                  "bits": W["bits"], "topk": k, "keys_per_step": n, "scores_per_step": n * nq,
+                  "record_bytes": rb}
+        enc = ("tq_encode", lambda: tq.tq_encode(plan, keys, codes))
+        enc_bytes = n * d * 4 + n * rb
+        if name == "retrieval":
+            # score and select in one call: the score matrix is never stored
+            return dict(
+                config=config,
+                phases=[enc, ("tq_score_topk",
+                              lambda: tq.tq_score_topk(plan, queries, codes, n, k, ids=ids, vals=vals))],
+                bytes={"tq_encode": enc_bytes, "tq_score_topk": n * rb + nq * d * 4 + nq * k * 12},
+                # MFMA work: the sign projection (2 k D per key, k = D) and the bit-sliced
+                # scorer's contraction of every key with every query (2 (D + k) per score)
+                flops={"tq_encode": 2.0 * D * D * n, "tq_score_topk": 2.0 * (2 * D) * n * nq},
+                n_keys=n, n_scores=n * nq, keep=(plan, keys, queries, codes, ids, vals))
+        scores = torch.empty((nq, n), dtype=torch.float32, device=dev)
         return dict(
-            config={"workload": W["name"], "keys": n, "queries": nq, "d": d,
-                    "D": plan.desc["sub"][0]["D"], "bits": W["bits"], "topk": k,
-                    "keys_per_step": n, "scores_per_step": n * nq, "record_bytes": rb},
-            phases=[("tq_encode", lambda: tq.tq_encode(plan, keys, codes)),
-                    ("tq_score", lambda: tq.tq_score(plan, queries, codes, n=n, scores=scores)),
+            config=config,
+            phases=[enc, ("tq_score", lambda: tq.tq_score(plan, queries, codes, n=n, scores=scores)),
                     ("tq_topk", lambda: tq.tq_topk(scores, k, ids, vals))],
-            bytes={"tq_encode": n * d * 4 + n * rb, "tq_score": n * rb + n * nq * 4 + nq * d * 4,
+            bytes={"tq_encode": enc_bytes, "tq_score": n * rb + n * nq * 4 + nq * d * 4,
                    "tq_topk": n * nq * 4 + nq * k * 12},
             n_keys=n, n_scores=n * nq, keep=(plan, keys, queries, codes, scores, ids, vals))
     raise ValueError(name)
@@ -264,10 +280,24 @@ def main():
         b = wl["bytes"][nm]
         kern[nm] = {"ms": ms, "bytes": b, "gbs": b / ms / 1e6}
     dom = max(kern, key=lambda k: kern[k]["ms"])
-    traffic = measured_traffic(dom) if args.workload == "longctx" else None
-    roof = {"kernel": dom, "bound": "hbm", "achieved": round(kern[dom]["gbs"], 1),
-            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
-            "traffic": traffic, "bytes_per_launch": kern[dom]["bytes"]}
+    flops = wl.get("flops")
+    if flops:
+        # a contraction-bound workload: algorithmic MFMA flops per launch against the dense
+        # bf16 peak (the sign projection runs on bf16 MFMA, the scorer on fp8 x fp4, whose
+        # own peak is twice that)
+        tf = flops[dom] / (kern[dom]["ms"] * 1e-3) / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_TFLOPS, 4), "traffic": None,
+                "flops_per_launch": flops[dom]}
+        for k, v in kern.items():
+            v["tflops"] = flops[k] / (v["ms"] * 1e-3) / 1e12
+    else:
+        traffic = measured_traffic(dom) if args.workload == "longctx" else None
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(kern[dom]["gbs"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "bytes_per_launch": kern[dom]["bytes"]}
+    score_key = "tq_score" if "tq_score" in kern else "tq_score_topk"
     out = {
         "metric": "quantized-key scores/sec + HBM GB/s (d=128, 3-bit); encode vectors/sec",
         "value": wl["n_scores"] / (ms_step / 1e3),
@@ -278,9 +308,14 @@ def main():
         "dtype": "f32", "data": "synthetic",
         "config": wl["config"],
         "encode_vectors_per_s": _rate(wl["n_keys"], kern["tq_encode"]["ms"]),
-        "score_scores_per_s": _rate(wl["n_scores"], kern["tq_score"]["ms"]),
-        "kernels": {k: {"ms": round(v["ms"], 4), "alg_bytes": v["bytes"], "alg_gbs": round(v["gbs"], 1),
-                        "hbm_frac": round(v["gbs"] / HBM_PEAK_GBS, 4)} for k, v in kern.items()},
+        "score_scores_per_s": _rate(wl["n_scores"], kern[score_key]["ms"]),
+        "kernels": {k: dict({"ms": round(v["ms"], 4), "alg_bytes": v["bytes"],
+                             "alg_gbs": round(v["gbs"], 1),
+                             "hbm_frac": round(v["gbs"] / HBM_PEAK_GBS, 4)},
+                            **({"mfma_tflops": round(v["tflops"], 1),
+                                "mfma_bf16_frac": round(v["tflops"] / MFMA_BF16_TFLOPS, 4)}
+                               if "tflops" in v else {}))
+                    for k, v in kern.items()},
         "roofline": roof,
     }
     if args.workload == "longctx" and not args.no_cpu_baseline:

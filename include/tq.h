@@ -151,6 +151,26 @@ tq_status tq_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* id
                   void* stream);
 
 /*
+ * Score and select in one call (overview §4.2.2: the quantized first stage of
+ * two-stage retrieval): for each query row, the k largest estimates of
+ * tq_score against its group's n records, ordered by (-value, index), with
+ * the same values tq_score would write.  Arguments as in tq_score, plus
+ *   ids   device int64 [n_groups*nq_per_group][k]: record index within the group
+ *   vals  device float32 [n_groups*nq_per_group][k]
+ * For a single sub-plan with D > 128, D a multiple of 128 and at least 8
+ * queries per group, the score matrix is never stored: the scorer keeps each
+ * query's running best k in on-chip memory and a second launch merges the
+ * per-workgroup lists (a stream-ordered temporary of 8*k bytes per query and
+ * workgroup slice, about 16384 workgroups).  Other shapes score into a
+ * stream-ordered temporary of 4*n bytes per query row and select from it.
+ * Errors: TQ_EINVAL (as tq_score; k < 1, k > 64, k > n, n >= 2^31),
+ * TQ_ENOMEM, TQ_EDEVICE.  NaN estimates are not supported.
+ */
+tq_status tq_score_topk(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_per_group,
+                        int64_t n_groups, int64_t ldq, const void* codes, int64_t n, int k,
+                        int64_t* ids, float* vals, void* stream);
+
+/*
  * The QJL stage alone (overview §2.3.2): beta_j = [ (S r)_j >= 0 ] for n
  * residual vectors r already in the rotated domain of sub-plan `subplan`.
  *   r     device float32 [n][D]

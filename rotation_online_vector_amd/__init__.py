@@ -37,7 +37,7 @@ class tq_plan_desc(ctypes.Structure):
 
 
 EXPORTED = ["tq_status_string", "tq_plan_create", "tq_plan_destroy", "tq_plan_info",
-            "tq_encode", "tq_score", "tq_topk", "tq_qjl", "tq_codebook",
+            "tq_encode", "tq_score", "tq_score_topk", "tq_topk", "tq_qjl", "tq_codebook",
             "tq_rotation_signs", "tq_qjl_matrix"]
 
 _lib = None
@@ -71,6 +71,8 @@ def load_library(path=LIB_PATH):
     lib.tq_score.restype = i32
     lib.tq_topk.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.tq_topk.restype = i32
+    lib.tq_score_topk.argtypes = [vp, vp, i32, i64, i64, i64, vp, i64, i32, vp, vp, vp]
+    lib.tq_score_topk.restype = i32
     lib.tq_qjl.argtypes = [vp, i32, vp, i64, vp, vp]
     lib.tq_qjl.restype = i32
     lib.tq_codebook.argtypes = [i32, i32, vp, vp]
@@ -218,6 +220,28 @@ def tq_topk(scores, k, ids=None, vals=None, stream=None):
         vals = torch.empty((nq, k), dtype=torch.float32, device=scores.device)
     _check("tq_topk", load_library().tq_topk(
         ctypes.c_void_p(scores.data_ptr()), nq, n, int(k), ctypes.c_void_p(ids.data_ptr()),
+        ctypes.c_void_p(vals.data_ptr()), _stream(stream)))
+    return ids, vals
+
+
+def tq_score_topk(plan, q, codes, n, k, nq_per_group=None, n_groups=1, ids=None, vals=None,
+                  stream=None):
+    """Top-k (ids [rows, k] int64, vals [rows, k] float32) of the scores tq_score would give."""
+    import torch
+    nq, ld = _rows(q, plan.d)
+    if nq_per_group is None:
+        nq_per_group = nq // n_groups
+    if nq_per_group * n_groups != nq:
+        raise ValueError("query rows != nq_per_group * n_groups")
+    if codes.numel() < n_groups * n * plan.record_bytes:
+        raise ValueError("codes buffer too small")
+    if ids is None:
+        ids = torch.empty((nq, k), dtype=torch.int64, device=q.device)
+    if vals is None:
+        vals = torch.empty((nq, k), dtype=torch.float32, device=q.device)
+    _check("tq_score_topk", load_library().tq_score_topk(
+        plan.handle, ctypes.c_void_p(q.data_ptr()), _dtype_code(q), nq_per_group, n_groups, ld,
+        ctypes.c_void_p(codes.data_ptr()), n, int(k), ctypes.c_void_p(ids.data_ptr()),
         ctypes.c_void_p(vals.data_ptr()), _stream(stream)))
     return ids, vals
 

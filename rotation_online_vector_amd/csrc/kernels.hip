@@ -1553,12 +1553,122 @@ __global__ void __launch_bounds__(kBlock) qimage_wide_kernel(WideImgArgs a) {
   }
 }
 
+// One estimate from the MFMA sums of one (query, key) pair and the query's epilogue constants
+// e = (-c_sum * sum y', 4 / image scale, -K * sum w, 4 K / image scale): the same expression
+// for the score matrix and for the fused top-k, so both see identical values.
+__device__ __forceinline__ float wide_estimate(const float (&e)[4], float sm, float sq, float nrm,
+                                               float gam) {
+  return nrm * fmaf(gam, fmaf(e[3], sq, e[2]), fmaf(e[1], sm, e[0]));
+}
+
+// Fused top-k on the wide scorer (the quantized first stage of two-stage retrieval, technical
+// overview §4.2.2, without materializing the score matrix).  Each wave keeps, per query of
+// its image tile, a list in LDS of the scores that beat the query's running k-th best; a key
+// block appends at most 128 entries per query, and a list that could overflow is cut back to
+// its best k (order (-value, index)), which also raises the query's threshold.  The keys a
+// wave visits arrive in increasing index order, so a later score equal to the threshold
+// loses to every kept entry and a strict comparison drops nothing that could be selected.
+struct WideTopk {
+  int k;
+  int64_t n_slices;      // = gridDim.y: per query, n_slices lists of k candidates
+  float* cv;             // [rows][n_slices][k]
+  int* ci;               // [rows][n_slices][k]
+};
+
+constexpr int kListCap = 2 * kWideKT * 16;            // k kept (k <= 128) + one key block
+constexpr int kListPer = kListCap / kWave;            // entries per lane while cutting
+static_assert(kListCap - kWideKT * 16 >= 64, "a cut list plus one key block must fit");
+
+__device__ __forceinline__ bool better(float v, int i, float w, int j) {
+  return v > w || (v == w && i < j);
+}
+
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                         __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Unsigned key with the order of the float values (both zeros map to the key of +0, since
+// they compare equal); no NaN.
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t b = v == 0.f ? 0u : __float_as_uint(v);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_value(uint32_t t) {
+  return __uint_as_float((t & 0x80000000u) ? (t & 0x7FFFFFFFu) : ~t);
+}
+
+// Cut one query's list of cnt > k entries down to its best k (unordered, at the front of the
+// list).  Called by a whole wave.  The k-th best value T is found bit by bit on the order
+// keys, counting entries with ballots; entries above T stay, and of those equal to T the
+// ones with the smallest indices (a second bit-by-bit search when there are more than
+// needed).  Returns T, the query's new threshold.
+__device__ float wide_list_cut(float* lv, int* li, int cnt, int k, int lane) {
+  // entries written by other lanes of this wave must be visible to this lane's loads
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  float v[kListPer];
+  int id[kListPer];
+  uint32_t key[kListPer];
+#pragma unroll
+  for (int s = 0; s < kListPer; ++s) {
+    const int j = lane + kWave * s;
+    const bool ok = j < cnt;
+    v[s] = ok ? lv[j] : 0.f;
+    id[s] = ok ? li[j] : 0x7FFFFFFF;
+    key[s] = ok ? order_key(v[s]) : 0u;        // below every real key
+  }
+  uint32_t T = 0;                              // largest key with >= k entries at or above it
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = T | (1u << b);
+    int n = 0;
+#pragma unroll
+    for (int s = 0; s < kListPer; ++s) n += __popcll(__ballot(key[s] >= c));
+    if (n >= k) T = c;
+  }
+  int above = 0, equal = 0;
+#pragma unroll
+  for (int s = 0; s < kListPer; ++s) {
+    above += __popcll(__ballot(key[s] > T));
+    equal += __popcll(__ballot(key[s] == T));
+  }
+  const int need = k - above;                  // 1 <= need <= equal
+  uint32_t X = 0x7FFFFFFFu;                    // equal entries with index <= X stay
+  if (equal > need) {
+    X = 0;                                     // largest X with fewer than `need` below it
+    for (int b = 30; b >= 0; --b) {
+      const uint32_t c = X | (1u << b);
+      int n = 0;
+#pragma unroll
+      for (int s = 0; s < kListPer; ++s) n += __popcll(__ballot(key[s] == T && (uint32_t)id[s] < c));
+      if (n < need) X = c;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  int base = 0;
+#pragma unroll
+  for (int s = 0; s < kListPer; ++s) {
+    const bool keep = key[s] > T || (key[s] == T && (uint32_t)id[s] <= X);
+    const uint64_t m = __ballot(keep);
+    if (keep) {
+      const int pos = base + lanes_below(m);
+      lv[pos] = v[s];
+      li[pos] = id[s];
+    }
+    base += __popcll(m);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  return key_value(T);
+}
+
 // grid.x = (group, block of 4 image tiles), fastest, so that the blocks reading the same keys
 // run together and share them through the caches; grid.y strides over 128-key blocks.  Each
 // wave owns one image tile (8 queries) and 8 key tiles, whose accumulators stay in registers
 // across the chunks; per chunk it loads the plane images once for its 8 key tiles.
-template <int R>
-__global__ void __launch_bounds__(kBlock) score_wide_kernel(ScoreArgs a, int64_t n_qblocks) {
+// TOPK = false writes the score matrix; TOPK = true keeps the best k per query instead.
+template <int R, bool TOPK>
+__global__ void __launch_bounds__(kBlock) score_wide_kernel(ScoreArgs a, int64_t n_qblocks,
+                                                            WideTopk tk) {
   constexpr int NP = 1 << (R - 1);
   const SubDev& s = a.p.sub[0];
   const int nch = s.D / 128;
@@ -1582,6 +1692,16 @@ __global__ void __launch_bounds__(kBlock) score_wide_kernel(ScoreArgs a, int64_t
   float* out_a = a.scores + (grp * a.nq_per_group + qa) * a.n;
   float* out_b = out_a + a.n;
   const uint32_t* img = a.img[0] + (size_t)gt * nch * (NP + 1) * 64 * 8 + lane * 8;
+  // top-k state: this wave's lists (query q at q * kCap) and, per lane, the count and the
+  // threshold of its two queries (equal across the 16 lanes of a lane group)
+  constexpr int kCap = kListCap;
+  __shared__ float list_v[TOPK ? (kBlock / kWave) * kWideQT * kCap : 1];
+  __shared__ int list_i[TOPK ? (kBlock / kWave) * kWideQT * kCap : 1];
+  float* lv = list_v + (TOPK ? wave * kWideQT * kCap : 0);
+  int* li = list_i + (TOPK ? wave * kWideQT * kCap : 0);
+  int cnt_a = 0, cnt_b = 0;
+  float thr_a = -INFINITY, thr_b = -INFINITY;
+  const uint64_t gmask = 0xFFFFull << (16 * G);
   for (int64_t kb = blockIdx.y; kb < nkb; kb += gridDim.y) {
     const int64_t k0 = kb * kWideKT * 16;
     f32x4 am[kWideKT], aq[kWideKT];
@@ -1630,14 +1750,68 @@ __global__ void __launch_bounds__(kBlock) score_wide_kernel(ScoreArgs a, int64_t
       const uint32_t* tail = reinterpret_cast<const uint32_t*>(codes + ks * a.p.rec_bytes +
                                                                (s.D / 32) * (R + 1) * 4);
       const float nrm = __uint_as_float(tail[0]), gam = __uint_as_float(tail[1]);
-      float est_a = nrm * (fmaf(ea[1], am[t][0] + am[t][1], ea[0]) +
-                           gam * fmaf(ea[3], aq[t][0] + aq[t][1], ea[2]));
-      float est_b = nrm * (fmaf(eb[1], am[t][2] + am[t][3], eb[0]) +
-                           gam * fmaf(eb[3], aq[t][2] + aq[t][3], eb[2]));
+      float est_a = wide_estimate(ea, am[t][0] + am[t][1], aq[t][0] + aq[t][1], nrm, gam);
+      float est_b = wide_estimate(eb, am[t][2] + am[t][3], aq[t][2] + aq[t][3], nrm, gam);
       // full-wave region: keep the MFMA results from being sunk into the masked stores
       asm volatile("" : "+v"(est_a), "+v"(est_b));
-      if (key_ok && qa_ok) out_a[key] = est_a;
-      if (key_ok && qb_ok) out_b[key] = est_b;
+      if constexpr (!TOPK) {
+        if (key_ok && qa_ok) out_a[key] = est_a;
+        if (key_ok && qb_ok) out_b[key] = est_b;
+      } else {
+        const bool pa = key_ok && qa_ok && est_a > thr_a;
+        const bool pb = key_ok && qb_ok && est_b > thr_b;
+        const uint64_t ma = __ballot(pa), mb = __ballot(pb);
+        if ((ma | mb) != 0) {
+          if (pa) {
+            const int pos = cnt_a + lanes_below(ma & gmask);
+            lv[(2 * G) * kCap + pos] = est_a;
+            li[(2 * G) * kCap + pos] = (int)key;
+          }
+          if (pb) {
+            const int pos = cnt_b + lanes_below(mb & gmask);
+            lv[(2 * G + 1) * kCap + pos] = est_b;
+            li[(2 * G + 1) * kCap + pos] = (int)key;
+          }
+          cnt_a += __popcll(ma & gmask);
+          cnt_b += __popcll(mb & gmask);
+        }
+      }
+    }
+    if constexpr (TOPK) {
+      // cut every list that the next key block could overflow
+      const int lim = kCap - kWideKT * 16;
+      if (__ballot(cnt_a > lim || cnt_b > lim) != 0) {
+#pragma unroll
+        for (int q = 0; q < kWideQT; ++q) {
+          const int c = __builtin_amdgcn_readlane((q & 1) ? cnt_b : cnt_a, 16 * (q >> 1));
+          if (c > lim) {
+            const float th = wide_list_cut(lv + q * kCap, li + q * kCap, c, tk.k, lane);
+            if ((q >> 1) == G) {
+              if (q & 1) { cnt_b = tk.k; thr_b = th; } else { cnt_a = tk.k; thr_a = th; }
+            }
+          }
+        }
+      }
+    }
+  }
+  if constexpr (TOPK) {
+    // final cut, then this wave's k candidates per query (padding: -inf, index 2^31 - 1)
+#pragma unroll
+    for (int q = 0; q < kWideQT; ++q) {
+      int c = __builtin_amdgcn_readlane((q & 1) ? cnt_b : cnt_a, 16 * (q >> 1));
+      if (c > tk.k) {
+        wide_list_cut(lv + q * kCap, li + q * kCap, c, tk.k, lane);
+        c = tk.k;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+      const int64_t qi = qt * kWideQT + q;
+      if (qi < a.nq_per_group) {
+        const size_t o = (((size_t)(grp * a.nq_per_group + qi)) * tk.n_slices + blockIdx.y) * tk.k;
+        for (int r = lane; r < tk.k; r += kWave) {
+          tk.cv[o + r] = r < c ? lv[q * kCap + r] : -INFINITY;
+          tk.ci[o + r] = r < c ? li[q * kCap + r] : 0x7FFFFFFF;
+        }
+      }
     }
   }
 }
@@ -1710,10 +1884,6 @@ __global__ void __launch_bounds__(kBlock) score_generic_kernel(ScoreArgs a) {
 // two-stage retrieval (technical overview §4.2.2).  Each lane keeps a sorted list of its
 // KMAX best; lists are merged by k rounds of wave- and block-wide arg-max.
 
-__device__ __forceinline__ bool better(float v, int i, float w, int j) {
-  return v > w || (v == w && i < j);
-}
-
 // Insert (cv, ci) into a thread's sorted list when it beats the current k-th entry.
 template <int KMAX>
 __device__ __forceinline__ void topk_consider(float (&lv)[KMAX], int (&li)[KMAX], float& thr,
@@ -1732,6 +1902,43 @@ __device__ __forceinline__ void topk_consider(float (&lv)[KMAX], int (&li)[KMAX]
 #pragma unroll
   for (int s = 0; s < KMAX; ++s)
     if (s == k - 1) { thr = lv[s]; thr_i = li[s]; }
+}
+
+// Merge the per-thread sorted lists of a block: k rounds of wave- and block-wide arg-max,
+// each writing one (index, value) of the row.
+template <int KMAX>
+__device__ void topk_emit(float (&lv)[KMAX], int (&li)[KMAX], int k, int64_t* ids, float* vals) {
+  __shared__ float wv[kBlock / kWave];
+  __shared__ int wi[kBlock / kWave];
+  __shared__ int winner;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int r = 0; r < k; ++r) {
+    float bv = lv[0];
+    int bi = li[0];
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(bv, m);
+      const int oi = __shfl_xor(bi, m);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    if (lane == 0) { wv[wave] = bv; wi[wave] = bi; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      float v = wv[0];
+      int i = wi[0];
+      for (int w = 1; w < kBlock / kWave; ++w)
+        if (better(wv[w], wi[w], v, i)) { v = wv[w]; i = wi[w]; }
+      winner = i;
+      ids[r] = i;
+      vals[r] = v;
+    }
+    __syncthreads();
+    if (li[0] == winner) {
+#pragma unroll
+      for (int s = 0; s + 1 < KMAX; ++s) { lv[s] = lv[s + 1]; li[s] = li[s + 1]; }
+      lv[KMAX - 1] = -INFINITY;
+      li[KMAX - 1] = 0x7FFFFFFF;
+    }
+  }
 }
 
 template <int KMAX>
@@ -1770,37 +1977,25 @@ __global__ void __launch_bounds__(kBlock) topk_kernel(const float* scores, int64
     for (int64_t j = threadIdx.x; j < n; j += kBlock)
       topk_consider<KMAX>(lv, li, thr, thr_i, k, x[j], (int)j);
   }
-  __shared__ float wv[kBlock / kWave];
-  __shared__ int wi[kBlock / kWave];
-  __shared__ int winner;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r = 0; r < k; ++r) {
-    float bv = lv[0];
-    int bi = li[0];
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m);
-      const int oi = __shfl_xor(bi, m);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if (lane == 0) { wv[wave] = bv; wi[wave] = bi; }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      float v = wv[0];
-      int i = wi[0];
-      for (int w = 1; w < kBlock / kWave; ++w)
-        if (better(wv[w], wi[w], v, i)) { v = wv[w]; i = wi[w]; }
-      winner = i;
-      ids[row * k + r] = i;
-      vals[row * k + r] = v;
-    }
-    __syncthreads();
-    if (li[0] == winner) {
+  topk_emit<KMAX>(lv, li, k, ids + row * k, vals + row * k);
+}
+
+// Second stage of the fused score + top-k: per query row, the best k of its m candidates
+// (value, index) from the wide scorer's lists.
+template <int KMAX>
+__global__ void __launch_bounds__(kBlock) topk_merge_kernel(const float* cv, const int* ci,
+                                                            int64_t m, int k, int64_t* ids,
+                                                            float* vals) {
+  const int64_t row = blockIdx.x;
+  float lv[KMAX];
+  int li[KMAX];
 #pragma unroll
-      for (int s = 0; s + 1 < KMAX; ++s) { lv[s] = lv[s + 1]; li[s] = li[s + 1]; }
-      lv[KMAX - 1] = -INFINITY;
-      li[KMAX - 1] = 0x7FFFFFFF;
-    }
-  }
+  for (int s = 0; s < KMAX; ++s) { lv[s] = -INFINITY; li[s] = 0x7FFFFFFF; }
+  float thr = -INFINITY;
+  int thr_i = 0x7FFFFFFF;
+  for (int64_t j = threadIdx.x; j < m; j += kBlock)
+    topk_consider<KMAX>(lv, li, thr, thr_i, k, cv[row * m + j], ci[row * m + j]);
+  topk_emit<KMAX>(lv, li, k, ids + row * k, vals + row * k);
 }
 
 // ============================================================================ launchers
@@ -1988,10 +2183,35 @@ static bool dispatch_bitslice(const ScoreArgs& sa, int64_t n_gt, hipStream_t st)
   return false;
 }
 
-int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, int64_t n_groups,
-                 int64_t ldq, const uint8_t* codes, int64_t n, float* scores, void* stream) {
-  if (n == 0 || nq_per_group == 0 || n_groups == 0) return 0;
-  hipStream_t st = (hipStream_t)stream;
+// Top-k request of launch_score_impl: k best per query row instead of (or, on the paths
+// without a fused form, after) the score matrix.
+struct TopkOut {
+  int k;
+  int64_t* ids;
+  float* vals;
+};
+
+template <int R, bool TOPK>
+static void launch_wide(dim3 grid, hipStream_t st, const ScoreArgs& sa, int64_t n_qblocks,
+                        const WideTopk& tk) {
+  hipLaunchKernelGGL((score_wide_kernel<R, TOPK>), grid, dim3(kBlock), 0, st, sa, n_qblocks, tk);
+}
+
+template <bool TOPK>
+static int dispatch_wide(int R, dim3 grid, hipStream_t st, const ScoreArgs& sa, int64_t n_qblocks,
+                         const WideTopk& tk) {
+  switch (R) {
+    case 1: launch_wide<1, TOPK>(grid, st, sa, n_qblocks, tk); return 0;
+    case 2: launch_wide<2, TOPK>(grid, st, sa, n_qblocks, tk); return 0;
+    case 3: launch_wide<3, TOPK>(grid, st, sa, n_qblocks, tk); return 0;
+    case 4: launch_wide<4, TOPK>(grid, st, sa, n_qblocks, tk); return 0;
+  }
+  return (int)hipErrorInvalidValue;
+}
+
+static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq_per_group,
+                             int64_t n_groups, int64_t ldq, const uint8_t* codes, int64_t n,
+                             float* scores, const TopkOut* tko, hipStream_t st) {
   const int64_t nq = nq_per_group * n_groups;
   bool small = true;
   for (int sb = 0; sb < p.nsub; ++sb) small = small && p.sub[sb].D <= 128;
@@ -1999,10 +2219,30 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
   // long vectors with many queries per group: the bit-sliced form over 128-coordinate chunks
   const bool wide = !small && p.nsub == 1 && nq_per_group >= kWideQT && p.sub[0].D % 128 == 0;
   const int qt_w = (int)((nq_per_group + kWideQT - 1) / kWideQT);
+  const int64_t n_qblocks = (qt_w + kBlock / kWave - 1) / (kBlock / kWave);
+  const int64_t nkb = (n + kWideKT * 16 - 1) / (kWideKT * 16);
+  // fused top-k on the wide scorer: about 16384 workgroups, each walking a slice of the key
+  // blocks (measured on the 10^6-key retrieval shape: 4096 longer-lived workgroups run the
+  // same scorer 1.5 times slower, while 65536 pay more in list cuts and merging); otherwise
+  // the scores go to a temporary and the top-k kernel reads them back
+  const bool fused = tko != nullptr && wide;
+  int64_t n_slices = 0;
+  if (fused) {
+    const int64_t gx = n_groups * n_qblocks;
+    n_slices = (16384 + gx - 1) / gx;
+    n_slices = n_slices > nkb ? nkb : n_slices;
+    n_slices = n_slices > 65535 ? 65535 : n_slices;
+  }
   // workspace: per sub-plan y', w, sums, images, epilogue constants
   size_t bytes = 0;
-  size_t off_y[2], off_w[2], off_s[2], off_img[2], off_ec[2];
+  size_t off_y[2], off_w[2], off_s[2], off_img[2], off_ec[2], off_sc = 0, off_cv = 0, off_ci = 0;
   auto take = [&](size_t b) { size_t o = bytes; bytes += (b + 255) / 256 * 256; return o; };
+  if (fused) {
+    off_cv = take((size_t)nq * n_slices * tko->k * 4);
+    off_ci = take((size_t)nq * n_slices * tko->k * 4);
+  } else if (tko != nullptr) {
+    off_sc = take((size_t)nq * n * 4);
+  }
   for (int sb = 0; sb < p.nsub; ++sb) {
     const size_t D = p.sub[sb].D;
     off_y[sb] = take(nq * D * 4);
@@ -2020,6 +2260,7 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
   hipError_t e = hipMallocAsync(&ws, bytes, st);
   if (e != hipSuccess) return (int)e;
   uint8_t* wb = static_cast<uint8_t*>(ws);
+  if (tko != nullptr && !fused) scores = reinterpret_cast<float*>(wb + off_sc);
   ScoreArgs sa;
   sa.p = p;
   sa.codes = codes;
@@ -2084,15 +2325,24 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
     if (!dispatch_bitslice(sa, n_groups * qt_bs, st)) rc = (int)hipErrorInvalidValue;
   } else if (wide) {
     sa.n_qtiles = qt_w;
-    const int64_t n_qblocks = (qt_w + kBlock / kWave - 1) / (kBlock / kWave);
-    const int64_t nkb = (n + kWideKT * 16 - 1) / (kWideKT * 16);
-    const dim3 grid((unsigned)(n_groups * n_qblocks), (unsigned)(nkb < 65535 ? nkb : 65535));
-    switch (p.sub[0].R) {
-      case 1: hipLaunchKernelGGL(score_wide_kernel<1>, grid, dim3(kBlock), 0, st, sa, n_qblocks); break;
-      case 2: hipLaunchKernelGGL(score_wide_kernel<2>, grid, dim3(kBlock), 0, st, sa, n_qblocks); break;
-      case 3: hipLaunchKernelGGL(score_wide_kernel<3>, grid, dim3(kBlock), 0, st, sa, n_qblocks); break;
-      case 4: hipLaunchKernelGGL(score_wide_kernel<4>, grid, dim3(kBlock), 0, st, sa, n_qblocks); break;
-      default: rc = (int)hipErrorInvalidValue;
+    WideTopk tk;
+    tk.k = fused ? tko->k : 0;
+    tk.n_slices = n_slices;
+    tk.cv = fused ? reinterpret_cast<float*>(wb + off_cv) : nullptr;
+    tk.ci = fused ? reinterpret_cast<int*>(wb + off_ci) : nullptr;
+    const int64_t gy = fused ? n_slices : (nkb < 65535 ? nkb : 65535);
+    const dim3 grid((unsigned)(n_groups * n_qblocks), (unsigned)gy);
+    const int R = p.sub[0].R;
+    rc = fused ? dispatch_wide<true>(R, grid, st, sa, n_qblocks, tk)
+               : dispatch_wide<false>(R, grid, st, sa, n_qblocks, tk);
+    if (!rc && fused) {
+      const int64_t m = n_slices * tko->k;
+      if (tko->k <= 16)
+        hipLaunchKernelGGL(topk_merge_kernel<16>, dim3((unsigned)nq), dim3(kBlock), 0, st, tk.cv,
+                           tk.ci, m, tko->k, tko->ids, tko->vals);
+      else
+        hipLaunchKernelGGL(topk_merge_kernel<64>, dim3((unsigned)nq), dim3(kBlock), 0, st, tk.cv,
+                           tk.ci, m, tko->k, tko->ids, tko->vals);
     }
   } else {
     int sumD = 0;
@@ -2110,9 +2360,27 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
       hipLaunchKernelGGL(score_generic_kernel<2>, grid, dim3(kBlock), lds, st, sa);
   }
   if (!rc) rc = hip_rc(hipGetLastError());
+  if (!rc && tko != nullptr && !fused)
+    rc = launch_topk(scores, nq, n, tko->k, tko->ids, tko->vals, st);
   e = hipFreeAsync(ws, st);
   if (!rc && e != hipSuccess) rc = (int)e;
   return rc;
+}
+
+int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, int64_t n_groups,
+                 int64_t ldq, const uint8_t* codes, int64_t n, float* scores, void* stream) {
+  if (n == 0 || nq_per_group == 0 || n_groups == 0) return 0;
+  return launch_score_impl(p, q, dt, nq_per_group, n_groups, ldq, codes, n, scores, nullptr,
+                           (hipStream_t)stream);
+}
+
+int launch_score_topk(const PlanDev& p, const void* q, int dt, int64_t nq_per_group,
+                      int64_t n_groups, int64_t ldq, const uint8_t* codes, int64_t n, int k,
+                      int64_t* ids, float* vals, void* stream) {
+  if (nq_per_group == 0 || n_groups == 0) return 0;
+  const TopkOut tko{k, ids, vals};
+  return launch_score_impl(p, q, dt, nq_per_group, n_groups, ldq, codes, n, nullptr, &tko,
+                           (hipStream_t)stream);
 }
 
 int launch_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids, float* vals,

@@ -395,6 +395,23 @@ tq_status tq_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* id
   return from_hip(launch_topk(scores, nq, n, k, ids, vals, stream));
 }
 
+tq_status tq_score_topk(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_per_group,
+                        int64_t n_groups, int64_t ldq, const void* codes, int64_t n, int k,
+                        int64_t* ids, float* vals, void* stream) {
+  if (!plan || nq_per_group < 0 || n_groups < 0 || (dt != TQ_F32 && dt != TQ_BF16) || k < 1 ||
+      k > 64 || k > n || n >= ((int64_t)1 << 31))
+    return TQ_EINVAL;
+  if (nq_per_group == 0 || n_groups == 0) return TQ_OK;
+  const int es = dt == TQ_BF16 ? 2 : 4;
+  if (!q || !codes || !ids || !vals || ldq < plan->dev.d || (uintptr_t)q % es ||
+      (uintptr_t)codes % 16 || (uintptr_t)ids % 8 || (uintptr_t)vals % 4)
+    return TQ_EINVAL;
+  if (nq_per_group * n_groups > (int64_t)1 << 31 || n_groups > 65535 * 64) return TQ_EINVAL;
+  if (!plan_device_ok(plan)) return TQ_EINVAL;
+  return from_hip(launch_score_topk(plan->dev, q, (int)dt, nq_per_group, n_groups, ldq,
+                                    static_cast<const uint8_t*>(codes), n, k, ids, vals, stream));
+}
+
 tq_status tq_qjl(const tq_plan* plan, int subplan, const float* r, int64_t n, uint32_t* beta,
                  void* stream) {
   if (!plan || subplan < 0 || subplan >= plan->dev.nsub || n < 0) return TQ_EINVAL;

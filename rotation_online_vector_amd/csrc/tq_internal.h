@@ -69,4 +69,7 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
                  int64_t ldq, const uint8_t* codes, int64_t n, float* scores, void* stream);
 int launch_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids, float* vals,
                 void* stream);
+int launch_score_topk(const PlanDev& p, const void* q, int dt, int64_t nq_per_group,
+                      int64_t n_groups, int64_t ldq, const uint8_t* codes, int64_t n, int k,
+                      int64_t* ids, float* vals, void* stream);
 }  // namespace tq

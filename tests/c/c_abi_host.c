@@ -59,6 +59,10 @@ int main(void) {
   CHECK(tq_plan_create(128, 9, 0, NULL, 0, &plan) == TQ_EINVAL, "plan bits = 9 rejected");
   CHECK(tq_encode(NULL, NULL, TQ_BF16, 1, 128, NULL, NULL) == TQ_EINVAL, "encode without plan");
   CHECK(tq_topk(NULL, 1, 10, 3, NULL, NULL, NULL) == TQ_EINVAL, "topk with null buffers");
+  CHECK(tq_score_topk(NULL, NULL, TQ_F32, 8, 1, 128, NULL, 100, 10, NULL, NULL, NULL) == TQ_EINVAL,
+        "score_topk without plan");
+  CHECK(tq_score_topk(NULL, NULL, TQ_F32, 8, 1, 128, NULL, 5, 10, NULL, NULL, NULL) == TQ_EINVAL,
+        "score_topk with k > n");
   tq_plan_destroy(NULL);
   printf("all passed\n");
   return 0;

@@ -137,6 +137,11 @@ def test_retrieval_shape_full_with_topk():
         qn = float(np.linalg.norm(_np64(queries[q])))
         kth = est[:k].min()
         assert np.all(est[k:] <= kth + 2e-3 * qn), "query %d: a sampled key beats the top-%d" % (q, k)
+    # the fused call (as timed) returns exactly what score + top-k returned
+    ids_f, vals_f = tq.tq_score_topk(plan, queries, codes, n, k)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids_f.cpu().numpy(), ids_np)
+    assert np.array_equal(vals_f.cpu().numpy(), vals_np)
     # recall@10 of the estimate against exact fp32 inner products (reported)
     exact = queries[qi] @ keys.T
     top_exact = torch.topk(exact, k, dim=1).indices.cpu().numpy()
