@@ -34,7 +34,7 @@ MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix peak of the MI355X
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-groups", type=int, default=16)
@@ -42,6 +42,8 @@ def parse():
                     choices=["longctx", "kv", "split35", "split25", "retrieval", "small"],
                     help="long-context decode (default, the headline line); the other shapes "
                          "report the same fields for their own step (no CPU leg)")
+    ap.add_argument("--no-hbm-ceiling", action="store_true",
+                    help="skip the plain copy / read of 2 GiB measured after the timed steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB three times (untimed), so a "
                          "counter run can scale its byte counters by a copy of known size")
@@ -94,6 +96,29 @@ def cpu_baseline(keys, queries, group, bits, seed, n_groups):
             "sample": "%d of %d (sequence, KV head) groups: %d keys encoded and scored against "
                       "their %d query heads in fp64 (plan solve excluded), %.1f s of CPU time"
                       % (n_groups, n_seq * n_kv, n_groups * n_tok, group, dt)}
+
+
+def hbm_ceiling(dev, mib=2048, reps=5):
+    """What a plain streaming kernel reaches on this device, next to the 8 TB/s nominal: a
+    device-to-device copy of `mib` MiB (the runtime's copy kernel), bytes read + written,
+    mean of `reps` runs, measured after the timed steps."""
+    import torch
+    nb = mib << 20
+    src = torch.ones(nb // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    out = {}
+    for name, fn, moved in (("copy_gbs", lambda: dst.copy_(src), 2 * nb),):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        out[name] = round(moved * reps / (a.elapsed_time(b) * 1e-3) / 1e9, 1)
+    out["note"] = "device copy of %d MiB (read + write), mean of %d" % (mib, reps)
+    del src, dst
+    return out
 
 
 def _rate(n, ms):
@@ -243,6 +268,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = build_workload(args.workload, dev, W_all)
+    # the code set of the smaller shapes fits the 256 MB Infinity Cache: their GB/s are
+    # cache-resident effective rates, not HBM rates
+    code_bytes = wl["config"]["keys_per_step"] * wl["config"]["record_bytes"]
+    wl["config"]["residency"] = (
+        ("cache-resident: %.0f MB of codes, under the 256 MB Infinity Cache (effective GB/s)"
+         if code_bytes < 256e6 else "HBM: %.0f MB of codes") % (code_bytes / 1e6))
     phases = wl["phases"]
     stream = torch.cuda.current_stream()
 
@@ -276,9 +307,12 @@ def main():
     ms_step = wall * 1e3 / args.steps
     kern = {}
     for i, (nm, _) in enumerate(phases):
-        ms = float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+        t = np.array([e[i].elapsed_time(e[i + 1]) for e in evs])
+        ms = float(np.mean(t))
         b = wl["bytes"][nm]
-        kern[nm] = {"ms": ms, "bytes": b, "gbs": b / ms / 1e6}
+        kern[nm] = {"ms": ms, "bytes": b, "gbs": b / ms / 1e6,
+                    "pct": [float(x) for x in np.percentile(t, [10, 50, 90])]}
+    ceiling = hbm_ceiling(dev) if not args.no_hbm_ceiling else None
     dom = max(kern, key=lambda k: kern[k]["ms"])
     flops = wl.get("flops")
     if flops:
@@ -309,7 +343,9 @@ def main():
         "config": wl["config"],
         "encode_vectors_per_s": _rate(wl["n_keys"], kern["tq_encode"]["ms"]),
         "score_scores_per_s": _rate(wl["n_scores"], kern[score_key]["ms"]),
-        "kernels": {k: dict({"ms": round(v["ms"], 4), "alg_bytes": v["bytes"],
+        "kernels": {k: dict({"ms": round(v["ms"], 4),
+                             "ms_p10_p50_p90": [round(x, 4) for x in v["pct"]],
+                             "alg_bytes": v["bytes"],
                              "alg_gbs": round(v["gbs"], 1),
                              "hbm_frac": round(v["gbs"] / HBM_PEAK_GBS, 4)},
                             **({"mfma_tflops": round(v["tflops"], 1),
@@ -317,6 +353,7 @@ def main():
                                if "tflops" in v else {}))
                     for k, v in kern.items()},
         "roofline": roof,
+        "hbm_ceiling": ceiling,
     }
     if args.workload == "longctx" and not args.no_cpu_baseline:
         W = W_all["longctx"]
