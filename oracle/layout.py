@@ -15,6 +15,11 @@ Layout of one vector's record for a (sub-)plan with length D and R index bits
   float32 norm, float32 gamma
 Record bytes = 4 (R + 1) D / 32 + 8.  A vector split by an outlier mask stores
 the regular sub-plan's record followed by the outlier sub-plan's record.
+
+A TurboQuant-MSE record (R = b index bits, no QJL stage) drops the sign word and
+the residual norm:
+  for chunk g: R words as above;  then float32 norm.
+Record bytes = 4 R D / 32 + 4.
 """
 import numpy as np
 
@@ -72,3 +77,37 @@ def unpack_split(sp, records):
         out.append(unpack(records[:, off:off + nb], p.D, p.R))
         off += nb
     return out
+
+
+def record_bytes_mse(D, R):
+    return 4 * R * (D // 32) + 4
+
+
+def pack_mse(codes, D, R):
+    """codes: dict with idx (n, D), norm (n,) -> uint8 (n, record_bytes_mse)."""
+    idx = np.asarray(codes["idx"], dtype=np.int64)
+    n = idx.shape[0]
+    G = D // 32
+    words = np.zeros((n, G, R), dtype=np.uint64)
+    for g in range(G):
+        for t in range(32):
+            for m in range(R):
+                words[:, g, m] |= ((idx[:, 32 * g + t] >> m) & 1).astype(np.uint64) << np.uint64(t)
+    body = words.astype("<u4").reshape(n, -1).view(np.uint8)
+    tail = np.asarray(codes["norm"], dtype="<f4").reshape(n, 1).view(np.uint8)
+    return np.concatenate([body, tail], axis=1)
+
+
+def unpack_mse(records, D, R):
+    """Inverse of pack_mse: uint8 (n, record_bytes_mse) -> dict idx, norm."""
+    records = np.ascontiguousarray(records, dtype=np.uint8)
+    n = records.shape[0]
+    G = D // 32
+    words = records[:, :4 * G * R].copy().view("<u4").reshape(n, G, R).astype(np.int64)
+    idx = np.zeros((n, D), dtype=np.int64)
+    for g in range(G):
+        for t in range(32):
+            for m in range(R):
+                idx[:, 32 * g + t] |= ((words[:, g, m] >> t) & 1) << m
+    norm = records[:, 4 * G * R:4 * G * R + 4].copy().view("<f4")[:, 0]
+    return dict(idx=idx, norm=norm.astype(np.float64))

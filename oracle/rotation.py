@@ -48,6 +48,18 @@ def rotate(U, signs):
     return Z * float(D) ** -1.5
 
 
+def unrotate(Z, signs):
+    """Rows of Z mapped through Pi^T = S1 Ht S2 Ht S3 Ht, the inverse of `rotate` since Pi is
+    orthogonal: for each round from the last, multiply by the Hadamard matrix, then by that
+    round's diagonal; the three 1/sqrt(D) factors are applied together at the end."""
+    D = Z.shape[-1]
+    H = sylvester_hadamard(D)
+    U = np.asarray(Z, dtype=np.float64)
+    for r in (2, 1, 0):
+        U = (U @ H.T) * signs[r][None, :]
+    return U * float(D) ** -1.5
+
+
 def rotation_matrix(signs):
     """Pi as a dense D x D matrix (column j = Pi e_j)."""
     D = signs.shape[1]

@@ -27,6 +27,13 @@ With an outlier mask (overview §4.1.1: a share of outlier channels kept at a
 higher bit-width) the channels split into two independent sub-plans, each
 padded to its own power of two with its own rotation, codebook and QJL
 matrix; the estimate is the sum of the two sub-estimates.
+
+TurboQuant-MSE (overview §1.2.1-1.2.2; §4.1.1 recommends it at 3 bits for most
+attention heads, §4.2.1 for the vectors of an index): steps 1-3 with all b bits
+on the Lloyd-Max quantizer and no residual stage; the norm is kept.
+Dequantization (overview §4.1.2: dequantize in one batch before attention)
+inverts the rotation, which is orthogonal: xhat = n * (Pi^T c[idx])[:d].  For
+an inner-product plan the same reconstruction uses the (b-1)-bit first stage.
 """
 import math
 from dataclasses import dataclass
@@ -59,7 +66,8 @@ class Plan:
     levels: np.ndarray     # 2^R ascending, fp64
     thresholds: np.ndarray  # 2^R - 1 ascending, fp64
     signs: np.ndarray      # (3, D) +-1
-    S: np.ndarray          # (k, D), bf16-valued fp64
+    S: np.ndarray          # (k, D), bf16-valued fp64 (None for an MSE plan)
+    mse: bool = False      # TurboQuant-MSE: R = b, no QJL stage
 
 
 def make_plan(d, bits, seed, subset=0):
@@ -70,6 +78,16 @@ def make_plan(d, bits, seed, subset=0):
     S = philox.qjl_matrix(seed, subset, D, D)
     return Plan(d=d, bits=bits, seed=seed, subset=subset, D=D, R=R, k=D,
                 levels=levels, thresholds=thresholds, signs=signs, S=S)
+
+
+def make_mse_plan(d, bits, seed):
+    """TurboQuant-MSE plan: a b-bit Lloyd-Max codebook for the rotated-coordinate law and
+    the same rotation a plan with this seed uses; no QJL matrix."""
+    D = padded_length(d)
+    levels, thresholds = codebook.solve_codebook(D, bits)
+    signs = philox.rotation_signs(seed, 0, D)
+    return Plan(d=d, bits=bits, seed=seed, subset=0, D=D, R=bits, k=0,
+                levels=levels, thresholds=thresholds, signs=signs, S=None, mse=True)
 
 
 @dataclass
@@ -123,6 +141,33 @@ def encode(plan, X):
     gamma = np.sqrt(np.sum(r * r, axis=-1))
     beta, p = qjl_signs(plan.S, r)
     return dict(idx=idx, beta=beta, norm=norm, gamma=gamma, z=z, r=r, p=p)
+
+
+def encode_mse(plan, X):
+    """TurboQuant-MSE codes of the rows of X (n x d): dict with idx (n, D), norm (n,) and
+    the rotated direction z."""
+    Xp = pad(X, plan.D)
+    norm = np.sqrt(np.sum(Xp * Xp, axis=-1))
+    safe = np.where(norm > 0, norm, 1.0)
+    U = np.where(norm[:, None] > 0, Xp / safe[:, None], 0.0)
+    z = rotation.rotate(U, plan.signs)
+    return dict(idx=bucketize(z, plan.thresholds), norm=norm, z=z)
+
+
+def dequantize(plan, codes):
+    """xhat = n * (Pi^T c[idx])[:d] for each stored vector: the centroids of its cells taken
+    back through the inverse rotation and scaled by its norm (uses idx and norm only)."""
+    zhat = plan.levels[np.asarray(codes["idx"])]
+    return np.asarray(codes["norm"])[:, None] * rotation.unrotate(zhat, plan.signs)[:, :plan.d]
+
+
+def dequantize_split(sp, codes_list):
+    """Per sub-plan reconstruction, each written back to its own channels."""
+    n = len(codes_list[0]["norm"])
+    out = np.zeros((n, sp.d))
+    for p, c, ch in zip(sp.plans, codes_list, sp.channels):
+        out[:, ch] = dequantize(p, c)
+    return out
 
 
 def prepare_query(plan, Y):

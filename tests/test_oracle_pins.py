@@ -398,3 +398,79 @@ def test_layout_roundtrip(D, R):
     u = layout.unpack(layout.pack(c, D, R), D, R)
     assert np.array_equal(u["idx"], c["idx"]) and np.array_equal(u["beta"], c["beta"])
     assert np.array_equal(u["norm"], c["norm"]) and np.array_equal(u["gamma"], c["gamma"])
+
+
+# ---------------------------------------------------------------- TurboQuant-MSE and dequantization
+
+@pytest.mark.parametrize("D", [32, 128, 2048])
+def test_unrotate_inverts_rotation_and_is_the_transpose(D):
+    """Pi^T undoes Pi (Pi is orthogonal), and applying Pi^T row-wise equals multiplying by
+    the dense matrix of Pi built column by column from its images of the basis vectors."""
+    rng = np.random.default_rng(D + 1)
+    signs = philox.rotation_signs(11, 0, D)
+    U = rng.standard_normal((6, D))
+    assert np.max(np.abs(rotation.unrotate(rotation.rotate(U, signs), signs) - U)) < 1e-12
+    if D <= 128:
+        M = np.stack([rotation.rotate(np.eye(D)[j:j + 1], signs)[0] for j in range(D)], axis=1)
+        Z = rng.standard_normal((6, D))
+        assert np.max(np.abs(rotation.unrotate(Z, signs) - Z @ M)) < 1e-12
+
+
+@pytest.mark.parametrize("D,b", [(128, 3), (128, 2), (32, 4), (2048, 3)])
+def test_mse_dequantize_distortion_matches_analytic(D, b):
+    """Uniform directions (normalized Gaussian rows) rotate to exactly Beta-law coordinates,
+    so E||u - uhat||^2 over unit vectors is D times the codebook's per-coordinate MSE
+    (overview §3.1), within 3 standard errors."""
+    plan = tq.make_mse_plan(D, b, seed=2)
+    rng = np.random.default_rng(D * 10 + b)
+    n = 4000 if D <= 128 else 600
+    X = rng.standard_normal((n, D))
+    X /= np.linalg.norm(X, axis=1, keepdims=True)
+    Xh = tq.dequantize(plan, tq.encode_mse(plan, X))
+    err = np.sum((X - Xh) ** 2, axis=1)
+    analytic = D * codebook.codebook_mse(D, plan.levels, plan.thresholds)
+    assert abs(err.mean() - analytic) < 3 * err.std() / math.sqrt(n)
+    assert analytic <= 2.7 * 4.0 ** (-b)
+
+
+def test_mse_dequantize_many_bits_nearly_exact_and_norm_scaled():
+    """At b = 6 (per-vector MSE 6.3e-4) the reconstruction is within 5% of the input;
+    scaling x scales xhat; padded channels (d = 100 < D = 128) are dropped."""
+    plan = tq.make_mse_plan(100, 6, seed=4)
+    X = np.random.default_rng(9).standard_normal((50, 100))
+    Xh = tq.dequantize(plan, tq.encode_mse(plan, X))
+    assert Xh.shape == X.shape
+    assert np.max(np.linalg.norm(X - Xh, axis=1) / np.linalg.norm(X, axis=1)) < 0.05
+    Xh2 = tq.dequantize(plan, tq.encode_mse(plan, 3.0 * X))
+    assert np.max(np.abs(Xh2 - 3.0 * Xh)) < 1e-12
+
+
+def test_mse_zero_vector_dequantizes_to_zero():
+    plan = tq.make_mse_plan(64, 3, seed=0)
+    c = tq.encode_mse(plan, np.zeros((2, 64)))
+    assert np.all(c["norm"] == 0) and np.all(tq.dequantize(plan, c) == 0)
+
+
+def test_inner_product_plan_dequantizes_its_first_stage():
+    """An inner-product plan's reconstruction uses its (b-1)-bit codebook: the distortion is
+    D times that codebook's per-coordinate MSE."""
+    D, b = 128, 4
+    plan = tq.make_plan(D, b, seed=1)
+    X = np.random.default_rng(5).standard_normal((3000, D))
+    X /= np.linalg.norm(X, axis=1, keepdims=True)
+    err = np.sum((X - tq.dequantize(plan, tq.encode(plan, X))) ** 2, axis=1)
+    analytic = D * codebook.codebook_mse(D, plan.levels, plan.thresholds)
+    assert abs(err.mean() - analytic) < 3 * err.std() / math.sqrt(len(err))
+
+
+def test_layout_mse_bit_positions_by_hand():
+    D, R = 64, 3
+    idx = np.zeros((1, D), dtype=np.int64)
+    idx[0, 0] = 5          # chunk 0: planes 0 and 2, bit 0
+    idx[0, 63] = 2         # chunk 1: plane 1, bit 31
+    rec = layout.pack_mse(dict(idx=idx, norm=np.array([1.5])), D, R)
+    assert rec.shape == (1, layout.record_bytes_mse(D, R)) == (1, 28)
+    assert list(rec[0, :24].view("<u4")) == [1, 0, 1, 0, 1 << 31, 0]
+    assert list(rec[0, 24:].view("<f4")) == [1.5]
+    u = layout.unpack_mse(rec, D, R)
+    assert np.array_equal(u["idx"], idx) and u["norm"][0] == 1.5
