@@ -9,9 +9,10 @@ the streaming estimator).  Inputs are resident in HBM before timing starts.
                     [--copy-calibration MIB] [--workload NAME]
 
 `--workload` selects one of the other synthetic shapes (kv, split35, split25,
-retrieval, small); their step is encode + score (+ top-k for `small`; one fused
-score + top-k call for `retrieval`, whose roofline is the MFMA one) and the line
-carries the same fields, without the CPU leg.
+retrieval, small, mse); their step is encode + score (+ top-k for `small`; one
+fused score + top-k call for `retrieval`, whose roofline is the MFMA one; for
+`mse`, TurboQuant-MSE encode + dequantize of the long-context keys, counted in
+vectors/s) and the line carries the same fields, without the CPU leg.
 
 Prints one JSON line.  `value` is scores per second over whole steps; the
 per-kernel rates, the roofline of the dominant kernel (algorithmic bytes per
@@ -39,7 +40,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-groups", type=int, default=16)
     ap.add_argument("--workload", default="longctx",
-                    choices=["longctx", "kv", "split35", "split25", "retrieval", "small"],
+                    choices=["longctx", "kv", "split35", "split25", "retrieval", "small", "mse"],
                     help="long-context decode (default, the headline line); the other shapes "
                          "report the same fields for their own step (no CPU leg)")
     ap.add_argument("--no-hbm-ceiling", action="store_true",
@@ -155,6 +156,27 @@ def build_workload(name, dev, W_all):
                    "tq_score": n_keys * rb + n_scores * 4 + n_groups * G * d * 2},
             n_keys=n_keys, n_scores=n_scores,
             keep=(plan, keys, queries, codes, scores))
+    if name == "mse":
+        keys, _, _ = workloads.longctx_inputs(dev)
+        n_seq, n_kv, n_tok, d = W["n_seq"], W["n_kv"], W["n_tok"], W["d"]
+        n_keys = n_seq * n_kv * n_tok
+        plan = tq.tq_plan_create_mse(d, W["bits"], W["seed"])
+        rb = plan.record_bytes
+        codes = torch.empty((n_keys, rb), dtype=torch.uint8, device=dev)
+        xh = torch.empty((n_keys, d), dtype=torch.bfloat16, device=dev)
+        xk = keys.view(n_keys, d)
+        return dict(
+            config={"workload": W["name"], "n_seq": n_seq, "kv_heads": n_kv, "tokens": n_tok,
+                    "d": d, "bits": W["bits"], "mode": "mse", "keys_per_step": n_keys,
+                    "record_bytes": rb},
+            phases=[("tq_encode", lambda: tq.tq_encode(plan, xk, codes)),
+                    ("tq_dequantize", lambda: tq.tq_dequantize(plan, codes, n_keys, x=xh))],
+            bytes={"tq_encode": n_keys * d * 2 + n_keys * rb,
+                   "tq_dequantize": n_keys * rb + n_keys * d * 2},
+            n_keys=n_keys, n_scores=None,
+            value=(n_keys, "vectors/s",
+                   "TurboQuant-MSE encode + dequantize vectors/sec (d=128, 3-bit)"),
+            keep=(plan, keys, codes, xh))
     if name == "kv":
         keys, queries, _ = workloads.kv_inputs(dev, n_kv=W["n_kv"], n_tok=W["n_tok"], d=W["d"],
                                                group=W["group"], n_outlier=W["n_outlier"],
@@ -264,13 +286,16 @@ def main():
 
     W_all = {"longctx": workloads.LONGCTX, "kv": workloads.KV, "split35": workloads.SPLIT,
              "split25": workloads.SPLIT_25, "retrieval": workloads.RETRIEVAL,
-             "small": workloads.SMALL}
+             "small": workloads.SMALL, "mse": workloads.MSE_LONGCTX}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = build_workload(args.workload, dev, W_all)
     # the code set of the smaller shapes fits the 256 MB Infinity Cache: their GB/s are
     # cache-resident effective rates, not HBM rates
     code_bytes = wl["config"]["keys_per_step"] * wl["config"]["record_bytes"]
+    n_value, unit, metric = wl.get("value") or (
+        wl["n_scores"], "scores/s",
+        "quantized-key scores/sec + HBM GB/s (d=128, 3-bit); encode vectors/sec")
     wl["config"]["residency"] = (
         ("cache-resident: %.0f MB of codes, under the 256 MB Infinity Cache (effective GB/s)"
          if code_bytes < 256e6 else "HBM: %.0f MB of codes") % (code_bytes / 1e6))
@@ -331,18 +356,19 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
                 "traffic": traffic, "bytes_per_launch": kern[dom]["bytes"]}
-    score_key = "tq_score" if "tq_score" in kern else "tq_score_topk"
+    score_key = "tq_score" if "tq_score" in kern else (
+        "tq_score_topk" if "tq_score_topk" in kern else None)
     out = {
-        "metric": "quantized-key scores/sec + HBM GB/s (d=128, 3-bit); encode vectors/sec",
-        "value": wl["n_scores"] / (ms_step / 1e3),
-        "unit": "scores/s",
+        "metric": metric,
+        "value": n_value / (ms_step / 1e3),
+        "unit": unit,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": wl["config"],
         "encode_vectors_per_s": _rate(wl["n_keys"], kern["tq_encode"]["ms"]),
-        "score_scores_per_s": _rate(wl["n_scores"], kern[score_key]["ms"]),
+        "score_scores_per_s": _rate(wl["n_scores"], kern[score_key]["ms"]) if score_key else None,
         "kernels": {k: dict({"ms": round(v["ms"], 4),
                              "ms_p10_p50_p90": [round(x, 4) for x in v["pct"]],
                              "alg_bytes": v["bytes"],

@@ -16,7 +16,8 @@
  *   - "device" pointers are HIP device memory of the current device; "host"
  *     pointers are ordinary CPU memory.  The caller owns every buffer it passes.
  *   - `stream` is a hipStream_t (NULL = the default stream).  tq_encode,
- *     tq_score, tq_qjl and tq_topk only enqueue work on it and return; their
+ *     tq_score, tq_score_topk, tq_dequantize, tq_qjl and tq_topk only enqueue
+ *     work on it and return; their
  *     outputs are valid once the stream reaches that point.  A launch failure
  *     is reported as TQ_EDEVICE.
  *   - A plan is immutable after creation and may be used from several streams
@@ -32,6 +33,9 @@
  *   Size: 4*(R+1)*D/32 + 8 bytes.  With an outlier mask the record of a vector
  *   is the regular sub-plan's record followed by the outlier sub-plan's
  *   record.  Records of consecutive vectors are contiguous.
+ *   A TurboQuant-MSE plan (tq_plan_create_mse: all b bits on the Lloyd-Max
+ *   codebook, R = b, no QJL stage) stores per chunk only the R index words,
+ *   then float32 norm: 4*R*D/32 + 4 bytes.
  */
 #ifndef TQ_H
 #define TQ_H
@@ -54,20 +58,22 @@ typedef enum tq_dtype { TQ_F32 = 0, TQ_BF16 = 1 } tq_dtype;
 
 typedef struct tq_plan tq_plan;
 
+typedef enum tq_mode { TQ_MODE_INNER_PRODUCT = 0, TQ_MODE_MSE = 1 } tq_mode;
+
 typedef struct tq_subplan_desc {
   int32_t d;              /* input channels of this sub-plan */
   int32_t D;              /* rotated length: max(32, next power of two >= d) */
-  int32_t R;              /* index bits per coordinate (b - 1) */
-  int32_t k;              /* QJL rows (= D: one sign bit per rotated coordinate) */
+  int32_t R;              /* index bits per coordinate (b - 1; b for an MSE plan) */
+  int32_t k;              /* QJL rows (= D: one sign bit per rotated coordinate; 0 for MSE) */
   int32_t record_offset;  /* byte offset of this sub-plan's record in a vector's record */
-  int32_t record_bytes;   /* 4*(R+1)*D/32 + 8 */
+  int32_t record_bytes;   /* 4*(R+1)*D/32 + 8 (MSE: 4*R*D/32 + 4) */
 } tq_subplan_desc;
 
 typedef struct tq_plan_desc {
   int32_t d;              /* channels of an input vector */
   int32_t n_subplans;     /* 1, or 2 with an outlier mask (0 = regular, 1 = outlier) */
   int32_t record_bytes;   /* bytes per encoded vector */
-  int32_t reserved;
+  int32_t mode;           /* tq_mode */
   tq_subplan_desc sub[2];
 } tq_plan_desc;
 
@@ -93,6 +99,20 @@ const char* tq_status_string(tq_status status);
  */
 tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_mask,
                          int outlier_bits, tq_plan** out);
+
+/*
+ * Create a TurboQuant-MSE plan (overview §1.2.1-1.2.2: rotation and a Lloyd-Max
+ * quantizer on every coordinate; §4.1.1 recommends 3-bit MSE for most
+ * attention heads, §4.2.1 MSE codes with the norm kept for the vectors of an
+ * index): all b bits go to the codebook and there is no QJL matrix.  The
+ * rotation is the one an inner-product plan with the same seed uses.
+ *   d     input dimension, 1 <= d <= 2048
+ *   bits  b = R, 1..4
+ * tq_encode writes its records (layout above) and tq_dequantize reconstructs
+ * them; tq_score, tq_score_topk and tq_qjl return TQ_EUNSUPPORTED for it.
+ * Errors: TQ_EINVAL, TQ_ENOMEM, TQ_EDEVICE.  On error *out is set to NULL.
+ */
+tq_status tq_plan_create_mse(int d, int bits, uint64_t seed, tq_plan** out);
 
 /* Release a plan's host and device tables.  NULL is accepted. */
 void tq_plan_destroy(tq_plan* plan);
@@ -133,7 +153,7 @@ tq_status tq_encode(const tq_plan* plan, const void* x, tq_dtype dt, int64_t n, 
  * Uses a stream-ordered temporary of n_groups*nq_per_group*(6*D) floats per
  * sub-plan (hipMallocAsync / hipFreeAsync on `stream`).
  * Errors: TQ_EINVAL (null, negative sizes, ldq < d, misalignment), TQ_ENOMEM,
- * TQ_EDEVICE.  Empty sizes are a no-op.
+ * TQ_EDEVICE; TQ_EUNSUPPORTED for an MSE plan.  Empty sizes are a no-op.
  */
 tq_status tq_score(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_per_group,
                    int64_t n_groups, int64_t ldq, const void* codes, int64_t n, float* scores,
@@ -169,6 +189,23 @@ tq_status tq_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* id
 tq_status tq_score_topk(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_per_group,
                         int64_t n_groups, int64_t ldq, const void* codes, int64_t n, int k,
                         int64_t* ids, float* vals, void* stream);
+
+/*
+ * Reconstruct n vectors from their records (overview §4.1.2: dequantize in
+ * one batch before the attention step): xhat = n_x * (Pi^T c[idx])[:d], the
+ * centroids of the stored cells taken back through the rotation (Pi is
+ * orthogonal, so its inverse is its transpose) and scaled by the stored norm.
+ * For an inner-product plan this is the reconstruction of its (b-1)-bit first
+ * stage (the sign sketch is not inverted); with an outlier mask each sub-plan
+ * writes its own channels.
+ *   codes  device, n records, 16-byte aligned
+ *   x      device, n rows of d elements of type dt, row i at x + i*ldx
+ *          elements; element-aligned; written entirely
+ * Errors: TQ_EINVAL (null with n > 0, n < 0, ldx < d, misalignment),
+ * TQ_EDEVICE.  n = 0 is a no-op.
+ */
+tq_status tq_dequantize(const tq_plan* plan, const void* codes, int64_t n, void* x, tq_dtype dt,
+                        int64_t ldx, void* stream);
 
 /*
  * The QJL stage alone (overview §2.3.2): beta_j = [ (S r)_j >= 0 ] for n

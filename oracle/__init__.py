@@ -10,7 +10,8 @@ Modules:
   philox      Philox4x32-10 counter RNG, Box-Muller, bf16 rounding, plan randomness
   codebook    Lloyd-Max codebook for the rotated-coordinate Beta law
   rotation    randomized Hadamard rotation as dense fp64 matrices
-  turboquant  encode / query preparation / estimate / top-k
+  turboquant  encode / query preparation / estimate / top-k; TurboQuant-MSE encode and
+              dequantization
   layout      packed byte layout of the codes
 
 Parity status of each function is listed in the module docstrings; the only

@@ -32,12 +32,13 @@ class tq_subplan_desc(ctypes.Structure):
 
 class tq_plan_desc(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("n_subplans", ctypes.c_int32),
-                ("record_bytes", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("record_bytes", ctypes.c_int32), ("mode", ctypes.c_int32),
                 ("sub", tq_subplan_desc * 2)]
 
 
 EXPORTED = ["tq_status_string", "tq_plan_create", "tq_plan_destroy", "tq_plan_info",
-            "tq_encode", "tq_score", "tq_score_topk", "tq_topk", "tq_qjl", "tq_codebook",
+            "tq_plan_create_mse", "tq_encode", "tq_score", "tq_score_topk", "tq_topk",
+            "tq_dequantize", "tq_qjl", "tq_codebook",
             "tq_rotation_signs", "tq_qjl_matrix"]
 
 _lib = None
@@ -71,6 +72,10 @@ def load_library(path=LIB_PATH):
     lib.tq_score.restype = i32
     lib.tq_topk.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.tq_topk.restype = i32
+    lib.tq_plan_create_mse.argtypes = [i32, i32, u64, ctypes.POINTER(vp)]
+    lib.tq_plan_create_mse.restype = i32
+    lib.tq_dequantize.argtypes = [vp, vp, i64, vp, i32, i64, vp]
+    lib.tq_dequantize.restype = i32
     lib.tq_score_topk.argtypes = [vp, vp, i32, i64, i64, i64, vp, i64, i32, vp, vp, vp]
     lib.tq_score_topk.restype = i32
     lib.tq_qjl.argtypes = [vp, i32, vp, i64, vp, vp]
@@ -160,9 +165,23 @@ def tq_plan_create(d, bits, seed, outlier_mask=None, outlier_bits=0):
         int(d), int(bits), ctypes.c_uint64(int(seed)),
         None if mask_buf is None else mask_buf.ctypes.data_as(ctypes.c_void_p),
         int(outlier_bits), ctypes.byref(h)))
+    return _plan_from_handle(lib, h)
+
+
+def tq_plan_create_mse(d, bits, seed):
+    """TurboQuant-MSE plan: all b bits on the Lloyd-Max codebook, no QJL stage."""
+    lib = load_library()
+    h = ctypes.c_void_p()
+    _check("tq_plan_create_mse", lib.tq_plan_create_mse(
+        int(d), int(bits), ctypes.c_uint64(int(seed)), ctypes.byref(h)))
+    return _plan_from_handle(lib, h)
+
+
+def _plan_from_handle(lib, h):
     desc = tq_plan_desc()
     _check("tq_plan_info", lib.tq_plan_info(h, ctypes.byref(desc)))
     info = {"d": desc.d, "n_subplans": desc.n_subplans, "record_bytes": desc.record_bytes,
+            "mode": "mse" if desc.mode == 1 else "inner_product",
             "sub": [{f: getattr(desc.sub[i], f) for f, _ in tq_subplan_desc._fields_}
                     for i in range(desc.n_subplans)]}
     return Plan(h, info)
@@ -244,6 +263,22 @@ def tq_score_topk(plan, q, codes, n, k, nq_per_group=None, n_groups=1, ids=None,
         ctypes.c_void_p(codes.data_ptr()), n, int(k), ctypes.c_void_p(ids.data_ptr()),
         ctypes.c_void_p(vals.data_ptr()), _stream(stream)))
     return ids, vals
+
+
+def tq_dequantize(plan, codes, n, x=None, dtype=None, stream=None):
+    """Reconstructed vectors [n, d] (float32 or bfloat16) from n records."""
+    import torch
+    if codes.numel() < n * plan.record_bytes:
+        raise ValueError("codes buffer too small")
+    if x is None:
+        x = torch.empty((n, plan.d), dtype=dtype or torch.float32, device=codes.device)
+    rows, ld = _rows(x, plan.d)
+    if rows != n:
+        raise ValueError("output rows != n")
+    _check("tq_dequantize", load_library().tq_dequantize(
+        plan.handle, ctypes.c_void_p(codes.data_ptr()), n, ctypes.c_void_p(x.data_ptr()),
+        _dtype_code(x), ld, _stream(stream)))
+    return x
 
 
 def tq_qjl(plan, subplan, r, beta=None, stream=None):

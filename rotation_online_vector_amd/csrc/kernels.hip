@@ -156,15 +156,17 @@ struct EncodeArgs {
 
 // SPLIT: the QJL stage is left to qjl_gemm_kernel; the residual limbs go to a.rw_hi/rw_lo
 // instead of LDS and the sign words of the records are written by that kernel.
-template <int D, int R, bool SPLIT = false>
+// MSE: TurboQuant-MSE records (R = b index bits, then the norm): no residual, no QJL stage.
+template <int D, int R, bool SPLIT = false, bool MSE = false>
 __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
   using C = EncCfg<D>;
   constexpr int EPT = C::EPT, TPV = C::TPV, VPP = C::VPP, V = C::V, RS = C::RSTRIDE;
   constexpr int L = 1 << R;
+  constexpr int W = MSE ? R : R + 1;   // words per 32-coordinate chunk of a record
   const SubDev& s = a.s;
   const int recw = s.rec_sub / 4;   // words per sub-record
-  __shared__ __attribute__((aligned(16))) uint16_t rhi[SPLIT ? 8 : V * RS];
-  __shared__ __attribute__((aligned(16))) uint16_t rlo[SPLIT ? 8 : V * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t rhi[SPLIT || MSE ? 8 : V * RS];
+  __shared__ __attribute__((aligned(16))) uint16_t rlo[SPLIT || MSE ? 8 : V * RS];
   __shared__ __attribute__((aligned(16))) uint32_t rec[V * ((4 * (R + 1) * D / 32 + 8) / 4)];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -264,9 +266,9 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
 #pragma unroll
       for (int m = 0; m < R; ++m) planes[m] |= (uint32_t)((idx >> m) & 1) << e;
     }
-    gg = lane_group_sum<TPV>(gg);
+    if constexpr (!MSE) gg = lane_group_sum<TPV>(gg);
     // ---- residual limbs to LDS ----
-    {
+    if constexpr (!MSE) {
       uint32_t hi[EPT / 2], lo[EPT / 2];
 #pragma unroll
       for (int e = 0; e < EPT; e += 2) {
@@ -298,21 +300,21 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
     uint32_t* myrec = rec + vl * recw;
     if (EPT == 32) {
 #pragma unroll
-      for (int m = 0; m < R; ++m) myrec[(c0 / 32) * (R + 1) + m] = planes[m];
+      for (int m = 0; m < R; ++m) myrec[(c0 / 32) * W + m] = planes[m];
     } else {
 #pragma unroll
       for (int m = 0; m < R; ++m) {
         const uint32_t other = __shfl_xor(planes[m], 1);
-        if ((t & 1) == 0) myrec[(c0 / 32) * (R + 1) + m] = planes[m] | (other << 16);
+        if ((t & 1) == 0) myrec[(c0 / 32) * W + m] = planes[m] | (other << 16);
       }
     }
     if (t == 0) {
-      myrec[(D / 32) * (R + 1)] = __float_as_uint(nrm);
-      myrec[(D / 32) * (R + 1) + 1] = __float_as_uint(sqrtf(gg));
+      myrec[(D / 32) * W] = __float_as_uint(nrm);
+      if constexpr (!MSE) myrec[(D / 32) * W + 1] = __float_as_uint(sqrtf(gg));
     }
   }
   __syncthreads();
-  if constexpr (!SPLIT) {
+  if constexpr (!SPLIT && !MSE) {
     qjl_signs_mfma<D, V>(s, rhi, rlo, rec, recw, R + 1, R);
     __syncthreads();
   }
@@ -683,7 +685,8 @@ __device__ __forceinline__ uint32_t combine_word(uint32_t part, int G) {
 // copy of x scaled per vector by a power of two (2^14 / 2^ceil(log2 ||x||), so every scaled
 // element is below 2^14 and the bf16 values convert exactly unless they sit 2^28 below the
 // norm), in place of two bf16 products with K split in two limbs.
-template <int D, int R, int XL, bool VEC, bool F16>
+// MSE: TurboQuant-MSE records (R = b index bits, then the norm): no residual, no QJL stage.
+template <int D, int R, int XL, bool VEC, bool F16, bool MSE>
 __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeArgs a) {
   constexpr int NJT = D / 16;        // 16-row tiles of coordinates
   constexpr int NKS = D / 32;        // 32-wide k steps
@@ -692,13 +695,16 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
   constexpr uint32_t kPartMask = D >= 128 ? 0xFFFFFFFFu : (1u << (D / 4)) - 1u;
   static_assert(!F16 || XL == 1, "fp16 rotation takes bf16 input");
   constexpr int KLIMBS = F16 ? 1 : 2;
+  constexpr int W = MSE ? R : R + 1;  // words per 32-coordinate chunk of a record
   __shared__ uint4 kop[KLIMBS * NJT * NKS * 64];
-  __shared__ uint4 sop[NJT * NKS * 64];
+  __shared__ uint4 sop[MSE ? 1 : NJT * NKS * 64];
   const SubDev& s = a.s;
   for (int i = threadIdx.x; i < KLIMBS * NJT * NKS * 64; i += kEncWaves * kWave)
     kop[i] = reinterpret_cast<const uint4*>(F16 ? s.rotk16 : s.rotk)[i];
-  for (int i = threadIdx.x; i < NJT * NKS * 64; i += kEncWaves * kWave)
-    sop[i] = reinterpret_cast<const uint4*>(s.sperm)[i];
+  if constexpr (!MSE) {
+    for (int i = threadIdx.x; i < NJT * NKS * 64; i += kEncWaves * kWave)
+      sop[i] = reinterpret_cast<const uint4*>(s.sperm)[i];
+  }
   __shared__ __attribute__((aligned(16))) int chl[VEC ? 8 : D];   // input channel per coordinate
   if constexpr (!VEC) {
     for (int i = threadIdx.x; i < D; i += kEncWaves * kWave)
@@ -855,10 +861,12 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
 #pragma unroll
           for (int e = 3; e >= 0; --e) {
             const float r = bucket_sym<R>(acc[t][jb][e], Ts[t], As[t], P[t], J[t]);
-            g2[t] = fmaf(r, r, g2[t]);
-            acc[t][jb][e] = r;
+            if constexpr (!MSE) {
+              g2[t] = fmaf(r, r, g2[t]);
+              acc[t][jb][e] = r;
+            }
           }
-          if (jb % 2 == 0) {
+          if (!MSE && jb % 2 == 0) {
             // residual limbs of k step ks: element e' = tile 2 ks + e'/4, element e' % 4
             const int ks = jb / 2;
             uint32_t hw[4], lw[4];
@@ -886,14 +894,15 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
       words[t][R - 1] = combine_word<D>(~P[t] & kPartMask, G);
 #pragma unroll
       for (int m = 0; m < R - 1; ++m) words[t][m] = combine_word<D>((J[t][m] ^ P[t]) & kPartMask, G);
-      gam[t] = __builtin_amdgcn_sqrtf(sum_over_lane_groups(g2[t])) * __builtin_amdgcn_rcpf(sc[t]);
+      if constexpr (!MSE)
+        gam[t] = __builtin_amdgcn_sqrtf(sum_over_lane_groups(g2[t])) * __builtin_amdgcn_rcpf(sc[t]);
     }
     // ---- QJL: P^T = S_perm R^T and its signs, four row tiles at a time, highest first ----
     uint32_t B[NT];                     // sign bits of the projections (set = negative)
 #pragma unroll
     for (int t = 0; t < NT; ++t) B[t] = 0;
 #pragma unroll
-    for (int jq = NJT - 4 < 0 ? 0 : NJT - 4; jq >= 0; jq -= 4) {
+    for (int jq = NJT - 4 < 0 ? 0 : NJT - 4; jq >= 0 && !MSE; jq -= 4) {
       constexpr int NQ = NJT < 4 ? NJT : 4;
       f32x4 qa[NT][NQ];
 #pragma unroll
@@ -921,8 +930,10 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
 #pragma unroll
           for (int e = 3; e >= 0; --e) B[t] = shift_in_sign(B[t], qa[t][h][e]);
     }
+    if constexpr (!MSE) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) words[t][R] = combine_word<D>(~B[t] & kPartMask, G);
+      for (int t = 0; t < NT; ++t) words[t][R] = combine_word<D>(~B[t] & kPartMask, G);
+    }
     // ---- store: lane group G writes code word G of its vector, group 0 the norms ----
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -932,11 +943,11 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
         if ((G * (D / 4)) % 32 == 0) {          // first lane group of its code word
           const int g = G * D / 128;
 #pragma unroll
-          for (int m = 0; m <= R; ++m) rec[g * (R + 1) + m] = words[t][m];
+          for (int m = 0; m < W; ++m) rec[g * W + m] = words[t][m];
         }
         if (G == 0) {
-          rec[(D / 32) * (R + 1)] = __float_as_uint(nrm[t]);
-          rec[(D / 32) * (R + 1) + 1] = __float_as_uint(gam[t]);
+          rec[(D / 32) * W] = __float_as_uint(nrm[t]);
+          if constexpr (!MSE) rec[(D / 32) * W + 1] = __float_as_uint(gam[t]);
         }
       }
     }
@@ -966,6 +977,254 @@ __global__ void __launch_bounds__(kBlock) qjl_kernel(SubDev s, const float* r, i
   for (int i = threadIdx.x; i < V * (D / 32); i += kBlock) {
     const int vv = i / (D / 32);
     if (tile0 + vv < n) beta[tile0 * (D / 32) + i] = words[i];
+  }
+}
+
+// ============================================================================ dequantize
+// xhat = n * (Pi^T c[idx])[:d]: the centroids of a record's cells taken back through the
+// rotation and scaled by its norm (technical overview §4.1.2: dequantize in one batch before
+// the attention step; Pi is orthogonal, so its inverse is Pi^T = S1 Ht S2 Ht S3 Ht).  For an
+// inner-product record this is the reconstruction of its (b-1)-bit first stage.  Lanes hold
+// EPT consecutive rotated coordinates of a vector as in the encoder; the waves of a block
+// walk the vectors in a grid-stride loop whose trip count is the same for every lane of a
+// wave (the transform exchanges values between lanes).
+struct DequantArgs {
+  SubDev s;
+  const uint8_t* codes;
+  int rec_bytes;        // bytes per vector record, all sub-plans
+  int64_t n;
+  void* out;
+  int64_t ldo;          // output row stride, elements
+  int out_bf16;
+  int vec_store;        // 16-byte aligned rows, identity channels: vector stores
+  int zero;             // always 0 (see dequant_mfma_kernel)
+};
+
+template <int D, int R>
+__global__ void __launch_bounds__(kBlock) dequant_kernel(DequantArgs a) {
+  using C = EncCfg<D>;
+  constexpr int EPT = C::EPT, TPV = C::TPV, VPP = C::VPP;
+  constexpr int VPB = (kBlock / kWave) * VPP;         // vectors per block and pass
+  const SubDev& s = a.s;
+  const int W = s.mse ? R : R + 1;                    // words per 32-coordinate chunk
+  __shared__ float lev[1 << R];
+  if (threadIdx.x < (1 << R)) lev[threadIdx.x] = s.lev[threadIdx.x];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = lane % TPV, c0 = t * EPT;
+  uint32_t sw[3];
+#pragma unroll
+  for (int r = 0; r < 3; ++r) sw[r] = s.signs[r * (D / 32) + c0 / 32] >> (c0 % 32);
+  for (int64_t base = (int64_t)blockIdx.x * VPB + wave * VPP; base < a.n;
+       base += (int64_t)gridDim.x * VPB) {
+    const int64_t row = base + lane / TPV;
+    const bool live = row < a.n;
+    const uint32_t* rec = reinterpret_cast<const uint32_t*>(
+        a.codes + (live ? row : a.n - 1) * a.rec_bytes + s.rec_off);
+    uint32_t pw[R];
+#pragma unroll
+    for (int m = 0; m < R; ++m) pw[m] = rec[(c0 / 32) * W + m] >> (c0 % 32);
+    const float nrm = __uint_as_float(rec[(D / 32) * W]);
+    float v[EPT];
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      int idx = 0;
+#pragma unroll
+      for (int m = 0; m < R; ++m) idx |= (int)((pw[m] >> e) & 1u) << m;
+      v[e] = lev[idx];
+    }
+#pragma unroll
+    for (int r = 2; r >= 0; --r) {
+      fwht_lanes<EPT, TPV>(v, t);
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) v[e] = flip_sign(v[e], (sw[r] >> e) & 1u);
+    }
+    const float sc = nrm * s.inv_scale;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) v[e] *= sc;
+    if (!live) continue;
+    if (a.vec_store && c0 + EPT <= s.d) {
+      if (a.out_bf16) {
+        uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + row * a.ldo + c0);
+#pragma unroll
+        for (int q = 0; q < EPT / 8; ++q) {
+          uint32_t w[4];
+#pragma unroll
+          for (int h = 0; h < 4; ++h)
+            w[h] = f32_to_bf16_rne(v[8 * q + 2 * h]) | (f32_to_bf16_rne(v[8 * q + 2 * h + 1]) << 16);
+          o[q] = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+      } else {
+        float4* o = reinterpret_cast<float4*>(static_cast<float*>(a.out) + row * a.ldo + c0);
+#pragma unroll
+        for (int q = 0; q < EPT / 4; ++q)
+          o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        const int i = c0 + e;
+        if (i >= s.d) continue;
+        const int64_t at = row * a.ldo + (s.chan ? s.chan[i] : i);
+        if (a.out_bf16)
+          static_cast<uint16_t*>(a.out)[at] = (uint16_t)f32_to_bf16_rne(v[e]);
+        else
+          static_cast<float*>(a.out)[at] = v[e];
+      }
+    }
+  }
+}
+
+// D <= 128 with the exact fp16 K: the inverse transform on the matrix cores.  For a
+// symmetric codebook c[idx] = sum over the odd subsets S of the index bits of a_S chi_S,
+// chi_S = 2 p_S - 1 = +-1 with p_S the parity of those bits, so
+// Pi^T c = D^(-3/2) sum_S a_S K^T chi_S: one exact fp16 product per parity plane (|K| <= 2048,
+// sums of D such terms stay below 2^24), combined in fp32 with a_S.  The B operand (chi_S on
+// 8 rotated coordinates of one vector, fp16 +-1) is one 16-byte entry of a 256-entry table
+// indexed by a byte of the parity word.  Output rows are permuted so that lane group G holds
+// the input coordinates G D/4 .. G D/4 + D/4 - 1 of its column's vector (wide stores).
+template <int D, int R>
+__global__ void __launch_bounds__(kEncWaves * kWave) dequant_mfma_kernel(DequantArgs a) {
+  constexpr int NJT = D / 16, NKS = D / 32, NT = 2;
+  constexpr int NP = 1 << (R - 1);
+  constexpr int Q = D / 4;                      // coordinates per lane
+  __shared__ uint4 kt[NJT * NKS * 64];
+  __shared__ uint4 lut[256];
+  // the plane coefficients and subsets, indexed by the loop's plane number, come from LDS:
+  // indexing them in the kernel arguments lets the compiler emit a scalar load with both a
+  // register and an immediate offset, which returned the wrong word on this target
+  __shared__ float coef_s[NP];
+  __shared__ uint32_t pmask_s[NP];
+  const SubDev& s = a.s;
+  if (threadIdx.x < NP) {
+    coef_s[threadIdx.x] = s.coef[threadIdx.x];
+    pmask_s[threadIdx.x] = s.plane_mask[threadIdx.x];
+  }
+  for (int i = threadIdx.x; i < NJT * NKS * 64; i += kEncWaves * kWave)
+    kt[i] = reinterpret_cast<const uint4*>(s.rotkt16)[i];
+  for (int i = threadIdx.x; i < 256; i += kEncWaves * kWave) {
+    uint32_t w[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      w[q] = (((i >> (2 * q)) & 1) ? 0x3C00u : 0xBC00u) |
+             ((((i >> (2 * q + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
+    lut[i] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+  __syncthreads();
+  const int W = s.mse ? R : R + 1;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, G = lane >> 4;
+  for (int64_t v0 = ((int64_t)blockIdx.x * kEncWaves + wave) * 16 * NT; v0 < a.n;
+       v0 += (int64_t)gridDim.x * kEncWaves * 16 * NT) {
+    uint32_t pw[NT][NKS][R];
+    float nrm[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t row = v0 + 16 * t + col;
+      const uint32_t* rec = reinterpret_cast<const uint32_t*>(
+          a.codes + (row < a.n ? row : a.n - 1) * a.rec_bytes + s.rec_off);
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int m = 0; m < R; ++m) pw[t][ks][m] = rec[ks * W + m];
+      nrm[t] = __uint_as_float(rec[NKS * W]);
+    }
+    float out[NT][NJT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[t][jt][e] = 0.f;
+    // One parity plane at a time (its subset of index bits read from the plan), so only one
+    // set of accumulators is live.  Per plane: every B operand first, then the products,
+    // then the accumulation with a_S, which reads every product -- so no instruction writes
+    // a register an MFMA may still be reading (operands are built before the MFMAs, and the
+    // next plane's only start after this plane's results have been consumed).
+#pragma unroll 1
+    for (int p = 0; p < NP; ++p) {
+      const uint32_t pm = pmask_s[p];
+      // a zero the compiler cannot see (a.zero is 0) ties the operand addresses to the
+      // plane: reloading K^T from LDS per plane is cheaper than the 128 registers that
+      // loads hoisted out of this loop would hold
+      const int kz = p & a.zero;
+      f16x8 b[NKS][NT];
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          uint32_t P = 0;
+#pragma unroll
+          for (int m = 0; m < R; ++m) P ^= ((pm >> m) & 1u) ? pw[t][ks][m] : 0u;
+          const uint4 u = lut[(P >> (8 * G)) & 0xFFu];
+          b[ks][t] = f16x8_from_words(u.x, u.y, u.z, u.w);
+        }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc[NT][NJT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) acc[t][jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt) {
+          const uint4 ua = kt[(jt * NKS + ks) * 64 + lane + kz];
+          const f16x8 A = f16x8_from_words(ua.x, ua.y, ua.z, ua.w);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+            acc[t][jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b[ks][t], acc[t][jt], 0, 0, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const float cf = coef_s[p];
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int jt = 0; jt < NJT; ++jt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[t][jt][e] = fmaf(cf, acc[t][jt][e], out[t][jt][e]);
+    }
+    // ---- scale and store: lane group G writes coordinates G Q .. G Q + Q - 1 ----
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int64_t row = v0 + 16 * t + col;
+      if (row >= a.n) continue;
+      const float sc = nrm[t] * s.inv_scale;
+      float* v = &out[t][0][0];                 // coordinate G Q + 4 jt + e at v[4 jt + e]
+#pragma unroll
+      for (int i = 0; i < Q; ++i) v[i] *= sc;
+      const int c0 = G * Q;
+      if (a.vec_store && c0 + Q <= s.d) {
+        if (a.out_bf16) {
+          uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + row * a.ldo + c0);
+#pragma unroll
+          for (int q = 0; q < Q / 8; ++q) {
+            uint32_t w[4];
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+              w[h] = f32_to_bf16_rne(v[8 * q + 2 * h]) | (f32_to_bf16_rne(v[8 * q + 2 * h + 1]) << 16);
+            o[q] = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+        } else {
+          float4* o = reinterpret_cast<float4*>(static_cast<float*>(a.out) + row * a.ldo + c0);
+#pragma unroll
+          for (int q = 0; q < Q / 4; ++q)
+            o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < Q; ++e) {
+          const int i = c0 + e;
+          if (i >= s.d) continue;
+          const int64_t at = row * a.ldo + (s.chan ? s.chan[i] : i);
+          if (a.out_bf16)
+            static_cast<uint16_t*>(a.out)[at] = (uint16_t)f32_to_bf16_rne(v[e]);
+          else
+            static_cast<float*>(a.out)[at] = v[e];
+        }
+      }
+    }
   }
 }
 
@@ -2002,15 +2261,15 @@ __global__ void __launch_bounds__(kBlock) topk_merge_kernel(const float* cv, con
 
 static inline int hip_rc(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }
 
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool MSE = false>
 static int launch_encode_kernel(const EncodeArgs& ea, hipStream_t st) {
   const int64_t tiles = (ea.n + EncCfg<D>::V - 1) / EncCfg<D>::V;
   const dim3 grid((unsigned)tiles), block(kBlock);
   switch (ea.s.R) {
-    case 1: hipLaunchKernelGGL((encode_kernel<D, 1, SPLIT>), grid, block, 0, st, ea); break;
-    case 2: hipLaunchKernelGGL((encode_kernel<D, 2, SPLIT>), grid, block, 0, st, ea); break;
-    case 3: hipLaunchKernelGGL((encode_kernel<D, 3, SPLIT>), grid, block, 0, st, ea); break;
-    case 4: hipLaunchKernelGGL((encode_kernel<D, 4, SPLIT>), grid, block, 0, st, ea); break;
+    case 1: hipLaunchKernelGGL((encode_kernel<D, 1, SPLIT, MSE>), grid, block, 0, st, ea); break;
+    case 2: hipLaunchKernelGGL((encode_kernel<D, 2, SPLIT, MSE>), grid, block, 0, st, ea); break;
+    case 3: hipLaunchKernelGGL((encode_kernel<D, 3, SPLIT, MSE>), grid, block, 0, st, ea); break;
+    case 4: hipLaunchKernelGGL((encode_kernel<D, 4, SPLIT, MSE>), grid, block, 0, st, ea); break;
     default: return (int)hipErrorInvalidValue;
   }
   return hip_rc(hipGetLastError());
@@ -2022,6 +2281,7 @@ constexpr int64_t kSplitBatch = 32768;
 
 template <int D>
 static int launch_encode_d(const EncodeArgs& ea, hipStream_t st) {
+  if (ea.s.mse) return launch_encode_kernel<D, false, true>(ea, st);   // one pass, no signs
   if constexpr (D >= 1024) {
     const int64_t nb = ea.n < kSplitBatch ? ea.n : kSplitBatch;
     void* ws = nullptr;
@@ -2059,15 +2319,23 @@ static int launch_encode_d(const EncodeArgs& ea, hipStream_t st) {
   }
 }
 
-template <int D, int XL, bool VEC, bool F16>
-static void launch_encode_mfma_dxvf(const EncodeArgs& ea, hipStream_t st, dim3 grid) {
+template <int D, int XL, bool VEC, bool F16, bool MSE>
+static void launch_encode_mfma_dxvfm(const EncodeArgs& ea, hipStream_t st, dim3 grid) {
   const dim3 block(kEncWaves * kWave);
   switch (ea.s.R) {
-    case 1: hipLaunchKernelGGL((encode_mfma_kernel<D, 1, XL, VEC, F16>), grid, block, 0, st, ea); break;
-    case 2: hipLaunchKernelGGL((encode_mfma_kernel<D, 2, XL, VEC, F16>), grid, block, 0, st, ea); break;
-    case 3: hipLaunchKernelGGL((encode_mfma_kernel<D, 3, XL, VEC, F16>), grid, block, 0, st, ea); break;
-    case 4: hipLaunchKernelGGL((encode_mfma_kernel<D, 4, XL, VEC, F16>), grid, block, 0, st, ea); break;
+    case 1: hipLaunchKernelGGL((encode_mfma_kernel<D, 1, XL, VEC, F16, MSE>), grid, block, 0, st, ea); break;
+    case 2: hipLaunchKernelGGL((encode_mfma_kernel<D, 2, XL, VEC, F16, MSE>), grid, block, 0, st, ea); break;
+    case 3: hipLaunchKernelGGL((encode_mfma_kernel<D, 3, XL, VEC, F16, MSE>), grid, block, 0, st, ea); break;
+    case 4: hipLaunchKernelGGL((encode_mfma_kernel<D, 4, XL, VEC, F16, MSE>), grid, block, 0, st, ea); break;
   }
+}
+
+template <int D, int XL, bool VEC, bool F16>
+static void launch_encode_mfma_dxvf(const EncodeArgs& ea, hipStream_t st, dim3 grid) {
+  if (ea.s.mse)
+    launch_encode_mfma_dxvfm<D, XL, VEC, F16, true>(ea, st, grid);
+  else
+    launch_encode_mfma_dxvfm<D, XL, VEC, F16, false>(ea, st, grid);
 }
 
 template <int D, int XL, bool VEC>
@@ -2381,6 +2649,79 @@ int launch_score_topk(const PlanDev& p, const void* q, int dt, int64_t nq_per_gr
   const TopkOut tko{k, ids, vals};
   return launch_score_impl(p, q, dt, nq_per_group, n_groups, ldq, codes, n, nullptr, &tko,
                            (hipStream_t)stream);
+}
+
+template <int D>
+static int launch_dequant_mfma_d(const DequantArgs& da, hipStream_t st) {
+  const int64_t iters = (da.n + 31) / 32;
+  int64_t blocks = (iters + kEncWaves - 1) / kEncWaves;
+  if (blocks > 2048) blocks = 2048;
+  const dim3 grid((unsigned)blocks), block(kEncWaves * kWave);
+  switch (da.s.R) {
+    case 1: hipLaunchKernelGGL((dequant_mfma_kernel<D, 1>), grid, block, 0, st, da); break;
+    case 2: hipLaunchKernelGGL((dequant_mfma_kernel<D, 2>), grid, block, 0, st, da); break;
+    case 3: hipLaunchKernelGGL((dequant_mfma_kernel<D, 3>), grid, block, 0, st, da); break;
+    case 4: hipLaunchKernelGGL((dequant_mfma_kernel<D, 4>), grid, block, 0, st, da); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return hip_rc(hipGetLastError());
+}
+
+template <int D>
+static int launch_dequant_d(const DequantArgs& da, hipStream_t st) {
+  constexpr int VPB = (kBlock / kWave) * EncCfg<D>::VPP;
+  int64_t blocks = (da.n + VPB - 1) / VPB;
+  if (blocks > 8192) blocks = 8192;
+  const dim3 grid((unsigned)blocks), block(kBlock);
+  switch (da.s.R) {
+    case 1: hipLaunchKernelGGL((dequant_kernel<D, 1>), grid, block, 0, st, da); break;
+    case 2: hipLaunchKernelGGL((dequant_kernel<D, 2>), grid, block, 0, st, da); break;
+    case 3: hipLaunchKernelGGL((dequant_kernel<D, 3>), grid, block, 0, st, da); break;
+    case 4: hipLaunchKernelGGL((dequant_kernel<D, 4>), grid, block, 0, st, da); break;
+    default: return (int)hipErrorInvalidValue;
+  }
+  return hip_rc(hipGetLastError());
+}
+
+int launch_dequantize(const PlanDev& p, const uint8_t* codes, int64_t n, void* out, int dt,
+                      int64_t ldo, void* stream) {
+  if (n == 0) return 0;
+  hipStream_t st = (hipStream_t)stream;
+  const int es = dt == TQ_BF16 ? 2 : 4;
+  for (int sb = 0; sb < p.nsub; ++sb) {
+    DequantArgs da;
+    da.s = p.sub[sb];
+    da.codes = codes;
+    da.rec_bytes = p.rec_bytes;
+    da.n = n;
+    da.out = out;
+    da.ldo = ldo;
+    da.out_bf16 = dt == TQ_BF16;
+    da.vec_store = da.s.chan == nullptr && (uintptr_t)out % 16 == 0 && (ldo * es) % 16 == 0;
+    da.zero = 0;
+    int rc;
+    if (da.s.rotkt16 != nullptr && da.s.D <= 128) {
+      switch (da.s.D) {
+        case 32: rc = launch_dequant_mfma_d<32>(da, st); break;
+        case 64: rc = launch_dequant_mfma_d<64>(da, st); break;
+        default: rc = launch_dequant_mfma_d<128>(da, st); break;
+      }
+      if (rc) return rc;
+      continue;
+    }
+    switch (da.s.D) {
+      case 32: rc = launch_dequant_d<32>(da, st); break;
+      case 64: rc = launch_dequant_d<64>(da, st); break;
+      case 128: rc = launch_dequant_d<128>(da, st); break;
+      case 256: rc = launch_dequant_d<256>(da, st); break;
+      case 512: rc = launch_dequant_d<512>(da, st); break;
+      case 1024: rc = launch_dequant_d<1024>(da, st); break;
+      case 2048: rc = launch_dequant_d<2048>(da, st); break;
+      default: rc = (int)hipErrorInvalidValue;
+    }
+    if (rc) return rc;
+  }
+  return 0;
 }
 
 int launch_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids, float* vals,

@@ -22,6 +22,7 @@ int padded_length(int d) {
 }
 
 int record_bytes_of(int D, int R) { return 4 * (R + 1) * (D / 32) + 8; }
+int record_bytes_mse_of(int D, int R) { return 4 * R * (D / 32) + 4; }
 
 bool current_device(int* dev) {
   int count = 0;
@@ -49,6 +50,7 @@ struct SubHost {
   std::vector<uint16_t> S;       // [D][D]
   std::vector<uint16_t> rotk;    // MFMA operand tables (D <= 128)
   std::vector<uint16_t> rotk16;  // K in one fp16 limb, when every |K| <= 2048 (else empty)
+  std::vector<uint16_t> rotkt16; // K^T the same way (dequantization), with rotk16
   std::vector<uint16_t> sperm;
 };
 
@@ -107,10 +109,13 @@ void mfma_operand_tables(SubHost& h) {
   const int D = h.D, NJT = D / 16, NKS = D / 32;
   const std::vector<int64_t> K = rotation_integer_matrix(h.signs, D);
   h.rotk.assign((size_t)2 * NJT * NKS * 64 * 8, 0);
-  h.sperm.assign((size_t)NJT * NKS * 64 * 8, 0);
+  if (!h.S.empty()) h.sperm.assign((size_t)NJT * NKS * 64 * 8, 0);
   int64_t kmax = 0;
   for (int64_t v : K) kmax = std::max<int64_t>(kmax, v < 0 ? -v : v);
-  if (kmax <= 2048) h.rotk16.assign((size_t)NJT * NKS * 64 * 8, 0);
+  if (kmax <= 2048) {
+    h.rotk16.assign((size_t)NJT * NKS * 64 * 8, 0);
+    h.rotkt16.assign((size_t)NJT * NKS * 64 * 8, 0);
+  }
   for (int jt = 0; jt < NJT; ++jt)
     for (int ks = 0; ks < NKS; ++ks)
       for (int l = 0; l < 64; ++l)
@@ -125,10 +130,13 @@ void mfma_operand_tables(SubHost& h) {
           const size_t at = (((size_t)jt * NKS + ks) * 64 + l) * 8 + e;
           h.rotk[at] = hi;
           h.rotk[(size_t)NJT * NKS * 64 * 8 + at] = lo;
-          if (!h.rotk16.empty())
+          if (!h.rotk16.empty()) {
             h.rotk16[at] = fp16_bits_of_small_int(K[(size_t)row * D + 32 * ks + 8 * G + e]);
+            // K^T: output (input-domain) coordinate `row`, rotated coordinate as the k index
+            h.rotkt16[at] = fp16_bits_of_small_int(K[(size_t)(32 * ks + 8 * G + e) * D + row]);
+          }
           const int col = G * (D / 4) + 8 * ks + e;
-          h.sperm[at] = h.S[(size_t)row * D + col];
+          if (!h.S.empty()) h.sperm[at] = h.S[(size_t)row * D + col];
         }
 }
 
@@ -213,11 +221,15 @@ tq_status tq_qjl_matrix(uint64_t seed, int subset, int k, int D, uint16_t* S_bf1
   return TQ_OK;
 }
 
-tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_mask,
-                         int outlier_bits, tq_plan** out) {
-  if (!out) return TQ_EINVAL;
+}  // extern "C"
+
+namespace {
+
+// Both plan kinds: inner-product (R = b - 1 index bits + QJL signs) and TurboQuant-MSE
+// (R = b index bits, no QJL matrix).  Arguments are validated by the callers.
+tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mask,
+                      int outlier_bits, bool mse, tq_plan** out) {
   *out = nullptr;
-  if (d < 1 || d > kMaxD || bits < 2 || bits > kMaxR + 1) return TQ_EINVAL;
   std::vector<SubHost> subs;
   if (outlier_mask) {
     if (outlier_bits < 2 || outlier_bits > kMaxR + 1) return TQ_EINVAL;
@@ -230,7 +242,7 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
     subs.push_back(std::move(out_s));
   } else {
     SubHost s;
-    s.d = d; s.R = bits - 1;
+    s.d = d; s.R = mse ? bits : bits - 1;
     subs.push_back(std::move(s));
   }
   int dev = -1;
@@ -250,7 +262,7 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
   // host tables and device layout
   size_t bytes = 0;
   size_t off_sign[2] = {0, 0}, off_S[2] = {0, 0}, off_chan[2] = {0, 0};
-  size_t off_rotk[2] = {0, 0}, off_rotk16[2] = {0, 0}, off_sperm[2] = {0, 0};
+  size_t off_rotk[2] = {0, 0}, off_rotk16[2] = {0, 0}, off_rotkt16[2] = {0, 0}, off_sperm[2] = {0, 0};
   auto take = [&](size_t b) { size_t o = bytes; bytes += (b + 255) / 256 * 256; return o; };
   for (int i = 0; i < pd.nsub; ++i) {
     SubHost& h = subs[i];
@@ -261,17 +273,20 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
     solve_codebook(h.D, h.R, h.lev.data(), h.thr.data());
     h.signs.resize(3 * (h.D / 32));
     sign_words(seed, i, h.D, h.signs.data());
-    h.S.resize((size_t)h.D * h.D);
-    qjl_matrix_bf16(seed, i, h.D, h.D, h.S.data());
+    if (!mse) {
+      h.S.resize((size_t)h.D * h.D);
+      qjl_matrix_bf16(seed, i, h.D, h.D, h.S.data());
+    }
     SubDev& s = pd.sub[i];
     memset(&s, 0, sizeof(s));
     s.d = h.d;
     s.D = h.D;
     s.logD = __builtin_ctz(h.D);
     s.R = h.R;
-    s.k = h.D;
+    s.k = mse ? 0 : h.D;
+    s.mse = mse ? 1 : 0;
     s.rec_off = pd.rec_bytes;
-    s.rec_sub = record_bytes_of(h.D, h.R);
+    s.rec_sub = mse ? record_bytes_mse_of(h.D, h.R) : record_bytes_of(h.D, h.R);
     pd.rec_bytes += s.rec_sub;
     s.inv_scale = (float)std::pow((double)h.D, -1.5);
     for (int l = 0; l < L; ++l) s.lev[l] = (float)h.lev[l];
@@ -281,12 +296,13 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
       return TQ_EDEVICE;
     }
     off_sign[i] = take(h.signs.size() * 4);
-    off_S[i] = take(h.S.size() * 2);
+    if (!h.S.empty()) off_S[i] = take(h.S.size() * 2);
     if (!h.chan.empty()) off_chan[i] = take(h.chan.size() * 4);
     if (h.D <= kMfmaMaxD) {
       mfma_operand_tables(h);
       off_rotk[i] = take(h.rotk.size() * 2);
       off_rotk16[i] = take(h.rotk16.size() * 2);
+      off_rotkt16[i] = take(h.rotkt16.size() * 2);
       off_sperm[i] = take(h.sperm.size() * 2);
     }
   }
@@ -302,7 +318,7 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
     SubHost& h = subs[i];
     SubDev& s = pd.sub[i];
     e = hipMemcpy(base + off_sign[i], h.signs.data(), h.signs.size() * 4, hipMemcpyHostToDevice);
-    if (e == hipSuccess)
+    if (e == hipSuccess && !h.S.empty())
       e = hipMemcpy(base + off_S[i], h.S.data(), h.S.size() * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess && !h.chan.empty())
       e = hipMemcpy(base + off_chan[i], h.chan.data(), h.chan.size() * 4, hipMemcpyHostToDevice);
@@ -310,6 +326,9 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
       e = hipMemcpy(base + off_rotk[i], h.rotk.data(), h.rotk.size() * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess && !h.rotk16.empty())
       e = hipMemcpy(base + off_rotk16[i], h.rotk16.data(), h.rotk16.size() * 2,
+                    hipMemcpyHostToDevice);
+    if (e == hipSuccess && !h.rotkt16.empty())
+      e = hipMemcpy(base + off_rotkt16[i], h.rotkt16.data(), h.rotkt16.size() * 2,
                     hipMemcpyHostToDevice);
     if (e == hipSuccess && !h.sperm.empty())
       e = hipMemcpy(base + off_sperm[i], h.sperm.data(), h.sperm.size() * 2, hipMemcpyHostToDevice);
@@ -319,14 +338,37 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
       return TQ_EDEVICE;
     }
     s.signs = reinterpret_cast<const uint32_t*>(base + off_sign[i]);
-    s.S = reinterpret_cast<const uint16_t*>(base + off_S[i]);
+    s.S = h.S.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_S[i]);
     s.chan = h.chan.empty() ? nullptr : reinterpret_cast<const int32_t*>(base + off_chan[i]);
     s.rotk = h.rotk.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_rotk[i]);
     s.rotk16 = h.rotk16.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_rotk16[i]);
+    s.rotkt16 = h.rotkt16.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_rotkt16[i]);
     s.sperm = h.sperm.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_sperm[i]);
   }
   *out = plan;
   return TQ_OK;
+}
+
+bool is_mse(const tq_plan* p) { return p->dev.sub[0].mse != 0; }
+
+}  // namespace
+
+extern "C" {
+
+tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_mask,
+                         int outlier_bits, tq_plan** out) {
+  if (!out) return TQ_EINVAL;
+  *out = nullptr;
+  if (d < 1 || d > kMaxD || bits < 2 || bits > kMaxR + 1) return TQ_EINVAL;
+  if (outlier_mask && (outlier_bits < 2 || outlier_bits > kMaxR + 1)) return TQ_EINVAL;
+  return create_plan(d, bits, seed, outlier_mask, outlier_bits, false, out);
+}
+
+tq_status tq_plan_create_mse(int d, int bits, uint64_t seed, tq_plan** out) {
+  if (!out) return TQ_EINVAL;
+  *out = nullptr;
+  if (d < 1 || d > kMaxD || bits < 1 || bits > kMaxR) return TQ_EINVAL;
+  return create_plan(d, bits, seed, nullptr, 0, true, out);
 }
 
 void tq_plan_destroy(tq_plan* plan) {
@@ -341,6 +383,7 @@ tq_status tq_plan_info(const tq_plan* plan, tq_plan_desc* desc) {
   desc->d = plan->dev.d;
   desc->n_subplans = plan->dev.nsub;
   desc->record_bytes = plan->dev.rec_bytes;
+  desc->mode = is_mse(plan) ? TQ_MODE_MSE : TQ_MODE_INNER_PRODUCT;
   for (int i = 0; i < plan->dev.nsub; ++i) {
     const SubDev& s = plan->dev.sub[i];
     desc->sub[i].d = s.d;
@@ -380,6 +423,7 @@ tq_status tq_score(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_p
     return TQ_EINVAL;
   if (nq_per_group * n_groups > (int64_t)1 << 31 || n_groups > 65535 * 64) return TQ_EINVAL;
   if (!plan_device_ok(plan)) return TQ_EINVAL;
+  if (is_mse(plan)) return TQ_EUNSUPPORTED;
   return from_hip(launch_score(plan->dev, q, (int)dt, nq_per_group, n_groups, ldq,
                                static_cast<const uint8_t*>(codes), n, scores, stream));
 }
@@ -408,8 +452,21 @@ tq_status tq_score_topk(const tq_plan* plan, const void* q, tq_dtype dt, int64_t
     return TQ_EINVAL;
   if (nq_per_group * n_groups > (int64_t)1 << 31 || n_groups > 65535 * 64) return TQ_EINVAL;
   if (!plan_device_ok(plan)) return TQ_EINVAL;
+  if (is_mse(plan)) return TQ_EUNSUPPORTED;
   return from_hip(launch_score_topk(plan->dev, q, (int)dt, nq_per_group, n_groups, ldq,
                                     static_cast<const uint8_t*>(codes), n, k, ids, vals, stream));
+}
+
+tq_status tq_dequantize(const tq_plan* plan, const void* codes, int64_t n, void* x, tq_dtype dt,
+                        int64_t ldx, void* stream) {
+  if (!plan || n < 0 || (dt != TQ_F32 && dt != TQ_BF16)) return TQ_EINVAL;
+  if (n == 0) return TQ_OK;
+  const int es = dt == TQ_BF16 ? 2 : 4;
+  if (!codes || !x || ldx < plan->dev.d || (uintptr_t)codes % 16 || (uintptr_t)x % es)
+    return TQ_EINVAL;
+  if (!plan_device_ok(plan)) return TQ_EINVAL;
+  return from_hip(launch_dequantize(plan->dev, static_cast<const uint8_t*>(codes), n, x, (int)dt,
+                                    ldx, stream));
 }
 
 tq_status tq_qjl(const tq_plan* plan, int subplan, const float* r, int64_t n, uint32_t* beta,
@@ -418,6 +475,7 @@ tq_status tq_qjl(const tq_plan* plan, int subplan, const float* r, int64_t n, ui
   if (n == 0) return TQ_OK;
   if (!r || !beta || (uintptr_t)r % 4 || (uintptr_t)beta % 4) return TQ_EINVAL;
   if (!plan_device_ok(plan)) return TQ_EINVAL;
+  if (is_mse(plan)) return TQ_EUNSUPPORTED;
   return from_hip(launch_qjl(plan->dev.sub[subplan], r, n, beta, stream));
 }
 

@@ -26,6 +26,7 @@ struct SubDev {
   int k;            // QJL rows (= D)
   int rec_off;      // byte offset of the sub-record inside a vector record
   int rec_sub;      // bytes of the sub-record
+  int mse;          // 1: TurboQuant-MSE record (R words per chunk, then the norm; k = 0)
   int n_planes;     // 2^(R-1) odd-subset planes used by the bit-sliced scorer
   float inv_scale;  // D^(-3/2): the three normalized transforms folded into one multiply
   float thr[15];    // 2^R - 1 thresholds (ascending)
@@ -40,6 +41,8 @@ struct SubDev {
   // (16x16x32 bf16 tiles, 64 lanes x 8 values each)
   const uint16_t* rotk;   // [2 limbs][D/16 row tiles][D/32 k steps][64][8]: D^(3/2) Pi
   const uint16_t* rotk16; // [D/16][D/32][64][8]: the same in one exact fp16 limb, or null
+  const uint16_t* rotkt16; // [D/16][D/32][64][8]: K^T likewise (rows = input coordinates,
+                           // permuted as above; k = rotated coordinate), with rotk16
   const uint16_t* sperm;  // [D/16][D/32][64][8]: S with columns in the residual register order
 };
 
@@ -69,6 +72,8 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
                  int64_t ldq, const uint8_t* codes, int64_t n, float* scores, void* stream);
 int launch_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids, float* vals,
                 void* stream);
+int launch_dequantize(const PlanDev& p, const uint8_t* codes, int64_t n, void* out, int dt,
+                      int64_t ldo, void* stream);
 int launch_score_topk(const PlanDev& p, const void* q, int dt, int64_t nq_per_group,
                       int64_t n_groups, int64_t ldq, const uint8_t* codes, int64_t n, int k,
                       int64_t* ids, float* vals, void* stream);

@@ -63,6 +63,10 @@ int main(void) {
         "score_topk without plan");
   CHECK(tq_score_topk(NULL, NULL, TQ_F32, 8, 1, 128, NULL, 5, 10, NULL, NULL, NULL) == TQ_EINVAL,
         "score_topk with k > n");
+  CHECK(tq_plan_create_mse(128, 0, 0, &plan) == TQ_EINVAL && plan == NULL, "mse plan bits = 0 rejected");
+  CHECK(tq_plan_create_mse(128, 5, 0, &plan) == TQ_EINVAL, "mse plan bits = 5 rejected");
+  CHECK(tq_plan_create_mse(128, 3, 0, NULL) == TQ_EINVAL, "mse plan without output");
+  CHECK(tq_dequantize(NULL, NULL, 1, NULL, TQ_F32, 128, NULL) == TQ_EINVAL, "dequantize without plan");
   tq_plan_destroy(NULL);
   printf("all passed\n");
   return 0;

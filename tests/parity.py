@@ -92,3 +92,30 @@ def check_topk(ids_gpu, vals_gpu, est_ref, k, qnorm, xnorm, what=""):
 
 def unpack_gpu(sp, codes_u8):
     return layout.unpack_split(sp, codes_u8)
+
+
+def compare_codes_mse(plan, ocodes, gcodes, what=""):
+    """TurboQuant-MSE codes: indices as in compare_codes (exact outside the band), norms to
+    1e-6 relative, zero norms exact."""
+    idx_mis = ocodes["idx"] != gcodes["idx"]
+    out_of_band = idx_mis & ~code_band(plan, ocodes["z"])
+    assert not out_of_band.any(), "%s: %d index mismatches outside the band (first at %s)" % (
+        what, int(out_of_band.sum()), np.argwhere(out_of_band)[:3].tolist())
+    n_idx = idx_mis.sum()
+    assert n_idx <= max(1, MISMATCH_FRACTION * idx_mis.size), \
+        "%s: %d in-band index mismatches of %d" % (what, n_idx, idx_mis.size)
+    nrm_rel = np.abs(gcodes["norm"] - ocodes["norm"]) / np.maximum(ocodes["norm"], 1e-30)
+    assert np.all(nrm_rel[ocodes["norm"] > 0] <= 1e-6), "%s: norm rel err %g" % (what, nrm_rel.max())
+    assert np.all(gcodes["norm"][ocodes["norm"] == 0] == 0)
+    return dict(idx_mismatch=int(n_idx), norm_rel=float(nrm_rel.max()))
+
+
+def check_dequantized(x_gpu, x_ref, norms, bf16, what=""):
+    """Reconstruction vs the oracle's on the same codes: within 2e-6 of the vector norm per
+    element (fp32 transform rounding), plus half a bf16 step of the value for bf16 output."""
+    tol = 2e-6 * norms[:, None] + (2.0 ** -8 * np.abs(x_ref) if bf16 else 0.0)
+    err = np.abs(x_gpu - x_ref)
+    bad = err > tol
+    assert not bad.any(), "%s: %d elements off (max err/tol %g)" % (
+        what, int(bad.sum()), float(np.max(err / np.maximum(tol, 1e-30))))
+    return float(np.max(err / np.maximum(tol, 1e-30)))

@@ -148,3 +148,28 @@ def test_retrieval_shape_full_with_topk():
     recall = np.mean([len(set(top_exact[j]) & set(ids_np[q])) / k for j, q in enumerate(qidx)])
     print("recall@10 vs exact fp32 on %d queries: %.3f" % (len(qidx), recall))
     assert recall > 0.5
+
+
+def test_mse_long_context_shape_full_as_benchmarked():
+    """TurboQuant-MSE encode + dequantize of all 16.8 M long-context keys (the MSE bench
+    step); sampled records against the oracle's encode, their reconstructions against the
+    oracle's dequantization of the stored codes."""
+    from oracle import layout
+    W = workloads.MSE_LONGCTX
+    keys, _, _ = workloads.longctx_inputs(DEV)
+    d = W["d"]
+    plan = tq.tq_plan_create_mse(d, W["bits"], W["seed"])
+    op = otq.make_mse_plan(d, W["bits"], W["seed"])
+    flat = keys.view(-1, d)
+    n = flat.shape[0]
+    codes = tq.tq_encode(plan, flat)
+    xh = tq.tq_dequantize(plan, codes, n, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(8)
+    rows = np.sort(np.concatenate([rng.choice(n, 3000, replace=False), [0, n - 1]]))
+    ri = torch.as_tensor(rows, device=DEV)
+    got = layout.unpack_mse(codes[ri].cpu().numpy(), op.D, W["bits"])
+    ref = otq.encode_mse(op, _np64(flat[ri]))
+    parity.compare_codes_mse(op, ref, got, "mse long-context")
+    xr = otq.dequantize(op, dict(idx=got["idx"], norm=got["norm"]))
+    parity.check_dequantized(_np64(xh[ri]), xr, got["norm"], True, "mse long-context dequant")

@@ -30,6 +30,9 @@ RETRIEVAL = dict(name="retrieval-1e6x1536-fp32-b4", n_keys=1_000_000, n_queries=
                  bits=4, topk=10, seed=0)
 LONGCTX = dict(name="longctx-16x8x131072x128-bf16-b3", n_seq=16, n_kv=8, n_tok=131072, d=128,
                group=4, bits=3, n_heavy=6, dof=3, seed=0)
+# TurboQuant-MSE on the same keys: 3-bit codes for most heads (technical overview §4.1.1),
+# dequantized in one batch before attention (§4.1.2)
+MSE_LONGCTX = dict(LONGCTX, name="mse-longctx-16x8x131072x128-bf16-b3")
 
 
 def small_inputs(n_keys=4096, n_queries=64, d=128, seed=0):
