@@ -997,7 +997,6 @@ struct DequantArgs {
   int64_t ldo;          // output row stride, elements
   int out_bf16;
   int vec_store;        // 16-byte aligned rows, identity channels: vector stores
-  int zero;             // always 0 (see dequant_mfma_kernel)
 };
 
 template <int D, int R>
@@ -1051,7 +1050,7 @@ __global__ void __launch_bounds__(kBlock) dequant_kernel(DequantArgs a) {
           uint32_t w[4];
 #pragma unroll
           for (int h = 0; h < 4; ++h)
-            w[h] = f32_to_bf16_rne(v[8 * q + 2 * h]) | (f32_to_bf16_rne(v[8 * q + 2 * h + 1]) << 16);
+            w[h] = pack_bf16_rne(v[8 * q + 2 * h], v[8 * q + 2 * h + 1]);
           o[q] = make_uint4(w[0], w[1], w[2], w[3]);
         }
       } else {
@@ -1067,7 +1066,7 @@ __global__ void __launch_bounds__(kBlock) dequant_kernel(DequantArgs a) {
         if (i >= s.d) continue;
         const int64_t at = row * a.ldo + (s.chan ? s.chan[i] : i);
         if (a.out_bf16)
-          static_cast<uint16_t*>(a.out)[at] = (uint16_t)f32_to_bf16_rne(v[e]);
+          static_cast<uint16_t*>(a.out)[at] = (uint16_t)pack_bf16_rne(v[e], 0.f);
         else
           static_cast<float*>(a.out)[at] = v[e];
       }
@@ -1075,153 +1074,148 @@ __global__ void __launch_bounds__(kBlock) dequant_kernel(DequantArgs a) {
   }
 }
 
-// D <= 128 with the exact fp16 K: the inverse transform on the matrix cores.  For a
-// symmetric codebook c[idx] = sum over the odd subsets S of the index bits of a_S chi_S,
-// chi_S = 2 p_S - 1 = +-1 with p_S the parity of those bits, so
-// Pi^T c = D^(-3/2) sum_S a_S K^T chi_S: one exact fp16 product per parity plane (|K| <= 2048,
-// sums of D such terms stay below 2^24), combined in fp32 with a_S.  The B operand (chi_S on
-// 8 rotated coordinates of one vector, fp16 +-1) is one 16-byte entry of a 256-entry table
-// indexed by a byte of the parity word.  Output rows are permuted so that lane group G holds
-// the input coordinates G D/4 .. G D/4 + D/4 - 1 of its column's vector (wide stores).
+// D <= 128 with the exact fp16 K: the inverse transform on the matrix cores,
+// Pi^T c = D^(-3/2) K^T c, with c (the centroids of a vector's cells, scaled by 2^10) in two
+// fp16 limbs, hi = fp16(c) and lo = fp16(c - hi): K^T c_hi + K^T c_lo accumulated in fp32
+// (the fp16 products are exact; the sums round like an fp32 transform).  A lane's B operand
+// covers 8 rotated coordinates of one vector; both limbs of a pair of coordinates come from
+// one 8-byte entry of an LDS table indexed by the pair's 2R index bits.  Every B operand of
+// the iteration is built before the first product.  Output rows are permuted so that lane
+// group G holds input coordinates 32 q + 8 G + (0..7), q = 0 .. D/32 - 1, of its column's
+// vector (tile jt = 2 q + i/4, element i%4): each store covers 32 adjacent coordinates.
+constexpr float kDequantLevelScale = 1024.f;   // keeps the low limbs of the levels normal
+
+constexpr int kDqWaves = 4;     // waves per workgroup of the matrix-core reconstruction
+
 template <int D, int R>
-__global__ void __launch_bounds__(kEncWaves * kWave) dequant_mfma_kernel(DequantArgs a) {
+__global__ void __launch_bounds__(kDqWaves * kWave) dequant_mfma_kernel(DequantArgs a) {
   constexpr int NJT = D / 16, NKS = D / 32, NT = 2;
-  constexpr int NP = 1 << (R - 1);
-  constexpr int Q = D / 4;                      // coordinates per lane
+  constexpr int NPAIR = 1 << (2 * R);
   __shared__ uint4 kt[NJT * NKS * 64];
-  __shared__ uint4 lut[256];
-  // the plane coefficients and subsets, indexed by the loop's plane number, come from LDS:
-  // indexing them in the kernel arguments lets the compiler emit a scalar load with both a
-  // register and an immediate offset, which returned the wrong word on this target
-  __shared__ float coef_s[NP];
-  __shared__ uint32_t pmask_s[NP];
+  __shared__ uint2 pair_tab[NPAIR];
   const SubDev& s = a.s;
-  if (threadIdx.x < NP) {
-    coef_s[threadIdx.x] = s.coef[threadIdx.x];
-    pmask_s[threadIdx.x] = s.plane_mask[threadIdx.x];
-  }
-  for (int i = threadIdx.x; i < NJT * NKS * 64; i += kEncWaves * kWave)
+  for (int i = threadIdx.x; i < NJT * NKS * 64; i += kDqWaves * kWave)
     kt[i] = reinterpret_cast<const uint4*>(s.rotkt16)[i];
-  for (int i = threadIdx.x; i < 256; i += kEncWaves * kWave) {
-    uint32_t w[4];
+  // entry i: coordinate A has index bits i_0, i_2, i_4, ..., coordinate B i_1, i_3, ...
+  for (int i = threadIdx.x; i < NPAIR; i += kDqWaves * kWave) {
+    int ia = 0, ib = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      w[q] = (((i >> (2 * q)) & 1) ? 0x3C00u : 0xBC00u) |
-             ((((i >> (2 * q + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
-    lut[i] = make_uint4(w[0], w[1], w[2], w[3]);
+    for (int m = 0; m < R; ++m) {
+      ia |= ((i >> (2 * m)) & 1) << m;
+      ib |= ((i >> (2 * m + 1)) & 1) << m;
+    }
+    const float ca = s.lev[ia] * kDequantLevelScale, cb = s.lev[ib] * kDequantLevelScale;
+    typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
+    const f16x2 hv = __builtin_amdgcn_cvt_pkrtz(ca, cb);
+    const uint32_t hi = __builtin_bit_cast(uint32_t, hv);
+    const uint32_t lo = __builtin_bit_cast(
+        uint32_t, __builtin_amdgcn_cvt_pkrtz(ca - (float)hv[0], cb - (float)hv[1]));
+    pair_tab[i] = make_uint2(hi, lo);
   }
   __syncthreads();
   const int W = s.mse ? R : R + 1;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, G = lane >> 4;
-  for (int64_t v0 = ((int64_t)blockIdx.x * kEncWaves + wave) * 16 * NT; v0 < a.n;
-       v0 += (int64_t)gridDim.x * kEncWaves * 16 * NT) {
-    uint32_t pw[NT][NKS][R];
-    float nrm[NT];
+  const float osc = s.inv_scale / kDequantLevelScale;
+  const int64_t step = (int64_t)gridDim.x * kDqWaves * 16 * NT;
+  // this iteration's record words (index planes, norm), loaded one iteration ahead
+  uint32_t rw[NT][NKS][R], rn[NT];
+  auto load_records = [&](int64_t v0, uint32_t (&pw)[NT][NKS][R], uint32_t (&pn)[NT]) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int64_t row = v0 + 16 * t + col;
-      const uint32_t* rec = reinterpret_cast<const uint32_t*>(
-          a.codes + (row < a.n ? row : a.n - 1) * a.rec_bytes + s.rec_off);
+      const int64_t rr = row < a.n ? row : a.n - 1;
+      const uint32_t* rec = reinterpret_cast<const uint32_t*>(a.codes + rr * a.rec_bytes + s.rec_off);
+      pn[t] = rec[NKS * W];
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int m = 0; m < R; ++m) pw[t][ks][m] = rec[ks * W + m];
-      nrm[t] = __uint_as_float(rec[NKS * W]);
     }
-    float out[NT][NJT][4];
+  };
+  int64_t v0 = ((int64_t)blockIdx.x * kDqWaves + wave) * 16 * NT;
+  if (v0 < a.n) load_records(v0, rw, rn);
+  for (; v0 < a.n; v0 += step) {
+    uint32_t cw[NT][NKS][R];
+    float nrm[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int jt = 0; jt < NJT; ++jt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) out[t][jt][e] = 0.f;
-    // One parity plane at a time (its subset of index bits read from the plan), so only one
-    // set of accumulators is live.  Per plane: every B operand first, then the products,
-    // then the accumulation with a_S, which reads every product -- so no instruction writes
-    // a register an MFMA may still be reading (operands are built before the MFMAs, and the
-    // next plane's only start after this plane's results have been consumed).
-#pragma unroll 1
-    for (int p = 0; p < NP; ++p) {
-      const uint32_t pm = pmask_s[p];
-      // a zero the compiler cannot see (a.zero is 0) ties the operand addresses to the
-      // plane: reloading K^T from LDS per plane is cheaper than the 128 registers that
-      // loads hoisted out of this loop would hold
-      const int kz = p & a.zero;
-      f16x8 b[NKS][NT];
+    for (int t = 0; t < NT; ++t) {
+      nrm[t] = __uint_as_float(rn[t]);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          uint32_t P = 0;
+        for (int m = 0; m < R; ++m) cw[t][ks][m] = rw[t][ks][m] >> (8 * G);  // coordinate 8 G + e at bit e
+    }
+    // the next iteration's records, in flight during this one
+    if (v0 + step < a.n) load_records(v0 + step, rw, rn);
+    // ---- K^T c, both limbs into one accumulator, k step by k step ----
+    f32x4 acc[NT][NJT];
 #pragma unroll
-          for (int m = 0; m < R; ++m) P ^= ((pm >> m) & 1u) ? pw[t][ks][m] : 0u;
-          const uint4 u = lut[(P >> (8 * G)) & 0xFFu];
-          b[ks][t] = f16x8_from_words(u.x, u.y, u.z, u.w);
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int jt = 0; jt < NJT; ++jt) acc[t][jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      f16x8 bh[NT], bl[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          uint32_t pi = 0;
+#pragma unroll
+          for (int m = 0; m < R; ++m) pi |= ((cw[t][ks][m] >> (2 * w)) & 3u) << (2 * m);
+          const uint2 e = pair_tab[pi];
+          hw[w] = e.x;
+          lw[w] = e.y;
         }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 acc[NT][NJT];
+        bh[t] = f16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
+        bl[t] = f16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
+      }
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
+      for (int jt = 0; jt < NJT; ++jt) {
+        const uint4 ua = kt[(jt * NKS + ks) * 64 + lane];
+        const f16x8 A = f16x8_from_words(ua.x, ua.y, ua.z, ua.w);
 #pragma unroll
-        for (int jt = 0; jt < NJT; ++jt) acc[t][jt] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-#pragma unroll
-        for (int jt = 0; jt < NJT; ++jt) {
-          const uint4 ua = kt[(jt * NKS + ks) * 64 + lane + kz];
-          const f16x8 A = f16x8_from_words(ua.x, ua.y, ua.z, ua.w);
-#pragma unroll
-          for (int t = 0; t < NT; ++t)
-            acc[t][jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, b[ks][t], acc[t][jt], 0, 0, 0);
+        for (int t = 0; t < NT; ++t) {
+          acc[t][jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[t], acc[t][jt], 0, 0, 0);
+          acc[t][jt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[t], acc[t][jt], 0, 0, 0);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      const float cf = coef_s[p];
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int jt = 0; jt < NJT; ++jt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) out[t][jt][e] = fmaf(cf, acc[t][jt][e], out[t][jt][e]);
     }
-    // ---- scale and store: lane group G writes coordinates G Q .. G Q + Q - 1 ----
+    // ---- scale and store: lane group G writes coordinates 32 q + 8 G .. + 7 ----
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int64_t row = v0 + 16 * t + col;
       if (row >= a.n) continue;
-      const float sc = nrm[t] * s.inv_scale;
-      float* v = &out[t][0][0];                 // coordinate G Q + 4 jt + e at v[4 jt + e]
+      const float sc = nrm[t] * osc;
 #pragma unroll
-      for (int i = 0; i < Q; ++i) v[i] *= sc;
-      const int c0 = G * Q;
-      if (a.vec_store && c0 + Q <= s.d) {
-        if (a.out_bf16) {
-          uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + row * a.ldo + c0);
+      for (int q = 0; q < NKS; ++q) {
+        float v[8];
 #pragma unroll
-          for (int q = 0; q < Q / 8; ++q) {
-            uint32_t w[4];
-#pragma unroll
-            for (int h = 0; h < 4; ++h)
-              w[h] = f32_to_bf16_rne(v[8 * q + 2 * h]) | (f32_to_bf16_rne(v[8 * q + 2 * h + 1]) << 16);
-            o[q] = make_uint4(w[0], w[1], w[2], w[3]);
+        for (int i = 0; i < 8; ++i) v[i] = acc[t][2 * q + i / 4][i % 4] * sc;
+        const int c0 = 32 * q + 8 * G;
+        if (a.vec_store && c0 + 8 <= s.d) {
+          if (a.out_bf16) {
+            uint4* o = reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + row * a.ldo + c0);
+            *o = make_uint4(pack_bf16_rne(v[0], v[1]), pack_bf16_rne(v[2], v[3]),
+                            pack_bf16_rne(v[4], v[5]), pack_bf16_rne(v[6], v[7]));
+          } else {
+            float4* o = reinterpret_cast<float4*>(static_cast<float*>(a.out) + row * a.ldo + c0);
+            o[0] = make_float4(v[0], v[1], v[2], v[3]);
+            o[1] = make_float4(v[4], v[5], v[6], v[7]);
           }
         } else {
-          float4* o = reinterpret_cast<float4*>(static_cast<float*>(a.out) + row * a.ldo + c0);
 #pragma unroll
-          for (int q = 0; q < Q / 4; ++q)
-            o[q] = make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < Q; ++e) {
-          const int i = c0 + e;
-          if (i >= s.d) continue;
-          const int64_t at = row * a.ldo + (s.chan ? s.chan[i] : i);
-          if (a.out_bf16)
-            static_cast<uint16_t*>(a.out)[at] = (uint16_t)f32_to_bf16_rne(v[e]);
-          else
-            static_cast<float*>(a.out)[at] = v[e];
+          for (int e = 0; e < 8; ++e) {
+            const int i = c0 + e;
+            if (i >= s.d) continue;
+            const int64_t at = row * a.ldo + (s.chan ? s.chan[i] : i);
+            if (a.out_bf16)
+              static_cast<uint16_t*>(a.out)[at] = (uint16_t)pack_bf16_rne(v[e], 0.f);
+            else
+              static_cast<float*>(a.out)[at] = v[e];
+          }
         }
       }
     }
@@ -2654,9 +2648,9 @@ int launch_score_topk(const PlanDev& p, const void* q, int dt, int64_t nq_per_gr
 template <int D>
 static int launch_dequant_mfma_d(const DequantArgs& da, hipStream_t st) {
   const int64_t iters = (da.n + 31) / 32;
-  int64_t blocks = (iters + kEncWaves - 1) / kEncWaves;
-  if (blocks > 2048) blocks = 2048;
-  const dim3 grid((unsigned)blocks), block(kEncWaves * kWave);
+  int64_t blocks = (iters + kDqWaves - 1) / kDqWaves;
+  if (blocks > 4096) blocks = 4096;
+  const dim3 grid((unsigned)blocks), block(kDqWaves * kWave);
   switch (da.s.R) {
     case 1: hipLaunchKernelGGL((dequant_mfma_kernel<D, 1>), grid, block, 0, st, da); break;
     case 2: hipLaunchKernelGGL((dequant_mfma_kernel<D, 2>), grid, block, 0, st, da); break;
@@ -2698,7 +2692,6 @@ int launch_dequantize(const PlanDev& p, const uint8_t* codes, int64_t n, void* o
     da.ldo = ldo;
     da.out_bf16 = dt == TQ_BF16;
     da.vec_store = da.s.chan == nullptr && (uintptr_t)out % 16 == 0 && (ldo * es) % 16 == 0;
-    da.zero = 0;
     int rc;
     if (da.s.rotkt16 != nullptr && da.s.D <= 128) {
       switch (da.s.D) {

@@ -95,6 +95,14 @@ int permuted_row(int D, int tile, int row_in_tile) {
   return (row_in_tile / 4) * (D / 4) + 4 * tile + row_in_tile % 4;
 }
 
+// Output rows of the dequantization table (K^T): lane group G = row/4 of tile jt, element
+// e = row%4, receives input coordinate 32 (jt/2) + 8 G + 4 (jt%2) + e, so that every 32
+// consecutive coordinates are split over the four lane groups, 8 each: one store instruction
+// then writes 4 x 8 adjacent coordinates of a vector.
+int dequant_row(int tile, int row_in_tile) {
+  return 32 * (tile / 2) + 8 * (row_in_tile / 4) + 4 * (tile % 2) + row_in_tile % 4;
+}
+
 // fp16 bit pattern of an integer with |v| <= 2048 (exact).
 uint16_t fp16_bits_of_small_int(int64_t v) {
   if (v == 0) return 0;
@@ -132,8 +140,9 @@ void mfma_operand_tables(SubHost& h) {
           h.rotk[(size_t)NJT * NKS * 64 * 8 + at] = lo;
           if (!h.rotk16.empty()) {
             h.rotk16[at] = fp16_bits_of_small_int(K[(size_t)row * D + 32 * ks + 8 * G + e]);
-            // K^T: output (input-domain) coordinate `row`, rotated coordinate as the k index
-            h.rotkt16[at] = fp16_bits_of_small_int(K[(size_t)(32 * ks + 8 * G + e) * D + row]);
+            // K^T: output (input-domain) coordinate, rotated coordinate as the k index
+            const int orow = dequant_row(jt, l % 16);
+            h.rotkt16[at] = fp16_bits_of_small_int(K[(size_t)(32 * ks + 8 * G + e) * D + orow]);
           }
           const int col = G * (D / 4) + 8 * ks + e;
           if (!h.S.empty()) h.sperm[at] = h.S[(size_t)row * D + col];

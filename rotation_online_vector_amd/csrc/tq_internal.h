@@ -42,7 +42,8 @@ struct SubDev {
   const uint16_t* rotk;   // [2 limbs][D/16 row tiles][D/32 k steps][64][8]: D^(3/2) Pi
   const uint16_t* rotk16; // [D/16][D/32][64][8]: the same in one exact fp16 limb, or null
   const uint16_t* rotkt16; // [D/16][D/32][64][8]: K^T likewise (rows = input coordinates,
-                           // permuted as above; k = rotated coordinate), with rotk16
+                           // lane group G of tile jt, element e: 32 (jt/2) + 8 G + 4 (jt%2) + e;
+                           // k = rotated coordinate), with rotk16
   const uint16_t* sperm;  // [D/16][D/32][64][8]: S with columns in the residual register order
 };
 
