@@ -21,7 +21,7 @@ dive, blog.hotdry.top):
      makes the estimate unbiased (overview §1.2.3): for a Gaussian row s,
      E[sign(<s, r>) <s, y'>] = sqrt(2/pi) <r, y'> / ||r||.
   7. top-k by estimate, ties broken by the smaller key index (overview §4.2.2,
-     first retrieval stage).
+     first retrieval stage); the second stage re-scores the candidates exactly.
 
 With an outlier mask (overview §4.1.1: a share of outlier channels kept at a
 higher bit-width) the channels split into two independent sub-plans, each
@@ -209,6 +209,27 @@ def encode_split(sp, X):
 def score_split(sp, codes_list, Y):
     Y = np.asarray(Y)
     return sum(score(p, c, Y[..., ch]) for p, c, ch in zip(sp.plans, codes_list, sp.channels))
+
+
+def rerank(Y, X, cand, k):
+    """Second stage of two-stage retrieval (overview §4.2.2: the quantized first stage screens
+    a top-K, the second refines on the candidate set): for each query row y of Y, the exact
+    inner products <y, x_j> with the full-precision rows x_j of X for j in cand[q] (ids
+    outside [0, n) are ignored), and the k best of them ordered by (-value, id).  Returns
+    (ids, values); slots past the valid candidates hold id -1 and value -inf."""
+    Y = np.asarray(Y, dtype=np.float64)
+    X = np.asarray(X, dtype=np.float64)
+    cand = np.asarray(cand)
+    n = X.shape[0]
+    ids = np.full((Y.shape[0], k), -1, dtype=np.int64)
+    vals = np.full((Y.shape[0], k), -np.inf)
+    for q in range(Y.shape[0]):
+        c = np.unique(cand[q][(cand[q] >= 0) & (cand[q] < n)])
+        v = X[c] @ Y[q]
+        order = np.lexsort((c, -v))[:k]
+        ids[q, :len(order)] = c[order]
+        vals[q, :len(order)] = v[order]
+    return ids, vals
 
 
 def topk(est, k):

@@ -474,3 +474,30 @@ def test_layout_mse_bit_positions_by_hand():
     assert list(rec[0, 24:].view("<f4")) == [1.5]
     u = layout.unpack_mse(rec, D, R)
     assert np.array_equal(u["idx"], idx) and u["norm"][0] == 1.5
+
+
+# ---------------------------------------------------------------- two-stage retrieval
+
+def test_rerank_is_exact_top_k_when_candidates_cover_it():
+    """With every key a candidate, the second stage is the exact top-k by brute force; with
+    a candidate set that holds the true top-k plus distractors, it returns the true top-k;
+    duplicate and out-of-range candidates are ignored; ties go to the smaller id."""
+    rng = np.random.default_rng(12)
+    X = rng.standard_normal((300, 24))
+    Y = rng.standard_normal((5, 24))
+    exact = Y @ X.T
+    k = 7
+    ids, vals = tq.rerank(Y, X, np.tile(np.arange(300), (5, 1)), k)
+    for q in range(5):
+        order = sorted(range(300), key=lambda j: (-exact[q, j], j))[:k]
+        assert ids[q].tolist() == order
+        assert np.allclose(vals[q], exact[q, order], rtol=0, atol=1e-12)
+    cand = np.concatenate([ids, rng.integers(0, 300, (5, 20)), ids[:, :2], np.full((5, 3), 999),
+                           np.full((5, 1), -4)], axis=1)
+    ids2, _ = tq.rerank(Y, X, cand, k)
+    assert np.array_equal(ids2, ids)
+    Xt = np.ones((4, 3))                       # four equal inner products
+    ids3, vals3 = tq.rerank(np.ones((1, 3)), Xt, np.array([[3, 1, 2, 0]]), 2)
+    assert ids3.tolist() == [[0, 1]] and vals3.tolist() == [[3.0, 3.0]]
+    ids4, vals4 = tq.rerank(np.ones((1, 3)), Xt, np.array([[2, 2, 9]]), 3)
+    assert ids4.tolist() == [[2, -1, -1]] and vals4[0, 1] == -np.inf
