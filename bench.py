@@ -9,10 +9,12 @@ the streaming estimator).  Inputs are resident in HBM before timing starts.
                     [--copy-calibration MIB] [--workload NAME]
 
 `--workload` selects one of the other synthetic shapes (kv, split35, split25,
-retrieval, small, mse); their step is encode + score (+ top-k for `small`; one
-fused score + top-k call for `retrieval`, whose roofline is the MFMA one; for
-`mse`, TurboQuant-MSE encode + dequantize of the long-context keys, counted in
-vectors/s) and the line carries the same fields, without the CPU leg.
+retrieval, retrieval2, small, mse); their step is encode + score (+ top-k for
+`small`; one fused score + top-k call for `retrieval`, whose roofline is the
+MFMA one; `retrieval2` adds the exact re-rank of a quantized top-64; for `mse`,
+TurboQuant-MSE encode + dequantize of the long-context keys, counted in
+vectors/s) and the line carries the same fields, without the CPU leg; the two
+retrieval lines also report recall@10 against an exact fp32 search.
 
 Prints one JSON line.  `value` is scores per second over whole steps; the
 per-kernel rates, the roofline of the dominant kernel (algorithmic bytes per
@@ -40,7 +42,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-groups", type=int, default=16)
     ap.add_argument("--workload", default="longctx",
-                    choices=["longctx", "kv", "split35", "split25", "retrieval", "small", "mse"],
+                    choices=["longctx", "kv", "split35", "split25", "retrieval", "retrieval2",
+                             "small", "mse"],
                     help="long-context decode (default, the headline line); the other shapes "
                          "report the same fields for their own step (no CPU leg)")
     ap.add_argument("--no-hbm-ceiling", action="store_true",
@@ -232,8 +235,8 @@ def build_workload(name, dev, W_all):
             bytes={"tq_encode": n_keys * d * 2 + n_keys * rb,
                    "tq_score": n_keys * rb + n_scores * 4 + n_kv * G * d * 2},
             n_keys=n_keys, n_scores=n_scores, keep=(plans, keys, queries, codes, scores))
-    if name in ("retrieval", "small"):
-        if name == "retrieval":
+    if name in ("retrieval", "retrieval2", "small"):
+        if name != "small":
             keys, queries = workloads.retrieval_inputs(dev, n_keys=W["n_keys"],
                                                        n_queries=W["n_queries"], d=W["d"],
                                                        seed=W["seed"])
@@ -252,6 +255,34 @@ def build_workload(name, dev, W_all):
                   "record_bytes": rb}
         enc = ("tq_encode", lambda: tq.tq_encode(plan, keys, codes))
         enc_bytes = n * d * 4 + n * rb
+        def recall_at_k(ids_fn, sample=64):
+            """recall@k of the step's ids against an exact fp32 search, on the first
+            `sample` queries (measured after the timed steps)."""
+            def run():
+                got = ids_fn()[:sample].cpu().numpy()
+                exact = torch.topk(queries[:sample] @ keys.T, k, dim=1).indices.cpu().numpy()
+                r = float(np.mean([len(set(exact[q]) & set(got[q].tolist())) / k
+                                   for q in range(len(got))]))
+                return {"recall_at_%d" % k: round(r, 4), "queries_sampled": len(got),
+                        "against": "exact fp32 inner products over all keys"}
+            return run
+        import numpy as np
+        if name == "retrieval2":
+            # two-stage retrieval: quantized top-64, then the exact top-k of those 64
+            kc = 64
+            cand = torch.empty((nq, kc), dtype=torch.int64, device=dev)
+            cvals = torch.empty((nq, kc), dtype=torch.float32, device=dev)
+            return dict(
+                config=dict(config, candidates=kc),
+                phases=[enc, ("tq_score_topk",
+                              lambda: tq.tq_score_topk(plan, queries, codes, n, kc, ids=cand, vals=cvals)),
+                        ("tq_rerank", lambda: tq.tq_rerank(queries, keys, cand, k, ids=ids, vals=vals))],
+                bytes={"tq_encode": enc_bytes, "tq_score_topk": n * rb + nq * d * 4 + nq * kc * 12,
+                       "tq_rerank": nq * kc * (8 + d * 4) + nq * d * 4 + nq * k * 12},
+                flops={"tq_encode": 2.0 * D * D * n, "tq_score_topk": 2.0 * (2 * D) * n * nq,
+                       "tq_rerank": 2.0 * d * kc * nq},
+                quality=recall_at_k(lambda: ids),
+                n_keys=n, n_scores=n * nq, keep=(plan, keys, queries, codes, ids, vals, cand, cvals))
         if name == "retrieval":
             # score and select in one call: the score matrix is never stored
             return dict(
@@ -262,6 +293,7 @@ def build_workload(name, dev, W_all):
                 # MFMA work: the sign projection (2 k D per key, k = D) and the bit-sliced
                 # scorer's contraction of every key with every query (2 (D + k) per score)
                 flops={"tq_encode": 2.0 * D * D * n, "tq_score_topk": 2.0 * (2 * D) * n * nq},
+                quality=recall_at_k(lambda: ids),
                 n_keys=n, n_scores=n * nq, keep=(plan, keys, queries, codes, ids, vals))
         scores = torch.empty((nq, n), dtype=torch.float32, device=dev)
         return dict(
@@ -286,7 +318,8 @@ def main():
 
     W_all = {"longctx": workloads.LONGCTX, "kv": workloads.KV, "split35": workloads.SPLIT,
              "split25": workloads.SPLIT_25, "retrieval": workloads.RETRIEVAL,
-             "small": workloads.SMALL, "mse": workloads.MSE_LONGCTX}
+             "small": workloads.SMALL, "mse": workloads.MSE_LONGCTX,
+             "retrieval2": dict(workloads.RETRIEVAL, name=workloads.RETRIEVAL["name"] + "-2stage")}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = build_workload(args.workload, dev, W_all)
@@ -381,6 +414,8 @@ def main():
         "roofline": roof,
         "hbm_ceiling": ceiling,
     }
+    if "quality" in wl:
+        out["quality"] = wl["quality"]()
     if args.workload == "longctx" and not args.no_cpu_baseline:
         W = W_all["longctx"]
         keys, queries = wl["keep"][1], wl["keep"][2]

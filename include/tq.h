@@ -208,6 +208,25 @@ tq_status tq_dequantize(const tq_plan* plan, const void* codes, int64_t n, void*
                         int64_t ldx, void* stream);
 
 /*
+ * Second stage of two-stage retrieval (overview §4.2.2: the quantized first
+ * stage screens a top-K, the second refines on the candidates): for each of nq
+ * queries, the exact inner products with the full-precision vectors of its kc
+ * candidates (fp32 accumulation), and the k best ordered by (-value, id).  No
+ * plan is involved.
+ *   q     device, nq rows of d elements (qdt), row stride ldq elements
+ *   x     device, n rows of d elements (xdt), row stride ldx elements
+ *   cand  device int64 [nq][kc]: candidate row ids (e.g. from tq_score_topk);
+ *         ids outside [0, n) are skipped and repeated ids count once
+ *   ids   device int64 [nq][k], vals device float32 [nq][k]; slots past the
+ *         valid candidates get id -1 and value -inf
+ * Limits: 1 <= d <= 8192, 1 <= k <= kc <= 256.
+ * Errors: TQ_EINVAL (range, null, misalignment), TQ_EDEVICE.
+ */
+tq_status tq_rerank(const void* q, tq_dtype qdt, int64_t nq, int64_t ldq, const void* x,
+                    tq_dtype xdt, int64_t n, int64_t ldx, int d, const int64_t* cand, int kc, int k,
+                    int64_t* ids, float* vals, void* stream);
+
+/*
  * The QJL stage alone (overview §2.3.2): beta_j = [ (S r)_j >= 0 ] for n
  * residual vectors r already in the rotated domain of sub-plan `subplan`.
  *   r     device float32 [n][D]

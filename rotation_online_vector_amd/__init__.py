@@ -38,7 +38,7 @@ class tq_plan_desc(ctypes.Structure):
 
 EXPORTED = ["tq_status_string", "tq_plan_create", "tq_plan_destroy", "tq_plan_info",
             "tq_plan_create_mse", "tq_encode", "tq_score", "tq_score_topk", "tq_topk",
-            "tq_dequantize", "tq_qjl", "tq_codebook",
+            "tq_dequantize", "tq_rerank", "tq_qjl", "tq_codebook",
             "tq_rotation_signs", "tq_qjl_matrix"]
 
 _lib = None
@@ -75,6 +75,8 @@ def load_library(path=LIB_PATH):
     lib.tq_plan_create_mse.argtypes = [i32, i32, u64, ctypes.POINTER(vp)]
     lib.tq_plan_create_mse.restype = i32
     lib.tq_dequantize.argtypes = [vp, vp, i64, vp, i32, i64, vp]
+    lib.tq_rerank.argtypes = [vp, i32, i64, i64, vp, i32, i64, i64, i32, vp, i32, i32, vp, vp, vp]
+    lib.tq_rerank.restype = i32
     lib.tq_dequantize.restype = i32
     lib.tq_score_topk.argtypes = [vp, vp, i32, i64, i64, i64, vp, i64, i32, vp, vp, vp]
     lib.tq_score_topk.restype = i32
@@ -279,6 +281,26 @@ def tq_dequantize(plan, codes, n, x=None, dtype=None, stream=None):
         plan.handle, ctypes.c_void_p(codes.data_ptr()), n, ctypes.c_void_p(x.data_ptr()),
         _dtype_code(x), ld, _stream(stream)))
     return x
+
+
+def tq_rerank(q, x, cand, k, ids=None, vals=None, stream=None):
+    """Exact top-k of each query row over its candidate rows of x (cand: int64 [nq, kc])."""
+    import torch
+    d = q.shape[-1]
+    nq, ldq = _rows(q, d)
+    n, ldx = _rows(x, d)
+    if cand.dtype != torch.int64 or not cand.is_contiguous() or cand.dim() != 2 or cand.shape[0] != nq:
+        raise ValueError("cand must be contiguous int64 [nq, kc]")
+    if ids is None:
+        ids = torch.empty((nq, k), dtype=torch.int64, device=q.device)
+    if vals is None:
+        vals = torch.empty((nq, k), dtype=torch.float32, device=q.device)
+    _check("tq_rerank", load_library().tq_rerank(
+        ctypes.c_void_p(q.data_ptr()), _dtype_code(q), nq, ldq, ctypes.c_void_p(x.data_ptr()),
+        _dtype_code(x), n, ldx, int(d), ctypes.c_void_p(cand.data_ptr()), int(cand.shape[1]),
+        int(k), ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(vals.data_ptr()),
+        _stream(stream)))
+    return ids, vals
 
 
 def tq_qjl(plan, subplan, r, beta=None, stream=None):

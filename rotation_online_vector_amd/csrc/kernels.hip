@@ -2251,6 +2251,115 @@ __global__ void __launch_bounds__(kBlock) topk_merge_kernel(const float* cv, con
   topk_emit<KMAX>(lv, li, k, ids + row * k, vals + row * k);
 }
 
+// ============================================================================ re-rank
+// Second stage of two-stage retrieval (technical overview §4.2.2): exact inner products of
+// each query with its candidates' full-precision vectors, and the k best by (-value, id).
+// One workgroup per query: the query in LDS as fp32; each wave scores candidates (lanes
+// stride over the coordinates, so a wave reads 64 consecutive elements of a row at a time,
+// then a wave-wide sum); wave 0 takes k rounds of wave arg-max, dropping every copy of each
+// winner, so a candidate listed twice counts once.  Ids outside [0, n) are skipped; slots
+// past the valid candidates get id -1 and value -inf.
+constexpr int kRerankMaxD = 8192, kRerankMaxC = 256;
+
+struct RerankArgs {
+  const void* q;
+  int64_t ldq;
+  int q_bf16;
+  const void* x;
+  int64_t ldx;
+  int x_bf16;
+  int64_t n;
+  int d;
+  const int64_t* cand;
+  int kc;
+  int k;
+  int64_t* ids;
+  float* vals;
+};
+
+__device__ __forceinline__ bool better_id64(float v, int64_t i, float w, int64_t j) {
+  return v > w || (v == w && i < j);
+}
+
+__global__ void __launch_bounds__(kBlock) rerank_kernel(RerankArgs a) {
+  __shared__ float qs[kRerankMaxD];
+  __shared__ float cv[kRerankMaxC];
+  __shared__ int64_t cid[kRerankMaxC];
+  const int64_t qi = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int c = threadIdx.x; c < a.d; c += kBlock)
+    qs[c] = a.q_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(a.q)[qi * a.ldq + c])
+                     : static_cast<const float*>(a.q)[qi * a.ldq + c];
+  __syncthreads();
+  for (int j = wave; j < a.kc; j += kBlock / kWave) {
+    const int64_t id = a.cand[qi * a.kc + j];
+    const bool ok = id >= 0 && id < a.n;
+    float acc = 0.f;
+    if (ok) {
+      if (a.x_bf16) {
+        const uint16_t* xr = static_cast<const uint16_t*>(a.x) + id * a.ldx;
+        for (int c = lane; c < a.d; c += kWave) acc = fmaf(qs[c], bf16_bits_to_f32(xr[c]), acc);
+      } else {
+        const float* xr = static_cast<const float*>(a.x) + id * a.ldx;
+        for (int c = lane; c < a.d; c += kWave) acc = fmaf(qs[c], xr[c], acc);
+      }
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) acc += __shfl_xor(acc, m);
+    if (lane == 0) {
+      cv[j] = ok ? acc : -INFINITY;
+      cid[j] = ok ? id : INT64_MAX;
+    }
+  }
+  __syncthreads();
+  if (wave != 0) return;
+  constexpr int P = kRerankMaxC / kWave;
+  float v[P];
+  int64_t id[P];
+#pragma unroll
+  for (int s2 = 0; s2 < P; ++s2) {
+    const int j = lane + kWave * s2;
+    v[s2] = j < a.kc ? cv[j] : -INFINITY;
+    id[s2] = j < a.kc ? cid[j] : INT64_MAX;
+  }
+  for (int r = 0; r < a.k; ++r) {
+    float bv = v[0];
+    int64_t bi = id[0];
+#pragma unroll
+    for (int s2 = 1; s2 < P; ++s2)
+      if (better_id64(v[s2], id[s2], bv, bi)) { bv = v[s2]; bi = id[s2]; }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(bv, m);
+      const int64_t oi = (int64_t)(((uint64_t)(uint32_t)__shfl_xor((int)(uint32_t)((uint64_t)bi >> 32), m) << 32) |
+                                   (uint32_t)__shfl_xor((int)(uint32_t)bi, m));
+      if (better_id64(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    const bool valid = bi != INT64_MAX;
+    if (lane == 0) {
+      a.ids[qi * a.k + r] = valid ? bi : -1;
+      a.vals[qi * a.k + r] = valid ? bv : -INFINITY;
+    }
+    if (valid) {
+#pragma unroll
+      for (int s2 = 0; s2 < P; ++s2)
+        if (id[s2] == bi) { v[s2] = -INFINITY; id[s2] = INT64_MAX; }
+    }
+  }
+}
+
+int launch_rerank(const void* q, int q_bf16, int64_t nq, int64_t ldq, const void* x, int x_bf16,
+                  int64_t n, int64_t ldx, int d, const int64_t* cand, int kc, int k, int64_t* ids,
+                  float* vals, void* stream) {
+  if (nq == 0) return 0;
+  RerankArgs ra;
+  ra.q = q; ra.ldq = ldq; ra.q_bf16 = q_bf16;
+  ra.x = x; ra.ldx = ldx; ra.x_bf16 = x_bf16; ra.n = n; ra.d = d;
+  ra.cand = cand; ra.kc = kc; ra.k = k; ra.ids = ids; ra.vals = vals;
+  hipLaunchKernelGGL(rerank_kernel, dim3((unsigned)nq), dim3(kBlock), 0, (hipStream_t)stream, ra);
+  return (int)hipGetLastError();
+}
+
 // ============================================================================ launchers
 
 static inline int hip_rc(hipError_t e) { return e == hipSuccess ? 0 : (int)e; }

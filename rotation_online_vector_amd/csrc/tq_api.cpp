@@ -478,6 +478,23 @@ tq_status tq_dequantize(const tq_plan* plan, const void* codes, int64_t n, void*
                                     ldx, stream));
 }
 
+tq_status tq_rerank(const void* q, tq_dtype qdt, int64_t nq, int64_t ldq, const void* x,
+                    tq_dtype xdt, int64_t n, int64_t ldx, int d, const int64_t* cand, int kc, int k,
+                    int64_t* ids, float* vals, void* stream) {
+  if (nq < 0 || n < 0 || d < 1 || d > 8192 || kc < 1 || kc > 256 || k < 1 || k > kc ||
+      (qdt != TQ_F32 && qdt != TQ_BF16) || (xdt != TQ_F32 && xdt != TQ_BF16))
+    return TQ_EINVAL;
+  if (nq == 0) return TQ_OK;
+  const int qs = qdt == TQ_BF16 ? 2 : 4, xs = xdt == TQ_BF16 ? 2 : 4;
+  if (!q || !cand || !ids || !vals || (n > 0 && !x) || ldq < d || ldx < d || (uintptr_t)q % qs ||
+      (uintptr_t)x % xs || (uintptr_t)cand % 8 || (uintptr_t)ids % 8 || (uintptr_t)vals % 4)
+    return TQ_EINVAL;
+  int dev;
+  if (hipGetDevice(&dev) != hipSuccess) return TQ_EDEVICE;
+  return from_hip(launch_rerank(q, qdt == TQ_BF16, nq, ldq, x, xdt == TQ_BF16, n, ldx, d, cand,
+                                kc, k, ids, vals, stream));
+}
+
 tq_status tq_qjl(const tq_plan* plan, int subplan, const float* r, int64_t n, uint32_t* beta,
                  void* stream) {
   if (!plan || subplan < 0 || subplan >= plan->dev.nsub || n < 0) return TQ_EINVAL;
