@@ -211,6 +211,26 @@ def score_split(sp, codes_list, Y):
     return sum(score(p, c, Y[..., ch]) for p, c, ch in zip(sp.plans, codes_list, sp.channels))
 
 
+def attend(vplan, logits, vcodes, scale, nq_per_group):
+    """Decode attention over quantized values (overview §4.1.2: the cache is dequantized in
+    one batch for the attention step; the attention arithmetic itself is the model's, taken
+    here in its plain form): for query row r of group g = r // nq_per_group,
+        p = softmax(scale * logits[r]) over the group's n tokens,
+        out[r] = sum_j p_j vhat_j,
+    with vhat the dequantized value vectors of group g (vcodes holds n_groups * n records,
+    group after group).  Returns (rows, d) fp64."""
+    logits = np.asarray(logits, dtype=np.float64)
+    rows, n = logits.shape
+    V = dequantize(vplan, vcodes)
+    out = np.zeros((rows, V.shape[1]))
+    for r in range(rows):
+        g = r // nq_per_group
+        l = scale * logits[r]
+        e = np.exp(l - l.max())
+        out[r] = (e / e.sum()) @ V[g * n:(g + 1) * n]
+    return out
+
+
 def rerank(Y, X, cand, k):
     """Second stage of two-stage retrieval (overview §4.2.2: the quantized first stage screens
     a top-K, the second refines on the candidate set): for each query row y of Y, the exact

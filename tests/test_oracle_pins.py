@@ -501,3 +501,48 @@ def test_rerank_is_exact_top_k_when_candidates_cover_it():
     assert ids3.tolist() == [[0, 1]] and vals3.tolist() == [[3.0, 3.0]]
     ids4, vals4 = tq.rerank(np.ones((1, 3)), Xt, np.array([[2, 2, 9]]), 3)
     assert ids4.tolist() == [[2, -1, -1]] and vals4[0, 1] == -np.inf
+
+
+# ---------------------------------------------------------------- decode attention over quantized values
+
+def _values(n, d=64, bits=3, seed=0):
+    plan = tq.make_mse_plan(d, bits, seed)
+    V = np.random.default_rng(seed + 1).standard_normal((n, d))
+    c = tq.encode_mse(plan, V)
+    return plan, c, tq.dequantize(plan, c)
+
+
+def test_attend_closed_forms():
+    """One token: its value.  Equal logits (or scale 0): the mean of the values.  A logit far
+    above the rest: that token's value.  Two groups read their own values."""
+    plan, c, Vh = _values(1)
+    assert np.allclose(tq.attend(plan, np.array([[3.7]]), c, 0.5, 1), Vh, atol=1e-15)
+    plan, c, Vh = _values(40)
+    out = tq.attend(plan, np.full((2, 40), 1.25), c, 1.0, 2)
+    assert np.allclose(out, np.tile(Vh.mean(0), (2, 1)), atol=1e-14)
+    out0 = tq.attend(plan, np.random.default_rng(3).standard_normal((1, 40)), c, 0.0, 1)
+    assert np.allclose(out0[0], Vh.mean(0), atol=1e-14)
+    l = np.zeros((1, 40))
+    l[0, 17] = 1000.0
+    assert np.allclose(tq.attend(plan, l, c, 1.0, 1)[0], Vh[17], atol=1e-12)
+    # two groups of 20 tokens, one query row each: row r reads group r's tokens only
+    l2 = np.zeros((2, 20))
+    l2[0, 3] = l2[1, 5] = 1000.0
+    out2 = tq.attend(plan, l2, c, 1.0, 1)
+    assert np.allclose(out2[0], Vh[3], atol=1e-12) and np.allclose(out2[1], Vh[20 + 5], atol=1e-12)
+
+
+def test_attend_invariances():
+    """Softmax ignores a constant shift of a row's logits; permuting tokens together with
+    their values leaves the output unchanged."""
+    plan, c, Vh = _values(50, d=128, bits=2, seed=4)
+    rng = np.random.default_rng(8)
+    L = rng.standard_normal((3, 50)) * 4
+    out = tq.attend(plan, L, c, 0.7, 3)
+    assert np.allclose(tq.attend(plan, L + 123.0, c, 0.7, 3), out, atol=1e-12)
+    perm = rng.permutation(50)
+    cp = {k: v[perm] for k, v in c.items()}
+    assert np.allclose(tq.attend(plan, L[:, perm], cp, 0.7, 3), out, atol=1e-12)
+    # the plain definition: softmax weights times the dequantized rows
+    w = np.exp(0.7 * L[1] - (0.7 * L[1]).max())
+    assert np.allclose(out[1], (w / w.sum()) @ Vh, atol=1e-12)
