@@ -13,8 +13,10 @@ retrieval, retrieval2, small, mse); their step is encode + score (+ top-k for
 `small`; one fused score + top-k call for `retrieval`, whose roofline is the
 MFMA one; `retrieval2` adds the exact re-rank of a quantized top-64; for `mse`,
 TurboQuant-MSE encode + dequantize of the long-context keys, counted in
-vectors/s) and the line carries the same fields, without the CPU leg; the two
-retrieval lines also report recall@10 against an exact fp32 search.
+vectors/s; `attend` is one decode step over the long-context cache held
+quantized, keys scored and values attended, counted in (query, token) pairs/s)
+and the line carries the same fields, without the CPU leg; the two retrieval
+lines also report recall@10 against an exact fp32 search.
 
 Prints one JSON line.  `value` is scores per second over whole steps; the
 per-kernel rates, the roofline of the dominant kernel (algorithmic bytes per
@@ -23,6 +25,7 @@ timed on a bounded sample of the same workload ride along.
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -43,7 +46,7 @@ def parse():
     ap.add_argument("--cpu-sample-groups", type=int, default=16)
     ap.add_argument("--workload", default="longctx",
                     choices=["longctx", "kv", "split35", "split25", "retrieval", "retrieval2",
-                             "small", "mse"],
+                             "small", "mse", "attend"],
                     help="long-context decode (default, the headline line); the other shapes "
                          "report the same fields for their own step (no CPU leg)")
     ap.add_argument("--no-hbm-ceiling", action="store_true",
@@ -180,6 +183,41 @@ def build_workload(name, dev, W_all):
             value=(n_keys, "vectors/s",
                    "TurboQuant-MSE encode + dequantize vectors/sec (d=128, 3-bit)"),
             keep=(plan, keys, codes, xh))
+    if name == "attend":
+        keys, queries, _ = workloads.longctx_inputs(dev)
+        vals, _, _ = workloads.longctx_inputs(dev, seed=W["v_seed"])
+        n_seq, n_kv, n_tok, d, G = W["n_seq"], W["n_kv"], W["n_tok"], W["d"], W["group"]
+        n_keys, n_groups = n_seq * n_kv * n_tok, n_seq * n_kv
+        kplan = tq.tq_plan_create(d, W["bits"], W["seed"])
+        vplan = tq.tq_plan_create_mse(d, W["v_bits"], W["v_seed"])
+        kcodes = tq.tq_encode(kplan, keys.view(n_keys, d))
+        vcodes = tq.tq_encode(vplan, vals.view(n_keys, d))
+        del keys, vals
+        rows = n_groups * G
+        logits = torch.empty((rows, n_tok), dtype=torch.float32, device=dev)
+        out = torch.empty((rows, d), dtype=torch.bfloat16, device=dev)
+        qv = queries.view(rows, d)
+        n_scores = rows * n_tok
+        krb, vrb = kplan.record_bytes, vplan.record_bytes
+        return dict(
+            config={"workload": W["name"], "n_seq": n_seq, "kv_heads": n_kv, "tokens": n_tok,
+                    "d": d, "k_bits": W["bits"], "v_bits": W["v_bits"], "v_mode": "mse",
+                    "query_heads_per_seq": n_kv * G, "gqa_group": G, "keys_per_step": n_keys,
+                    "scores_per_step": n_scores, "record_bytes": krb + vrb,
+                    "k_record_bytes": krb, "v_record_bytes": vrb,
+                    "cache": "encoded before the timed steps (a decode step reads it)"},
+            phases=[("tq_score", lambda: tq.tq_score(kplan, qv, kcodes, n=n_tok, nq_per_group=G,
+                                                     n_groups=n_groups, scores=logits)),
+                    ("tq_attend", lambda: tq.tq_attend(vplan, logits, vcodes, n_tok,
+                                                       1.0 / math.sqrt(d), nq_per_group=G,
+                                                       n_groups=n_groups, out=out))],
+            bytes={"tq_score": n_keys * krb + n_scores * 4 + rows * d * 2,
+                   "tq_attend": n_keys * vrb + n_scores * 4 + rows * d * 2},
+            n_keys=n_keys, n_scores=n_scores,
+            value=(n_scores, "pairs/s",
+                   "decode attention over a quantized KV cache: (query, token) pairs/sec "
+                   "(d=128, 3-bit keys scored, 3-bit MSE values attended)"),
+            keep=(kplan, vplan, queries, kcodes, vcodes, logits, out))
     if name == "kv":
         keys, queries, _ = workloads.kv_inputs(dev, n_kv=W["n_kv"], n_tok=W["n_tok"], d=W["d"],
                                                group=W["group"], n_outlier=W["n_outlier"],
@@ -319,6 +357,7 @@ def main():
     W_all = {"longctx": workloads.LONGCTX, "kv": workloads.KV, "split35": workloads.SPLIT,
              "split25": workloads.SPLIT_25, "retrieval": workloads.RETRIEVAL,
              "small": workloads.SMALL, "mse": workloads.MSE_LONGCTX,
+             "attend": workloads.ATTEND_LONGCTX,
              "retrieval2": dict(workloads.RETRIEVAL, name=workloads.RETRIEVAL["name"] + "-2stage")}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -400,7 +439,8 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": wl["config"],
-        "encode_vectors_per_s": _rate(wl["n_keys"], kern["tq_encode"]["ms"]),
+        "encode_vectors_per_s": (_rate(wl["n_keys"], kern["tq_encode"]["ms"])
+                                 if "tq_encode" in kern else None),
         "score_scores_per_s": _rate(wl["n_scores"], kern[score_key]["ms"]) if score_key else None,
         "kernels": {k: dict({"ms": round(v["ms"], 4),
                              "ms_p10_p50_p90": [round(x, 4) for x in v["pct"]],

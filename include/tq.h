@@ -208,6 +208,30 @@ tq_status tq_dequantize(const tq_plan* plan, const void* codes, int64_t n, void*
                         int64_t ldx, void* stream);
 
 /*
+ * Decode attention over quantized values (overview §4.1.2: the cache is
+ * dequantized for the attention step): for query row r of group g,
+ *   out[r] = sum_j softmax(scale * logits[r])_j * vhat_j,
+ * with vhat_j the reconstruction (as tq_dequantize) of group g's record j.
+ * The weighted centroids are summed in the rotated domain and the rotation is
+ * undone once per row, so no value vector is reconstructed on its own.
+ *   vplan   the values' plan (MSE or inner-product; one sub-plan)
+ *   logits  device float32 [n_groups*nq_per_group][n], e.g. from tq_score;
+ *           finite
+ *   vcodes  device, n_groups * n records of vplan (group g from record g*n)
+ *   out     device, n_groups*nq_per_group rows of d elements (dt), stride ldo
+ * Uses a stream-ordered temporary of (D + 2) floats per row and 1024-token
+ * chunk.  Limits: n >= 1, n_groups <= 65535, nq_per_group <= 262140, scale
+ * finite.  nq_per_group = 0 or n_groups = 0 is a no-op.
+ * Errors: TQ_EINVAL (range, null, ldo < d, misalignment: logits 4-byte,
+ * vcodes 16-byte, out element-aligned), TQ_ENOMEM, TQ_EDEVICE;
+ * TQ_EUNSUPPORTED for a plan with an outlier mask or more than 4 index bits
+ * per coordinate (an MSE plan of 1..4 bits, an inner-product plan of 2..5).
+ */
+tq_status tq_attend(const tq_plan* vplan, const float* logits, int64_t nq_per_group,
+                    int64_t n_groups, int64_t n, float scale, const void* vcodes, void* out,
+                    tq_dtype dt, int64_t ldo, void* stream);
+
+/*
  * Second stage of two-stage retrieval (overview §4.2.2: the quantized first
  * stage screens a top-K, the second refines on the candidates): for each of nq
  * queries, the exact inner products with the full-precision vectors of its kc

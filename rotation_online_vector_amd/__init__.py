@@ -38,7 +38,7 @@ class tq_plan_desc(ctypes.Structure):
 
 EXPORTED = ["tq_status_string", "tq_plan_create", "tq_plan_destroy", "tq_plan_info",
             "tq_plan_create_mse", "tq_encode", "tq_score", "tq_score_topk", "tq_topk",
-            "tq_dequantize", "tq_rerank", "tq_qjl", "tq_codebook",
+            "tq_dequantize", "tq_attend", "tq_rerank", "tq_qjl", "tq_codebook",
             "tq_rotation_signs", "tq_qjl_matrix"]
 
 _lib = None
@@ -75,6 +75,8 @@ def load_library(path=LIB_PATH):
     lib.tq_plan_create_mse.argtypes = [i32, i32, u64, ctypes.POINTER(vp)]
     lib.tq_plan_create_mse.restype = i32
     lib.tq_dequantize.argtypes = [vp, vp, i64, vp, i32, i64, vp]
+    lib.tq_attend.argtypes = [vp, vp, i64, i64, i64, ctypes.c_float, vp, vp, i32, i64, vp]
+    lib.tq_attend.restype = i32
     lib.tq_rerank.argtypes = [vp, i32, i64, i64, vp, i32, i64, i64, i32, vp, i32, i32, vp, vp, vp]
     lib.tq_rerank.restype = i32
     lib.tq_dequantize.restype = i32
@@ -281,6 +283,31 @@ def tq_dequantize(plan, codes, n, x=None, dtype=None, stream=None):
         plan.handle, ctypes.c_void_p(codes.data_ptr()), n, ctypes.c_void_p(x.data_ptr()),
         _dtype_code(x), ld, _stream(stream)))
     return x
+
+
+def tq_attend(vplan, logits, vcodes, n, scale, nq_per_group=None, n_groups=1, out=None,
+              dtype=None, stream=None):
+    """softmax(scale * logits) times the dequantized values, per query row: [rows, d]."""
+    import torch
+    if logits.dtype != torch.float32 or not logits.is_contiguous() or logits.shape[-1] != n:
+        raise ValueError("logits must be contiguous float32 [rows, n]")
+    rows = logits.numel() // n
+    if nq_per_group is None:
+        nq_per_group = rows // n_groups
+    if nq_per_group * n_groups != rows:
+        raise ValueError("logit rows != nq_per_group * n_groups")
+    if vcodes.numel() < n_groups * n * vplan.record_bytes:
+        raise ValueError("codes buffer too small")
+    if out is None:
+        out = torch.empty((rows, vplan.d), dtype=dtype or torch.float32, device=logits.device)
+    r2, ldo = _rows(out, vplan.d)
+    if r2 != rows:
+        raise ValueError("output rows != logit rows")
+    _check("tq_attend", load_library().tq_attend(
+        vplan.handle, ctypes.c_void_p(logits.data_ptr()), nq_per_group, n_groups, n,
+        ctypes.c_float(float(scale)), ctypes.c_void_p(vcodes.data_ptr()),
+        ctypes.c_void_p(out.data_ptr()), _dtype_code(out), ldo, _stream(stream)))
+    return out
 
 
 def tq_rerank(q, x, cand, k, ids=None, vals=None, stream=None):

@@ -2251,6 +2251,430 @@ __global__ void __launch_bounds__(kBlock) topk_merge_kernel(const float* cv, con
   topk_emit<KMAX>(lv, li, k, ids + row * k, vals + row * k);
 }
 
+// ============================================================================ attention
+// Decode attention over quantized values: for query row r of group g,
+//   out[r] = sum_j softmax(scale * logits[r])_j vhat_j,   vhat_j = n_j Pi^T c[idx_j],
+// so out[r] = Pi^T (sum_j p_j n_j c[idx_j]): the weighted centroids are summed in the rotated
+// domain and the rotation is undone once per row (technical overview §4.1.2 dequantizes the
+// cache for the attention step; here that dequantization folds into one transform per row).
+// Pass 1, per (1024-token chunk, group, up to 8 query rows): the chunk's max of scale * logit
+// per row, the sum of exp(scale * l - max), and the partial sums y[r][i] (fp32).
+// Pass 2, per row: chunks merged with exp(m_c - M) factors (as in split-token decoding),
+// then Pi^T in LDS, the 1/sum and D^(-3/2) scale, and the first d coordinates stored.
+//
+// Pass 1 is a contraction over tokens on the matrix cores (16x16x32 fp16, fp32 accumulation):
+//   y[r][2q + p] = sum_j w[r][j] c(j, 2q + p),   w = exp(scale * l - max) n_j / max_j n_j.
+// Output row m of an MFMA tile is (parity p, weight limb, query row): the A operand holds the
+// limb of w[r][j] in the K slot (token j, parity p) and zero in the slot of the other parity,
+// so the B operand's dword for token j is exactly the pair-table entry (c of coordinate 2q in
+// the low half, 2q + 1 in the high half).  Both operands are split in two fp16 limbs (w in
+// [0, 1]; c scaled by 2^10), the four limb products are exact and summed in fp32.  The plane
+// words of a stage of tokens are held in LDS token-contiguous ([chunk][plane][token]), so one
+// 16-byte read gives a lane its 4 tokens; a lane keeps one 32-coordinate chunk across up to
+// 4 column tiles (pairs k = j LPC + col % LPC of chunk col / LPC), reusing each word read.
+constexpr int kAttnChunk = 1024;     // tokens per pass-1 workgroup
+
+struct AttnArgs {
+  SubDev s;
+  const float* logits;       // [rows][n]
+  int64_t n;
+  int64_t nq_per_group;
+  float scale;
+  const uint8_t* codes;      // group g's records from g * n
+  int rec_bytes;
+  int64_t n_chunks;
+  float* part;               // [chunk][row][D + 2]: y, then max, then sum
+  void* out;
+  int64_t ldo;
+  int out_bf16;
+};
+
+// tokens per LDS stage: the largest power of two <= 1024 whose plane words fit 32 KiB
+constexpr int attn_stage_tokens(int cmw) {
+  int t = kAttnChunk;
+  while (t > 16 && cmw * (t + 4) * 4 > 32768) t >>= 1;
+  return t;
+}
+
+template <int D, int R, int RQ>
+__global__ void __launch_bounds__(kBlock) attend_mfma_kernel(AttnArgs a) {
+  constexpr int NW = kBlock / kWave;
+  constexpr int NJT = D / 32;                       // column tiles of 16 pairs = chunks
+  constexpr int ST = NJT < 4 ? NJT : 4;             // tiles sharing a lane's chunk
+  constexpr int LPC = 16 / ST;                      // columns per chunk within those tiles
+  constexpr int TW = NJT < 16 / RQ ? NJT : 16 / RQ; // tiles per wave
+  constexpr int NTG = NJT / TW;                     // tile groups
+  static_assert(NTG <= NW && TW % ST == 0, "tile split");
+  constexpr int TSP = NW / NTG;                     // waves splitting the tokens of a tile group
+  constexpr int CMW = NJT * R;                      // staged plane words per token
+  constexpr int TS = attn_stage_tokens(CMW);
+  constexpr int SWS = TS + 4;                       // dword stride of a staged word row
+  constexpr int WLS = TS + 8;                       // fp16 stride of a staged weight row
+  constexpr int NRW = 4 * RQ;
+  constexpr int STAGE_BYTES = CMW * SWS * 4 + 2 * NRW * WLS * 2;
+  constexpr int RED_BYTES = TSP > 1 ? TSP * NRW * D * 4 : 0;
+  constexpr int RAW = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
+  constexpr int NPAIR = 1 << (2 * R);
+  __shared__ __attribute__((aligned(16))) unsigned char raw[RAW];
+  __shared__ uint2 ptab[NPAIR];
+  __shared__ float red[NW][NRW + 1];
+  __shared__ float rmax[NRW + 1];
+  uint32_t* sw = reinterpret_cast<uint32_t*>(raw);
+  uint16_t* wl = reinterpret_cast<uint16_t*>(raw + CMW * SWS * 4);
+  const SubDev& s = a.s;
+  const int W = s.mse ? R : R + 1;
+  const int rb = a.rec_bytes;
+  const int64_t chunk = blockIdx.x, grp = blockIdx.y;
+  const int64_t q0 = (int64_t)blockIdx.z * NRW;
+  const int nr = (int)((a.nq_per_group - q0) < NRW ? (a.nq_per_group - q0) : NRW);
+  const int64_t t0 = chunk * kAttnChunk;
+  const int nt = (int)((a.n - t0) < kAttnChunk ? (a.n - t0) : kAttnChunk);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint8_t* codes = a.codes + (grp * a.n + t0) * (int64_t)rb + s.rec_off;
+  const float* lg = a.logits + (grp * a.nq_per_group + q0) * a.n + t0;
+  auto norm_of = [&](int j) {
+    return __uint_as_float(reinterpret_cast<const uint32_t*>(codes + (int64_t)j * rb)[NJT * W]);
+  };
+  // pair table: entry i holds coordinate 2q's level (index bits i_0, i_2, ..) in the low
+  // fp16 half and 2q + 1's (bits i_1, i_3, ..) in the high half; .x the high limbs, .y the low
+  for (int i = tid; i < NPAIR; i += kBlock) {
+    int ia = 0, ib = 0;
+#pragma unroll
+    for (int m = 0; m < R; ++m) {
+      ia |= ((i >> (2 * m)) & 1) << m;
+      ib |= ((i >> (2 * m + 1)) & 1) << m;
+    }
+    const float ca = s.lev[ia] * kDequantLevelScale, cb = s.lev[ib] * kDequantLevelScale;
+    typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
+    const f16x2 hv = __builtin_amdgcn_cvt_pkrtz(ca, cb);
+    ptab[i] = make_uint2(__builtin_bit_cast(uint32_t, hv),
+                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
+                                                          ca - (float)hv[0], cb - (float)hv[1])));
+  }
+  // ---- the chunk's max of scale * logit per row and max norm ----
+  {
+    float mx[NRW], nm = 0.f;
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) mx[r] = -INFINITY;
+    for (int j = tid; j < nt; j += kBlock) {
+      nm = fmaxf(nm, norm_of(j));
+#pragma unroll
+      for (int r = 0; r < NRW; ++r)
+        if (r < nr) mx[r] = fmaxf(mx[r], a.scale * lg[r * a.n + j]);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      nm = fmaxf(nm, __shfl_xor(nm, m));
+#pragma unroll
+      for (int r = 0; r < NRW; ++r) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], m));
+    }
+    if (lane == 0) {
+#pragma unroll
+      for (int r = 0; r < NRW; ++r) red[wave][r] = mx[r];
+      red[wave][NRW] = nm;
+    }
+    __syncthreads();
+    if (tid <= NRW) {
+      float v = red[0][tid];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) v = fmaxf(v, red[w][tid]);
+      rmax[tid] = v;
+    }
+    __syncthreads();
+  }
+  const float nmax = rmax[NRW];
+  const float inv_nm = nmax > 0.f ? 1.f / nmax : 0.f;
+  // ---- stages: plane words and weight limbs into LDS, then the contraction ----
+  const int col = lane & 15, G = lane >> 4;
+  const int tg = wave / TSP, ts = wave % TSP;
+  const int am = lane & 15, ap = am >> 3, alimb = (am >> 2) & 1, ar = am & 3;
+  float esum[NRW];
+#pragma unroll
+  for (int r = 0; r < NRW; ++r) esum[r] = 0.f;
+  f32x4 acc[RQ][TW];
+#pragma unroll
+  for (int q = 0; q < RQ; ++q)
+#pragma unroll
+    for (int t = 0; t < TW; ++t) acc[q][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < nt; s0 += TS) {
+    const int ns = (nt - s0) < TS ? (nt - s0) : TS;
+    __syncthreads();                      // the previous stage's reads are done
+    for (int idx = tid; idx < TS * CMW; idx += kBlock) {
+      const int t = idx / CMW, cm = idx - t * CMW;
+      const int c = cm / R, m = cm - c * R;
+      uint32_t v = 0u;
+      if (t < ns) v = reinterpret_cast<const uint32_t*>(codes + (int64_t)(s0 + t) * rb)[c * W + m];
+      sw[cm * SWS + t] = v;
+    }
+    for (int t = tid; t < TS; t += kBlock) {
+      const float nw = t < ns ? norm_of(s0 + t) * inv_nm : 0.f;
+#pragma unroll
+      for (int r = 0; r < NRW; ++r) {
+        float e = 0.f;
+        if (t < ns && r < nr) e = __expf(a.scale * lg[r * a.n + s0 + t] - rmax[r]);
+        esum[r] += e;
+        const float w = e * nw;
+        typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
+        const f16x2 h = __builtin_amdgcn_cvt_pkrtz(w, 0.f);
+        const f16x2 l = __builtin_amdgcn_cvt_pkrtz(w - (float)h[0], 0.f);
+        wl[r * WLS + t] = (uint16_t)(__builtin_bit_cast(uint32_t, h) & 0xFFFFu);
+        wl[(NRW + r) * WLS + t] = (uint16_t)(__builtin_bit_cast(uint32_t, l) & 0xFFFFu);
+      }
+    }
+    __syncthreads();
+    const int nblk = (ns + 15) >> 4;
+    for (int b = ts; b < nblk; b += TSP) {
+      // A: row am = (parity, limb, row) takes its weight limb in its parity's K slots
+      f16x8 A[RQ];
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        const uint2 x = *reinterpret_cast<const uint2*>(
+            &wl[(alimb * NRW + 4 * q + ar) * WLS + b * 16 + 4 * G]);
+        const uint32_t d0 = ap ? x.x << 16 : x.x & 0xFFFFu;
+        const uint32_t d1 = ap ? x.x & 0xFFFF0000u : x.x >> 16;
+        const uint32_t d2 = ap ? x.y << 16 : x.y & 0xFFFFu;
+        const uint32_t d3 = ap ? x.y & 0xFFFF0000u : x.y >> 16;
+        A[q] = f16x8_from_words(d0, d1, d2, d3);
+      }
+#pragma unroll
+      for (int st = 0; st < TW / ST; ++st) {
+        const int cch = tg * TW + st * ST + col / LPC;      // this lane's chunk
+        uint4 wd[R];
+#pragma unroll
+        for (int m = 0; m < R; ++m)
+          wd[m] = *reinterpret_cast<const uint4*>(&sw[(cch * R + m) * SWS + b * 16 + 4 * G]);
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+          const int k2 = 2 * (j * LPC + col % LPC);         // bit offset of the pair
+          uint32_t hw[4], lw[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            uint32_t pi = 0;
+#pragma unroll
+            for (int m = 0; m < R; ++m) {
+              const uint32_t wv = u == 0 ? wd[m].x : u == 1 ? wd[m].y : u == 2 ? wd[m].z : wd[m].w;
+              pi |= ((wv >> k2) & 3u) << (2 * m);
+            }
+            const uint2 e = ptab[pi];
+            hw[u] = e.x;
+            lw[u] = e.y;
+          }
+          const f16x8 bh = f16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
+          const f16x8 bl = f16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
+#pragma unroll
+          for (int q = 0; q < RQ; ++q) {
+            acc[q][st * ST + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[q], bh, acc[q][st * ST + j], 0, 0, 0);
+            acc[q][st * ST + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[q], bl, acc[q][st * ST + j], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+  // ---- partial sums: lane groups G = 2p (high limb) and 2p + 1 (low limb) hold parity p ----
+#pragma unroll
+  for (int r = 0; r < NRW; ++r) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) esum[r] += __shfl_xor(esum[r], m);
+  }
+  __syncthreads();                        // staging memory is free
+  if (lane == 0) {
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) red[wave][r] = esum[r];
+  }
+  const float osc = nmax / kDequantLevelScale;
+  float* yb = reinterpret_cast<float*>(raw);
+  const size_t rows_total = (size_t)a.nq_per_group * gridDim.y;
+  const size_t row0 = (size_t)(grp * a.nq_per_group + q0);
+  float* pbase = a.part + ((size_t)chunk * rows_total + row0) * (D + 2);
+#pragma unroll
+  for (int q = 0; q < RQ; ++q)
+#pragma unroll
+    for (int t = 0; t < TW; ++t) {
+      f32x4 v = acc[q][t];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] += __shfl_xor(v[i], 16);
+      const int jt = tg * TW + t;
+      const int cch = (jt / ST) * ST + col / LPC;
+      const int coord = 32 * cch + 2 * ((jt % ST) * LPC + col % LPC) + (G >> 1);
+      if ((G & 1) == 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 4 * q + i;
+          if (TSP > 1)
+            yb[(ts * NRW + r) * D + coord] = v[i];
+          else if (r < nr)
+            pbase[(size_t)r * (D + 2) + coord] = v[i] * osc;
+        }
+      }
+    }
+  __syncthreads();
+  if (TSP > 1) {
+    for (int idx = tid; idx < nr * D; idx += kBlock) {
+      const int r = idx / D, i = idx - r * D;
+      float y = 0.f;
+#pragma unroll
+      for (int h = 0; h < TSP; ++h) y += yb[(h * NRW + r) * D + i];
+      pbase[(size_t)r * (D + 2) + i] = y * osc;
+    }
+  }
+  if (tid < nr) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) sum += red[w][tid];
+    pbase[(size_t)tid * (D + 2) + D] = rmax[tid];
+    pbase[(size_t)tid * (D + 2) + D + 1] = sum;
+  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(kBlock) attend_combine_kernel(AttnArgs a, int64_t rows) {
+  constexpr int NW = kBlock / kWave;
+  constexpr int TPC = D < kBlock ? kBlock / D : 1;     // threads per coordinate (chunk subsets)
+  __shared__ float y[D];
+  __shared__ float sub[TPC > 1 ? TPC : 1][D < kBlock ? D : 1];
+  __shared__ float wred[NW];
+  __shared__ float scl[2];
+  const SubDev& s = a.s;
+  const int64_t row = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t nch = a.n_chunks;
+  auto at = [&](int64_t c) { return a.part + ((size_t)c * rows + row) * (D + 2); };
+  float m = -INFINITY;
+  for (int64_t c = tid; c < nch; c += kBlock) m = fmaxf(m, at(c)[D]);
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
+  if (lane == 0) wred[wave] = m;
+  __syncthreads();
+  if (tid == 0) {
+    float v = wred[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v = fmaxf(v, wred[w]);
+    scl[0] = v;
+  }
+  __syncthreads();
+  const float M = scl[0];
+  float sacc = 0.f;
+  for (int64_t c = tid; c < nch; c += kBlock) sacc += at(c)[D + 1] * __expf(at(c)[D] - M);
+#pragma unroll
+  for (int k = 32; k >= 1; k >>= 1) sacc += __shfl_xor(sacc, k);
+  __syncthreads();
+  if (lane == 0) wred[wave] = sacc;
+  __syncthreads();
+  if (tid == 0) {
+    float v = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) v += wred[w];
+    scl[1] = v;
+  }
+  if (TPC > 1) {
+    const int i = tid % D, h = tid / D;
+    float t = 0.f;
+    for (int64_t c = h; c < nch; c += TPC) t = fmaf(at(c)[i], __expf(at(c)[D] - M), t);
+    sub[h][i] = t;
+    __syncthreads();
+    if (tid < D) {
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < TPC; ++q) v += sub[q][tid];
+      y[tid] = v;
+    }
+  } else {
+    for (int i = tid; i < D; i += kBlock) {
+      float t = 0.f;
+      for (int64_t c = 0; c < nch; ++c) t = fmaf(at(c)[i], __expf(at(c)[D] - M), t);
+      y[i] = t;
+    }
+  }
+  __syncthreads();
+  // Pi^T: rounds from the last, each a Walsh-Hadamard transform then that round's diagonal
+  for (int r = 2; r >= 0; --r) {
+    for (int hh = 1; hh < D; hh <<= 1) {
+      for (int p = tid; p < D / 2; p += kBlock) {
+        const int i = (p / hh) * 2 * hh + (p % hh);
+        const float u = y[i], v = y[i + hh];
+        y[i] = u + v;
+        y[i + hh] = u - v;
+      }
+      __syncthreads();
+    }
+    for (int i = tid; i < D; i += kBlock)
+      y[i] = flip_sign(y[i], (s.signs[r * (D / 32) + i / 32] >> (i % 32)) & 1u);
+    __syncthreads();
+  }
+  const float sc = s.inv_scale / scl[1];
+  for (int i = tid; i < s.d; i += kBlock) {
+    const float v = y[i] * sc;
+    if (a.out_bf16)
+      static_cast<uint16_t*>(a.out)[row * a.ldo + i] = (uint16_t)pack_bf16_rne(v, 0.f);
+    else
+      static_cast<float*>(a.out)[row * a.ldo + i] = v;
+  }
+}
+
+template <int D, int RQ>
+static void launch_attend_rq(const AttnArgs& aa, int64_t n_groups, hipStream_t st) {
+  const int64_t qtiles = (aa.nq_per_group + 4 * RQ - 1) / (4 * RQ);
+  const dim3 g1((unsigned)aa.n_chunks, (unsigned)n_groups, (unsigned)qtiles);
+  switch (aa.s.R) {
+    case 1: hipLaunchKernelGGL((attend_mfma_kernel<D, 1, RQ>), g1, dim3(kBlock), 0, st, aa); break;
+    case 2: hipLaunchKernelGGL((attend_mfma_kernel<D, 2, RQ>), g1, dim3(kBlock), 0, st, aa); break;
+    case 3: hipLaunchKernelGGL((attend_mfma_kernel<D, 3, RQ>), g1, dim3(kBlock), 0, st, aa); break;
+    default: hipLaunchKernelGGL((attend_mfma_kernel<D, 4, RQ>), g1, dim3(kBlock), 0, st, aa); break;
+  }
+}
+
+template <int D>
+static int launch_attend_d(const AttnArgs& aa, int64_t n_groups, hipStream_t st) {
+  if (aa.s.R < 1 || aa.s.R > 4) return (int)hipErrorInvalidValue;
+  // two row quads per workgroup when there are more than 4 rows (one at D = 2048, where the
+  // accumulators of 8 rows would not fit a wave's share of the tiles)
+  if (aa.nq_per_group > 4 && D <= 1024)
+    launch_attend_rq<D, D <= 1024 ? 2 : 1>(aa, n_groups, st);
+  else
+    launch_attend_rq<D, 1>(aa, n_groups, st);
+  const int64_t rows = aa.nq_per_group * n_groups;
+  hipLaunchKernelGGL(attend_combine_kernel<D>, dim3((unsigned)rows), dim3(kBlock), 0, st, aa, rows);
+  return (int)hipGetLastError();
+}
+
+int launch_attend(const PlanDev& p, const float* logits, int64_t nq_per_group, int64_t n_groups,
+                  int64_t n, float scale, const uint8_t* codes, void* out, int dt, int64_t ldo,
+                  void* stream) {
+  if (nq_per_group == 0 || n_groups == 0) return 0;
+  hipStream_t st = (hipStream_t)stream;
+  AttnArgs aa;
+  aa.s = p.sub[0];
+  aa.logits = logits;
+  aa.n = n;
+  aa.nq_per_group = nq_per_group;
+  aa.scale = scale;
+  aa.codes = codes;
+  aa.rec_bytes = p.rec_bytes;
+  aa.n_chunks = (n + kAttnChunk - 1) / kAttnChunk;
+  aa.out = out;
+  aa.ldo = ldo;
+  aa.out_bf16 = dt == TQ_BF16;
+  const size_t bytes = (size_t)aa.n_chunks * nq_per_group * n_groups * (aa.s.D + 2) * 4;
+  void* ws = nullptr;
+  hipError_t e = hipMallocAsync(&ws, bytes, st);
+  if (e != hipSuccess) return (int)e;
+  aa.part = static_cast<float*>(ws);
+  int rc;
+  switch (aa.s.D) {
+    case 32: rc = launch_attend_d<32>(aa, n_groups, st); break;
+    case 64: rc = launch_attend_d<64>(aa, n_groups, st); break;
+    case 128: rc = launch_attend_d<128>(aa, n_groups, st); break;
+    case 256: rc = launch_attend_d<256>(aa, n_groups, st); break;
+    case 512: rc = launch_attend_d<512>(aa, n_groups, st); break;
+    case 1024: rc = launch_attend_d<1024>(aa, n_groups, st); break;
+    case 2048: rc = launch_attend_d<2048>(aa, n_groups, st); break;
+    default: rc = (int)hipErrorInvalidValue;
+  }
+  e = hipFreeAsync(ws, st);
+  if (!rc && e != hipSuccess) rc = (int)e;
+  return rc;
+}
+
 // ============================================================================ re-rank
 // Second stage of two-stage retrieval (technical overview §4.2.2): exact inner products of
 // each query with its candidates' full-precision vectors, and the k best by (-value, id).

@@ -478,6 +478,25 @@ tq_status tq_dequantize(const tq_plan* plan, const void* codes, int64_t n, void*
                                     ldx, stream));
 }
 
+tq_status tq_attend(const tq_plan* vplan, const float* logits, int64_t nq_per_group,
+                    int64_t n_groups, int64_t n, float scale, const void* vcodes, void* out,
+                    tq_dtype dt, int64_t ldo, void* stream) {
+  if (!vplan || nq_per_group < 0 || n_groups < 0 || n < 1 || (dt != TQ_F32 && dt != TQ_BF16) ||
+      !std::isfinite(scale))
+    return TQ_EINVAL;
+  if (nq_per_group == 0 || n_groups == 0) return TQ_OK;
+  if (vplan->dev.nsub != 1 || vplan->dev.sub[0].R > 4) return TQ_EUNSUPPORTED;
+  const int es = dt == TQ_BF16 ? 2 : 4;
+  if (!logits || !vcodes || !out || ldo < vplan->dev.d || (uintptr_t)logits % 4 ||
+      (uintptr_t)vcodes % 16 || (uintptr_t)out % es)
+    return TQ_EINVAL;
+  if (n_groups > 65535 || (nq_per_group + 3) / 4 > 65535 || (n + 1023) / 1024 > ((int64_t)1 << 31))
+    return TQ_EINVAL;
+  if (!plan_device_ok(vplan)) return TQ_EINVAL;
+  return from_hip(launch_attend(vplan->dev, logits, nq_per_group, n_groups, n, scale,
+                                static_cast<const uint8_t*>(vcodes), out, (int)dt, ldo, stream));
+}
+
 tq_status tq_rerank(const void* q, tq_dtype qdt, int64_t nq, int64_t ldq, const void* x,
                     tq_dtype xdt, int64_t n, int64_t ldx, int d, const int64_t* cand, int kc, int k,
                     int64_t* ids, float* vals, void* stream) {

@@ -75,6 +75,9 @@ int launch_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids,
                 void* stream);
 int launch_dequantize(const PlanDev& p, const uint8_t* codes, int64_t n, void* out, int dt,
                       int64_t ldo, void* stream);
+int launch_attend(const PlanDev& p, const float* logits, int64_t nq_per_group, int64_t n_groups,
+                  int64_t n, float scale, const uint8_t* codes, void* out, int dt, int64_t ldo,
+                  void* stream);
 int launch_rerank(const void* q, int q_bf16, int64_t nq, int64_t ldq, const void* x, int x_bf16,
                   int64_t n, int64_t ldx, int d, const int64_t* cand, int kc, int k, int64_t* ids,
                   float* vals, void* stream);

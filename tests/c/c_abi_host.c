@@ -67,6 +67,16 @@ int main(void) {
   CHECK(tq_plan_create_mse(128, 5, 0, &plan) == TQ_EINVAL, "mse plan bits = 5 rejected");
   CHECK(tq_plan_create_mse(128, 3, 0, NULL) == TQ_EINVAL, "mse plan without output");
   CHECK(tq_dequantize(NULL, NULL, 1, NULL, TQ_F32, 128, NULL) == TQ_EINVAL, "dequantize without plan");
+  CHECK(tq_attend(NULL, NULL, 4, 1, 10, 1.0f, NULL, NULL, TQ_F32, 128, NULL) == TQ_EINVAL,
+        "attend without plan");
+  CHECK(tq_rerank(NULL, TQ_F32, 1, 64, NULL, TQ_F32, 10, 64, 64, NULL, 8, 9, NULL, NULL, NULL) ==
+            TQ_EINVAL,
+        "rerank with k > kc");
+  CHECK(tq_rerank(NULL, TQ_F32, 1, 64, NULL, TQ_F32, 10, 64, 64, NULL, 300, 10, NULL, NULL, NULL) ==
+            TQ_EINVAL,
+        "rerank with kc > 256");
+  CHECK(tq_rerank(NULL, TQ_F32, 0, 64, NULL, TQ_F32, 10, 64, 64, NULL, 8, 4, NULL, NULL, NULL) == TQ_OK,
+        "rerank with no queries is a no-op");
   tq_plan_destroy(NULL);
   printf("all passed\n");
   return 0;

@@ -1,0 +1,93 @@
+"""Decode attention over quantized values (tq_attend) through the C ABI against the fp64
+oracle, on the library's own value codes and the same logits: single and ragged chunks of
+1024 tokens, several query tiles, every thread layout (D below, at and above the block
+size), inner-product value plans, logits produced by tq_score, fp32 and bf16 output."""
+import numpy as np
+import pytest
+
+from oracle import layout
+from oracle import turboquant as otq
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+import rotation_online_vector_amd as tq  # noqa: E402
+
+DEV = "cuda:0"
+
+
+def _np(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def _check(out, ref, vmax, bf16, what):
+    tol = 2e-5 * vmax + (2.0 ** -8 * np.abs(ref) if bf16 else 0.0)
+    err = np.abs(out - ref)
+    assert np.all(err <= tol), "%s: max err/tol %g" % (what, float(np.max(err / tol)))
+
+
+@pytest.mark.parametrize("d,bits,n,nqg,groups,mode,dtype", [
+    (128, 3, 5000, 4, 2, "mse", "float32"), (128, 2, 1024, 8, 1, "mse", "bfloat16"),
+    (64, 4, 3000, 12, 1, "mse", "float32"), (256, 3, 2500, 4, 1, "mse", "float32"),
+    (2048, 3, 700, 4, 1, "mse", "bfloat16"), (100, 4, 1500, 4, 1, "ip", "float32"),
+    (1, 2, 10, 1, 1, "mse", "float32"), (32, 1, 2049, 3, 3, "mse", "float32")])
+def test_attend_matches_oracle(d, bits, n, nqg, groups, mode, dtype):
+    rng = np.random.default_rng(d * 11 + n)
+    V = rng.standard_normal((groups * n, d)).astype(np.float32)
+    L = (rng.standard_normal((groups * nqg, n)) * 3.0).astype(np.float32)
+    if mode == "mse":
+        plan, op = tq.tq_plan_create_mse(d, bits, 6), otq.make_mse_plan(d, bits, 6)
+    else:
+        plan, op = tq.tq_plan_create(d, bits, 6), otq.make_plan(d, bits, 6)
+    vcodes = tq.tq_encode(plan, torch.from_numpy(V).to(DEV).to(getattr(torch, dtype)))
+    logits = torch.from_numpy(L).to(DEV)
+    out = tq.tq_attend(plan, logits, vcodes, n, 0.4, nq_per_group=nqg, n_groups=groups,
+                       dtype=getattr(torch, dtype))
+    torch.cuda.synchronize()
+    c = vcodes.cpu().numpy()
+    st = layout.unpack_mse(c, op.D, op.R) if mode == "mse" else layout.unpack(c, op.D, op.R)
+    ref = otq.attend(op, L.astype(np.float64), dict(idx=st["idx"], norm=st["norm"]), 0.4, nqg)
+    vmax = np.max(np.linalg.norm(otq.dequantize(op, st), axis=1))
+    _check(_np(out), ref, vmax, dtype == "bfloat16", "attend d=%d n=%d" % (d, n))
+
+
+def test_attend_with_logits_from_score():
+    """The decode step as used: K codes scored (tq_score), then attention over V codes."""
+    d, n, G, groups = 128, 3000, 4, 2
+    rng = np.random.default_rng(2)
+    K = torch.from_numpy(rng.standard_normal((groups * n, d)).astype(np.float32)).to(DEV)
+    V = torch.from_numpy(rng.standard_normal((groups * n, d)).astype(np.float32)).to(DEV)
+    Q = torch.from_numpy(rng.standard_normal((groups * G, d)).astype(np.float32)).to(DEV)
+    kplan, vplan = tq.tq_plan_create(d, 3, 1), tq.tq_plan_create_mse(d, 3, 2)
+    kc, vc = tq.tq_encode(kplan, K), tq.tq_encode(vplan, V)
+    logits = tq.tq_score(kplan, Q, kc, n=n, nq_per_group=G, n_groups=groups)
+    out = tq.tq_attend(vplan, logits, vc, n, 1.0 / np.sqrt(d), nq_per_group=G, n_groups=groups)
+    torch.cuda.synchronize()
+    op = otq.make_mse_plan(d, 3, 2)
+    st = layout.unpack_mse(vc.cpu().numpy(), op.D, 3)
+    ref = otq.attend(op, _np(logits), st, 1.0 / np.sqrt(d), G)
+    vmax = np.max(np.linalg.norm(otq.dequantize(op, st), axis=1))
+    _check(_np(out), ref, vmax, False, "score + attend")
+
+
+def test_attend_uniform_logits_full_context_is_the_mean():
+    """131072 tokens (128 chunks) with equal logits: the output is the mean of the
+    dequantized values (computed from tq_dequantize), for every query row."""
+    d, n = 128, 131072
+    rng = np.random.default_rng(4)
+    V = torch.from_numpy(rng.standard_normal((n, d)).astype(np.float32)).to(DEV)
+    plan = tq.tq_plan_create_mse(d, 3, 0)
+    vc = tq.tq_encode(plan, V)
+    out = tq.tq_attend(plan, torch.full((4, n), 0.5, device=DEV), vc, n, 2.0)
+    mean = tq.tq_dequantize(plan, vc, n).double().mean(0)
+    torch.cuda.synchronize()
+    assert torch.allclose(out.double(), mean.expand(4, d), rtol=0, atol=2e-5 * float(mean.norm()) + 1e-6)
+
+
+def test_attend_rejects_split_plans_and_bad_sizes():
+    m = np.zeros(64, dtype=np.uint8)
+    m[:8] = 1
+    plan = tq.tq_plan_create(64, 3, 0, m, 4)
+    vc = torch.zeros((10, plan.record_bytes), dtype=torch.uint8, device=DEV)
+    with pytest.raises(tq.TqError):
+        tq.tq_attend(plan, torch.zeros((2, 10), device=DEV), vc, 10, 1.0)

@@ -17,6 +17,8 @@ Shapes (all keys/queries are row vectors of the key dimension):
             eigenvalues 1/i along the axes; 1024 queries of the same law; b = 4
   longctx : 16 sequences x 8 KV heads x 131072 tokens x 128, bf16 N(0, 1) with
             6 channels per (sequence, head) drawn Student-t (3 d.o.f.); b = 3
+  attend  : the longctx keys (b = 3) and values drawn the same way with seed 1
+            (3-bit MSE plan), both held encoded; one decode step scores and attends
 """
 import numpy as np
 
@@ -33,6 +35,10 @@ LONGCTX = dict(name="longctx-16x8x131072x128-bf16-b3", n_seq=16, n_kv=8, n_tok=1
 # TurboQuant-MSE on the same keys: 3-bit codes for most heads (technical overview §4.1.1),
 # dequantized in one batch before attention (§4.1.2)
 MSE_LONGCTX = dict(LONGCTX, name="mse-longctx-16x8x131072x128-bf16-b3")
+# one decode step over the same cache held quantized: keys under the inner-product plan
+# (scored), values under a 3-bit MSE plan (attended), both encoded before the step
+ATTEND_LONGCTX = dict(LONGCTX, name="attend-longctx-16x8x131072x128-k3ip-v3mse",
+                      v_bits=3, v_seed=1)
 
 
 def small_inputs(n_keys=4096, n_queries=64, d=128, seed=0):
