@@ -2283,60 +2283,131 @@ struct AttnArgs {
   const uint8_t* codes;      // group g's records from g * n
   int rec_bytes;
   int64_t n_chunks;
+  int64_t chunks_per_block;  // consecutive chunks streamed by one workgroup
   float* part;               // [chunk][row][D + 2]: y, then max, then sum
   void* out;
   int64_t ldo;
   int out_bf16;
 };
 
-// tokens per LDS stage: the largest power of two <= 1024 whose plane words fit 32 KiB
-constexpr int attn_stage_tokens(int cmw) {
-  int t = kAttnChunk;
-  while (t > 16 && cmw * (t + 4) * 4 > 32768) t >>= 1;
+// Staging: thread (tt, cm) reads word slot cm of tokens tt, tt + TPI, .. (CMWP = the words per
+// token rounded up to a power of two threads per token, TPI = 256 / CMWP tokens per step).
+constexpr int attn_pow2_at_least(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+// tokens per stage: the largest power of two <= 512 whose words fit 32 KiB of LDS and take
+// at most 16 loads per thread
+constexpr int attn_stage_tokens(int wpt) {
+  int t = 512;
+  while (t > 16 && (wpt * (t + 4) * 4 > 32768 || t * attn_pow2_at_least(wpt) > 16 * kBlock)) t >>= 1;
   return t;
 }
 
+// A workgroup streams the stages of up to chunks_per_block consecutive chunks of one group and
+// row tile: the next stage's plane words, norms and logits are loaded while the current stage
+// is contracted.  The softmax max and the norm scale are running values over the chunk (as in
+// online softmax): when a stage raises them, the accumulators and the partial sums of the
+// exponentials are rescaled.  At the end of each chunk its partial (y, max, sum) is written.
 template <int D, int R, int RQ>
-__global__ void __launch_bounds__(kBlock) attend_mfma_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D <= 256 && RQ == 1 ? 4 : 1)))
+attend_mfma_kernel(AttnArgs a) {
   constexpr int NW = kBlock / kWave;
   constexpr int NJT = D / 32;                       // column tiles of 16 pairs = chunks
   constexpr int ST = NJT < 4 ? NJT : 4;             // tiles sharing a lane's chunk
   constexpr int LPC = 16 / ST;                      // columns per chunk within those tiles
+  constexpr int FW = 2 * LPC;                       // bits between the pairs of those tiles
   constexpr int TW = NJT < 16 / RQ ? NJT : 16 / RQ; // tiles per wave
   constexpr int NTG = NJT / TW;                     // tile groups
   static_assert(NTG <= NW && TW % ST == 0, "tile split");
   constexpr int TSP = NW / NTG;                     // waves splitting the tokens of a tile group
-  constexpr int CMW = NJT * R;                      // staged plane words per token
-  constexpr int TS = attn_stage_tokens(CMW);
+  constexpr int CMW = NJT * R;                      // plane words per token
+  constexpr int WPT = CMW + 1;                      // and the norm
+  constexpr int TS = attn_stage_tokens(WPT);
+  constexpr int CMWP = attn_pow2_at_least(WPT);
+  constexpr int SPT = CMWP > kBlock ? CMWP / kBlock : 1;   // word slots per thread and token
+  constexpr int TPI = CMWP > kBlock ? 1 : kBlock / CMWP;   // tokens per staging step
+  static_assert(TS % TPI == 0 && kAttnChunk % TS == 0, "stage split");
+  constexpr int NLD = TS / TPI * SPT;               // staged words per thread
+  constexpr int LPT = TS >= kBlock ? TS / kBlock : 1;   // stage tokens per thread (logits)
   constexpr int SWS = TS + 4;                       // dword stride of a staged word row
-  constexpr int WLS = TS + 8;                       // fp16 stride of a staged weight row
+  constexpr int WLS = TS + 8;                       // fp16 stride of a weight row
   constexpr int NRW = 4 * RQ;
-  constexpr int STAGE_BYTES = CMW * SWS * 4 + 2 * NRW * WLS * 2;
+  constexpr int SW_BYTES = WPT * SWS * 4;
+  constexpr int STAGE_BYTES = SW_BYTES + 2 * NRW * WLS * 2;
   constexpr int RED_BYTES = TSP > 1 ? TSP * NRW * D * 4 : 0;
   constexpr int RAW = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
   constexpr int NPAIR = 1 << (2 * R);
+  // pair fields pre-multiplied by 4 (the byte offset of a table entry) when they fit
+  constexpr int SH = 2 * R + 2 <= FW ? 2 : 0;
+  constexpr uint32_t FMASK = (1u << (2 * R + SH)) - 1u;
+  uint32_t pm = 0;
+  for (int j = 0; j < ST; ++j) pm |= 3u << (FW * j);
+  const uint32_t PMASK = pm;
   __shared__ __attribute__((aligned(16))) unsigned char raw[RAW];
-  __shared__ uint2 ptab[NPAIR];
-  __shared__ float red[NW][NRW + 1];
-  __shared__ float rmax[NRW + 1];
+  __shared__ uint32_t ptab[2 * NPAIR];              // high limbs, then low limbs
+  __shared__ float red[2][NW][NRW + 1];             // per stage (two in flight): maxima
+  __shared__ float ered[NW][NRW];                   // sums of the exponentials at a flush
   uint32_t* sw = reinterpret_cast<uint32_t*>(raw);
-  uint16_t* wl = reinterpret_cast<uint16_t*>(raw + CMW * SWS * 4);
+  const float* snrm = reinterpret_cast<const float*>(sw + CMW * SWS);   // row CMW: the norms
+  uint16_t* wl = reinterpret_cast<uint16_t*>(raw + SW_BYTES);
   const SubDev& s = a.s;
   const int W = s.mse ? R : R + 1;
   const int rb = a.rec_bytes;
-  const int64_t chunk = blockIdx.x, grp = blockIdx.y;
+  const int64_t grp = blockIdx.y;
   const int64_t q0 = (int64_t)blockIdx.z * NRW;
   const int nr = (int)((a.nq_per_group - q0) < NRW ? (a.nq_per_group - q0) : NRW);
-  const int64_t t0 = chunk * kAttnChunk;
-  const int nt = (int)((a.n - t0) < kAttnChunk ? (a.n - t0) : kAttnChunk);
+  const int64_t cb = (int64_t)blockIdx.x * a.chunks_per_block;
+  const int64_t ce = (cb + a.chunks_per_block) < a.n_chunks ? cb + a.chunks_per_block : a.n_chunks;
+  const int64_t T0 = cb * kAttnChunk;
+  const int64_t T1 = (ce * kAttnChunk) < a.n ? ce * kAttnChunk : a.n;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint8_t* codes = a.codes + (grp * a.n + t0) * (int64_t)rb + s.rec_off;
-  const float* lg = a.logits + (grp * a.nq_per_group + q0) * a.n + t0;
-  auto norm_of = [&](int j) {
-    return __uint_as_float(reinterpret_cast<const uint32_t*>(codes + (int64_t)j * rb)[NJT * W]);
+  const uint8_t* gcodes = a.codes + grp * a.n * (int64_t)rb + s.rec_off;
+  const float* glg = a.logits + (grp * a.nq_per_group + q0) * a.n;
+  // ---- staging roles; full stages load unconditionally (all loads in flight together) ----
+  const int stt = CMWP > kBlock ? 0 : tid / CMWP;
+  int sslot[SPT];
+  uint32_t svoff[SPT];
+#pragma unroll
+  for (int i = 0; i < SPT; ++i) {
+    sslot[i] = CMWP > kBlock ? tid + kBlock * i : tid % CMWP;
+    const int scw = sslot[i] < WPT ? sslot[i] : 0;
+    const int sword = scw == CMW ? NJT * W : (scw / R) * W + scw % R;
+    svoff[i] = (uint32_t)(stt * rb + sword * 4);
+  }
+  uint32_t pw[NLD];
+  float pl[NRW][LPT];
+  auto load_stage = [&](int64_t S) {
+    const int ns = (T1 - S) < TS ? (int)(T1 - S) : TS;
+    const uint8_t* b0 = gcodes + S * rb;
+    if (ns == TS) {
+#pragma unroll
+      for (int k = 0; k < NLD; ++k)
+        pw[k] = *reinterpret_cast<const uint32_t*>(b0 + (int64_t)(TPI * (k / SPT)) * rb + svoff[k % SPT]);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NLD; ++k)
+        pw[k] = stt + TPI * (k / SPT) < ns
+                    ? *reinterpret_cast<const uint32_t*>(b0 + (int64_t)(TPI * (k / SPT)) * rb +
+                                                         svoff[k % SPT])
+                    : 0u;
+    }
+    // logits of this thread's stage tokens, indices clamped and values masked arithmetically
+#pragma unroll
+    for (int k = 0; k < LPT; ++k) {
+      const int t = tid + kBlock * k;
+      const int tc = t < ns ? t : ns - 1;
+#pragma unroll
+      for (int r = 0; r < NRW; ++r) {
+        const int rc = r < nr ? r : nr - 1;
+        pl[r][k] = fminf(a.scale * glg[rc * a.n + S + tc], (t < ns && r < nr) ? INFINITY : -INFINITY);
+      }
+    }
   };
+  load_stage(T0);
   // pair table: entry i holds coordinate 2q's level (index bits i_0, i_2, ..) in the low
-  // fp16 half and 2q + 1's (bits i_1, i_3, ..) in the high half; .x the high limbs, .y the low
+  // fp16 half and 2q + 1's (bits i_1, i_3, ..) in the high half
   for (int i = tid; i < NPAIR; i += kBlock) {
     int ia = 0, ib = 0;
 #pragma unroll
@@ -2344,23 +2415,52 @@ __global__ void __launch_bounds__(kBlock) attend_mfma_kernel(AttnArgs a) {
       ia |= ((i >> (2 * m)) & 1) << m;
       ib |= ((i >> (2 * m + 1)) & 1) << m;
     }
-    const float ca = s.lev[ia] * kDequantLevelScale, cb = s.lev[ib] * kDequantLevelScale;
+    const float ca = s.lev[ia] * kDequantLevelScale, cb2 = s.lev[ib] * kDequantLevelScale;
     typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
-    const f16x2 hv = __builtin_amdgcn_cvt_pkrtz(ca, cb);
-    ptab[i] = make_uint2(__builtin_bit_cast(uint32_t, hv),
-                         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(
-                                                          ca - (float)hv[0], cb - (float)hv[1])));
+    const f16x2 hv = __builtin_amdgcn_cvt_pkrtz(ca, cb2);
+    ptab[i] = __builtin_bit_cast(uint32_t, hv);
+    ptab[NPAIR + i] =
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ca - (float)hv[0], cb2 - (float)hv[1]));
   }
-  // ---- the chunk's max of scale * logit per row and max norm ----
-  {
-    float mx[NRW], nm = 0.f;
+  const int col = lane & 15, G = lane >> 4;
+  const int tg = wave / TSP, ts = wave % TSP;
+  const int am = lane & 15, ap = am >> 3, alimb = (am >> 2) & 1, ar = am & 3;
+  // A operand: a weight limb into the low (parity 0) or high (parity 1) half of a dword
+  const uint32_t sel_a = ap ? 0x01000C0Cu : 0x0C0C0100u;
+  const uint32_t sel_b = ap ? 0x03020C0Cu : 0x0C0C0302u;
+  const int psh = 2 * (col % LPC);                  // this lane's pair offset in a word
+  const unsigned char* tab = reinterpret_cast<const unsigned char*>(ptab);
+  float rm[NRW], esum[NRW];                         // running max of scale * logit, partial sums
+  float nsc = 0.f;                                  // running max norm
 #pragma unroll
-    for (int r = 0; r < NRW; ++r) mx[r] = -INFINITY;
-    for (int j = tid; j < nt; j += kBlock) {
-      nm = fmaxf(nm, norm_of(j));
+  for (int r = 0; r < NRW; ++r) {
+    rm[r] = -INFINITY;
+    esum[r] = 0.f;
+  }
+  f32x4 acc[RQ][TW];
 #pragma unroll
-      for (int r = 0; r < NRW; ++r)
-        if (r < nr) mx[r] = fmaxf(mx[r], a.scale * lg[r * a.n + j]);
+  for (int q = 0; q < RQ; ++q)
+#pragma unroll
+    for (int t = 0; t < TW; ++t) acc[q][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  int par = 0;
+  for (int64_t S = T0; S < T1; S += TS, par ^= 1) {
+    const int ns = (T1 - S) < TS ? (int)(T1 - S) : TS;
+    __syncthreads();                      // the previous stage's LDS reads are done
+    // ---- words and norms into LDS; this stage's maxima ----
+    float nm = 0.f, mx[NRW];
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      const int sl = sslot[k % SPT];
+      if (sl < WPT) {
+        sw[sl * SWS + stt + TPI * (k / SPT)] = pw[k];
+        if (sl == CMW) nm = fmaxf(nm, __uint_as_float(pw[k]));
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+      mx[r] = pl[r][0];
+#pragma unroll
+      for (int k = 1; k < LPT; ++k) mx[r] = fmaxf(mx[r], pl[r][k]);
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) {
@@ -2370,71 +2470,67 @@ __global__ void __launch_bounds__(kBlock) attend_mfma_kernel(AttnArgs a) {
     }
     if (lane == 0) {
 #pragma unroll
-      for (int r = 0; r < NRW; ++r) red[wave][r] = mx[r];
-      red[wave][NRW] = nm;
+      for (int r = 0; r < NRW; ++r) red[par][wave][r] = mx[r];
+      red[par][wave][NRW] = nm;
     }
     __syncthreads();
-    if (tid <= NRW) {
-      float v = red[0][tid];
+    // ---- running maxima; rescale what was accumulated under the old ones ----
+    float nn = nsc;
 #pragma unroll
-      for (int w = 1; w < NW; ++w) v = fmaxf(v, red[w][tid]);
-      rmax[tid] = v;
+    for (int w = 0; w < NW; ++w) nn = fmaxf(nn, red[par][w][NRW]);
+    bool changed = nn != nsc;
+    float fr[NRW];
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+      float mn = rm[r];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) mn = fmaxf(mn, red[par][w][r]);
+      const float fe = (r < nr && mn != rm[r]) ? __expf(rm[r] - mn) : 1.f;
+      changed |= fe != 1.f;
+      esum[r] *= fe;
+      fr[r] = fe * (nsc > 0.f ? nsc / nn : 1.f);
+      rm[r] = mn;
     }
-    __syncthreads();
-  }
-  const float nmax = rmax[NRW];
-  const float inv_nm = nmax > 0.f ? 1.f / nmax : 0.f;
-  // ---- stages: plane words and weight limbs into LDS, then the contraction ----
-  const int col = lane & 15, G = lane >> 4;
-  const int tg = wave / TSP, ts = wave % TSP;
-  const int am = lane & 15, ap = am >> 3, alimb = (am >> 2) & 1, ar = am & 3;
-  float esum[NRW];
+    if (changed) {
 #pragma unroll
-  for (int r = 0; r < NRW; ++r) esum[r] = 0.f;
-  f32x4 acc[RQ][TW];
+      for (int q = 0; q < RQ; ++q)
 #pragma unroll
-  for (int q = 0; q < RQ; ++q)
+        for (int t = 0; t < TW; ++t)
 #pragma unroll
-    for (int t = 0; t < TW; ++t) acc[q][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  for (int s0 = 0; s0 < nt; s0 += TS) {
-    const int ns = (nt - s0) < TS ? (nt - s0) : TS;
-    __syncthreads();                      // the previous stage's reads are done
-    for (int idx = tid; idx < TS * CMW; idx += kBlock) {
-      const int t = idx / CMW, cm = idx - t * CMW;
-      const int c = cm / R, m = cm - c * R;
-      uint32_t v = 0u;
-      if (t < ns) v = reinterpret_cast<const uint32_t*>(codes + (int64_t)(s0 + t) * rb)[c * W + m];
-      sw[cm * SWS + t] = v;
+          for (int i = 0; i < 4; ++i) acc[q][t][i] *= fr[4 * q + i];
     }
-    for (int t = tid; t < TS; t += kBlock) {
-      const float nw = t < ns ? norm_of(s0 + t) * inv_nm : 0.f;
+    nsc = nn;
+    // ---- weights w = exp(scale l - max) n_j / nsc, two fp16 limbs ----
+    const float inv = nsc > 0.f ? 1.f / nsc : 0.f;
 #pragma unroll
-      for (int r = 0; r < NRW; ++r) {
-        float e = 0.f;
-        if (t < ns && r < nr) e = __expf(a.scale * lg[r * a.n + s0 + t] - rmax[r]);
-        esum[r] += e;
-        const float w = e * nw;
-        typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
-        const f16x2 h = __builtin_amdgcn_cvt_pkrtz(w, 0.f);
-        const f16x2 l = __builtin_amdgcn_cvt_pkrtz(w - (float)h[0], 0.f);
-        wl[r * WLS + t] = (uint16_t)(__builtin_bit_cast(uint32_t, h) & 0xFFFFu);
-        wl[(NRW + r) * WLS + t] = (uint16_t)(__builtin_bit_cast(uint32_t, l) & 0xFFFFu);
+    for (int k = 0; k < LPT; ++k) {
+      const int t = tid + kBlock * k;
+      if (t < TS) {
+        const float nw = snrm[t] * inv;
+#pragma unroll
+        for (int r = 0; r < NRW; ++r) {
+          const float e = r < nr ? __expf(pl[r][k] - rm[r]) : 0.f;
+          esum[r] += e;
+          const float w = e * nw;
+          typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
+          const f16x2 h = __builtin_amdgcn_cvt_pkrtz(w, 0.f);
+          const f16x2 l = __builtin_amdgcn_cvt_pkrtz(w - (float)h[0], 0.f);
+          wl[r * WLS + t] = (uint16_t)(__builtin_bit_cast(uint32_t, h) & 0xFFFFu);
+          wl[(NRW + r) * WLS + t] = (uint16_t)(__builtin_bit_cast(uint32_t, l) & 0xFFFFu);
+        }
       }
     }
+    if (S + TS < T1) load_stage(S + TS);    // in flight during the contraction
     __syncthreads();
+    // ---- the contraction over this stage's tokens ----
     const int nblk = (ns + 15) >> 4;
     for (int b = ts; b < nblk; b += TSP) {
-      // A: row am = (parity, limb, row) takes its weight limb in its parity's K slots
       f16x8 A[RQ];
 #pragma unroll
       for (int q = 0; q < RQ; ++q) {
-        const uint2 x = *reinterpret_cast<const uint2*>(
-            &wl[(alimb * NRW + 4 * q + ar) * WLS + b * 16 + 4 * G]);
-        const uint32_t d0 = ap ? x.x << 16 : x.x & 0xFFFFu;
-        const uint32_t d1 = ap ? x.x & 0xFFFF0000u : x.x >> 16;
-        const uint32_t d2 = ap ? x.y << 16 : x.y & 0xFFFFu;
-        const uint32_t d3 = ap ? x.y & 0xFFFF0000u : x.y >> 16;
-        A[q] = f16x8_from_words(d0, d1, d2, d3);
+        const uint2 x = *reinterpret_cast<const uint2*>(&wl[(alimb * NRW + 4 * q + ar) * WLS + b * 16 + 4 * G]);
+        A[q] = f16x8_from_words(__builtin_amdgcn_perm(0u, x.x, sel_a), __builtin_amdgcn_perm(0u, x.x, sel_b),
+                                __builtin_amdgcn_perm(0u, x.y, sel_a), __builtin_amdgcn_perm(0u, x.y, sel_b));
       }
 #pragma unroll
       for (int st = 0; st < TW / ST; ++st) {
@@ -2443,21 +2539,26 @@ __global__ void __launch_bounds__(kBlock) attend_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int m = 0; m < R; ++m)
           wd[m] = *reinterpret_cast<const uint4*>(&sw[(cch * R + m) * SWS + b * 16 + 4 * G]);
+        // per token: the pair fields of all ST tiles at once (tile j at bit FW j)
+        uint32_t P[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          uint32_t v = 0;
+#pragma unroll
+          for (int m = 0; m < R; ++m) {
+            const uint32_t wv = u == 0 ? wd[m].x : u == 1 ? wd[m].y : u == 2 ? wd[m].z : wd[m].w;
+            v |= ((wv >> psh) & PMASK) << (2 * m + SH);
+          }
+          P[u] = v;
+        }
 #pragma unroll
         for (int j = 0; j < ST; ++j) {
-          const int k2 = 2 * (j * LPC + col % LPC);         // bit offset of the pair
           uint32_t hw[4], lw[4];
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
-            uint32_t pi = 0;
-#pragma unroll
-            for (int m = 0; m < R; ++m) {
-              const uint32_t wv = u == 0 ? wd[m].x : u == 1 ? wd[m].y : u == 2 ? wd[m].z : wd[m].w;
-              pi |= ((wv >> k2) & 3u) << (2 * m);
-            }
-            const uint2 e = ptab[pi];
-            hw[u] = e.x;
-            lw[u] = e.y;
+            const uint32_t off = SH ? (P[u] >> (FW * j)) & FMASK : ((P[u] >> (FW * j)) & FMASK) << 2;
+            hw[u] = *reinterpret_cast<const uint32_t*>(tab + off);
+            lw[u] = *reinterpret_cast<const uint32_t*>(tab + NPAIR * 4 + off);
           }
           const f16x8 bh = f16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
           const f16x8 bl = f16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
@@ -2469,60 +2570,75 @@ __global__ void __launch_bounds__(kBlock) attend_mfma_kernel(AttnArgs a) {
         }
       }
     }
-  }
-  // ---- partial sums: lane groups G = 2p (high limb) and 2p + 1 (low limb) hold parity p ----
+    // ---- end of a chunk: its partial sums (lane groups G = 2p and 2p + 1 hold the high
+    // and low weight limbs of parity p), then a fresh start for the next chunk ----
+    const int64_t Se = S + ns;
+    if (Se == T1 || Se % kAttnChunk == 0) {
+      const int64_t chunk = (Se - 1) / kAttnChunk;
 #pragma unroll
-  for (int r = 0; r < NRW; ++r) {
+      for (int r = 0; r < NRW; ++r) {
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) esum[r] += __shfl_xor(esum[r], m);
-  }
-  __syncthreads();                        // staging memory is free
-  if (lane == 0) {
+        for (int m = 32; m >= 1; m >>= 1) esum[r] += __shfl_xor(esum[r], m);
+      }
+      if (lane == 0) {
 #pragma unroll
-    for (int r = 0; r < NRW; ++r) red[wave][r] = esum[r];
-  }
-  const float osc = nmax / kDequantLevelScale;
-  float* yb = reinterpret_cast<float*>(raw);
-  const size_t rows_total = (size_t)a.nq_per_group * gridDim.y;
-  const size_t row0 = (size_t)(grp * a.nq_per_group + q0);
-  float* pbase = a.part + ((size_t)chunk * rows_total + row0) * (D + 2);
+        for (int r = 0; r < NRW; ++r) ered[wave][r] = esum[r];
+      }
+      __syncthreads();                    // the contraction's LDS reads are done
+      const float osc = nsc / kDequantLevelScale;
+      float* yb = reinterpret_cast<float*>(raw);
+      const size_t rows_total = (size_t)a.nq_per_group * gridDim.y;
+      const size_t row0 = (size_t)(grp * a.nq_per_group + q0);
+      float* pbase = a.part + ((size_t)chunk * rows_total + row0) * (D + 2);
 #pragma unroll
-  for (int q = 0; q < RQ; ++q)
+      for (int q = 0; q < RQ; ++q)
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      f32x4 v = acc[q][t];
+        for (int t = 0; t < TW; ++t) {
+          f32x4 v = acc[q][t];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] += __shfl_xor(v[i], 16);
-      const int jt = tg * TW + t;
-      const int cch = (jt / ST) * ST + col / LPC;
-      const int coord = 32 * cch + 2 * ((jt % ST) * LPC + col % LPC) + (G >> 1);
-      if ((G & 1) == 0) {
+          for (int i = 0; i < 4; ++i) v[i] += __shfl_xor(v[i], 16);
+          const int jt = tg * TW + t;
+          const int cch = (jt / ST) * ST + col / LPC;
+          const int coord = 32 * cch + 2 * ((jt % ST) * LPC + col % LPC) + (G >> 1);
+          if ((G & 1) == 0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * q + i;
-          if (TSP > 1)
-            yb[(ts * NRW + r) * D + coord] = v[i];
-          else if (r < nr)
-            pbase[(size_t)r * (D + 2) + coord] = v[i] * osc;
+            for (int i = 0; i < 4; ++i) {
+              const int r = 4 * q + i;
+              if (TSP > 1)
+                yb[(ts * NRW + r) * D + coord] = v[i];
+              else if (r < nr)
+                pbase[(size_t)r * (D + 2) + coord] = v[i] * osc;
+            }
+          }
+          acc[q][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+      __syncthreads();
+      if (TSP > 1) {
+        for (int idx = tid; idx < nr * D; idx += kBlock) {
+          const int r = idx / D, i = idx - r * D;
+          float y = 0.f;
+#pragma unroll
+          for (int h = 0; h < TSP; ++h) y += yb[(h * NRW + r) * D + i];
+          pbase[(size_t)r * (D + 2) + i] = y * osc;
         }
       }
-    }
-  __syncthreads();
-  if (TSP > 1) {
-    for (int idx = tid; idx < nr * D; idx += kBlock) {
-      const int r = idx / D, i = idx - r * D;
-      float y = 0.f;
+      if (tid < nr) {
+        float sum = 0.f, mrow = 0.f;
 #pragma unroll
-      for (int h = 0; h < TSP; ++h) y += yb[(h * NRW + r) * D + i];
-      pbase[(size_t)r * (D + 2) + i] = y * osc;
-    }
-  }
-  if (tid < nr) {
-    float sum = 0.f;
+        for (int w = 0; w < NW; ++w) sum += ered[w][tid];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) sum += red[w][tid];
-    pbase[(size_t)tid * (D + 2) + D] = rmax[tid];
-    pbase[(size_t)tid * (D + 2) + D + 1] = sum;
+        for (int r = 0; r < NRW; ++r)
+          if (r == tid) mrow = rm[r];
+        pbase[(size_t)tid * (D + 2) + D] = mrow;
+        pbase[(size_t)tid * (D + 2) + D + 1] = sum;
+      }
+#pragma unroll
+      for (int r = 0; r < NRW; ++r) {
+        rm[r] = -INFINITY;
+        esum[r] = 0.f;
+      }
+      nsc = 0.f;
+    }
   }
 }
 
@@ -2614,12 +2730,18 @@ __global__ void __launch_bounds__(kBlock) attend_combine_kernel(AttnArgs a, int6
 template <int D, int RQ>
 static void launch_attend_rq(const AttnArgs& aa, int64_t n_groups, hipStream_t st) {
   const int64_t qtiles = (aa.nq_per_group + 4 * RQ - 1) / (4 * RQ);
-  const dim3 g1((unsigned)aa.n_chunks, (unsigned)n_groups, (unsigned)qtiles);
+  // up to 4 chunks per workgroup while at least 2048 workgroups remain
+  AttnArgs ab = aa;
+  ab.chunks_per_block = 1;
+  while (ab.chunks_per_block < 4 && aa.n_chunks * n_groups * qtiles / (2 * ab.chunks_per_block) >= 2048)
+    ab.chunks_per_block *= 2;
+  const dim3 g1((unsigned)((aa.n_chunks + ab.chunks_per_block - 1) / ab.chunks_per_block),
+                (unsigned)n_groups, (unsigned)qtiles);
   switch (aa.s.R) {
-    case 1: hipLaunchKernelGGL((attend_mfma_kernel<D, 1, RQ>), g1, dim3(kBlock), 0, st, aa); break;
-    case 2: hipLaunchKernelGGL((attend_mfma_kernel<D, 2, RQ>), g1, dim3(kBlock), 0, st, aa); break;
-    case 3: hipLaunchKernelGGL((attend_mfma_kernel<D, 3, RQ>), g1, dim3(kBlock), 0, st, aa); break;
-    default: hipLaunchKernelGGL((attend_mfma_kernel<D, 4, RQ>), g1, dim3(kBlock), 0, st, aa); break;
+    case 1: hipLaunchKernelGGL((attend_mfma_kernel<D, 1, RQ>), g1, dim3(kBlock), 0, st, ab); break;
+    case 2: hipLaunchKernelGGL((attend_mfma_kernel<D, 2, RQ>), g1, dim3(kBlock), 0, st, ab); break;
+    case 3: hipLaunchKernelGGL((attend_mfma_kernel<D, 3, RQ>), g1, dim3(kBlock), 0, st, ab); break;
+    default: hipLaunchKernelGGL((attend_mfma_kernel<D, 4, RQ>), g1, dim3(kBlock), 0, st, ab); break;
   }
 }
 
@@ -2651,6 +2773,7 @@ int launch_attend(const PlanDev& p, const float* logits, int64_t nq_per_group, i
   aa.codes = codes;
   aa.rec_bytes = p.rec_bytes;
   aa.n_chunks = (n + kAttnChunk - 1) / kAttnChunk;
+  aa.chunks_per_block = 1;
   aa.out = out;
   aa.ldo = ldo;
   aa.out_bf16 = dt == TQ_BF16;

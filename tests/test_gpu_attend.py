@@ -91,3 +91,30 @@ def test_attend_rejects_split_plans_and_bad_sizes():
     vc = torch.zeros((10, plan.record_bytes), dtype=torch.uint8, device=DEV)
     with pytest.raises(tq.TqError):
         tq.tq_attend(plan, torch.zeros((2, 10), device=DEV), vc, 10, 1.0)
+
+
+@pytest.mark.parametrize("d,bits,n,nqg", [(128, 3, 4 * 1024 + 500, 4), (32, 1, 3 * 1024 + 100, 1),
+                                          (64, 2, 2 * 1024 + 7, 6)])
+def test_attend_many_groups_streams_several_chunks_per_workgroup(d, bits, n, nqg):
+    """2048 groups: enough work that one workgroup streams several consecutive chunks (with
+    the running max and norm scale carried across stages and reset per chunk); sampled groups
+    against the oracle, the ragged last chunk included."""
+    groups = 2048
+    g = torch.Generator(device=DEV)
+    g.manual_seed(d + n)
+    V = torch.randn((groups * n, d), generator=g, device=DEV).to(torch.bfloat16)
+    # a few large norms late in the sequence, so that the norm scale rises mid-chunk
+    V[torch.arange(700, groups * n, 1537, device=DEV)] *= 40
+    L = torch.randn((groups * nqg, n), generator=g, device=DEV) * 4
+    L[:, 2000:2100] += 6          # the max of a row moves up in a later stage
+    plan, op = tq.tq_plan_create_mse(d, bits, 3), otq.make_mse_plan(d, bits, 3)
+    vc = tq.tq_encode(plan, V)
+    out = tq.tq_attend(plan, L, vc, n, 0.7, nq_per_group=nqg, n_groups=groups)
+    torch.cuda.synchronize()
+    for grp in (0, 1, 1000, groups - 1):
+        c = vc[grp * n:(grp + 1) * n].cpu().numpy()
+        st = layout.unpack_mse(c, op.D, op.R)
+        Lg = _np(L[grp * nqg:(grp + 1) * nqg])
+        ref = otq.attend(op, Lg, st, 0.7, nqg)
+        vmax = np.max(np.linalg.norm(otq.dequantize(op, st), axis=1))
+        _check(_np(out[grp * nqg:(grp + 1) * nqg]), ref, vmax, False, "group %d" % grp)
