@@ -2283,7 +2283,8 @@ struct AttnArgs {
   const uint8_t* codes;      // group g's records from g * n
   int rec_bytes;
   int64_t n_chunks;
-  int64_t chunks_per_block;  // consecutive chunks streamed by one workgroup
+  int64_t chunks_per_block;  // consecutive chunks streamed by one workgroup (or wave)
+  int64_t n_groups;
   float* part;               // [chunk][row][D + 2]: y, then max, then sum
   void* out;
   int64_t ldo;
@@ -2305,6 +2306,94 @@ constexpr int attn_stage_tokens(int wpt) {
   return t;
 }
 
+// One 16-token block of the contraction.  A: lane row am = (parity, limb, row) takes the weight
+// limb of its row for its 4 tokens into its parity's K slots; B: per token, the pair fields of
+// ST tiles from one shift and mask per plane word, each field the byte offset (or index) of
+// a pair-table entry.  wl: [limb][row][token] fp16 (row stride wls); sw: [chunk][plane][token]
+// words (row stride sws); tok: the block's first token in the staging; tile0: this lane's
+// first column tile.
+template <int R, int RQ, int TW, int ST, int LPC>
+__device__ __forceinline__ void attn_contract16(f32x4 (&acc)[RQ][TW], const uint16_t* wl, int wls,
+                                                int nrw, const uint32_t* sw, int sws, int tok,
+                                                int tile0, int lane, const unsigned char* tab) {
+  constexpr int FW = 2 * LPC;
+  constexpr int NPAIR = 1 << (2 * R);
+  constexpr int SH = 2 * R + 2 <= FW ? 2 : 0;
+  constexpr uint32_t FMASK = (1u << (2 * R + SH)) - 1u;
+  uint32_t pm = 0;
+#pragma unroll
+  for (int j = 0; j < ST; ++j) pm |= 3u << (FW * j);
+  const int col = lane & 15, G = lane >> 4;
+  const int am = lane & 15, ap = am >> 3, alimb = (am >> 2) & 1, ar = am & 3;
+  const uint32_t sel_a = ap ? 0x01000C0Cu : 0x0C0C0100u;
+  const uint32_t sel_b = ap ? 0x03020C0Cu : 0x0C0C0302u;
+  const int psh = 2 * (col % LPC);
+  f16x8 A[RQ];
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) {
+    const uint2 x = *reinterpret_cast<const uint2*>(&wl[(alimb * nrw + 4 * q + ar) * wls + tok + 4 * G]);
+    A[q] = f16x8_from_words(__builtin_amdgcn_perm(0u, x.x, sel_a), __builtin_amdgcn_perm(0u, x.x, sel_b),
+                            __builtin_amdgcn_perm(0u, x.y, sel_a), __builtin_amdgcn_perm(0u, x.y, sel_b));
+  }
+#pragma unroll
+  for (int st = 0; st < TW / ST; ++st) {
+    const int cch = tile0 + st * ST + col / LPC;      // this lane's chunk
+    uint4 wd[R];
+#pragma unroll
+    for (int m = 0; m < R; ++m)
+      wd[m] = *reinterpret_cast<const uint4*>(&sw[(cch * R + m) * sws + tok + 4 * G]);
+    uint32_t P[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint32_t v = 0;
+#pragma unroll
+      for (int m = 0; m < R; ++m) {
+        const uint32_t wv = u == 0 ? wd[m].x : u == 1 ? wd[m].y : u == 2 ? wd[m].z : wd[m].w;
+        v |= ((wv >> psh) & pm) << (2 * m + SH);
+      }
+      P[u] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < ST; ++j) {
+      uint32_t hw[4], lw[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t off = SH ? (P[u] >> (FW * j)) & FMASK : ((P[u] >> (FW * j)) & FMASK) << 2;
+        hw[u] = *reinterpret_cast<const uint32_t*>(tab + off);
+        lw[u] = *reinterpret_cast<const uint32_t*>(tab + NPAIR * 4 + off);
+      }
+      const f16x8 bh = f16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
+      const f16x8 bl = f16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
+#pragma unroll
+      for (int q = 0; q < RQ; ++q) {
+        acc[q][st * ST + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[q], bh, acc[q][st * ST + j], 0, 0, 0);
+        acc[q][st * ST + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[q], bl, acc[q][st * ST + j], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Pair table in LDS: entry i holds coordinate 2q's level (index bits i_0, i_2, ..) in the
+// low fp16 half and 2q + 1's (bits i_1, i_3, ..) in the high half; high limbs, then low limbs.
+template <int R>
+__device__ __forceinline__ void attn_pair_table(const SubDev& s, uint32_t* ptab) {
+  constexpr int NPAIR = 1 << (2 * R);
+  for (int i = threadIdx.x; i < NPAIR; i += blockDim.x) {
+    int ia = 0, ib = 0;
+#pragma unroll
+    for (int m = 0; m < R; ++m) {
+      ia |= ((i >> (2 * m)) & 1) << m;
+      ib |= ((i >> (2 * m + 1)) & 1) << m;
+    }
+    const float ca = s.lev[ia] * kDequantLevelScale, cb = s.lev[ib] * kDequantLevelScale;
+    typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
+    const f16x2 hv = __builtin_amdgcn_cvt_pkrtz(ca, cb);
+    ptab[i] = __builtin_bit_cast(uint32_t, hv);
+    ptab[NPAIR + i] =
+        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ca - (float)hv[0], cb - (float)hv[1]));
+  }
+}
+
 // A workgroup streams the stages of up to chunks_per_block consecutive chunks of one group and
 // row tile: the next stage's plane words, norms and logits are loaded while the current stage
 // is contracted.  The softmax max and the norm scale are running values over the chunk (as in
@@ -2317,7 +2406,6 @@ attend_mfma_kernel(AttnArgs a) {
   constexpr int NJT = D / 32;                       // column tiles of 16 pairs = chunks
   constexpr int ST = NJT < 4 ? NJT : 4;             // tiles sharing a lane's chunk
   constexpr int LPC = 16 / ST;                      // columns per chunk within those tiles
-  constexpr int FW = 2 * LPC;                       // bits between the pairs of those tiles
   constexpr int TW = NJT < 16 / RQ ? NJT : 16 / RQ; // tiles per wave
   constexpr int NTG = NJT / TW;                     // tile groups
   static_assert(NTG <= NW && TW % ST == 0, "tile split");
@@ -2339,12 +2427,6 @@ attend_mfma_kernel(AttnArgs a) {
   constexpr int RED_BYTES = TSP > 1 ? TSP * NRW * D * 4 : 0;
   constexpr int RAW = STAGE_BYTES > RED_BYTES ? STAGE_BYTES : RED_BYTES;
   constexpr int NPAIR = 1 << (2 * R);
-  // pair fields pre-multiplied by 4 (the byte offset of a table entry) when they fit
-  constexpr int SH = 2 * R + 2 <= FW ? 2 : 0;
-  constexpr uint32_t FMASK = (1u << (2 * R + SH)) - 1u;
-  uint32_t pm = 0;
-  for (int j = 0; j < ST; ++j) pm |= 3u << (FW * j);
-  const uint32_t PMASK = pm;
   __shared__ __attribute__((aligned(16))) unsigned char raw[RAW];
   __shared__ uint32_t ptab[2 * NPAIR];              // high limbs, then low limbs
   __shared__ float red[2][NW][NRW + 1];             // per stage (two in flight): maxima
@@ -2406,29 +2488,9 @@ attend_mfma_kernel(AttnArgs a) {
     }
   };
   load_stage(T0);
-  // pair table: entry i holds coordinate 2q's level (index bits i_0, i_2, ..) in the low
-  // fp16 half and 2q + 1's (bits i_1, i_3, ..) in the high half
-  for (int i = tid; i < NPAIR; i += kBlock) {
-    int ia = 0, ib = 0;
-#pragma unroll
-    for (int m = 0; m < R; ++m) {
-      ia |= ((i >> (2 * m)) & 1) << m;
-      ib |= ((i >> (2 * m + 1)) & 1) << m;
-    }
-    const float ca = s.lev[ia] * kDequantLevelScale, cb2 = s.lev[ib] * kDequantLevelScale;
-    typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
-    const f16x2 hv = __builtin_amdgcn_cvt_pkrtz(ca, cb2);
-    ptab[i] = __builtin_bit_cast(uint32_t, hv);
-    ptab[NPAIR + i] =
-        __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ca - (float)hv[0], cb2 - (float)hv[1]));
-  }
+  attn_pair_table<R>(s, ptab);
   const int col = lane & 15, G = lane >> 4;
   const int tg = wave / TSP, ts = wave % TSP;
-  const int am = lane & 15, ap = am >> 3, alimb = (am >> 2) & 1, ar = am & 3;
-  // A operand: a weight limb into the low (parity 0) or high (parity 1) half of a dword
-  const uint32_t sel_a = ap ? 0x01000C0Cu : 0x0C0C0100u;
-  const uint32_t sel_b = ap ? 0x03020C0Cu : 0x0C0C0302u;
-  const int psh = 2 * (col % LPC);                  // this lane's pair offset in a word
   const unsigned char* tab = reinterpret_cast<const unsigned char*>(ptab);
   float rm[NRW], esum[NRW];                         // running max of scale * logit, partial sums
   float nsc = 0.f;                                  // running max norm
@@ -2524,52 +2586,8 @@ attend_mfma_kernel(AttnArgs a) {
     __syncthreads();
     // ---- the contraction over this stage's tokens ----
     const int nblk = (ns + 15) >> 4;
-    for (int b = ts; b < nblk; b += TSP) {
-      f16x8 A[RQ];
-#pragma unroll
-      for (int q = 0; q < RQ; ++q) {
-        const uint2 x = *reinterpret_cast<const uint2*>(&wl[(alimb * NRW + 4 * q + ar) * WLS + b * 16 + 4 * G]);
-        A[q] = f16x8_from_words(__builtin_amdgcn_perm(0u, x.x, sel_a), __builtin_amdgcn_perm(0u, x.x, sel_b),
-                                __builtin_amdgcn_perm(0u, x.y, sel_a), __builtin_amdgcn_perm(0u, x.y, sel_b));
-      }
-#pragma unroll
-      for (int st = 0; st < TW / ST; ++st) {
-        const int cch = tg * TW + st * ST + col / LPC;      // this lane's chunk
-        uint4 wd[R];
-#pragma unroll
-        for (int m = 0; m < R; ++m)
-          wd[m] = *reinterpret_cast<const uint4*>(&sw[(cch * R + m) * SWS + b * 16 + 4 * G]);
-        // per token: the pair fields of all ST tiles at once (tile j at bit FW j)
-        uint32_t P[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          uint32_t v = 0;
-#pragma unroll
-          for (int m = 0; m < R; ++m) {
-            const uint32_t wv = u == 0 ? wd[m].x : u == 1 ? wd[m].y : u == 2 ? wd[m].z : wd[m].w;
-            v |= ((wv >> psh) & PMASK) << (2 * m + SH);
-          }
-          P[u] = v;
-        }
-#pragma unroll
-        for (int j = 0; j < ST; ++j) {
-          uint32_t hw[4], lw[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const uint32_t off = SH ? (P[u] >> (FW * j)) & FMASK : ((P[u] >> (FW * j)) & FMASK) << 2;
-            hw[u] = *reinterpret_cast<const uint32_t*>(tab + off);
-            lw[u] = *reinterpret_cast<const uint32_t*>(tab + NPAIR * 4 + off);
-          }
-          const f16x8 bh = f16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
-          const f16x8 bl = f16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
-#pragma unroll
-          for (int q = 0; q < RQ; ++q) {
-            acc[q][st * ST + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[q], bh, acc[q][st * ST + j], 0, 0, 0);
-            acc[q][st * ST + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[q], bl, acc[q][st * ST + j], 0, 0, 0);
-          }
-        }
-      }
-    }
+    for (int b = ts; b < nblk; b += TSP)
+      attn_contract16<R, RQ, TW, ST, LPC>(acc, wl, WLS, NRW, sw, SWS, b * 16, tg * TW, lane, tab);
     // ---- end of a chunk: its partial sums (lane groups G = 2p and 2p + 1 hold the high
     // and low weight limbs of parity p), then a fresh start for the next chunk ----
     const int64_t Se = S + ns;
@@ -2634,6 +2652,206 @@ attend_mfma_kernel(AttnArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < NRW; ++r) {
+        rm[r] = -INFINITY;
+        esum[r] = 0.f;
+      }
+      nsc = 0.f;
+    }
+  }
+}
+
+// D <= 256: each wave owns every column tile of its tokens, so waves need not meet.  A wave
+// streams its own run of consecutive chunks (one work item: chunks_per_block chunks of one
+// group and row tile) through a private LDS region, in stages of up to 64 tokens whose plane
+// words, norms and logits load while the previous stage is contracted; maxima are wave
+// reductions; each chunk's partial is written by the wave itself.  The only workgroup
+// barrier follows the pair table.
+template <int D, int R, int RQ>
+__global__ void __launch_bounds__(kBlock)
+__attribute__((amdgpu_waves_per_eu(RQ == 1 && D <= 128 && R <= 3 ? 4 : 1))) attend_wave_kernel(AttnArgs a, int64_t n_seq, int64_t n_items) {
+  constexpr int NW = kBlock / kWave;
+  constexpr int NJT = D / 32;
+  constexpr int ST = NJT < 4 ? NJT : 4;
+  constexpr int LPC = 16 / ST;
+  constexpr int TW = NJT;
+  static_assert(TW * RQ <= 16 && TW % ST == 0, "tiles per wave");
+  constexpr int CMW = NJT * R;
+  constexpr int WPT = CMW + 1;                      // plane words and the norm
+  constexpr int CMWP = attn_pow2_at_least(WPT);
+  static_assert(CMWP <= kWave, "words per token");
+  constexpr int TPI = kWave / CMWP;                 // tokens per staging step
+  constexpr int TSW = 16 * TPI < 64 ? 16 * TPI : 64;   // tokens per stage (at most 16 loads)
+  constexpr int NLD = TSW / TPI;
+  constexpr int SWS = TSW + 4;
+  constexpr int WLS = TSW + 8;
+  constexpr int NRW = 4 * RQ;
+  constexpr int WAVE_BYTES = WPT * SWS * 4 + 2 * NRW * WLS * 2;
+  constexpr int NPAIR = 1 << (2 * R);
+  __shared__ __attribute__((aligned(16))) unsigned char raw[NW * WAVE_BYTES];
+  __shared__ uint32_t ptab[2 * NPAIR];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  attn_pair_table<R>(a.s, ptab);
+  __syncthreads();
+  const int64_t item = (int64_t)blockIdx.x * NW + wave;
+  if (item >= n_items) return;
+  uint32_t* sw = reinterpret_cast<uint32_t*>(raw + wave * WAVE_BYTES);
+  const float* snrm = reinterpret_cast<const float*>(sw + CMW * SWS);
+  uint16_t* wl = reinterpret_cast<uint16_t*>(raw + wave * WAVE_BYTES + WPT * SWS * 4);
+  const unsigned char* tab = reinterpret_cast<const unsigned char*>(ptab);
+  const SubDev& s = a.s;
+  const int W = s.mse ? R : R + 1;
+  const int rb = a.rec_bytes;
+  const int64_t seq = item % n_seq, rest = item / n_seq;
+  const int64_t grp = rest % a.n_groups;
+  const int64_t q0 = (rest / a.n_groups) * NRW;
+  const int nr = (int)((a.nq_per_group - q0) < NRW ? (a.nq_per_group - q0) : NRW);
+  const int64_t cb = seq * a.chunks_per_block;
+  const int64_t ce = (cb + a.chunks_per_block) < a.n_chunks ? cb + a.chunks_per_block : a.n_chunks;
+  const int64_t T0 = cb * kAttnChunk;
+  const int64_t T1 = (ce * kAttnChunk) < a.n ? ce * kAttnChunk : a.n;
+  const uint8_t* gcodes = a.codes + grp * a.n * (int64_t)rb + s.rec_off;
+  const float* glg = a.logits + (grp * a.nq_per_group + q0) * a.n;
+  // staging roles: lane (tt, slot); full stages load unconditionally
+  const int stt = lane / CMWP, sl = lane % CMWP;
+  const int scw = sl < WPT ? sl : 0;
+  const int sword = scw == CMW ? NJT * W : (scw / R) * W + scw % R;
+  const uint32_t svoff = (uint32_t)(stt * rb + sword * 4);
+  uint32_t pw[NLD];
+  float pl[NRW];
+  auto load_stage = [&](int64_t S) {
+    const int ns = (T1 - S) < TSW ? (int)(T1 - S) : TSW;
+    const uint8_t* b0 = gcodes + S * rb;
+    if (ns == TSW) {
+#pragma unroll
+      for (int k = 0; k < NLD; ++k)
+        pw[k] = *reinterpret_cast<const uint32_t*>(b0 + (int64_t)(TPI * k) * rb + svoff);
+    } else {
+#pragma unroll
+      for (int k = 0; k < NLD; ++k)
+        pw[k] = stt + TPI * k < ns
+                    ? *reinterpret_cast<const uint32_t*>(b0 + (int64_t)(TPI * k) * rb + svoff)
+                    : 0u;
+    }
+    const int tc = lane < ns ? lane : ns - 1;
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+      const int rc = r < nr ? r : nr - 1;
+      pl[r] = fminf(a.scale * glg[rc * a.n + S + tc], (lane < ns && r < nr) ? INFINITY : -INFINITY);
+    }
+  };
+  load_stage(T0);
+  float rm[NRW], esum[NRW];
+  float nsc = 0.f;
+#pragma unroll
+  for (int r = 0; r < NRW; ++r) {
+    rm[r] = -INFINITY;
+    esum[r] = 0.f;
+  }
+  f32x4 acc[RQ][TW];
+#pragma unroll
+  for (int q = 0; q < RQ; ++q)
+#pragma unroll
+    for (int t = 0; t < TW; ++t) acc[q][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int64_t S = T0; S < T1; S += TSW) {
+    const int ns = (T1 - S) < TSW ? (int)(T1 - S) : TSW;
+    // ---- words and norms into this wave's LDS; the stage maxima by wave reductions ----
+    __builtin_amdgcn_wave_barrier();      // the previous stage's LDS reads precede these writes
+    float nm = 0.f;
+#pragma unroll
+    for (int k = 0; k < NLD; ++k) {
+      if (sl < WPT) {
+        sw[sl * SWS + stt + TPI * k] = pw[k];
+        if (sl == CMW) nm = fmaxf(nm, __uint_as_float(pw[k]));
+      }
+    }
+    float mx[NRW];
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) mx[r] = pl[r];
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+      nm = fmaxf(nm, __shfl_xor(nm, m));
+#pragma unroll
+      for (int r = 0; r < NRW; ++r) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], m));
+    }
+    const float nn = fmaxf(nsc, nm);
+    bool changed = nn != nsc;
+    float fr[NRW];
+#pragma unroll
+    for (int r = 0; r < NRW; ++r) {
+      const float mn = fmaxf(rm[r], mx[r]);
+      const float fe = (r < nr && mn != rm[r]) ? __expf(rm[r] - mn) : 1.f;
+      changed |= fe != 1.f;
+      esum[r] *= fe;
+      fr[r] = fe * (nsc > 0.f ? nsc / nn : 1.f);
+      rm[r] = mn;
+    }
+    if (changed) {
+#pragma unroll
+      for (int q = 0; q < RQ; ++q)
+#pragma unroll
+        for (int t = 0; t < TW; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[q][t][i] *= fr[4 * q + i];
+    }
+    nsc = nn;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // ---- this lane's token: weights w = exp(scale l - max) n / nsc in two fp16 limbs ----
+    if (lane < TSW) {
+      const float nw = snrm[lane] * (nsc > 0.f ? 1.f / nsc : 0.f);
+#pragma unroll
+      for (int r = 0; r < NRW; ++r) {
+        const float e = r < nr ? __expf(pl[r] - rm[r]) : 0.f;
+        esum[r] += e;
+        const float w = e * nw;
+        typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
+        const f16x2 h = __builtin_amdgcn_cvt_pkrtz(w, 0.f);
+        const f16x2 l = __builtin_amdgcn_cvt_pkrtz(w - (float)h[0], 0.f);
+        wl[r * WLS + lane] = (uint16_t)(__builtin_bit_cast(uint32_t, h) & 0xFFFFu);
+        wl[(NRW + r) * WLS + lane] = (uint16_t)(__builtin_bit_cast(uint32_t, l) & 0xFFFFu);
+      }
+    }
+    if (S + TSW < T1) load_stage(S + TSW);  // in flight during the contraction
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int nblk = (ns + 15) >> 4;
+    for (int b = 0; b < nblk; ++b)
+      attn_contract16<R, RQ, TW, ST, LPC>(acc, wl, WLS, NRW, sw, SWS, b * 16, 0, lane, tab);
+    // ---- end of a chunk: the wave writes its partial and starts afresh ----
+    const int64_t Se = S + ns;
+    if (Se == T1 || Se % kAttnChunk == 0) {
+      const int64_t chunk = (Se - 1) / kAttnChunk;
+      const float osc = nsc / kDequantLevelScale;
+      const size_t rows_total = (size_t)a.nq_per_group * a.n_groups;
+      float* pbase = a.part + ((size_t)chunk * rows_total + (size_t)(grp * a.nq_per_group + q0)) * (D + 2);
+      const int col = lane & 15, G = lane >> 4;
+#pragma unroll
+      for (int q = 0; q < RQ; ++q)
+#pragma unroll
+        for (int t = 0; t < TW; ++t) {
+          f32x4 v = acc[q][t];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] += __shfl_xor(v[i], 16);
+          const int cch = (t / ST) * ST + col / LPC;
+          const int coord = 32 * cch + 2 * ((t % ST) * LPC + col % LPC) + (G >> 1);
+          if ((G & 1) == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * q + i < nr) pbase[(size_t)(4 * q + i) * (D + 2) + coord] = v[i] * osc;
+          }
+          acc[q][t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+#pragma unroll
+      for (int r = 0; r < NRW; ++r) {
+        float e = esum[r];
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) e += __shfl_xor(e, m);
+        if (lane == 0 && r < nr) {
+          pbase[(size_t)r * (D + 2) + D] = rm[r];
+          pbase[(size_t)r * (D + 2) + D + 1] = e;
+        }
         rm[r] = -INFINITY;
         esum[r] = 0.f;
       }
@@ -2745,15 +2963,40 @@ static void launch_attend_rq(const AttnArgs& aa, int64_t n_groups, hipStream_t s
   }
 }
 
+template <int D, int RQ>
+static void launch_attend_wave(const AttnArgs& aa, int64_t n_groups, hipStream_t st) {
+  const int64_t qtiles = (aa.nq_per_group + 4 * RQ - 1) / (4 * RQ);
+  // up to 4 chunks per wave while at least 8192 waves remain
+  AttnArgs ab = aa;
+  ab.chunks_per_block = 1;
+  while (ab.chunks_per_block < 4 && aa.n_chunks * n_groups * qtiles / (2 * ab.chunks_per_block) >= 8192)
+    ab.chunks_per_block *= 2;
+  const int64_t n_seq = (aa.n_chunks + ab.chunks_per_block - 1) / ab.chunks_per_block;
+  const int64_t items = n_seq * n_groups * qtiles;
+  const dim3 g1((unsigned)((items + kBlock / kWave - 1) / (kBlock / kWave)));
+  switch (aa.s.R) {
+    case 1: hipLaunchKernelGGL((attend_wave_kernel<D, 1, RQ>), g1, dim3(kBlock), 0, st, ab, n_seq, items); break;
+    case 2: hipLaunchKernelGGL((attend_wave_kernel<D, 2, RQ>), g1, dim3(kBlock), 0, st, ab, n_seq, items); break;
+    case 3: hipLaunchKernelGGL((attend_wave_kernel<D, 3, RQ>), g1, dim3(kBlock), 0, st, ab, n_seq, items); break;
+    default: hipLaunchKernelGGL((attend_wave_kernel<D, 4, RQ>), g1, dim3(kBlock), 0, st, ab, n_seq, items); break;
+  }
+}
+
 template <int D>
 static int launch_attend_d(const AttnArgs& aa, int64_t n_groups, hipStream_t st) {
   if (aa.s.R < 1 || aa.s.R > 4) return (int)hipErrorInvalidValue;
   // two row quads per workgroup when there are more than 4 rows (one at D = 2048, where the
   // accumulators of 8 rows would not fit a wave's share of the tiles)
-  if (aa.nq_per_group > 4 && D <= 1024)
+  if (D <= 256) {
+    if (aa.nq_per_group > 4)
+      launch_attend_wave<D <= 256 ? D : 256, 2>(aa, n_groups, st);
+    else
+      launch_attend_wave<D <= 256 ? D : 256, 1>(aa, n_groups, st);
+  } else if (aa.nq_per_group > 4 && D <= 1024) {
     launch_attend_rq<D, D <= 1024 ? 2 : 1>(aa, n_groups, st);
-  else
+  } else {
     launch_attend_rq<D, 1>(aa, n_groups, st);
+  }
   const int64_t rows = aa.nq_per_group * n_groups;
   hipLaunchKernelGGL(attend_combine_kernel<D>, dim3((unsigned)rows), dim3(kBlock), 0, st, aa, rows);
   return (int)hipGetLastError();
@@ -2774,6 +3017,7 @@ int launch_attend(const PlanDev& p, const float* logits, int64_t nq_per_group, i
   aa.rec_bytes = p.rec_bytes;
   aa.n_chunks = (n + kAttnChunk - 1) / kAttnChunk;
   aa.chunks_per_block = 1;
+  aa.n_groups = n_groups;
   aa.out = out;
   aa.ldo = ldo;
   aa.out_bf16 = dt == TQ_BF16;
