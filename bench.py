@@ -57,17 +57,17 @@ def parse():
     return ap.parse_args()
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_longctx.json")
 KERNEL_SOURCE = os.path.join(ROOT, "rotation_online_vector_amd", "csrc", "kernels.hip")
 
 
-def measured_traffic(kernel_key):
-    """HBM bytes per launch of `kernel_key` from the stored counter runs (FETCH_SIZE and
-    WRITE_SIZE scaled by a copy of known size), or None when there is no record or the
-    kernel source changed since the counters were taken."""
+def measured_traffic(workload, kernel_key):
+    """HBM bytes per launch of entry point `kernel_key` on `workload` from the stored counter
+    runs (profiles/traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE scaled by a copy of known
+    size), or None when there is no record or the kernel source changed since the counters
+    were taken."""
     import hashlib
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)))
         src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
     except (OSError, ValueError):
         return None
@@ -423,7 +423,7 @@ def main():
         for k, v in kern.items():
             v["tflops"] = flops[k] / (v["ms"] * 1e-3) / 1e12
     else:
-        traffic = measured_traffic(dom) if args.workload == "longctx" else None
+        traffic = measured_traffic(args.workload, dom)
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(kern[dom]["gbs"], 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),
