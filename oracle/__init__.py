@@ -13,6 +13,7 @@ Modules:
   turboquant  encode / query preparation / estimate / top-k; TurboQuant-MSE encode and
               dequantization
   layout      packed byte layout of the codes
+  policy      outlier channels by variance; appending encoded tokens to a cache
 
 Parity status of each function is listed in the module docstrings; the only
 function without an external pin is the exact Philox bit stream (no published

@@ -546,3 +546,48 @@ def test_attend_invariances():
     # the plain definition: softmax weights times the dequantized rows
     w = np.exp(0.7 * L[1] - (0.7 * L[1]).max())
     assert np.allclose(out[1], (w / w.sum()) @ Vh, atol=1e-12)
+
+
+# ---- policy layer: outlier channels by variance, appending tokens -------------------------
+def test_channel_variance_equals_pairwise_difference_form():
+    """Population variance = (1 / (2 n^2)) sum_{i,j} (x_i - x_j)^2, an identity that shares
+    nothing with the mean-based form."""
+    from oracle import policy
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((37, 9)) * rng.uniform(0.1, 5, 9) + rng.uniform(-3, 3, 9)
+    diff = X[:, None, :] - X[None, :, :]
+    ref = (diff ** 2).sum(axis=(0, 1)) / (2 * X.shape[0] ** 2)
+    assert np.allclose(policy.channel_variance(X), ref, rtol=1e-12, atol=0)
+
+
+def test_outlier_channels_planted_shift_invariant_and_ties():
+    from oracle import policy
+    rng = np.random.default_rng(12)
+    X = rng.standard_normal((500, 64))
+    planted = [3, 17, 40, 41, 63]
+    X[:, planted] *= 10
+    ch, mask = policy.outlier_channels(X, 5)
+    assert list(ch) == planted and mask.sum() == 5 and all(mask[planted] == 1)
+    # a per-channel shift changes no variance; a channel permutation permutes the choice
+    ch2, _ = policy.outlier_channels(X + rng.uniform(-100, 100, 64), 5)
+    assert list(ch2) == planted
+    perm = rng.permutation(64)
+    ch3, _ = policy.outlier_channels(X[:, perm], 5)
+    assert sorted(perm[ch3]) == planted
+    # equal variances: the lower channel index wins
+    Y = np.tile(np.array([[1.0], [-1.0]]), (1, 6))
+    Y[:, 4] *= 2
+    ch4, _ = policy.outlier_channels(Y, 3)
+    assert list(ch4) == [0, 1, 4]
+    # n_out = 0 and n_out = d
+    assert policy.outlier_channels(X, 0)[1].sum() == 0
+    assert policy.outlier_channels(X, 64)[1].sum() == 64
+
+
+def test_place_appends_and_drops_out_of_range_rows():
+    from oracle import policy
+    cache = np.zeros((6, 4), dtype=np.uint8)
+    rec = np.arange(12, dtype=np.uint8).reshape(3, 4) + 1
+    out = policy.place(cache, rec, [5, -1, 2])
+    assert np.array_equal(out[5], rec[0]) and np.array_equal(out[2], rec[2])
+    assert out[[0, 1, 3, 4]].sum() == 0 and cache.sum() == 0
