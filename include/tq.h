@@ -232,6 +232,41 @@ tq_status tq_attend(const tq_plan* vplan, const float* logits, int64_t nq_per_gr
                     tq_dtype dt, int64_t ldo, void* stream);
 
 /*
+ * Outlier channels of a head by variance (overview §4.1.1: about a quarter of
+ * a head's channels are kept at a higher bit width; the outliers here are the
+ * channels of largest variance over a calibration sample).  For every channel,
+ * the population variance over the n sample rows in fp64 (two passes: the
+ * mean, then the mean squared deviation, each summed in a fixed order); then
+ * mask[c] = 1 for the n_out channels first in the order (-variance, channel),
+ * 0 for the rest.  The mask, copied to the host, is the outlier_mask of
+ * tq_plan_create.
+ *   x     device, n rows of d elements (dt), row stride ldx elements; finite
+ *   var   device double [d]; mask device uint8 [d]
+ * Uses a stream-ordered temporary of at most 32 MiB.
+ * Limits: n >= 1, 1 <= d <= 65536, 0 <= n_out <= d.
+ * Errors: TQ_EINVAL (range, null, ldx < d, misalignment), TQ_ENOMEM,
+ * TQ_EDEVICE.
+ */
+tq_status tq_calibrate_outliers(const void* x, tq_dtype dt, int64_t n, int64_t ldx, int d,
+                                int n_out, double* var, uint8_t* mask, void* stream);
+
+/*
+ * Streaming append (overview §4.1.2: the cache grows by one record per head
+ * and decode step): encode n vectors as tq_encode does and write record i to
+ * row index[i] of a cache of cache_rows records, e.g. row g * capacity + t for
+ * token t of group g.  Rows outside [0, cache_rows) are skipped; the other
+ * rows of the cache are left as they are; with repeated rows, which record
+ * lands there is unspecified.
+ *   cache  device, cache_rows * record_bytes bytes, 16-byte aligned
+ *   index  device int64 [n]
+ * The records pass through a stream-ordered temporary of n * record_bytes.
+ * Errors: TQ_EINVAL (null with n > 0, n < 0, ldx < d, misalignment),
+ * TQ_ENOMEM, TQ_EDEVICE.  n = 0 is a no-op.
+ */
+tq_status tq_encode_scatter(const tq_plan* plan, const void* x, tq_dtype dt, int64_t n, int64_t ldx,
+                            void* cache, int64_t cache_rows, const int64_t* index, void* stream);
+
+/*
  * Second stage of two-stage retrieval (overview §4.2.2: the quantized first
  * stage screens a top-K, the second refines on the candidates): for each of nq
  * queries, the exact inner products with the full-precision vectors of its kc

@@ -38,8 +38,8 @@ class tq_plan_desc(ctypes.Structure):
 
 EXPORTED = ["tq_status_string", "tq_plan_create", "tq_plan_destroy", "tq_plan_info",
             "tq_plan_create_mse", "tq_encode", "tq_score", "tq_score_topk", "tq_topk",
-            "tq_dequantize", "tq_attend", "tq_rerank", "tq_qjl", "tq_codebook",
-            "tq_rotation_signs", "tq_qjl_matrix"]
+            "tq_dequantize", "tq_attend", "tq_rerank", "tq_calibrate_outliers",
+            "tq_encode_scatter", "tq_qjl", "tq_codebook", "tq_rotation_signs", "tq_qjl_matrix"]
 
 _lib = None
 
@@ -79,6 +79,10 @@ def load_library(path=LIB_PATH):
     lib.tq_attend.restype = i32
     lib.tq_rerank.argtypes = [vp, i32, i64, i64, vp, i32, i64, i64, i32, vp, i32, i32, vp, vp, vp]
     lib.tq_rerank.restype = i32
+    lib.tq_calibrate_outliers.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp]
+    lib.tq_calibrate_outliers.restype = i32
+    lib.tq_encode_scatter.argtypes = [vp, vp, i32, i64, i64, vp, i64, vp, vp]
+    lib.tq_encode_scatter.restype = i32
     lib.tq_dequantize.restype = i32
     lib.tq_score_topk.argtypes = [vp, vp, i32, i64, i64, i64, vp, i64, i32, vp, vp, vp]
     lib.tq_score_topk.restype = i32
@@ -328,6 +332,39 @@ def tq_rerank(q, x, cand, k, ids=None, vals=None, stream=None):
         int(k), ctypes.c_void_p(ids.data_ptr()), ctypes.c_void_p(vals.data_ptr()),
         _stream(stream)))
     return ids, vals
+
+
+def tq_calibrate_outliers(x, n_out, var=None, mask=None, stream=None):
+    """Per-channel variance (fp64) of the rows of x and the mask of its n_out channels of
+    largest variance (ties to the lower channel): (var float64 [d], mask uint8 [d])."""
+    import torch
+    d = x.shape[-1]
+    n, ldx = _rows(x, d)
+    if var is None:
+        var = torch.empty(d, dtype=torch.float64, device=x.device)
+    if mask is None:
+        mask = torch.empty(d, dtype=torch.uint8, device=x.device)
+    _check("tq_calibrate_outliers", load_library().tq_calibrate_outliers(
+        ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ldx, int(d), int(n_out),
+        ctypes.c_void_p(var.data_ptr()), ctypes.c_void_p(mask.data_ptr()), _stream(stream)))
+    return var, mask
+
+
+def tq_encode_scatter(plan, x, cache, index, stream=None):
+    """Encode the rows of x and write record i to row index[i] of cache (uint8
+    [rows, record_bytes]); rows outside the cache are skipped."""
+    import torch
+    n, ld = _rows(x, plan.d)
+    if cache.dtype != torch.uint8 or not cache.is_contiguous() or cache.dim() != 2 or \
+            cache.shape[1] != plan.record_bytes:
+        raise ValueError("cache must be contiguous uint8 [rows, record_bytes]")
+    if index.dtype != torch.int64 or not index.is_contiguous() or index.numel() != n:
+        raise ValueError("index must be contiguous int64 [n]")
+    _check("tq_encode_scatter", load_library().tq_encode_scatter(
+        plan.handle, ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ld,
+        ctypes.c_void_p(cache.data_ptr()), int(cache.shape[0]), ctypes.c_void_p(index.data_ptr()),
+        _stream(stream)))
+    return cache
 
 
 def tq_qjl(plan, subplan, r, beta=None, stream=None):

@@ -3628,4 +3628,121 @@ int launch_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids,
   return hip_rc(hipGetLastError());
 }
 
+// ============================================================================ KV-cache policy
+// Outlier channels by variance (technical overview §4.1.1: about a quarter of a head's channels
+// kept at a higher bit width; here the channels of largest variance over a calibration sample).
+// Two passes over the sample, each writing per-(row block, channel) fp64 partials that a
+// second kernel sums in a fixed order: sum_x, then sum (x - mean)^2; var = that / n.
+constexpr int kVarRows = 256;          // rows per partial
+
+__global__ void __launch_bounds__(kBlock) chan_partial_kernel(const void* x, int x_bf16, int64_t n,
+                                                              int64_t ldx, int d, int64_t rows_per,
+                                                              const double* mean, double* part) {
+  const int c = blockIdx.x * kBlock + threadIdx.x;
+  if (c >= d) return;
+  const int64_t r0 = (int64_t)blockIdx.y * rows_per;
+  const int64_t r1 = (r0 + rows_per) < n ? r0 + rows_per : n;
+  const double mu = mean ? mean[c] : 0.0;
+  double acc = 0.0;
+  for (int64_t r = r0; r < r1; ++r) {
+    const double v = x_bf16 ? (double)__uint_as_float((uint32_t)static_cast<const uint16_t*>(x)[r * ldx + c] << 16)
+                            : (double)static_cast<const float*>(x)[r * ldx + c];
+    acc += mean ? (v - mu) * (v - mu) : v;
+  }
+  part[(size_t)blockIdx.y * d + c] = acc;
+}
+
+__global__ void __launch_bounds__(kBlock) chan_sum_kernel(const double* part, int nblk, int d, int64_t n,
+                                                          double* out) {
+  const int c = blockIdx.x * kBlock + threadIdx.x;
+  if (c >= d) return;
+  double s = 0.0;
+  for (int b = 0; b < nblk; ++b) s += part[(size_t)b * d + c];
+  out[c] = s / (double)n;
+}
+
+// channel i is an outlier when fewer than n_out channels come before it in the order
+// (-variance, channel)
+__global__ void __launch_bounds__(kBlock) outlier_rank_kernel(const double* var, int d, int n_out,
+                                                              uint8_t* mask) {
+  __shared__ double tile[kBlock];
+  const int i = blockIdx.x * kBlock + threadIdx.x;
+  const double vi = i < d ? var[i] : 0.0;
+  int before = 0;
+  for (int j0 = 0; j0 < d; j0 += kBlock) {
+    __syncthreads();
+    tile[threadIdx.x] = j0 + (int)threadIdx.x < d ? var[j0 + threadIdx.x] : 0.0;
+    __syncthreads();
+    const int m = (d - j0) < kBlock ? d - j0 : kBlock;
+    for (int t = 0; t < m; ++t) {
+      const double vj = tile[t];
+      before += (vj > vi || (vj == vi && j0 + t < i)) ? 1 : 0;
+    }
+  }
+  if (i < d) mask[i] = before < n_out ? 1 : 0;
+}
+
+int launch_calibrate_outliers(const void* x, int x_bf16, int64_t n, int64_t ldx, int d, int n_out,
+                              double* var, uint8_t* mask, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  // at most 4 M fp64 partials (32 MiB) and at least kVarRows rows per partial
+  int64_t nblk = (n + kVarRows - 1) / kVarRows;
+  const int64_t cap = ((int64_t)4 << 20) / d > 1 ? ((int64_t)4 << 20) / d : 1;
+  if (nblk > cap) nblk = cap;
+  if (nblk > 65535) nblk = 65535;
+  const int64_t rows_per = (n + nblk - 1) / nblk;
+  nblk = (n + rows_per - 1) / rows_per;
+  double* ws = nullptr;
+  hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&ws), (size_t)(nblk * d + d) * sizeof(double), st);
+  if (e != hipSuccess) return (int)e;
+  double* part = ws;
+  double* mean = ws + nblk * d;
+  const dim3 g((unsigned)((d + kBlock - 1) / kBlock), (unsigned)nblk);
+  const dim3 g1((unsigned)((d + kBlock - 1) / kBlock));
+  hipLaunchKernelGGL(chan_partial_kernel, g, dim3(kBlock), 0, st, x, x_bf16, n, ldx, d, rows_per,
+                     (const double*)nullptr, part);
+  hipLaunchKernelGGL(chan_sum_kernel, g1, dim3(kBlock), 0, st, (const double*)part, (int)nblk, d, n, mean);
+  hipLaunchKernelGGL(chan_partial_kernel, g, dim3(kBlock), 0, st, x, x_bf16, n, ldx, d, rows_per,
+                     (const double*)mean, part);
+  hipLaunchKernelGGL(chan_sum_kernel, g1, dim3(kBlock), 0, st, (const double*)part, (int)nblk, d, n, var);
+  hipLaunchKernelGGL(outlier_rank_kernel, g1, dim3(kBlock), 0, st, (const double*)var, d, n_out, mask);
+  int rc = (int)hipGetLastError();
+  e = hipFreeAsync(ws, st);
+  if (!rc && e != hipSuccess) rc = (int)e;
+  return rc;
+}
+
+// Streaming append (technical overview §4.1.2: the cache grows by one record per head and
+// decode step): records encoded into a temporary are copied to their cache rows, word by word
+// (records are 4-byte multiples); rows outside [0, cap) are skipped.
+__global__ void __launch_bounds__(kBlock) scatter_records_kernel(const uint32_t* src, int64_t n, int words,
+                                                                 const int64_t* index, int64_t cap,
+                                                                 uint32_t* cache) {
+  const int64_t i = (int64_t)blockIdx.x * (kBlock / kWave) + (threadIdx.x >> 6);
+  if (i >= n) return;
+  const int64_t row = index[i];
+  if (row < 0 || row >= cap) return;
+  for (int w = threadIdx.x & 63; w < words; w += kWave) cache[row * words + w] = src[i * words + w];
+}
+
+int launch_encode_scatter(const PlanDev& p, const void* x, int dt, int64_t n, int64_t ldx,
+                          uint8_t* cache, int64_t cap, const int64_t* index, void* stream) {
+  hipStream_t st = (hipStream_t)stream;
+  void* tmp = nullptr;
+  hipError_t e = hipMallocAsync(&tmp, (size_t)n * p.rec_bytes, st);
+  if (e != hipSuccess) return (int)e;
+  int rc = 0;
+  for (int i = 0; i < p.nsub && !rc; ++i)
+    rc = launch_encode(p, i, x, dt, n, ldx, static_cast<uint8_t*>(tmp), stream);
+  if (!rc) {
+    const dim3 g((unsigned)((n + kBlock / kWave - 1) / (kBlock / kWave)));
+    hipLaunchKernelGGL(scatter_records_kernel, g, dim3(kBlock), 0, st, (const uint32_t*)tmp, n,
+                       p.rec_bytes / 4, index, cap, reinterpret_cast<uint32_t*>(cache));
+    rc = (int)hipGetLastError();
+  }
+  e = hipFreeAsync(tmp, st);
+  if (!rc && e != hipSuccess) rc = (int)e;
+  return rc;
+}
+
 }  // namespace tq

@@ -497,6 +497,30 @@ tq_status tq_attend(const tq_plan* vplan, const float* logits, int64_t nq_per_gr
                                 static_cast<const uint8_t*>(vcodes), out, (int)dt, ldo, stream));
 }
 
+tq_status tq_calibrate_outliers(const void* x, tq_dtype dt, int64_t n, int64_t ldx, int d,
+                                int n_out, double* var, uint8_t* mask, void* stream) {
+  if (n < 1 || d < 1 || d > 65536 || n_out < 0 || n_out > d || (dt != TQ_F32 && dt != TQ_BF16))
+    return TQ_EINVAL;
+  const int es = dt == TQ_BF16 ? 2 : 4;
+  if (!x || !var || !mask || ldx < d || (uintptr_t)x % es || (uintptr_t)var % 8) return TQ_EINVAL;
+  int dev;
+  if (hipGetDevice(&dev) != hipSuccess) return TQ_EDEVICE;
+  return from_hip(launch_calibrate_outliers(x, dt == TQ_BF16, n, ldx, d, n_out, var, mask, stream));
+}
+
+tq_status tq_encode_scatter(const tq_plan* plan, const void* x, tq_dtype dt, int64_t n, int64_t ldx,
+                            void* cache, int64_t cache_rows, const int64_t* index, void* stream) {
+  if (!plan || n < 0 || cache_rows < 0 || (dt != TQ_F32 && dt != TQ_BF16)) return TQ_EINVAL;
+  if (n == 0) return TQ_OK;
+  const int es = dt == TQ_BF16 ? 2 : 4;
+  if (!x || !cache || !index || ldx < plan->dev.d || (uintptr_t)x % es || (uintptr_t)cache % 16 ||
+      (uintptr_t)index % 8)
+    return TQ_EINVAL;
+  if (!plan_device_ok(plan)) return TQ_EINVAL;
+  return from_hip(launch_encode_scatter(plan->dev, x, (int)dt, n, ldx, static_cast<uint8_t*>(cache),
+                                        cache_rows, index, stream));
+}
+
 tq_status tq_rerank(const void* q, tq_dtype qdt, int64_t nq, int64_t ldq, const void* x,
                     tq_dtype xdt, int64_t n, int64_t ldx, int d, const int64_t* cand, int kc, int k,
                     int64_t* ids, float* vals, void* stream) {

@@ -81,6 +81,10 @@ int launch_attend(const PlanDev& p, const float* logits, int64_t nq_per_group, i
 int launch_rerank(const void* q, int q_bf16, int64_t nq, int64_t ldq, const void* x, int x_bf16,
                   int64_t n, int64_t ldx, int d, const int64_t* cand, int kc, int k, int64_t* ids,
                   float* vals, void* stream);
+int launch_calibrate_outliers(const void* x, int x_bf16, int64_t n, int64_t ldx, int d, int n_out,
+                              double* var, uint8_t* mask, void* stream);
+int launch_encode_scatter(const PlanDev& p, const void* x, int dt, int64_t n, int64_t ldx,
+                          uint8_t* cache, int64_t cap, const int64_t* index, void* stream);
 int launch_score_topk(const PlanDev& p, const void* q, int dt, int64_t nq_per_group,
                       int64_t n_groups, int64_t ldq, const uint8_t* codes, int64_t n, int k,
                       int64_t* ids, float* vals, void* stream);

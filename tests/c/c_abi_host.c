@@ -77,6 +77,12 @@ int main(void) {
         "rerank with kc > 256");
   CHECK(tq_rerank(NULL, TQ_F32, 0, 64, NULL, TQ_F32, 10, 64, 64, NULL, 8, 4, NULL, NULL, NULL) == TQ_OK,
         "rerank with no queries is a no-op");
+  CHECK(tq_calibrate_outliers(NULL, TQ_F32, 0, 128, 128, 8, NULL, NULL, NULL) == TQ_EINVAL,
+        "calibrate with no rows");
+  CHECK(tq_calibrate_outliers(NULL, TQ_F32, 10, 128, 128, 129, NULL, NULL, NULL) == TQ_EINVAL,
+        "calibrate with n_out > d");
+  CHECK(tq_encode_scatter(NULL, NULL, TQ_BF16, 1, 128, NULL, 10, NULL, NULL) == TQ_EINVAL,
+        "scatter without plan");
   tq_plan_destroy(NULL);
   printf("all passed\n");
   return 0;
