@@ -9,13 +9,14 @@ the streaming estimator).  Inputs are resident in HBM before timing starts.
                     [--copy-calibration MIB] [--workload NAME]
 
 `--workload` selects one of the other synthetic shapes (kv, split35, split25,
-retrieval, retrieval2, small, mse); their step is encode + score (+ top-k for
+retrieval, retrieval2, small, mse, attend, decode); their step is encode + score (+ top-k for
 `small`; one fused score + top-k call for `retrieval`, whose roofline is the
 MFMA one; `retrieval2` adds the exact re-rank of a quantized top-64; for `mse`,
 TurboQuant-MSE encode + dequantize of the long-context keys, counted in
 vectors/s; `attend` is one decode step over the long-context cache held
-quantized, keys scored and values attended, counted in (query, token) pairs/s)
-and the line carries the same fields, without the CPU leg; the two retrieval
+quantized, keys scored and values attended, counted in (query, token) pairs/s;
+`decode` is the whole decode step over that cache, one token per head appended
+to both caches, then scoring and attention, counted in steps/s) and the line carries the same fields, without the CPU leg; the two retrieval
 lines also report recall@10 against an exact fp32 search.
 
 Prints one JSON line.  `value` is scores per second over whole steps; the
@@ -46,7 +47,7 @@ def parse():
     ap.add_argument("--cpu-sample-groups", type=int, default=16)
     ap.add_argument("--workload", default="longctx",
                     choices=["longctx", "kv", "split35", "split25", "retrieval", "retrieval2",
-                             "small", "mse", "attend"],
+                             "small", "mse", "attend", "decode"],
                     help="long-context decode (default, the headline line); the other shapes "
                          "report the same fields for their own step (no CPU leg)")
     ap.add_argument("--no-hbm-ceiling", action="store_true",
@@ -183,6 +184,52 @@ def build_workload(name, dev, W_all):
             value=(n_keys, "vectors/s",
                    "TurboQuant-MSE encode + dequantize vectors/sec (d=128, 3-bit)"),
             keep=(plan, keys, codes, xh))
+    if name == "decode":
+        keys, queries, _ = workloads.longctx_inputs(dev)
+        vals, _, _ = workloads.longctx_inputs(dev, seed=W["v_seed"])
+        n_seq, n_kv, n_tok, d, G = W["n_seq"], W["n_kv"], W["n_tok"], W["d"], W["group"]
+        n_keys, n_groups = n_seq * n_kv * n_tok, n_seq * n_kv
+        kplan = tq.tq_plan_create(d, W["bits"], W["seed"])
+        vplan = tq.tq_plan_create_mse(d, W["v_bits"], W["v_seed"])
+        kcodes = tq.tq_encode(kplan, keys.view(n_keys, d))
+        vcodes = tq.tq_encode(vplan, vals.view(n_keys, d))
+        # the step's new tokens: row n_tok - 1 of every group, appended in place
+        gidx = torch.arange(n_groups, device=dev, dtype=torch.int64) * n_tok + (n_tok - 1)
+        new_k = keys.view(n_keys, d)[gidx].clone()
+        new_v = vals.view(n_keys, d)[gidx].clone()
+        del keys, vals
+        rows = n_groups * G
+        logits = torch.empty((rows, n_tok), dtype=torch.float32, device=dev)
+        out = torch.empty((rows, d), dtype=torch.bfloat16, device=dev)
+        qv = queries.view(rows, d)
+        n_scores = rows * n_tok
+        krb, vrb = kplan.record_bytes, vplan.record_bytes
+
+        def append():
+            tq.tq_encode_scatter(kplan, new_k, kcodes, gidx)
+            tq.tq_encode_scatter(vplan, new_v, vcodes, gidx)
+        return dict(
+            config={"workload": W["name"], "n_seq": n_seq, "kv_heads": n_kv, "tokens": n_tok,
+                    "d": d, "k_bits": W["bits"], "v_bits": W["v_bits"], "v_mode": "mse",
+                    "query_heads_per_seq": n_kv * G, "gqa_group": G, "keys_per_step": n_groups,
+                    "scores_per_step": n_scores, "record_bytes": krb + vrb,
+                    "k_record_bytes": krb, "v_record_bytes": vrb, "cache_tokens": n_keys,
+                    "cache_bytes": n_keys * (krb + vrb),
+                    "append": "one token per (sequence, KV head) to both caches per step"},
+            phases=[("tq_encode_scatter", append),
+                    ("tq_score", lambda: tq.tq_score(kplan, qv, kcodes, n=n_tok, nq_per_group=G,
+                                                     n_groups=n_groups, scores=logits)),
+                    ("tq_attend", lambda: tq.tq_attend(vplan, logits, vcodes, n_tok,
+                                                       1.0 / math.sqrt(d), nq_per_group=G,
+                                                       n_groups=n_groups, out=out))],
+            bytes={"tq_encode_scatter": n_groups * (4 * d + krb + vrb + 16),
+                   "tq_score": n_keys * krb + n_scores * 4 + rows * d * 2,
+                   "tq_attend": n_keys * vrb + n_scores * 4 + rows * d * 2},
+            n_keys=n_groups, n_scores=n_scores,
+            value=(1, "steps/s",
+                   "decode steps/sec over a quantized KV cache (d=128, 16x8x131072 tokens: "
+                   "append 1 token per head, score 3-bit keys, attend 3-bit MSE values)"),
+            keep=(kplan, vplan, queries, kcodes, vcodes, logits, out, new_k, new_v, gidx))
     if name == "attend":
         keys, queries, _ = workloads.longctx_inputs(dev)
         vals, _, _ = workloads.longctx_inputs(dev, seed=W["v_seed"])
@@ -357,14 +404,15 @@ def main():
     W_all = {"longctx": workloads.LONGCTX, "kv": workloads.KV, "split35": workloads.SPLIT,
              "split25": workloads.SPLIT_25, "retrieval": workloads.RETRIEVAL,
              "small": workloads.SMALL, "mse": workloads.MSE_LONGCTX,
-             "attend": workloads.ATTEND_LONGCTX,
+             "attend": workloads.ATTEND_LONGCTX, "decode": workloads.DECODE_LONGCTX,
              "retrieval2": dict(workloads.RETRIEVAL, name=workloads.RETRIEVAL["name"] + "-2stage")}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = build_workload(args.workload, dev, W_all)
     # the code set of the smaller shapes fits the 256 MB Infinity Cache: their GB/s are
     # cache-resident effective rates, not HBM rates
-    code_bytes = wl["config"]["keys_per_step"] * wl["config"]["record_bytes"]
+    code_bytes = wl["config"].get("cache_bytes",
+                                  wl["config"]["keys_per_step"] * wl["config"]["record_bytes"])
     n_value, unit, metric = wl.get("value") or (
         wl["n_scores"], "scores/s",
         "quantized-key scores/sec + HBM GB/s (d=128, 3-bit); encode vectors/sec")
@@ -423,7 +471,8 @@ def main():
         for k, v in kern.items():
             v["tflops"] = flops[k] / (v["ms"] * 1e-3) / 1e12
     else:
-        traffic = measured_traffic(args.workload, dom)
+        # the decode step runs the attention workload's kernels on the same cache
+        traffic = measured_traffic("attend" if args.workload == "decode" else args.workload, dom)
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(kern[dom]["gbs"], 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),

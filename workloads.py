@@ -19,6 +19,8 @@ Shapes (all keys/queries are row vectors of the key dimension):
             6 channels per (sequence, head) drawn Student-t (3 d.o.f.); b = 3
   attend  : the longctx keys (b = 3) and values drawn the same way with seed 1
             (3-bit MSE plan), both held encoded; one decode step scores and attends
+  decode  : the attend caches; a step appends one token per (sequence, KV head) to both
+            caches (at the last slot, so the length stays 131072), then scores and attends
 """
 import numpy as np
 
@@ -39,6 +41,9 @@ MSE_LONGCTX = dict(LONGCTX, name="mse-longctx-16x8x131072x128-bf16-b3")
 # (scored), values under a 3-bit MSE plan (attended), both encoded before the step
 ATTEND_LONGCTX = dict(LONGCTX, name="attend-longctx-16x8x131072x128-k3ip-v3mse",
                       v_bits=3, v_seed=1)
+# a whole decode step over that cache: one new token per (sequence, KV head) appended to the
+# key and value caches (overview §4.1.2), then scoring and attention over all 131072 tokens
+DECODE_LONGCTX = dict(ATTEND_LONGCTX, name="decode-longctx-16x8x131072x128-k3ip-v3mse")
 
 
 def small_inputs(n_keys=4096, n_queries=64, d=128, seed=0):
