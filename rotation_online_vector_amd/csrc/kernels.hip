@@ -2273,6 +2273,7 @@ __global__ void __launch_bounds__(kBlock) topk_merge_kernel(const float* cv, con
 // 16-byte read gives a lane its 4 tokens; a lane keeps one 32-coordinate chunk across up to
 // 4 column tiles (pairs k = j LPC + col % LPC of chunk col / LPC), reusing each word read.
 constexpr int kAttnChunk = 1024;     // tokens per pass-1 workgroup
+constexpr float kAttnSlack = 8.f;    // a logit may exceed its row's reference max by this
 
 struct AttnArgs {
   SubDev s;
@@ -2306,12 +2307,15 @@ constexpr int attn_stage_tokens(int wpt) {
   return t;
 }
 
-// One 16-token block of the contraction.  A: lane row am = (parity, limb, row) takes the weight
-// limb of its row for its 4 tokens into its parity's K slots; B: per token, the pair fields of
-// ST tiles from one shift and mask per plane word, each field the byte offset (or index) of
-// a pair-table entry.  wl: [limb][row][token] fp16 (row stride wls); sw: [chunk][plane][token]
-// words (row stride sws); tok: the block's first token in the staging; tile0: this lane's
-// first column tile.
+// One 16-token block of the contraction, as two MFMAs of 8 tokens per tile.  K slots are
+// (token, level limb) pairs, each a dword holding the two parities: the B dwords of a token
+// are its pair-table entry (high limbs, low limbs) as read, and the A dword of a (token, level
+// limb) slot holds the weight limb of the lane's row in its parity's half (the same for both
+// level limbs), so one product sums w (c_hi + c_lo).  Lane group G takes tokens 4G .. 4G + 3 of
+// the block, 4G + 2h + {0, 1} in half h.  B fields: per token, the pair fields of ST tiles from
+// one shift and mask per plane word, each field the byte offset (or index) of a table entry.
+// wl: [limb][row][token] fp16 (row stride wls); sw: [chunk][plane][token] words (row stride
+// sws); tok: the block's first token in the staging; tile0: this lane's first column tile.
 template <int R, int RQ, int TW, int ST, int LPC>
 __device__ __forceinline__ void attn_contract16(f32x4 (&acc)[RQ][TW], const uint16_t* wl, int wls,
                                                 int nrw, const uint32_t* sw, int sws, int tok,
@@ -2328,12 +2332,16 @@ __device__ __forceinline__ void attn_contract16(f32x4 (&acc)[RQ][TW], const uint
   const uint32_t sel_a = ap ? 0x01000C0Cu : 0x0C0C0100u;
   const uint32_t sel_b = ap ? 0x03020C0Cu : 0x0C0C0302u;
   const int psh = 2 * (col % LPC);
-  f16x8 A[RQ];
+  f16x8 A[2][RQ];
 #pragma unroll
   for (int q = 0; q < RQ; ++q) {
     const uint2 x = *reinterpret_cast<const uint2*>(&wl[(alimb * nrw + 4 * q + ar) * wls + tok + 4 * G]);
-    A[q] = f16x8_from_words(__builtin_amdgcn_perm(0u, x.x, sel_a), __builtin_amdgcn_perm(0u, x.x, sel_b),
-                            __builtin_amdgcn_perm(0u, x.y, sel_a), __builtin_amdgcn_perm(0u, x.y, sel_b));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t xh = h ? x.y : x.x;
+      const uint32_t a0 = __builtin_amdgcn_perm(0u, xh, sel_a), a1 = __builtin_amdgcn_perm(0u, xh, sel_b);
+      A[h][q] = f16x8_from_words(a0, a0, a1, a1);
+    }
   }
 #pragma unroll
   for (int st = 0; st < TW / ST; ++st) {
@@ -2355,19 +2363,20 @@ __device__ __forceinline__ void attn_contract16(f32x4 (&acc)[RQ][TW], const uint
     }
 #pragma unroll
     for (int j = 0; j < ST; ++j) {
-      uint32_t hw[4], lw[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const uint32_t off = SH ? (P[u] >> (FW * j)) & FMASK : ((P[u] >> (FW * j)) & FMASK) << 2;
-        hw[u] = *reinterpret_cast<const uint32_t*>(tab + off);
-        lw[u] = *reinterpret_cast<const uint32_t*>(tab + NPAIR * 4 + off);
-      }
-      const f16x8 bh = f16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
-      const f16x8 bl = f16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
+      for (int h = 0; h < 2; ++h) {
+        uint32_t e[4];
 #pragma unroll
-      for (int q = 0; q < RQ; ++q) {
-        acc[q][st * ST + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[q], bh, acc[q][st * ST + j], 0, 0, 0);
-        acc[q][st * ST + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[q], bl, acc[q][st * ST + j], 0, 0, 0);
+        for (int v = 0; v < 2; ++v) {
+          const uint32_t pu = P[2 * h + v];
+          const uint32_t off = SH ? (pu >> (FW * j)) & FMASK : ((pu >> (FW * j)) & FMASK) << 2;
+          e[2 * v] = *reinterpret_cast<const uint32_t*>(tab + off);
+          e[2 * v + 1] = *reinterpret_cast<const uint32_t*>(tab + NPAIR * 4 + off);
+        }
+        const f16x8 b = f16x8_from_words(e[0], e[1], e[2], e[3]);
+#pragma unroll
+        for (int q = 0; q < RQ; ++q)
+          acc[q][st * ST + j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[h][q], b, acc[q][st * ST + j], 0, 0, 0);
       }
     }
   }
@@ -2687,17 +2696,21 @@ __attribute__((amdgpu_waves_per_eu(RQ == 1 && D <= 128 && R <= 3 ? 4 : 1))) atte
   constexpr int NRW = 4 * RQ;
   constexpr int WAVE_BYTES = WPT * SWS * 4 + 2 * NRW * WLS * 2;
   constexpr int NPAIR = 1 << (2 * R);
-  __shared__ __attribute__((aligned(16))) unsigned char raw[NW * WAVE_BYTES];
-  __shared__ uint32_t ptab[2 * NPAIR];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  attn_pair_table<R>(a.s, ptab);
+  constexpr int PTAB_BYTES = 2 * NPAIR * 4;
+  // one LDS object: the pair table first (so that table reads take immediate offsets), then
+  // the waves' regions
+  __shared__ __attribute__((aligned(16))) unsigned char lds[PTAB_BYTES + NW * WAVE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  attn_pair_table<R>(a.s, reinterpret_cast<uint32_t*>(lds));
   __syncthreads();
   const int64_t item = (int64_t)blockIdx.x * NW + wave;
   if (item >= n_items) return;
+  unsigned char* raw = lds + PTAB_BYTES;
   uint32_t* sw = reinterpret_cast<uint32_t*>(raw + wave * WAVE_BYTES);
   const float* snrm = reinterpret_cast<const float*>(sw + CMW * SWS);
   uint16_t* wl = reinterpret_cast<uint16_t*>(raw + wave * WAVE_BYTES + WPT * SWS * 4);
-  const unsigned char* tab = reinterpret_cast<const unsigned char*>(ptab);
+  const unsigned char* tab = lds;
   const SubDev& s = a.s;
   const int W = s.mse ? R : R + 1;
   const int rb = a.rec_bytes;
@@ -2764,36 +2777,45 @@ __attribute__((amdgpu_waves_per_eu(RQ == 1 && D <= 128 && R <= 3 ? 4 : 1))) atte
         if (sl == CMW) nm = fmaxf(nm, __uint_as_float(pw[k]));
       }
     }
-    float mx[NRW];
+    // The reference max of a row and the norm scale move only when a lane exceeds them (a
+    // logit by more than kAttnSlack): the weights stay below e^kAttnSlack, well inside fp16,
+    // and a stage without a new maximum needs no reduction.  Any reference point is exact:
+    // the partial carries it and the combine weighs chunks by exp(reference - max).
+    bool need = nm > nsc;
 #pragma unroll
-    for (int r = 0; r < NRW; ++r) mx[r] = pl[r];
+    for (int r = 0; r < NRW; ++r) need |= r < nr && pl[r] > rm[r] + kAttnSlack;
+    if (__any(need)) {
+      float mx[NRW];
 #pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-      nm = fmaxf(nm, __shfl_xor(nm, m));
+      for (int r = 0; r < NRW; ++r) mx[r] = pl[r];
 #pragma unroll
-      for (int r = 0; r < NRW; ++r) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], m));
+      for (int m = 32; m >= 1; m >>= 1) {
+        nm = fmaxf(nm, __shfl_xor(nm, m));
+#pragma unroll
+        for (int r = 0; r < NRW; ++r) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], m));
+      }
+      const float nn = fmaxf(nsc, nm);
+      bool changed = nn != nsc;
+      float fr[NRW];
+#pragma unroll
+      for (int r = 0; r < NRW; ++r) {
+        const float mn = fmaxf(rm[r], mx[r]);
+        const float fe = (r < nr && mn != rm[r]) ? __expf(rm[r] - mn) : 1.f;
+        changed |= fe != 1.f;
+        esum[r] *= fe;
+        fr[r] = fe * (nsc > 0.f ? nsc / nn : 1.f);
+        rm[r] = mn;
+      }
+      if (changed) {
+#pragma unroll
+        for (int q = 0; q < RQ; ++q)
+#pragma unroll
+          for (int t = 0; t < TW; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[q][t][i] *= fr[4 * q + i];
+      }
+      nsc = nn;
     }
-    const float nn = fmaxf(nsc, nm);
-    bool changed = nn != nsc;
-    float fr[NRW];
-#pragma unroll
-    for (int r = 0; r < NRW; ++r) {
-      const float mn = fmaxf(rm[r], mx[r]);
-      const float fe = (r < nr && mn != rm[r]) ? __expf(rm[r] - mn) : 1.f;
-      changed |= fe != 1.f;
-      esum[r] *= fe;
-      fr[r] = fe * (nsc > 0.f ? nsc / nn : 1.f);
-      rm[r] = mn;
-    }
-    if (changed) {
-#pragma unroll
-      for (int q = 0; q < RQ; ++q)
-#pragma unroll
-        for (int t = 0; t < TW; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[q][t][i] *= fr[4 * q + i];
-    }
-    nsc = nn;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
