@@ -2734,22 +2734,24 @@ __attribute__((amdgpu_waves_per_eu(RQ == 1 && D <= 128 && R <= 3 ? 4 : 1))) atte
   auto load_stage = [&](int64_t S) {
     const int ns = (T1 - S) < TSW ? (int)(T1 - S) : TSW;
     const uint8_t* b0 = gcodes + S * rb;
+    // (32-bit lane offsets from a uniform base: one load instruction each)
     if (ns == TSW) {
 #pragma unroll
       for (int k = 0; k < NLD; ++k)
-        pw[k] = *reinterpret_cast<const uint32_t*>(b0 + (int64_t)(TPI * k) * rb + svoff);
+        pw[k] = *reinterpret_cast<const uint32_t*>(b0 + (uint32_t)(TPI * k * rb + svoff));
     } else {
 #pragma unroll
       for (int k = 0; k < NLD; ++k)
         pw[k] = stt + TPI * k < ns
-                    ? *reinterpret_cast<const uint32_t*>(b0 + (int64_t)(TPI * k) * rb + svoff)
+                    ? *reinterpret_cast<const uint32_t*>(b0 + (uint32_t)(TPI * k * rb + svoff))
                     : 0u;
     }
-    const int tc = lane < ns ? lane : ns - 1;
+    const uint32_t tc = (uint32_t)(lane < ns ? lane : ns - 1);
 #pragma unroll
     for (int r = 0; r < NRW; ++r) {
       const int rc = r < nr ? r : nr - 1;
-      pl[r] = fminf(a.scale * glg[rc * a.n + S + tc], (lane < ns && r < nr) ? INFINITY : -INFINITY);
+      const float* lr = glg + rc * a.n + S;
+      pl[r] = fminf(a.scale * lr[tc], (lane < ns && r < nr) ? INFINITY : -INFINITY);
     }
   };
   load_stage(T0);
