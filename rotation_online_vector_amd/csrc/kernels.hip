@@ -2316,12 +2316,15 @@ constexpr int attn_stage_tokens(int wpt) {
 // one shift and mask per plane word, each field the byte offset (or index) of a table entry.
 // wl: [limb][row][token] fp16 (row stride wls); sw: [chunk][plane][token] words (row stride
 // sws); tok: the block's first token in the staging; tile0: this lane's first column tile.
-template <int R, int RQ, int TW, int ST, int LPC>
+template <int R, int RQ, int TW, int ST, int LPC, int REP = 1>
 __device__ __forceinline__ void attn_contract16(f32x4 (&acc)[RQ][TW], const uint16_t* wl, int wls,
                                                 int nrw, const uint32_t* sw, int sws, int tok,
                                                 int tile0, int lane, const unsigned char* tab) {
   constexpr int FW = 2 * LPC;
   constexpr int NPAIR = 1 << (2 * R);
+  // REP > 1: entry e of copy c at dword e * REP + c, and lane l reads copy l % REP, so that the
+  // lanes of a table read fall in distinct banks
+  const unsigned char* ltab = tab + (REP > 1 ? (lane % REP) * 4 : 0);
   constexpr int SH = 2 * R + 2 <= FW ? 2 : 0;
   constexpr uint32_t FMASK = (1u << (2 * R + SH)) - 1u;
   uint32_t pm = 0;
@@ -2369,9 +2372,9 @@ __device__ __forceinline__ void attn_contract16(f32x4 (&acc)[RQ][TW], const uint
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
           const uint32_t pu = P[2 * h + v];
-          const uint32_t off = SH ? (pu >> (FW * j)) & FMASK : ((pu >> (FW * j)) & FMASK) << 2;
-          e[2 * v] = *reinterpret_cast<const uint32_t*>(tab + off);
-          e[2 * v + 1] = *reinterpret_cast<const uint32_t*>(tab + NPAIR * 4 + off);
+          const uint32_t off = (SH ? (pu >> (FW * j)) & FMASK : ((pu >> (FW * j)) & FMASK) << 2) * REP;
+          e[2 * v] = *reinterpret_cast<const uint32_t*>(ltab + off);
+          e[2 * v + 1] = *reinterpret_cast<const uint32_t*>(ltab + NPAIR * REP * 4 + off);
         }
         const f16x8 b = f16x8_from_words(e[0], e[1], e[2], e[3]);
 #pragma unroll
@@ -2384,10 +2387,11 @@ __device__ __forceinline__ void attn_contract16(f32x4 (&acc)[RQ][TW], const uint
 
 // Pair table in LDS: entry i holds coordinate 2q's level (index bits i_0, i_2, ..) in the
 // low fp16 half and 2q + 1's (bits i_1, i_3, ..) in the high half; high limbs, then low limbs.
-template <int R>
+template <int R, int REP = 1>
 __device__ __forceinline__ void attn_pair_table(const SubDev& s, uint32_t* ptab) {
   constexpr int NPAIR = 1 << (2 * R);
-  for (int i = threadIdx.x; i < NPAIR; i += blockDim.x) {
+  for (int ic = threadIdx.x; ic < NPAIR * REP; ic += blockDim.x) {
+    const int i = ic / REP;
     int ia = 0, ib = 0;
 #pragma unroll
     for (int m = 0; m < R; ++m) {
@@ -2397,8 +2401,8 @@ __device__ __forceinline__ void attn_pair_table(const SubDev& s, uint32_t* ptab)
     const float ca = s.lev[ia] * kDequantLevelScale, cb = s.lev[ib] * kDequantLevelScale;
     typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
     const f16x2 hv = __builtin_amdgcn_cvt_pkrtz(ca, cb);
-    ptab[i] = __builtin_bit_cast(uint32_t, hv);
-    ptab[NPAIR + i] =
+    ptab[ic] = __builtin_bit_cast(uint32_t, hv);
+    ptab[NPAIR * REP + ic] =
         __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(ca - (float)hv[0], cb - (float)hv[1]));
   }
 }
@@ -2696,13 +2700,14 @@ __attribute__((amdgpu_waves_per_eu(RQ == 1 && D <= 128 && R <= 3 ? 4 : 1))) atte
   constexpr int NRW = 4 * RQ;
   constexpr int WAVE_BYTES = WPT * SWS * 4 + 2 * NRW * WLS * 2;
   constexpr int NPAIR = 1 << (2 * R);
-  constexpr int PTAB_BYTES = 2 * NPAIR * 4;
+  constexpr int REP = R <= 3 ? 32 : 1;               // table copies (at most 16 KiB)
+  constexpr int PTAB_BYTES = 2 * NPAIR * REP * 4;
   // one LDS object: the pair table first (so that table reads take immediate offsets), then
   // the waves' regions
   __shared__ __attribute__((aligned(16))) unsigned char lds[PTAB_BYTES + NW * WAVE_BYTES];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  attn_pair_table<R>(a.s, reinterpret_cast<uint32_t*>(lds));
+  attn_pair_table<R, REP>(a.s, reinterpret_cast<uint32_t*>(lds));
   __syncthreads();
   const int64_t item = (int64_t)blockIdx.x * NW + wave;
   if (item >= n_items) return;
@@ -2842,7 +2847,7 @@ __attribute__((amdgpu_waves_per_eu(RQ == 1 && D <= 128 && R <= 3 ? 4 : 1))) atte
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int nblk = (ns + 15) >> 4;
     for (int b = 0; b < nblk; ++b)
-      attn_contract16<R, RQ, TW, ST, LPC>(acc, wl, WLS, NRW, sw, SWS, b * 16, 0, lane, tab);
+      attn_contract16<R, RQ, TW, ST, LPC, REP>(acc, wl, WLS, NRW, sw, SWS, b * 16, 0, lane, tab);
     // ---- end of a chunk: the wave writes its partial and starts afresh ----
     const int64_t Se = S + ns;
     if (Se == T1 || Se % kAttnChunk == 0) {
