@@ -3016,15 +3016,16 @@ static int launch_attend_d(const AttnArgs& aa, int64_t n_groups, hipStream_t st)
   if (aa.s.R < 1 || aa.s.R > 4) return (int)hipErrorInvalidValue;
   // two row quads per workgroup when there are more than 4 rows (one at D = 2048, where the
   // accumulators of 8 rows would not fit a wave's share of the tiles)
-  if (D <= 256) {
+  if constexpr (D <= 256) {
     if (aa.nq_per_group > 4)
-      launch_attend_wave<D <= 256 ? D : 256, 2>(aa, n_groups, st);
+      launch_attend_wave<D, 2>(aa, n_groups, st);
     else
-      launch_attend_wave<D <= 256 ? D : 256, 1>(aa, n_groups, st);
-  } else if (aa.nq_per_group > 4 && D <= 1024) {
-    launch_attend_rq<D, D <= 1024 ? 2 : 1>(aa, n_groups, st);
+      launch_attend_wave<D, 1>(aa, n_groups, st);
   } else {
-    launch_attend_rq<D, 1>(aa, n_groups, st);
+    if (aa.nq_per_group > 4 && D <= 1024)
+      launch_attend_rq<D, D <= 1024 ? 2 : 1>(aa, n_groups, st);
+    else
+      launch_attend_rq<D, 1>(aa, n_groups, st);
   }
   const int64_t rows = aa.nq_per_group * n_groups;
   hipLaunchKernelGGL(attend_combine_kernel<D>, dim3((unsigned)rows), dim3(kBlock), 0, st, aa, rows);

@@ -30,7 +30,9 @@ def _check(out, ref, vmax, bf16, what):
     (128, 3, 5000, 4, 2, "mse", "float32"), (128, 2, 1024, 8, 1, "mse", "bfloat16"),
     (64, 4, 3000, 12, 1, "mse", "float32"), (256, 3, 2500, 4, 1, "mse", "float32"),
     (2048, 3, 700, 4, 1, "mse", "bfloat16"), (100, 4, 1500, 4, 1, "ip", "float32"),
-    (1, 2, 10, 1, 1, "mse", "float32"), (32, 1, 2049, 3, 3, "mse", "float32")])
+    (1, 2, 10, 1, 1, "mse", "float32"), (32, 1, 2049, 3, 3, "mse", "float32"),
+    (256, 4, 1300, 8, 2, "mse", "float32"), (512, 3, 1100, 7, 1, "ip", "bfloat16"),
+    (1000, 2, 1500, 5, 1, "mse", "float32")])
 def test_attend_matches_oracle(d, bits, n, nqg, groups, mode, dtype):
     rng = np.random.default_rng(d * 11 + n)
     V = rng.standard_normal((groups * n, d)).astype(np.float32)
