@@ -2390,6 +2390,9 @@ __device__ __forceinline__ void attn_contract16(f32x4 (&acc)[RQ][TW], const uint
 template <int R, int REP = 1>
 __device__ __forceinline__ void attn_pair_table(const SubDev& s, uint32_t* ptab) {
   constexpr int NPAIR = 1 << (2 * R);
+  __shared__ float slev[1 << R];                  // the levels, read once per workgroup
+  if (threadIdx.x < (1 << R)) slev[threadIdx.x] = s.lev[threadIdx.x] * kDequantLevelScale;
+  __syncthreads();
   for (int ic = threadIdx.x; ic < NPAIR * REP; ic += blockDim.x) {
     const int i = ic / REP;
     int ia = 0, ib = 0;
@@ -2398,7 +2401,7 @@ __device__ __forceinline__ void attn_pair_table(const SubDev& s, uint32_t* ptab)
       ia |= ((i >> (2 * m)) & 1) << m;
       ib |= ((i >> (2 * m + 1)) & 1) << m;
     }
-    const float ca = s.lev[ia] * kDequantLevelScale, cb = s.lev[ib] * kDequantLevelScale;
+    const float ca = slev[ia], cb = slev[ib];
     typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
     const f16x2 hv = __builtin_amdgcn_cvt_pkrtz(ca, cb);
     ptab[ic] = __builtin_bit_cast(uint32_t, hv);
