@@ -220,8 +220,9 @@ tq_status tq_dequantize(const tq_plan* plan, const void* codes, int64_t n, void*
  *   vcodes  device, n_groups * n records of vplan (group g from record g*n)
  *   out     device, n_groups*nq_per_group rows of d elements (dt), stride ldo
  * Uses a stream-ordered temporary of (D + 2) floats per row and 1024-token
- * chunk.  Limits: n >= 1, n_groups <= 65535, nq_per_group <= 262140, scale
- * finite.  nq_per_group = 0 or n_groups = 0 is a no-op.
+ * chunk.  Limits: n >= 1, n_groups <= 65535, nq_per_group <= 262140,
+ * nq_per_group * n_groups < 2^31, ceil(n / 1024) * nq_per_group * n_groups
+ * <= 2^33, scale finite.  nq_per_group = 0 or n_groups = 0 is a no-op.
  * Errors: TQ_EINVAL (range, null, ldo < d, misalignment: logits 4-byte,
  * vcodes 16-byte, out element-aligned), TQ_ENOMEM, TQ_EDEVICE;
  * TQ_EUNSUPPORTED for a plan with an outlier mask or more than 4 index bits

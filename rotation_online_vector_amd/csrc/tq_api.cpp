@@ -492,6 +492,10 @@ tq_status tq_attend(const tq_plan* vplan, const float* logits, int64_t nq_per_gr
     return TQ_EINVAL;
   if (n_groups > 65535 || (nq_per_group + 3) / 4 > 65535 || (n + 1023) / 1024 > ((int64_t)1 << 31))
     return TQ_EINVAL;
+  // one combine workgroup per query row; at most 4 (chunk run, group, row tile) items per
+  // pass-1 workgroup
+  const int64_t rows = nq_per_group * n_groups;
+  if (rows > 0x7FFFFFFF || ((n + 1023) / 1024) > ((int64_t)1 << 33) / rows) return TQ_EINVAL;
   if (!plan_device_ok(vplan)) return TQ_EINVAL;
   return from_hip(launch_attend(vplan->dev, logits, nq_per_group, n_groups, n, scale,
                                 static_cast<const uint8_t*>(vcodes), out, (int)dt, ldo, stream));

@@ -69,6 +69,19 @@ int main(void) {
   CHECK(tq_dequantize(NULL, NULL, 1, NULL, TQ_F32, 128, NULL) == TQ_EINVAL, "dequantize without plan");
   CHECK(tq_attend(NULL, NULL, 4, 1, 10, 1.0f, NULL, NULL, TQ_F32, 128, NULL) == TQ_EINVAL,
         "attend without plan");
+  {
+    tq_plan* vp = NULL;
+    if (tq_plan_create_mse(128, 3, 1, &vp) == TQ_OK) {
+      /* host-side limits fail before any device use */
+      CHECK(tq_attend(vp, (const float*)16, 262140, 65535, 10, 1.0f, (const void*)16, (void*)16,
+                      TQ_F32, 128, NULL) == TQ_EINVAL,
+            "attend with 2^34 rows");
+      CHECK(tq_attend(vp, (const float*)16, 4, 1, 1, 1.0f / 0.0f, (const void*)16, (void*)16,
+                      TQ_F32, 128, NULL) == TQ_EINVAL,
+            "attend with an infinite scale");
+      tq_plan_destroy(vp);
+    }
+  }
   CHECK(tq_rerank(NULL, TQ_F32, 1, 64, NULL, TQ_F32, 10, 64, 64, NULL, 8, 9, NULL, NULL, NULL) ==
             TQ_EINVAL,
         "rerank with k > kc");
