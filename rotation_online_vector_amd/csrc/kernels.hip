@@ -2906,6 +2906,7 @@ __global__ void __launch_bounds__(kBlock) attend_combine_kernel(AttnArgs a, int6
   const int64_t nch = a.n_chunks;
   auto at = [&](int64_t c) { return a.part + ((size_t)c * rows + row) * (D + 2); };
   float m = -INFINITY;
+#pragma unroll 4
   for (int64_t c = tid; c < nch; c += kBlock) m = fmaxf(m, at(c)[D]);
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
@@ -2920,6 +2921,7 @@ __global__ void __launch_bounds__(kBlock) attend_combine_kernel(AttnArgs a, int6
   __syncthreads();
   const float M = scl[0];
   float sacc = 0.f;
+#pragma unroll 4
   for (int64_t c = tid; c < nch; c += kBlock) sacc += at(c)[D + 1] * __expf(at(c)[D] - M);
 #pragma unroll
   for (int k = 32; k >= 1; k >>= 1) sacc += __shfl_xor(sacc, k);
@@ -2935,6 +2937,7 @@ __global__ void __launch_bounds__(kBlock) attend_combine_kernel(AttnArgs a, int6
   if (TPC > 1) {
     const int i = tid % D, h = tid / D;
     float t = 0.f;
+#pragma unroll 8
     for (int64_t c = h; c < nch; c += TPC) t = fmaf(at(c)[i], __expf(at(c)[D] - M), t);
     sub[h][i] = t;
     __syncthreads();
@@ -2947,6 +2950,7 @@ __global__ void __launch_bounds__(kBlock) attend_combine_kernel(AttnArgs a, int6
   } else {
     for (int i = tid; i < D; i += kBlock) {
       float t = 0.f;
+#pragma unroll 8
       for (int64_t c = 0; c < nch; ++c) t = fmaf(at(c)[i], __expf(at(c)[D] - M), t);
       y[i] = t;
     }

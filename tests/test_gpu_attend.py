@@ -120,3 +120,14 @@ def test_attend_many_groups_streams_several_chunks_per_workgroup(d, bits, n, nqg
         ref = otq.attend(op, Lg, st, 0.7, nqg)
         vmax = np.max(np.linalg.norm(otq.dequantize(op, st), axis=1))
         _check(_np(out[grp * nqg:(grp + 1) * nqg]), ref, vmax, False, "group %d" % grp)
+
+
+def test_attend_zero_values_give_zero_rows():
+    """Values that are all zero vectors (norm 0): every output row is exactly 0."""
+    d, n = 128, 2500
+    plan = tq.tq_plan_create_mse(d, 3, 1)
+    vc = tq.tq_encode(plan, torch.zeros((n, d), device=DEV))
+    L = torch.randn((4, n), device=DEV)
+    out = tq.tq_attend(plan, L, vc, n, 1.0)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
