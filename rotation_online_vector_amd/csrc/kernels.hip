@@ -2257,22 +2257,24 @@ __global__ void __launch_bounds__(kBlock) topk_merge_kernel(const float* cv, con
 // so out[r] = Pi^T (sum_j p_j n_j c[idx_j]): the weighted centroids are summed in the rotated
 // domain and the rotation is undone once per row (technical overview §4.1.2 dequantizes the
 // cache for the attention step; here that dequantization folds into one transform per row).
-// Pass 1, per (1024-token chunk, group, up to 8 query rows): the chunk's max of scale * logit
-// per row, the sum of exp(scale * l - max), and the partial sums y[r][i] (fp32).
-// Pass 2, per row: chunks merged with exp(m_c - M) factors (as in split-token decoding),
-// then Pi^T in LDS, the 1/sum and D^(-3/2) scale, and the first d coordinates stored.
+// Pass 1, per 1024-token chunk and query row: a reference point m of scale * logit (the
+// chunk's max, or up to kAttnSlack below it), the sum of exp(scale * l - m), and the partial
+// sums y[r][i] relative to m (fp32).  Pass 2, per row: chunks merged with exp(m_c - M) factors,
+// M the largest reference (as in split-token decoding), then Pi^T in LDS, the 1/sum and
+// D^(-3/2) scale, and the first d coordinates stored.
 //
 // Pass 1 is a contraction over tokens on the matrix cores (16x16x32 fp16, fp32 accumulation):
-//   y[r][2q + p] = sum_j w[r][j] c(j, 2q + p),   w = exp(scale * l - max) n_j / max_j n_j.
-// Output row m of an MFMA tile is (parity p, weight limb, query row): the A operand holds the
-// limb of w[r][j] in the K slot (token j, parity p) and zero in the slot of the other parity,
-// so the B operand's dword for token j is exactly the pair-table entry (c of coordinate 2q in
-// the low half, 2q + 1 in the high half).  Both operands are split in two fp16 limbs (w in
-// [0, 1]; c scaled by 2^10), the four limb products are exact and summed in fp32.  The plane
-// words of a stage of tokens are held in LDS token-contiguous ([chunk][plane][token]), so one
-// 16-byte read gives a lane its 4 tokens; a lane keeps one 32-coordinate chunk across up to
-// 4 column tiles (pairs k = j LPC + col % LPC of chunk col / LPC), reusing each word read.
-constexpr int kAttnChunk = 1024;     // tokens per pass-1 workgroup
+//   y[r][2q + p] = sum_j w[r][j] c(j, 2q + p),   w = exp(scale * l - m) n_j / nsc,
+// nsc the largest norm seen in the chunk so far.  Output row m of an MFMA tile is (parity p,
+// weight limb, query row); K slots are (token, level limb) pairs whose dwords hold the two
+// parities, so a token's B dwords are its pair-table entry (levels of coordinates 2q and
+// 2q + 1, high limbs then low limbs) as read, and the A dword of a slot holds the row's weight
+// limb in its parity's half.  Weights and levels are each two fp16 limbs (levels scaled by
+// 2^10): the four limb products are exact and summed in fp32.  The plane words of a stage of
+// tokens are held in LDS token-contiguous ([chunk][plane][token]), so one 16-byte read gives a
+// lane its 4 tokens; a lane keeps one 32-coordinate chunk across up to 4 column tiles (pairs
+// k = j LPC + col % LPC of chunk col / LPC), reusing each word read.
+constexpr int kAttnChunk = 1024;     // tokens per chunk partial
 constexpr float kAttnSlack = 8.f;    // a logit may exceed its row's reference max by this
 
 struct AttnArgs {
@@ -2410,14 +2412,14 @@ __device__ __forceinline__ void attn_pair_table(const SubDev& s, uint32_t* ptab)
   }
 }
 
-// A workgroup streams the stages of up to chunks_per_block consecutive chunks of one group and
+// D >= 512: the waves of a workgroup split the column tiles, so they share each stage.  A
+// workgroup streams the stages of up to chunks_per_block consecutive chunks of one group and
 // row tile: the next stage's plane words, norms and logits are loaded while the current stage
 // is contracted.  The softmax max and the norm scale are running values over the chunk (as in
 // online softmax): when a stage raises them, the accumulators and the partial sums of the
 // exponentials are rescaled.  At the end of each chunk its partial (y, max, sum) is written.
 template <int D, int R, int RQ>
-__global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(D <= 256 && RQ == 1 ? 4 : 1)))
-attend_mfma_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(kBlock) attend_mfma_kernel(AttnArgs a) {
   constexpr int NW = kBlock / kWave;
   constexpr int NJT = D / 32;                       // column tiles of 16 pairs = chunks
   constexpr int ST = NJT < 4 ? NJT : 4;             // tiles sharing a lane's chunk
