@@ -10,16 +10,20 @@
  * rotated coordinate; the residual gets a 1-bit QJL sign sketch under a
  * seeded Gaussian matrix.  A full-precision query is rotated the same way and
  * scored against the packed codes with an unbiased inner-product estimate.
+ * Around that path: top-k selection (fused with scoring or on a score
+ * matrix), the exact re-rank of a candidate set, TurboQuant-MSE plans and
+ * dequantization, decode attention over quantized values, and the KV-cache
+ * policy layer (outlier channels by variance, appending one record per head).
  *
  * Conventions for every call:
  *   - Status is returned, never thrown; nothing aborts or prints.
  *   - "device" pointers are HIP device memory of the current device; "host"
  *     pointers are ordinary CPU memory.  The caller owns every buffer it passes.
  *   - `stream` is a hipStream_t (NULL = the default stream).  tq_encode,
- *     tq_score, tq_score_topk, tq_dequantize, tq_qjl and tq_topk only enqueue
- *     work on it and return; their
- *     outputs are valid once the stream reaches that point.  A launch failure
- *     is reported as TQ_EDEVICE.
+ *     tq_encode_scatter, tq_score, tq_score_topk, tq_topk, tq_dequantize,
+ *     tq_attend, tq_rerank, tq_calibrate_outliers and tq_qjl only enqueue work
+ *     on it and return; their outputs are valid once the stream reaches that
+ *     point.  A launch failure is reported as TQ_EDEVICE.
  *   - A plan is immutable after creation and may be used from several streams
  *     and threads at once.  Destroying a plan while work that uses it is still
  *     queued is undefined.
