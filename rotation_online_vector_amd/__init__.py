@@ -126,6 +126,21 @@ def _dtype_code(t):
     raise TypeError("expected a bfloat16 or float32 tensor, got %s" % t.dtype)
 
 
+def _on_gpu(*tensors):
+    """Every tensor must live on one GPU: the library takes device pointers, and a host
+    pointer in a kernel would fault the device."""
+    dev = None
+    for t in tensors:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors passed to the library must be on a GPU (got %s)" % t.device)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("tensors on different devices: %s and %s" % (dev, t.device))
+
+
 def _rows(t, d):
     """(n, ld) of a tensor viewed as rows of d elements with unit inner stride."""
     if t.shape[-1] != d or t.stride(-1) != 1:
@@ -208,6 +223,7 @@ def tq_plan_info(plan):
 def tq_encode(plan, x, codes=None, stream=None):
     """Encode the rows of x (cuda bf16/f32, last dim d) into codes (uint8 [n, record_bytes])."""
     import torch
+    _on_gpu(x, codes)
     n, ld = _rows(x, plan.d)
     if codes is None:
         codes = torch.empty((n, plan.record_bytes), dtype=torch.uint8, device=x.device)
@@ -220,6 +236,7 @@ def tq_encode(plan, x, codes=None, stream=None):
 def tq_score(plan, q, codes, n, nq_per_group=None, n_groups=1, scores=None, stream=None):
     """Scores [n_groups*nq_per_group, n] of query rows q against grouped codes."""
     import torch
+    _on_gpu(q, codes, scores)
     nq, ld = _rows(q, plan.d)
     if nq_per_group is None:
         nq_per_group = nq // n_groups
@@ -237,6 +254,7 @@ def tq_score(plan, q, codes, n, nq_per_group=None, n_groups=1, scores=None, stre
 
 def tq_topk(scores, k, ids=None, vals=None, stream=None):
     import torch
+    _on_gpu(scores, ids, vals)
     if scores.dtype != torch.float32 or not scores.is_contiguous():
         raise ValueError("scores must be contiguous float32")
     n = scores.shape[-1]
@@ -255,6 +273,7 @@ def tq_score_topk(plan, q, codes, n, k, nq_per_group=None, n_groups=1, ids=None,
                   stream=None):
     """Top-k (ids [rows, k] int64, vals [rows, k] float32) of the scores tq_score would give."""
     import torch
+    _on_gpu(q, codes, ids, vals)
     nq, ld = _rows(q, plan.d)
     if nq_per_group is None:
         nq_per_group = nq // n_groups
@@ -276,6 +295,7 @@ def tq_score_topk(plan, q, codes, n, k, nq_per_group=None, n_groups=1, ids=None,
 def tq_dequantize(plan, codes, n, x=None, dtype=None, stream=None):
     """Reconstructed vectors [n, d] (float32 or bfloat16) from n records."""
     import torch
+    _on_gpu(codes, x)
     if codes.numel() < n * plan.record_bytes:
         raise ValueError("codes buffer too small")
     if x is None:
@@ -293,6 +313,7 @@ def tq_attend(vplan, logits, vcodes, n, scale, nq_per_group=None, n_groups=1, ou
               dtype=None, stream=None):
     """softmax(scale * logits) times the dequantized values, per query row: [rows, d]."""
     import torch
+    _on_gpu(logits, vcodes, out)
     if logits.dtype != torch.float32 or not logits.is_contiguous() or logits.shape[-1] != n:
         raise ValueError("logits must be contiguous float32 [rows, n]")
     rows = logits.numel() // n
@@ -317,6 +338,7 @@ def tq_attend(vplan, logits, vcodes, n, scale, nq_per_group=None, n_groups=1, ou
 def tq_rerank(q, x, cand, k, ids=None, vals=None, stream=None):
     """Exact top-k of each query row over its candidate rows of x (cand: int64 [nq, kc])."""
     import torch
+    _on_gpu(q, x, cand, ids, vals)
     d = q.shape[-1]
     nq, ldq = _rows(q, d)
     n, ldx = _rows(x, d)
@@ -338,6 +360,7 @@ def tq_calibrate_outliers(x, n_out, var=None, mask=None, stream=None):
     """Per-channel variance (fp64) of the rows of x and the mask of its n_out channels of
     largest variance (ties to the lower channel): (var float64 [d], mask uint8 [d])."""
     import torch
+    _on_gpu(x, var, mask)
     d = x.shape[-1]
     n, ldx = _rows(x, d)
     if var is None:
@@ -354,6 +377,7 @@ def tq_encode_scatter(plan, x, cache, index, stream=None):
     """Encode the rows of x and write record i to row index[i] of cache (uint8
     [rows, record_bytes]); rows outside the cache are skipped."""
     import torch
+    _on_gpu(x, cache, index)
     n, ld = _rows(x, plan.d)
     if cache.dtype != torch.uint8 or not cache.is_contiguous() or cache.dim() != 2 or \
             cache.shape[1] != plan.record_bytes:
@@ -369,6 +393,7 @@ def tq_encode_scatter(plan, x, cache, index, stream=None):
 
 def tq_qjl(plan, subplan, r, beta=None, stream=None):
     import torch
+    _on_gpu(r, beta)
     D = plan.desc["sub"][subplan]["D"]
     if r.dtype != torch.float32 or not r.is_contiguous() or r.shape[-1] != D:
         raise ValueError("r must be contiguous float32 [n, D]")

@@ -135,3 +135,18 @@ def test_c_abi_from_plain_c(tmp_path):
     out = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert out.returncode == 0, out.stdout + out.stderr
     assert out.stdout.strip().endswith("all passed")
+
+
+def test_bindings_refuse_host_tensors():
+    """Host tensors never reach the library: their pointers would fault the device."""
+    import torch
+    import rotation_online_vector_amd as tq
+    q = torch.zeros((2, 16))
+    x = torch.zeros((5, 16))
+    cand = torch.zeros((2, 4), dtype=torch.int64)
+    with pytest.raises(ValueError, match="GPU"):
+        tq.tq_rerank(q, x, cand, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        tq.tq_calibrate_outliers(x, 2)
+    with pytest.raises(ValueError, match="GPU"):
+        tq.tq_topk(torch.zeros((2, 8)), 2)
