@@ -7,6 +7,9 @@ distributions, keep about a quarter of the channels as outliers at a higher bit 
 the channels of largest variance over a calibration sample, the plainest reading of "outlier
 channel"), 3-bit TurboQuant-MSE for most heads and the inner-product variant for key heads;
 §4.1.2: the cache is written as tokens arrive (one record per head and decode step).
+
+Pins (tests/test_oracle_pins.py): the variance against the pairwise-difference identity;
+planted channels, shift and permutation invariance and ties for the choice; placement by hand.
 """
 import numpy as np
 
