@@ -131,3 +131,22 @@ def test_attend_zero_values_give_zero_rows():
     out = tq.tq_attend(plan, L, vc, n, 1.0)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out).item() == 0
+
+
+@pytest.mark.parametrize("d,bits", [(32, 3), (32, 4), (64, 1), (512, 1), (512, 4), (1024, 4),
+                                    (2048, 1), (2048, 4), (200, 1)])
+def test_attend_every_index_width_on_each_kernel(d, bits):
+    """Each (D, index bits) instantiation of both pass-1 kernels against the oracle, with 6
+    query rows (two row quads where D <= 1024) and a ragged second chunk."""
+    n, nqg = 1300, 6
+    rng = np.random.default_rng(d * 7 + bits)
+    V = rng.standard_normal((n, d)).astype(np.float32)
+    L = (rng.standard_normal((nqg, n)) * 2.0).astype(np.float32)
+    plan, op = tq.tq_plan_create_mse(d, bits, 4), otq.make_mse_plan(d, bits, 4)
+    vc = tq.tq_encode(plan, torch.from_numpy(V).to(DEV))
+    out = tq.tq_attend(plan, torch.from_numpy(L).to(DEV), vc, n, 0.5)
+    torch.cuda.synchronize()
+    st = layout.unpack_mse(vc.cpu().numpy(), op.D, op.R)
+    ref = otq.attend(op, L.astype(np.float64), st, 0.5, nqg)
+    vmax = np.max(np.linalg.norm(otq.dequantize(op, st), axis=1))
+    _check(_np(out), ref, vmax, False, "attend d=%d bits=%d" % (d, bits))
