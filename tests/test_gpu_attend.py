@@ -150,3 +150,34 @@ def test_attend_every_index_width_on_each_kernel(d, bits):
     ref = otq.attend(op, L.astype(np.float64), st, 0.5, nqg)
     vmax = np.max(np.linalg.norm(otq.dequantize(op, st), axis=1))
     _check(_np(out), ref, vmax, False, "attend d=%d bits=%d" % (d, bits))
+
+
+@pytest.mark.parametrize("pattern", ["rising", "falling", "sharp", "very_negative"])
+def test_attend_logit_patterns_that_move_the_reference(pattern):
+    """Logits that climb across each chunk (the reference max moves by more than the slack
+    many times), that fall (it never moves after the first stage), a large scale (most weights
+    underflow to zero) and logits near -1e4 (only the differences matter)."""
+    d, n, nqg, groups = 128, 2 * 1024 + 333, 4, 2
+    rng = np.random.default_rng(len(pattern))
+    V = rng.standard_normal((groups * n, d)).astype(np.float32)
+    base = rng.standard_normal((groups * nqg, n))
+    ramp = np.arange(n)[None, :] * 0.05
+    scale = 1.0
+    if pattern == "rising":
+        L = base + ramp
+    elif pattern == "falling":
+        L = base - ramp
+    elif pattern == "sharp":
+        L, scale = base, 40.0
+    else:
+        L = base - 1e4
+    L = L.astype(np.float32)
+    plan, op = tq.tq_plan_create_mse(d, 3, 8), otq.make_mse_plan(d, 3, 8)
+    vc = tq.tq_encode(plan, torch.from_numpy(V).to(DEV))
+    out = tq.tq_attend(plan, torch.from_numpy(L).to(DEV), vc, n, scale, nq_per_group=nqg,
+                       n_groups=groups)
+    torch.cuda.synchronize()
+    st = layout.unpack_mse(vc.cpu().numpy(), op.D, op.R)
+    ref = otq.attend(op, L.astype(np.float64), st, scale, nqg)
+    vmax = np.max(np.linalg.norm(otq.dequantize(op, st), axis=1))
+    _check(_np(out), ref, vmax, False, "attend %s" % pattern)
