@@ -173,3 +173,34 @@ def test_mse_long_context_shape_full_as_benchmarked():
     parity.compare_codes_mse(op, ref, got, "mse long-context")
     xr = otq.dequantize(op, dict(idx=got["idx"], norm=got["norm"]))
     parity.check_dequantized(_np64(xh[ri]), xr, got["norm"], True, "mse long-context dequant")
+
+
+def test_attend_long_context_shape_full_as_benchmarked():
+    """Decode attention over the whole 16 x 8 x 131072 cache in the launch configuration the
+    attend bench times (keys scored, values under the 3-bit MSE plan); sampled groups against
+    the oracle's attention over the same logits and stored value codes."""
+    import math
+    from oracle import layout
+    W = workloads.ATTEND_LONGCTX
+    keys, queries, _ = workloads.longctx_inputs(DEV)
+    vals, _, _ = workloads.longctx_inputs(DEV, seed=W["v_seed"])
+    n_seq, n_kv, n_tok, d, G = W["n_seq"], W["n_kv"], W["n_tok"], W["d"], W["group"]
+    n_groups = n_seq * n_kv
+    kplan = tq.tq_plan_create(d, W["bits"], W["seed"])
+    vplan = tq.tq_plan_create_mse(d, W["v_bits"], W["v_seed"])
+    op = otq.make_mse_plan(d, W["v_bits"], W["v_seed"])
+    kc = tq.tq_encode(kplan, keys.view(-1, d))
+    vc = tq.tq_encode(vplan, vals.view(-1, d))
+    del keys, vals
+    logits = tq.tq_score(kplan, queries.view(-1, d), kc, n=n_tok, nq_per_group=G, n_groups=n_groups)
+    out = tq.tq_attend(vplan, logits, vc, n_tok, 1.0 / math.sqrt(d), nq_per_group=G,
+                       n_groups=n_groups, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    for g in (0, 77, n_groups - 1):
+        st = layout.unpack_mse(vc[g * n_tok:(g + 1) * n_tok].cpu().numpy(), op.D, op.R)
+        L = logits[g * G:(g + 1) * G].double().cpu().numpy()
+        ref = otq.attend(op, L, st, 1.0 / math.sqrt(d), G)
+        got = out[g * G:(g + 1) * G].double().cpu().numpy()
+        vmax = np.max(np.linalg.norm(otq.dequantize(op, st), axis=1))
+        tol = 2e-5 * vmax + 2.0 ** -8 * np.abs(ref)
+        assert np.all(np.abs(got - ref) <= tol), "group %d: max err/tol %g" % (g, np.max(np.abs(got - ref) / tol))
