@@ -141,6 +141,13 @@ def _on_gpu(*tensors):
             raise ValueError("tensors on different devices: %s and %s" % (dev, t.device))
 
 
+def _out(t, dtype, numel, name):
+    """A caller-provided output: contiguous, of the right dtype and at least numel elements,
+    so that the library never writes past it."""
+    if t.dtype != dtype or not t.is_contiguous() or t.numel() < numel:
+        raise ValueError("%s must be contiguous %s with at least %d elements" % (name, dtype, numel))
+
+
 def _rows(t, d):
     """(n, ld) of a tensor viewed as rows of d elements with unit inner stride."""
     if t.shape[-1] != d or t.stride(-1) != 1:
@@ -227,6 +234,7 @@ def tq_encode(plan, x, codes=None, stream=None):
     n, ld = _rows(x, plan.d)
     if codes is None:
         codes = torch.empty((n, plan.record_bytes), dtype=torch.uint8, device=x.device)
+    _out(codes, torch.uint8, n * plan.record_bytes, "codes")
     _check("tq_encode", load_library().tq_encode(
         plan.handle, ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ld,
         ctypes.c_void_p(codes.data_ptr()), _stream(stream)))
@@ -246,6 +254,7 @@ def tq_score(plan, q, codes, n, nq_per_group=None, n_groups=1, scores=None, stre
         raise ValueError("codes buffer too small")
     if scores is None:
         scores = torch.empty((nq, n), dtype=torch.float32, device=q.device)
+    _out(scores, torch.float32, nq * n, "scores")
     _check("tq_score", load_library().tq_score(
         plan.handle, ctypes.c_void_p(q.data_ptr()), _dtype_code(q), nq_per_group, n_groups, ld,
         ctypes.c_void_p(codes.data_ptr()), n, ctypes.c_void_p(scores.data_ptr()), _stream(stream)))
@@ -263,6 +272,8 @@ def tq_topk(scores, k, ids=None, vals=None, stream=None):
         ids = torch.empty((nq, k), dtype=torch.int64, device=scores.device)
     if vals is None:
         vals = torch.empty((nq, k), dtype=torch.float32, device=scores.device)
+    _out(ids, torch.int64, nq * k, "ids")
+    _out(vals, torch.float32, nq * k, "vals")
     _check("tq_topk", load_library().tq_topk(
         ctypes.c_void_p(scores.data_ptr()), nq, n, int(k), ctypes.c_void_p(ids.data_ptr()),
         ctypes.c_void_p(vals.data_ptr()), _stream(stream)))
@@ -285,6 +296,8 @@ def tq_score_topk(plan, q, codes, n, k, nq_per_group=None, n_groups=1, ids=None,
         ids = torch.empty((nq, k), dtype=torch.int64, device=q.device)
     if vals is None:
         vals = torch.empty((nq, k), dtype=torch.float32, device=q.device)
+    _out(ids, torch.int64, nq * k, "ids")
+    _out(vals, torch.float32, nq * k, "vals")
     _check("tq_score_topk", load_library().tq_score_topk(
         plan.handle, ctypes.c_void_p(q.data_ptr()), _dtype_code(q), nq_per_group, n_groups, ld,
         ctypes.c_void_p(codes.data_ptr()), n, int(k), ctypes.c_void_p(ids.data_ptr()),
@@ -348,6 +361,8 @@ def tq_rerank(q, x, cand, k, ids=None, vals=None, stream=None):
         ids = torch.empty((nq, k), dtype=torch.int64, device=q.device)
     if vals is None:
         vals = torch.empty((nq, k), dtype=torch.float32, device=q.device)
+    _out(ids, torch.int64, nq * k, "ids")
+    _out(vals, torch.float32, nq * k, "vals")
     _check("tq_rerank", load_library().tq_rerank(
         ctypes.c_void_p(q.data_ptr()), _dtype_code(q), nq, ldq, ctypes.c_void_p(x.data_ptr()),
         _dtype_code(x), n, ldx, int(d), ctypes.c_void_p(cand.data_ptr()), int(cand.shape[1]),
@@ -367,6 +382,8 @@ def tq_calibrate_outliers(x, n_out, var=None, mask=None, stream=None):
         var = torch.empty(d, dtype=torch.float64, device=x.device)
     if mask is None:
         mask = torch.empty(d, dtype=torch.uint8, device=x.device)
+    _out(var, torch.float64, d, "var")
+    _out(mask, torch.uint8, d, "mask")
     _check("tq_calibrate_outliers", load_library().tq_calibrate_outliers(
         ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ldx, int(d), int(n_out),
         ctypes.c_void_p(var.data_ptr()), ctypes.c_void_p(mask.data_ptr()), _stream(stream)))
@@ -400,6 +417,7 @@ def tq_qjl(plan, subplan, r, beta=None, stream=None):
     n = r.numel() // D
     if beta is None:
         beta = torch.empty((n, D // 32), dtype=torch.int32, device=r.device)
+    _out(beta, torch.int32, n * (D // 32), "beta")
     _check("tq_qjl", load_library().tq_qjl(
         plan.handle, int(subplan), ctypes.c_void_p(r.data_ptr()), n,
         ctypes.c_void_p(beta.data_ptr()), _stream(stream)))

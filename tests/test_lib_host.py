@@ -150,3 +150,16 @@ def test_bindings_refuse_host_tensors():
         tq.tq_calibrate_outliers(x, 2)
     with pytest.raises(ValueError, match="GPU"):
         tq.tq_topk(torch.zeros((2, 8)), 2)
+
+
+def test_bindings_check_caller_outputs():
+    """A caller-provided output of the wrong dtype or size is refused before the library runs
+    (checked on the host; the device check comes first, so CPU tensors exercise only that)."""
+    import torch
+    import rotation_online_vector_amd as tq
+    t = torch.zeros(3, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        tq._out(t, torch.float64, 3, "var")
+    with pytest.raises(ValueError):
+        tq._out(t, torch.float32, 4, "vals")
+    tq._out(t, torch.float32, 3, "vals")
