@@ -15,8 +15,7 @@ Modules:
   layout      packed byte layout of the codes
   policy      outlier channels by variance; appending encoded tokens to a cache
 
-Parity status of each function is listed in the module docstrings; the only
-function without an external pin is the exact Philox bit stream (no published
-known-answer vectors are available here): it is pinned by statistics and by
-agreement with the library's independent implementation only.
+Parity status of each function is listed in the module docstrings.  Every
+function has an external pin (tests/test_oracle_pins.py); the Philox bit stream
+is pinned by the generator's published known-answer vectors.
 """

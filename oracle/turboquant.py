@@ -143,6 +143,18 @@ def encode(plan, X):
     return dict(idx=idx, beta=beta, norm=norm, gamma=gamma, z=z, r=r, p=p)
 
 
+def qjl_given_idx(plan, z, idx):
+    """Steps 4-5 of `encode` for rotated directions z whose cells were chosen elsewhere:
+    r = z - c[idx], gamma = ||r||, p = S r, beta = [p >= 0].  A coordinate within rounding of
+    a threshold may be placed in either neighbouring cell; the residual, and with it the sign
+    bits, then follow the cell actually chosen (overview §2.3.1-2.3.2: the residual is the
+    error of the first stage as quantized).  Returns dict(r, gamma, p, beta)."""
+    r = np.asarray(z, dtype=np.float64) - plan.levels[np.asarray(idx)]
+    gamma = np.sqrt(np.sum(r * r, axis=-1))
+    beta, p = qjl_signs(plan.S, r)
+    return dict(r=r, gamma=gamma, p=p, beta=beta)
+
+
 def encode_mse(plan, X):
     """TurboQuant-MSE codes of the rows of X (n x d): dict with idx (n, D), norm (n,) and
     the rotated direction z."""

@@ -20,18 +20,14 @@ def _np64(t):
 
 
 def _check_sampled(sp, codes_u8, x_rows, keys_idx, q_rows, scores_rows, tag):
-    """codes of sampled keys vs the oracle; scores of the sampled (query, key) pairs."""
+    """codes of sampled keys vs the oracle; scores of the sampled (query, key) pairs, against
+    the oracle's own codes where the codes are identical and the oracle on the GPU's codes
+    elsewhere.  Returns the fraction of vectors with identical codes."""
     got = parity.unpack_gpu(sp, codes_u8)
     ref = otq.encode_split(sp, x_rows)
     for i, (p, r, g) in enumerate(zip(sp.plans, ref, got)):
         parity.compare_codes(p, r, g, "%s/sub%d" % (tag, i))
-    same = np.ones(len(keys_idx), dtype=bool)
-    for r, g in zip(ref, got):
-        same &= np.all(r["idx"] == g["idx"], 1) & np.all(r["beta"] == g["beta"], 1)
-    est_ref = otq.score_split(sp, [parity.stored(c) for c in ref], q_rows)
-    parity.check_scores(scores_rows[:, same], est_ref[:, same], np.linalg.norm(q_rows, axis=1),
-                        np.linalg.norm(x_rows, axis=1)[same], tag)
-    return same.mean()
+    return parity.check_scores_end_to_end(sp, ref, got, scores_rows, q_rows, x_rows, tag)
 
 
 def test_kv_cache_shape_full():

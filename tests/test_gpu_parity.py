@@ -73,7 +73,7 @@ def test_qjl_stage_matches_oracle(small):
     mis = got != ref
     band = parity.sign_band(p, r.astype(np.float64), proj)
     assert not (mis & ~band).any()
-    assert mis.sum() <= 1
+    assert mis.sum() <= parity.MISMATCH_FRACTION * mis.size
 
 
 def test_score_small_matches_oracle_on_oracle_codes(small):
@@ -98,14 +98,14 @@ def test_end_to_end_small_and_topk(small):
     ids, vals = tq.tq_topk(est, 10)
     torch.cuda.synchronize()
     est = est.cpu().numpy()
-    got = parity.unpack_gpu(sp, codes.cpu().numpy())[0]
-    ref = otq.encode(sp.plans[0], keys.astype(np.float64))
-    same = np.all(got["idx"] == ref["idx"], axis=1) & np.all(got["beta"] == ref["beta"], axis=1)
-    assert same.mean() > 0.99
-    est_ref = otq.score(sp.plans[0], parity.stored(ref), queries.astype(np.float64))
+    got = parity.unpack_gpu(sp, codes.cpu().numpy())
+    ref = [otq.encode(sp.plans[0], keys.astype(np.float64))]
+    parity.compare_codes(sp.plans[0], ref[0], got[0], "small e2e")
+    parity.check_scores_end_to_end(sp, ref, got, est, queries, keys, "small e2e")
+    # selection: against the oracle's top-k of its estimates for the codes the GPU scored
+    est_g = parity.oracle_scores_on_gpu_codes(sp, got, queries)
     qn, xn = np.linalg.norm(queries, axis=1), np.linalg.norm(keys, axis=1)
-    parity.check_scores(est[:, same], est_ref[:, same], qn, xn[same], "small e2e")
-    parity.check_topk(ids.cpu().numpy(), vals.cpu().numpy(), est_ref, 10, qn, xn, "small top-10")
+    parity.check_topk(ids.cpu().numpy(), vals.cpu().numpy(), est_g, 10, qn, xn, "small top-10")
     # values returned are the GPU scores of the returned ids
     assert np.array_equal(vals.cpu().numpy(), np.take_along_axis(est, ids.cpu().numpy(), 1))
 
@@ -225,16 +225,19 @@ def test_strided_rows_and_query_groups():
     sp = otq.make_split_plan(d, 3, 2)
     plan = tq.tq_plan_create(d, 3, 2)
     _encode_and_compare(sp, plan, x, "strided")
+    ref = [otq.encode(sp.plans[0], _np(x))]
     for g in (1, 2, 3, 5, 8):
         y = torch.from_numpy(rng.standard_normal((2 * g, d)).astype(np.float32)).to(DEV)
         codes = tq.tq_encode(plan, torch.cat([x, x]).contiguous())
         est = tq.tq_score(plan, y, codes, n=n, nq_per_group=g, n_groups=2).cpu().numpy()
-        ref = parity.stored(otq.encode(sp.plans[0], _np(x)))
-        got = parity.unpack_gpu(sp, codes[:n].cpu().numpy())[0]
-        same = np.all(got["idx"] == ref["idx"], 1) & np.all(got["beta"] == ref["beta"], 1)
-        est_ref = otq.score(sp.plans[0], ref, _np(y))
-        parity.check_scores(est[:, same], est_ref[:, same], np.linalg.norm(_np(y), axis=1),
-                            np.linalg.norm(_np(x), axis=1)[same], "group %d" % g)
+        c = codes.cpu().numpy()
+        assert np.array_equal(c[:n], c[n:])                 # both groups hold the same records
+        got = parity.unpack_gpu(sp, c[:n])
+        parity.compare_codes(sp.plans[0], ref[0], got[0], "strided, group %d" % g)
+        for h in range(2):
+            parity.check_scores_end_to_end(sp, ref, got, est[h * g:(h + 1) * g],
+                                           _np(y)[h * g:(h + 1) * g], _np(x),
+                                           "group size %d, group %d" % (g, h))
 
 
 def test_outlier_split_plan_small():

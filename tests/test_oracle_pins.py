@@ -316,6 +316,121 @@ def test_split_plan_scores_sum_of_subsets():
     assert not np.array_equal(sp.plans[0].signs[:, :32], sp.plans[1].signs)
 
 
+def test_split_plan_channels_and_bits_follow_the_mask():
+    """The mask's zero channels form sub-plan 0 at `bits`, its set channels sub-plan 1 at
+    `outlier_bits`, each padded to its own power of two with subset-1 randomness for the
+    outliers (overview §4.1.1: outlier channels kept at a higher bit-width)."""
+    d = 128
+    mask = np.zeros(d, dtype=np.uint8)
+    mask[np.random.default_rng(31).choice(d, 32, replace=False)] = 1
+    sp = tq.make_split_plan(d, 3, 7, mask, 5)
+    assert np.array_equal(sp.channels[0], np.flatnonzero(mask == 0))
+    assert np.array_equal(sp.channels[1], np.flatnonzero(mask == 1))
+    p0, p1 = sp.plans
+    assert (p0.d, p0.D, p0.bits, p0.R, p0.k, p0.subset) == (96, 128, 3, 2, 128, 0)
+    assert (p1.d, p1.D, p1.bits, p1.R, p1.k, p1.subset) == (32, 32, 5, 4, 32, 1)
+    # channel j of the input reaches sub-plan 1 exactly when the mask selects it
+    X = np.zeros((1, d))
+    j = int(np.flatnonzero(mask)[5])
+    X[0, j] = 3.0
+    c = tq.encode_split(sp, X)
+    assert c[0]["norm"][0] == 0.0 and c[1]["norm"][0] == 3.0
+
+
+@pytest.fixture
+def cached_codebooks(monkeypatch):
+    """Plans for many seeds share their codebooks: solve each (D, R) once."""
+    cache = {}
+    solve = codebook.solve_codebook
+
+    def cached(D, R):
+        if (D, R) not in cache:
+            cache[(D, R)] = solve(D, R)
+        return cache[(D, R)]
+    monkeypatch.setattr(codebook, "solve_codebook", cached)
+
+
+@pytest.mark.parametrize("bits,obits", [(3, 5), (2, 4)])
+def test_split_estimator_unbiased_over_seeds(bits, obits, cached_codebooks):
+    """E[est_O + est_R] = <x, y> over 10^4 plan seeds for a split plan of 96 regular and 32
+    outlier channels (overview §4.1.1 split, §1.2.3 unbiasedness): |mean - <x,y>| < 3 SE.
+    Keys and queries carry the x10 scale on the mask's channels, as in the split workload."""
+    d, n_seeds = 128, 10000
+    rng = np.random.default_rng(32)
+    mask = np.zeros(d, dtype=np.uint8)
+    mask[rng.choice(d, 32, replace=False)] = 1
+    x = rng.standard_normal(d)
+    y = rng.standard_normal(d)
+    x[mask == 1] *= 10
+    y[mask == 1] *= 10
+    ests = np.empty(n_seeds)
+    for s in range(n_seeds):
+        sp = tq.make_split_plan(d, bits, s, mask, obits)
+        ests[s] = tq.score_split(sp, tq.encode_split(sp, x[None]), y[None])[0, 0]
+    se = ests.std(ddof=1) / math.sqrt(n_seeds)
+    assert abs(ests.mean() - x @ y) < 3 * se
+
+
+def test_split_estimate_converges_with_bits():
+    """As both bit-widths grow the split estimate tends to the exact inner product and the
+    residual norms of both sub-plans shrink (the large-R limit of each sub-plan)."""
+    d = 128
+    rng = np.random.default_rng(33)
+    mask = np.zeros(d, dtype=np.uint8)
+    mask[rng.choice(d, 32, replace=False)] = 1
+    X = rng.standard_normal((200, d))
+    Y = rng.standard_normal((8, d))
+    X[:, mask == 1] *= 10
+    Y[:, mask == 1] *= 10
+    exact = Y @ X.T
+    errs, g0, g1 = [], [], []
+    for bits, obits in [(2, 3), (3, 4), (4, 5), (5, 6), (6, 7)]:
+        sp = tq.make_split_plan(d, bits, 0, mask, obits)
+        c = tq.encode_split(sp, X)
+        errs.append(np.sqrt(np.mean((tq.score_split(sp, c, Y) - exact) ** 2)))
+        g0.append(c[0]["gamma"].mean())
+        g1.append(c[1]["gamma"].mean())
+    # each extra bit on both sub-plans about halves the error (distortion ~ 4^-R per plan)
+    assert all(0.4 < b / a < 0.6 for a, b in zip(errs, errs[1:])), errs
+    assert all(a > b for a, b in zip(g0, g0[1:])) and all(a > b for a, b in zip(g1, g1[1:]))
+    assert errs[-1] < 0.04 * np.sqrt(np.mean(exact ** 2))
+
+
+def test_qjl_given_idx_any_cell_choice_stays_unbiased():
+    """With the cells of a few coordinates moved to a neighbour (as a coordinate within
+    rounding of a threshold may be), the residual follows the cell chosen and the estimate
+    built from those codes is still unbiased over draws of S (the QJL term estimates
+    <y', r'> for whatever residual r' it is given), and with the cells of the quantizer
+    itself it reproduces the encoder's own residual, norm and signs."""
+    D, bits, draws = 32, 3, 20000
+    levels, t = codebook.solve_codebook(D, bits - 1)
+    base = _plan_for_seed(D, bits, 0, levels, t)
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal(D)
+    y = rng.standard_normal(D)
+    c0 = tq.encode(base, x[None])
+    own = tq.qjl_given_idx(base, c0["z"], c0["idx"])
+    assert np.array_equal(own["beta"], c0["beta"]) and np.allclose(own["r"], c0["r"], 0, 0)
+    assert own["gamma"][0] == c0["gamma"][0]
+    idx = c0["idx"].copy()
+    moved = [2, 9, 17]
+    idx[0, moved] = np.where(idx[0, moved] > 0, idx[0, moved] - 1, idx[0, moved] + 1)
+    yr = rotation.rotate(y[None], base.signs)[0]
+    n = c0["norm"][0]
+    mse_part = n * yr @ base.levels[idx[0]]
+    vals = np.empty(draws)
+    for s in range(1, draws + 1):
+        p = tq.Plan(**{**base.__dict__, "S": philox.qjl_matrix(s, 0, D, D)})
+        q = tq.qjl_given_idx(p, c0["z"], idx)
+        codes = dict(idx=idx, beta=q["beta"], gamma=q["gamma"], norm=c0["norm"])
+        vals[s - 1] = tq.score(p, codes, y[None])[0, 0]
+    se = vals.std(ddof=1) / math.sqrt(draws)
+    assert abs(vals.mean() - x @ y) < 3 * se
+    # the QJL part alone is centred on n <y', r'> for the moved cells' residual r'
+    r_moved = c0["z"][0] - base.levels[idx[0]]
+    assert abs((vals - mse_part).mean() - n * yr @ r_moved) < 3 * se
+
+
 def test_topk_matches_brute_force_with_ties():
     rng = np.random.default_rng(13)
     est = np.round(rng.standard_normal((5, 300)), 1)     # many exact ties
@@ -327,6 +442,21 @@ def test_topk_matches_brute_force_with_ties():
 
 
 # ---------------------------------------------------------------- randomness
+
+def test_philox_known_answer_vectors():
+    """The generator reproduces the published Philox4x32-10 known-answer vectors (Random123,
+    Salmon et al. SC'11), so a wrong multiplier, Weyl constant, round count or output-word
+    order fails here; the library's own implementation is compared with this stream bit for
+    bit elsewhere."""
+    with open(os.path.join(GOLDEN, "philox4x32_10_kat.json")) as f:
+        kat = json.load(f)
+    assert len(kat["vectors"]) == 3
+    for v in kat["vectors"]:
+        c = [int(h, 16) for h in v["ctr"]]
+        k = [int(h, 16) for h in v["key"]]
+        got = ["%08x" % int(w) for w in philox.philox4x32_10(*c, *k)]
+        assert got == v["out"], (v, got)
+
 
 def test_philox_uniform_and_gaussian_statistics():
     w = philox.stream_words(0, philox.PURPOSE_GAUSS, 0, 0, 1 << 18)
