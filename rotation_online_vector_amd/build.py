@@ -17,7 +17,7 @@ LIB = os.path.join(LIBDIR, "libtq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kernels.hip", "tq_api.cpp", "host_tables.cpp"]
+SOURCES = ["kernels.hip", "encode128.hip", "tq_api.cpp", "host_tables.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
@@ -32,19 +32,24 @@ def _run(cmd):
         print(out)
 
 
+def _compile(src, verbose):
+    path = os.path.join(CSRC, src)
+    obj = os.path.join(LIBDIR, src.replace(".", "_") + ".o")
+    cmd = [HIPCC, "--offload-arch=" + ARCH] + COMMON + ["-c", path, "-o", obj]
+    if src.endswith(".hip"):
+        cmd[1:1] = ["-x", "hip"]
+    if verbose:
+        print("[build]", src, flush=True)
+    _run(cmd)
+    return obj
+
+
 def build(verbose=True):
+    """Compile every source (in parallel) and link libtq.so."""
+    from concurrent.futures import ThreadPoolExecutor
     os.makedirs(LIBDIR, exist_ok=True)
-    objs = []
-    for src in SOURCES:
-        path = os.path.join(CSRC, src)
-        obj = os.path.join(LIBDIR, src.replace(".", "_") + ".o")
-        cmd = [HIPCC, "--offload-arch=" + ARCH] + COMMON + ["-c", path, "-o", obj]
-        if src.endswith(".hip"):
-            cmd[1:1] = ["-x", "hip"]
-        if verbose:
-            print("[build]", src, flush=True)
-        _run(cmd)
-        objs.append(obj)
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as pool:
+        objs = list(pool.map(lambda src: _compile(src, verbose), SOURCES))
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
     os.replace(tmp, LIB)

@@ -1,0 +1,351 @@
+// Encoder for D = 128 inner-product plans with bf16 input on 32 x 32 matrix-core tiles
+// (gfx950).  Same codes as the general encoders: norm split, z = Pi x / ||x|| with
+// Pi = Ht S3 Ht S2 Ht S1 (TurboQuant technical overview §2.1.1-2.1.2), Lloyd-Max bucketize
+// idx = #{t_j <= z} (§1.2.2), residual r = z - c[idx] and gamma = ||r|| (§2.3.1), QJL signs
+// beta = [S r >= 0] (§2.3.2; deep dive §三: one sign bit per rotated coordinate).
+//
+// A wave encodes 32 vectors per iteration; lane l works on vector l % 32 and owns half
+// h = l / 32 of its coordinates, 64h .. 64h + 63, i.e. two whole 32-coordinate code chunks,
+// so every code word is assembled inside one lane.
+//
+//  - rotation: z_raw = K x with the exact integer K = D^(3/2) Pi in fp16 (|K| <= 2048) on
+//    32x32x16 f16 MFMAs, x converted exactly from bf16 to fp16 (with a per-vector power of
+//    two when its norm is far from 1).  K's rows are permuted on the host so that element
+//    4i + j of accumulator tile t in lane half h is coordinate 64h + 16t + 4i + j.
+//  - bucketize on z_raw against thresholds scaled by ||z_raw||; the residual is produced at
+//    a fixed per-vector power-of-two scale r' = r 2^s with ||z'|| in [2^13, 2^14).
+//  - QJL: P = S r' as a high limb fp16(r') (round to nearest) against 2^8 S (exact in
+//    fp16), plus the remainder r' - fp16(r') in fp8 e4m3 against S in e4m3 with an E8M0
+//    block scale of 2^8, both accumulated in fp32.  The remainder is below 2^-11 |r'|, so
+//    its 2^-4 operand rounding leaves a sign error near 6e-7 ||S_j|| ||r|| (worst seen:
+//    5e-6 over 1.3e7 signs), inside the 1e-5 band in which a sign may differ from exact
+//    arithmetic.  S's rows (outputs) are permuted like K's.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "device_common.h"
+
+namespace tq {
+
+namespace {
+
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int kD = 128;
+constexpr int kNT = 4;           // 32-row tiles of coordinates (and of QJL outputs)
+constexpr int kKS = 8;           // 16-wide k steps of the fp16 products
+constexpr int kQS = 2;           // 64-wide k steps of the fp8 product
+constexpr int kWaves = 8;        // waves per workgroup
+
+__device__ __forceinline__ f16x8 f16x8_of(uint4 u) { return f16x8_from_words(u.x, u.y, u.z, u.w); }
+
+__device__ __forceinline__ uint32_t pack_f16_rne(float a, float b) {
+  typedef __attribute__((ext_vector_type(2))) float f32x2;
+  typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+}
+
+// v - (half HI of the packed fp16 pair hp), exact when that half is v rounded to fp16: one
+// mixed-precision fma reading the fp16 half in place (neither operand is a matrix-core
+// result, so no wait states are owed to the inline assembly).
+template <int HI>
+__device__ __forceinline__ float residual_below_f16(uint32_t hp, float v) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hp), "v"(v));
+  else
+    asm("v_fma_mix_f32 %0, %1, -1.0, %2 op_sel:[0,0,0] op_sel_hi:[1,0,0]" : "=v"(r) : "v"(hp), "v"(v));
+  return r;
+}
+
+// One coordinate of the symmetric quantizer (as bucket_sym), returning the NEGATED residual
+// at the per-vector scale s: -r' = copysign(level, z) - s z with levels already multiplied
+// by s (one fma; the QJL signs are taken of S (-r') accordingly).
+template <int R>
+__device__ __forceinline__ float bucket_sym_scaled(float z, float s, const float* tp,
+                                                   const float* ap, uint32_t& P, uint32_t* J) {
+  constexpr int H = 1 << (R - 1);
+  float tc[H > 1 ? H - 1 : 1], lc[H];
+#pragma unroll
+  for (int j = 0; j < H - 1; ++j) tc[j] = tp[j];
+#pragma unroll
+  for (int j = 0; j < H; ++j) lc[j] = ap[j];
+#pragma unroll
+  for (int m = R - 2; m >= 0; --m) {
+    const int half = 1 << m;
+    const uint64_t mk = abs_ge_mask(z, tc[half - 1]);
+    J[m] = shift_in_mask(J[m], mk);
+#pragma unroll
+    for (int j = 0; j < half - 1; ++j) tc[j] = select_mask(mk, tc[j], tc[half + j]);
+#pragma unroll
+    for (int j = 0; j < half; ++j) lc[j] = select_mask(mk, lc[j], lc[half + j]);
+  }
+  P = shift_in_sign(P, z);
+  return fmaf(-z, s, copysignf(lc[0], z));
+}
+
+}  // namespace
+
+// Operand tables of this kernel, per plan (device, read into LDS once per workgroup):
+//   k16 [4 tiles][8 k steps][64 lanes][8]  fp16 K, rows permuted (see above), k = 16 s + 8 h + e
+//   s16 [4 tiles][8 k steps][64 lanes][8]  fp16 2^8 S, rows permuted, k = coordinate 64 h + 8 s + e
+//   s8  [4 tiles][2 k steps][64 lanes][32] e4m3 S, rows permuted, byte e of lane half h =
+//                                          coordinate 64 h + 32 q + e (the same k slot map on
+//                                          both operands of the fp8 product)
+template <int R, bool VEC>
+__global__ void __launch_bounds__(kWaves * kWave) encode128_kernel(EncodeArgs a) {
+  constexpr int H = 1 << (R - 1);
+  __shared__ uint4 lk[kNT * kKS * 64];
+  __shared__ uint4 ls16[kNT * kKS * 64];
+  __shared__ uint4 ls8[kNT * kQS * 64 * 2];
+  __shared__ __attribute__((aligned(16))) int chl[VEC ? 4 : kD];
+  const SubDev& s = a.s;
+  for (int i = threadIdx.x; i < kNT * kKS * 64; i += kWaves * kWave) {
+    lk[i] = reinterpret_cast<const uint4*>(s.k16_32)[i];
+    ls16[i] = reinterpret_cast<const uint4*>(s.s16_32)[i];
+  }
+  // fp8 operands: [tile][k step][16-byte half][lane] in LDS, so that each read instruction
+  // takes lane-consecutive 16-byte pieces (the table is [tile][k step][lane][32 bytes])
+  for (int i = threadIdx.x; i < kNT * kQS * 64 * 2; i += kWaves * kWave) {
+    const int blk = i >> 7, half = (i >> 6) & 1, l = i & 63;
+    ls8[i] = reinterpret_cast<const uint4*>(s.s8_32)[(blk * 64 + l) * 2 + half];
+  }
+  if constexpr (!VEC) {
+    for (int i = threadIdx.x; i < kD; i += kWaves * kWave)
+      chl[i] = i < s.d ? (s.chan ? s.chan[i] : i) : -1;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  float tpos[H > 1 ? H - 1 : 1], apos[H];
+#pragma unroll
+  for (int j = 0; j < H - 1; ++j) tpos[j] = s.thr[H + j];
+#pragma unroll
+  for (int j = 0; j < H; ++j) apos[j] = s.lev[H + j];
+  const float kscale = 1.f / s.inv_scale;   // D^(3/2)
+
+  // x: k step s holds input coordinates 16 s + 8 h + (0..7) of vector c.  The rows of the
+  // next iteration are loaded while the current one is encoded.
+  auto load_x = [&](int64_t v0, uint32_t (&xw)[kKS][4]) {
+    const int64_t row = v0 + c < a.n ? v0 + c : a.n - 1;   // past the end: repeat the last
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks) {
+      const int c0 = 16 * ks + 8 * h;
+      if constexpr (VEC) {
+        const uint4 u = *reinterpret_cast<const uint4*>(
+            reinterpret_cast<const uint16_t*>(a.x) + row * a.ldx + c0);
+        xw[ks][0] = u.x; xw[ks][1] = u.y; xw[ks][2] = u.z; xw[ks][3] = u.w;
+      } else {
+        const uint16_t* xr = reinterpret_cast<const uint16_t*>(a.x) + row * a.ldx;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int ch0 = chl[c0 + 2 * w], ch1 = chl[c0 + 2 * w + 1];
+          const uint32_t e0 = ch0 >= 0 ? xr[ch0] : 0u, e1 = ch1 >= 0 ? xr[ch1] : 0u;
+          xw[ks][w] = e0 | (e1 << 16);
+        }
+      }
+    }
+  };
+  const int64_t stride = (int64_t)gridDim.x * kWaves * 32;
+  int64_t v0 = ((int64_t)blockIdx.x * kWaves + wave) * 32;
+  uint32_t xn[kKS][4];
+  if (v0 < a.n) load_x(v0, xn);
+  for (; v0 < a.n; v0 += stride) {
+    uint32_t xw[kKS][4];
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) xw[ks][w] = xn[ks][w];
+    // unconditional (the rows are clamped), so that the memory-counter wait for these
+    // loads in the next iteration can count this iteration's stores instead of draining them
+    load_x(v0 + stride, xn);
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- norm: sum of squares of this half's 64 elements, then both halves ----
+    float ss = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+        const bf16x2 p = __builtin_bit_cast(bf16x2, xw[ks][w]);
+        ss = __builtin_amdgcn_fdot2_f32_bf16(p, p, ss, false);
+      }
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(ss), __float_as_uint(ss), false, false);
+      ss = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const float nrm = __builtin_amdgcn_sqrtf(ss);
+    float sc = nrm * kscale;                     // ||z_raw||
+    // fp16 copy of x, unscaled when every norm of the wave lies in [2^-4, 2^14)
+    uint32_t xh[kKS][4];
+    if (__all(nrm >= 0.0625f && nrm < 16384.f)) {
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) xh[ks][w] = bf16x2_to_f16x2<false>(xw[ks][w], 1.f);
+    } else {
+      const int e = __builtin_amdgcn_frexp_expf(nrm);
+      const float xs = __builtin_amdgcn_ldexpf(1.f, 14 - (e < -100 ? -100 : e));
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) xh[ks][w] = bf16x2_to_f16x2<true>(xw[ks][w], xs);
+      sc *= xs;
+    }
+    if (!(sc > 0.f)) sc = 1.f;                   // zero vector: z = 0, codes of z = 0
+    // residual scale: ||z'|| = sc 2^rs in [2^13, 2^14)
+    const float rsc = __builtin_amdgcn_ldexpf(1.f, 14 - __builtin_amdgcn_frexp_expf(sc));
+    float Ts[H > 1 ? H - 1 : 1], As[H];
+#pragma unroll
+    for (int j = 0; j < H - 1; ++j) Ts[j] = tpos[j] * sc;
+#pragma unroll
+    for (int j = 0; j < H; ++j) As[j] = apos[j] * sc * rsc;
+
+    // ---- rotation, one 32-row tile at a time from the highest; the tile rotated in the
+    // previous step is bucketized meanwhile, and the QJL products of the k steps whose
+    // residual limbs are ready run behind it ----
+    const f32x16 zero = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    f32x16 acc[kNT];
+    f32x16 qa[kNT];
+    uint32_t P[2] = {0u, 0u}, J[2][R > 1 ? R - 1 : 1];
+#pragma unroll
+    for (int g = 0; g < 2; ++g)
+#pragma unroll
+      for (int m = 0; m < R - 1; ++m) J[g][m] = 0u;
+    float g2 = 0.f;
+    uint32_t rh[kKS][4];       // fp16 high limbs: k step s = coordinates 64h + 8s + (0..7)
+    uint32_t rl[kQS][8];       // e4m3 remainders: k step q = coordinates 64h + 32q + (0..31)
+
+#pragma unroll
+    for (int step = 0; step <= kNT + 1; ++step) {
+      const int tr = kNT - 1 - step;        // tile rotated in this step
+      const int tb = tr + 1;                // tile bucketized
+      const int tq = tr + 2;                // tile whose k steps enter the QJL product
+      if (tr >= 0) {
+#pragma unroll
+        for (int ks = 0; ks < kKS; ++ks)
+          acc[tr] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f16x8_of(lk[(tr * kKS + ks) * 64 + lane]),
+                                                          f16x8_from_words(xh[ks][0], xh[ks][1], xh[ks][2], xh[ks][3]),
+                                                          ks == 0 ? zero : acc[tr], 0, 0, 0);
+      }
+      if (tq >= 0 && tq < kNT) {
+#pragma unroll
+        for (int u = 0; u < kNT; ++u)
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const int ks = 2 * tq + kk;
+            qa[u] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f16x8_of(ls16[(u * kKS + ks) * 64 + lane]),
+                                                          f16x8_from_words(rh[ks][0], rh[ks][1], rh[ks][2], rh[ks][3]),
+                                                          (tq == kNT - 1 && kk == 0) ? zero : qa[u], 0, 0, 0);
+          }
+        if (tq % 2 == 0) {
+          const int q = tq / 2;
+#pragma unroll
+          for (int u = 0; u < kNT; ++u) {
+            const uint4 b0 = ls8[(u * kQS + q) * 128 + lane];
+            const uint4 b1 = ls8[(u * kQS + q) * 128 + 64 + lane];
+            const i32x8 sa = {(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w,
+                              (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+            const i32x8 rb = {(int)rl[q][0], (int)rl[q][1], (int)rl[q][2], (int)rl[q][3],
+                              (int)rl[q][4], (int)rl[q][5], (int)rl[q][6], (int)rl[q][7]};
+            qa[u] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(sa, rb, qa[u], 0, 0, 0, 127 + 8, 0, 127);
+          }
+        }
+      }
+      if (tb >= 0 && tb < kNT) {
+        const int g = tb / 2;                 // this half's chunk receiving the bits
+        float r[16];
+#pragma unroll
+        for (int e = 15; e >= 0; --e) {
+          r[e] = bucket_sym_scaled<R>(acc[tb][e], rsc, Ts, As, P[g], J[g]);
+          g2 = fmaf(r[e], r[e], g2);
+        }
+        // limbs: k steps 2 tb, 2 tb + 1 take elements 0..7 and 8..15 of this tile
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+          for (int w2 = 0; w2 < 2; ++w2) {
+            // elements e0 .. e0 + 3 of the tile: two fp16 pairs and one e4m3 dword (dword
+            // (tb % 2) * 4 + 2 kk + w2 of k step tb / 2 holds coordinates 4 apart)
+            const int e0 = 8 * kk + 4 * w2;
+            const uint32_t hp0 = pack_f16_rne(r[e0], r[e0 + 1]);
+            const uint32_t hp1 = pack_f16_rne(r[e0 + 2], r[e0 + 3]);
+            rh[2 * tb + kk][2 * w2] = hp0;
+            rh[2 * tb + kk][2 * w2 + 1] = hp1;
+            uint32_t q8;
+            asm("" : "=v"(q8));   // both halves are written below; no initial value needed
+            q8 = __builtin_amdgcn_cvt_pk_fp8_f32(residual_below_f16<0>(hp0, r[e0]),
+                                                 residual_below_f16<1>(hp0, r[e0 + 1]), q8, false);
+            q8 = __builtin_amdgcn_cvt_pk_fp8_f32(residual_below_f16<0>(hp1, r[e0 + 2]),
+                                                 residual_below_f16<1>(hp1, r[e0 + 3]),
+                                                 q8, true);
+            rl[tb / 2][(tb % 2) * 4 + 2 * kk + w2] = q8;
+          }
+      }
+    }
+    // ---- signs: output j = 64h + 16u + e of tile u, fed from the highest.  The products
+    // are of -r', so a set sign bit means p = S r >= 0 (an exact zero lies in the band) ----
+    uint32_t B[2] = {0u, 0u};
+#pragma unroll
+    for (int u = kNT - 1; u >= 0; --u)
+#pragma unroll
+      for (int e = 15; e >= 0; --e) B[u / 2] = shift_in_sign(B[u / 2], qa[u][e]);
+    float gsum;
+    {
+      auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(g2), __float_as_uint(g2), false, false);
+      gsum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    const float gam = __builtin_amdgcn_sqrtf(gsum) * __builtin_amdgcn_rcpf(sc * rsc);
+    // ---- store: half h writes chunks 2h and 2h + 1 (R plane words and the sign word
+    // each); half 0 also the norm and gamma.  Lanes past the last vector encoded a copy of
+    // the last vector and write the same bytes to its record (no branch around the stores,
+    // which keeps the memory-counter waits exact) ----
+    {
+      const int64_t row = v0 + c < a.n ? v0 + c : a.n - 1;
+      uint32_t* rec = reinterpret_cast<uint32_t*>(a.codes + row * a.rec_bytes + s.rec_off);
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        uint32_t* w = rec + (2 * h + g) * (R + 1);
+        w[R - 1] = ~P[g];
+#pragma unroll
+        for (int m = 0; m < R - 1; ++m) w[m] = J[g][m] ^ P[g];
+        w[R] = B[g];
+      }
+      if (h == 0) {
+        rec[4 * (R + 1)] = __float_as_uint(nrm);
+        rec[4 * (R + 1) + 1] = __float_as_uint(gam);
+      }
+    }
+  }
+}
+
+int launch_encode128(const EncodeArgs& ea, hipStream_t st) {
+  const int64_t iters = (ea.n + 31) / 32;
+  int64_t blocks = (iters + kWaves - 1) / kWaves;
+  if (blocks > 1024) blocks = 1024;
+  const dim3 grid((unsigned)blocks), block(kWaves * kWave);
+  const bool vec = ea.vec_load && ea.s.d == kD;
+#define TQ_E128(RR)                                                                          \
+  case RR:                                                                                   \
+    if (vec)                                                                                 \
+      hipLaunchKernelGGL((encode128_kernel<RR, true>), grid, block, 0, st, ea);              \
+    else                                                                                     \
+      hipLaunchKernelGGL((encode128_kernel<RR, false>), grid, block, 0, st, ea);             \
+    break;
+  switch (ea.s.R) {
+    TQ_E128(1)
+    TQ_E128(2)
+    TQ_E128(3)
+    TQ_E128(4)
+    default: return (int)hipErrorInvalidValue;
+  }
+#undef TQ_E128
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? 0 : (int)e;
+}
+
+}  // namespace tq

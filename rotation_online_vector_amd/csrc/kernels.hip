@@ -8,42 +8,10 @@
 #include <cmath>
 #include <cstdint>
 
-#include "tq_internal.h"
+#include "device_common.h"
 
 namespace tq {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(4))) float f32x4;
-typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
-typedef __attribute__((ext_vector_type(8))) int i32x8;
-
-constexpr int kWave = 64;
-constexpr int kBlock = 256;   // 4 waves per workgroup
-
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ __forceinline__ float flip_sign(float v, uint32_t bit) {
-  return __uint_as_float(__float_as_uint(v) ^ (bit << 31));
-}
-
-// The p-th odd-popcount subset of R index bits, in increasing order (the order in which
-// the host lists the parity planes and their coefficients).
-template <int R>
-__host__ __device__ constexpr uint32_t pmask_c(int p) {
-  int n = 0;
-  for (uint32_t S = 1; S < (1u << R); ++S) {
-    if (__builtin_popcount(S) % 2 == 0) continue;
-    if (n == p) return S;
-    ++n;
-  }
-  return 0;
-}
 
 // ============================================================================ encode
 // Norm split, rotation z = Pi x / ||x|| with Pi = Ht S3 Ht S2 Ht S1 (TurboQuant technical
@@ -141,18 +109,6 @@ __device__ __forceinline__ void qjl_signs_mfma(const SubDev& s, const uint16_t* 
   }
 }
 
-struct EncodeArgs {
-  SubDev s;
-  const void* x;
-  int64_t n;
-  int64_t ldx;
-  uint8_t* codes;
-  int rec_bytes;
-  int is_bf16;
-  int vec_load;   // rows 16-byte aligned and no channel gather: vector loads
-  uint16_t* rw_hi;  // two-pass encode (long vectors): residual limbs [n][D], high and low
-  uint16_t* rw_lo;
-};
 
 // SPLIT: the QJL stage is left to qjl_gemm_kernel; the residual limbs go to a.rw_hi/rw_lo
 // instead of LDS and the sign words of the records are written by that kernel.
@@ -475,71 +431,6 @@ __global__ void __launch_bounds__(512) qjl_gemm_kernel(QjlGemmArgs a) {
 // coordinates, i.e. one whole code word at D = 128 (two or four lane groups share a word at
 // D = 64 or 32 and are combined with lane-group swaps).  The QJL rows are permuted alike.
 
-constexpr int kEncWaves = 8;
-
-__device__ __forceinline__ uint32_t or_over_lane_groups(uint32_t v) {
-  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  const uint32_t x = a[0] | a[1];
-  auto b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-  return b[0] | b[1];
-}
-
-__device__ __forceinline__ float sum_over_lane_groups(float v) {
-  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  const float x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__device__ __forceinline__ bf16x8 bf16x8_from_words(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
-  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-  const u32x4 u = {w0, w1, w2, w3};
-  return __builtin_bit_cast(bf16x8, u);
-}
-
-__device__ __forceinline__ f16x8 f16x8_from_words(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3) {
-  typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
-  const u32x4 u = {w0, w1, w2, w3};
-  return __builtin_bit_cast(f16x8, u);
-}
-
-// Two bf16 values (one word), times a power of two when SCALE, as two fp16 values (one
-// word).  Exact when the (scaled) values lie in the fp16 normal range; smaller ones round
-// toward zero on the fp16 subnormal grid (absolute error below 2^-24).
-template <bool SCALE>
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w, float scale) {
-  float lo = __uint_as_float(w << 16), hi = __uint_as_float(w & 0xFFFF0000u);
-  if constexpr (SCALE) {
-    lo *= scale;
-    hi *= scale;
-  }
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
-}
-
-__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
-  typedef __attribute__((ext_vector_type(2))) float f32x2;
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-  const f32x2 v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-#define pack2_bf16 pack_bf16_rne
-
-// v - (one half of the packed bf16 pair hp), exact when that half is v rounded to bf16: one
-// bf16 dot product hp . sel + v with sel = -1 in the chosen half and 0 in the other, which
-// reads the packed pair directly instead of unpacking it first.
-__device__ __forceinline__ float residual_below_bf16(uint32_t hp, uint32_t sel, float v) {
-  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, hp),
-                                         __builtin_bit_cast(bf16x2, sel), v, false);
-}
-
-// The selector (-1, 0) as a register value.  Written as a constant it is folded into the
-// inline constant -1.0, which this instruction reads as the pair (0, -1): the wrong half.
-__device__ __forceinline__ uint32_t neg_one_low_half() {
-  uint32_t v;
-  asm("v_mov_b32 %0, 0xbf80" : "=v"(v));
-  return v;
-}
 
 // 8 consecutive input elements of one row (zero beyond d), as XL exact bf16 limbs packed
 // two per word: limbs[l][w] holds elements 2w, 2w+1 of limb l.  `row` must be a valid row
@@ -609,61 +500,6 @@ __device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0
   }
 }
 
-// Per-lane building blocks of the bucketize.  The select and the shift-in are written out
-// as single instructions, so that chains of them stay a fixed sequence (the compiler
-// otherwise rebuilds the selects into an integer index and compare chains).  The comparison,
-// which reads the matrix-core results, stays a builtin: the compiler inserts the wait states
-// a read of an MFMA result needs, which it does not do for an inline-assembly operand.
-// Lane mask of |z| >= t (one v_cmp with the abs modifier; 3 = ordered greater-or-equal).
-__device__ __forceinline__ uint64_t abs_ge_mask(float z, float t) {
-  return __builtin_amdgcn_fcmpf(__builtin_fabsf(z), t, 3);
-}
-// Per lane: m ? b : a.
-__device__ __forceinline__ float select_mask(uint64_t m, float a, float b) {
-  float r;
-  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(m));
-  return r;
-}
-// w = 2 w + (this lane's bit of m).
-__device__ __forceinline__ uint32_t shift_in_mask(uint32_t w, uint64_t m) {
-  uint64_t carry;
-  asm("v_addc_co_u32_e64 %0, %1, %0, %0, %2" : "+v"(w), "=s"(carry) : "s"(m));
-  return w;
-}
-// w = 2 w + sign bit of f.
-__device__ __forceinline__ uint32_t shift_in_sign(uint32_t w, float f) {
-  return __builtin_amdgcn_alignbit(w, __float_as_uint(f), 31);
-}
-
-// One coordinate of the symmetric Lloyd-Max quantizer.  The codebook is mirror-symmetric
-// with its middle threshold at 0, so idx = 2^(R-1) [z >= 0] + (z >= 0 ? j : 2^(R-1) - 1 - j)
-// with j the cell of |z| among the positive thresholds tp[] (levels ap[]).  The sign goes to
-// P (bit set = negative), the bits of j to J[R-2..0]; the index planes are formed per word
-// afterwards: plane R-1 = ~P, plane m = J[m] ^ P.  Returns the residual z - c[idx].
-// (|z| equal to a threshold may land in either neighbouring cell; such a coordinate is
-// within rounding of the boundary in any precision.)
-template <int R>
-__device__ __forceinline__ float bucket_sym(float z, const float* tp, const float* ap,
-                                            uint32_t& P, uint32_t* J) {
-  constexpr int H = 1 << (R - 1);
-  float tc[H > 1 ? H - 1 : 1], lc[H];
-#pragma unroll
-  for (int j = 0; j < H - 1; ++j) tc[j] = tp[j];
-#pragma unroll
-  for (int j = 0; j < H; ++j) lc[j] = ap[j];
-#pragma unroll
-  for (int m = R - 2; m >= 0; --m) {
-    const int half = 1 << m;                 // thresholds left: 2 half - 1, middle half - 1
-    const uint64_t mk = abs_ge_mask(z, tc[half - 1]);
-    J[m] = shift_in_mask(J[m], mk);
-#pragma unroll
-    for (int j = 0; j < half - 1; ++j) tc[j] = select_mask(mk, tc[j], tc[half + j]);
-#pragma unroll
-    for (int j = 0; j < half; ++j) lc[j] = select_mask(mk, lc[j], lc[half + j]);
-  }
-  P = shift_in_sign(P, z);
-  return z - copysignf(lc[0], z);
-}
 
 // A lane's partial code word holds its D/4 bits at the top of the order fed (bit 0 = its
 // first coordinate); place it at its offset in the 32-bit word and merge the lane groups
@@ -3324,6 +3160,7 @@ int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, i
   ea.vec_load = (ea.s.chan == nullptr) && ((uintptr_t)x % 16 == 0) && ((ldx * es) % 16 == 0);
   ea.rw_hi = ea.rw_lo = nullptr;
   hipStream_t st = (hipStream_t)stream;
+  if (ea.s.D == 128 && ea.is_bf16 && ea.s.k16_32 && !ea.s.mse) return launch_encode128(ea, st);
   if (ea.s.D <= 128 && ea.s.rotk) return launch_encode_mfma(ea, st);
   switch (ea.s.D) {
     case 32: return launch_encode_d<32>(ea, st);

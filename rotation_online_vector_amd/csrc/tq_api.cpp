@@ -52,6 +52,9 @@ struct SubHost {
   std::vector<uint16_t> rotk16;  // K in one fp16 limb, when every |K| <= 2048 (else empty)
   std::vector<uint16_t> rotkt16; // K^T the same way (dequantization), with rotk16
   std::vector<uint16_t> sperm;
+  std::vector<uint16_t> k16_32;  // operands of the D = 128 32x32 encoder (may stay empty)
+  std::vector<uint16_t> s16_32;
+  std::vector<uint8_t> s8_32;
 };
 
 constexpr int kMfmaMaxD = 128;
@@ -113,6 +116,8 @@ uint16_t fp16_bits_of_small_int(int64_t v) {
   return (uint16_t)(sign | (uint32_t)(e + 15) << 10 | mant);
 }
 
+void mfma32_operand_tables(SubHost& h, const std::vector<int64_t>& K);
+
 void mfma_operand_tables(SubHost& h) {
   const int D = h.D, NJT = D / 16, NKS = D / 32;
   const std::vector<int64_t> K = rotation_integer_matrix(h.signs, D);
@@ -147,6 +152,87 @@ void mfma_operand_tables(SubHost& h) {
           const int col = G * (D / 4) + 8 * ks + e;
           if (!h.S.empty()) h.sperm[at] = h.S[(size_t)row * D + col];
         }
+  mfma32_operand_tables(h, K);
+}
+
+// Output row rho of a 32-row tile t of the 32x32 encoder (lane half h' = (rho / 4) % 2,
+// accumulator element 4 i + j with i = rho / 8, j = rho % 4) is coordinate
+// 64 h' + 16 t + 4 i + j: each lane half then holds 64 consecutive coordinates.
+int permuted_row32(int tile, int rho) {
+  return 64 * ((rho >> 2) & 1) + 16 * tile + 4 * (rho >> 3) + (rho & 3);
+}
+
+// fp16 bit pattern of v when v is exactly representable (normal or subnormal), else false.
+bool fp16_bits_exact(double v, uint16_t* out) {
+  if (v == 0.0) { *out = std::signbit(v) ? 0x8000u : 0u; return true; }
+  const uint16_t sign = v < 0 ? 0x8000u : 0u;
+  const double a = std::fabs(v);
+  int e;
+  const double m = std::frexp(a, &e);             // a = m 2^e, m in [0.5, 1)
+  if (e > 16) return false;                       // beyond the largest fp16
+  if (e >= -13) {                                 // normal: 11 significant bits
+    const double q = std::ldexp(m, 11);
+    if (q != std::floor(q)) return false;
+    *out = (uint16_t)(sign | (uint32_t)(e - 1 + 15) << 10 | ((uint32_t)q & 0x3FFu));
+    return true;
+  }
+  const double q = std::ldexp(a, 24);             // subnormal: multiples of 2^-24
+  if (q != std::floor(q) || q >= 1024.0) return false;
+  *out = (uint16_t)(sign | (uint32_t)q);
+  return true;
+}
+
+// fp8 e4m3 (bias 7, 3 mantissa bits, subnormals in steps of 2^-9, largest 448), rounded to
+// nearest with ties to even; magnitudes past 448 saturate.
+uint8_t e4m3_rne_bits(double v) {
+  const uint8_t sign = std::signbit(v) ? 0x80u : 0u;
+  double a = std::fabs(v);
+  if (a >= 448.0) return sign | 0x7Eu;
+  int e;
+  std::frexp(a, &e);                              // a in [2^(e-1), 2^e)
+  int ex = e - 1;                                 // unbiased exponent of a
+  if (ex < -6) ex = -6;                           // subnormal range shares 2^-6's step
+  const double step = std::ldexp(1.0, ex - 3);
+  double q = std::nearbyint(a / step);            // ties to even (default rounding mode)
+  double r = q * step;
+  if (r == 0.0) return sign;
+  std::frexp(r, &e);
+  const int er = e - 1;
+  if (er < -6) return sign | (uint8_t)(int)std::ldexp(r, 9);           // subnormal: m 2^-9
+  const int mant = (int)(std::ldexp(r, -er) * 8.0) - 8;
+  return sign | (uint8_t)((er + 7) << 3) | (uint8_t)mant;
+}
+
+// Operand tables of the D = 128 32x32 encoder (see encode128.hip); left empty when K or
+// 2^8 S is not exact in fp16 (the 16x16 encoder then serves the plan).
+void mfma32_operand_tables(SubHost& h, const std::vector<int64_t>& K) {
+  if (h.D != 128 || h.S.empty() || h.rotk16.empty()) return;
+  const int D = 128;
+  std::vector<uint16_t> k16((size_t)4 * 8 * 64 * 8), s16((size_t)4 * 8 * 64 * 8);
+  std::vector<uint8_t> s8((size_t)4 * 2 * 64 * 32);
+  for (int t = 0; t < 4; ++t)
+    for (int l = 0; l < 64; ++l) {
+      const int row = permuted_row32(t, l % 32), hh = l / 32;
+      for (int ks = 0; ks < 8; ++ks)
+        for (int e = 0; e < 8; ++e) {
+          const size_t at = (((size_t)t * 8 + ks) * 64 + l) * 8 + e;
+          k16[at] = fp16_bits_of_small_int(K[(size_t)row * D + 16 * ks + 8 * hh + e]);
+          const uint32_t sb = (uint32_t)h.S[(size_t)row * D + 64 * hh + 8 * ks + e] << 16;
+          float sf;
+          memcpy(&sf, &sb, 4);
+          if (!fp16_bits_exact(256.0 * (double)sf, &s16[at])) return;
+        }
+      for (int q = 0; q < 2; ++q)
+        for (int e = 0; e < 32; ++e) {
+          const uint32_t sb = (uint32_t)h.S[(size_t)row * D + 64 * hh + 32 * q + e] << 16;
+          float sf;
+          memcpy(&sf, &sb, 4);
+          s8[(((size_t)t * 2 + q) * 64 + l) * 32 + e] = e4m3_rne_bits((double)sf);
+        }
+    }
+  h.k16_32 = std::move(k16);
+  h.s16_32 = std::move(s16);
+  h.s8_32 = std::move(s8);
 }
 
 // Coefficients a_S of the parity planes of odd subsets S of the R index bits:
@@ -272,6 +358,7 @@ tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mas
   size_t bytes = 0;
   size_t off_sign[2] = {0, 0}, off_S[2] = {0, 0}, off_chan[2] = {0, 0};
   size_t off_rotk[2] = {0, 0}, off_rotk16[2] = {0, 0}, off_rotkt16[2] = {0, 0}, off_sperm[2] = {0, 0};
+  size_t off_k16_32[2] = {0, 0}, off_s16_32[2] = {0, 0}, off_s8_32[2] = {0, 0};
   auto take = [&](size_t b) { size_t o = bytes; bytes += (b + 255) / 256 * 256; return o; };
   for (int i = 0; i < pd.nsub; ++i) {
     SubHost& h = subs[i];
@@ -313,6 +400,9 @@ tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mas
       off_rotk16[i] = take(h.rotk16.size() * 2);
       off_rotkt16[i] = take(h.rotkt16.size() * 2);
       off_sperm[i] = take(h.sperm.size() * 2);
+      off_k16_32[i] = take(h.k16_32.size() * 2);
+      off_s16_32[i] = take(h.s16_32.size() * 2);
+      off_s8_32[i] = take(h.s8_32.size());
     }
   }
   void* mem = nullptr;
@@ -341,6 +431,12 @@ tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mas
                     hipMemcpyHostToDevice);
     if (e == hipSuccess && !h.sperm.empty())
       e = hipMemcpy(base + off_sperm[i], h.sperm.data(), h.sperm.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && !h.k16_32.empty())
+      e = hipMemcpy(base + off_k16_32[i], h.k16_32.data(), h.k16_32.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && !h.s16_32.empty())
+      e = hipMemcpy(base + off_s16_32[i], h.s16_32.data(), h.s16_32.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && !h.s8_32.empty())
+      e = hipMemcpy(base + off_s8_32[i], h.s8_32.data(), h.s8_32.size(), hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(mem);
       delete plan;
@@ -353,6 +449,10 @@ tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mas
     s.rotk16 = h.rotk16.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_rotk16[i]);
     s.rotkt16 = h.rotkt16.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_rotkt16[i]);
     s.sperm = h.sperm.empty() ? nullptr : reinterpret_cast<const uint16_t*>(base + off_sperm[i]);
+    const bool e32 = !h.k16_32.empty() && !h.s16_32.empty() && !h.s8_32.empty();
+    s.k16_32 = e32 ? reinterpret_cast<const uint16_t*>(base + off_k16_32[i]) : nullptr;
+    s.s16_32 = e32 ? reinterpret_cast<const uint16_t*>(base + off_s16_32[i]) : nullptr;
+    s.s8_32 = e32 ? reinterpret_cast<const uint8_t*>(base + off_s8_32[i]) : nullptr;
   }
   *out = plan;
   return TQ_OK;

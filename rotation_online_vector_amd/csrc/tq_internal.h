@@ -45,6 +45,11 @@ struct SubDev {
                            // lane group G of tile jt, element e: 32 (jt/2) + 8 G + 4 (jt%2) + e;
                            // k = rotated coordinate), with rotk16
   const uint16_t* sperm;  // [D/16][D/32][64][8]: S with columns in the residual register order
+  // D = 128 inner-product plans whose K is exact in fp16 and whose 2^8 S is exact in fp16:
+  // operands of the 32x32 encoder (encode128.hip; layouts described there), else null
+  const uint16_t* k16_32;  // [4][8][64][8] fp16 K
+  const uint16_t* s16_32;  // [4][8][64][8] fp16 2^8 S
+  const uint8_t* s8_32;    // [4][2][64][32] e4m3 S
 };
 
 struct PlanDev {

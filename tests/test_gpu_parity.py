@@ -269,3 +269,31 @@ def test_invalid_calls_raise():
         tq.tq_encode(plan, x)
     with pytest.raises(tq.TqError):
         tq.tq_topk(torch.zeros((2, 5), device=DEV), 6)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 5])
+def test_encode_d128_bf16_every_index_width(bits):
+    """bf16 keys at d = 128 (the 32-vector matrix-core encoder): every index width, a ragged
+    count (not a multiple of 32 or of a workgroup's 256), zero vectors, strided rows, and
+    norms from 1e-8 to 1e8 in one batch (so waves take both the unscaled and the scaled fp16
+    conversion)."""
+    d = 128
+    rng = np.random.default_rng(100 + bits)
+    n = 4096 + 77
+    xs = rng.standard_normal((n, d))
+    xs[:, :6] = rng.standard_t(3, (n, 6))
+    xs[2048:] *= 10.0 ** rng.uniform(-8, 8, (n - 2048, 1))
+    xs[[0, 31, 32, 4100]] = 0.0
+    big = torch.zeros((n, 192), dtype=torch.bfloat16, device=DEV)
+    big[:, 40:168] = torch.from_numpy(xs.astype(np.float32)).to(DEV).to(torch.bfloat16)
+    x = big[:, 40:168]                                        # row stride 192, offset 40
+    sp = otq.make_split_plan(d, bits, 21)
+    plan = tq.tq_plan_create(d, bits, 21)
+    codes, ref, got, stats = _encode_and_compare(sp, plan, x, "d=128 b=%d" % bits)
+    # the same vectors as a contiguous tensor give the same records
+    again = tq.tq_encode(plan, x.contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(codes, again)
+    ys = rng.standard_normal((8, d)).astype(np.float32)
+    est = tq.tq_score(plan, torch.from_numpy(ys).to(DEV), codes, n=n).cpu().numpy()
+    parity.check_scores_end_to_end(sp, ref, got, est, ys, _np(x), "d=128 b=%d" % bits)
