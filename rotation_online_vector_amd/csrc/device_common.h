@@ -179,4 +179,72 @@ __device__ __forceinline__ float bucket_sym(float z, const float* tp, const floa
   return z - copysignf(lc[0], z);
 }
 
+
+// ----------------------------------------------------------------- bit-sliced scorer images
+// For a symmetric codebook the level of an R-bit index expands over the parity planes of odd
+// subsets of its bits: c[idx] = sum_S a_S (2 p_S - 1).  The MSE term of a key becomes
+// 2 sum_S a_S <y', p_S> - A0 sum y', and the QJL term 2 <w, beta> - sum w: binary dot
+// products.  Keys are fed to the MFMA as fp4 values 0 / 0.5 straight from their bits; the
+// query side is an fp8 image holding three limbs of a_S y' (or w) per query, so that the
+// four queries of a group and their three limbs fill the 16 rows of one MFMA tile.
+//
+// A-operand (fp8, 16 x 128) lane layout of v_mfma_scale_f32_16x16x128_f8f6f4 on gfx950:
+// row = lane % 16; element e of lane group G = lane / 16 is K = 16 G + e (e < 16) or
+// K = 64 + 16 G + (e - 16).  B-operand (fp4, 128 x 16): column = lane % 16, element e of
+// lane group G is K = 32 G + e.  A key plane word W of chunk G gives the B dwords
+// (W >> j) & 0x11111111, j = 0..3: nibble m of dword j is coordinate 32 G + 4 m + j at
+// K = 32 G + 8 j + m.
+
+__device__ __forceinline__ int bitslice_coord(int K) {
+  const int G = K >> 5, j = (K & 31) >> 3, m = K & 7;
+  return 32 * G + 4 * m + j;
+}
+
+struct QFusedArgs {
+  SubDev s;
+  const void* q;
+  int64_t ldq;
+  int is_bf16;
+  int64_t nq;            // total query rows
+  int64_t nq_per_group;
+  int n_qtiles;
+  uint32_t* img;         // [groups*qtiles][n_planes+1][64][8]
+  float* ec;             // [groups*qtiles][4][4]
+};
+
+// ============================================================================ scorers
+// est = n (<y', c[idx]> + gamma sqrt(pi/2)/k <w, 2 beta - 1>), summed over sub-plans
+// (technical overview §1.2.3 unbiased two-stage estimate, §4.2.2 per-coordinate centroid
+// lookup with the query under the same rotation).
+
+struct ScoreArgs {
+  PlanDev p;
+  const uint8_t* codes;
+  int64_t n;
+  int64_t nq_per_group;
+  int n_qtiles;
+  int vec_out;           // score rows 16-byte aligned (scores and n % 4): vector stores
+  float* scores;
+  const uint32_t* img[2];
+  const float* ec[2];
+  const float* yrot[2];
+  const float* w[2];
+};
+
+template <int NP> struct PlaneImg { i32x8 a[NP + 1]; };
+
+__device__ __forceinline__ i32x8 fp4_operand(uint32_t W) {
+  i32x8 b;
+  b[0] = (int)(W & 0x11111111u);
+  b[1] = (int)((W >> 1) & 0x11111111u);
+  b[2] = (int)((W >> 2) & 0x11111111u);
+  b[3] = (int)((W >> 3) & 0x11111111u);
+  b[4] = 0; b[5] = 0; b[6] = 0; b[7] = 0;
+  return b;
+}
+
+// Bit-sliced scorer for sub-plans with D <= 128 (score128.hip): query images, then scores.
+int launch_qprep_bitslice(const QFusedArgs& fa, int D, int64_t nq, hipStream_t st);
+bool dispatch_bitslice(const ScoreArgs& sa, int64_t n_gt, hipStream_t st);
+
 }  // namespace tq
