@@ -164,6 +164,25 @@ tq_status tq_score(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_p
                    void* stream);
 
 /*
+ * tq_score without any allocation, for callers that cannot allocate: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors are those of tq_score (identical scores from the
+ * same kernels), except that the query workspace is a fixed 16 MiB device array
+ * inside the library (one per device, kept until the process ends) instead of a
+ * stream-ordered temporary; no hipMalloc, hipFree or allocating routine is called.
+ * A request whose workspace exceeds 16 MiB returns TQ_EINVAL before any launch.
+ * For plans with every D <= 128 the workspace is about
+ *   n_groups * ceil(nq_per_group/4) * (2^(R-1) + 1) * 2 KiB per sub-plan
+ * (R index bits), e.g. 128 groups of 4 queries at 3 bits use 0.78 MiB; longer
+ * vectors also keep y' and S y' per query (8 D bytes each).  Every call on a
+ * device shares that device's array: calls that overlap on one device (different
+ * streams, or host threads) race and must be ordered by the caller.
+ */
+tq_status tq_score_noalloc(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_per_group,
+                           int64_t n_groups, int64_t ldq, const void* codes, int64_t n,
+                           float* scores, void* stream);
+
+/*
  * Top-k per row of a score matrix (the first, quantized stage of two-stage
  * retrieval: overview §4.2.2): for each of nq rows of `scores` (device
  * float32 [nq][n]) the k largest values, ordered by (-value, index).

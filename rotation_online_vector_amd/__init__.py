@@ -37,7 +37,7 @@ class tq_plan_desc(ctypes.Structure):
 
 
 EXPORTED = ["tq_status_string", "tq_plan_create", "tq_plan_destroy", "tq_plan_info",
-            "tq_plan_create_mse", "tq_encode", "tq_score", "tq_score_topk", "tq_topk",
+            "tq_plan_create_mse", "tq_encode", "tq_score", "tq_score_noalloc", "tq_score_topk", "tq_topk",
             "tq_dequantize", "tq_attend", "tq_rerank", "tq_calibrate_outliers",
             "tq_encode_scatter", "tq_qjl", "tq_codebook", "tq_rotation_signs", "tq_qjl_matrix"]
 
@@ -70,6 +70,8 @@ def load_library(path=LIB_PATH):
     lib.tq_encode.restype = i32
     lib.tq_score.argtypes = [vp, vp, i32, i64, i64, i64, vp, i64, vp, vp]
     lib.tq_score.restype = i32
+    lib.tq_score_noalloc.argtypes = [vp, vp, i32, i64, i64, i64, vp, i64, vp, vp]
+    lib.tq_score_noalloc.restype = i32
     lib.tq_topk.argtypes = [vp, i64, i64, i32, vp, vp, vp]
     lib.tq_topk.restype = i32
     lib.tq_plan_create_mse.argtypes = [i32, i32, u64, ctypes.POINTER(vp)]
@@ -256,6 +258,27 @@ def tq_score(plan, q, codes, n, nq_per_group=None, n_groups=1, scores=None, stre
         scores = torch.empty((nq, n), dtype=torch.float32, device=q.device)
     _out(scores, torch.float32, nq * n, "scores")
     _check("tq_score", load_library().tq_score(
+        plan.handle, ctypes.c_void_p(q.data_ptr()), _dtype_code(q), nq_per_group, n_groups, ld,
+        ctypes.c_void_p(codes.data_ptr()), n, ctypes.c_void_p(scores.data_ptr()), _stream(stream)))
+    return scores
+
+
+def tq_score_noalloc(plan, q, codes, n, scores, nq_per_group=None, n_groups=1, stream=None):
+    """tq_score through the entry point that allocates nothing (the query workspace is the
+    library's fixed per-device array); `scores` must be provided by the caller."""
+    import torch
+    if scores is None:
+        raise ValueError("tq_score_noalloc writes into a caller-provided scores tensor")
+    _on_gpu(q, codes, scores)
+    nq, ld = _rows(q, plan.d)
+    if nq_per_group is None:
+        nq_per_group = nq // n_groups
+    if nq_per_group * n_groups != nq:
+        raise ValueError("query rows != nq_per_group * n_groups")
+    if codes.numel() < n_groups * n * plan.record_bytes:
+        raise ValueError("codes buffer too small")
+    _out(scores, torch.float32, nq * n, "scores")
+    _check("tq_score_noalloc", load_library().tq_score_noalloc(
         plan.handle, ctypes.c_void_p(q.data_ptr()), _dtype_code(q), nq_per_group, n_groups, ld,
         ctypes.c_void_p(codes.data_ptr()), n, ctypes.c_void_p(scores.data_ptr()), _stream(stream)))
     return scores

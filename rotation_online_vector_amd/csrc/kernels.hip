@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "device_common.h"
 
@@ -2868,9 +2869,13 @@ static int dispatch_wide(int R, dim3 grid, hipStream_t st, const ScoreArgs& sa, 
   return (int)hipErrorInvalidValue;
 }
 
+// ws_ext: a workspace the caller provides (ws_cap bytes) instead of a stream-ordered
+// temporary; requests that need more than ws_cap return hipErrorOutOfMemory without
+// launching anything.
 static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq_per_group,
                              int64_t n_groups, int64_t ldq, const uint8_t* codes, int64_t n,
-                             float* scores, const TopkOut* tko, hipStream_t st) {
+                             float* scores, const TopkOut* tko, hipStream_t st,
+                             void* ws_ext = nullptr, size_t ws_cap = 0) {
   const int64_t nq = nq_per_group * n_groups;
   bool small = true;
   for (int sb = 0; sb < p.nsub; ++sb) small = small && p.sub[sb].D <= 128;
@@ -2918,8 +2923,14 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
     }
   }
   void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, bytes, st);
-  if (e != hipSuccess) return (int)e;
+  hipError_t e = hipSuccess;
+  if (ws_ext != nullptr) {
+    if (bytes > ws_cap) return (int)hipErrorOutOfMemory;
+    ws = ws_ext;
+  } else {
+    e = hipMallocAsync(&ws, bytes, st);
+    if (e != hipSuccess) return (int)e;
+  }
   uint8_t* wb = static_cast<uint8_t*>(ws);
   if (tko != nullptr && !fused) scores = reinterpret_cast<float*>(wb + off_sc);
   ScoreArgs sa;
@@ -2954,7 +2965,7 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
       fa.ec = reinterpret_cast<float*>(wb + off_ec[sb]);
       const int prc = launch_qprep_bitslice(fa, p.sub[sb].D, nq, st);
       if (prc) {
-        (void)hipFreeAsync(ws, st);
+        if (ws_ext == nullptr) (void)hipFreeAsync(ws, st);
         return prc;
       }
       sa.img[sb] = fa.img;
@@ -3023,8 +3034,10 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
   if (!rc) rc = hip_rc(hipGetLastError());
   if (!rc && tko != nullptr && !fused)
     rc = launch_topk(scores, nq, n, tko->k, tko->ids, tko->vals, st);
-  e = hipFreeAsync(ws, st);
-  if (!rc && e != hipSuccess) rc = (int)e;
+  if (ws_ext == nullptr) {
+    e = hipFreeAsync(ws, st);
+    if (!rc && e != hipSuccess) rc = (int)e;
+  }
   return rc;
 }
 
@@ -3033,6 +3046,50 @@ int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, 
   if (n == 0 || nq_per_group == 0 || n_groups == 0) return 0;
   return launch_score_impl(p, q, dt, nq_per_group, n_groups, ldq, codes, n, scores, nullptr,
                            (hipStream_t)stream);
+}
+
+// ------------------------------------------------------- scoring without any allocation
+// A fixed device array serves as the query workspace of tq_score_noalloc, for callers that
+// cannot allocate (HIP graph capture, serving loops, harnesses that forbid hipMalloc).  Each
+// device holds its own copy for the life of the process; its address is looked up once per
+// device (with that device current) and only that address is handed to kernels (the array's
+// name in host code is a host-side stand-in, not a device address).  Calls that overlap on
+// one device share the array and race; the kernels write every byte they later read, so
+// nothing needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[kScoreScratchBytes];
+
+namespace {
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kScratchMaxDevices] = {};
+}  // namespace
+
+// The current device's address of `scratch`, resolved on first use.
+static int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kScratchMaxDevices) return (int)hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return (int)e;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return 0;
+}
+
+int launch_score_noalloc(const PlanDev& p, const void* q, int dt, int64_t nq_per_group,
+                         int64_t n_groups, int64_t ldq, const uint8_t* codes, int64_t n,
+                         float* scores, void* stream) {
+  if (n == 0 || nq_per_group == 0 || n_groups == 0) return 0;
+  void* ws = nullptr;
+  const int rc = scratch_address(&ws);
+  if (rc) return rc;
+  return launch_score_impl(p, q, dt, nq_per_group, n_groups, ldq, codes, n, scores, nullptr,
+                           (hipStream_t)stream, ws, kScoreScratchBytes);
 }
 
 int launch_score_topk(const PlanDev& p, const void* q, int dt, int64_t nq_per_group,

@@ -537,6 +537,25 @@ tq_status tq_score(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_p
                                static_cast<const uint8_t*>(codes), n, scores, stream));
 }
 
+tq_status tq_score_noalloc(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_per_group,
+                           int64_t n_groups, int64_t ldq, const void* codes, int64_t n,
+                           float* scores, void* stream) {
+  if (!plan || nq_per_group < 0 || n_groups < 0 || n < 0 || (dt != TQ_F32 && dt != TQ_BF16))
+    return TQ_EINVAL;
+  if (nq_per_group == 0 || n_groups == 0 || n == 0) return TQ_OK;
+  const int es = dt == TQ_BF16 ? 2 : 4;
+  if (!q || !codes || !scores || ldq < plan->dev.d || (uintptr_t)q % es || (uintptr_t)codes % 16 ||
+      (uintptr_t)scores % 4)
+    return TQ_EINVAL;
+  if (nq_per_group * n_groups > (int64_t)1 << 31 || n_groups > 65535 * 64) return TQ_EINVAL;
+  if (!plan_device_ok(plan)) return TQ_EINVAL;
+  if (is_mse(plan)) return TQ_EUNSUPPORTED;
+  const int rc = launch_score_noalloc(plan->dev, q, (int)dt, nq_per_group, n_groups, ldq,
+                                      static_cast<const uint8_t*>(codes), n, scores, stream);
+  if (rc == (int)hipErrorOutOfMemory) return TQ_EINVAL;   // workspace beyond the fixed array
+  return from_hip(rc);
+}
+
 tq_status tq_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids, float* vals,
                   void* stream) {
   if (nq < 0 || n < 0 || k < 1 || k > 64 || k > n || n >= ((int64_t)1 << 31)) return TQ_EINVAL;

@@ -76,6 +76,12 @@ int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, i
 int launch_qjl(const SubDev& s, const float* r, int64_t n, uint32_t* beta, void* stream);
 int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, int64_t n_groups,
                  int64_t ldq, const uint8_t* codes, int64_t n, float* scores, void* stream);
+// Bytes of the fixed per-device array behind launch_score_noalloc; a request whose query
+// workspace exceeds it returns hipErrorOutOfMemory before any launch.
+constexpr size_t kScoreScratchBytes = (size_t)16 << 20;
+int launch_score_noalloc(const PlanDev& p, const void* q, int dt, int64_t nq_per_group,
+                         int64_t n_groups, int64_t ldq, const uint8_t* codes, int64_t n,
+                         float* scores, void* stream);
 int launch_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids, float* vals,
                 void* stream);
 int launch_dequantize(const PlanDev& p, const uint8_t* codes, int64_t n, void* out, int dt,
