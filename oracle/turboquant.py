@@ -127,14 +127,23 @@ def qjl_signs(S, r):
     return (p >= 0).astype(np.uint8), p
 
 
+def unit_rotated(Xp, signs):
+    """(norm, z) with z = Pi (x / ||x||) for each row x of Xp (z = 0 for a zero row).  Pi is
+    linear, so the row is rotated first and divided by its norm afterwards: the Hadamard
+    rounds then act on the stored values themselves, exactly when these carry few significant
+    bits, and a rotated coordinate that is exactly zero stays zero instead of picking up a
+    rounding residue of either sign (which would move it across a threshold at 0)."""
+    norm = np.sqrt(np.sum(Xp * Xp, axis=-1))
+    safe = np.where(norm > 0, norm, 1.0)
+    z = np.where(norm[:, None] > 0, rotation.rotate(Xp, signs) / safe[:, None], 0.0)
+    return norm, z
+
+
 def encode(plan, X):
     """Codes of the rows of X (n x d): dict with idx (n, D), beta (n, k),
     norm (n,), gamma (n,), and the intermediates z, r, p."""
     Xp = pad(X, plan.D)
-    norm = np.sqrt(np.sum(Xp * Xp, axis=-1))
-    safe = np.where(norm > 0, norm, 1.0)
-    U = np.where(norm[:, None] > 0, Xp / safe[:, None], 0.0)
-    z = rotation.rotate(U, plan.signs)
+    norm, z = unit_rotated(Xp, plan.signs)
     idx = bucketize(z, plan.thresholds)
     zhat = plan.levels[idx]
     r = z - zhat
@@ -159,10 +168,7 @@ def encode_mse(plan, X):
     """TurboQuant-MSE codes of the rows of X (n x d): dict with idx (n, D), norm (n,) and
     the rotated direction z."""
     Xp = pad(X, plan.D)
-    norm = np.sqrt(np.sum(Xp * Xp, axis=-1))
-    safe = np.where(norm > 0, norm, 1.0)
-    U = np.where(norm[:, None] > 0, Xp / safe[:, None], 0.0)
-    z = rotation.rotate(U, plan.signs)
+    norm, z = unit_rotated(Xp, plan.signs)
     return dict(idx=bucketize(z, plan.thresholds), norm=norm, z=z)
 
 

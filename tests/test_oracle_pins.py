@@ -208,6 +208,43 @@ def test_bucketize_is_nearest_codeword(D, n):
     assert np.array_equal(grid[best], tq.bucketize(z, t))
 
 
+@pytest.mark.parametrize("D,bits", [(32, 5), (64, 3)])
+def test_exactly_zero_rotated_coordinate_lands_above_the_zero_threshold(D, bits):
+    """An even number of cells puts a threshold at exactly 0, and a coordinate of Pi x that is
+    exactly 0 counts it (idx = number of thresholds <= z), whatever the norm.  The inputs are
+    integer rows x = S1 H S2 H S3 H w (integer arithmetic here, written with the Hadamard
+    butterfly rather than the oracle's dense matrix), so that Pi x = D^(3/2) w exactly: the
+    coordinates of the integer vector w that are 0 rotate to exact zeros."""
+    plan = tq.make_plan(D, bits, 3, 0)
+    L = 1 << plan.R
+    assert plan.thresholds[L // 2 - 1] == 0.0
+    rng = np.random.default_rng(6)
+    w = rng.integers(-40, 41, (50, D))
+    w[:, 0] = 0
+    w[np.arange(50), rng.integers(1, D, 50)] = 0
+
+    def fwht(v):                                   # integer Sylvester transform along rows
+        v = v.copy()
+        h = 1
+        while h < D:
+            a = v.reshape(-1, D // (2 * h), 2, h)
+            v = np.concatenate([a[:, :, 0] + a[:, :, 1], a[:, :, 0] - a[:, :, 1]], axis=2).reshape(-1, D)
+            h *= 2
+        return v
+
+    sg = plan.signs.astype(np.int64)
+    x = w
+    for r in (2, 1, 0):                            # Pi^T up to D^(3/2): S1 H S2 H S3 H
+        x = fwht(x) * sg[r][None, :]
+    for scale in (1.0, 2.0 ** -30, 3.0 ** 20):
+        codes = tq.encode(plan, x.astype(np.float64) * scale)
+        zero = w == 0
+        assert np.all(codes["z"][zero] == 0.0)
+        assert np.all(codes["idx"][zero] == L // 2)
+        nz = ~zero
+        assert np.all((codes["idx"][nz] >= L // 2) == (w[nz] > 0))
+
+
 # ---------------------------------------------------------------- estimator
 
 def _plan_for_seed(D, bits, seed, levels, t):
