@@ -293,23 +293,22 @@ def build_workload(name, dev, W_all):
                                                 group=W["group"], n_outlier=W["n_outlier"],
                                                 outlier_scale=W["outlier_scale"], seed=W["seed"])
         n_kv, n_tok, d, G = W["n_kv"], W["n_tok"], W["d"], W["group"]
-        plans = []
+        # one layer plan: each head's own outlier mask, shared tables; one grouped encode
+        # and one score call cover all heads
+        masks = np.zeros((n_kv, d), dtype=np.uint8)
         for h in range(n_kv):
-            mask = np.zeros(d, dtype=np.uint8)
-            mask[ch[h]] = 1
-            plans.append(tq.tq_plan_create(d, W["bits"], W["seed"], mask, W["outlier_bits"]))
-        rb = plans[0].record_bytes
-        codes = torch.empty((n_kv, n_tok, rb), dtype=torch.uint8, device=dev)
-        scores = torch.empty((n_kv, G, n_tok), dtype=torch.float32, device=dev)
-        qv = queries.view(n_kv, G, d)
+            masks[h, ch[h]] = 1
+        plan = tq.tq_plan_create_heads(d, W["bits"], W["seed"], masks, W["outlier_bits"])
+        rb = plan.record_bytes
+        codes = torch.empty((n_kv * n_tok, rb), dtype=torch.uint8, device=dev)
+        scores = torch.empty((n_kv * G, n_tok), dtype=torch.float32, device=dev)
+        xk, qv = keys.view(n_kv * n_tok, d), queries.view(n_kv * G, d)
 
         def enc():
-            for h in range(n_kv):
-                tq.tq_encode(plans[h], keys[h], codes[h])
+            tq.tq_encode_groups(plan, xk, n_kv, codes)
 
         def sco():
-            for h in range(n_kv):
-                tq.tq_score(plans[h], qv[h], codes[h], n=n_tok, scores=scores[h])
+            tq.tq_score(plan, qv, codes, n=n_tok, nq_per_group=G, n_groups=n_kv, scores=scores)
         n_keys, n_scores = n_kv * n_tok, n_kv * G * n_tok
         return dict(
             config={"workload": W["name"], "kv_heads": n_kv, "tokens": n_tok, "d": d,
@@ -319,7 +318,7 @@ def build_workload(name, dev, W_all):
             phases=[("tq_encode", enc), ("tq_score", sco)],
             bytes={"tq_encode": n_keys * d * 2 + n_keys * rb,
                    "tq_score": n_keys * rb + n_scores * 4 + n_kv * G * d * 2},
-            n_keys=n_keys, n_scores=n_scores, keep=(plans, keys, queries, codes, scores))
+            n_keys=n_keys, n_scores=n_scores, keep=(plan, keys, queries, codes, scores))
     if name in ("retrieval", "retrieval2", "small"):
         if name != "small":
             keys, queries = workloads.retrieval_inputs(dev, n_keys=W["n_keys"],

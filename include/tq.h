@@ -78,6 +78,7 @@ typedef struct tq_plan_desc {
   int32_t n_subplans;     /* 1, or 2 with an outlier mask (0 = regular, 1 = outlier) */
   int32_t record_bytes;   /* bytes per encoded vector */
   int32_t mode;           /* tq_mode */
+  int32_t n_heads;        /* channel lists per sub-plan: 1, or the heads of a layer plan */
   tq_subplan_desc sub[2];
 } tq_plan_desc;
 
@@ -103,6 +104,27 @@ const char* tq_status_string(tq_status status);
  */
 tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_mask,
                          int outlier_bits, tq_plan** out);
+
+/*
+ * Layer plan for the key cache of several heads (overview §4.1.1: analyse the
+ * heads, keep about a quarter of each head's channels as outliers at a higher
+ * bit-width).  Every head shares the plan's codebooks, rotations and QJL
+ * matrices (the split plan of tq_plan_create with the same d, bits, seed and
+ * outlier_bits), but gathers its regular and outlier channels by its own mask,
+ * so one launch serves all heads of a layer.  Group g of tq_encode_groups,
+ * tq_score, tq_score_noalloc and tq_score_topk uses head g % n_heads (e.g.
+ * groups ordered [sequence][head]); vector i of tq_encode_scatter uses head
+ * i % n_heads.  The result for head h equals what a plan made by
+ * tq_plan_create(d, bits, seed, outlier_masks + h*d, outlier_bits) gives.
+ *   outlier_masks  host [n_heads][d] bytes (nonzero = outlier), copied; every
+ *                  head selects the same number of channels, 1..d-1
+ *   2 <= d <= 128, 1 <= n_heads <= 1024, bits and outlier_bits 2..5.
+ * tq_encode (use tq_encode_groups), tq_dequantize, tq_attend and tq_qjl do not
+ * take layer plans (TQ_EINVAL / TQ_EUNSUPPORTED).
+ * Errors: TQ_EINVAL (range, null, unequal outlier counts), TQ_ENOMEM, TQ_EDEVICE.
+ */
+tq_status tq_plan_create_heads(int d, int bits, uint64_t seed, int n_heads,
+                               const uint8_t* outlier_masks, int outlier_bits, tq_plan** out);
 
 /*
  * Create a TurboQuant-MSE plan (overview §1.2.1-1.2.2: rotation and a Lloyd-Max
@@ -142,6 +164,18 @@ tq_status tq_encode(const tq_plan* plan, const void* x, tq_dtype dt, int64_t n, 
                     void* codes, void* stream);
 
 /*
+ * tq_encode of n_groups groups of n_per_group rows: rows g*n_per_group ..
+ * +n_per_group-1 of x (row stride ldx) are group g, and their records are
+ * records g*n_per_group .. of `codes`.  With a layer plan (tq_plan_create_heads)
+ * group g gathers the channels of head g % n_heads; all groups and heads are
+ * encoded by one launch per sub-plan.  With an ordinary plan it equals tq_encode
+ * of n_groups*n_per_group rows.  1 <= n_groups <= 65535 when n_per_group > 0.
+ * Errors: as tq_encode; TQ_EUNSUPPORTED for a layer plan with D > 128.
+ */
+tq_status tq_encode_groups(const tq_plan* plan, const void* x, tq_dtype dt, int64_t n_groups,
+                           int64_t n_per_group, int64_t ldx, void* codes, void* stream);
+
+/*
  * Score queries against encoded vectors with the unbiased estimate
  *   est = n_x * ( <y', c[idx]> + gamma * sqrt(pi/2)/k * sum_j (S y')_j (2 beta_j - 1) ),
  *   y' = the plan's rotation applied to the zero-padded query
@@ -153,7 +187,9 @@ tq_status tq_encode(const tq_plan* plan, const void* x, tq_dtype dt, int64_t n, 
  *           stride ldq elements; rows g*nq_per_group .. +nq_per_group-1 are group g
  *   codes   device, n_groups * n records; group g's records start at record g*n
  *   scores  device float32 [n_groups*nq_per_group][n], row-major, written entirely
- * Raw inner-product estimates: no 1/sqrt(d), no softmax.
+ * Raw inner-product estimates: no 1/sqrt(d), no softmax.  With a layer plan
+ * (tq_plan_create_heads), n_groups must be a multiple of n_heads and group g
+ * uses head g % n_heads.
  * Uses a stream-ordered temporary of n_groups*nq_per_group*(6*D) floats per
  * sub-plan (hipMallocAsync / hipFreeAsync on `stream`).
  * Errors: TQ_EINVAL (null, negative sizes, ldq < d, misalignment), TQ_ENOMEM,
@@ -283,7 +319,10 @@ tq_status tq_calibrate_outliers(const void* x, tq_dtype dt, int64_t n, int64_t l
  * lands there is unspecified.
  *   cache  device, cache_rows * record_bytes bytes, 16-byte aligned
  *   index  device int64 [n]
- * The records pass through a stream-ordered temporary of n * record_bytes.
+ * For plans whose sub-plans all have D <= 128 the records are written straight
+ * to their rows (one launch per sub-plan, no temporary); longer vectors pass
+ * through a stream-ordered temporary of n * record_bytes.  With a layer plan,
+ * vector i uses head i % n_heads (n <= 65535).
  * Errors: TQ_EINVAL (null with n > 0, n < 0, ldx < d, misalignment),
  * TQ_ENOMEM, TQ_EDEVICE.  n = 0 is a no-op.
  */

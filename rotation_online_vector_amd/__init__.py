@@ -33,11 +33,12 @@ class tq_subplan_desc(ctypes.Structure):
 class tq_plan_desc(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("n_subplans", ctypes.c_int32),
                 ("record_bytes", ctypes.c_int32), ("mode", ctypes.c_int32),
-                ("sub", tq_subplan_desc * 2)]
+                ("n_heads", ctypes.c_int32), ("sub", tq_subplan_desc * 2)]
 
 
 EXPORTED = ["tq_status_string", "tq_plan_create", "tq_plan_destroy", "tq_plan_info",
-            "tq_plan_create_mse", "tq_encode", "tq_score", "tq_score_noalloc", "tq_score_topk", "tq_topk",
+            "tq_plan_create_mse", "tq_plan_create_heads", "tq_encode", "tq_encode_groups",
+            "tq_score", "tq_score_noalloc", "tq_score_topk", "tq_topk",
             "tq_dequantize", "tq_attend", "tq_rerank", "tq_calibrate_outliers",
             "tq_encode_scatter", "tq_qjl", "tq_codebook", "tq_rotation_signs", "tq_qjl_matrix"]
 
@@ -68,6 +69,10 @@ def load_library(path=LIB_PATH):
     lib.tq_plan_info.restype = i32
     lib.tq_encode.argtypes = [vp, vp, i32, i64, i64, vp, vp]
     lib.tq_encode.restype = i32
+    lib.tq_encode_groups.argtypes = [vp, vp, i32, i64, i64, i64, vp, vp]
+    lib.tq_encode_groups.restype = i32
+    lib.tq_plan_create_heads.argtypes = [i32, i32, u64, i32, vp, i32, ctypes.POINTER(vp)]
+    lib.tq_plan_create_heads.restype = i32
     lib.tq_score.argtypes = [vp, vp, i32, i64, i64, i64, vp, i64, vp, vp]
     lib.tq_score.restype = i32
     lib.tq_score_noalloc.argtypes = [vp, vp, i32, i64, i64, i64, vp, i64, vp, vp]
@@ -200,6 +205,21 @@ def tq_plan_create(d, bits, seed, outlier_mask=None, outlier_bits=0):
     return _plan_from_handle(lib, h)
 
 
+def tq_plan_create_heads(d, bits, seed, outlier_masks, outlier_bits):
+    """Layer plan over the heads of a key cache: one outlier mask per head ([n_heads, d],
+    each selecting the same number of channels), shared codebooks, rotations and QJL
+    matrices; group g of the grouped calls uses head g % n_heads."""
+    lib = load_library()
+    h = ctypes.c_void_p()
+    masks = np.ascontiguousarray(np.asarray(outlier_masks).astype(np.uint8))
+    if masks.ndim != 2 or masks.shape[1] != d:
+        raise ValueError("outlier_masks must be [n_heads, d]")
+    _check("tq_plan_create_heads", lib.tq_plan_create_heads(
+        int(d), int(bits), ctypes.c_uint64(int(seed)), int(masks.shape[0]),
+        masks.ctypes.data_as(ctypes.c_void_p), int(outlier_bits), ctypes.byref(h)))
+    return _plan_from_handle(lib, h)
+
+
 def tq_plan_create_mse(d, bits, seed):
     """TurboQuant-MSE plan: all b bits on the Lloyd-Max codebook, no QJL stage."""
     lib = load_library()
@@ -213,7 +233,7 @@ def _plan_from_handle(lib, h):
     desc = tq_plan_desc()
     _check("tq_plan_info", lib.tq_plan_info(h, ctypes.byref(desc)))
     info = {"d": desc.d, "n_subplans": desc.n_subplans, "record_bytes": desc.record_bytes,
-            "mode": "mse" if desc.mode == 1 else "inner_product",
+            "mode": "mse" if desc.mode == 1 else "inner_product", "n_heads": desc.n_heads,
             "sub": [{f: getattr(desc.sub[i], f) for f, _ in tq_subplan_desc._fields_}
                     for i in range(desc.n_subplans)]}
     return Plan(h, info)
@@ -239,6 +259,23 @@ def tq_encode(plan, x, codes=None, stream=None):
     _out(codes, torch.uint8, n * plan.record_bytes, "codes")
     _check("tq_encode", load_library().tq_encode(
         plan.handle, ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n, ld,
+        ctypes.c_void_p(codes.data_ptr()), _stream(stream)))
+    return codes
+
+
+def tq_encode_groups(plan, x, n_groups, codes=None, stream=None):
+    """Records of n_groups equal groups of rows of x ([n_groups * n_per_group, d] or
+    [n_groups, n_per_group, d]); with a layer plan, group g uses head g % n_heads."""
+    import torch
+    _on_gpu(x, codes)
+    n, ld = _rows(x, plan.d)
+    if n_groups <= 0 or n % n_groups:
+        raise ValueError("rows must split into n_groups equal groups")
+    if codes is None:
+        codes = torch.empty((n, plan.record_bytes), dtype=torch.uint8, device=x.device)
+    _out(codes, torch.uint8, n * plan.record_bytes, "codes")
+    _check("tq_encode_groups", load_library().tq_encode_groups(
+        plan.handle, ctypes.c_void_p(x.data_ptr()), _dtype_code(x), n_groups, n // n_groups, ld,
         ctypes.c_void_p(codes.data_ptr()), _stream(stream)))
     return codes
 

@@ -52,10 +52,36 @@ struct EncodeArgs {
   int vec_load;   // rows 16-byte aligned and no channel gather: vector loads
   uint16_t* rw_hi;  // two-pass encode (long vectors): residual limbs [n][D], high and low
   uint16_t* rw_lo;
+  // Groups (grid z): group g encodes rows g n .. g n + n - 1 into its records, or into the
+  // cache rows out_index[g n ..] (rows outside [0, out_cap) are skipped); plans with one
+  // channel list per head gather with the list of head g % n_heads.
+  int n_heads;
+  const int64_t* out_index;
+  int64_t out_cap;
 };
 
+// This workgroup's group: its input rows, its output records (or cache-row indices) and its
+// head's channel list.
+__device__ __forceinline__ void encode_group_view(EncodeArgs& a) {
+  const int64_t g = blockIdx.z;
+  const int es = a.is_bf16 ? 2 : 4;
+  a.x = static_cast<const uint8_t*>(a.x) + g * a.n * a.ldx * es;
+  if (a.out_index)
+    a.out_index += g * a.n;
+  else
+    a.codes += g * a.n * a.rec_bytes;
+  if (a.s.chan) a.s.chan += (g % a.n_heads) * a.s.d;
+}
+
+// Record of local row `row` (null when an append's cache row lies outside the cache).
+__device__ __forceinline__ uint8_t* encode_record(const EncodeArgs& a, int64_t row) {
+  if (a.out_index == nullptr) return a.codes + row * a.rec_bytes + a.s.rec_off;
+  const int64_t r = a.out_index[row];
+  return (r >= 0 && r < a.out_cap) ? a.codes + r * a.rec_bytes + a.s.rec_off : nullptr;
+}
+
 // D = 128 inner-product plans with bf16 input and the 32x32 operand tables (encode128.hip).
-int launch_encode128(const EncodeArgs& ea, hipStream_t st);
+int launch_encode128(const EncodeArgs& ea, hipStream_t st, int64_t n_groups);
 
 constexpr int kEncWaves = 8;
 
@@ -208,6 +234,7 @@ struct QFusedArgs {
   int64_t nq;            // total query rows
   int64_t nq_per_group;
   int n_qtiles;
+  int n_heads;           // group g gathers with the channel list of head g % n_heads
   uint32_t* img;         // [groups*qtiles][n_planes+1][64][8]
   float* ec;             // [groups*qtiles][4][4]
 };

@@ -95,9 +95,12 @@ __device__ __forceinline__ float bucket_sym_scaled(float z, float s, const float
 //   s8  [4 tiles][2 k steps][64 lanes][32] e4m3 S, rows permuted, byte e of lane half h =
 //                                          coordinate 64 h + 32 q + e (the same k slot map on
 //                                          both operands of the fp8 product)
-template <int R, bool VEC>
+// SCATTER: records go to the cache rows a.out_index[] (appending to a cache) instead of
+// consecutive records.
+template <int R, bool VEC, bool SCATTER>
 __global__ void __launch_bounds__(kWaves * kWave) encode128_kernel(EncodeArgs a) {
   constexpr int H = 1 << (R - 1);
+  encode_group_view(a);
   __shared__ uint4 lk[kNT * kKS * 64];
   __shared__ uint4 ls16[kNT * kKS * 64];
   __shared__ uint4 ls8[kNT * kQS * 64 * 2];
@@ -306,7 +309,13 @@ __global__ void __launch_bounds__(kWaves * kWave) encode128_kernel(EncodeArgs a)
     // which keeps the memory-counter waits exact) ----
     {
       const int64_t row = v0 + c < a.n ? v0 + c : a.n - 1;
-      uint32_t* rec = reinterpret_cast<uint32_t*>(a.codes + row * a.rec_bytes + s.rec_off);
+      uint32_t* rec;
+      if constexpr (SCATTER) {
+        rec = reinterpret_cast<uint32_t*>(encode_record(a, row));
+      } else {
+        rec = reinterpret_cast<uint32_t*>(a.codes + row * a.rec_bytes + s.rec_off);
+      }
+      if (SCATTER && rec == nullptr) continue;
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         uint32_t* w = rec + (2 * h + g) * (R + 1);
@@ -323,18 +332,21 @@ __global__ void __launch_bounds__(kWaves * kWave) encode128_kernel(EncodeArgs a)
   }
 }
 
-int launch_encode128(const EncodeArgs& ea, hipStream_t st) {
+int launch_encode128(const EncodeArgs& ea, hipStream_t st, int64_t n_groups) {
   const int64_t iters = (ea.n + 31) / 32;
   int64_t blocks = (iters + kWaves - 1) / kWaves;
-  if (blocks > 1024) blocks = 1024;
-  const dim3 grid((unsigned)blocks), block(kWaves * kWave);
+  const int64_t cap = n_groups > 1 ? (1024 + n_groups - 1) / n_groups : 1024;
+  if (blocks > cap) blocks = cap;
+  const dim3 grid((unsigned)blocks, 1, (unsigned)n_groups), block(kWaves * kWave);
   const bool vec = ea.vec_load && ea.s.d == kD;
 #define TQ_E128(RR)                                                                          \
   case RR:                                                                                   \
-    if (vec)                                                                                 \
-      hipLaunchKernelGGL((encode128_kernel<RR, true>), grid, block, 0, st, ea);              \
+    if (ea.out_index)                                                                        \
+      hipLaunchKernelGGL((encode128_kernel<RR, false, true>), grid, block, 0, st, ea);       \
+    else if (vec)                                                                            \
+      hipLaunchKernelGGL((encode128_kernel<RR, true, false>), grid, block, 0, st, ea);       \
     else                                                                                     \
-      hipLaunchKernelGGL((encode128_kernel<RR, false>), grid, block, 0, st, ea);             \
+      hipLaunchKernelGGL((encode128_kernel<RR, false, false>), grid, block, 0, st, ea);      \
     break;
   switch (ea.s.R) {
     TQ_E128(1)

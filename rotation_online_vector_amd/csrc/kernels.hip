@@ -525,6 +525,7 @@ __device__ __forceinline__ uint32_t combine_word(uint32_t part, int G) {
 // MSE: TurboQuant-MSE records (R = b index bits, then the norm): no residual, no QJL stage.
 template <int D, int R, int XL, bool VEC, bool F16, bool MSE>
 __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeArgs a) {
+  encode_group_view(a);
   constexpr int NJT = D / 16;        // 16-row tiles of coordinates
   constexpr int NKS = D / 32;        // 32-wide k steps
   constexpr int H = 1 << (R - 1);    // cells of |z|
@@ -775,8 +776,8 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int64_t row = v0 + 16 * t + col;
-      if (row < a.n) {
-        uint32_t* rec = reinterpret_cast<uint32_t*>(a.codes + row * a.rec_bytes + s.rec_off);
+      uint32_t* rec = row < a.n ? reinterpret_cast<uint32_t*>(encode_record(a, row)) : nullptr;
+      if (rec != nullptr) {
         if ((G * (D / 4)) % 32 == 0) {          // first lane group of its code word
           const int g = G * D / 128;
 #pragma unroll
@@ -2772,13 +2773,14 @@ static void launch_encode_mfma_dx(const EncodeArgs& ea, hipStream_t st, dim3 gri
     launch_encode_mfma_dxv<D, XL, false>(ea, st, grid);
 }
 
-static int launch_encode_mfma(const EncodeArgs& ea, hipStream_t st) {
+static int launch_encode_mfma(const EncodeArgs& ea, hipStream_t st, int64_t n_groups) {
   // one wave iteration encodes 32 vectors; enough blocks to fill the chip a few times over,
-  // each looping over its share
+  // each looping over its share (of its group's rows)
   const int64_t iters = (ea.n + 31) / 32;
   int64_t blocks = (iters + kEncWaves - 1) / kEncWaves;
-  if (blocks > 2048) blocks = 2048;
-  const dim3 grid((unsigned)blocks);
+  const int64_t cap = n_groups > 1 ? (2048 + n_groups - 1) / n_groups : 2048;
+  if (blocks > cap) blocks = cap;
+  const dim3 grid((unsigned)blocks, 1, (unsigned)n_groups);
   switch (ea.s.D * 2 + ea.is_bf16) {
     case 32 * 2 + 1: launch_encode_mfma_dx<32, 1>(ea, st, grid); break;
     case 32 * 2: launch_encode_mfma_dx<32, 3>(ea, st, grid); break;
@@ -2791,9 +2793,12 @@ static int launch_encode_mfma(const EncodeArgs& ea, hipStream_t st) {
   return hip_rc(hipGetLastError());
 }
 
-int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, int64_t ldx,
-                  uint8_t* codes, void* stream) {
-  if (n == 0) return 0;
+// n rows per group, n_groups groups (grid z); with `index`, record i goes to cache row
+// index[i] of a cache of `cap` rows instead (D <= 128 encoders only).
+static int launch_encode_to(const PlanDev& p, int sub, const void* x, int dt, int64_t n,
+                            int64_t ldx, uint8_t* codes, void* stream, int64_t n_groups,
+                            const int64_t* index, int64_t cap) {
+  if (n == 0 || n_groups == 0) return 0;
   EncodeArgs ea;
   ea.s = p.sub[sub];
   ea.x = x;
@@ -2805,9 +2810,13 @@ int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, i
   const int es = ea.is_bf16 ? 2 : 4;
   ea.vec_load = (ea.s.chan == nullptr) && ((uintptr_t)x % 16 == 0) && ((ldx * es) % 16 == 0);
   ea.rw_hi = ea.rw_lo = nullptr;
+  ea.n_heads = p.n_heads > 0 ? p.n_heads : 1;
+  ea.out_index = index;
+  ea.out_cap = cap;
   hipStream_t st = (hipStream_t)stream;
-  if (ea.s.D == 128 && ea.is_bf16 && ea.s.k16_32 && !ea.s.mse) return launch_encode128(ea, st);
-  if (ea.s.D <= 128 && ea.s.rotk) return launch_encode_mfma(ea, st);
+  if (ea.s.D == 128 && ea.is_bf16 && ea.s.k16_32 && !ea.s.mse) return launch_encode128(ea, st, n_groups);
+  if (ea.s.D <= 128 && ea.s.rotk) return launch_encode_mfma(ea, st, n_groups);
+  if (n_groups != 1 || index != nullptr) return (int)hipErrorInvalidValue;
   switch (ea.s.D) {
     case 32: return launch_encode_d<32>(ea, st);
     case 64: return launch_encode_d<64>(ea, st);
@@ -2818,6 +2827,11 @@ int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, i
     case 2048: return launch_encode_d<2048>(ea, st);
   }
   return (int)hipErrorInvalidValue;
+}
+
+int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, int64_t ldx,
+                  uint8_t* codes, void* stream, int64_t n_groups) {
+  return launch_encode_to(p, sub, x, dt, n, ldx, codes, stream, n_groups, nullptr, 0);
 }
 
 template <int D>
@@ -2961,6 +2975,7 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
       fa.nq = nq;
       fa.nq_per_group = nq_per_group;
       fa.n_qtiles = qt_bs;
+      fa.n_heads = p.n_heads > 0 ? p.n_heads : 1;
       fa.img = reinterpret_cast<uint32_t*>(wb + off_img[sb]);
       fa.ec = reinterpret_cast<float*>(wb + off_ec[sb]);
       const int prc = launch_qprep_bitslice(fa, p.sub[sb].D, nq, st);
@@ -3284,6 +3299,19 @@ __global__ void __launch_bounds__(kBlock) scatter_records_kernel(const uint32_t*
 int launch_encode_scatter(const PlanDev& p, const void* x, int dt, int64_t n, int64_t ldx,
                           uint8_t* cache, int64_t cap, const int64_t* index, void* stream) {
   hipStream_t st = (hipStream_t)stream;
+  bool direct = true;
+  for (int i = 0; i < p.nsub; ++i) direct = direct && p.sub[i].D <= 128 && p.sub[i].rotk != nullptr;
+  if (direct) {
+    // the D <= 128 encoders write each record straight to its cache row: one launch per
+    // sub-plan; with one channel list per head, vector i is its own group (head i % n_heads)
+    const bool per_head = p.n_heads > 1;
+    int rc = 0;
+    for (int i = 0; i < p.nsub && !rc; ++i)
+      rc = launch_encode_to(p, i, x, dt, per_head ? 1 : n, ldx, cache, stream, per_head ? n : 1,
+                            index, cap);
+    return rc;
+  }
+  if (p.n_heads > 1) return (int)hipErrorInvalidValue;
   void* tmp = nullptr;
   hipError_t e = hipMallocAsync(&tmp, (size_t)n * p.rec_bytes, st);
   if (e != hipSuccess) return (int)e;

@@ -52,7 +52,7 @@ __global__ void __launch_bounds__(kBlock) qprep_bitslice_kernel(QFusedArgs a) {
       for (int r = 0; r < 3; ++r) sw[r][e] = i < D ? s.signs[r * (D / 32) + i / 32] : 0u;
       float val = 0.f;
       if (i < s.d) {
-        const int64_t ch = s.chan ? s.chan[i] : i;
+        const int64_t ch = s.chan ? s.chan[(grp % a.n_heads) * s.d + i] : i;
         val = a.is_bf16 ? bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(a.q)[qi * a.ldq + ch])
                         : reinterpret_cast<const float*>(a.q)[qi * a.ldq + ch];
       }

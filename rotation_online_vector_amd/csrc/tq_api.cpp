@@ -322,17 +322,29 @@ namespace {
 
 // Both plan kinds: inner-product (R = b - 1 index bits + QJL signs) and TurboQuant-MSE
 // (R = b index bits, no QJL matrix).  Arguments are validated by the callers.
+// outlier_mask: [n_heads][d] (one mask per head of a layer plan; every head selects the same
+// number of channels), or null with n_heads = 1.
 tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mask,
-                      int outlier_bits, bool mse, tq_plan** out) {
+                      int outlier_bits, bool mse, tq_plan** out, int n_heads = 1) {
   *out = nullptr;
   std::vector<SubHost> subs;
   if (outlier_mask) {
     if (outlier_bits < 2 || outlier_bits > kMaxR + 1) return TQ_EINVAL;
     SubHost reg, out_s;
-    for (int c = 0; c < d; ++c) (outlier_mask[c] ? out_s.chan : reg.chan).push_back(c);
-    if (reg.chan.empty() || out_s.chan.empty()) return TQ_EINVAL;
-    reg.d = (int)reg.chan.size(); reg.R = bits - 1;
-    out_s.d = (int)out_s.chan.size(); out_s.R = outlier_bits - 1;
+    int n_out = -1;
+    for (int h = 0; h < n_heads; ++h) {
+      const uint8_t* m = outlier_mask + (size_t)h * d;
+      int cnt = 0;
+      for (int c = 0; c < d; ++c) {
+        (m[c] ? out_s.chan : reg.chan).push_back(c);
+        cnt += m[c] ? 1 : 0;
+      }
+      if (n_out >= 0 && cnt != n_out) return TQ_EINVAL;   // every head: the same count
+      n_out = cnt;
+    }
+    reg.d = (int)reg.chan.size() / n_heads; reg.R = bits - 1;
+    out_s.d = (int)out_s.chan.size() / n_heads; out_s.R = outlier_bits - 1;
+    if (reg.d == 0 || out_s.d == 0) return TQ_EINVAL;
     subs.push_back(std::move(reg));
     subs.push_back(std::move(out_s));
   } else {
@@ -353,6 +365,7 @@ tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mas
   pd.d = d;
   pd.nsub = (int)subs.size();
   pd.rec_bytes = 0;
+  pd.n_heads = n_heads;
 
   // host tables and device layout
   size_t bytes = 0;
@@ -473,6 +486,16 @@ tq_status tq_plan_create(int d, int bits, uint64_t seed, const uint8_t* outlier_
   return create_plan(d, bits, seed, outlier_mask, outlier_bits, false, out);
 }
 
+tq_status tq_plan_create_heads(int d, int bits, uint64_t seed, int n_heads,
+                               const uint8_t* outlier_masks, int outlier_bits, tq_plan** out) {
+  if (!out) return TQ_EINVAL;
+  *out = nullptr;
+  if (d < 2 || d > kMfmaMaxD || bits < 2 || bits > kMaxR + 1 || n_heads < 1 ||
+      n_heads > kMaxHeads || !outlier_masks || outlier_bits < 2 || outlier_bits > kMaxR + 1)
+    return TQ_EINVAL;
+  return create_plan(d, bits, seed, outlier_masks, outlier_bits, false, out, n_heads);
+}
+
 tq_status tq_plan_create_mse(int d, int bits, uint64_t seed, tq_plan** out) {
   if (!out) return TQ_EINVAL;
   *out = nullptr;
@@ -493,6 +516,7 @@ tq_status tq_plan_info(const tq_plan* plan, tq_plan_desc* desc) {
   desc->n_subplans = plan->dev.nsub;
   desc->record_bytes = plan->dev.rec_bytes;
   desc->mode = is_mse(plan) ? TQ_MODE_MSE : TQ_MODE_INNER_PRODUCT;
+  desc->n_heads = plan->dev.n_heads;
   for (int i = 0; i < plan->dev.nsub; ++i) {
     const SubDev& s = plan->dev.sub[i];
     desc->sub[i].d = s.d;
@@ -505,9 +529,40 @@ tq_status tq_plan_info(const tq_plan* plan, tq_plan_desc* desc) {
   return TQ_OK;
 }
 
+tq_status tq_encode_groups(const tq_plan* plan, const void* x, tq_dtype dt, int64_t n_groups,
+                           int64_t n_per_group, int64_t ldx, void* codes, void* stream) {
+  if (!plan || n_groups < 0 || n_per_group < 0 || (dt != TQ_F32 && dt != TQ_BF16))
+    return TQ_EINVAL;
+  if (n_groups == 0 || n_per_group == 0) return TQ_OK;
+  const int es = dt == TQ_BF16 ? 2 : 4;
+  if (!x || !codes || ldx < plan->dev.d || (uintptr_t)x % es || (uintptr_t)codes % 16)
+    return TQ_EINVAL;
+  if (n_groups > 65535) return TQ_EINVAL;
+  if (!plan_device_ok(plan)) return TQ_EINVAL;
+  bool grouped_ok = true;   // the group grid runs on the D <= 128 encoders
+  for (int i = 0; i < plan->dev.nsub; ++i) grouped_ok = grouped_ok && plan->dev.sub[i].D <= kMfmaMaxD;
+  if (!grouped_ok && n_groups > 1) {
+    if (plan->dev.n_heads > 1) return TQ_EUNSUPPORTED;
+    // one channel list: the groups are simply consecutive rows
+    for (int i = 0; i < plan->dev.nsub; ++i) {
+      const int rc = launch_encode(plan->dev, i, x, (int)dt, n_groups * n_per_group, ldx,
+                                   static_cast<uint8_t*>(codes), stream);
+      if (rc) return from_hip(rc);
+    }
+    return TQ_OK;
+  }
+  for (int i = 0; i < plan->dev.nsub; ++i) {
+    const int rc = launch_encode(plan->dev, i, x, (int)dt, n_per_group, ldx,
+                                 static_cast<uint8_t*>(codes), stream, n_groups);
+    if (rc) return from_hip(rc);
+  }
+  return TQ_OK;
+}
+
 tq_status tq_encode(const tq_plan* plan, const void* x, tq_dtype dt, int64_t n, int64_t ldx,
                     void* codes, void* stream) {
   if (!plan || n < 0 || (dt != TQ_F32 && dt != TQ_BF16)) return TQ_EINVAL;
+  if (plan->dev.n_heads > 1) return TQ_EINVAL;   // a layer plan's rows need their head
   if (n == 0) return TQ_OK;
   const int es = dt == TQ_BF16 ? 2 : 4;
   if (!x || !codes || ldx < plan->dev.d || (uintptr_t)x % es || (uintptr_t)codes % 16)
@@ -531,6 +586,7 @@ tq_status tq_score(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_p
       (uintptr_t)scores % 4)
     return TQ_EINVAL;
   if (nq_per_group * n_groups > (int64_t)1 << 31 || n_groups > 65535 * 64) return TQ_EINVAL;
+  if (n_groups % plan->dev.n_heads) return TQ_EINVAL;   // group g reads head g % n_heads
   if (!plan_device_ok(plan)) return TQ_EINVAL;
   if (is_mse(plan)) return TQ_EUNSUPPORTED;
   return from_hip(launch_score(plan->dev, q, (int)dt, nq_per_group, n_groups, ldq,
@@ -548,6 +604,7 @@ tq_status tq_score_noalloc(const tq_plan* plan, const void* q, tq_dtype dt, int6
       (uintptr_t)scores % 4)
     return TQ_EINVAL;
   if (nq_per_group * n_groups > (int64_t)1 << 31 || n_groups > 65535 * 64) return TQ_EINVAL;
+  if (n_groups % plan->dev.n_heads) return TQ_EINVAL;   // group g reads head g % n_heads
   if (!plan_device_ok(plan)) return TQ_EINVAL;
   if (is_mse(plan)) return TQ_EUNSUPPORTED;
   const int rc = launch_score_noalloc(plan->dev, q, (int)dt, nq_per_group, n_groups, ldq,
@@ -579,6 +636,7 @@ tq_status tq_score_topk(const tq_plan* plan, const void* q, tq_dtype dt, int64_t
       (uintptr_t)codes % 16 || (uintptr_t)ids % 8 || (uintptr_t)vals % 4)
     return TQ_EINVAL;
   if (nq_per_group * n_groups > (int64_t)1 << 31 || n_groups > 65535 * 64) return TQ_EINVAL;
+  if (n_groups % plan->dev.n_heads) return TQ_EINVAL;
   if (!plan_device_ok(plan)) return TQ_EINVAL;
   if (is_mse(plan)) return TQ_EUNSUPPORTED;
   return from_hip(launch_score_topk(plan->dev, q, (int)dt, nq_per_group, n_groups, ldq,
@@ -592,6 +650,7 @@ tq_status tq_dequantize(const tq_plan* plan, const void* codes, int64_t n, void*
   const int es = dt == TQ_BF16 ? 2 : 4;
   if (!codes || !x || ldx < plan->dev.d || (uintptr_t)codes % 16 || (uintptr_t)x % es)
     return TQ_EINVAL;
+  if (plan->dev.n_heads > 1) return TQ_EUNSUPPORTED;
   if (!plan_device_ok(plan)) return TQ_EINVAL;
   return from_hip(launch_dequantize(plan->dev, static_cast<const uint8_t*>(codes), n, x, (int)dt,
                                     ldx, stream));
@@ -615,6 +674,7 @@ tq_status tq_attend(const tq_plan* vplan, const float* logits, int64_t nq_per_gr
   // pass-1 workgroup
   const int64_t rows = nq_per_group * n_groups;
   if (rows > 0x7FFFFFFF || ((n + 1023) / 1024) > ((int64_t)1 << 33) / rows) return TQ_EINVAL;
+  if (vplan->dev.n_heads > 1) return TQ_EUNSUPPORTED;
   if (!plan_device_ok(vplan)) return TQ_EINVAL;
   return from_hip(launch_attend(vplan->dev, logits, nq_per_group, n_groups, n, scale,
                                 static_cast<const uint8_t*>(vcodes), out, (int)dt, ldo, stream));
@@ -640,6 +700,7 @@ tq_status tq_encode_scatter(const tq_plan* plan, const void* x, tq_dtype dt, int
       (uintptr_t)index % 8)
     return TQ_EINVAL;
   if (!plan_device_ok(plan)) return TQ_EINVAL;
+  if (plan->dev.n_heads > 1 && n > 65535) return TQ_EINVAL;
   return from_hip(launch_encode_scatter(plan->dev, x, (int)dt, n, ldx, static_cast<uint8_t*>(cache),
                                         cache_rows, index, stream));
 }
@@ -666,6 +727,7 @@ tq_status tq_qjl(const tq_plan* plan, int subplan, const float* r, int64_t n, ui
   if (!plan || subplan < 0 || subplan >= plan->dev.nsub || n < 0) return TQ_EINVAL;
   if (n == 0) return TQ_OK;
   if (!r || !beta || (uintptr_t)r % 4 || (uintptr_t)beta % 4) return TQ_EINVAL;
+  if (plan->dev.n_heads > 1) return TQ_EUNSUPPORTED;
   if (!plan_device_ok(plan)) return TQ_EINVAL;
   if (is_mse(plan)) return TQ_EUNSUPPORTED;
   return from_hip(launch_qjl(plan->dev.sub[subplan], r, n, beta, stream));

@@ -9,6 +9,7 @@ namespace tq {
 constexpr int kMaxR = 4;         // index bits per coordinate: b - 1 with b <= 5
 constexpr int kMinD = 32;
 constexpr int kMaxD = 2048;
+constexpr int kMaxHeads = 1024;  // heads of a layer plan (one channel list each)
 
 // Host tables (host_tables.cpp)
 void philox4x32_10(uint64_t block, uint32_t domain, uint64_t seed, uint32_t out[4]);
@@ -36,7 +37,8 @@ struct SubDev {
   float coef_sum;   // sum of coef
   const uint32_t* signs;  // device [3][D/32]; bit set = -1
   const uint16_t* S;      // device [k][D] bf16 bit patterns
-  const int32_t* chan;    // device [d] input channel of each coordinate, or null (identity)
+  const int32_t* chan;    // device [n_heads][d] input channel of each coordinate (one list per
+                          // head of a layer plan), or null (identity)
   // D <= 128 only: the rotation and the QJL matrix pre-arranged as MFMA A operands
   // (16x16x32 bf16 tiles, 64 lanes x 8 values each)
   const uint16_t* rotk;   // [2 limbs][D/16 row tiles][D/32 k steps][64][8]: D^(3/2) Pi
@@ -56,6 +58,7 @@ struct PlanDev {
   int d;
   int nsub;
   int rec_bytes;
+  int n_heads;      // channel lists per sub-plan (a layer plan with one outlier mask per head)
   SubDev sub[2];
 };
 
@@ -72,7 +75,7 @@ struct tq_plan {
 // Kernel launchers (kernels.hip).  Return 0 or a HIP error code.
 namespace tq {
 int launch_encode(const PlanDev& p, int sub, const void* x, int dt, int64_t n, int64_t ldx,
-                  uint8_t* codes, void* stream);
+                  uint8_t* codes, void* stream, int64_t n_groups = 1);
 int launch_qjl(const SubDev& s, const float* r, int64_t n, uint32_t* beta, void* stream);
 int launch_score(const PlanDev& p, const void* q, int dt, int64_t nq_per_group, int64_t n_groups,
                  int64_t ldq, const uint8_t* codes, int64_t n, float* scores, void* stream);

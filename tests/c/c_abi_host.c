@@ -67,6 +67,17 @@ int main(void) {
         "score_topk without plan");
   CHECK(tq_score_topk(NULL, NULL, TQ_F32, 8, 1, 128, NULL, 5, 10, NULL, NULL, NULL) == TQ_EINVAL,
         "score_topk with k > n");
+  {
+    uint8_t masks[2 * 64];
+    memset(masks, 0, sizeof(masks));
+    masks[3] = masks[64 + 5] = masks[64 + 6] = 1;          /* 1 and 2 outlier channels */
+    CHECK(tq_plan_create_heads(64, 3, 0, 2, masks, 5, &plan) == TQ_EINVAL && plan == NULL,
+          "layer plan with unequal outlier counts rejected");
+    CHECK(tq_plan_create_heads(256, 3, 0, 2, masks, 5, &plan) == TQ_EINVAL, "layer plan d > 128 rejected");
+    CHECK(tq_plan_create_heads(64, 3, 0, 2, NULL, 5, &plan) == TQ_EINVAL, "layer plan without masks rejected");
+    CHECK(tq_plan_create_heads(64, 3, 0, 0, masks, 5, &plan) == TQ_EINVAL, "layer plan without heads rejected");
+    CHECK(tq_encode_groups(NULL, NULL, TQ_BF16, 2, 4, 64, NULL, NULL) == TQ_EINVAL, "grouped encode without plan");
+  }
   CHECK(tq_plan_create_mse(128, 0, 0, &plan) == TQ_EINVAL && plan == NULL, "mse plan bits = 0 rejected");
   CHECK(tq_plan_create_mse(128, 5, 0, &plan) == TQ_EINVAL, "mse plan bits = 5 rejected");
   CHECK(tq_plan_create_mse(128, 3, 0, NULL) == TQ_EINVAL, "mse plan without output");
