@@ -58,7 +58,35 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "rotation_online_vector_amd", "csrc", "kernels.hip")
+KERNEL_DIR = os.path.join(ROOT, "rotation_online_vector_amd", "csrc")
+
+# the arithmetic of each workload's step, by the operand formats its kernels use
+MIXED_D128 = "f16+f8+f4 mfma, f32 acc"
+DTYPES = {
+    "longctx": MIXED_D128, "kv": MIXED_D128, "split35": MIXED_D128, "split25": MIXED_D128,
+    "small": "bf16+f8+f4 mfma, f32 acc", "attend": MIXED_D128 + "; bf16 mfma attention",
+    "decode": MIXED_D128 + "; bf16 mfma attention", "mse": "bf16 mfma, f32 acc",
+    "retrieval": "f32 fwht, bf16+f8+f4 mfma, f32 acc",
+    "retrieval2": "f32 fwht, bf16+f8+f4 mfma, f32 acc",
+}
+OPERANDS_D128 = {
+    "tq_encode": "bf16 keys scaled to fp16 against the exact integer rotation in fp16; the "
+                 "residual as an fp16 limb against 2^8 S in fp16 plus an fp8 e4m3 limb against "
+                 "S in e4m3; fp32 accumulation, norms and comparisons",
+    "tq_score": "the rotated query and its QJL projection as three fp8 e4m3 limbs against "
+                "the key bit planes as fp4 {0, 1/2}; fp32 accumulation and epilogue",
+}
+
+
+def kernel_sources_sha256():
+    """sha256 over every kernel source (the .hip files and their headers), in name order."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(KERNEL_DIR)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(KERNEL_DIR, f), "rb").read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload, kernel_key):
@@ -66,10 +94,9 @@ def measured_traffic(workload, kernel_key):
     runs (profiles/traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE scaled by a copy of known
     size), or None when there is no record or the kernel source changed since the counters
     were taken."""
-    import hashlib
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)))
-        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        src = kernel_sources_sha256()
     except (OSError, ValueError):
         return None
     if rec.get("kernels_sha256") != src:
@@ -485,7 +512,7 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
+        "dtype": DTYPES[args.workload], "data": "synthetic",
         "config": wl["config"],
         "encode_vectors_per_s": (_rate(wl["n_keys"], kern["tq_encode"]["ms"])
                                  if "tq_encode" in kern else None),
@@ -502,6 +529,8 @@ def main():
         "roofline": roof,
         "hbm_ceiling": ceiling,
     }
+    if args.workload in ("longctx", "kv", "split35", "split25"):
+        out["operands"] = OPERANDS_D128
     if "quality" in wl:
         out["quality"] = wl["quality"]()
     if args.workload == "longctx" and not args.no_cpu_baseline:

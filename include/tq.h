@@ -27,6 +27,16 @@
  *   - A plan is immutable after creation and may be used from several streams
  *     and threads at once.  Destroying a plan while work that uses it is still
  *     queued is undefined.
+ *   - Workspaces: tq_score, tq_score_topk and tq_attend take their short-lived
+ *     workspace (at most 256 MiB; larger ones are allocated per call) from a
+ *     buffer kept per (device, stream), which the next such call on the same
+ *     stream reuses: the stream orders the two calls' kernels, so no call
+ *     allocates once the buffer is large enough.  The buffer grows by a
+ *     stream-ordered free and allocation (hipFreeAsync / hipMallocAsync) and
+ *     is held until the process ends.  A stream that is being captured into a
+ *     graph gets a per-call allocation instead.  A stream handle that is
+ *     destroyed while such a call's work is still queued must not be reused for
+ *     a new stream until that work has finished.
  *
  * Code layout (the "record" of one vector; little-endian 32-bit words):
  *   For a sub-plan with rotated length D (a power of two, 32..2048) and R
@@ -190,8 +200,8 @@ tq_status tq_encode_groups(const tq_plan* plan, const void* x, tq_dtype dt, int6
  * Raw inner-product estimates: no 1/sqrt(d), no softmax.  With a layer plan
  * (tq_plan_create_heads), n_groups must be a multiple of n_heads and group g
  * uses head g % n_heads.
- * Uses a stream-ordered temporary of n_groups*nq_per_group*(6*D) floats per
- * sub-plan (hipMallocAsync / hipFreeAsync on `stream`).
+ * Uses a workspace of n_groups*nq_per_group*(6*D) floats per sub-plan (the
+ * per-stream buffer above).
  * Errors: TQ_EINVAL (null, negative sizes, ldq < d, misalignment), TQ_ENOMEM,
  * TQ_EDEVICE; TQ_EUNSUPPORTED for an MSE plan.  Empty sizes are a no-op.
  */
@@ -239,9 +249,9 @@ tq_status tq_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* id
  * For a single sub-plan with D > 128, D a multiple of 128 and at least 8
  * queries per group, the score matrix is never stored: the scorer keeps each
  * query's running best k in on-chip memory and a second launch merges the
- * per-workgroup lists (a stream-ordered temporary of 8*k bytes per query and
- * workgroup slice, about 16384 workgroups).  Other shapes score into a
- * stream-ordered temporary of 4*n bytes per query row and select from it.
+ * per-workgroup lists (8*k bytes per query and workgroup slice, about 16384
+ * workgroups).  Other shapes score into 4*n bytes per query row and select from
+ * it.  Both live in the per-stream workspace above.
  * Errors: TQ_EINVAL (as tq_score; k < 1, k > 64, k > n, n >= 2^31),
  * TQ_ENOMEM, TQ_EDEVICE.  NaN estimates are not supported.
  */
@@ -278,8 +288,8 @@ tq_status tq_dequantize(const tq_plan* plan, const void* codes, int64_t n, void*
  *           finite
  *   vcodes  device, n_groups * n records of vplan (group g from record g*n)
  *   out     device, n_groups*nq_per_group rows of d elements (dt), stride ldo
- * Uses a stream-ordered temporary of (D + 2) floats per row and 1024-token
- * chunk.  Limits: n >= 1, n_groups <= 65535, nq_per_group <= 262140,
+ * Uses a workspace of (D + 2) floats per row and 1024-token chunk (the
+ * per-stream buffer above).  Limits: n >= 1, n_groups <= 65535, nq_per_group <= 262140,
  * nq_per_group * n_groups < 2^31, ceil(n / 1024) * nq_per_group * n_groups
  * <= 2^33, scale finite.  nq_per_group = 0 or n_groups = 0 is a no-op.
  * Errors: TQ_EINVAL (range, null, ldo < d, misalignment: logits 4-byte,

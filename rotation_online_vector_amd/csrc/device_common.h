@@ -111,6 +111,25 @@ __device__ __forceinline__ f16x8 f16x8_from_words(uint32_t w0, uint32_t w1, uint
   return __builtin_bit_cast(f16x8, u);
 }
 
+// Copies an operand table of N 16-byte pieces into LDS with a block of NT threads, every
+// global load issued before the first LDS store: the block waits for one round of memory
+// latency instead of one per loop trip, which is most of a short call's time.
+template <int N, int NT>
+__device__ __forceinline__ void table_to_lds(uint4* dst, const uint4* src) {
+  constexpr int J = (N + NT - 1) / NT;
+  uint4 t[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = threadIdx.x + j * NT;
+    if (N % NT == 0 || i < N) t[j] = src[i];
+  }
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = threadIdx.x + j * NT;
+    if (N % NT == 0 || i < N) dst[i] = t[j];
+  }
+}
+
 // Two bf16 values (one word), times a power of two when SCALE, as two fp16 values (one
 // word).  Exact when the (scaled) values lie in the fp16 normal range; smaller ones round
 // toward zero on the fp16 subnormal grid (absolute error below 2^-24).

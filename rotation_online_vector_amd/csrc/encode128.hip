@@ -106,15 +106,33 @@ __global__ void __launch_bounds__(kWaves * kWave) encode128_kernel(EncodeArgs a)
   __shared__ uint4 ls8[kNT * kQS * 64 * 2];
   __shared__ __attribute__((aligned(16))) int chl[VEC ? 4 : kD];
   const SubDev& s = a.s;
-  for (int i = threadIdx.x; i < kNT * kKS * 64; i += kWaves * kWave) {
-    lk[i] = reinterpret_cast<const uint4*>(s.k16_32)[i];
-    ls16[i] = reinterpret_cast<const uint4*>(s.s16_32)[i];
-  }
-  // fp8 operands: [tile][k step][16-byte half][lane] in LDS, so that each read instruction
-  // takes lane-consecutive 16-byte pieces (the table is [tile][k step][lane][32 bytes])
-  for (int i = threadIdx.x; i < kNT * kQS * 64 * 2; i += kWaves * kWave) {
-    const int blk = i >> 7, half = (i >> 6) & 1, l = i & 63;
-    ls8[i] = reinterpret_cast<const uint4*>(s.s8_32)[(blk * 64 + l) * 2 + half];
+  {
+    // every table load is issued before the first LDS store, so the block waits for one
+    // round of memory latency rather than one per loop trip (this dominates short calls)
+    constexpr int NT = kWaves * kWave;
+    constexpr int N16 = kNT * kKS * 64 / NT, N8 = kNT * kQS * 64 * 2 / NT;
+    static_assert(N16 * NT == kNT * kKS * 64 && N8 * NT == kNT * kQS * 64 * 2, "table split");
+    uint4 tk[N16], ts[N16], t8[N8];
+#pragma unroll
+    for (int j = 0; j < N16; ++j) {
+      tk[j] = reinterpret_cast<const uint4*>(s.k16_32)[threadIdx.x + j * NT];
+      ts[j] = reinterpret_cast<const uint4*>(s.s16_32)[threadIdx.x + j * NT];
+    }
+    // fp8 operands: [tile][k step][16-byte half][lane] in LDS, so that each read instruction
+    // takes lane-consecutive 16-byte pieces (the table is [tile][k step][lane][32 bytes])
+#pragma unroll
+    for (int j = 0; j < N8; ++j) {
+      const int i = threadIdx.x + j * NT;
+      const int blk = i >> 7, half = (i >> 6) & 1, l = i & 63;
+      t8[j] = reinterpret_cast<const uint4*>(s.s8_32)[(blk * 64 + l) * 2 + half];
+    }
+#pragma unroll
+    for (int j = 0; j < N16; ++j) {
+      lk[threadIdx.x + j * NT] = tk[j];
+      ls16[threadIdx.x + j * NT] = ts[j];
+    }
+#pragma unroll
+    for (int j = 0; j < N8; ++j) ls8[threadIdx.x + j * NT] = t8[j];
   }
   if constexpr (!VEC) {
     for (int i = threadIdx.x; i < kD; i += kWaves * kWave)
@@ -155,17 +173,25 @@ __global__ void __launch_bounds__(kWaves * kWave) encode128_kernel(EncodeArgs a)
   };
   const int64_t stride = (int64_t)gridDim.x * kWaves * 32;
   int64_t v0 = ((int64_t)blockIdx.x * kWaves + wave) * 32;
-  uint32_t xn[kKS][4];
-  if (v0 < a.n) load_x(v0, xn);
+  // appends (SCATTER) are short calls: no prefetch, which also frees its registers
+  uint32_t xn[SCATTER ? 1 : kKS][4];
+  if constexpr (!SCATTER) {
+    if (v0 < a.n) load_x(v0, xn);
+  }
   for (; v0 < a.n; v0 += stride) {
     uint32_t xw[kKS][4];
+    if constexpr (SCATTER) {
+      load_x(v0, xw);
+    } else {
 #pragma unroll
-    for (int ks = 0; ks < kKS; ++ks)
+      for (int ks = 0; ks < kKS; ++ks)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) xw[ks][w] = xn[ks][w];
-    // unconditional (the rows are clamped), so that the memory-counter wait for these
-    // loads in the next iteration can count this iteration's stores instead of draining them
-    load_x(v0 + stride, xn);
+        for (int w = 0; w < 4; ++w) xw[ks][w] = xn[ks][w];
+      // unconditional (the rows are clamped), so that the memory-counter wait for these
+      // loads in the next iteration can count this iteration's stores instead of draining
+      // them
+      load_x(v0 + stride, xn);
+    }
     __builtin_amdgcn_sched_barrier(0);
     // ---- norm: sum of squares of this half's 64 elements, then both halves ----
     float ss = 0.f;
@@ -341,7 +367,9 @@ int launch_encode128(const EncodeArgs& ea, hipStream_t st, int64_t n_groups) {
   const bool vec = ea.vec_load && ea.s.d == kD;
 #define TQ_E128(RR)                                                                          \
   case RR:                                                                                   \
-    if (ea.out_index)                                                                        \
+    if (ea.out_index && vec)                                                                 \
+      hipLaunchKernelGGL((encode128_kernel<RR, true, true>), grid, block, 0, st, ea);        \
+    else if (ea.out_index)                                                                   \
       hipLaunchKernelGGL((encode128_kernel<RR, false, true>), grid, block, 0, st, ea);       \
     else if (vec)                                                                            \
       hipLaunchKernelGGL((encode128_kernel<RR, true, false>), grid, block, 0, st, ea);       \

@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdint>
 #include <mutex>
+#include <vector>
 
 #include "device_common.h"
 
@@ -537,12 +538,10 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
   __shared__ uint4 kop[KLIMBS * NJT * NKS * 64];
   __shared__ uint4 sop[MSE ? 1 : NJT * NKS * 64];
   const SubDev& s = a.s;
-  for (int i = threadIdx.x; i < KLIMBS * NJT * NKS * 64; i += kEncWaves * kWave)
-    kop[i] = reinterpret_cast<const uint4*>(F16 ? s.rotk16 : s.rotk)[i];
-  if constexpr (!MSE) {
-    for (int i = threadIdx.x; i < NJT * NKS * 64; i += kEncWaves * kWave)
-      sop[i] = reinterpret_cast<const uint4*>(s.sperm)[i];
-  }
+  table_to_lds<KLIMBS * NJT * NKS * 64, kEncWaves * kWave>(
+      kop, reinterpret_cast<const uint4*>(F16 ? s.rotk16 : s.rotk));
+  if constexpr (!MSE)
+    table_to_lds<NJT * NKS * 64, kEncWaves * kWave>(sop, reinterpret_cast<const uint4*>(s.sperm));
   __shared__ __attribute__((aligned(16))) int chl[VEC ? 8 : D];   // input channel per coordinate
   if constexpr (!VEC) {
     for (int i = threadIdx.x; i < D; i += kEncWaves * kWave)
@@ -932,8 +931,7 @@ __global__ void __launch_bounds__(kDqWaves * kWave) dequant_mfma_kernel(DequantA
   __shared__ uint4 kt[NJT * NKS * 64];
   __shared__ uint2 pair_tab[NPAIR];
   const SubDev& s = a.s;
-  for (int i = threadIdx.x; i < NJT * NKS * 64; i += kDqWaves * kWave)
-    kt[i] = reinterpret_cast<const uint4*>(s.rotkt16)[i];
+  table_to_lds<NJT * NKS * 64, kDqWaves * kWave>(kt, reinterpret_cast<const uint4*>(s.rotkt16));
   // entry i: coordinate A has index bits i_0, i_2, i_4, ..., coordinate B i_1, i_3, ...
   for (int i = threadIdx.x; i < NPAIR; i += kDqWaves * kWave) {
     int ia = 0, ib = 0;
@@ -2524,6 +2522,86 @@ static int launch_attend_d(const AttnArgs& aa, int64_t n_groups, hipStream_t st)
   return (int)hipGetLastError();
 }
 
+// ------------------------------------------------------------ per-stream workspaces
+// The score and attention calls need a short-lived workspace (query images, partial
+// results).  A stream-ordered allocation per call costs several microseconds of device time
+// between launches, so one buffer per (device, stream) is kept and reused by the next call on
+// that stream: the stream runs the two calls' kernels one after the other, so the reuse is
+// safe.  The buffer grows when a call needs more (a stream-ordered free of the old one, then
+// a new allocation) up to kCachedWorkspaceMax; larger requests, and calls on a stream that is
+// being captured into a graph, allocate per call as before.  The lock is held from the
+// lookup until the lease ends (after the caller has enqueued its kernels), so a growth on
+// another host thread cannot free a buffer before its last use is ordered on its stream.
+constexpr size_t kCachedWorkspaceMax = (size_t)256 << 20;
+
+struct CachedWorkspace {
+  int dev;
+  hipStream_t st;
+  void* ptr;
+  size_t cap;
+};
+std::mutex g_ws_mu;
+std::vector<CachedWorkspace> g_ws;
+
+class WorkspaceLease {
+ public:
+  WorkspaceLease() = default;
+  WorkspaceLease(const WorkspaceLease&) = delete;
+  WorkspaceLease& operator=(const WorkspaceLease&) = delete;
+  ~WorkspaceLease() {
+    if (own_ != nullptr) (void)hipFreeAsync(own_, st_);
+  }
+  void* ptr() const { return ptr_; }
+  // returns 0 or a hipError_t
+  int acquire(size_t bytes, hipStream_t st) {
+    st_ = st;
+    if (bytes == 0) bytes = 256;
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e != hipSuccess) return (int)e;
+    if (bytes > kCachedWorkspaceMax || cs != hipStreamCaptureStatusNone) {
+      e = hipMallocAsync(&own_, bytes, st);
+      if (e != hipSuccess) {
+        own_ = nullptr;
+        return (int)e;
+      }
+      ptr_ = own_;
+      return 0;
+    }
+    int dev = 0;
+    e = hipGetDevice(&dev);
+    if (e != hipSuccess) return (int)e;
+    lock_ = std::unique_lock<std::mutex>(g_ws_mu);
+    CachedWorkspace* w = nullptr;
+    for (auto& c : g_ws)
+      if (c.dev == dev && c.st == st) w = &c;
+    if (w == nullptr) {
+      g_ws.push_back({dev, st, nullptr, 0});
+      w = &g_ws.back();
+    }
+    if (w->cap < bytes) {
+      if (w->ptr != nullptr) (void)hipFreeAsync(w->ptr, st);
+      w->ptr = nullptr;
+      w->cap = 0;
+      size_t cap = bytes < ((size_t)1 << 20) ? ((size_t)1 << 20) : bytes;
+      e = hipMallocAsync(&w->ptr, cap, st);
+      if (e != hipSuccess) {
+        w->ptr = nullptr;
+        return (int)e;
+      }
+      w->cap = cap;
+    }
+    ptr_ = w->ptr;
+    return 0;
+  }
+
+ private:
+  std::unique_lock<std::mutex> lock_;
+  hipStream_t st_ = nullptr;
+  void* own_ = nullptr;
+  void* ptr_ = nullptr;
+};
+
 int launch_attend(const PlanDev& p, const float* logits, int64_t nq_per_group, int64_t n_groups,
                   int64_t n, float scale, const uint8_t* codes, void* out, int dt, int64_t ldo,
                   void* stream) {
@@ -2544,10 +2622,10 @@ int launch_attend(const PlanDev& p, const float* logits, int64_t nq_per_group, i
   aa.ldo = ldo;
   aa.out_bf16 = dt == TQ_BF16;
   const size_t bytes = (size_t)aa.n_chunks * nq_per_group * n_groups * (aa.s.D + 2) * 4;
-  void* ws = nullptr;
-  hipError_t e = hipMallocAsync(&ws, bytes, st);
-  if (e != hipSuccess) return (int)e;
-  aa.part = static_cast<float*>(ws);
+  WorkspaceLease lease;
+  const int wrc = lease.acquire(bytes, st);
+  if (wrc) return wrc;
+  aa.part = static_cast<float*>(lease.ptr());
   int rc;
   switch (aa.s.D) {
     case 32: rc = launch_attend_d<32>(aa, n_groups, st); break;
@@ -2559,8 +2637,6 @@ int launch_attend(const PlanDev& p, const float* logits, int64_t nq_per_group, i
     case 2048: rc = launch_attend_d<2048>(aa, n_groups, st); break;
     default: rc = (int)hipErrorInvalidValue;
   }
-  e = hipFreeAsync(ws, st);
-  if (!rc && e != hipSuccess) rc = (int)e;
   return rc;
 }
 
@@ -2937,13 +3013,14 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
     }
   }
   void* ws = nullptr;
-  hipError_t e = hipSuccess;
+  WorkspaceLease lease;
   if (ws_ext != nullptr) {
     if (bytes > ws_cap) return (int)hipErrorOutOfMemory;
     ws = ws_ext;
   } else {
-    e = hipMallocAsync(&ws, bytes, st);
-    if (e != hipSuccess) return (int)e;
+    const int wrc = lease.acquire(bytes, st);
+    if (wrc) return wrc;
+    ws = lease.ptr();
   }
   uint8_t* wb = static_cast<uint8_t*>(ws);
   if (tko != nullptr && !fused) scores = reinterpret_cast<float*>(wb + off_sc);
@@ -2979,10 +3056,7 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
       fa.img = reinterpret_cast<uint32_t*>(wb + off_img[sb]);
       fa.ec = reinterpret_cast<float*>(wb + off_ec[sb]);
       const int prc = launch_qprep_bitslice(fa, p.sub[sb].D, nq, st);
-      if (prc) {
-        if (ws_ext == nullptr) (void)hipFreeAsync(ws, st);
-        return prc;
-      }
+      if (prc) return prc;
       sa.img[sb] = fa.img;
       sa.ec[sb] = fa.ec;
     } else {
@@ -3049,10 +3123,6 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
   if (!rc) rc = hip_rc(hipGetLastError());
   if (!rc && tko != nullptr && !fused)
     rc = launch_topk(scores, nq, n, tko->k, tko->ids, tko->vals, st);
-  if (ws_ext == nullptr) {
-    e = hipFreeAsync(ws, st);
-    if (!rc && e != hipSuccess) rc = (int)e;
-  }
   return rc;
 }
 
