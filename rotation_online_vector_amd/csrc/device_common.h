@@ -82,6 +82,8 @@ __device__ __forceinline__ uint8_t* encode_record(const EncodeArgs& a, int64_t r
 
 // D = 128 inner-product plans with bf16 input and the 32x32 operand tables (encode128.hip).
 int launch_encode128(const EncodeArgs& ea, hipStream_t st, int64_t n_groups);
+// Compute units of the current device (cached per device; 256 if the query fails).
+int compute_units();
 
 constexpr int kEncWaves = 8;
 

@@ -95,17 +95,33 @@ __device__ __forceinline__ float bucket_sym_scaled(float z, float s, const float
 //   s8  [4 tiles][2 k steps][64 lanes][32] e4m3 S, rows permuted, byte e of lane half h =
 //                                          coordinate 64 h + 32 q + e (the same k slot map on
 //                                          both operands of the fp8 product)
+// LOAD: how a vector's coordinates are read.  kGather: one element per coordinate through the
+// channel list; kRows: 16-byte pieces of a row that is the sub-plan's input as it stands;
+// kFolded: 16-byte pieces of a whole input row, with the channel selection folded into the
+// rotation table of the vector's head (kfold) and the unselected columns masked to zero
+// before the norm (xmask).
 // SCATTER: records go to the cache rows a.out_index[] (appending to a cache) instead of
 // consecutive records.
-template <int R, bool VEC, bool SCATTER>
+constexpr int kGather = 0, kRows = 1, kFolded = 2;
+
+template <int R, int LOAD, bool SCATTER>
 __global__ void __launch_bounds__(kWaves * kWave) encode128_kernel(EncodeArgs a) {
   constexpr int H = 1 << (R - 1);
+  constexpr bool VEC = LOAD != kGather;
   encode_group_view(a);
   __shared__ uint4 lk[kNT * kKS * 64];
   __shared__ uint4 ls16[kNT * kKS * 64];
   __shared__ uint4 ls8[kNT * kQS * 64 * 2];
   __shared__ __attribute__((aligned(16))) int chl[VEC ? 4 : kD];
+  __shared__ uint4 xm[LOAD == kFolded ? kKS * 2 : 1];
   const SubDev& s = a.s;
+  const uint4* ktab = reinterpret_cast<const uint4*>(s.k16_32);
+  if constexpr (LOAD == kFolded) {
+    const int head = (int)(blockIdx.z % a.n_heads);
+    ktab = reinterpret_cast<const uint4*>(s.kfold) + (size_t)head * kNT * kKS * 64;
+    if (threadIdx.x < kKS * 2)
+      xm[threadIdx.x] = reinterpret_cast<const uint4*>(s.xmask)[head * kKS * 2 + threadIdx.x];
+  }
   {
     // every table load is issued before the first LDS store, so the block waits for one
     // round of memory latency rather than one per loop trip (this dominates short calls)
@@ -115,7 +131,7 @@ __global__ void __launch_bounds__(kWaves * kWave) encode128_kernel(EncodeArgs a)
     uint4 tk[N16], ts[N16], t8[N8];
 #pragma unroll
     for (int j = 0; j < N16; ++j) {
-      tk[j] = reinterpret_cast<const uint4*>(s.k16_32)[threadIdx.x + j * NT];
+      tk[j] = ktab[threadIdx.x + j * NT];
       ts[j] = reinterpret_cast<const uint4*>(s.s16_32)[threadIdx.x + j * NT];
     }
     // fp8 operands: [tile][k step][16-byte half][lane] in LDS, so that each read instruction
@@ -156,9 +172,15 @@ __global__ void __launch_bounds__(kWaves * kWave) encode128_kernel(EncodeArgs a)
 #pragma unroll
     for (int ks = 0; ks < kKS; ++ks) {
       const int c0 = 16 * ks + 8 * h;
-      if constexpr (VEC) {
+      if constexpr (LOAD == kRows) {
         const uint4 u = *reinterpret_cast<const uint4*>(
             reinterpret_cast<const uint16_t*>(a.x) + row * a.ldx + c0);
+        xw[ks][0] = u.x; xw[ks][1] = u.y; xw[ks][2] = u.z; xw[ks][3] = u.w;
+      } else if constexpr (LOAD == kFolded) {
+        // columns past the row (x_cols) carry zero weight in the folded table
+        uint4 u = {0u, 0u, 0u, 0u};
+        if (c0 < s.x_cols)
+          u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(a.x) + row * a.ldx + c0);
         xw[ks][0] = u.x; xw[ks][1] = u.y; xw[ks][2] = u.z; xw[ks][3] = u.w;
       } else {
         const uint16_t* xr = reinterpret_cast<const uint16_t*>(a.x) + row * a.ldx;
@@ -193,6 +215,14 @@ __global__ void __launch_bounds__(kWaves * kWave) encode128_kernel(EncodeArgs a)
       load_x(v0 + stride, xn);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (LOAD == kFolded) {
+      // the head's unselected columns count neither in the norm nor (zero weight) in z
+#pragma unroll
+      for (int ks = 0; ks < kKS; ++ks) {
+        const uint4 m = xm[ks * 2 + h];
+        xw[ks][0] &= m.x; xw[ks][1] &= m.y; xw[ks][2] &= m.z; xw[ks][3] &= m.w;
+      }
+    }
     // ---- norm: sum of squares of this half's 64 elements, then both halves ----
     float ss = 0.f;
 #pragma unroll
@@ -358,23 +388,47 @@ __global__ void __launch_bounds__(kWaves * kWave) encode128_kernel(EncodeArgs a)
   }
 }
 
+int compute_units() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cu = 0;
+    if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cu <= 0)
+      cu = 256;
+    cached[dev] = cu;
+  }
+  return cached[dev];
+}
+
+// The kernel's registers allow one 8-wave workgroup per compute unit, so a grid of one
+// workgroup per compute unit runs in a single round and loads the operand tables once per
+// unit; more workgroups only repeat that prologue.
 int launch_encode128(const EncodeArgs& ea, hipStream_t st, int64_t n_groups) {
   const int64_t iters = (ea.n + 31) / 32;
   int64_t blocks = (iters + kWaves - 1) / kWaves;
-  const int64_t cap = n_groups > 1 ? (1024 + n_groups - 1) / n_groups : 1024;
+  const int64_t cus = compute_units();
+  const int64_t cap = n_groups > 1 ? (cus + n_groups - 1) / n_groups : cus;
   if (blocks > cap) blocks = cap;
   const dim3 grid((unsigned)blocks, 1, (unsigned)n_groups), block(kWaves * kWave);
-  const bool vec = ea.vec_load && ea.s.d == kD;
+  const bool aligned = ((uintptr_t)ea.x % 16 == 0) && ((ea.ldx * 2) % 16 == 0);
+  const int load = (ea.s.chan == nullptr && aligned && ea.s.d == kD) ? kRows
+                 : (ea.s.chan != nullptr && ea.s.kfold != nullptr && aligned) ? kFolded
+                 : kGather;
+#define TQ_E128_L(RR, LL)                                                                    \
+  if (ea.out_index)                                                                          \
+    hipLaunchKernelGGL((encode128_kernel<RR, LL, true>), grid, block, 0, st, ea);            \
+  else                                                                                       \
+    hipLaunchKernelGGL((encode128_kernel<RR, LL, false>), grid, block, 0, st, ea);
 #define TQ_E128(RR)                                                                          \
   case RR:                                                                                   \
-    if (ea.out_index && vec)                                                                 \
-      hipLaunchKernelGGL((encode128_kernel<RR, true, true>), grid, block, 0, st, ea);        \
-    else if (ea.out_index)                                                                   \
-      hipLaunchKernelGGL((encode128_kernel<RR, false, true>), grid, block, 0, st, ea);       \
-    else if (vec)                                                                            \
-      hipLaunchKernelGGL((encode128_kernel<RR, true, false>), grid, block, 0, st, ea);       \
-    else                                                                                     \
-      hipLaunchKernelGGL((encode128_kernel<RR, false, false>), grid, block, 0, st, ea);      \
+    if (load == kRows) {                                                                     \
+      TQ_E128_L(RR, kRows)                                                                   \
+    } else if (load == kFolded) {                                                            \
+      TQ_E128_L(RR, kFolded)                                                                 \
+    } else {                                                                                 \
+      TQ_E128_L(RR, kGather)                                                                 \
+    }                                                                                        \
     break;
   switch (ea.s.R) {
     TQ_E128(1)
@@ -384,6 +438,7 @@ int launch_encode128(const EncodeArgs& ea, hipStream_t st, int64_t n_groups) {
     default: return (int)hipErrorInvalidValue;
   }
 #undef TQ_E128
+#undef TQ_E128_L
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? 0 : (int)e;
 }

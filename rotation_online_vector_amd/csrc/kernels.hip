@@ -524,22 +524,36 @@ __device__ __forceinline__ uint32_t combine_word(uint32_t part, int G) {
 // element is below 2^14 and the bf16 values convert exactly unless they sit 2^28 below the
 // norm), in place of two bf16 products with K split in two limbs.
 // MSE: TurboQuant-MSE records (R = b index bits, then the norm): no residual, no QJL stage.
-template <int D, int R, int XL, bool VEC, bool F16, bool MSE>
+// FOLD (D <= 64, bf16 rows of at most 128 columns, fp16 K): the whole input row is read in
+// 16-byte pieces and the channel selection is folded into the rotation table of the vector's
+// head (kfold, 4 k steps of 32 columns), the unselected columns masked to zero before the norm
+// (xmask); without it a split plan's channels are gathered one element at a time.
+template <int D, int R, int XL, bool VEC, bool F16, bool MSE, bool FOLD = false>
 __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeArgs a) {
   encode_group_view(a);
+  static_assert(!FOLD || (D <= 64 && XL == 1 && VEC && F16 && !MSE), "folded rows");
   constexpr int NJT = D / 16;        // 16-row tiles of coordinates
   constexpr int NKS = D / 32;        // 32-wide k steps
+  constexpr int NKX = FOLD ? 4 : NKS;  // k steps of the rotation over the input row
   constexpr int H = 1 << (R - 1);    // cells of |z|
   constexpr int NT = 2;              // 16-vector tiles per wave iteration
   constexpr uint32_t kPartMask = D >= 128 ? 0xFFFFFFFFu : (1u << (D / 4)) - 1u;
   static_assert(!F16 || XL == 1, "fp16 rotation takes bf16 input");
   constexpr int KLIMBS = F16 ? 1 : 2;
   constexpr int W = MSE ? R : R + 1;  // words per 32-coordinate chunk of a record
-  __shared__ uint4 kop[KLIMBS * NJT * NKS * 64];
+  __shared__ uint4 kop[KLIMBS * NJT * NKX * 64];
   __shared__ uint4 sop[MSE ? 1 : NJT * NKS * 64];
+  __shared__ uint4 xm[FOLD ? 16 : 1];
   const SubDev& s = a.s;
-  table_to_lds<KLIMBS * NJT * NKS * 64, kEncWaves * kWave>(
-      kop, reinterpret_cast<const uint4*>(F16 ? s.rotk16 : s.rotk));
+  if constexpr (FOLD) {
+    const int head = (int)(blockIdx.z % a.n_heads);
+    table_to_lds<NJT * NKX * 64, kEncWaves * kWave>(
+        kop, reinterpret_cast<const uint4*>(s.kfold) + (size_t)head * NJT * NKX * 64);
+    if (threadIdx.x < 16) xm[threadIdx.x] = reinterpret_cast<const uint4*>(s.xmask)[head * 16 + threadIdx.x];
+  } else {
+    table_to_lds<KLIMBS * NJT * NKX * 64, kEncWaves * kWave>(
+        kop, reinterpret_cast<const uint4*>(F16 ? s.rotk16 : s.rotk));
+  }
   if constexpr (!MSE)
     table_to_lds<NJT * NKS * 64, kEncWaves * kWave>(sop, reinterpret_cast<const uint4*>(s.sperm));
   __shared__ __attribute__((aligned(16))) int chl[VEC ? 8 : D];   // input channel per coordinate
@@ -563,16 +577,25 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
   for (int64_t v0 = ((int64_t)blockIdx.x * kEncWaves + wave) * 16 * NT; v0 < a.n;
        v0 += (int64_t)gridDim.x * kEncWaves * 16 * NT) {
     // ---- x^T operands (columns past the last vector repeat the last one) ----
-    uint32_t xw[NT][NKS][XL][4];
+    uint32_t xw[NT][NKX][XL][4];
     float ss[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       ss[t] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
+      for (int ks = 0; ks < NKX; ++ks) {
         uint32_t lb[XL][4];
         const int64_t row = v0 + 16 * t + col;
-        load_x8<XL, VEC>(a, row < a.n ? row : a.n - 1, 32 * ks + 8 * G, lb, ss[t], chl);
+        if constexpr (FOLD) {
+          // columns past the row carry zero weight; the head's unselected ones are masked
+          lb[0][0] = lb[0][1] = lb[0][2] = lb[0][3] = 0u;
+          if (32 * ks + 8 * G < s.x_cols)
+            load_x8<1, true>(a, row < a.n ? row : a.n - 1, 32 * ks + 8 * G, lb, ss[t], chl);
+          const uint4 m = xm[ks * 4 + G];
+          lb[0][0] &= m.x; lb[0][1] &= m.y; lb[0][2] &= m.z; lb[0][3] &= m.w;
+        } else {
+          load_x8<XL, VEC>(a, row < a.n ? row : a.n - 1, 32 * ks + 8 * G, lb, ss[t], chl);
+        }
 #pragma unroll
         for (int l = 0; l < XL; ++l)
 #pragma unroll
@@ -588,7 +611,7 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
       if constexpr (XL == 1) {
         f32x4 gram = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
+        for (int ks = 0; ks < NKX; ++ks) {
           const bf16x8 xb = bf16x8_from_words(xw[t][ks][0][0], xw[t][ks][0][1], xw[t][ks][0][2],
                                               xw[t][ks][0][3]);
           gram = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xb, xb, gram, 0, 0, 0);
@@ -607,7 +630,7 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
       }
       sc[t] = zn > 0.f ? zn : 1.f;
     }
-    uint32_t xh[F16 ? NT : 1][NKS][4];   // fp16 copy of x (F16 only)
+    uint32_t xh[F16 ? NT : 1][NKX][4];   // fp16 copy of x (F16 only)
     if constexpr (F16) {
       // Unscaled when every norm of the wave lies in [2^-4, 2^14): elements then stay below
       // the fp16 maximum, and the subnormal rounding (< 2^-24) is below 2^-20 ||x||.
@@ -618,14 +641,14 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
 #pragma unroll
         for (int t = 0; t < NT; ++t)
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
+          for (int ks = 0; ks < NKX; ++ks)
 #pragma unroll
             for (int w = 0; w < 4; ++w) xh[t][ks][w] = bf16x2_to_f16x2<false>(xw[t][ks][0][w], 1.f);
       } else {
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
 #pragma unroll
-          for (int ks = 0; ks < NKS; ++ks)
+          for (int ks = 0; ks < NKX; ++ks)
 #pragma unroll
             for (int w = 0; w < 4; ++w) xh[t][ks][w] = bf16x2_to_f16x2<true>(xw[t][ks][0][w], xs[t]);
           sc[t] *= xs[t];              // z_raw carries the factor (zero vectors: harmless)
@@ -664,9 +687,9 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[t][jr] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
+        for (int ks = 0; ks < NKX; ++ks) {
           if constexpr (F16) {
-            const uint4 uk = kop[(jr * NKS + ks) * 64 + lane];
+            const uint4 uk = kop[(jr * NKX + ks) * 64 + lane];
             const f16x8 kh = f16x8_from_words(uk.x, uk.y, uk.z, uk.w);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -675,8 +698,8 @@ __global__ void __launch_bounds__(kEncWaves * kWave) encode_mfma_kernel(EncodeAr
             }
             continue;
           }
-          const uint4 uh = kop[(jr * NKS + ks) * 64 + lane];
-          const uint4 ul = kop[((NJT + jr) * NKS + ks) * 64 + lane];
+          const uint4 uh = kop[(jr * NKX + ks) * 64 + lane];
+          const uint4 ul = kop[((NJT + jr) * NKX + ks) * 64 + lane];
           const bf16x8 khi = bf16x8_from_words(uh.x, uh.y, uh.z, uh.w);
           const bf16x8 klo = bf16x8_from_words(ul.x, ul.y, ul.z, ul.w);
 #pragma unroll
@@ -2843,6 +2866,20 @@ static void launch_encode_mfma_dxv(const EncodeArgs& ea, hipStream_t st, dim3 gr
 
 template <int D, int XL>
 static void launch_encode_mfma_dx(const EncodeArgs& ea, hipStream_t st, dim3 grid) {
+  if constexpr (D <= 64 && XL == 1) {
+    const bool aligned = ((uintptr_t)ea.x % 16 == 0) && ((ea.ldx * 2) % 16 == 0);
+    if (ea.s.chan != nullptr && ea.s.kfold != nullptr && ea.s.rotk16 != nullptr && !ea.s.mse &&
+        aligned) {
+      const dim3 block(kEncWaves * kWave);
+      switch (ea.s.R) {
+        case 1: hipLaunchKernelGGL((encode_mfma_kernel<D, 1, 1, true, true, false, true>), grid, block, 0, st, ea); break;
+        case 2: hipLaunchKernelGGL((encode_mfma_kernel<D, 2, 1, true, true, false, true>), grid, block, 0, st, ea); break;
+        case 3: hipLaunchKernelGGL((encode_mfma_kernel<D, 3, 1, true, true, false, true>), grid, block, 0, st, ea); break;
+        case 4: hipLaunchKernelGGL((encode_mfma_kernel<D, 4, 1, true, true, false, true>), grid, block, 0, st, ea); break;
+      }
+      return;
+    }
+  }
   if (ea.vec_load && ea.s.d == D)
     launch_encode_mfma_dxv<D, XL, true>(ea, st, grid);
   else
@@ -2850,11 +2887,13 @@ static void launch_encode_mfma_dx(const EncodeArgs& ea, hipStream_t st, dim3 gri
 }
 
 static int launch_encode_mfma(const EncodeArgs& ea, hipStream_t st, int64_t n_groups) {
-  // one wave iteration encodes 32 vectors; enough blocks to fill the chip a few times over,
-  // each looping over its share (of its group's rows)
+  // one wave iteration encodes 32 vectors; two 8-wave blocks per compute unit (what the
+  // registers of the common variants allow), each looping over its share of its group's rows,
+  // so the operand tables are loaded once per block rather than once per few iterations
   const int64_t iters = (ea.n + 31) / 32;
   int64_t blocks = (iters + kEncWaves - 1) / kEncWaves;
-  const int64_t cap = n_groups > 1 ? (2048 + n_groups - 1) / n_groups : 2048;
+  const int64_t full = 2 * (int64_t)compute_units();
+  const int64_t cap = n_groups > 1 ? (full + n_groups - 1) / n_groups : full;
   if (blocks > cap) blocks = cap;
   const dim3 grid((unsigned)blocks, 1, (unsigned)n_groups);
   switch (ea.s.D * 2 + ea.is_bf16) {

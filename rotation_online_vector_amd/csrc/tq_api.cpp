@@ -55,6 +55,8 @@ struct SubHost {
   std::vector<uint16_t> k16_32;  // operands of the D = 128 32x32 encoder (may stay empty)
   std::vector<uint16_t> s16_32;
   std::vector<uint8_t> s8_32;
+  std::vector<uint16_t> kf16;    // 32x32 encoder, channel selection folded in (per head)
+  std::vector<uint32_t> xmask;   // the selected columns of each head, for the norm
 };
 
 constexpr int kMfmaMaxD = 128;
@@ -160,6 +162,64 @@ void mfma_operand_tables(SubHost& h) {
 // 64 h' + 16 t + 4 i + j: each lane half then holds 64 consecutive coordinates.
 int permuted_row32(int tile, int rho) {
   return 64 * ((rho >> 2) & 1) + 16 * tile + 4 * (rho >> 3) + (rho & 3);
+}
+
+// Sub-plans of split and layer plans whose channels come from rows of at most 128 columns
+// (a multiple of 8): the rotation with the channel selection folded in, K_h = K P_h, where
+// P_h sends column c of the input row to coordinate i when chan_h[i] = c (the other columns
+// get zero weight), in fp16 with k = the input column, one table per head; and per head the
+// 16-bit lane masks of the selected columns, with which the encoder zeroes the unselected
+// columns before the norm.  The encoder then reads whole rows with 16-byte loads instead of
+// gathering channels.  D = 128 (with the 32x32 tables): the 32x32 encoder's layout, masks
+// [k step of 16][lane half][word]; D <= 64 (with rotk16): rotk16's layout over 4 k steps of
+// 32 columns, masks [k step][lane group][word] (word w: columns 2w and 2w + 1 of the 8 a lane
+// reads).
+void folded_operand_tables(SubHost& h, const std::vector<int64_t>& K, int n_heads, int cols) {
+  if (h.chan.empty() || cols > 128 || cols % 8 != 0) return;
+  const int D = h.D;
+  const bool wide = D == 128 && !h.k16_32.empty();
+  const bool narrow = D <= 64 && !h.rotk16.empty() && !h.S.empty();
+  if (!wide && !narrow) return;
+  const size_t per = wide ? (size_t)4 * 8 * 64 * 8 : (size_t)(D / 16) * 4 * 64 * 8;
+  h.kf16.assign(per * n_heads, 0);
+  h.xmask.assign((size_t)64 * n_heads, 0);
+  std::vector<int> inv(cols);
+  auto kval = [&](int row, int col) -> uint16_t {
+    const int i = col < cols ? inv[col] : -1;
+    return i >= 0 ? fp16_bits_of_small_int(K[(size_t)row * D + i]) : 0;
+  };
+  auto mask_word = [&](int c0) -> uint32_t {
+    const uint32_t lo = (c0 < cols && inv[c0] >= 0) ? 0xFFFFu : 0u;
+    const uint32_t hi = (c0 + 1 < cols && inv[c0 + 1] >= 0) ? 0xFFFF0000u : 0u;
+    return lo | hi;
+  };
+  for (int hd = 0; hd < n_heads; ++hd) {
+    std::fill(inv.begin(), inv.end(), -1);
+    for (int i = 0; i < h.d; ++i) inv[h.chan[(size_t)hd * h.d + i]] = i;
+    uint16_t* kf = h.kf16.data() + per * hd;
+    uint32_t* mw = h.xmask.data() + (size_t)64 * hd;
+    if (wide) {
+      for (int t = 0; t < 4; ++t)
+        for (int l = 0; l < 64; ++l)
+          for (int ks = 0; ks < 8; ++ks)
+            for (int e = 0; e < 8; ++e)
+              kf[(((size_t)t * 8 + ks) * 64 + l) * 8 + e] =
+                  kval(permuted_row32(t, l % 32), 16 * ks + 8 * (l / 32) + e);
+      for (int ks = 0; ks < 8; ++ks)
+        for (int hh = 0; hh < 2; ++hh)
+          for (int w = 0; w < 4; ++w) mw[(ks * 2 + hh) * 4 + w] = mask_word(16 * ks + 8 * hh + 2 * w);
+    } else {
+      for (int jt = 0; jt < D / 16; ++jt)
+        for (int ks = 0; ks < 4; ++ks)
+          for (int l = 0; l < 64; ++l)
+            for (int e = 0; e < 8; ++e)
+              kf[(((size_t)jt * 4 + ks) * 64 + l) * 8 + e] =
+                  kval(permuted_row(D, jt, l % 16), 32 * ks + 8 * (l / 16) + e);
+      for (int ks = 0; ks < 4; ++ks)
+        for (int G = 0; G < 4; ++G)
+          for (int w = 0; w < 4; ++w) mw[(ks * 4 + G) * 4 + w] = mask_word(32 * ks + 8 * G + 2 * w);
+    }
+  }
 }
 
 // fp16 bit pattern of v when v is exactly representable (normal or subnormal), else false.
@@ -372,6 +432,7 @@ tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mas
   size_t off_sign[2] = {0, 0}, off_S[2] = {0, 0}, off_chan[2] = {0, 0};
   size_t off_rotk[2] = {0, 0}, off_rotk16[2] = {0, 0}, off_rotkt16[2] = {0, 0}, off_sperm[2] = {0, 0};
   size_t off_k16_32[2] = {0, 0}, off_s16_32[2] = {0, 0}, off_s8_32[2] = {0, 0};
+  size_t off_kf16[2] = {0, 0}, off_xmask[2] = {0, 0};
   auto take = [&](size_t b) { size_t o = bytes; bytes += (b + 255) / 256 * 256; return o; };
   for (int i = 0; i < pd.nsub; ++i) {
     SubHost& h = subs[i];
@@ -409,6 +470,8 @@ tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mas
     if (!h.chan.empty()) off_chan[i] = take(h.chan.size() * 4);
     if (h.D <= kMfmaMaxD) {
       mfma_operand_tables(h);
+      if (!h.chan.empty())
+        folded_operand_tables(h, rotation_integer_matrix(h.signs, h.D), n_heads, d);
       off_rotk[i] = take(h.rotk.size() * 2);
       off_rotk16[i] = take(h.rotk16.size() * 2);
       off_rotkt16[i] = take(h.rotkt16.size() * 2);
@@ -416,6 +479,8 @@ tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mas
       off_k16_32[i] = take(h.k16_32.size() * 2);
       off_s16_32[i] = take(h.s16_32.size() * 2);
       off_s8_32[i] = take(h.s8_32.size());
+      off_kf16[i] = take(h.kf16.size() * 2);
+      off_xmask[i] = take(h.xmask.size() * 4);
     }
   }
   void* mem = nullptr;
@@ -450,6 +515,10 @@ tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mas
       e = hipMemcpy(base + off_s16_32[i], h.s16_32.data(), h.s16_32.size() * 2, hipMemcpyHostToDevice);
     if (e == hipSuccess && !h.s8_32.empty())
       e = hipMemcpy(base + off_s8_32[i], h.s8_32.data(), h.s8_32.size(), hipMemcpyHostToDevice);
+    if (e == hipSuccess && !h.kf16.empty())
+      e = hipMemcpy(base + off_kf16[i], h.kf16.data(), h.kf16.size() * 2, hipMemcpyHostToDevice);
+    if (e == hipSuccess && !h.xmask.empty())
+      e = hipMemcpy(base + off_xmask[i], h.xmask.data(), h.xmask.size() * 4, hipMemcpyHostToDevice);
     if (e != hipSuccess) {
       (void)hipFree(mem);
       delete plan;
@@ -466,6 +535,10 @@ tq_status create_plan(int d, int bits, uint64_t seed, const uint8_t* outlier_mas
     s.k16_32 = e32 ? reinterpret_cast<const uint16_t*>(base + off_k16_32[i]) : nullptr;
     s.s16_32 = e32 ? reinterpret_cast<const uint16_t*>(base + off_s16_32[i]) : nullptr;
     s.s8_32 = e32 ? reinterpret_cast<const uint8_t*>(base + off_s8_32[i]) : nullptr;
+    const bool fold = !h.kf16.empty() && !h.xmask.empty();
+    s.kfold = fold ? reinterpret_cast<const uint16_t*>(base + off_kf16[i]) : nullptr;
+    s.xmask = fold ? reinterpret_cast<const uint32_t*>(base + off_xmask[i]) : nullptr;
+    s.x_cols = fold ? d : 0;
   }
   *out = plan;
   return TQ_OK;

@@ -52,6 +52,15 @@ struct SubDev {
   const uint16_t* k16_32;  // [4][8][64][8] fp16 K
   const uint16_t* s16_32;  // [4][8][64][8] fp16 2^8 S
   const uint8_t* s8_32;    // [4][2][64][32] e4m3 S
+  // Split and layer plans whose input rows have at most 128 columns (a multiple of 8), for
+  // D = 128 sub-plans with the 32x32 operands above and D <= 64 sub-plans with rotk16: per
+  // head h, K in fp16 with the channel selection folded in (k = the input column; unselected
+  // columns zero) and the masks of the selected columns, else null
+  const uint16_t* kfold;   // D = 128: [n_heads][4][8][64][8] (32x32 encoder layout);
+                           // D <= 64: [n_heads][D/16][4][64][8] (rotk16 layout, 4 k steps)
+  const uint32_t* xmask;   // [n_heads][64 words]: D = 128 [8 k steps][2 halves][4 words],
+                           // D <= 64 [4 k steps][4 lane groups][4 words]
+  int x_cols;              // columns of the input rows the folded tables expect
 };
 
 struct PlanDev {

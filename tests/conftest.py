@@ -17,7 +17,7 @@ def pytest_terminal_summary(terminalreporter):
         return
     st = mod.STATS
     terminalreporter.write_line(
-        "parity: norm rel %.3g, gamma rel %.3g, score err/tol %.3g; in-band index mismatches "
-        "%d of %d, sign mismatches %d of %d, vectors with recomputed signs %d"
-        % (st["norm_rel"], st["gamma_rel"], st["score_ratio"], st["idx_mismatch"],
+        "parity: norm rel %.3g, gamma rel %.3g (err/tol %.3g), score err/tol %.3g; in-band index "
+        "mismatches %d of %d, sign mismatches %d of %d, vectors with recomputed signs %d"
+        % (st["norm_rel"], st["gamma_rel"], st["gamma_ratio"], st["score_ratio"], st["idx_mismatch"],
            st["idx_compared"], st["sign_mismatch"], st["sign_compared"], st["vectors_recomputed"]))

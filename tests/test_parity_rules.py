@@ -89,13 +89,31 @@ def test_sign_flip_outside_the_band_fails(case):
         parity.compare_codes(plan, ref, g, "planted")
 
 
-@pytest.mark.parametrize("key,rel", [("gamma", 2e-6), ("norm", 2e-6)])
-def test_norm_and_gamma_beyond_1e6_fail(case, key, rel):
+def test_norm_beyond_1e6_fails(case):
     sp, plan, X, ref, got = case
     g = _copy(got)
-    g[key] = np.asarray(ref[key]) * (1 + rel)
+    g["norm"] = np.asarray(ref["norm"]) * (1 + 2e-6)
     with pytest.raises(AssertionError, match="rel err"):
         parity.compare_codes(plan, ref, g, "planted")
+
+
+def test_gamma_beyond_its_bound_fails(case):
+    """gamma may differ by 1e-6 of itself plus 4 ulps (2^-22) of ||z|| = 1: 1.1 times that
+    bound fails (the next test: 0.9 times it passes)."""
+    sp, plan, X, ref, got = case
+    g = _copy(got)
+    gam = np.asarray(ref["gamma"])
+    g["gamma"] = gam + 1.1 * (1e-6 * gam + 2.0 ** -22)
+    with pytest.raises(AssertionError, match="gamma err"):
+        parity.compare_codes(plan, ref, g, "planted")
+
+
+def test_gamma_within_its_bound_passes(case):
+    sp, plan, X, ref, got = case
+    g = _copy(got)
+    gam = np.asarray(ref["gamma"])
+    g["gamma"] = gam + 0.9 * (1e-6 * gam + 2.0 ** -22)
+    parity.compare_codes(plan, ref, g, "at the bound")
 
 
 def test_scores_end_to_end_use_gpu_codes_where_codes_differ(case):
