@@ -78,31 +78,30 @@ OPERANDS_D128 = {
 }
 
 
-def kernel_sources_sha256():
-    """sha256 over every kernel source (the .hip files and their headers), in name order."""
+def kernel_sources_sha256(files):
+    """sha256 over the named kernel sources (files of the library's csrc/), in the given
+    order: a stored counter record names the sources of the kernels it measured."""
     import hashlib
     h = hashlib.sha256()
-    for f in sorted(os.listdir(KERNEL_DIR)):
-        if f.endswith((".hip", ".h")):
-            h.update(f.encode())
-            h.update(open(os.path.join(KERNEL_DIR, f), "rb").read())
+    for f in files:
+        h.update(f.encode())
+        h.update(open(os.path.join(KERNEL_DIR, f), "rb").read())
     return h.hexdigest()
 
 
 def measured_traffic(workload, kernel_key):
     """HBM bytes per launch of entry point `kernel_key` on `workload` from the stored counter
     runs (profiles/traffic_<workload>.json: FETCH_SIZE and WRITE_SIZE scaled by a copy of known
-    size), or None when there is no record or the kernel source changed since the counters
-    were taken."""
+    size), or None when there is no record or the sources of the measured kernels (listed in
+    the record) changed since the counters were taken."""
     try:
         rec = json.load(open(os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)))
-        src = kernel_sources_sha256()
-    except (OSError, ValueError):
+        k = rec.get("kernels", {}).get(kernel_key)
+        if k is None or kernel_sources_sha256(k["sources"]) != k.get("sources_sha256"):
+            return None
+    except (OSError, ValueError, KeyError, TypeError):
         return None
-    if rec.get("kernels_sha256") != src:
-        return None
-    k = rec.get("kernels", {}).get(kernel_key)
-    return None if k is None else k.get("hbm_bytes")
+    return k.get("hbm_bytes")
 
 
 def cpu_baseline(keys, queries, group, bits, seed, n_groups):
