@@ -17,7 +17,8 @@ LIB = os.path.join(LIBDIR, "libtq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kernels.hip", "encode128.hip", "score128.hip", "tq_api.cpp", "host_tables.cpp"]
+SOURCES = ["kernels.hip", "encode128.hip", "score128.hip", "score_f16.hip", "tq_api.cpp",
+           "host_tables.cpp"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -84,6 +84,15 @@ __device__ __forceinline__ uint8_t* encode_record(const EncodeArgs& a, int64_t r
 int launch_encode128(const EncodeArgs& ea, hipStream_t st, int64_t n_groups);
 // Compute units of the current device (cached per device; 256 if the query fails).
 int compute_units();
+// Scorer on decoded fp16 key tiles (score_f16.hip): one inner-product sub-plan with D >= 256
+// and at least kScoreF16MinQueries queries per group.  yrot and w are the queries' y' and
+// S y' (fp32, [rows][D]); img (n_groups x ceil(nq_per_group / 32) x 32 rows x 2D fp16) and
+// isc ([rows]) are its workspace.
+constexpr int64_t kScoreF16MinQueries = 128;
+bool score_f16_applies(const PlanDev& p, int64_t nq_per_group);
+int launch_score_f16(const PlanDev& p, const float* yrot, const float* w, uint16_t* img,
+                     float* isc, int64_t nq_per_group, int64_t n_groups, const uint8_t* codes,
+                     int64_t n, float* scores, hipStream_t st);
 
 constexpr int kEncWaves = 8;
 

@@ -1637,122 +1637,220 @@ __global__ void __launch_bounds__(kBlock) score_generic_kernel(ScoreArgs a) {
 }
 
 // ============================================================================ top-k
-// Per row, the k largest scores ordered by (-score, index): the quantized first stage of
-// two-stage retrieval (technical overview §4.2.2).  Each lane keeps a sorted list of its
-// KMAX best; lists are merged by k rounds of wave- and block-wide arg-max.
+// Per row, the k largest (value, index) pairs ordered by (-value, index): the quantized first
+// stage of two-stage retrieval (technical overview §4.2.2).  One workgroup streams its row
+// and appends every pair that beats the current k-th best to a candidate buffer in LDS.
+// Before the buffer could overflow, an exact radix select over 64-bit keys (ordered value
+// bits, then the complemented index) finds the k-th best of the buffer, keeps the k best and
+// raises the threshold to that pair.  Once the threshold has risen, nearly every element is
+// rejected by one comparison and the row streams at the rate its loads allow.
+constexpr int kSelRound = kBlock * 16;            // pairs one round of loads brings in
+constexpr int kSelCap = kSelRound + 768;          // buffer entries (4 workgroups per CU)
+constexpr int kSelKMax = 64;
+static_assert(kSelCap - kSelRound >= kSelKMax, "a compacted buffer plus one round must fit");
 
-// Insert (cv, ci) into a thread's sorted list when it beats the current k-th entry.
-template <int KMAX>
-__device__ __forceinline__ void topk_consider(float (&lv)[KMAX], int (&li)[KMAX], float& thr,
-                                              int& thr_i, int k, float cv, int ci) {
-  if (!better(cv, ci, thr, thr_i)) return;
-#pragma unroll
-  for (int s = 0; s < KMAX; ++s) {
-    const bool sw = better(cv, ci, lv[s], li[s]);
-    const float tv = lv[s];
-    const int ti = li[s];
-    lv[s] = sw ? cv : tv;
-    li[s] = sw ? ci : ti;
-    cv = sw ? tv : cv;
-    ci = sw ? ti : ci;
-  }
-#pragma unroll
-  for (int s = 0; s < KMAX; ++s)
-    if (s == k - 1) { thr = lv[s]; thr_i = li[s]; }
+struct SelShared {
+  float v[kSelCap];
+  int i[kSelCap];
+  alignas(16) int hist[256];
+  float kv[kSelKMax];
+  int ki[kSelKMax];
+  int cnt, nk, digit, above, bin;
+  float tv;
+  int ti;
+};
+
+// Larger key = better pair; -0 ranks as +0, since the two compare equal.
+__device__ __forceinline__ uint64_t sel_key(float v, int i) {
+  uint32_t b = __float_as_uint(v);
+  if ((b & 0x7FFFFFFFu) == 0) b = 0;
+  b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)b << 32) | (uint32_t)(0x7FFFFFFF - i);
 }
 
-// Merge the per-thread sorted lists of a block: k rounds of wave- and block-wide arg-max,
-// each writing one (index, value) of the row.
-template <int KMAX>
-__device__ void topk_emit(float (&lv)[KMAX], int (&li)[KMAX], int k, int64_t* ids, float* vals) {
-  __shared__ float wv[kBlock / kWave];
-  __shared__ int wi[kBlock / kWave];
-  __shared__ int winner;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int r = 0; r < k; ++r) {
-    float bv = lv[0];
-    int bi = li[0];
-    for (int m = 32; m >= 1; m >>= 1) {
-      const float ov = __shfl_xor(bv, m);
-      const int oi = __shfl_xor(bi, m);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-    }
-    if (lane == 0) { wv[wave] = bv; wi[wave] = bi; }
+// Keep the k best of the cnt buffered pairs at the front of the buffer and return the k-th
+// best as the new threshold.  Radix select, 8 bits a pass from the top of the key, until the
+// bin that holds the k-th key holds no more keys than are still needed.  Called by the whole
+// workgroup with cnt = sh.cnt >= k; ends with a barrier.
+__device__ void sel_compact(SelShared& sh, int cnt, int k, float& tv, int& ti) {
+  static_assert(kBlock == 256, "one histogram bin per thread");
+  const int t = threadIdx.x, lane = t & (kWave - 1);
+  uint64_t prefix = 0, mask = 0;
+  int need = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    sh.hist[t] = 0;
+    if (t == 0) sh.nk = 0;
     __syncthreads();
-    if (threadIdx.x == 0) {
-      float v = wv[0];
-      int i = wi[0];
-      for (int w = 1; w < kBlock / kWave; ++w)
-        if (better(wv[w], wi[w], v, i)) { v = wv[w]; i = wi[w]; }
-      winner = i;
-      ids[r] = i;
-      vals[r] = v;
+    for (int e = t; e < cnt; e += kBlock) {
+      const uint64_t key = sel_key(sh.v[e], sh.i[e]);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(int)(key >> shift) & 255], 1);
     }
     __syncthreads();
-    if (li[0] == winner) {
-#pragma unroll
-      for (int s = 0; s + 1 < KMAX; ++s) { lv[s] = lv[s + 1]; li[s] = li[s + 1]; }
-      lv[KMAX - 1] = -INFINITY;
-      li[KMAX - 1] = 0x7FFFFFFF;
+    if (t < kWave) {
+      // lane l holds bins 4l .. 4l + 3; suf = keys in bins >= 4l
+      const int4 h = reinterpret_cast<const int4*>(sh.hist)[lane];
+      const int s = h.x + h.y + h.z + h.w;
+      int suf = s;
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_down(suf, off);
+        if (lane + off < kWave) suf += o;
+      }
+      int run = suf - s;
+      if (run < need && need <= suf) {
+        const int hb[4] = {h.x, h.y, h.z, h.w};
+        for (int b = 3; b >= 0; --b) {
+          if (run + hb[b] >= need) {
+            sh.digit = 4 * lane + b;
+            sh.above = run;
+            sh.bin = hb[b];
+            break;
+          }
+          run += hb[b];
+        }
+      }
+    }
+    __syncthreads();
+    need -= sh.above;
+    prefix |= (uint64_t)sh.digit << shift;
+    mask |= (uint64_t)0xFF << shift;
+    if (sh.bin == need) break;
+  }
+  // the kept pairs: every key whose top bits exceed the selected prefix, and the whole
+  // selected bin (exactly k pairs, the indices being distinct)
+  for (int e = t; e < cnt; e += kBlock) {
+    const float v = sh.v[e];
+    const int i = sh.i[e];
+    if ((sel_key(v, i) & mask) >= prefix) {
+      const int p = atomicAdd(&sh.nk, 1);
+      if (p < kSelKMax) { sh.kv[p] = v; sh.ki[p] = i; }
     }
   }
+  __syncthreads();
+  if (t < kWave) {
+    float v = INFINITY;
+    int i = -1;  // ranks above every pair
+    if (t < k) {
+      v = sh.kv[t];
+      i = sh.ki[t];
+      sh.v[t] = v;
+      sh.i[t] = i;
+    }
+    for (int m = kWave / 2; m >= 1; m >>= 1) {
+      const float ov = __shfl_xor(v, m);
+      const int oi = __shfl_xor(i, m);
+      if (better(v, i, ov, oi)) { v = ov; i = oi; }
+    }
+    if (t == 0) { sh.tv = v; sh.ti = i; sh.cnt = k; }
+  }
+  __syncthreads();
+  tv = sh.tv;
+  ti = sh.ti;
 }
 
-template <int KMAX>
-__global__ void __launch_bounds__(kBlock) topk_kernel(const float* scores, int64_t n, int k,
-                                                      int64_t* ids, float* vals) {
-  const int64_t row = blockIdx.x;
-  const float* x = scores + row * n;
-  float lv[KMAX];
-  int li[KMAX];
-#pragma unroll
-  for (int s = 0; s < KMAX; ++s) { lv[s] = -INFINITY; li[s] = 0x7FFFFFFF; }
-  float thr = -INFINITY;
-  int thr_i = 0x7FFFFFFF;
-  if ((reinterpret_cast<uintptr_t>(x) & 15) == 0 && (n & 3) == 0) {
-    // 16-byte loads, four per thread in flight; a candidate is inserted only when it beats
-    // the thread's current k-th value (the common case is one comparison)
+// One round's 16 pairs per thread.  MODE 0: a score row read as float4 (16-byte aligned, n a
+// multiple of 4); MODE 1: a score row read as floats; MODE 2: candidate (value, index) lists.
+// Pairs past the end get a NaN value, which never beats the threshold.
+template <int MODE>
+__device__ __forceinline__ void sel_load(const float* x, const int* xi, int64_t n, int64_t base,
+                                         float (&v)[16], int (&id)[16]) {
+  const int t = threadIdx.x;
+  if constexpr (MODE == 0) {
     const float4* x4 = reinterpret_cast<const float4*>(x);
-    const int64_t n4 = n >> 2;
-    for (int64_t j0 = threadIdx.x; j0 < n4; j0 += 4 * kBlock) {
-      float4 u[4];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int64_t j = j0 + b * kBlock;
-        u[b] = j < n4 ? x4[j] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
-      }
+    for (int b = 0; b < 4; ++b) {
+      const int64_t j = (base >> 2) + b * kBlock + t;
+      const float4 u = 4 * j < n ? x4[j] : make_float4(NAN, NAN, NAN, NAN);
+      v[4 * b] = u.x;
+      v[4 * b + 1] = u.y;
+      v[4 * b + 2] = u.z;
+      v[4 * b + 3] = u.w;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const int ci = (int)(4 * (j0 + b * kBlock));
-        topk_consider<KMAX>(lv, li, thr, thr_i, k, u[b].x, ci);
-        topk_consider<KMAX>(lv, li, thr, thr_i, k, u[b].y, ci + 1);
-        topk_consider<KMAX>(lv, li, thr, thr_i, k, u[b].z, ci + 2);
-        topk_consider<KMAX>(lv, li, thr, thr_i, k, u[b].w, ci + 3);
-      }
+      for (int c = 0; c < 4; ++c) id[4 * b + c] = (int)(4 * j) + c;
     }
   } else {
-    for (int64_t j = threadIdx.x; j < n; j += kBlock)
-      topk_consider<KMAX>(lv, li, thr, thr_i, k, x[j], (int)j);
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+      const int64_t j = base + b * kBlock + t;
+      v[b] = j < n ? x[j] : NAN;
+      if constexpr (MODE == 2)
+        id[b] = j < n ? xi[j] : 0;
+      else
+        id[b] = (int)j;
+    }
   }
-  topk_emit<KMAX>(lv, li, k, ids + row * k, vals + row * k);
 }
 
-// Second stage of the fused score + top-k: per query row, the best k of its m candidates
-// (value, index) from the wide scorer's lists.
-template <int KMAX>
-__global__ void __launch_bounds__(kBlock) topk_merge_kernel(const float* cv, const int* ci,
-                                                            int64_t m, int k, int64_t* ids,
-                                                            float* vals) {
+template <int MODE>
+__global__ void __launch_bounds__(kBlock) select_kernel(const float* x, const int* xi, int64_t n,
+                                                        int k, int64_t* ids, float* vals) {
+  __shared__ SelShared sh;
   const int64_t row = blockIdx.x;
-  float lv[KMAX];
-  int li[KMAX];
+  x += row * n;
+  if (MODE == 2) xi += row * n;
+  ids += row * k;
+  vals += row * k;
+  const int t = threadIdx.x, lane = t & (kWave - 1);
+  if (t == 0) sh.cnt = 0;
+  float tv = -INFINITY;
+  int ti = 0x7FFFFFFF;
+  float v[16], nv[16];
+  int id[16], nid[16];
+  sel_load<MODE>(x, xi, n, 0, v, id);
+  __syncthreads();
+  for (int64_t base = 0; base < n; base += kSelRound) {
+    sel_load<MODE>(x, xi, n, base + kSelRound, nv, nid);
+    bool pass[16];
+    bool any = false;
 #pragma unroll
-  for (int s = 0; s < KMAX; ++s) { lv[s] = -INFINITY; li[s] = 0x7FFFFFFF; }
-  float thr = -INFINITY;
-  int thr_i = 0x7FFFFFFF;
-  for (int64_t j = threadIdx.x; j < m; j += kBlock)
-    topk_consider<KMAX>(lv, li, thr, thr_i, k, cv[row * m + j], ci[row * m + j]);
-  topk_emit<KMAX>(lv, li, k, ids + row * k, vals + row * k);
+    for (int b = 0; b < 16; ++b) {
+      pass[b] = better(v[b], id[b], tv, ti);
+      any |= pass[b];
+    }
+    if (__ballot(any)) {
+#pragma unroll
+      for (int b = 0; b < 16; ++b) {
+        const uint64_t m = __ballot(pass[b]);
+        if (m) {
+          int at = 0;
+          if (lane == 0) at = atomicAdd(&sh.cnt, __popcll(m));
+          at = __shfl(at, 0);
+          if (pass[b]) {
+            const int pos = at + lanes_below(m);
+            sh.v[pos] = v[b];
+            sh.i[pos] = id[b];
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // every thread reads the count before any appends again (both branches end in a barrier)
+    const int c = sh.cnt;
+    if (c > kSelCap - kSelRound)
+      sel_compact(sh, c, k, tv, ti);
+    else
+      __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 16; ++b) { v[b] = nv[b]; id[b] = nid[b]; }
+  }
+  int cnt = sh.cnt;
+  if (cnt > k) {
+    sel_compact(sh, cnt, k, tv, ti);
+    cnt = k;
+  }
+  // rank the k kept pairs; a short row (all but fewer than k values NaN) is padded
+  if (t < k) {
+    float pv = -INFINITY;
+    int pi = 0x7FFFFFFF;
+    if (t < cnt) { pv = sh.v[t]; pi = sh.i[t]; }
+    int r = 0;
+    for (int u = 0; u < k; ++u) {
+      const float uv = u < cnt ? sh.v[u] : -INFINITY;
+      const int ui = u < cnt ? sh.i[u] : 0x7FFFFFFF;
+      r += better(uv, ui, pv, pi) || (uv == pv && ui == pi && u < t);
+    }
+    ids[r] = pi;
+    vals[r] = pv;
+  }
 }
 
 // ============================================================================ attention
@@ -3010,7 +3108,13 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
   for (int sb = 0; sb < p.nsub; ++sb) small = small && p.sub[sb].D <= 128;
   const int qt_bs = (int)((nq_per_group + 3) / 4);
   // long vectors with many queries per group: the bit-sliced form over 128-coordinate chunks
-  const bool wide = !small && p.nsub == 1 && nq_per_group >= kWideQT && p.sub[0].D % 128 == 0;
+  // many queries per group on one long inner-product sub-plan: decoded fp16 key tiles on
+  // 32x32 fp16 matrix cores (score_f16.hip).  With top-k, the k <= 16 selection then runs over
+  // the stored scores; a larger k keeps the fused wide scorer (selecting 64 of 10^6 stored
+  // scores per row takes several times the scoring)
+  const bool f16 = !small && score_f16_applies(p, nq_per_group);
+  const bool wide = !small && !f16 && p.nsub == 1 && nq_per_group >= kWideQT &&
+                    p.sub[0].D % 128 == 0;
   const int qt_w = (int)((nq_per_group + kWideQT - 1) / kWideQT);
   const int64_t n_qblocks = (qt_w + kBlock / kWave - 1) / (kBlock / kWave);
   const int64_t nkb = (n + kWideKT * 16 - 1) / (kWideKT * 16);
@@ -3029,6 +3133,7 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
   // workspace: per sub-plan y', w, sums, images, epilogue constants
   size_t bytes = 0;
   size_t off_y[2], off_w[2], off_s[2], off_img[2], off_ec[2], off_sc = 0, off_cv = 0, off_ci = 0;
+  size_t off_i16 = 0, off_isc = 0;
   auto take = [&](size_t b) { size_t o = bytes; bytes += (b + 255) / 256 * 256; return o; };
   if (fused) {
     off_cv = take((size_t)nq * n_slices * tko->k * 4);
@@ -3050,6 +3155,10 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
       off_img[sb] = take((size_t)n_groups * qt_w * (D / 128) * (p.sub[sb].n_planes + 1) * 64 * 32);
       off_ec[sb] = take((size_t)n_groups * qt_w * kWideQT * 4 * 4);
     }
+  }
+  if (f16) {
+    off_i16 = take((size_t)n_groups * ((nq_per_group + 31) / 32) * 32 * 2 * p.sub[0].D * 2);
+    off_isc = take((size_t)nq * 4);
   }
   void* ws = nullptr;
   WorkspaceLease lease;
@@ -3123,6 +3232,10 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
   if (small) {
     sa.n_qtiles = qt_bs;
     if (!dispatch_bitslice(sa, n_groups * qt_bs, st)) rc = (int)hipErrorInvalidValue;
+  } else if (f16) {
+    rc = launch_score_f16(p, sa.yrot[0], sa.w[0], reinterpret_cast<uint16_t*>(wb + off_i16),
+                          reinterpret_cast<float*>(wb + off_isc), nq_per_group, n_groups, codes, n,
+                          scores, st);
   } else if (wide) {
     sa.n_qtiles = qt_w;
     WideTopk tk;
@@ -3137,12 +3250,8 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
                : dispatch_wide<false>(R, grid, st, sa, n_qblocks, tk);
     if (!rc && fused) {
       const int64_t m = n_slices * tko->k;
-      if (tko->k <= 16)
-        hipLaunchKernelGGL(topk_merge_kernel<16>, dim3((unsigned)nq), dim3(kBlock), 0, st, tk.cv,
-                           tk.ci, m, tko->k, tko->ids, tko->vals);
-      else
-        hipLaunchKernelGGL(topk_merge_kernel<64>, dim3((unsigned)nq), dim3(kBlock), 0, st, tk.cv,
-                           tk.ci, m, tko->k, tko->ids, tko->vals);
+      hipLaunchKernelGGL(select_kernel<2>, dim3((unsigned)nq), dim3(kBlock), 0, st, tk.cv,
+                         tk.ci, m, tko->k, tko->ids, tko->vals);
     }
   } else {
     int sumD = 0;
@@ -3301,10 +3410,12 @@ int launch_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* ids,
                 void* stream) {
   if (nq == 0) return 0;
   hipStream_t st = (hipStream_t)stream;
-  if (k <= 16)
-    hipLaunchKernelGGL(topk_kernel<16>, dim3((unsigned)nq), dim3(kBlock), 0, st, scores, n, k, ids, vals);
+  if ((reinterpret_cast<uintptr_t>(scores) & 15) == 0 && (n & 3) == 0)
+    hipLaunchKernelGGL(select_kernel<0>, dim3((unsigned)nq), dim3(kBlock), 0, st, scores,
+                       (const int*)nullptr, n, k, ids, vals);
   else
-    hipLaunchKernelGGL(topk_kernel<64>, dim3((unsigned)nq), dim3(kBlock), 0, st, scores, n, k, ids, vals);
+    hipLaunchKernelGGL(select_kernel<1>, dim3((unsigned)nq), dim3(kBlock), 0, st, scores,
+                       (const int*)nullptr, n, k, ids, vals);
   return hip_rc(hipGetLastError());
 }
 

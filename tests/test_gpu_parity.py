@@ -123,6 +123,37 @@ def test_topk_matches_oracle_exactly_with_ties(nq, n, k):
     assert np.array_equal(vals.cpu().numpy().astype(np.float64), vals_ref)
 
 
+@pytest.mark.parametrize("pattern,nq,n,k", [
+    ("rising", 3, 50001, 64),      # every element beats the threshold: a compaction per round
+    ("falling", 2, 40000, 64),     # the first round holds the answer
+    ("signed_zero", 2, 9001, 64),  # -0 and +0 tie, decided by index
+    ("half_neg_inf", 2, 10000, 33),
+    ("rising", 2, 4099, 7),        # one full round of loads and three elements
+    ("normal", 4, 1000003, 64),    # odd length: element loads
+])
+def test_topk_streaming_patterns(pattern, nq, n, k):
+    """Row patterns that drive the selection's candidate buffer to its limits, against the
+    oracle's top-k (ordered by (-value, index))."""
+    rng = np.random.default_rng(n + k)
+    if pattern == "rising":
+        s = np.tile(np.arange(n, dtype=np.float32) / n, (nq, 1))
+    elif pattern == "falling":
+        s = np.tile(-np.arange(n, dtype=np.float32), (nq, 1))
+    elif pattern == "signed_zero":
+        s = np.zeros((nq, n), dtype=np.float32)
+        s[:, ::3] = -0.0
+        s[:, 5::7] = -1.0
+    elif pattern == "half_neg_inf":
+        s = rng.standard_normal((nq, n)).astype(np.float32)
+        s[rng.random((nq, n)) < 0.5] = -np.inf
+    else:
+        s = rng.standard_normal((nq, n)).astype(np.float32)
+    ids, vals = tq.tq_topk(torch.from_numpy(s).to(DEV), k)
+    ids_ref, vals_ref = otq.topk(s.astype(np.float64), k)
+    assert np.array_equal(ids.cpu().numpy(), ids_ref), pattern
+    assert np.array_equal(vals.cpu().numpy().astype(np.float64), vals_ref), pattern
+
+
 # ----------------------------------------------------------------------------- shapes and edges
 
 @pytest.mark.parametrize("d,bits,n,dtype", [
@@ -174,10 +205,15 @@ def test_encode_over_a_wide_range_of_norms(d, dtype, lo, hi):
 
 @pytest.mark.parametrize("d,bits,n,nqg,groups", [
     (256, 4, 1000, 8, 1), (2048, 4, 300, 13, 1), (1536, 3, 517, 40, 1), (512, 2, 260, 16, 2),
-    (1024, 5, 129, 9, 2), (200, 3, 777, 64, 1)])
+    (1024, 5, 129, 9, 2), (200, 3, 777, 64, 1),
+    # at least 128 queries per group: the decoded fp16 key tiles (blocks of 256 queries and
+    # 128 keys), with ragged query blocks, ragged key blocks and every index width
+    (256, 4, 1000, 128, 1), (2048, 3, 333, 300, 1), (1536, 5, 517, 256, 2), (512, 2, 129, 200, 1),
+    (300, 3, 700, 513, 1), (1024, 4, 2000, 1000, 1)])
 def test_score_many_queries_long_vectors(d, bits, n, nqg, groups):
-    """The chunked bit-sliced scorer (D > 128, at least 8 queries per group), on oracle codes:
-    ragged key counts (not a multiple of the 256-key block), ragged query tiles of 8."""
+    """The scorers for D > 128 with many queries per group, on oracle codes: the chunked
+    bit-sliced scorer (8 to 127 queries per group) and the decoded fp16 key tiles (128 or
+    more); ragged key counts, ragged query tiles."""
     rng = np.random.default_rng(d + nqg)
     xs = rng.standard_normal((groups * n, d)).astype(np.float32)
     xs[3] = 0.0

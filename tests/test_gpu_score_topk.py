@@ -42,6 +42,8 @@ def _unfused(plan, y, rec, n, k, nqg, groups):
     (128, 3, 4096, 4, 8, 10, False),        # D = 128: scores to a temporary, then top-k
     (200, 3, 777, 4, 1, 10, False),         # fewer than 8 queries per group: not fused
     (128, 4, 1500, 4, 2, 10, True),         # outlier split: two sub-plans, not fused
+    (1536, 4, 5077, 256, 1, 10, False),     # 256 queries: decoded fp16 key tiles, then top-k
+    (2048, 3, 3000, 130, 2, 64, False),     # two groups, a ragged query block
 ])
 def test_score_topk_equals_score_then_topk_and_oracle(d, bits, n, nqg, groups, k, mask):
     rng = np.random.default_rng(d * 7 + n)
