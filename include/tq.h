@@ -285,7 +285,9 @@ tq_status tq_dequantize(const tq_plan* plan, const void* codes, int64_t n, void*
  * undone once per row, so no value vector is reconstructed on its own.
  *   vplan   the values' plan (MSE or inner-product; one sub-plan)
  *   logits  device float32 [n_groups*nq_per_group][n], e.g. from tq_score;
- *           finite
+ *           finite, or -inf for a masked token (weight 0).  A row needs at
+ *           least one finite logit: a row masked everywhere has no softmax and
+ *           its output is NaN.  NaN and +inf logits are not supported.
  *   vcodes  device, n_groups * n records of vplan (group g from record g*n)
  *   out     device, n_groups*nq_per_group rows of d elements (dt), stride ldo
  * Uses a workspace of (D + 2) floats per row and 1024-token chunk (the

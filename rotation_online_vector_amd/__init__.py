@@ -155,6 +155,25 @@ def _out(t, dtype, numel, name):
         raise ValueError("%s must be contiguous %s with at least %d elements" % (name, dtype, numel))
 
 
+def _codes(t, nbytes, name="codes"):
+    """An input of records: contiguous uint8 holding at least nbytes, since the library reads
+    the records as bytes from data_ptr on."""
+    import torch
+    if t.dtype != torch.uint8 or not t.is_contiguous() or t.numel() < nbytes:
+        raise ValueError("%s must be contiguous uint8 with at least %d bytes" % (name, nbytes))
+
+
+def _groups(rows, nq_per_group, n_groups, what="query rows"):
+    """nq_per_group (by default rows / n_groups); empty groups stay empty, as in the C ABI."""
+    if n_groups < 0 or (nq_per_group is not None and nq_per_group < 0):
+        raise ValueError("group sizes must be >= 0")
+    if nq_per_group is None:
+        nq_per_group = rows // n_groups if n_groups else 0
+    if nq_per_group * n_groups != rows:
+        raise ValueError("%s != nq_per_group * n_groups" % what)
+    return nq_per_group
+
+
 def _rows(t, d):
     """(n, ld) of a tensor viewed as rows of d elements with unit inner stride."""
     if t.shape[-1] != d or t.stride(-1) != 1:
@@ -285,12 +304,8 @@ def tq_score(plan, q, codes, n, nq_per_group=None, n_groups=1, scores=None, stre
     import torch
     _on_gpu(q, codes, scores)
     nq, ld = _rows(q, plan.d)
-    if nq_per_group is None:
-        nq_per_group = nq // n_groups
-    if nq_per_group * n_groups != nq:
-        raise ValueError("query rows != nq_per_group * n_groups")
-    if codes.numel() < n_groups * n * plan.record_bytes:
-        raise ValueError("codes buffer too small")
+    nq_per_group = _groups(nq, nq_per_group, n_groups)
+    _codes(codes, n_groups * n * plan.record_bytes)
     if scores is None:
         scores = torch.empty((nq, n), dtype=torch.float32, device=q.device)
     _out(scores, torch.float32, nq * n, "scores")
@@ -308,12 +323,8 @@ def tq_score_noalloc(plan, q, codes, n, scores, nq_per_group=None, n_groups=1, s
         raise ValueError("tq_score_noalloc writes into a caller-provided scores tensor")
     _on_gpu(q, codes, scores)
     nq, ld = _rows(q, plan.d)
-    if nq_per_group is None:
-        nq_per_group = nq // n_groups
-    if nq_per_group * n_groups != nq:
-        raise ValueError("query rows != nq_per_group * n_groups")
-    if codes.numel() < n_groups * n * plan.record_bytes:
-        raise ValueError("codes buffer too small")
+    nq_per_group = _groups(nq, nq_per_group, n_groups)
+    _codes(codes, n_groups * n * plan.record_bytes)
     _out(scores, torch.float32, nq * n, "scores")
     _check("tq_score_noalloc", load_library().tq_score_noalloc(
         plan.handle, ctypes.c_void_p(q.data_ptr()), _dtype_code(q), nq_per_group, n_groups, ld,
@@ -346,12 +357,8 @@ def tq_score_topk(plan, q, codes, n, k, nq_per_group=None, n_groups=1, ids=None,
     import torch
     _on_gpu(q, codes, ids, vals)
     nq, ld = _rows(q, plan.d)
-    if nq_per_group is None:
-        nq_per_group = nq // n_groups
-    if nq_per_group * n_groups != nq:
-        raise ValueError("query rows != nq_per_group * n_groups")
-    if codes.numel() < n_groups * n * plan.record_bytes:
-        raise ValueError("codes buffer too small")
+    nq_per_group = _groups(nq, nq_per_group, n_groups)
+    _codes(codes, n_groups * n * plan.record_bytes)
     if ids is None:
         ids = torch.empty((nq, k), dtype=torch.int64, device=q.device)
     if vals is None:
@@ -369,8 +376,7 @@ def tq_dequantize(plan, codes, n, x=None, dtype=None, stream=None):
     """Reconstructed vectors [n, d] (float32 or bfloat16) from n records."""
     import torch
     _on_gpu(codes, x)
-    if codes.numel() < n * plan.record_bytes:
-        raise ValueError("codes buffer too small")
+    _codes(codes, n * plan.record_bytes)
     if x is None:
         x = torch.empty((n, plan.d), dtype=dtype or torch.float32, device=codes.device)
     rows, ld = _rows(x, plan.d)
@@ -389,13 +395,10 @@ def tq_attend(vplan, logits, vcodes, n, scale, nq_per_group=None, n_groups=1, ou
     _on_gpu(logits, vcodes, out)
     if logits.dtype != torch.float32 or not logits.is_contiguous() or logits.shape[-1] != n:
         raise ValueError("logits must be contiguous float32 [rows, n]")
-    rows = logits.numel() // n
-    if nq_per_group is None:
-        nq_per_group = rows // n_groups
-    if nq_per_group * n_groups != rows:
-        raise ValueError("logit rows != nq_per_group * n_groups")
-    if vcodes.numel() < n_groups * n * vplan.record_bytes:
-        raise ValueError("codes buffer too small")
+    # n = 0 reaches the library, which rejects it (TQ_EINVAL)
+    rows = logits.numel() // n if n else (logits.shape[0] if logits.dim() > 1 else 0)
+    nq_per_group = _groups(rows, nq_per_group, n_groups, "logit rows")
+    _codes(vcodes, n_groups * n * vplan.record_bytes, "vcodes")
     if out is None:
         out = torch.empty((rows, vplan.d), dtype=dtype or torch.float32, device=logits.device)
     r2, ldo = _rows(out, vplan.d)

@@ -2191,7 +2191,7 @@ __global__ void __launch_bounds__(kBlock) attend_mfma_kernel(AttnArgs a) {
         const float nw = snrm[t] * inv;
 #pragma unroll
         for (int r = 0; r < NRW; ++r) {
-          const float e = r < nr ? __expf(pl[r][k] - rm[r]) : 0.f;
+          const float e = r < nr ? __expf(fmaxf(pl[r][k] - rm[r], -INFINITY)) : 0.f;
           esum[r] += e;
           const float w = e * nw;
           typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;
@@ -2438,7 +2438,7 @@ __attribute__((amdgpu_waves_per_eu(RQ == 1 && D <= 128 && R <= 3 ? 4 : 1))) atte
       const float nw = snrm[lane] * (nsc > 0.f ? 1.f / nsc : 0.f);
 #pragma unroll
       for (int r = 0; r < NRW; ++r) {
-        const float e = r < nr ? __expf(pl[r] - rm[r]) : 0.f;
+        const float e = r < nr ? __expf(fmaxf(pl[r] - rm[r], -INFINITY)) : 0.f;
         esum[r] += e;
         const float w = e * nw;
         typedef __attribute__((ext_vector_type(2))) __fp16 f16x2;

@@ -181,3 +181,29 @@ def test_attend_logit_patterns_that_move_the_reference(pattern):
     ref = otq.attend(op, L.astype(np.float64), st, scale, nqg)
     vmax = np.max(np.linalg.norm(otq.dequantize(op, st), axis=1))
     _check(_np(out), ref, vmax, False, "attend %s" % pattern)
+
+
+@pytest.mark.parametrize("d,nqg", [(128, 4), (256, 8), (64, 16)])
+def test_attend_masked_tokens(d, nqg):
+    """-inf logits (masked tokens) weigh nothing: a row whose whole first chunk, or whole
+    middle chunk, is masked, rows with scattered masks, and a masked tail; every row keeps at
+    least one finite logit."""
+    n, groups = 3 * 1024 + 200, 2
+    rng = np.random.default_rng(d + nqg)
+    V = rng.standard_normal((groups * n, d)).astype(np.float32)
+    L = (rng.standard_normal((groups * nqg, n)) * 2.0).astype(np.float32)
+    L[0, :1024] = -np.inf                  # first chunk masked
+    L[1, 1024:2048] = -np.inf              # middle chunk masked
+    L[2, rng.random(n) < 0.7] = -np.inf    # scattered
+    L[3, 3 * 1024:] = -np.inf              # ragged tail masked
+    L[nqg + 1, 1:] = -np.inf               # one visible token
+    plan, op = tq.tq_plan_create_mse(d, 3, 8), otq.make_mse_plan(d, 3, 8)
+    vc = tq.tq_encode(plan, torch.from_numpy(V).to(DEV))
+    out = tq.tq_attend(plan, torch.from_numpy(L).to(DEV), vc, n, 0.7, nq_per_group=nqg,
+                       n_groups=groups)
+    torch.cuda.synchronize()
+    st = layout.unpack_mse(vc.cpu().numpy(), op.D, op.R)
+    ref = otq.attend(op, L.astype(np.float64), st, 0.7, nqg)
+    assert np.all(np.isfinite(ref))
+    vmax = np.max(np.linalg.norm(otq.dequantize(op, st), axis=1))
+    _check(_np(out), ref, vmax, False, "attend masked d=%d" % d)

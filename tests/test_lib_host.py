@@ -163,3 +163,25 @@ def test_bindings_check_caller_outputs():
     with pytest.raises(ValueError):
         tq._out(t, torch.float32, 4, "vals")
     tq._out(t, torch.float32, 3, "vals")
+
+
+def test_bindings_check_code_inputs_and_group_sizes():
+    """Record buffers are read as contiguous bytes: a non-uint8, non-contiguous or short
+    buffer is refused; empty groups give nq_per_group 0 (the C ABI's no-op) instead of a
+    division by zero, and mismatched group sizes are refused."""
+    import torch
+    import rotation_online_vector_amd as tq
+    tq._codes(torch.zeros(56, dtype=torch.uint8), 56)
+    with pytest.raises(ValueError):
+        tq._codes(torch.zeros(56, dtype=torch.uint8), 57)
+    with pytest.raises(ValueError):
+        tq._codes(torch.zeros(14, dtype=torch.int32), 56)
+    with pytest.raises(ValueError):
+        tq._codes(torch.zeros((2, 56), dtype=torch.uint8).t(), 56)
+    assert tq._groups(0, None, 0) == 0
+    assert tq._groups(12, None, 3) == 4
+    assert tq._groups(12, 6, 2) == 6
+    with pytest.raises(ValueError):
+        tq._groups(12, 5, 2)
+    with pytest.raises(ValueError):
+        tq._groups(4, None, -1)
