@@ -220,7 +220,8 @@ tq_status tq_score(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_p
  * For plans with every D <= 128 the workspace is about
  *   n_groups * ceil(nq_per_group/4) * (2^(R-1) + 1) * 2 KiB per sub-plan
  * (R index bits), e.g. 128 groups of 4 queries at 3 bits use 0.78 MiB; longer
- * vectors also keep y' and S y' per query (8 D bytes each).  Every call on a
+ * vectors also keep y', S y' and the shares of its sum per query (8 D +
+ * 4 ceil(D/128) bytes each, plus the images of the scorer).  Every call on a
  * device shares that device's array: calls that overlap on one device (different
  * streams, or host threads) race and must be ordered by the caller.
  */

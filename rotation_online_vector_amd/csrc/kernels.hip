@@ -445,7 +445,6 @@ __global__ void __launch_bounds__(512) qjl_gemm_kernel(QjlGemmArgs a) {
 template <int XL, bool VEC>
 __device__ __forceinline__ void load_x8(const EncodeArgs& a, int64_t row, int c0,
                                         uint32_t (&limbs)[XL][4], float& ss, const int* chl) {
-  const SubDev& s = a.s;
   float v[8];
   if (VEC) {
     if constexpr (XL == 1) {       // bf16 input: its own exact limb
@@ -1143,63 +1142,100 @@ __global__ void __launch_bounds__(kBlock) qprep_kernel(QPrepArgs a) {
   }
 }
 
-// w = S y' for kProjQB queries per workgroup: their y' sit in LDS, each thread owns rows
-// j = tid, tid + 256, ... and reads every row of S once for all kProjQB queries (16-byte
-// loads); also the sums of w.
-constexpr int kProjQB = 4;
+// w = S y' on the matrix cores (32x32x16 bf16).  S is exact in bf16 and y' is split into
+// three bf16 limbs (together y' to within 2^-24 of its value), so every product is exact
+// and the fp32 accumulation gives w to fp32 rounding.  A workgroup takes 64 queries and
+// kProjCols rows of S; each wave 32 queries and 64 rows (two output tiles sharing one limb
+// split of y').  The workgroup writes its share of each query's sum of w to
+// part[query][blockIdx.y], and qsum_kernel adds the shares in order, so that the sums do not
+// depend on scheduling.
+constexpr int kProjCols = 128;
+constexpr int kProjRows = 64;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
 
-__global__ void __launch_bounds__(kBlock) qproj_kernel(QPrepArgs a, int64_t nq) {
+__global__ void __launch_bounds__(kBlock) qproj_mfma_kernel(QPrepArgs a, int64_t nq, float* part) {
   const SubDev& s = a.s;
-  const int D = s.D;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t q0 = (int64_t)blockIdx.x * kProjQB;
-  const int nqb = (nq - q0) < kProjQB ? (int)(nq - q0) : kProjQB;
-  __shared__ __attribute__((aligned(16))) float ys[kProjQB][kMaxD];
-  __shared__ float red[kProjQB][kBlock / kWave];
-  for (int q = 0; q < kProjQB; ++q)
-    for (int i = tid; i < D; i += kBlock) ys[q][i] = q < nqb ? a.yrot[(q0 + q) * D + i] : 0.f;
-  __syncthreads();
-  float sw[kProjQB];
+  const int D = s.D, K = s.k;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int c = lane & 31, h = lane >> 5;
+  const int wq = wave & 1, wj = wave >> 1;
+  const int64_t q0 = (int64_t)blockIdx.x * kProjRows + 32 * wq;
+  const int jw = blockIdx.y * kProjCols + 64 * wj;
+  __shared__ float wsum[kBlock / kWave][32];
+  f32x16 acc[2];
 #pragma unroll
-  for (int q = 0; q < kProjQB; ++q) sw[q] = 0.f;
-  for (int j = tid; j < s.k; j += kBlock) {
-    const uint4* Sj = reinterpret_cast<const uint4*>(s.S + (size_t)j * D);
-    float acc[kProjQB];
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int q = 0; q < kProjQB; ++q) acc[q] = 0.f;
-    for (int c = 0; c < D / 8; ++c) {
-      const uint4 u = Sj[c];
-      const uint32_t wv[4] = {u.x, u.y, u.z, u.w};
+    for (int i = 0; i < 16; ++i) acc[t][i] = 0.f;
+  const bool ok0 = jw + c < K, ok1 = jw + 32 + c < K;
+  if (jw < K) {
+    // A: query q0 + c (the last query past the end); B: rows jw + c and jw + 32 + c of S
+    // (the last row past K)
+    const float* yr = a.yrot + (q0 + c < nq ? q0 + c : nq - 1) * D + 8 * h;
+    const uint16_t* S0 = s.S + (size_t)(ok0 ? jw + c : K - 1) * D + 8 * h;
+    const uint16_t* S1 = s.S + (size_t)(ok1 ? jw + 32 + c : K - 1) * D + 8 * h;
+    for (int i0 = 0; i0 < D; i0 += 16) {
+      const float4 ya = *reinterpret_cast<const float4*>(yr + i0);
+      const float4 yb = *reinterpret_cast<const float4*>(yr + i0 + 4);
+      const uint4 s0 = *reinterpret_cast<const uint4*>(S0 + i0);
+      const uint4 s1 = *reinterpret_cast<const uint4*>(S1 + i0);
+      const float v[8] = {ya.x, ya.y, ya.z, ya.w, yb.x, yb.y, yb.z, yb.w};
+      uint32_t hw[4], mw[4], lw[4];
 #pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const float s0 = __uint_as_float(wv[h] << 16), s1 = __uint_as_float(wv[h] & 0xFFFF0000u);
-#pragma unroll
-        for (int q = 0; q < kProjQB; ++q) {
-          acc[q] = fmaf(s0, ys[q][8 * c + 2 * h], acc[q]);
-          acc[q] = fmaf(s1, ys[q][8 * c + 2 * h + 1], acc[q]);
-        }
+      for (int pr = 0; pr < 4; ++pr) {
+        const float x0 = v[2 * pr], x1 = v[2 * pr + 1];
+        const uint32_t hp = pack_bf16_rne(x0, x1);
+        const float r0 = x0 - __uint_as_float(hp << 16), r1 = x1 - __uint_as_float(hp & 0xFFFF0000u);
+        const uint32_t mp = pack_bf16_rne(r0, r1);
+        const float t0 = r0 - __uint_as_float(mp << 16), t1 = r1 - __uint_as_float(mp & 0xFFFF0000u);
+        hw[pr] = hp;
+        mw[pr] = mp;
+        lw[pr] = pack_bf16_rne(t0, t1);
       }
-    }
-#pragma unroll
-    for (int q = 0; q < kProjQB; ++q) {
-      if (q < nqb) a.w[(q0 + q) * D + j] = acc[q];
-      sw[q] += acc[q];
+      const bf16x8 ah = bf16x8_from_words(hw[0], hw[1], hw[2], hw[3]);
+      const bf16x8 am = bf16x8_from_words(mw[0], mw[1], mw[2], mw[3]);
+      const bf16x8 al = bf16x8_from_words(lw[0], lw[1], lw[2], lw[3]);
+      const bf16x8 b0 = bf16x8_from_words(s0.x, s0.y, s0.z, s0.w);
+      const bf16x8 b1 = bf16x8_from_words(s1.x, s1.y, s1.z, s1.w);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b0, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b1, acc[1], 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, b0, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, b1, acc[1], 0, 0, 0);
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b0, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b1, acc[1], 0, 0, 0);
     }
   }
+  // element i of tile t in this lane: query q0 + 8 (i / 4) + 4 h + i % 4, output jw + 32 t + c
 #pragma unroll
-  for (int q = 0; q < kProjQB; ++q) {
-    for (int m = 32; m >= 1; m >>= 1) sw[q] += __shfl_xor(sw[q], m);
-    if (lane == 0) red[q][wave] = sw[q];
+  for (int i = 0; i < 16; ++i) {
+    const int64_t q = q0 + 8 * (i / 4) + 4 * h + i % 4;
+    if (q < nq) {
+      if (ok0) a.w[q * D + jw + c] = acc[0][i];
+      if (ok1) a.w[q * D + jw + 32 + c] = acc[1][i];
+    }
+    float t = (ok0 ? acc[0][i] : 0.f) + (ok1 ? acc[1][i] : 0.f);
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) t += __shfl_xor(t, m);
+    if (c == 0) wsum[wave][8 * (i / 4) + 4 * h + i % 4] = t;
   }
   __syncthreads();
-  if (tid < nqb) {
-    float t = 0.f;
-    for (int i = 0; i < kBlock / kWave; ++i) t += red[tid][i];
-    a.sums[(q0 + tid) * 2 + 1] = t;
+  // query r of the workgroup: waves (r / 32) and (r / 32) + 2 hold its two column halves
+  if (threadIdx.x < kProjRows) {
+    const int r = threadIdx.x;
+    const int64_t q = (int64_t)blockIdx.x * kProjRows + r;
+    if (q < nq) part[q * gridDim.y + blockIdx.y] = wsum[r / 32][r % 32] + wsum[r / 32 + 2][r % 32];
   }
 }
 
-
+// sum of w per query: the workgroups' shares in order
+__global__ void __launch_bounds__(kBlock) qsum_kernel(float* sums, const float* part, int64_t nq,
+                                                      int nparts) {
+  const int64_t q = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (q >= nq) return;
+  float t = 0.f;
+  for (int b = 0; b < nparts; ++b) t += part[q * nparts + b];
+  sums[q * 2 + 1] = t;
+}
 
 // ------------------------------------------------------------ bit-sliced scorer, D > 128
 // The same binary-plane form for long vectors and many queries per group (retrieval): the
@@ -3107,11 +3143,9 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
   bool small = true;
   for (int sb = 0; sb < p.nsub; ++sb) small = small && p.sub[sb].D <= 128;
   const int qt_bs = (int)((nq_per_group + 3) / 4);
-  // long vectors with many queries per group: the bit-sliced form over 128-coordinate chunks
   // many queries per group on one long inner-product sub-plan: decoded fp16 key tiles on
-  // 32x32 fp16 matrix cores (score_f16.hip).  With top-k, the k <= 16 selection then runs over
-  // the stored scores; a larger k keeps the fused wide scorer (selecting 64 of 10^6 stored
-  // scores per row takes several times the scoring)
+  // 32x32 fp16 matrix cores (score_f16.hip), top-k then selected from the stored scores;
+  // fewer queries per group: the bit-sliced form over 128-coordinate chunks (wide)
   const bool f16 = !small && score_f16_applies(p, nq_per_group);
   const bool wide = !small && !f16 && p.nsub == 1 && nq_per_group >= kWideQT &&
                     p.sub[0].D % 128 == 0;
@@ -3132,7 +3166,7 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
   }
   // workspace: per sub-plan y', w, sums, images, epilogue constants
   size_t bytes = 0;
-  size_t off_y[2], off_w[2], off_s[2], off_img[2], off_ec[2], off_sc = 0, off_cv = 0, off_ci = 0;
+  size_t off_y[2], off_w[2], off_s[2], off_p[2], off_img[2], off_ec[2], off_sc = 0, off_cv = 0, off_ci = 0;
   size_t off_i16 = 0, off_isc = 0;
   auto take = [&](size_t b) { size_t o = bytes; bytes += (b + 255) / 256 * 256; return o; };
   if (fused) {
@@ -3148,6 +3182,7 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
     off_y[sb] = small ? 0 : take(nq * D * 4);
     off_w[sb] = small ? 0 : take(nq * D * 4);
     off_s[sb] = small ? 0 : take(nq * 2 * 4);
+    off_p[sb] = small ? 0 : take(nq * ((p.sub[sb].k + kProjCols - 1) / kProjCols) * 4);
     if (small) {
       off_img[sb] = take((size_t)n_groups * qt_bs * (p.sub[sb].n_planes + 1) * 64 * 32);
       off_ec[sb] = take((size_t)n_groups * qt_bs * 16 * 4);
@@ -3209,8 +3244,12 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
       sa.ec[sb] = fa.ec;
     } else {
       hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)nq), dim3(kBlock), 0, st, qa);
-      hipLaunchKernelGGL(qproj_kernel, dim3((unsigned)((nq + kProjQB - 1) / kProjQB)), dim3(kBlock),
-                         0, st, qa, nq);
+      const int nparts = (p.sub[sb].k + kProjCols - 1) / kProjCols;
+      float* part = reinterpret_cast<float*>(wb + off_p[sb]);
+      hipLaunchKernelGGL(qproj_mfma_kernel, dim3((unsigned)((nq + kProjRows - 1) / kProjRows), (unsigned)nparts),
+                         dim3(kBlock), 0, st, qa, nq, part);
+      hipLaunchKernelGGL(qsum_kernel, dim3((unsigned)((nq + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                         st, qa.sums, part, nq, nparts);
       if (wide) {
         WideImgArgs wa;
         wa.s = p.sub[sb];
