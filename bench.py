@@ -50,6 +50,10 @@ def parse():
                              "small", "mse", "attend", "decode"],
                     help="long-context decode (default, the headline line); the other shapes "
                          "report the same fields for their own step (no CPU leg)")
+    ap.add_argument("--hbm-rotate", type=int, default=0, metavar="MIB",
+                    help="kv, split35, split25: keep copies of a step's inputs and outputs "
+                         "filling MIB MiB and use the next copy each step, so that every step "
+                         "reads HBM rather than the 256 MB Infinity Cache")
     ap.add_argument("--no-hbm-ceiling", action="store_true",
                     help="skip the plain copy / read of 2 GiB measured after the timed steps")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -159,7 +163,14 @@ def _rate(n, ms):
     return n / ms * 1e3 if ms > 0 else None
 
 
-def build_workload(name, dev, W_all):
+def _copies(rotate_mib, set_bytes):
+    """Number of copies of a step's buffers that fill rotate_mib MiB (1: no rotation)."""
+    if rotate_mib <= 0:
+        return 1
+    return max(2, -(-(rotate_mib << 20) // set_bytes))
+
+
+def build_workload(name, dev, W_all, rotate_mib=0):
     """Inputs resident on the device, plans, output buffers and the launch phases of one step.
 
     Returns dict(config, phases=[(entry point, fn)], bytes={entry point: algorithmic bytes},
@@ -303,16 +314,23 @@ def build_workload(name, dev, W_all):
         scores = torch.empty((n_kv * G, n_tok), dtype=torch.float32, device=dev)
         xk = keys.view(n_keys, d)
         n_scores = n_kv * G * n_tok
+        R = _copies(rotate_mib, n_keys * d * 2 + n_keys * rb + n_scores * 4)
+        xs = [xk] + [xk.clone() for _ in range(R - 1)]
+        cs = [codes] + [torch.empty_like(codes) for _ in range(R - 1)]
+        ss = [scores] + [torch.empty_like(scores) for _ in range(R - 1)]
+        cur = [0]
         return dict(
             config={"workload": W["name"], "kv_heads": n_kv, "tokens": n_tok, "d": d,
                     "bits": W["bits"], "gqa_group": G, "keys_per_step": n_keys,
                     "scores_per_step": n_scores, "record_bytes": rb},
-            phases=[("tq_encode", lambda: tq.tq_encode(plan, xk, codes)),
-                    ("tq_score", lambda: tq.tq_score(plan, queries, codes, n=n_tok, nq_per_group=G,
-                                                     n_groups=n_kv, scores=scores))],
+            phases=[("tq_encode", lambda: tq.tq_encode(plan, xs[cur[0]], cs[cur[0]])),
+                    ("tq_score", lambda: tq.tq_score(plan, queries, cs[cur[0]], n=n_tok,
+                                                     nq_per_group=G, n_groups=n_kv,
+                                                     scores=ss[cur[0]]))],
             bytes={"tq_encode": n_keys * d * 2 + n_keys * rb,
                    "tq_score": n_keys * rb + n_scores * 4 + n_kv * G * d * 2},
-            n_keys=n_keys, n_scores=n_scores, keep=(plan, keys, queries, codes, scores))
+            copies=R, advance=lambda: cur.__setitem__(0, (cur[0] + 1) % R),
+            n_keys=n_keys, n_scores=n_scores, keep=(plan, keys, queries, xs, cs, ss))
     if name in ("split35", "split25"):
         import numpy as np
         keys, queries, ch = workloads.kv_inputs(dev, n_kv=W["n_kv"], n_tok=W["n_tok"], d=W["d"],
@@ -329,12 +347,18 @@ def build_workload(name, dev, W_all):
         codes = torch.empty((n_kv * n_tok, rb), dtype=torch.uint8, device=dev)
         scores = torch.empty((n_kv * G, n_tok), dtype=torch.float32, device=dev)
         xk, qv = keys.view(n_kv * n_tok, d), queries.view(n_kv * G, d)
+        R = _copies(rotate_mib, n_kv * n_tok * (d * 2 + rb) + n_kv * G * n_tok * 4)
+        xs = [xk] + [xk.clone() for _ in range(R - 1)]
+        cs = [codes] + [torch.empty_like(codes) for _ in range(R - 1)]
+        ss = [scores] + [torch.empty_like(scores) for _ in range(R - 1)]
+        cur = [0]
 
         def enc():
-            tq.tq_encode_groups(plan, xk, n_kv, codes)
+            tq.tq_encode_groups(plan, xs[cur[0]], n_kv, cs[cur[0]])
 
         def sco():
-            tq.tq_score(plan, qv, codes, n=n_tok, nq_per_group=G, n_groups=n_kv, scores=scores)
+            tq.tq_score(plan, qv, cs[cur[0]], n=n_tok, nq_per_group=G, n_groups=n_kv,
+                        scores=ss[cur[0]])
         n_keys, n_scores = n_kv * n_tok, n_kv * G * n_tok
         return dict(
             config={"workload": W["name"], "kv_heads": n_kv, "tokens": n_tok, "d": d,
@@ -344,7 +368,8 @@ def build_workload(name, dev, W_all):
             phases=[("tq_encode", enc), ("tq_score", sco)],
             bytes={"tq_encode": n_keys * d * 2 + n_keys * rb,
                    "tq_score": n_keys * rb + n_scores * 4 + n_kv * G * d * 2},
-            n_keys=n_keys, n_scores=n_scores, keep=(plan, keys, queries, codes, scores))
+            copies=R, advance=lambda: cur.__setitem__(0, (cur[0] + 1) % R),
+            n_keys=n_keys, n_scores=n_scores, keep=(plan, keys, queries, xs, cs, ss))
     if name in ("retrieval", "retrieval2", "small"):
         if name != "small":
             keys, queries = workloads.retrieval_inputs(dev, n_keys=W["n_keys"],
@@ -433,7 +458,11 @@ def main():
              "retrieval2": dict(workloads.RETRIEVAL, name=workloads.RETRIEVAL["name"] + "-2stage")}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = build_workload(args.workload, dev, W_all)
+    if args.hbm_rotate and args.workload not in ("kv", "split35", "split25"):
+        print("--hbm-rotate applies to kv, split35 and split25 (the others exceed the cache)",
+              file=sys.stderr)
+        sys.exit(2)
+    wl = build_workload(args.workload, dev, W_all, args.hbm_rotate)
     # the code set of the smaller shapes fits the 256 MB Infinity Cache: their GB/s are
     # cache-resident effective rates, not HBM rates
     code_bytes = wl["config"].get("cache_bytes",
@@ -444,10 +473,19 @@ def main():
     wl["config"]["residency"] = (
         ("cache-resident: %.0f MB of codes, under the 256 MB Infinity Cache (effective GB/s)"
          if code_bytes < 256e6 else "HBM: %.0f MB of codes") % (code_bytes / 1e6))
+    if wl.get("copies", 1) > 1:
+        wl["config"]["residency"] = (
+            "HBM, buffer-rotated: %d copies of the step's inputs and outputs (%.0f MB of codes "
+            "each), the next copy every step" % (wl["copies"], code_bytes / 1e6))
+        wl["config"]["buffer_copies"] = wl["copies"]
     phases = wl["phases"]
     stream = torch.cuda.current_stream()
 
+    advance = wl.get("advance")
+
     def step(ev=None):
+        if advance is not None:
+            advance()
         for i, (_, fn) in enumerate(phases):
             if ev is not None:
                 ev[i].record(stream)
