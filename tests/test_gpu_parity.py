@@ -298,6 +298,34 @@ def test_outlier_split_plan_small():
                             np.linalg.norm(_np(x), axis=1), "split score")
 
 
+@pytest.mark.parametrize("nq", [5, 70])
+def test_outlier_split_plan_long_vectors(nq):
+    """A split plan whose sub-plans are D = 256 (240 regular channels) and D = 64 (60 outlier
+    channels): the long-vector query path for both (the projection w = S y' with fewer rows of
+    S than one workgroup covers for the short one), against the oracle's split estimate; two
+    calls give the same scores bit for bit (the sums of w are added in a fixed order)."""
+    d, n = 300, 900
+    rng = np.random.default_rng(nq)
+    mask = np.zeros(d, dtype=np.uint8)
+    mask[np.sort(rng.choice(d, 60, replace=False))] = 1
+    xs = rng.standard_normal((n, d)).astype(np.float32)
+    xs[:, mask == 1] *= 8
+    ys = rng.standard_normal((nq, d)).astype(np.float32)
+    sp = otq.make_split_plan(d, 3, 4, mask, 4)
+    plan = tq.tq_plan_create(d, 3, 4, mask, 4)
+    assert [p.D for p in sp.plans] == [256, 64]
+    st = [parity.stored(c) for c in otq.encode_split(sp, xs.astype(np.float64))]
+    rec = torch.from_numpy(layout.pack_split(sp, st)).to(DEV)
+    y = torch.from_numpy(ys).to(DEV)
+    est = tq.tq_score(plan, y, rec, n=n)
+    est2 = tq.tq_score(plan, y, rec, n=n)
+    torch.cuda.synchronize()
+    assert torch.equal(est, est2)
+    est_ref = otq.score_split(sp, st, ys.astype(np.float64))
+    parity.check_scores(est.cpu().numpy(), est_ref, np.linalg.norm(ys.astype(np.float64), axis=1),
+                        np.linalg.norm(xs.astype(np.float64), axis=1), "split d=300 nq=%d" % nq)
+
+
 def test_invalid_calls_raise():
     plan = tq.tq_plan_create(128, 3, 0)
     x = torch.zeros((4, 64), device=DEV)
