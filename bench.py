@@ -68,10 +68,10 @@ KERNEL_DIR = os.path.join(ROOT, "rotation_online_vector_amd", "csrc")
 MIXED_D128 = "f16+f8+f4 mfma, f32 acc"
 DTYPES = {
     "longctx": MIXED_D128, "kv": MIXED_D128, "split35": MIXED_D128, "split25": MIXED_D128,
-    "small": "bf16+f8+f4 mfma, f32 acc", "attend": MIXED_D128 + "; bf16 mfma attention",
-    "decode": MIXED_D128 + "; bf16 mfma attention", "mse": "bf16 mfma, f32 acc",
-    "retrieval": "f32 fwht, bf16+f8+f4 mfma, f32 acc",
-    "retrieval2": "f32 fwht, bf16+f8+f4 mfma, f32 acc",
+    "small": "bf16+f8+f4 mfma, f32 acc", "attend": MIXED_D128 + "; fp16 mfma attention",
+    "decode": MIXED_D128 + "; fp16 mfma attention", "mse": "fp16 mfma, f32 acc",
+    "retrieval": "f32 fwht; bf16 mfma signs and query projection; fp16 mfma scores; f32 acc",
+    "retrieval2": "f32 fwht; bf16 mfma signs and query projection; fp16 mfma scores; f32 acc",
 }
 OPERANDS_D128 = {
     "tq_encode": "bf16 keys scaled to fp16 against the exact integer rotation in fp16; the "
