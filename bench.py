@@ -35,7 +35,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_BF16_TFLOPS = 2500.0      # dense bf16 matrix peak of the MI355X
+MFMA_16BIT_TFLOPS = 2500.0     # dense bf16 and fp16 matrix peak of the MI355X
 
 
 def parse():
@@ -525,11 +525,10 @@ def main():
     flops = wl.get("flops")
     if flops:
         # a contraction-bound workload: algorithmic MFMA flops per launch against the dense
-        # bf16 peak (the sign projection runs on bf16 MFMA, the scorer on fp8 x fp4, whose
-        # own peak is twice that)
+        # 16-bit peak (the sign projection runs on bf16 MFMA, the scorer on fp16: one peak)
         tf = flops[dom] / (kern[dom]["ms"] * 1e-3) / 1e12
-        roof = {"kernel": dom, "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tf / MFMA_BF16_TFLOPS, 4), "traffic": None,
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_16BIT_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tf / MFMA_16BIT_TFLOPS, 4), "traffic": None,
                 "flops_per_launch": flops[dom]}
         for k, v in kern.items():
             v["tflops"] = flops[k] / (v["ms"] * 1e-3) / 1e12
@@ -560,7 +559,7 @@ def main():
                              "alg_gbs": round(v["gbs"], 1),
                              "hbm_frac": round(v["gbs"] / HBM_PEAK_GBS, 4)},
                             **({"mfma_tflops": round(v["tflops"], 1),
-                                "mfma_bf16_frac": round(v["tflops"] / MFMA_BF16_TFLOPS, 4)}
+                                "mfma_frac": round(v["tflops"] / MFMA_16BIT_TFLOPS, 4)}
                                if "tflops" in v else {}))
                     for k, v in kern.items()},
         "roofline": roof,

@@ -138,15 +138,24 @@ score_f16_kernel(ScoreF16Args a) {
 #pragma unroll
     for (int m = 0; m < W; ++m) wd[m] = wd0[m] >> (16 * h);
     const uint32_t nb = ~wd[R];                            // set bit = beta 0 = weight -G
+    // sign bit 2j + 1 moved to 2j + 16, so that one shift puts pair j's two bits at 15 and 31
+    const uint32_t z = (nb & 0x5555u) | ((nb & 0xAAAAu) << 15);
+    // planes 0 and 1 of pair j side by side: nibble j / 2 of pq[j % 2]
+    uint32_t pq[2] = {0u, 0u};
+    if constexpr (R >= 2) {
+      pq[0] = (wd[0] & 0x3333u) | ((wd[1] << 2) & 0xCCCCu);
+      pq[1] = ((wd[0] >> 2) & 0x3333u) | (wd[1] & 0xCCCCu);
+    }
     uint32_t cw[8], sw[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      uint32_t idx = 0;
+      uint32_t idx;
+      if constexpr (R >= 2) idx = (pq[j & 1] >> (4 * (j >> 1))) & 15u;
+      else idx = (wd[0] >> (2 * j)) & 3u;
 #pragma unroll
-      for (int m = 0; m < R; ++m) idx |= ((wd[m] >> (2 * j)) & 3u) << (2 * m);
+      for (int m = 2; m < R; ++m) idx |= ((wd[m] >> (2 * j)) & 3u) << (2 * m);
       cw[j] = ptab[idx];
-      // sign bits of the pair (bits 2j, 2j + 1) to bits 15 and 31; G's own are 0
-      sw[j] = (G2 | ((nb << (15 - 2 * j)) & 0x8000u)) | ((nb << (30 - 2 * j)) & 0x80000000u);
+      sw[j] = ((z << (15 - 2 * j)) & 0x80008000u) | G2;
     }
     bfr[buf][h][nt][col] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     bfr[buf][h][nt][col + 32] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
@@ -183,42 +192,62 @@ score_f16_kernel(ScoreF16Args a) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mt][t][i] = 0.f;
   uint4 a0[kMT][4], a1[kMT][4];
-  uint32_t wn[W];
+  uint32_t w0[W], w1[W];                                   // record words, two chunks ahead
   load_a(0, a0);
-  load_words(0, wn);
+  load_words(0, w0);
   __syncthreads();                                         // the pair table
-  decode(wn, 0);
+  decode(w0, 0);
+  if (NC > 1) load_words(1, w1);
   __syncthreads();
   // One chunk: the MFMAs of chunk g on the query rows av (loaded during chunk g - 1) and the
-  // keys in bfr[g % 2], while chunk g + 1's rows load into an and its keys are decoded into
-  // the other buffer (last read before the previous barrier).
-  auto chunk = [&](int g, const uint4 (&av)[kMT][4], uint4 (&an)[kMT][4]) {
+  // keys in bfr[g % 2], while chunk g + 1's rows load into an, chunk g + 2's record words into
+  // wl, and chunk g + 1's keys (words wd, loaded during chunk g - 1) are decoded into the
+  // other buffer (last read before the previous barrier).  The B fragments of k step ks + 1
+  // are read from LDS while the MFMAs of step ks issue, one read per two MFMAs, so that each
+  // read has about eight MFMAs of time to land.
+  auto chunk = [&](int g, const uint4 (&av)[kMT][4], uint4 (&an)[kMT][4], uint32_t (&wl)[W],
+                   const uint32_t (&wd)[W]) {
     const int buf = g & 1;
     const bool more = g + 1 < NC;
-    if (more) {
-      load_a(g + 1, an);
-      load_words(g + 1, wn);
-    }
+    if (more) load_a(g + 1, an);
+    if (g + 2 < NC) load_words(g + 2, wl);
+    uint4 bc[4], bn[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int t = 0; t < 4; ++t) bc[t] = bfr[buf][0][t][lane];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bn[t] = bfr[buf][ks + 1][t][lane];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const uint4 b = bfr[buf][ks][t][lane];
-        const f16x8 bv = f16x8_from_words(b.x, b.y, b.z, b.w);
+        const f16x8 bv = f16x8_from_words(bc[t].x, bc[t].y, bc[t].z, bc[t].w);
 #pragma unroll
         for (int mt = 0; mt < kMT; ++mt)
           acc[mt][t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
               f16x8_from_words(av[mt][ks].x, av[mt][ks].y, av[mt][ks].z, av[mt][ks].w), bv,
               acc[mt][t], 0, 0, 0);
       }
-    if (more) decode(wn, buf ^ 1);
+      if (ks < 3)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) bc[t] = bn[t];
+    }
+    // issue order: the 4 reads of step 0, then (1 LDS read, 2 MFMAs) x 12, then the last 8
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // 0x100: LDS reads
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 0x008: matrix instructions
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    if (more) decode(wd, buf ^ 1);
     __syncthreads();
   };
-  // two chunks per trip with the row buffers swapped (D / 32 is even), so that no registers
-  // are copied between chunks
+  // two chunks per trip with the row and word buffers swapped (D / 32 is even), so that no
+  // registers are copied between chunks
   for (int g = 0; g < NC; g += 2) {
-    chunk(g, a0, a1);
-    chunk(g + 1, a1, a0);
+    chunk(g, a0, a1, w0, w1);
+    chunk(g + 1, a1, a0, w1, w0);
   }
   // ---- epilogue: element i of tile (mt, t) is query 32 mt + 8 (i / 4) + 4 half + i % 4 of
   // the wave, key 32 t + lane % 32 ----
