@@ -301,8 +301,11 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
 // (8 MiB at D = 2048) for every 16 vectors, as the fused kernel does, would move far more
 // than the residuals themselves.  Block tile: 128 vectors x 256 rows of S, k steps of 32
 // coordinates through double-buffered LDS; 8 waves, each 64 vectors x 64 rows (4 x 4 MFMA
-// tiles, both limbs into one accumulator).  The signs go straight into the records.
-constexpr int kQgBN = 128, kQgBM = 256, kQgKS = 32, kQgRS = kQgKS + 8;   // LDS row: 80 B
+// tiles, both limbs into one accumulator).  The signs go straight into the records.  An LDS
+// row is four 16-byte pieces stored at piece q ^ ((row / 2) % 4): the 16-byte stores of two
+// consecutive rows and the fragment reads of eight consecutive rows then fall in distinct
+// banks.
+constexpr int kQgBN = 128, kQgBM = 256, kQgKS = 32, kQgRS = kQgKS;   // LDS row: 64 B, pieces swizzled
 constexpr int kQgNQ = kQgKS / 8;          // 16-byte pieces per row and k step
 constexpr int kQgNI = kQgBM * kQgNQ / 512; // pieces per thread, A and B alike
 
@@ -319,6 +322,7 @@ template <int D>
 __global__ void __launch_bounds__(512) qjl_gemm_kernel(QjlGemmArgs a) {
   static_assert(D % kQgBM == 0 && D % kQgKS == 0, "whole blocks and k steps");
   static_assert(2 * kQgBN == kQgBM, "A (two limbs) and B have the same piece count");
+  static_assert(kQgKS == 32, "four 16-byte pieces per row");
   __shared__ __attribute__((aligned(16))) uint16_t As[2][2][kQgBN * kQgRS];   // [buf][limb]
   __shared__ __attribute__((aligned(16))) uint16_t Bs[2][kQgBM * kQgRS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -337,10 +341,10 @@ __global__ void __launch_bounds__(512) qjl_gemm_kernel(QjlGemmArgs a) {
     int64_t v = v0 + vv;
     v = v < a.nv ? v : a.nv - 1;            // past the batch: a real row, never stored
     asrc[i] = (limb ? a.rl : a.rh) + v * D + 8 * q;
-    adst[i] = limb * kQgBN * kQgRS + vv * kQgRS + 8 * q;
+    adst[i] = limb * kQgBN * kQgRS + vv * kQgRS + 8 * (q ^ ((vv >> 1) & 3));
     const int rr = it / kQgNQ;
     bsrc[i] = a.S + (size_t)(r0 + rr) * D + 8 * q;
-    bdst[i] = rr * kQgRS + 8 * q;
+    bdst[i] = rr * kQgRS + 8 * (q ^ ((rr >> 1) & 3));
   }
   uint4 ra[kQgNI], rb[kQgNI];
 #define TQ_QG_LOAD(k0)                                                     \
@@ -365,16 +369,15 @@ __global__ void __launch_bounds__(512) qjl_gemm_kernel(QjlGemmArgs a) {
   for (int ks = 0; ks < NK; ++ks) {
     const int buf = ks & 1;
     if (ks + 1 < NK) { TQ_QG_LOAD(kQgKS * (ks + 1)) }   // next step's tiles, in flight
-#pragma unroll
-    for (int sub = 0; sub < kQgKS / 32; ++sub) {
+    {
       bf16x8 bo[4];
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
         bo[rt] = *reinterpret_cast<const bf16x8*>(
-            &Bs[buf][(64 * rq + 16 * rt + col) * kQgRS + 32 * sub + 8 * grp]);
+            &Bs[buf][(64 * rq + 16 * rt + col) * kQgRS + 8 * (grp ^ ((col >> 1) & 3))]);
 #pragma unroll
       for (int vt = 0; vt < 4; ++vt) {
-        const int arow = (64 * vh + 16 * vt + col) * kQgRS + 32 * sub + 8 * grp;
+        const int arow = (64 * vh + 16 * vt + col) * kQgRS + 8 * (grp ^ ((col >> 1) & 3));
         const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&As[buf][0][arow]);
         const bf16x8 al = *reinterpret_cast<const bf16x8*>(&As[buf][1][arow]);
 #pragma unroll
