@@ -301,7 +301,8 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
 // (8 MiB at D = 2048) for every 16 vectors, as the fused kernel does, would move far more
 // than the residuals themselves.  Block tile: 128 vectors x 256 rows of S, k steps of 32
 // coordinates through double-buffered LDS; 8 waves, each 64 vectors x 64 rows (4 x 4 MFMA
-// tiles, both limbs into one accumulator).  The signs go straight into the records.  An LDS
+// tiles, both limbs into one accumulator); a 1-D grid mapped to tiles per XCD (in the
+// kernel).  The signs go straight into the records.  An LDS
 // row is four 16-byte pieces stored at piece q ^ ((row / 2) % 4): the 16-byte stores of two
 // consecutive rows and the fragment reads of eight consecutive rows then fall in distinct
 // banks.
@@ -328,8 +329,15 @@ __global__ void __launch_bounds__(512) qjl_gemm_kernel(QjlGemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int vh = wave & 1, rq = wave >> 1;
-  const int64_t v0 = (int64_t)blockIdx.y * kQgBN;
-  const int r0 = blockIdx.x * kQgBM;
+  // block b runs on XCD b % 8 (workgroups are dealt round-robin); XCD x takes the key tiles
+  // kt = x (mod 8), each with all NR row tiles of S, so that every limb tile is fetched by
+  // one XCD and each XCD's L2 holds the 8 limb tiles and NR row tiles in use
+  constexpr int NR = D / kQgBM;
+  const int b = blockIdx.x, jx = b >> 3;
+  const int64_t kt = (int64_t)(jx / NR) * 8 + (b & 7);
+  if (kt * kQgBN >= a.nv) return;            // padding of the grid to whole groups of 8
+  const int64_t v0 = kt * kQgBN;
+  const int r0 = (jx % NR) * kQgBM;
   // global -> LDS pieces: A (limb, vector, 16-byte piece) and B (row, piece)
   const uint16_t* asrc[kQgNI];
   const uint16_t* bsrc[kQgNI];
@@ -2959,7 +2967,8 @@ static int launch_encode_d(const EncodeArgs& ea, hipStream_t st) {
       ga.rec_bytes = ea.rec_bytes;
       ga.rec_off = ea.s.rec_off;
       ga.R = ea.s.R;
-      const dim3 grid((unsigned)(D / kQgBM), (unsigned)((eb.n + kQgBN - 1) / kQgBN));
+      const int64_t nkt = (eb.n + kQgBN - 1) / kQgBN;
+      const dim3 grid((unsigned)(8 * (D / kQgBM) * ((nkt + 7) / 8)));
       hipLaunchKernelGGL(qjl_gemm_kernel<D>, grid, dim3(512), 0, st, ga);
       rc = hip_rc(hipGetLastError());
     }
