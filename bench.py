@@ -121,19 +121,36 @@ def cpu_baseline(keys, queries, group, bits, seed, n_groups):
         threads = os.cpu_count() or 1
     n_seq, n_kv, n_tok, d = keys.shape
     plan = otq.make_plan(d, bits, seed)
-    n_scores, dt = 0, 0.0
+    n_scores, n_keys, dt_enc, dt_sc = 0, 0, 0.0, 0.0
     for g in range(n_groups):
         s, h = divmod(g, n_kv)
         x = keys[s, h].float().cpu().numpy().astype(np.float64)
         y = queries[s, h * group:(h + 1) * group].float().cpu().numpy().astype(np.float64)
         t0 = time.perf_counter()
-        est = otq.score(plan, otq.encode(plan, x), y)
-        dt += time.perf_counter() - t0
+        codes = otq.encode(plan, x)
+        t1 = time.perf_counter()
+        est = otq.score(plan, codes, y)
+        dt_enc += t1 - t0
+        dt_sc += time.perf_counter() - t1
         n_scores += est.size
+        n_keys += x.shape[0]
+    dt = dt_enc + dt_sc
     return {"value": n_scores / dt, "unit": "scores/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "encode_vectors_per_s": n_keys / dt_enc, "score_scores_per_s": n_scores / dt_sc,
             "sample": "%d of %d (sequence, KV head) groups: %d keys encoded and scored against "
                       "their %d query heads in fp64 (plan solve excluded), %.1f s of CPU time"
                       % (n_groups, n_seq * n_kv, n_groups * n_tok, group, dt)}
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def hbm_ceiling(dev, mib=2048, reps=5):
