@@ -228,13 +228,14 @@ __global__ void __launch_bounds__(kBlock) encode_kernel(EncodeArgs a) {
     // ---- residual limbs to LDS ----
     if constexpr (!MSE) {
       uint32_t hi[EPT / 2], lo[EPT / 2];
+      const uint32_t sel_lo = neg_one_low_half();
 #pragma unroll
       for (int e = 0; e < EPT; e += 2) {
-        const uint32_t h0 = f32_to_bf16_rne(v[e]), h1 = f32_to_bf16_rne(v[e + 1]);
-        const uint32_t l0 = f32_to_bf16_rne(v[e] - bf16_bits_to_f32(h0));
-        const uint32_t l1 = f32_to_bf16_rne(v[e + 1] - bf16_bits_to_f32(h1));
-        hi[e / 2] = h0 | (h1 << 16);
-        lo[e / 2] = l0 | (l1 << 16);
+        // two hardware round-to-nearest-even conversions per pair; the remainders read the
+        // packed high limbs in place
+        hi[e / 2] = pack_bf16_rne(v[e], v[e + 1]);
+        lo[e / 2] = pack_bf16_rne(residual_below_bf16(hi[e / 2], sel_lo, v[e]),
+                                  residual_below_bf16(hi[e / 2], 0xBF800000u, v[e + 1]));
       }
       uint4* ph;
       uint4* pl;
