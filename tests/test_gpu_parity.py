@@ -160,7 +160,10 @@ def test_topk_streaming_patterns(pattern, nq, n, k):
     (128, 3, 1, "float32"), (128, 3, 1001, "bfloat16"), (100, 3, 517, "float32"),
     (33, 5, 300, "bfloat16"), (1, 2, 65, "float32"), (64, 2, 200, "float32"),
     (256, 4, 130, "bfloat16"), (512, 3, 70, "float32"), (1024, 2, 40, "float32"),
-    (1536, 4, 40, "float32"), (2048, 5, 20, "bfloat16"), (32, 4, 129, "float32")])
+    (1536, 4, 40, "float32"), (2048, 5, 20, "bfloat16"), (32, 4, 129, "float32"),
+    # D >= 1024: the sign GEMM's workgroups cover key tiles in groups of 8 per XCD; 12 and
+    # 10 tiles of 128 keys leave a partial group and a ragged last tile
+    (1024, 3, 128 * 11 + 5, "float32"), (2048, 4, 128 * 9 + 1, "bfloat16")])
 def test_encode_and_score_shapes(d, bits, n, dtype):
     rng = np.random.default_rng(d + n)
     xs = rng.standard_normal((n, d)).astype(np.float32)
