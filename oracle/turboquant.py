@@ -179,6 +179,23 @@ def dequantize(plan, codes):
     return np.asarray(codes["norm"])[:, None] * rotation.unrotate(zhat, plan.signs)[:, :plan.d]
 
 
+def score_mse(plan, codes, Y):
+    """est[q, n] from TurboQuant-MSE codes (uses idx and norm only).  The overview's quantized
+    distance (§4.2.2) rotates the query with the key rotation and sums, coordinate by
+    coordinate, the query value against the centroid of the key's cell; the index keeps the
+    norm apart (§4.2.1), so the sum is scaled by it:
+        est = n * <Pi pad(y), c[idx]>.
+    The query stays at full precision, as for the inner-product estimate (the page's sketch
+    also quantizes it; the asymmetric reading is the deep dive's, §三).  This is the plain
+    inner product of y with the reconstruction of `dequantize`, since Pi is orthogonal.  For an
+    inner-product plan the same sum over the (b-1)-bit first stage is the first term of
+    `score`.  The estimate is biased: the cell centroids shrink it, and over random rotations
+    its mean is <x, y> (1 - D E[(Z - c(Z))^2]) with Z a rotated coordinate."""
+    yr = rotation.rotate(pad(Y, plan.D), plan.signs)
+    zhat = plan.levels[np.asarray(codes["idx"])]
+    return np.asarray(codes["norm"])[None, :] * (yr @ zhat.T)
+
+
 def dequantize_split(sp, codes_list):
     """Per sub-plan reconstruction, each written back to its own channels."""
     n = len(codes_list[0]["norm"])
