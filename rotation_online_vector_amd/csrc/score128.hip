@@ -1,8 +1,10 @@
 // Bit-sliced scorer for sub-plans with D <= 128 (gfx950): per-query fp8 images of the
 // rotated query and of its QJL projection, then est = n (<y', c[idx]> + gamma sqrt(pi/2)/k
 // <w, 2 beta - 1>) for every key of the group as binary dot products on fp8 x fp4 MFMAs
-// (TurboQuant technical overview §1.2.3, §4.2.2; deep dive §三).  The image layout and the
-// parity-plane expansion are described with bitslice_coord in device_common.h.
+// (TurboQuant technical overview §1.2.3, §4.2.2; deep dive §三).  TurboQuant-MSE records
+// (overview §4.1.1, §4.2.1) are scored by the first term alone, est = n <y', c[idx]>.  The
+// image layout and the parity-plane expansion are described with bitslice_coord in
+// device_common.h.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -34,8 +36,9 @@ __global__ void __launch_bounds__(kBlock) qprep_bitslice_kernel(QFusedArgs a) {
   // overlaps the query's rotation
   constexpr int HALF = D / 2;
   const int row = tid >> 1, half = tid & 1;
+  const bool proj = s.k > 0;              // an MSE plan has no projection: w = 0
   uint4 u[HALF / 8];
-  if (row < D) {
+  if (row < D && proj) {
     const uint16_t* Sj = s.S + (size_t)row * D + half * HALF;
 #pragma unroll
     for (int c = 0; c < HALF / 8; ++c) u[c] = reinterpret_cast<const uint4*>(Sj)[c];
@@ -104,7 +107,7 @@ __global__ void __launch_bounds__(kBlock) qprep_bitslice_kernel(QFusedArgs a) {
   __syncthreads();
   // ---- w = S y' : thread pair (2 row, 2 row + 1) shares row tid / 2, k = D rows ----
   float acc = 0.f;
-  if (row < D) {
+  if (row < D && proj) {
     const float* yh = ys + half * HALF;
 #pragma unroll
     for (int c = 0; c < HALF / 8; ++c) {
@@ -198,33 +201,43 @@ __global__ void __launch_bounds__(kBlock) qprep_bitslice_kernel(QFusedArgs a) {
 // One sub-plan's share of a 16-key step (R index bits, D <= 128); lane l handles key column
 // l % 16 and code word l / 16.  The MFMA reads the B registers of every lane, so all lanes
 // must reach it with defined operands: loads are branch-free from an always-valid record
-// (`key_safe`) and masked by selects.
+// (`key_safe`) and masked by selects.  MSE records hold R index words per chunk and the norm
+// (no sign word, no gamma).
 template <int R> struct KeyWords {
   uint32_t wd[R + 1];
   float nrm, gam;
 };
 
-template <int R>
+template <int R, bool MSE = false>
 __device__ __forceinline__ KeyWords<R> load_key_words(const SubDev& s, const uint8_t* codes,
                                                       int rec_bytes, int64_t key_safe, bool key_ok) {
+  constexpr int W = MSE ? R : R + 1;      // words per 32-coordinate chunk
   const int G = (threadIdx.x & 63) >> 4;
   const bool chunk_ok = 32 * G < s.D;
   const uint8_t* rec = codes + key_safe * rec_bytes + s.rec_off;
-  const uint32_t* pw = reinterpret_cast<const uint32_t*>(rec) + (chunk_ok ? G : 0) * (R + 1);
+  const uint32_t* pw = reinterpret_cast<const uint32_t*>(rec) + (chunk_ok ? G : 0) * W;
   KeyWords<R> k;
 #pragma unroll
-  for (int m = 0; m <= R; ++m) {
+  for (int m = 0; m < W; ++m) {
     const uint32_t v = pw[m];
     k.wd[m] = (key_ok && chunk_ok) ? v : 0u;
   }
-  const uint32_t* tail = reinterpret_cast<const uint32_t*>(rec + (s.D / 32) * (R + 1) * 4);
-  const uint32_t t0 = tail[0], t1 = tail[1];
+  const uint32_t* tail = reinterpret_cast<const uint32_t*>(rec + (s.D / 32) * W * 4);
+  const uint32_t t0 = tail[0];
   k.nrm = key_ok ? __uint_as_float(t0) : 0.f;
-  k.gam = key_ok ? __uint_as_float(t1) : 0.f;
+  if constexpr (MSE) {
+    k.wd[R] = 0u;
+    k.gam = 0.f;
+  } else {
+    const uint32_t t1 = tail[1];
+    k.gam = key_ok ? __uint_as_float(t1) : 0.f;
+  }
   return k;
 }
 
-template <int R>
+// est = n (<y', c[idx]> + gamma sqrt(pi/2)/k <w, 2 beta - 1>); an MSE record gives the first
+// term alone, n <y', c[idx]> (overview §4.2.2's quantized distance with the norm of §4.2.1)
+template <int R, bool MSE = false>
 __device__ __forceinline__ float bitslice_estimate(const KeyWords<R>& k, const i32x8* A,
                                                    const float* e4) {
   constexpr int NP = 1 << (R - 1);
@@ -237,8 +250,9 @@ __device__ __forceinline__ float bitslice_estimate(const KeyWords<R>& k, const i
       if ((pmask_c<R>(p) >> m) & 1) P ^= k.wd[m];
     am = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[p], fp4_operand(P), am, 0, 4, 0, 127, 0, 127);
   }
-  aq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[NP], fp4_operand(k.wd[R]), aq, 0, 4, 0, 127, 0, 127);
   const float msum = am[0] + am[1] + am[2];
+  if constexpr (MSE) return k.nrm * fmaf(e4[1], msum, e4[0]);
+  aq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[NP], fp4_operand(k.wd[R]), aq, 0, 4, 0, 127, 0, 127);
   const float qsum = aq[0] + aq[1] + aq[2];
   return k.nrm * (fmaf(e4[1], msum, e4[0]) + k.gam * fmaf(e4[3], qsum, e4[2]));
 }
@@ -248,8 +262,9 @@ constexpr int kScoreSteps = 4;   // 16-key steps whose loads are issued together
 // logits of keys 16 u + col; read back as 4 consecutive keys per lane, they go out as one
 // 16-byte non-temporal store (the logits are written once and not read by this kernel).
 
-template <int R0, int R1>
+template <int R0, int R1, bool MSE = false>
 __global__ void __launch_bounds__(kBlock) score_bitslice_kernel(ScoreArgs a, int keys_per_block) {
+  static_assert(!MSE || R1 == 0, "MSE plans have one sub-plan");
   constexpr int NP0 = 1 << (R0 - 1);
   constexpr int NP1 = R1 > 0 ? (1 << (R1 - 1)) : 0;
   constexpr int U = kScoreSteps;
@@ -301,7 +316,7 @@ __global__ void __launch_bounds__(kBlock) score_bitslice_kernel(ScoreArgs a, int
       const int64_t key = k0 + 16 * u + col;
       const bool key_ok = key < kend;
       const int64_t key_safe = key_ok ? key : kend - 1;
-      w0[u] = load_key_words<R0>(a.p.sub[0], codes, a.p.rec_bytes, key_safe, key_ok);
+      w0[u] = load_key_words<R0, MSE>(a.p.sub[0], codes, a.p.rec_bytes, key_safe, key_ok);
       if constexpr (R1 > 0)
         w1[u] = load_key_words<R1>(a.p.sub[1], codes, a.p.rec_bytes, key_safe, key_ok);
     }
@@ -310,7 +325,7 @@ __global__ void __launch_bounds__(kBlock) score_bitslice_kernel(ScoreArgs a, int
     float* tr = xpose[wave];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      float est = bitslice_estimate<R0>(w0[u], A0, e0);
+      float est = bitslice_estimate<R0, MSE>(w0[u], A0, e0);
       if constexpr (R1 > 0) est += bitslice_estimate<R1>(w1[u], A1, e1);
       asm volatile("" : "+v"(est));
       tr[G * 64 + 16 * u + col] = est;
@@ -334,7 +349,7 @@ __global__ void __launch_bounds__(kBlock) score_bitslice_kernel(ScoreArgs a, int
   }
 }
 
-template <int R0, int R1>
+template <int R0, int R1, bool MSE = false>
 static void launch_bitslice(const ScoreArgs& sa, int64_t n_gt, hipStream_t st) {
   // 2048 keys per block when that still gives ~2048 blocks; fewer (down to one 256-key batch
   // per block) for short code sets, so that small problems still spread over the chip
@@ -343,12 +358,22 @@ static void launch_bitslice(const ScoreArgs& sa, int64_t n_gt, hipStream_t st) {
   kpb = (kpb + 255) / 256 * 256;
   kpb = kpb < 256 ? 256 : (kpb > 2048 ? 2048 : kpb);
   const int64_t kblocks = (sa.n + kpb - 1) / kpb;
-  hipLaunchKernelGGL((score_bitslice_kernel<R0, R1>), dim3((unsigned)kblocks, (unsigned)n_gt),
+  hipLaunchKernelGGL((score_bitslice_kernel<R0, R1, MSE>), dim3((unsigned)kblocks, (unsigned)n_gt),
                      dim3(kBlock), 0, st, sa, (int)kpb);
 }
 
 bool dispatch_bitslice(const ScoreArgs& sa, int64_t n_gt, hipStream_t st) {
   const int r0 = sa.p.sub[0].R, r1 = sa.p.nsub > 1 ? sa.p.sub[1].R : 0;
+  if (sa.p.sub[0].mse) {
+    if (sa.p.nsub != 1) return false;
+    switch (r0) {
+      case 1: launch_bitslice<1, 0, true>(sa, n_gt, st); return true;
+      case 2: launch_bitslice<2, 0, true>(sa, n_gt, st); return true;
+      case 3: launch_bitslice<3, 0, true>(sa, n_gt, st); return true;
+      case 4: launch_bitslice<4, 0, true>(sa, n_gt, st); return true;
+      default: return false;
+    }
+  }
 #define TQ_BS(A, B) if (r0 == A && r1 == B) { launch_bitslice<A, B>(sa, n_gt, st); return true; }
   TQ_BS(1, 0) TQ_BS(2, 0) TQ_BS(3, 0) TQ_BS(4, 0)
   TQ_BS(1, 1) TQ_BS(1, 2) TQ_BS(1, 3) TQ_BS(1, 4)

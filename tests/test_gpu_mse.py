@@ -103,10 +103,12 @@ def test_dequantize_inner_product_plans(d, bits, mask):
     parity.check_dequantized(_np(xh), xr, norms, False, "ip dequant d=%d" % d)
 
 
-def test_mse_plan_rejects_scoring_and_bad_arguments():
-    plan = tq.tq_plan_create_mse(128, 3, 0)
+def test_mse_plan_rejects_long_vector_scoring_and_bad_arguments():
+    """Scoring MSE records is implemented for D <= 128 (tests/test_gpu_mse_score.py); a
+    longer MSE plan is refused, as are bad bit widths and lengths."""
+    plan = tq.tq_plan_create_mse(256, 3, 0)
     codes = torch.zeros((10, plan.record_bytes), dtype=torch.uint8, device=DEV)
-    y = torch.zeros((4, 128), device=DEV)
+    y = torch.zeros((4, 256), device=DEV)
     with pytest.raises(tq.TqError):
         tq.tq_score(plan, y, codes, n=10)
     with pytest.raises(tq.TqError):
