@@ -145,9 +145,8 @@ tq_status tq_plan_create_heads(int d, int bits, uint64_t seed, int n_heads,
  *   d     input dimension, 1 <= d <= 2048
  *   bits  b = R, 1..4
  * tq_encode writes its records (layout above) and tq_dequantize reconstructs
- * them.  For D <= 128, tq_score, tq_score_noalloc and tq_score_topk score them
- * (n <Pi y, c[idx]>, see tq_score); for longer vectors those calls and tq_qjl
- * return TQ_EUNSUPPORTED.
+ * them; tq_score, tq_score_noalloc and tq_score_topk score them (n <Pi y,
+ * c[idx]>, see tq_score); tq_qjl returns TQ_EUNSUPPORTED for it.
  * Errors: TQ_EINVAL, TQ_ENOMEM, TQ_EDEVICE.  On error *out is set to NULL.
  */
 tq_status tq_plan_create_mse(int d, int bits, uint64_t seed, tq_plan** out);
@@ -204,13 +203,13 @@ tq_status tq_encode_groups(const tq_plan* plan, const void* x, tq_dtype dt, int6
  * uses head g % n_heads.
  * Uses a workspace of n_groups*nq_per_group*(6*D) floats per sub-plan (the
  * per-stream buffer above).
- * A TurboQuant-MSE plan (D <= 128) gives est = n <Pi pad(y), c[idx]>: the
- * overview's quantized distance (§4.2.2; the query stays full precision) with
- * the norm kept apart as §4.2.1 stores it.  It is not unbiased: over random
- * rotations its mean is <x, y> (1 - D E[(T - Q(T))^2]).
+ * A TurboQuant-MSE plan gives est = n <Pi pad(y), c[idx]>: the overview's
+ * quantized distance (§4.2.2; the query stays full precision) with the norm
+ * kept apart as §4.2.1 stores it.  It is not unbiased: over random rotations
+ * its mean is <x, y> (1 - D E[(T - Q(T))^2]).  For D >= 256 it runs on the
+ * decoded fp16 key tiles of the many-query scorer whatever the query count.
  * Errors: TQ_EINVAL (null, negative sizes, ldq < d, misalignment), TQ_ENOMEM,
- * TQ_EDEVICE; TQ_EUNSUPPORTED for an MSE plan with D > 128.  Empty sizes are a
- * no-op.
+ * TQ_EDEVICE.  Empty sizes are a no-op.
  */
 tq_status tq_score(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_per_group,
                    int64_t n_groups, int64_t ldq, const void* codes, int64_t n, float* scores,
@@ -261,8 +260,7 @@ tq_status tq_topk(const float* scores, int64_t nq, int64_t n, int k, int64_t* id
  * workgroups).  Other shapes score into 4*n bytes per query row and select from
  * it.  Both live in the per-stream workspace above.
  * Errors: TQ_EINVAL (as tq_score; k < 1, k > 64, k > n, n >= 2^31),
- * TQ_ENOMEM, TQ_EDEVICE; TQ_EUNSUPPORTED for an MSE plan with D > 128.  NaN
- * estimates are not supported.
+ * TQ_ENOMEM, TQ_EDEVICE.  NaN estimates are not supported.
  */
 tq_status tq_score_topk(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_per_group,
                         int64_t n_groups, int64_t ldq, const void* codes, int64_t n, int k,

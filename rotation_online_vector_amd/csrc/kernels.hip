@@ -3257,12 +3257,16 @@ static int launch_score_impl(const PlanDev& p, const void* q, int dt, int64_t nq
       sa.ec[sb] = fa.ec;
     } else {
       hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)nq), dim3(kBlock), 0, st, qa);
-      const int nparts = (p.sub[sb].k + kProjCols - 1) / kProjCols;
-      float* part = reinterpret_cast<float*>(wb + off_p[sb]);
-      hipLaunchKernelGGL(qproj_mfma_kernel, dim3((unsigned)((nq + kProjRows - 1) / kProjRows), (unsigned)nparts),
-                         dim3(kBlock), 0, st, qa, nq, part);
-      hipLaunchKernelGGL(qsum_kernel, dim3((unsigned)((nq + kBlock - 1) / kBlock)), dim3(kBlock), 0,
-                         st, qa.sums, part, nq, nparts);
+      if (p.sub[sb].k > 0) {               // w = S y' (an MSE plan has no projection)
+        const int nparts = (p.sub[sb].k + kProjCols - 1) / kProjCols;
+        float* part = reinterpret_cast<float*>(wb + off_p[sb]);
+        hipLaunchKernelGGL(qproj_mfma_kernel, dim3((unsigned)((nq + kProjRows - 1) / kProjRows), (unsigned)nparts),
+                           dim3(kBlock), 0, st, qa, nq, part);
+        hipLaunchKernelGGL(qsum_kernel, dim3((unsigned)((nq + kBlock - 1) / kBlock)), dim3(kBlock), 0,
+                           st, qa.sums, part, nq, nparts);
+      } else {
+        sa.w[sb] = nullptr;
+      }
       if (wide) {
         WideImgArgs wa;
         wa.s = p.sub[sb];

@@ -1,4 +1,5 @@
-// Scorer for long vectors with many queries per group (D >= 256, one inner-product sub-plan):
+// Scorer for long vectors with many queries per group (D >= 256, one inner-product sub-plan),
+// and for every TurboQuant-MSE plan with D >= 256 (centroid terms only, see below):
 // the estimate est = n (<y', c[idx]> + gamma sqrt(pi/2)/k <w, 2 beta - 1>) (TurboQuant
 // technical overview §1.2.3, §4.2.2; deep dive §三) as one fp16 matrix product over 2D terms
 // per (query, key): the key side holds, per 32-coordinate chunk, the 32 centroid values
@@ -14,6 +15,11 @@
 // multiply the current one.  Query blocks vary fastest over the grid, so with up to 8 of them
 // per group each of the chip's 8 L2 slices (workgroups go round-robin over them) serves a
 // fixed subset of the query images.
+//
+// MSE records (R index words per chunk and the norm; overview §4.2.1's index vectors) give
+// est = n <y', c[idx]> (the quantized distance of §4.2.2): the decode writes the centroid k
+// steps only and the product runs over D terms.  There is no other long-vector path for them,
+// so any query count takes this one (a group's rows pad to whole 32-row tiles).
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -50,10 +56,11 @@ __global__ void __launch_bounds__(kBlock) qimage_f16_kernel(const float* yrot, c
                                                             uint16_t* img, float* isc) {
   const int64_t q = blockIdx.x;
   const float* y = yrot + q * D;
-  const float* wq = w + q * D;
+  const float* wq = w ? w + q * D : nullptr;     // none for an MSE plan: its half of the image is 0
   __shared__ float red[kBlock / kWave];
   float m = 0.f;
-  for (int i = threadIdx.x; i < D; i += kBlock) m = fmaxf(m, fmaxf(fabsf(y[i]), fabsf(wq[i]) * kSignDown));
+  for (int i = threadIdx.x; i < D; i += kBlock)
+    m = fmaxf(m, fmaxf(fabsf(y[i]), wq ? fabsf(wq[i]) * kSignDown : 0.f));
   for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
@@ -69,7 +76,8 @@ __global__ void __launch_bounds__(kBlock) qimage_f16_kernel(const float* yrot, c
   const int r = (int)(qi & 31);
   for (int i = threadIdx.x; i < 2 * D; i += kBlock) {
     const int g = i >> 6, e = i & 63;                       // chunk, image entry
-    const float v = e < 32 ? y[32 * g + e] * sigma : wq[32 * g + e - 32] * (sigma * kSignDown);
+    const float v = e < 32 ? y[32 * g + e] * sigma
+                           : (wq ? wq[32 * g + e - 32] * (sigma * kSignDown) : 0.f);
     const int ks = e >> 4, hh = (e >> 3) & 1, j = e & 7;
     tile[((g * 4 + ks) * 64 + r + 32 * hh) * 8 + j] = (uint16_t)f16_bits(v);
   }
@@ -88,11 +96,12 @@ struct ScoreF16Args {
   float* scores;           // [n_groups * nq_per_group][n]
 };
 
-template <int R>
+template <int R, bool MSE>
 __global__ void __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(2)))
 score_f16_kernel(ScoreF16Args a) {
   static_assert(kBlock == 256 && kFK == 128, "thread t decodes half a chunk of key t / 2");
-  constexpr int W = R + 1;                 // words per chunk: R index planes, the sign word
+  constexpr int W = MSE ? R : R + 1;       // words per chunk: R index planes (, the sign word)
+  constexpr int KS = MSE ? 2 : 4;          // k steps per chunk: centroids (, sign weights)
   constexpr int NPAIR = 1 << (2 * R);
   const SubDev& s = a.s;
   const int D = s.D, NC = D / 32;
@@ -125,7 +134,7 @@ score_f16_kernel(ScoreF16Args a) {
   uint32_t G2;                                               // +gamma K 2^12, both halves
   {
     const float* tail = reinterpret_cast<const float*>(rec + NC * W * 4);
-    const float nk = tail[0], gam = tail[1];
+    const float nk = tail[0], gam = MSE ? 0.f : tail[1];
     const float K = sqrtf(0.5f * (float)M_PI) / (float)D;
     const uint32_t g16 = f16_bits(gam * K * kSignUp);
     G2 = g16 | (g16 << 16);
@@ -137,9 +146,12 @@ score_f16_kernel(ScoreF16Args a) {
     uint32_t wd[W];
 #pragma unroll
     for (int m = 0; m < W; ++m) wd[m] = wd0[m] >> (16 * h);
-    const uint32_t nb = ~wd[R];                            // set bit = beta 0 = weight -G
-    // sign bit 2j + 1 moved to 2j + 16, so that one shift puts pair j's two bits at 15 and 31
-    const uint32_t z = (nb & 0x5555u) | ((nb & 0xAAAAu) << 15);
+    uint32_t z = 0u;
+    if constexpr (!MSE) {
+      const uint32_t nb = ~wd[R];                          // set bit = beta 0 = weight -G
+      // sign bit 2j + 1 moved to 2j + 16, so that one shift puts pair j's two bits at 15, 31
+      z = (nb & 0x5555u) | ((nb & 0xAAAAu) << 15);
+    }
     // planes 0 and 1 of pair j side by side: nibble j / 2 of pq[j % 2]
     uint32_t pq[2] = {0u, 0u};
     if constexpr (R >= 2) {
@@ -159,8 +171,10 @@ score_f16_kernel(ScoreF16Args a) {
     }
     bfr[buf][h][nt][col] = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     bfr[buf][h][nt][col + 32] = make_uint4(cw[4], cw[5], cw[6], cw[7]);
-    bfr[buf][2 + h][nt][col] = make_uint4(sw[0], sw[1], sw[2], sw[3]);
-    bfr[buf][2 + h][nt][col + 32] = make_uint4(sw[4], sw[5], sw[6], sw[7]);
+    if constexpr (!MSE) {
+      bfr[buf][2 + h][nt][col] = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+      bfr[buf][2 + h][nt][col + 32] = make_uint4(sw[4], sw[5], sw[6], sw[7]);
+    }
   };
   auto load_words = [&](int g, uint32_t (&wd)[W]) {
 #pragma unroll
@@ -215,8 +229,8 @@ score_f16_kernel(ScoreF16Args a) {
 #pragma unroll
     for (int t = 0; t < 4; ++t) bc[t] = bfr[buf][0][t][lane];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3)
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks < KS - 1)
 #pragma unroll
         for (int t = 0; t < 4; ++t) bn[t] = bfr[buf][ks + 1][t][lane];
 #pragma unroll
@@ -228,14 +242,15 @@ score_f16_kernel(ScoreF16Args a) {
               f16x8_from_words(av[mt][ks].x, av[mt][ks].y, av[mt][ks].z, av[mt][ks].w), bv,
               acc[mt][t], 0, 0, 0);
       }
-      if (ks < 3)
+      if (ks < KS - 1)
 #pragma unroll
         for (int t = 0; t < 4; ++t) bc[t] = bn[t];
     }
-    // issue order: the 4 reads of step 0, then (1 LDS read, 2 MFMAs) x 12, then the last 8
+    // issue order: the 4 reads of step 0, then (1 LDS read, 2 MFMAs) x 4 (KS - 1), then the
+    // last 8
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);     // 0x100: LDS reads
 #pragma unroll
-    for (int i = 0; i < 12; ++i) {
+    for (int i = 0; i < 4 * (KS - 1); ++i) {
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 0x008: matrix instructions
     }
@@ -269,8 +284,9 @@ score_f16_kernel(ScoreF16Args a) {
 
 bool score_f16_applies(const PlanDev& p, int64_t nq_per_group) {
   const SubDev& s = p.sub[0];
-  return p.nsub == 1 && !s.mse && s.D >= 256 && s.R >= 1 && s.R <= 4 && s.k == s.D &&
-         nq_per_group >= kScoreF16MinQueries;
+  if (p.nsub != 1 || s.D < 256 || s.R < 1 || s.R > 4) return false;
+  if (s.mse) return true;                  // the only long-vector path for MSE records
+  return s.k == s.D && nq_per_group >= kScoreF16MinQueries;
 }
 
 int launch_score_f16(const PlanDev& p, const float* yrot, const float* w, uint16_t* img,
@@ -292,13 +308,21 @@ int launch_score_f16(const PlanDev& p, const float* yrot, const float* w, uint16
   fa.scores = scores;
   const int64_t nkb = (n + kFK - 1) / kFK;
   const dim3 grid((unsigned)(nkb * fa.n_qblocks), (unsigned)n_groups);
+#define TQ_F16(RR)                                                                          \
+  case RR:                                                                                  \
+    if (s.mse)                                                                              \
+      hipLaunchKernelGGL((score_f16_kernel<RR, true>), grid, dim3(kBlock), 0, st, fa);      \
+    else                                                                                    \
+      hipLaunchKernelGGL((score_f16_kernel<RR, false>), grid, dim3(kBlock), 0, st, fa);     \
+    break;
   switch (s.R) {
-    case 1: hipLaunchKernelGGL(score_f16_kernel<1>, grid, dim3(kBlock), 0, st, fa); break;
-    case 2: hipLaunchKernelGGL(score_f16_kernel<2>, grid, dim3(kBlock), 0, st, fa); break;
-    case 3: hipLaunchKernelGGL(score_f16_kernel<3>, grid, dim3(kBlock), 0, st, fa); break;
-    case 4: hipLaunchKernelGGL(score_f16_kernel<4>, grid, dim3(kBlock), 0, st, fa); break;
+    TQ_F16(1)
+    TQ_F16(2)
+    TQ_F16(3)
+    TQ_F16(4)
     default: return (int)hipErrorInvalidValue;
   }
+#undef TQ_F16
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? 0 : (int)e;
 }

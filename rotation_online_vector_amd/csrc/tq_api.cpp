@@ -661,7 +661,6 @@ tq_status tq_score(const tq_plan* plan, const void* q, tq_dtype dt, int64_t nq_p
   if (nq_per_group * n_groups > (int64_t)1 << 31 || n_groups > 65535 * 64) return TQ_EINVAL;
   if (n_groups % plan->dev.n_heads) return TQ_EINVAL;   // group g reads head g % n_heads
   if (!plan_device_ok(plan)) return TQ_EINVAL;
-  if (is_mse(plan) && plan->dev.sub[0].D > 128) return TQ_EUNSUPPORTED;
   return from_hip(launch_score(plan->dev, q, (int)dt, nq_per_group, n_groups, ldq,
                                static_cast<const uint8_t*>(codes), n, scores, stream));
 }
@@ -679,7 +678,6 @@ tq_status tq_score_noalloc(const tq_plan* plan, const void* q, tq_dtype dt, int6
   if (nq_per_group * n_groups > (int64_t)1 << 31 || n_groups > 65535 * 64) return TQ_EINVAL;
   if (n_groups % plan->dev.n_heads) return TQ_EINVAL;   // group g reads head g % n_heads
   if (!plan_device_ok(plan)) return TQ_EINVAL;
-  if (is_mse(plan) && plan->dev.sub[0].D > 128) return TQ_EUNSUPPORTED;
   const int rc = launch_score_noalloc(plan->dev, q, (int)dt, nq_per_group, n_groups, ldq,
                                       static_cast<const uint8_t*>(codes), n, scores, stream);
   if (rc == (int)hipErrorOutOfMemory) return TQ_EINVAL;   // workspace beyond the fixed array
@@ -711,7 +709,6 @@ tq_status tq_score_topk(const tq_plan* plan, const void* q, tq_dtype dt, int64_t
   if (nq_per_group * n_groups > (int64_t)1 << 31 || n_groups > 65535 * 64) return TQ_EINVAL;
   if (n_groups % plan->dev.n_heads) return TQ_EINVAL;
   if (!plan_device_ok(plan)) return TQ_EINVAL;
-  if (is_mse(plan) && plan->dev.sub[0].D > 128) return TQ_EUNSUPPORTED;
   return from_hip(launch_score_topk(plan->dev, q, (int)dt, nq_per_group, n_groups, ldq,
                                     static_cast<const uint8_t*>(codes), n, k, ids, vals, stream));
 }
