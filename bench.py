@@ -47,7 +47,7 @@ def parse():
     ap.add_argument("--cpu-sample-groups", type=int, default=16)
     ap.add_argument("--workload", default="longctx",
                     choices=["longctx", "kv", "split35", "split25", "retrieval", "retrieval2",
-                             "small", "mse", "attend", "decode"],
+                             "small", "mse", "attend", "decode", "msekeys", "retrievalmse"],
                     help="long-context decode (default, the headline line); the other shapes "
                          "report the same fields for their own step (no CPU leg)")
     ap.add_argument("--hbm-rotate", type=int, default=0, metavar="MIB",
@@ -72,6 +72,8 @@ DTYPES = {
     "decode": MIXED_D128 + "; fp16 mfma attention", "mse": "fp16 mfma, f32 acc",
     "retrieval": "f32 fwht; bf16 mfma signs and query projection; fp16 mfma scores; f32 acc",
     "retrieval2": "f32 fwht; bf16 mfma signs and query projection; fp16 mfma scores; f32 acc",
+    "msekeys": "fp16 mfma rotation (encode); f8+f4 mfma scores; f32 acc",
+    "retrievalmse": "f32 fwht; fp16 mfma scores; f32 acc",
 }
 OPERANDS_D128 = {
     "tq_encode": "bf16 keys scaled to fp16 against the exact integer rotation in fp16; the "
@@ -196,11 +198,12 @@ def build_workload(name, dev, W_all, rotate_mib=0):
     import rotation_online_vector_amd as tq
     import workloads
     W = W_all[name]
-    if name == "longctx":
+    if name in ("longctx", "msekeys"):
         keys, queries, _ = workloads.longctx_inputs(dev)
         n_seq, n_kv, n_tok, d, G = W["n_seq"], W["n_kv"], W["n_tok"], W["d"], W["group"]
         n_keys, n_groups = n_seq * n_kv * n_tok, n_seq * n_kv
-        plan = tq.tq_plan_create(d, W["bits"], W["seed"])
+        plan = (tq.tq_plan_create_mse if name == "msekeys" else tq.tq_plan_create)(
+            d, W["bits"], W["seed"])
         rb = plan.record_bytes
         codes = torch.empty((n_keys, rb), dtype=torch.uint8, device=dev)
         scores = torch.empty((n_groups * G, n_tok), dtype=torch.float32, device=dev)
@@ -209,7 +212,8 @@ def build_workload(name, dev, W_all, rotate_mib=0):
         return dict(
             config={"workload": W["name"], "n_seq": n_seq, "kv_heads": n_kv, "tokens": n_tok,
                     "d": d, "bits": W["bits"], "query_heads_per_seq": n_kv * G, "gqa_group": G,
-                    "keys_per_step": n_keys, "scores_per_step": n_scores, "record_bytes": rb},
+                    "keys_per_step": n_keys, "scores_per_step": n_scores, "record_bytes": rb,
+                    **({"mode": "mse"} if name == "msekeys" else {})},
             phases=[("tq_encode", lambda: tq.tq_encode(plan, xk, codes)),
                     ("tq_score", lambda: tq.tq_score(plan, qv, codes, n=n_tok, nq_per_group=G,
                                                      n_groups=n_groups, scores=scores))],
@@ -387,7 +391,7 @@ def build_workload(name, dev, W_all, rotate_mib=0):
                    "tq_score": n_keys * rb + n_scores * 4 + n_kv * G * d * 2},
             copies=R, advance=lambda: cur.__setitem__(0, (cur[0] + 1) % R),
             n_keys=n_keys, n_scores=n_scores, keep=(plan, keys, queries, xs, cs, ss))
-    if name in ("retrieval", "retrieval2", "small"):
+    if name in ("retrieval", "retrieval2", "small", "retrievalmse"):
         if name != "small":
             keys, queries = workloads.retrieval_inputs(dev, n_keys=W["n_keys"],
                                                        n_queries=W["n_queries"], d=W["d"],
@@ -396,7 +400,8 @@ def build_workload(name, dev, W_all, rotate_mib=0):
             k_np, q_np = workloads.small_inputs(W["n_keys"], W["n_queries"], W["d"], W["seed"])
             keys, queries = torch.from_numpy(k_np).to(dev), torch.from_numpy(q_np).to(dev)
         n, nq, d, k = W["n_keys"], W["n_queries"], W["d"], W.get("topk", 10)
-        plan = tq.tq_plan_create(d, W["bits"], W["seed"])
+        plan = (tq.tq_plan_create_mse if name == "retrievalmse" else tq.tq_plan_create)(
+            d, W["bits"], W["seed"])
         rb = plan.record_bytes
         D = plan.desc["sub"][0]["D"]
         codes = torch.empty((n, rb), dtype=torch.uint8, device=dev)
@@ -404,7 +409,7 @@ def build_workload(name, dev, W_all, rotate_mib=0):
         vals = torch.empty((nq, k), dtype=torch.float32, device=dev)
         config = {"workload": W["name"], "keys": n, "queries": nq, "d": d, "D": D,
                   "bits": W["bits"], "topk": k, "keys_per_step": n, "scores_per_step": n * nq,
-                  "record_bytes": rb}
+                  "record_bytes": rb, **({"mode": "mse"} if name == "retrievalmse" else {})}
         enc = ("tq_encode", lambda: tq.tq_encode(plan, keys, codes))
         enc_bytes = n * d * 4 + n * rb
         def recall_at_k(ids_fn, sample=64):
@@ -435,6 +440,19 @@ def build_workload(name, dev, W_all, rotate_mib=0):
                        "tq_rerank": 2.0 * d * kc * nq},
                 quality=recall_at_k(lambda: ids),
                 n_keys=n, n_scores=n * nq, keep=(plan, keys, queries, codes, ids, vals, cand, cvals))
+        if name == "retrievalmse":
+            # an MSE index (overview §4.2.1) searched by the quantized distance (§4.2.2): the
+            # scores go to the per-stream workspace and the top-k is selected from them
+            return dict(
+                config=config,
+                phases=[enc, ("tq_score_topk",
+                              lambda: tq.tq_score_topk(plan, queries, codes, n, k, ids=ids, vals=vals))],
+                bytes={"tq_encode": enc_bytes,
+                       "tq_score_topk": n * rb + nq * d * 4 + 2 * n * nq * 4 + nq * k * 12},
+                # MFMA work: the centroid terms of every (query, key) pair (2 D per score)
+                flops={"tq_score_topk": 2.0 * D * n * nq},
+                quality=recall_at_k(lambda: ids),
+                n_keys=n, n_scores=n * nq, keep=(plan, keys, queries, codes, ids, vals))
         if name == "retrieval":
             # score and select in one call: the score matrix is never stored
             return dict(
@@ -472,7 +490,8 @@ def main():
              "split25": workloads.SPLIT_25, "retrieval": workloads.RETRIEVAL,
              "small": workloads.SMALL, "mse": workloads.MSE_LONGCTX,
              "attend": workloads.ATTEND_LONGCTX, "decode": workloads.DECODE_LONGCTX,
-             "retrieval2": dict(workloads.RETRIEVAL, name=workloads.RETRIEVAL["name"] + "-2stage")}
+             "retrieval2": dict(workloads.RETRIEVAL, name=workloads.RETRIEVAL["name"] + "-2stage"),
+             "msekeys": workloads.MSEKEYS_LONGCTX, "retrievalmse": workloads.RETRIEVAL_MSE}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.hbm_rotate and args.workload not in ("kv", "split35", "split25"):
@@ -540,15 +559,16 @@ def main():
     ceiling = hbm_ceiling(dev) if not args.no_hbm_ceiling else None
     dom = max(kern, key=lambda k: kern[k]["ms"])
     flops = wl.get("flops")
-    if flops:
+    for k, v in kern.items():
+        if flops and k in flops:
+            v["tflops"] = flops[k] / (v["ms"] * 1e-3) / 1e12
+    if flops and dom in flops:
         # a contraction-bound workload: algorithmic MFMA flops per launch against the dense
         # 16-bit peak (the sign projection runs on bf16 MFMA, the scorer on fp16: one peak)
-        tf = flops[dom] / (kern[dom]["ms"] * 1e-3) / 1e12
+        tf = kern[dom]["tflops"]
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(tf, 1), "peak": MFMA_16BIT_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(tf / MFMA_16BIT_TFLOPS, 4), "traffic": None,
                 "flops_per_launch": flops[dom]}
-        for k, v in kern.items():
-            v["tflops"] = flops[k] / (v["ms"] * 1e-3) / 1e12
     else:
         # the decode step runs the attention workload's kernels on the same cache
         traffic = measured_traffic("attend" if args.workload == "decode" else args.workload, dom)

@@ -37,6 +37,11 @@ LONGCTX = dict(name="longctx-16x8x131072x128-bf16-b3", n_seq=16, n_kv=8, n_tok=1
 # TurboQuant-MSE on the same keys: 3-bit codes for most heads (technical overview §4.1.1),
 # dequantized in one batch before attention (§4.1.2)
 MSE_LONGCTX = dict(LONGCTX, name="mse-longctx-16x8x131072x128-bf16-b3")
+# the same keys held under the 3-bit MSE plan and scored (overview §4.1.1: 3-bit MSE for most
+# heads), and the retrieval shape as an MSE index (§4.2.1: every vector MSE-quantized, its
+# norm kept) searched by the quantized distance of §4.2.2
+MSEKEYS_LONGCTX = dict(LONGCTX, name="msekeys-longctx-16x8x131072x128-bf16-m3")
+RETRIEVAL_MSE = dict(RETRIEVAL, name="retrieval-mse-1e6x1536-fp32-m4")
 # one decode step over the same cache held quantized: keys under the inner-product plan
 # (scored), values under a 3-bit MSE plan (attended), both encoded before the step
 ATTEND_LONGCTX = dict(LONGCTX, name="attend-longctx-16x8x131072x128-k3ip-v3mse",
