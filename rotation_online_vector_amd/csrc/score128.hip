@@ -223,13 +223,14 @@ __device__ __forceinline__ KeyWords<R> load_key_words(const SubDev& s, const uin
     k.wd[m] = (key_ok && chunk_ok) ? v : 0u;
   }
   const uint32_t* tail = reinterpret_cast<const uint32_t*>(rec + (s.D / 32) * W * 4);
-  const uint32_t t0 = tail[0];
-  k.nrm = key_ok ? __uint_as_float(t0) : 0.f;
   if constexpr (MSE) {
+    const uint32_t t0 = tail[0];
+    k.nrm = key_ok ? __uint_as_float(t0) : 0.f;
     k.wd[R] = 0u;
     k.gam = 0.f;
   } else {
-    const uint32_t t1 = tail[1];
+    const uint32_t t0 = tail[0], t1 = tail[1];
+    k.nrm = key_ok ? __uint_as_float(t0) : 0.f;
     k.gam = key_ok ? __uint_as_float(t1) : 0.f;
   }
   return k;
@@ -250,9 +251,11 @@ __device__ __forceinline__ float bitslice_estimate(const KeyWords<R>& k, const i
       if ((pmask_c<R>(p) >> m) & 1) P ^= k.wd[m];
     am = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[p], fp4_operand(P), am, 0, 4, 0, 127, 0, 127);
   }
+  // the sign plane's product issues before the index planes' sums are read
+  if constexpr (!MSE)
+    aq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[NP], fp4_operand(k.wd[R]), aq, 0, 4, 0, 127, 0, 127);
   const float msum = am[0] + am[1] + am[2];
   if constexpr (MSE) return k.nrm * fmaf(e4[1], msum, e4[0]);
-  aq = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[NP], fp4_operand(k.wd[R]), aq, 0, 4, 0, 127, 0, 127);
   const float qsum = aq[0] + aq[1] + aq[2];
   return k.nrm * (fmaf(e4[1], msum, e4[0]) + k.gam * fmaf(e4[3], qsum, e4[2]));
 }
