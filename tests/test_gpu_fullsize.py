@@ -148,19 +148,44 @@ def test_retrieval_shape_full_with_topk():
 
 def test_mse_long_context_shape_full_as_benchmarked():
     """TurboQuant-MSE encode + dequantize of all 16.8 M long-context keys (the MSE bench
-    step); sampled records against the oracle's encode, their reconstructions against the
-    oracle's dequantization of the stored codes."""
+    step) and their scores against the 512 query heads (the MSE-key bench step); sampled
+    records against the oracle's encode, their reconstructions against the oracle's
+    dequantization of the stored codes, and sampled (query, key) scores against the oracle's
+    quantized distance on the stored codes and, where the cells match, on its own codes."""
     from oracle import layout
     W = workloads.MSE_LONGCTX
-    keys, _, _ = workloads.longctx_inputs(DEV)
-    d = W["d"]
+    assert workloads.MSEKEYS_LONGCTX["bits"] == W["bits"] and workloads.MSEKEYS_LONGCTX["seed"] == W["seed"]
+    keys, queries, _ = workloads.longctx_inputs(DEV)
+    n_seq, n_kv, n_tok, d, G = W["n_seq"], W["n_kv"], W["n_tok"], W["d"], W["group"]
     plan = tq.tq_plan_create_mse(d, W["bits"], W["seed"])
     op = otq.make_mse_plan(d, W["bits"], W["seed"])
     flat = keys.view(-1, d)
     n = flat.shape[0]
     codes = tq.tq_encode(plan, flat)
     xh = tq.tq_dequantize(plan, codes, n, dtype=torch.bfloat16)
+    scores = tq.tq_score(plan, queries.view(-1, d), codes, n=n_tok, nq_per_group=G,
+                         n_groups=n_seq * n_kv)
     torch.cuda.synchronize()
+    srng = np.random.default_rng(9)
+    for (s, h) in ((0, 1), (9, 4), (15, 7)):
+        kidx = np.sort(srng.choice(n_tok, 768, replace=False))
+        ki = torch.as_tensor(kidx, device=DEV)
+        g = s * n_kv + h
+        rows = torch.as_tensor(g * n_tok + kidx, device=DEV)
+        got = layout.unpack_mse(codes[rows].cpu().numpy(), op.D, W["bits"])
+        x = _np64(keys[s, h][ki])
+        own = otq.encode_mse(op, x)
+        parity.compare_codes_mse(op, own, got, "mse keys seq %d head %d" % (s, h))
+        y = _np64(queries[s, h * G:(h + 1) * G])
+        est = scores[g * G:(g + 1) * G][:, ki].cpu().numpy().astype(np.float64)
+        qn, xn = np.linalg.norm(y, axis=1), np.linalg.norm(x, axis=1)
+        parity.check_scores(est, otq.score_mse(op, dict(idx=got["idx"], norm=got["norm"]), y),
+                            qn, xn, "mse keys seq %d head %d" % (s, h))
+        same = np.all(own["idx"] == got["idx"], axis=1)
+        assert same.mean() > 0.99
+        own_s = dict(idx=own["idx"][same], norm=own["norm"][same].astype(np.float32).astype(np.float64))
+        parity.check_scores(est[:, same], otq.score_mse(op, own_s, y), qn, xn[same],
+                            "mse keys seq %d head %d (oracle codes)" % (s, h))
     rng = np.random.default_rng(8)
     rows = np.sort(np.concatenate([rng.choice(n, 3000, replace=False), [0, n - 1]]))
     ri = torch.as_tensor(rows, device=DEV)
