@@ -36,7 +36,8 @@ def _np(t):
     (128, 3, 17, 4, 5, "bfloat16", "float32"), (128, 3, 32768, 4, 8, "bfloat16", "bfloat16"),
     (200, 3, 1500, 4, 2, "float32", "float32"), (256, 2, 700, 300, 1, "bfloat16", "float32"),
     (512, 1, 401, 1, 3, "float32", "bfloat16"), (1536, 4, 3000, 130, 1, "float32", "float32"),
-    (2048, 3, 129, 33, 2, "bfloat16", "bfloat16")])
+    (2048, 3, 129, 33, 2, "bfloat16", "bfloat16"), (300, 2, 1, 5, 2, "float32", "float32"),
+    (128, 4, 1, 4, 3, "bfloat16", "float32")])
 def test_mse_scores_match_oracle(d, bits, n, nqg, groups, kdt, qdt):
     rng = np.random.default_rng(d * 13 + bits * 5 + n)
     X = rng.standard_normal((groups * n, d)).astype(np.float32)
