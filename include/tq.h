@@ -11,8 +11,9 @@
  * seeded Gaussian matrix.  A full-precision query is rotated the same way and
  * scored against the packed codes with an unbiased inner-product estimate.
  * Around that path: top-k selection (fused with scoring or on a score
- * matrix), the exact re-rank of a candidate set, TurboQuant-MSE plans and
- * dequantization, decode attention over quantized values, and the KV-cache
+ * matrix), the exact re-rank of a candidate set, TurboQuant-MSE plans (their
+ * records dequantized, or scored by the quantized distance n <Pi y, c[idx]>),
+ * decode attention over quantized values, and the KV-cache
  * policy layer (outlier channels by variance, appending one record per head).
  *
  * Conventions for every call:
