@@ -447,8 +447,7 @@ def build_workload(name, dev, W_all, rotate_mib=0):
                 config=config,
                 phases=[enc, ("tq_score_topk",
                               lambda: tq.tq_score_topk(plan, queries, codes, n, k, ids=ids, vals=vals))],
-                bytes={"tq_encode": enc_bytes,
-                       "tq_score_topk": n * rb + nq * d * 4 + 2 * n * nq * 4 + nq * k * 12},
+                bytes={"tq_encode": enc_bytes, "tq_score_topk": n * rb + nq * d * 4 + nq * k * 12},
                 # MFMA work: the centroid terms of every (query, key) pair (2 D per score)
                 flops={"tq_score_topk": 2.0 * D * n * nq},
                 quality=recall_at_k(lambda: ids),

@@ -21,6 +21,8 @@ Shapes (all keys/queries are row vectors of the key dimension):
             (3-bit MSE plan), both held encoded; one decode step scores and attends
   decode  : the attend caches; a step appends one token per (sequence, KV head) to both
             caches (at the last slot, so the length stays 131072), then scores and attends
+  msekeys : the longctx keys under the 3-bit MSE plan, encoded and scored
+  retrievalmse: the retrieval vectors as a 4-bit MSE index, encoded and searched (top-10)
 """
 import numpy as np
 
