@@ -47,7 +47,8 @@ def parse():
     ap.add_argument("--cpu-sample-groups", type=int, default=16)
     ap.add_argument("--workload", default="longctx",
                     choices=["longctx", "kv", "split35", "split25", "retrieval", "retrieval2",
-                             "small", "mse", "attend", "decode", "msekeys", "retrievalmse"],
+                             "small", "mse", "attend", "decode", "msekeys", "retrievalmse",
+                             "decodemse"],
                     help="long-context decode (default, the headline line); the other shapes "
                          "report the same fields for their own step (no CPU leg)")
     ap.add_argument("--hbm-rotate", type=int, default=0, metavar="MIB",
@@ -73,6 +74,7 @@ DTYPES = {
     "retrieval": "f32 fwht; bf16 mfma signs and query projection; fp16 mfma scores; f32 acc",
     "retrieval2": "f32 fwht; bf16 mfma signs and query projection; fp16 mfma scores; f32 acc",
     "msekeys": "fp16 mfma rotation (encode); f8+f4 mfma scores; f32 acc",
+    "decodemse": "f8+f4 mfma scores; fp16 mfma attention; f32 acc",
     "retrievalmse": "f32 fwht; fp16 mfma scores; f32 acc",
 }
 OPERANDS_D128 = {
@@ -242,12 +244,14 @@ def build_workload(name, dev, W_all, rotate_mib=0):
             value=(n_keys, "vectors/s",
                    "TurboQuant-MSE encode + dequantize vectors/sec (d=128, 3-bit)"),
             keep=(plan, keys, codes, xh))
-    if name == "decode":
+    if name in ("decode", "decodemse"):
         keys, queries, _ = workloads.longctx_inputs(dev)
         vals, _, _ = workloads.longctx_inputs(dev, seed=W["v_seed"])
         n_seq, n_kv, n_tok, d, G = W["n_seq"], W["n_kv"], W["n_tok"], W["d"], W["group"]
         n_keys, n_groups = n_seq * n_kv * n_tok, n_seq * n_kv
-        kplan = tq.tq_plan_create(d, W["bits"], W["seed"])
+        # decodemse: the keys too under the 3-bit MSE plan (overview §4.1.1, most heads)
+        kplan = (tq.tq_plan_create_mse if name == "decodemse" else tq.tq_plan_create)(
+            d, W["bits"], W["seed"])
         vplan = tq.tq_plan_create_mse(d, W["v_bits"], W["v_seed"])
         kcodes = tq.tq_encode(kplan, keys.view(n_keys, d))
         vcodes = tq.tq_encode(vplan, vals.view(n_keys, d))
@@ -269,6 +273,7 @@ def build_workload(name, dev, W_all, rotate_mib=0):
         return dict(
             config={"workload": W["name"], "n_seq": n_seq, "kv_heads": n_kv, "tokens": n_tok,
                     "d": d, "k_bits": W["bits"], "v_bits": W["v_bits"], "v_mode": "mse",
+                    "k_mode": "mse" if name == "decodemse" else "inner_product",
                     "query_heads_per_seq": n_kv * G, "gqa_group": G, "keys_per_step": n_groups,
                     "scores_per_step": n_scores, "record_bytes": krb + vrb,
                     "k_record_bytes": krb, "v_record_bytes": vrb, "cache_tokens": n_keys,
@@ -490,7 +495,8 @@ def main():
              "small": workloads.SMALL, "mse": workloads.MSE_LONGCTX,
              "attend": workloads.ATTEND_LONGCTX, "decode": workloads.DECODE_LONGCTX,
              "retrieval2": dict(workloads.RETRIEVAL, name=workloads.RETRIEVAL["name"] + "-2stage"),
-             "msekeys": workloads.MSEKEYS_LONGCTX, "retrievalmse": workloads.RETRIEVAL_MSE}
+             "msekeys": workloads.MSEKEYS_LONGCTX, "retrievalmse": workloads.RETRIEVAL_MSE,
+             "decodemse": workloads.DECODE_MSE_LONGCTX}
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     if args.hbm_rotate and args.workload not in ("kv", "split35", "split25"):
@@ -570,7 +576,7 @@ def main():
                 "flops_per_launch": flops[dom]}
     else:
         # the decode step runs the attention workload's kernels on the same cache
-        traffic = measured_traffic("attend" if args.workload == "decode" else args.workload, dom)
+        traffic = measured_traffic("attend" if args.workload in ("decode", "decodemse") else args.workload, dom)
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(kern[dom]["gbs"], 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(kern[dom]["gbs"] / HBM_PEAK_GBS, 4),

@@ -23,6 +23,7 @@ Shapes (all keys/queries are row vectors of the key dimension):
             caches (at the last slot, so the length stays 131072), then scores and attends
   msekeys : the longctx keys under the 3-bit MSE plan, encoded and scored
   retrievalmse: the retrieval vectors as a 4-bit MSE index, encoded and searched (top-10)
+  decodemse: the decode step with the keys also under the 3-bit MSE plan
 """
 import numpy as np
 
@@ -51,6 +52,8 @@ ATTEND_LONGCTX = dict(LONGCTX, name="attend-longctx-16x8x131072x128-k3ip-v3mse",
 # a whole decode step over that cache: one new token per (sequence, KV head) appended to the
 # key and value caches (overview §4.1.2), then scoring and attention over all 131072 tokens
 DECODE_LONGCTX = dict(ATTEND_LONGCTX, name="decode-longctx-16x8x131072x128-k3ip-v3mse")
+# the decode step with both caches under 3-bit MSE plans (the most-heads case of §4.1.1)
+DECODE_MSE_LONGCTX = dict(DECODE_LONGCTX, name="decode-longctx-16x8x131072x128-k3mse-v3mse")
 
 
 def small_inputs(n_keys=4096, n_queries=64, d=128, seed=0):
